@@ -1,0 +1,208 @@
+"""Benchmark of the conv2d hot path on one MI355X.
+
+One step = fprop (+bias+ReLU) + dgrad + wgrad of one batch of the workload
+(default: 64x56x56x64 -> 64, 3x3, stride 1, pad 1, fp16, Gaussian data), all
+through the C ABI, inputs resident in HBM before the timed region.  Prints one
+JSON line:
+  value      = FLOPs of the three passes / wall time per step (TFLOP/s),
+               2*N*P*Q*K*(C/G)*R*S FLOPs per pass;
+  passes     = per-pass time (HIP events on the launch stream), TFLOP/s and
+               fraction of the dense fp16 MFMA peak, and algorithmic GB/s;
+  roofline   = the pass that takes the most time, against its bound;
+  cpu_baseline = the fp64 CPU oracle on a bounded sample of the same
+               workload (first images of the batch), same FLOP convention.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv2d TFLOP/s (fprop/dgrad/wgrad) and % of MFMA peak, 56x56x64 3x3 fp16"
+# MI355X published dense peaks: fp16/bf16 MFMA 2.5 PFLOP/s (= 256 CU x 4096
+# FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s), int8 5.03 POP/s, HBM3E 8 TB/s.
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3a_resnet3x3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-images", type=int, default=0,
+                    help="images of the batch the oracle runs on (0 = auto)")
+    return ap.parse_args()
+
+
+def flops(prob, P, Q):
+    return 2.0 * prob["N"] * P * Q * prob["K"] * (prob["C"] // prob["groups"]) * prob["R"] * prob["S"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the data-parallel sharding across GPUs is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from convolution_nhwc_implicit_amd import binding as B
+    from convolution_nhwc_implicit_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    name = args.workload
+    wl = WL.WORKLOADS[name]
+    prob, dt = wl["prob"], wl["dtype"]
+    if dt == "i8":
+        print("bench.py times the fp16/bf16 three-pass step; int8 is fprop only", file=sys.stderr)
+        sys.exit(2)
+    P, Q = B.conv2d_output_size(prob)
+    x = WL.make_x(name).to(dev)
+    w = WL.make_w(name).to(dev)
+    b = WL.make_bias(name).to(dev) if wl["bias"] else None
+    dy = WL.make_dy(name, P, Q).to(dev)
+    relu = wl["relu"]
+    y = torch.empty((prob["N"], P, Q, prob["K"]), dtype=x.dtype, device=dev)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    ws = {op: B.workspace_for(op, prob, dt, dev) for op in (0, 1, 2)}
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        B.conv2d_fprop(prob, dt, x, w, b, relu, 1.0, 1.0, 1.0, y, ws[0], stream=stream)
+        if ev:
+            ev[1].record(stream)
+        B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream)
+        if ev:
+            ev[2].record(stream)
+        B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    fl = flops(prob, P, Q)
+    esz = 2
+    elems_x = prob["N"] * prob["H"] * prob["W"] * prob["C"]
+    elems_y = prob["N"] * P * Q * prob["K"]
+    elems_w = prob["K"] * prob["R"] * prob["S"] * (prob["C"] // prob["groups"])
+    alg_bytes = {
+        "fprop": esz * (elems_x + elems_w + elems_y + (prob["K"] if b is not None else 0)),
+        "dgrad": esz * (elems_y + elems_w + elems_x),
+        "wgrad": esz * (elems_x + elems_y + elems_w),
+    }
+    plans = {n: B.conv2d_plan_info(op, prob, dt) for op, n in enumerate(("fprop", "dgrad", "wgrad"))}
+    passes = {}
+    for j, pname in enumerate(("fprop", "dgrad", "wgrad")):
+        times = np.array([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])
+        us = float(np.mean(times)) * 1e3
+        passes[pname] = {
+            "us_mean": round(us, 3),
+            "us_median": round(float(np.median(times)) * 1e3, 3),
+            "tflops": round(fl / (us * 1e-6) / 1e12, 2),
+            "frac_mfma_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_TFLOPS[dt], 4),
+            "alg_gbs": round(alg_bytes[pname] / (us * 1e-6) / 1e9, 1),
+            "kernels": {"fprop": 1, "dgrad": 2, "wgrad": 2 if plans[pname]["split_k"] > 1 else 1}[pname],
+            "plan": plans[pname],
+        }
+    dom = max(passes, key=lambda k: passes[k]["us_mean"])
+    d = passes[dom]
+    # Compute-bound when the pass's arithmetic intensity exceeds the ridge point.
+    ai = fl / alg_bytes[dom]
+    ridge = PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge * 0.5:
+        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                "frac": round(d["tflops"] / PEAK_TFLOPS[dt], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": d["alg_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(d["alg_gbs"] / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["per_launch"] = {"flop": fl, "alg_bytes": alg_bytes[dom], "avg_us": d["us_mean"]}
+
+    total_fl = 3 * fl
+    result = {
+        "metric": METRIC,
+        "value": round(total_fl / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded Gaussian, shapes of the workload)",
+        "config": {"workload": name, "N": prob["N"], "H": prob["H"], "W": prob["W"], "C": prob["C"],
+                   "K": prob["K"], "R": prob["R"], "S": prob["S"], "stride": prob["stride_h"],
+                   "pad": prob["pad_h"], "dilation": prob["dil_h"], "groups": prob["groups"],
+                   "passes": "fprop(+bias+relu) + dgrad + wgrad", "gflop_per_pass": round(fl / 1e9, 3)},
+        "passes": passes,
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(name, prob, P, Q, args.cpu_sample_images)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(name, prob, P, Q, n_img):
+    """The fp64 oracle (as it stands) on the first n_img images of the batch,
+    all three passes, timed on the host's cores."""
+    import numpy as np
+
+    import oracle
+    from convolution_nhwc_implicit_amd import workloads as WL
+
+    sub = dict(prob)
+    if n_img <= 0:
+        n_img = prob["N"]
+    n_img = min(n_img, prob["N"])
+    sub["N"] = n_img
+    x = WL.make_x(name)[:n_img].to(dtype=__import__("torch").float64).numpy()
+    w = WL.make_w(name).to(dtype=__import__("torch").float64).numpy()
+    dy = WL.make_dy(name, P, Q)[:n_img].to(dtype=__import__("torch").float64).numpy()
+    bias = WL.make_bias(name).to(dtype=__import__("torch").float64).numpy() if WL.WORKLOADS[name]["bias"] else None
+    t0 = time.perf_counter()
+    oracle.fprop(sub, x, w, bias=bias, relu=WL.WORKLOADS[name]["relu"])
+    oracle.dgrad(sub, dy, w)
+    oracle.wgrad(sub, x, dy)
+    secs = time.perf_counter() - t0
+    fl = 3 * flops(sub, P, Q)
+    return {"value": round(fl / secs / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"fprop+dgrad+wgrad on images 0..{n_img - 1} of {prob['N']} "
+                      f"({fl / 1e9:.2f} GFLOP, {secs:.1f} s)",
+            "seconds": round(secs, 2)}
+
+
+if __name__ == "__main__":
+    main()

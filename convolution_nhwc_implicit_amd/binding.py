@@ -1,0 +1,299 @@
+"""ctypes binding of libconv2d_nhwc.so (the C ABI in include/conv2d_nhwc.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the shared library.  PyTorch supplies device memory and the
+current stream.  The functions named conv2d_* mirror the C entry points one to
+one; fprop / dgrad / wgrad are conveniences that allocate the outputs and the
+workspace with torch and call them.
+
+Before anything reaches the library, the binding checks that every tensor is
+a contiguous tensor on the GPU, of the problem's element type and of exactly
+the shape the problem implies, so no kernel is ever handed a buffer smaller
+than its grid assumes.  If the library has not been built the calls raise;
+there is no other implementation to fall back to.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconv2d_nhwc.so")
+
+CONV2D_OK = 0
+CONV2D_ERR_INVALID_ARGUMENT = 1
+CONV2D_ERR_UNSUPPORTED = 2
+CONV2D_ERR_WORKSPACE_TOO_SMALL = 3
+CONV2D_ERR_DEVICE = 4
+
+CONV2D_DTYPE_F16 = 0
+CONV2D_DTYPE_BF16 = 1
+CONV2D_DTYPE_I8 = 2
+
+CONV2D_OP_FPROP = 0
+CONV2D_OP_DGRAD = 1
+CONV2D_OP_WGRAD = 2
+
+DTYPE_CODE = {torch.float16: CONV2D_DTYPE_F16, torch.bfloat16: CONV2D_DTYPE_BF16,
+              torch.int8: CONV2D_DTYPE_I8}
+CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
+NAME_CODE = {"f16": CONV2D_DTYPE_F16, "bf16": CONV2D_DTYPE_BF16, "i8": CONV2D_DTYPE_I8}
+
+_PROB_FIELDS = ("n", "c", "h", "w", "k", "r", "s", "pad_h", "pad_w",
+                "stride_h", "stride_w", "dil_h", "dil_w", "groups")
+_PROB_KEYS = ("N", "C", "H", "W", "K", "R", "S", "pad_h", "pad_w",
+              "stride_h", "stride_w", "dil_h", "dil_w", "groups")
+
+
+class Conv2dProblem(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in _PROB_FIELDS]
+
+
+class Conv2dAlgo(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int), ("split_k", ctypes.c_int)]
+
+
+class Conv2dPlanInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("tile", ctypes.c_int), ("num_tiles", ctypes.c_int),
+                ("split_k", ctypes.c_int), ("phases", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class Conv2dError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {conv2d_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load():
+    """Load libconv2d_nhwc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m convolution_nhwc_implicit_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.conv2d_output_size.argtypes = [P(Conv2dProblem), P(ctypes.c_int), P(ctypes.c_int)]
+    lib.conv2d_workspace_size.argtypes = [ctypes.c_int, P(Conv2dProblem), ctypes.c_int,
+                                          P(Conv2dAlgo), P(ctypes.c_size_t)]
+    lib.conv2d_plan_info.argtypes = [ctypes.c_int, P(Conv2dProblem), ctypes.c_int,
+                                     P(Conv2dAlgo), P(Conv2dPlanInfo)]
+    lib.conv2d_fprop.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, vp, ctypes.c_int,
+                                 ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                 vp, vp, ctypes.c_size_t, P(Conv2dAlgo), vp]
+    lib.conv2d_dgrad.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t,
+                                 P(Conv2dAlgo), vp]
+    lib.conv2d_wgrad.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t,
+                                 P(Conv2dAlgo), vp]
+    lib.conv2d_status_string.argtypes = [ctypes.c_int]
+    lib.conv2d_status_string.restype = ctypes.c_char_p
+    for name in ("conv2d_output_size", "conv2d_workspace_size", "conv2d_plan_info",
+                 "conv2d_fprop", "conv2d_dgrad", "conv2d_wgrad"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_problem(prob):
+    """A ctypes problem from a mapping with keys N, C, H, W, K, R, S, pad_h, ..."""
+    if isinstance(prob, Conv2dProblem):
+        return prob
+    return Conv2dProblem(*[int(prob[k]) for k in _PROB_KEYS])
+
+
+def _algo(algo):
+    if algo is None:
+        return None
+    if isinstance(algo, Conv2dAlgo):
+        return ctypes.byref(algo)
+    return ctypes.byref(Conv2dAlgo(int(algo.get("tile", 0)), int(algo.get("split_k", 0))))
+
+
+def _dtype_code(dtype):
+    if isinstance(dtype, int):
+        return dtype
+    if isinstance(dtype, str):
+        return NAME_CODE[dtype]
+    return DTYPE_CODE[dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _raise(status, where):
+    if status != CONV2D_OK:
+        raise Conv2dError(status, where)
+
+
+# ------------------------------------------------------------ C entry points
+
+def conv2d_status_string(status):
+    return load().conv2d_status_string(int(status)).decode()
+
+
+def conv2d_output_size(prob):
+    """(P, Q) of the problem."""
+    P, Q = ctypes.c_int(), ctypes.c_int()
+    _raise(load().conv2d_output_size(ctypes.byref(make_problem(prob)), ctypes.byref(P),
+                                     ctypes.byref(Q)), "conv2d_output_size")
+    return P.value, Q.value
+
+
+def conv2d_workspace_size(op, prob, dtype, algo=None):
+    b = ctypes.c_size_t()
+    _raise(load().conv2d_workspace_size(int(op), ctypes.byref(make_problem(prob)), _dtype_code(dtype),
+                                        _algo(algo), ctypes.byref(b)), "conv2d_workspace_size")
+    return b.value
+
+
+def conv2d_plan_info(op, prob, dtype, algo=None):
+    info = Conv2dPlanInfo()
+    _raise(load().conv2d_plan_info(int(op), ctypes.byref(make_problem(prob)), _dtype_code(dtype),
+                                   _algo(algo), ctypes.byref(info)), "conv2d_plan_info")
+    return {f: getattr(info, f) for f, _ in Conv2dPlanInfo._fields_}
+
+
+def _check_tensor(t, name, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws, need):
+    if need == 0:
+        return None, 0
+    if ws is None:
+        raise ValueError(f"a workspace of {need} bytes is required")
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = ws.numel() * ws.element_size()
+    return ctypes.c_void_p(ws.data_ptr()), nbytes
+
+
+def _shapes(prob):
+    P, Q = conv2d_output_size(prob)
+    p = prob
+    x_shape = (p["N"], p["H"], p["W"], p["C"])
+    w_shape = (p["K"], p["R"], p["S"], p["C"] // p["groups"])
+    y_shape = (p["N"], P, Q, p["K"])
+    return x_shape, w_shape, y_shape
+
+
+def conv2d_fprop(prob, dtype, x, w, bias, relu, act_scale, w_scale, out_scale, y, workspace,
+                 algo=None, stream=None):
+    code = _dtype_code(dtype)
+    tdt = CODE_DTYPE[code]
+    xs, ws_, ys = _shapes(prob)
+    _check_tensor(x, "x", tdt, xs)
+    _check_tensor(w, "w", tdt, ws_)
+    _check_tensor(y, "y", tdt, ys)
+    if bias is not None:
+        _check_tensor(bias, "bias", torch.int32 if code == CONV2D_DTYPE_I8 else tdt, (prob["K"],))
+    need = conv2d_workspace_size(CONV2D_OP_FPROP, prob, code, algo)
+    wsp, wsb = _check_workspace(workspace, need)
+    st = load().conv2d_fprop(ctypes.byref(make_problem(prob)), code, x.data_ptr(), w.data_ptr(),
+                             None if bias is None else bias.data_ptr(), int(bool(relu)),
+                             float(act_scale), float(w_scale), float(out_scale), y.data_ptr(),
+                             wsp, wsb, _algo(algo), _stream(stream))
+    _raise(st, "conv2d_fprop")
+
+
+def conv2d_dgrad(prob, dtype, dy, w, dx, workspace, algo=None, stream=None):
+    code = _dtype_code(dtype)
+    tdt = CODE_DTYPE[code]
+    xs, ws_, ys = _shapes(prob)
+    _check_tensor(dy, "dy", tdt, ys)
+    _check_tensor(w, "w", tdt, ws_)
+    _check_tensor(dx, "dx", tdt, xs)
+    need = conv2d_workspace_size(CONV2D_OP_DGRAD, prob, code, algo)
+    wsp, wsb = _check_workspace(workspace, need)
+    st = load().conv2d_dgrad(ctypes.byref(make_problem(prob)), code, dy.data_ptr(), w.data_ptr(),
+                             dx.data_ptr(), wsp, wsb, _algo(algo), _stream(stream))
+    _raise(st, "conv2d_dgrad")
+
+
+def conv2d_wgrad(prob, dtype, x, dy, dw, workspace, algo=None, stream=None):
+    code = _dtype_code(dtype)
+    tdt = CODE_DTYPE[code]
+    xs, ws_, ys = _shapes(prob)
+    _check_tensor(x, "x", tdt, xs)
+    _check_tensor(dy, "dy", tdt, ys)
+    _check_tensor(dw, "dw", tdt, ws_)
+    need = conv2d_workspace_size(CONV2D_OP_WGRAD, prob, code, algo)
+    wsp, wsb = _check_workspace(workspace, need)
+    st = load().conv2d_wgrad(ctypes.byref(make_problem(prob)), code, x.data_ptr(), dy.data_ptr(),
+                             dw.data_ptr(), wsp, wsb, _algo(algo), _stream(stream))
+    _raise(st, "conv2d_wgrad")
+
+
+# --------------------------------------------------------------- conveniences
+
+def _pair(v):
+    return (v, v) if isinstance(v, int) else (int(v[0]), int(v[1]))
+
+
+def problem_from(x_shape, w_shape, stride=1, padding=0, dilation=1, groups=1):
+    N, H, W, C = x_shape
+    K, R, S, _ = w_shape
+    sh, sw = _pair(stride)
+    ph, pw = _pair(padding)
+    dh, dw = _pair(dilation)
+    return dict(N=N, C=C, H=H, W=W, K=K, R=R, S=S, pad_h=ph, pad_w=pw, stride_h=sh, stride_w=sw,
+                dil_h=dh, dil_w=dw, groups=groups)
+
+
+def workspace_for(op, prob, dtype, device, algo=None):
+    n = conv2d_workspace_size(op, prob, dtype, algo)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def fprop(x, w, bias=None, relu=False, stride=1, padding=0, dilation=1, groups=1, scales=None,
+          algo=None):
+    """y[N,P,Q,K] = conv2d(x[N,H,W,C], w[K,R,S,C/G]) (+bias) (ReLU) (int8 requant)."""
+    prob = problem_from(x.shape, w.shape, stride, padding, dilation, groups)
+    P, Q = conv2d_output_size(prob)
+    y = torch.empty((prob["N"], P, Q, prob["K"]), dtype=x.dtype, device=x.device)
+    act, ws_, out = scales if scales is not None else (1.0, 1.0, 1.0)
+    wsb = workspace_for(CONV2D_OP_FPROP, prob, x.dtype, x.device, algo)
+    conv2d_fprop(prob, x.dtype, x, w, bias, relu, act, ws_, out, y, wsb, algo)
+    return y
+
+
+def dgrad(dy, w, input_hw, stride=1, padding=0, dilation=1, groups=1, algo=None):
+    """dx[N,H,W,C] for output gradient dy[N,P,Q,K]; input_hw = (H, W)."""
+    N, _, _, K = dy.shape
+    C = w.shape[3] * groups
+    prob = problem_from((N, input_hw[0], input_hw[1], C), w.shape, stride, padding, dilation, groups)
+    dx = torch.empty((N, input_hw[0], input_hw[1], C), dtype=dy.dtype, device=dy.device)
+    wsb = workspace_for(CONV2D_OP_DGRAD, prob, dy.dtype, dy.device, algo)
+    conv2d_dgrad(prob, dy.dtype, dy, w, dx, wsb, algo)
+    return dx
+
+
+def wgrad(x, dy, filter_rs, stride=1, padding=0, dilation=1, groups=1, algo=None):
+    """dw[K,R,S,C/G] for input x[N,H,W,C] and output gradient dy[N,P,Q,K]."""
+    N, H, W, C = x.shape
+    K = dy.shape[3]
+    R, S = filter_rs
+    prob = problem_from(x.shape, (K, R, S, C // groups), stride, padding, dilation, groups)
+    dw = torch.empty((K, R, S, C // groups), dtype=x.dtype, device=x.device)
+    wsb = workspace_for(CONV2D_OP_WGRAD, prob, x.dtype, x.device, algo)
+    conv2d_wgrad(prob, x.dtype, x, dy, dw, wsb, algo)
+    return dw

@@ -1,0 +1,464 @@
+// api.cpp -- the C ABI of the conv2d library: argument validation, planning
+// (kernel, tile, split-K, dgrad stride phases, workspace layout) and launches
+// on the caller's stream.
+//
+// Dispatch rule (after the burn CubeCL conv dispatch, conv_forward_nhwc /
+// conv_weight_backward / conv_data_backward): groups > 1 runs the direct
+// kernels; groups == 1 runs the implicit GEMM for all three passes, including
+// strided dgrad (which that dispatch sends to a fallback).  Every check runs
+// before anything is enqueued, and an unsupported case is reported, never run
+// on another algorithm.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "conv2d_nhwc.h"
+#include "internal.h"
+
+using namespace cnv;
+
+namespace {
+
+constexpr long long kMaxElems = (1LL << 31) - 1;
+constexpr int kNumCUs = 256;  // MI355X
+
+struct Dims {
+    long long N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw, G, P, Q, Cg, Kg;
+};
+
+int validate(const conv2d_problem_t *p, Dims *d)
+{
+    if (!p) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (p->n < 1 || p->c < 1 || p->h < 1 || p->w < 1 || p->k < 1 || p->r < 1 || p->s < 1)
+        return CONV2D_ERR_INVALID_ARGUMENT;
+    if (p->pad_h < 0 || p->pad_w < 0 || p->stride_h < 1 || p->stride_w < 1 || p->dil_h < 1 ||
+        p->dil_w < 1 || p->groups < 1)
+        return CONV2D_ERR_INVALID_ARGUMENT;
+    if (p->c % p->groups || p->k % p->groups) return CONV2D_ERR_INVALID_ARGUMENT;
+    const long long span_h = (long long)p->dil_h * (p->r - 1) + 1;
+    const long long span_w = (long long)p->dil_w * (p->s - 1) + 1;
+    const long long ph = (long long)p->h + 2LL * p->pad_h, pw = (long long)p->w + 2LL * p->pad_w;
+    if (ph < span_h || pw < span_w) return CONV2D_ERR_INVALID_ARGUMENT;
+    d->N = p->n; d->C = p->c; d->H = p->h; d->W = p->w; d->K = p->k; d->R = p->r; d->S = p->s;
+    d->ph = p->pad_h; d->pw = p->pad_w; d->sh = p->stride_h; d->sw = p->stride_w;
+    d->dh = p->dil_h; d->dw = p->dil_w; d->G = p->groups;
+    d->P = (ph - span_h) / p->stride_h + 1;
+    d->Q = (pw - span_w) / p->stride_w + 1;
+    d->Cg = d->C / d->G;
+    d->Kg = d->K / d->G;
+    return CONV2D_OK;
+}
+
+// Sizes the kernels index with 32-bit arithmetic.
+bool fits_32bit(const Dims &d)
+{
+    return d.N * d.H * d.W * d.C <= kMaxElems && d.N * d.P * d.Q * d.K <= kMaxElems &&
+           d.K * d.R * d.S * d.Cg <= kMaxElems && d.N * d.P * d.Q <= kMaxElems &&
+           d.N * d.H * d.W <= kMaxElems && d.sh * (d.P + 1) + d.dh * d.R + d.H < (1LL << 28) &&
+           d.sw * (d.Q + 1) + d.dw * d.S + d.W < (1LL << 28);
+}
+
+int elem_size(int dtype) { return dtype == CONV2D_DTYPE_I8 ? 1 : 2; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- dgrad stride phases ---------------------------------------------------
+// Input row h is reached by tap r from output row p = (h + pad - r*dil)/stride
+// when that division is exact.  For rows h = ph + stride*i of one phase the
+// valid taps form an arithmetic progression r0, r0 + step, ... with
+// step = stride / gcd(stride, dil), and the source row is i + o with
+// o = (ph + pad - r*dil) / stride, which falls by lcm(stride, dil)/stride per tap.
+struct AxisPhase {
+    int extent;  // rows of the input in this phase
+    int r0, step, ntap;
+    int o0, dstep;
+};
+
+AxisPhase axis_phase(int ph, int extent_full, int stride, int pad, int dil, int R)
+{
+    AxisPhase a;
+    a.extent = ph < extent_full ? (extent_full - 1 - ph) / stride + 1 : 0;
+    int g = stride, t = dil;
+    while (t) {
+        int u = g % t;
+        g = t;
+        t = u;
+    }
+    a.step = stride / g;
+    a.r0 = -1;
+    for (int r = 0; r < R && r < stride; ++r)
+        if (((ph + pad - r * dil) % stride + stride) % stride == 0) {
+            a.r0 = r;
+            break;
+        }
+    if (a.r0 < 0) {
+        a.ntap = 0;
+        a.r0 = 0;
+        a.o0 = 0;
+        a.dstep = 0;
+        return a;
+    }
+    a.ntap = (R - 1 - a.r0) / a.step + 1;
+    a.o0 = (ph + pad - a.r0 * dil) / stride;  // exact
+    a.dstep = -(a.step * dil) / stride;       // exact
+    return a;
+}
+
+struct Plan {
+    int op, dtype;
+    int kernel;  // 1 implicit GEMM, 2 direct
+    int tile, num_tiles, split_k, phases;
+    size_t ws_bytes;
+    Dims d;
+};
+
+int choose_igemm_tile(long long m_total, long long ngemm)
+{
+    // Prefer the widest N tile the problem fills; shrink M until the grid has
+    // enough workgroups for 256 CUs.
+    if (ngemm <= 32) return 4;  // 64 x 32
+    auto tiles = [&](int t) {
+        TileShape s = igemm_tile_shape(t);
+        return ((m_total + s.bm - 1) / s.bm) * ((ngemm + s.bn - 1) / s.bn);
+    };
+    if (ngemm >= 128 && ngemm % 128 == 0 && tiles(1) >= 2 * kNumCUs) return 1;  // 128 x 128
+    if (tiles(0) >= 2 * kNumCUs) return 0;                                        // 128 x 64
+    return 2;                                                                      // 64 x 64
+}
+
+int choose_wgrad_splits(long long tiles, long long npix)
+{
+    const long long steps = (npix + kWgradPixStep - 1) / kWgradPixStep;
+    long long s = (3 * kNumCUs) / std::max(1LL, tiles);
+    s = std::min(s, std::max(1LL, steps / 8));
+    return (int)std::max(1LL, std::min(s, 4096LL));
+}
+
+int choose_direct_splits(long long outputs, long long npix)
+{
+    long long s = (256LL * 1024) / std::max(1LL, outputs);
+    s = std::min(s, std::max(1LL, npix / 64));
+    return (int)std::max(1LL, std::min(s, 4096LL));
+}
+
+int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, Plan *pl)
+{
+    int st = validate(prob, &pl->d);
+    if (st) return st;
+    const Dims &d = pl->d;
+    if (op != CONV2D_OP_FPROP && op != CONV2D_OP_DGRAD && op != CONV2D_OP_WGRAD)
+        return CONV2D_ERR_INVALID_ARGUMENT;
+    if (dtype != CONV2D_DTYPE_F16 && dtype != CONV2D_DTYPE_BF16 && dtype != CONV2D_DTYPE_I8)
+        return CONV2D_ERR_UNSUPPORTED;
+    if (dtype == CONV2D_DTYPE_I8 && op != CONV2D_OP_FPROP) return CONV2D_ERR_UNSUPPORTED;
+    if (!fits_32bit(d)) return CONV2D_ERR_UNSUPPORTED;
+    if (algo && (algo->tile < 0 || algo->split_k < 0)) return CONV2D_ERR_INVALID_ARGUMENT;
+    pl->op = op;
+    pl->dtype = dtype;
+    pl->split_k = 1;
+    pl->phases = 1;
+    pl->ws_bytes = 0;
+    pl->tile = 0;
+
+    if (d.G > 1) {
+        pl->kernel = 2;
+        pl->num_tiles = 1;
+        if (algo && algo->tile > 1) return CONV2D_ERR_UNSUPPORTED;
+        if (op == CONV2D_OP_WGRAD) {
+            const long long outputs = d.K * d.R * d.S * d.Cg;
+            const long long npix = d.N * d.P * d.Q;
+            int s = (algo && algo->split_k) ? algo->split_k : choose_direct_splits(outputs, npix);
+            if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
+            pl->split_k = s;
+            if (s > 1) pl->ws_bytes = round_up((size_t)s * splitk_stride(outputs) * sizeof(float), 256);
+        }
+        return CONV2D_OK;
+    }
+
+    // implicit GEMM: 128-bit chunks of channels along GEMM-K and GEMM-N
+    const int vec = dtype == CONV2D_DTYPE_I8 ? 16 : 8;
+    if (d.C % vec || d.K % vec) return CONV2D_ERR_UNSUPPORTED;
+    pl->kernel = 1;
+    if (op == CONV2D_OP_WGRAD) {
+        pl->num_tiles = wgrad_num_tiles();
+        if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
+        pl->tile = (algo && algo->tile) ? algo->tile - 1 : 0;
+        TileShape ts = wgrad_tile_shape(pl->tile);
+        const long long ncols = d.R * d.S * d.C;
+        const long long tiles = ((d.K + ts.bm - 1) / ts.bm) * ((ncols + ts.bn - 1) / ts.bn);
+        const long long npix = d.N * d.P * d.Q;
+        int s = (algo && algo->split_k) ? algo->split_k : choose_wgrad_splits(tiles, npix);
+        if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
+        pl->split_k = s;
+        if (s > 1) pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * ncols) * sizeof(float), 256);
+        return CONV2D_OK;
+    }
+    pl->num_tiles = igemm_num_tiles();
+    if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
+    if (op == CONV2D_OP_FPROP) {
+        pl->tile = (algo && algo->tile) ? algo->tile - 1 : choose_igemm_tile(d.N * d.P * d.Q, d.K);
+        return CONV2D_OK;
+    }
+    // dgrad
+    if (d.sh * d.sw > kMaxPhases) return CONV2D_ERR_UNSUPPORTED;
+    pl->phases = (int)(d.sh * d.sw);
+    pl->tile = (algo && algo->tile) ? algo->tile - 1 : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.C);
+    pl->ws_bytes = round_up((size_t)d.R * d.S * d.C * d.K * elem_size(dtype), 256);
+    return CONV2D_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_DEVICE; }
+
+void fill_phase_common(Phase &ph, int tile)
+{
+    TileShape ts = igemm_tile_shape(tile);
+    ph.tiles_m = (int)(((long long)ph.m_total + ts.bm - 1) / ts.bm);
+    ph.div_mj = make_fastdiv((uint32_t)std::max(1, ph.mj));
+    ph.div_mimj = make_fastdiv((uint32_t)std::max(1LL, (long long)ph.mi * ph.mj));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *conv2d_status_string(int status)
+{
+    switch (status) {
+    case CONV2D_OK: return "ok";
+    case CONV2D_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CONV2D_ERR_UNSUPPORTED: return "unsupported problem, dtype or alignment";
+    case CONV2D_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case CONV2D_ERR_DEVICE: return "device (HIP) error";
+    default: return "unknown status";
+    }
+}
+
+int conv2d_output_size(const conv2d_problem_t *prob, int *P, int *Q)
+{
+    Dims d;
+    int st = validate(prob, &d);
+    if (st) return st;
+    if (P) *P = (int)d.P;
+    if (Q) *Q = (int)d.Q;
+    return CONV2D_OK;
+}
+
+int conv2d_workspace_size(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo,
+                          size_t *bytes)
+{
+    if (!bytes) return CONV2D_ERR_INVALID_ARGUMENT;
+    Plan pl;
+    int st = make_plan(op, prob, dtype, algo, &pl);
+    if (st) return st;
+    *bytes = pl.ws_bytes;
+    return CONV2D_OK;
+}
+
+int conv2d_plan_info(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo,
+                     conv2d_plan_info_t *info)
+{
+    if (!info) return CONV2D_ERR_INVALID_ARGUMENT;
+    Plan pl;
+    int st = make_plan(op, prob, dtype, algo, &pl);
+    if (st) return st;
+    info->kernel = pl.kernel;
+    info->tile = pl.tile;
+    info->num_tiles = pl.num_tiles;
+    info->split_k = pl.split_k;
+    info->phases = pl.phases;
+    info->workspace_bytes = pl.ws_bytes;
+    return CONV2D_OK;
+}
+
+int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const void *w, const void *bias,
+                 int relu, double act_scale, double w_scale, double out_scale, void *y, void *workspace,
+                 size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+{
+    Plan pl;
+    int st = make_plan(CONV2D_OP_FPROP, prob, dtype, algo, &pl);
+    if (st) return st;
+    if (!x || !w || !y) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (relu != 0 && relu != 1) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return CONV2D_ERR_UNSUPPORTED;
+    const size_t bias_align = dtype == CONV2D_DTYPE_I8 ? 4 : 2;
+    if (bias && ((uintptr_t)bias % bias_align)) return CONV2D_ERR_UNSUPPORTED;
+    double m = 0.0;
+    if (dtype == CONV2D_DTYPE_I8) {
+        const double sc[3] = {act_scale, w_scale, out_scale};
+        for (double s : sc)
+            if (!(s > 0.0) || !(s < 1e300)) return CONV2D_ERR_INVALID_ARGUMENT;
+        m = act_scale * w_scale / out_scale;  // double, left to right
+    }
+    if (workspace_bytes < pl.ws_bytes) return CONV2D_ERR_WORKSPACE_TOO_SMALL;
+    const Dims &d = pl.d;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (pl.kernel == 2) {
+        DirectArgs a{};
+        a.a = x; a.b = w; a.bias = bias; a.out = y;
+        a.N = (int)d.N; a.H = (int)d.H; a.W = (int)d.W; a.C = (int)d.C; a.K = (int)d.K;
+        a.R = (int)d.R; a.S = (int)d.S; a.P = (int)d.P; a.Q = (int)d.Q;
+        a.pad_h = (int)d.ph; a.pad_w = (int)d.pw; a.sh = (int)d.sh; a.sw = (int)d.sw;
+        a.dh = (int)d.dh; a.dw = (int)d.dw; a.G = (int)d.G; a.Cg = (int)d.Cg; a.Kg = (int)d.Kg;
+        a.relu = relu; a.requant_m = m; a.splits = 1;
+        a.total = d.N * d.P * d.Q * d.K;
+        return hip_status(launch_direct_fprop(dtype, a, s));
+    }
+
+    IgemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.src = x; a.bmat = w; a.bias = bias; a.dst = y;
+    a.nimg = (int)d.N; a.hs = (int)d.H; a.ws = (int)d.W; a.cs = (int)d.C;
+    a.ngemm = (int)d.K;
+    a.ho = (int)d.P; a.wo = (int)d.Q; a.osh = 1; a.osw = 1;
+    a.gsh = (int)d.sh; a.gsw = (int)d.sw;
+    a.relu = relu; a.requant_m = m;
+    a.nphases = 1;
+    Phase &ph = a.ph[0];
+    ph.mi = (int)d.P; ph.mj = (int)d.Q; ph.oh0 = 0; ph.ow0 = 0;
+    ph.th0 = -(int)d.ph; ph.tw0 = -(int)d.pw; ph.tdh = (int)d.dh; ph.tdw = (int)d.dw;
+    ph.ntr = (int)d.R; ph.nts = (int)d.S;
+    ph.kgemm = (int)(d.R * d.S * d.C);
+    ph.m_total = (uint32_t)(d.N * d.P * d.Q);
+    ph.b_off = 0;
+    fill_phase_common(ph, pl.tile);
+    TileShape ts = igemm_tile_shape(pl.tile);
+    const int gn = (int)((d.K + ts.bn - 1) / ts.bn);
+    return hip_status(launch_igemm(dtype, pl.tile, a, ph.tiles_m, gn, s));
+}
+
+int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const void *w, void *dx,
+                 void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+{
+    Plan pl;
+    int st = make_plan(CONV2D_OP_DGRAD, prob, dtype, algo, &pl);
+    if (st) return st;
+    if (!dy || !w || !dx) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (!aligned16(dy) || !aligned16(w) || !aligned16(dx)) return CONV2D_ERR_UNSUPPORTED;
+    if (workspace_bytes < pl.ws_bytes) return CONV2D_ERR_WORKSPACE_TOO_SMALL;
+    if (pl.ws_bytes && (!workspace || !aligned16(workspace))) return CONV2D_ERR_INVALID_ARGUMENT;
+    const Dims &d = pl.d;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (pl.kernel == 2) {
+        DirectArgs a{};
+        a.a = dy; a.b = w; a.out = dx;
+        a.N = (int)d.N; a.H = (int)d.H; a.W = (int)d.W; a.C = (int)d.C; a.K = (int)d.K;
+        a.R = (int)d.R; a.S = (int)d.S; a.P = (int)d.P; a.Q = (int)d.Q;
+        a.pad_h = (int)d.ph; a.pad_w = (int)d.pw; a.sh = (int)d.sh; a.sw = (int)d.sw;
+        a.dh = (int)d.dh; a.dw = (int)d.dw; a.G = (int)d.G; a.Cg = (int)d.Cg; a.Kg = (int)d.Kg;
+        a.splits = 1;
+        a.total = d.N * d.H * d.W * d.C;
+        return hip_status(launch_direct_dgrad(dtype, a, s));
+    }
+
+    // One GEMM per stride phase (h mod sh, w mod sw), one launch for all.
+    PrepArgs pa;
+    memset(&pa, 0, sizeof(pa));
+    pa.w = w; pa.wt = workspace;
+    pa.K = (int)d.K; pa.R = (int)d.R; pa.S = (int)d.S; pa.C = (int)d.C;
+    IgemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.src = dy; a.bmat = workspace; a.bias = nullptr; a.dst = dx;
+    a.nimg = (int)d.N; a.hs = (int)d.P; a.ws = (int)d.Q; a.cs = (int)d.K;
+    a.ngemm = (int)d.C;
+    a.ho = (int)d.H; a.wo = (int)d.W; a.osh = (int)d.sh; a.osw = (int)d.sw;
+    a.gsh = 1; a.gsw = 1;
+    a.relu = 0;
+    long long off = 0;
+    int nph = 0, max_tiles = 0;
+    for (int py = 0; py < d.sh; ++py)
+        for (int px = 0; px < d.sw; ++px) {
+            AxisPhase ay = axis_phase(py, (int)d.H, (int)d.sh, (int)d.ph, (int)d.dh, (int)d.R);
+            AxisPhase ax = axis_phase(px, (int)d.W, (int)d.sw, (int)d.pw, (int)d.dw, (int)d.S);
+            if (ay.extent == 0 || ax.extent == 0) continue;
+            Phase &ph = a.ph[nph];
+            ph.mi = ay.extent; ph.mj = ax.extent; ph.oh0 = py; ph.ow0 = px;
+            ph.th0 = ay.o0; ph.tw0 = ax.o0; ph.tdh = ay.dstep; ph.tdw = ax.dstep;
+            ph.ntr = ay.ntap; ph.nts = ax.ntap;
+            ph.kgemm = (int)(ay.ntap * ax.ntap * d.K);
+            ph.m_total = (uint32_t)(d.N * ay.extent * ax.extent);
+            ph.b_off = off;
+            fill_phase_common(ph, pl.tile);
+            max_tiles = std::max(max_tiles, ph.tiles_m);
+            PrepPhase &pp = pa.ph[nph];
+            pp.r0 = ay.r0; pp.rstep = ay.step; pp.ntr = ay.ntap;
+            pp.s0 = ax.r0; pp.sstep = ax.step; pp.nts = ax.ntap;
+            pp.off = off;
+            const long long elems = d.C * ay.ntap * ax.ntap * d.K;
+            pa.max_elems = (int)std::max<long long>(pa.max_elems, elems);
+            off += elems;
+            ++nph;
+        }
+    a.nphases = nph;
+    pa.nphases = nph;
+    if (nph == 0) return CONV2D_OK;
+    hipError_t e = launch_dgrad_prep(dtype, pa, s);
+    if (e != hipSuccess) return CONV2D_ERR_DEVICE;
+    TileShape ts = igemm_tile_shape(pl.tile);
+    const int gn = (int)((d.C + ts.bn - 1) / ts.bn);
+    return hip_status(launch_igemm(dtype, pl.tile, a, max_tiles, gn, s));
+}
+
+int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const void *dy, void *dw,
+                 void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+{
+    Plan pl;
+    int st = make_plan(CONV2D_OP_WGRAD, prob, dtype, algo, &pl);
+    if (st) return st;
+    if (!x || !dy || !dw) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dw)) return CONV2D_ERR_UNSUPPORTED;
+    if (workspace_bytes < pl.ws_bytes) return CONV2D_ERR_WORKSPACE_TOO_SMALL;
+    if (pl.ws_bytes && (!workspace || !aligned16(workspace))) return CONV2D_ERR_INVALID_ARGUMENT;
+    const Dims &d = pl.d;
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t npix = (uint32_t)(d.N * d.P * d.Q);
+    void *out = pl.split_k > 1 ? workspace : dw;
+
+    if (pl.kernel == 2) {
+        DirectArgs a{};
+        a.a = x; a.b = dy; a.out = out;
+        a.N = (int)d.N; a.H = (int)d.H; a.W = (int)d.W; a.C = (int)d.C; a.K = (int)d.K;
+        a.R = (int)d.R; a.S = (int)d.S; a.P = (int)d.P; a.Q = (int)d.Q;
+        a.pad_h = (int)d.ph; a.pad_w = (int)d.pw; a.sh = (int)d.sh; a.sw = (int)d.sw;
+        a.dh = (int)d.dh; a.dw = (int)d.dw; a.G = (int)d.G; a.Cg = (int)d.Cg; a.Kg = (int)d.Kg;
+        a.splits = pl.split_k;
+        a.npix = npix;
+        a.pix_per_split = (npix + pl.split_k - 1) / pl.split_k;
+        a.total = d.K * d.R * d.S * d.Cg;
+        a.part_stride = splitk_stride(a.total);
+        hipError_t e = launch_direct_wgrad(dtype, a, s);
+        if (e != hipSuccess || pl.split_k == 1) return hip_status(e);
+        return hip_status(
+            launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k, a.total, a.part_stride, dw, s));
+    }
+
+    WgradArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = x; a.dy = dy; a.out = out;
+    a.N = (int)d.N; a.H = (int)d.H; a.W = (int)d.W; a.C = (int)d.C; a.K = (int)d.K;
+    a.R = (int)d.R; a.S = (int)d.S; a.P = (int)d.P; a.Q = (int)d.Q;
+    a.pad_h = (int)d.ph; a.pad_w = (int)d.pw; a.sh = (int)d.sh; a.sw = (int)d.sw;
+    a.dh = (int)d.dh; a.dw = (int)d.dw;
+    a.ncols = (int)(d.R * d.S * d.C);
+    a.npix = npix;
+    // slices are whole main-loop steps
+    const uint32_t steps = (npix + kWgradPixStep - 1) / kWgradPixStep;
+    a.pix_per_split = ((steps + pl.split_k - 1) / pl.split_k) * kWgradPixStep;
+    a.splits = pl.split_k;
+    a.part_stride = splitk_stride((long long)d.K * a.ncols);
+    a.div_Q = make_fastdiv((uint32_t)d.Q);
+    a.div_PQ = make_fastdiv((uint32_t)(d.P * d.Q));
+    a.div_C = make_fastdiv((uint32_t)d.C);
+    a.div_S = make_fastdiv((uint32_t)d.S);
+    hipError_t e = launch_wgrad(dtype, pl.tile, a, s);
+    if (e != hipSuccess || pl.split_k == 1) return hip_status(e);
+    return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,
+                                           (long long)d.K * a.ncols, a.part_stride, dw, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// device_common.h -- element-type traits, MFMA wrappers and conversions for
+// the gfx950 (CDNA4) kernels.  Device-side only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace cnv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- conversions (round to nearest even; the hardware default mode) -------
+__device__ inline float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ inline float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+__device__ inline uint16_t f32_to_f16(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+__device__ inline uint16_t f32_to_bf16(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+// ---- element traits --------------------------------------------------------
+// EPC: elements per 16-byte chunk.  One MFMA consumes 64 bytes of each
+// operand row: 16x16x32 for 16-bit types, 16x16x64 for int8.
+struct EF16 {
+    using elem = uint16_t;
+    using acc = f32x4;
+    static constexpr int EPC = 8;
+    static constexpr int kDtype = CONV2D_DTYPE_F16;
+    __device__ static inline acc mfma(u32x4 a, u32x4 b, acc c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ static inline float to_f32(elem e) { return f16_to_f32(e); }
+    __device__ static inline elem from_f32(float v) { return f32_to_f16(v); }
+};
+
+struct EBF16 {
+    using elem = uint16_t;
+    using acc = f32x4;
+    static constexpr int EPC = 8;
+    static constexpr int kDtype = CONV2D_DTYPE_BF16;
+    __device__ static inline acc mfma(u32x4 a, u32x4 b, acc c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static inline float to_f32(elem e) { return bf16_to_f32(e); }
+    __device__ static inline elem from_f32(float v) { return f32_to_bf16(v); }
+};
+
+struct EI8 {
+    using elem = int8_t;
+    using acc = i32x4;
+    static constexpr int EPC = 16;
+    static constexpr int kDtype = CONV2D_DTYPE_I8;
+    __device__ static inline acc mfma(u32x4 a, u32x4 b, acc c)
+    {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                                      __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    }
+};
+
+// int8 requantisation of one accumulator: + bias, ReLU, * m in fp64,
+// round half to even (v_rndne_f64), saturate.
+__device__ inline int8_t requant_i8(int v, double m)
+{
+    double t = rint((double)v * m);
+    t = t > 127.0 ? 127.0 : t;
+    t = t < -128.0 ? -128.0 : t;
+    return (int8_t)(int)t;
+}
+
+// Float epilogue value: acc + bias, then ReLU (v <= 0, including -0, -> +0).
+__device__ inline float bias_relu_f32(float v, float b, int relu)
+{
+    v += b;
+    return (relu && !(v > 0.0f)) ? 0.0f : v;
+}
+
+}  // namespace cnv

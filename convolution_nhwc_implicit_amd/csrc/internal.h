@@ -1,0 +1,168 @@
+// internal.h -- types shared by the host planner (api.cpp) and the HIP kernel
+// launchers of the conv2d library.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "conv2d_nhwc.h"
+
+namespace cnv {
+
+// Unsigned division by an invariant divisor d (1 <= d < 2^31) for dividends
+// n < 2^31: q = (umulhi(n, m) + n) >> s with s = ceil(log2 d) and
+// m = floor(2^32 * (2^s - d) / d) + 1 (Granlund & Montgomery, "Division by
+// invariant integers using multiplication", 1994).  Replaces the slow integer
+// divide in per-element index decomposition.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.d = d;
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.s = s;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+    return f;
+}
+
+__host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv &f)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t t = __umulhi(n, f.m);
+#else
+    uint32_t t = (uint32_t)(((uint64_t)n * f.m) >> 32);
+#endif
+    return (t + n) >> f.s;
+}
+
+// ---------------------------------------------------------------------------
+// Implicit GEMM (fprop, and dgrad per stride phase).
+//
+// The GEMM is D[m][n] = sum_kk A[m][kk] * B[n][kk] with
+//   m  = output pixel of an output sub-grid (image, i, j),
+//   n  = output channel,
+//   kk = (tap tr, tap ts, source channel c), c innermost,
+//   A[m][kk] = src[image][i*gsh + th0 + tr*tdh][j*gsw + tw0 + ts*tdw][c]
+//              (zero outside the source image: implicit padding),
+//   B        = a dense row-major [ngemm][kgemm] matrix.
+// fprop: src = x, B = w ([K][R*S*C]), one phase covering all of y.
+// dgrad: src = dy, B = the filter re-laid out per stride phase; each phase is
+//   the sub-grid of dx rows h = oh0 + i*osh (and columns likewise) that the
+//   same set of taps reaches.
+// ---------------------------------------------------------------------------
+constexpr int kMaxPhases = 16;
+
+struct Phase {
+    int mi, mj;       // sub-grid extent
+    int oh0, ow0;     // first output row / column of the sub-grid
+    int th0, tw0;     // source row / column of tap (0,0) at sub-grid origin
+    int tdh, tdw;     // source offset per tap index
+    int ntr, nts;     // taps per axis
+    int kgemm;        // ntr * nts * cs
+    int tiles_m;      // ceil(m_total / BM)
+    uint32_t m_total; // nimg * mi * mj
+    long long b_off;  // element offset of this phase's B matrix
+    FastDiv div_mj, div_mimj;
+};
+
+struct IgemmArgs {
+    const void *src;
+    const void *bmat;
+    const void *bias;  // [ngemm]; element type (float paths) or int32 (int8)
+    void *dst;
+    int nimg, hs, ws, cs;  // source image
+    int ngemm;
+    int ho, wo;            // full output image extent
+    int osh, osw;          // output step of the sub-grid
+    int gsh, gsw;          // source step per sub-grid step
+    int relu;
+    double requant_m;      // int8 only
+    int nphases;
+    Phase ph[kMaxPhases];
+};
+
+struct TileShape {
+    int bm, bn;
+};
+
+int igemm_num_tiles();
+TileShape igemm_tile_shape(int tile);
+hipError_t launch_igemm(int dtype, int tile, const IgemmArgs &a, int grid_m, int grid_n,
+                        hipStream_t st);
+
+// Re-lays the filter w[K][R][S][C] out as one dense [C][taps*K] matrix per
+// dgrad stride phase (taps of the phase in (jr, js) order, K innermost).
+struct PrepPhase {
+    int r0, rstep, ntr;
+    int s0, sstep, nts;
+    long long off;  // element offset in the output buffer
+};
+struct PrepArgs {
+    const void *w;
+    void *wt;
+    int K, R, S, C;
+    int nphases;
+    int max_elems;  // largest C*ntr*nts*K over phases
+    PrepPhase ph[kMaxPhases];
+};
+hipError_t launch_dgrad_prep(int dtype, const PrepArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// wgrad implicit GEMM: D[k][col] = sum over output pixels of
+//   dy[pix][k] * x[gather(pix, tap(col))][chan(col)],  col = (r, s, c).
+// Pixels are cut into `splits` contiguous slices of pix_per_split pixels; each
+// slice writes fp32 partials [splits][K][ncols] (or the final dw when
+// splits == 1), reduced in slice order by launch_splitk_reduce.
+// ---------------------------------------------------------------------------
+struct WgradArgs {
+    const void *x;
+    const void *dy;
+    void *out;
+    int N, H, W, C, K, R, S, P, Q;
+    int pad_h, pad_w, sh, sw, dh, dw;
+    int ncols;            // R*S*C
+    uint32_t npix;        // N*P*Q
+    uint32_t pix_per_split;
+    int splits;
+    long long part_stride;  // elements between consecutive slices' partials
+    FastDiv div_Q, div_PQ, div_C, div_S;
+};
+
+int wgrad_num_tiles();
+TileShape wgrad_tile_shape(int tile);
+constexpr int kWgradPixStep = 64;  // pixels per main-loop step
+hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st);
+hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long long count,
+                                long long stride, void *out, hipStream_t st);
+// Elements between consecutive slices' partials: count rounded up to 4.
+inline long long splitk_stride(long long count) { return (count + 3) / 4 * 4; }
+
+// ---------------------------------------------------------------------------
+// Direct convolution for groups > 1: one thread per output element, fp32
+// (int32 for int8) accumulation in a fixed (r, s, channel) order.
+// ---------------------------------------------------------------------------
+struct DirectArgs {
+    const void *a;     // fprop: x   dgrad: dy   wgrad: x
+    const void *b;     // fprop: w   dgrad: w    wgrad: dy
+    const void *bias;
+    void *out;         // y / dx / (dw or fp32 partials)
+    int N, H, W, C, K, R, S, P, Q;
+    int pad_h, pad_w, sh, sw, dh, dw, G, Cg, Kg;
+    int relu;
+    double requant_m;
+    int splits;
+    long long part_stride;  // wgrad: elements between slices' partials
+    uint32_t npix;          // wgrad: N*P*Q
+    uint32_t pix_per_split; // wgrad
+    long long total;        // output elements (per split for wgrad)
+};
+hipError_t launch_direct_fprop(int dtype, const DirectArgs &a, hipStream_t st);
+hipError_t launch_direct_dgrad(int dtype, const DirectArgs &a, hipStream_t st);
+hipError_t launch_direct_wgrad(int dtype, const DirectArgs &a, hipStream_t st);
+
+}  // namespace cnv

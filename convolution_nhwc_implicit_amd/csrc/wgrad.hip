@@ -1,0 +1,217 @@
+// wgrad.hip -- weight-gradient implicit GEMM for gfx950, and the fixed-order
+// split-K reduction.
+//
+// dw[k][r][s][c] = sum over output pixels (n,p,q) of
+//                  dy[n,p,q,k] * x[n, p*sh-ph+r*dh, q*sw-pw+s*dw, c].
+// As a GEMM: rows k, columns (r,s,c), reduction over the N*P*Q pixels -- the
+// very long GEMM-K the TVM CUTLASS wgrad pull request names as the reason
+// split-K is needed.  Both operands arrive pixel-major (NHWC), while MFMA wants
+// the reduction index inside each lane's registers, so each thread loads two
+// neighbouring pixels' 8-channel chunks and interleaves them into
+// channel-major LDS rows (pixels innermost).  The reduction over pixels is cut
+// into contiguous slices; each slice writes fp32 partials and a second kernel
+// sums them in slice order (the CUTLASS notebook's "parallel" split-K, with a
+// fixed order instead of atomics, so results are identical run to run).
+// Accumulation is fp32 throughout, as the TVM pull request requires for wgrad.
+#include "device_common.h"
+
+namespace cnv {
+
+template <class E, int BM, int BN>
+__global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
+{
+    constexpr int NT = 256;
+    constexpr int BKP = kWgradPixStep;  // pixels per step
+    constexpr int ROWB = BKP * 2 + 16;  // LDS row: 64 pixels of 2 bytes + pad
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int PAIRS = BKP / 2;      // 32 pixel pairs per step
+    constexpr int ACH = BM / 8, BCH = BN / 8;  // 8-wide channel chunks per step
+    static_assert(PAIRS * ACH == NT && PAIRS * BCH == NT, "one A and one B chunk pair per thread");
+    constexpr int WTM = BM / 2, WTN = BN / 2;  // 2x2 waves
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    using elem = typename E::elem;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int mt = blockIdx.x, nt = blockIdx.y, z = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int pp = tid % PAIRS, ch = tid / PAIRS;
+
+    // this thread's dy chunk: channels k0..k0+7
+    const int k0 = mt * BM + ch * 8;
+    const bool kval = k0 < a.K;
+    // this thread's x chunk: columns col0..col0+7, all in one tap (C % 8 == 0)
+    const int col0 = nt * BN + ch * 8;
+    const bool cval = col0 < a.ncols;
+    const uint32_t tap = fdiv((uint32_t)(cval ? col0 : 0), a.div_C);
+    const int cch = (cval ? col0 : 0) - (int)tap * a.C;
+    const uint32_t tr = fdiv(tap, a.div_S);
+    const int ts = (int)tap - (int)tr * a.S;
+    const int hoff = (int)tr * a.dh - a.pad_h;
+    const int woff = ts * a.dw - a.pad_w;
+
+    const uint32_t pbeg = (uint32_t)z * a.pix_per_split;
+    uint32_t pend = pbeg + a.pix_per_split;
+    if (pend > a.npix || pend < pbeg) pend = a.npix;
+    const int KT = pend > pbeg ? (int)((pend - pbeg + BKP - 1) / BKP) : 0;
+
+    const elem *dy = (const elem *)a.dy;
+    const elem *x = (const elem *)a.x;
+    const uint32_t PQ = (uint32_t)a.P * (uint32_t)a.Q;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 rdy[2], rx[2];
+
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const uint32_t pix = pbeg + (uint32_t)kt * BKP + 2 * pp + e;
+            const bool ok = pix < pend;
+            rdy[e] = (ok && kval) ? *(const u32x4 *)(dy + (size_t)pix * a.K + k0) : zero;
+            bool okx = ok && cval;
+            const uint32_t n = fdiv(ok ? pix : 0, a.div_PQ);
+            const uint32_t rem = (ok ? pix : 0) - n * PQ;
+            const uint32_t p = fdiv(rem, a.div_Q);
+            const uint32_t q = rem - p * a.Q;
+            const int h = (int)p * a.sh + hoff;
+            const int w = (int)q * a.sw + woff;
+            okx = okx && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W;
+            rx[e] = okx ? *(const u32x4 *)(x + (((size_t)n * a.H + h) * a.W + w) * a.C + cch) : zero;
+        }
+    };
+    // interleave the two pixels: LDS row = channel, 32-bit word = (pixel 2pp, pixel 2pp+1)
+    auto sstore = [&](int stage) {
+        unsigned char *base = smem + stage * STAGE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a0 = rdy[0][j], a1 = rdy[1][j];
+            *(uint32_t *)(base + (ch * 8 + 2 * j) * ROWB + pp * 4) = (a0 & 0xFFFFu) | (a1 << 16);
+            *(uint32_t *)(base + (ch * 8 + 2 * j + 1) * ROWB + pp * 4) = (a0 >> 16) | (a1 & 0xFFFF0000u);
+            const uint32_t b0 = rx[0][j], b1 = rx[1][j];
+            *(uint32_t *)(base + (BM + ch * 8 + 2 * j) * ROWB + pp * 4) = (b0 & 0xFFFFu) | (b1 << 16);
+            *(uint32_t *)(base + (BM + ch * 8 + 2 * j + 1) * ROWB + pp * 4) = (b0 >> 16) | (b1 & 0xFFFF0000u);
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int frag_row = lane & 15, frag_k = (lane >> 4) * 16;
+    if (KT > 0) {
+        gload(0);
+        sstore(0);
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < KT) gload(kt + 1);
+            const unsigned char *base = smem + cur * STAGE;
+#pragma unroll
+            for (int ks = 0; ks < BKP * 2 / 64; ++ks) {
+                u32x4 fa[FM], fb[FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    fa[i] = *(const u32x4 *)(base + (wm * WTM + i * 16 + frag_row) * ROWB + ks * 64 + frag_k);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    fb[j] = *(const u32x4 *)(base + (BM + wn * WTN + j * 16 + frag_row) * ROWB + ks * 64 + frag_k);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(fa[i], fb[j], acc[i][j]);
+            }
+            if (kt + 1 < KT) sstore(cur ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // result block layout: lane holds column (lane & 15), rows 4*(lane >> 4) + r
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = nt * BN + wn * WTN + j * 16 + (lane & 15);
+            if (col >= a.ncols) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k = mt * BM + wm * WTM + i * 16 + (lane >> 4) * 4 + r;
+                if (k >= a.K) continue;
+                if (a.splits == 1)
+                    ((elem *)a.out)[(size_t)k * a.ncols + col] = E::from_f32(acc[i][j][r]);
+                else
+                    ((float *)a.out)[(size_t)z * a.part_stride + (size_t)k * a.ncols + col] = acc[i][j][r];
+            }
+        }
+}
+
+int wgrad_num_tiles() { return 1; }
+TileShape wgrad_tile_shape(int tile)
+{
+    (void)tile;
+    return {64, 64};
+}
+
+hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st)
+{
+    if (tile != 0) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((a.K + 63) / 64), (unsigned)((a.ncols + 63) / 64), (unsigned)a.splits);
+    switch (dtype) {
+    case CONV2D_DTYPE_F16: wgrad_kernel<EF16, 64, 64><<<grid, 256, 0, st>>>(a); break;
+    case CONV2D_DTYPE_BF16: wgrad_kernel<EBF16, 64, 64><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// out[i] = round(sum_{z = 0..splits-1} parts[z*stride + i]), summed in slice
+// order in fp32, four elements per thread.  stride is a multiple of 4 and at
+// least count, so the 128-bit partial loads stay inside slice z; the last
+// thread stores only the elements below count.
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *parts, int splits, long long count,
+                                                            long long stride, typename E::elem *out)
+{
+    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= count) return;
+    f32x4 s = *(const f32x4 *)(parts + i);
+    for (int z = 1; z < splits; ++z) {
+        const f32x4 v = *(const f32x4 *)(parts + (size_t)z * stride + i);
+        s[0] += v[0];
+        s[1] += v[1];
+        s[2] += v[2];
+        s[3] += v[3];
+    }
+    typename E::elem o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = E::from_f32(s[j]);
+    if (i + 4 <= count) {
+        *(uint2 *)(out + i) = *(const uint2 *)o;
+    } else {
+        for (int j = 0; j < 4 && i + j < count; ++j) out[i + j] = o[j];
+    }
+}
+
+hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long long count,
+                                long long stride, void *out, hipStream_t st)
+{
+    if (stride % 4 || stride < count) return hipErrorInvalidValue;
+    const long long threads = (count + 3) / 4;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    if (blocks == 0) return hipSuccess;
+    switch (dtype) {
+    case CONV2D_DTYPE_F16:
+        splitk_reduce_kernel<EF16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, (uint16_t *)out);
+        break;
+    case CONV2D_DTYPE_BF16:
+        splitk_reduce_kernel<EBF16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, (uint16_t *)out);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cnv

@@ -1,0 +1,192 @@
+/*
+ * conv2d_nhwc.h -- C ABI of the MI355X (gfx950) implicit-GEMM NHWC conv2d library.
+ *
+ * Operations (deep-learning convolution, i.e. cross-correlation without a
+ * filter flip, as aten.conv2d computes it in the CUTLASS Python Conv2d
+ * notebook, "Declaring and running a Conv2d Fprop"):
+ *
+ *   fprop  y[n,p,q,k]   = sum_{r,s,c'} x[n, p*sh-ph+r*dh, q*sw-pw+s*dw, g*C/G+c'] * w[k,r,s,c']
+ *                         (+ bias[k]) (ReLU) -- then one rounding to the output type
+ *   dgrad  dx = gradient of fprop with respect to x, applied to dy
+ *          (torch.nn.grad.conv2d_input in the notebook's "Declaring and running
+ *          Conv2d Dgrad and Wgrad"; the input extent H,W is passed explicitly)
+ *   wgrad  dw = gradient of fprop with respect to w, applied to dy
+ *          (torch.nn.grad.conv2d_weight in the same section)
+ *
+ * Tensor layouts, all dense and row-major (channel-last, as the notebook's
+ * "General setup" declares them):
+ *   x, dx   [N][H][W][C]        w, dw   [K][R][S][C/G]
+ *   y, dy   [N][P][Q][K]        bias    [K]
+ * with P = floor((H + 2*pad_h - dil_h*(R-1) - 1) / stride_h) + 1 and likewise Q
+ * (the tensorcore Conv2D page's "Surface" formula, extended by the dilated
+ * filter span).  Group g owns input channels [g*C/G, (g+1)*C/G) and output
+ * channels [g*K/G, (g+1)*K/G).
+ *
+ * Element types:
+ *   CONV2D_DTYPE_F16, CONV2D_DTYPE_BF16: x, w, y, dx, dw, dy and bias in that
+ *     type; products accumulate in fp32; the result is rounded once, to nearest
+ *     even.  wgrad always accumulates in fp32 (the TVM CUTLASS wgrad pull request
+ *     forces fp32 accumulation for wgrad).
+ *   CONV2D_DTYPE_I8: fprop only.  x, w, y int8; bias int32 in accumulator
+ *     units; int32 accumulation; then + bias, ReLU if set, multiplication by
+ *     act_scale*w_scale/out_scale in double precision, rounding half to even
+ *     and saturation to [-128, 127] (the op-graph order of the quantized cuDNN
+ *     conv, apply_impl_helper on the "kReluFused" page).
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller owns every buffer.  The library never allocates or
+ *     frees memory and keeps no mutable global state.  Device pointers must be
+ *     16-byte aligned.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *     enqueued on it and the call returns after enqueue; results are ready when
+ *     the stream is synchronised.
+ *   - Errors: every check runs before anything is enqueued; on error no output
+ *     byte is written.  An unsupported case is an error, never a silent switch
+ *     to another algorithm (the quantized cuDNN conv's hard failure when no
+ *     engine can run it).
+ *   - Determinism: the same inputs, problem and algo give identical bits on
+ *     every run; reductions run in a fixed order, with no atomics on values.
+ */
+#ifndef CONV2D_NHWC_H
+#define CONV2D_NHWC_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (int). */
+#define CONV2D_OK                       0
+#define CONV2D_ERR_INVALID_ARGUMENT     1  /* bad sizes, P or Q < 1, C%G or K%G != 0, null pointer */
+#define CONV2D_ERR_UNSUPPORTED          2  /* dtype/op pair, alignment, channel multiple */
+#define CONV2D_ERR_WORKSPACE_TOO_SMALL  3
+#define CONV2D_ERR_DEVICE               4  /* a HIP launch failed */
+
+/* Element types. */
+#define CONV2D_DTYPE_F16   0
+#define CONV2D_DTYPE_BF16  1
+#define CONV2D_DTYPE_I8    2
+
+/* Operations (for the size and plan queries). */
+#define CONV2D_OP_FPROP  0
+#define CONV2D_OP_DGRAD  1
+#define CONV2D_OP_WGRAD  2
+
+/*
+ * Problem descriptor: the parameter set the burn CubeCL conv dispatch
+ * (ConvOptions: stride, padding, dilation, groups) and the tensorcore
+ * tc_conv2d_* surface pass.  All fields are plain ints; padding is symmetric
+ * and zero-valued per axis.
+ */
+typedef struct conv2d_problem {
+    int n, c, h, w;          /* input  [N][H][W][C] */
+    int k, r, s;             /* filter [K][R][S][C/G] */
+    int pad_h, pad_w;        /* >= 0 */
+    int stride_h, stride_w;  /* >= 1 */
+    int dil_h, dil_w;        /* >= 1 */
+    int groups;              /* >= 1, divides C and K */
+} conv2d_problem_t;
+
+/*
+ * Optional algorithm override (pass NULL for the library's choice).  The
+ * CUTLASS Python notebook exposes the same two knobs ("Tile Description",
+ * "Split-K") and requires every choice to give the same answer.
+ *   tile:    0 = library choice, otherwise 1 + index into the kernel's tile
+ *            table (see conv2d_plan_info).  Out-of-range -> UNSUPPORTED.
+ *   split_k: 0 = library choice, otherwise the number of slices the wgrad
+ *            reduction over N*P*Q is cut into (partials are summed in slice
+ *            order by a second kernel).  Ignored by fprop and dgrad.
+ */
+typedef struct conv2d_algo {
+    int tile;
+    int split_k;
+} conv2d_algo_t;
+
+/* What the library will launch for a problem (diagnostics and tests). */
+typedef struct conv2d_plan_info {
+    int kernel;        /* 1 = implicit GEMM, 2 = direct (groups > 1) */
+    int tile;          /* index of the tile configuration used (0-based) */
+    int num_tiles;     /* number of tile configurations available for this op/dtype */
+    int split_k;       /* reduction slices (wgrad), 1 otherwise */
+    int phases;        /* dgrad stride phases launched, 1 otherwise */
+    size_t workspace_bytes;
+} conv2d_plan_info_t;
+
+/*
+ * Output extent of fprop (and extent of dy for dgrad / wgrad).
+ * P and Q receive floor((H + 2*pad - dil*(R-1) - 1)/stride) + 1 per axis.
+ * Returns INVALID_ARGUMENT for non-positive sizes, negative padding, a
+ * dilated filter longer than the padded input (P or Q < 1), or groups that do
+ * not divide C and K.  P and Q may be NULL.
+ */
+int conv2d_output_size(const conv2d_problem_t *prob, int *P, int *Q);
+
+/*
+ * Workspace bytes the caller must pass to the given op (0 is a valid answer).
+ * A pure function of its arguments.  dgrad uses the workspace for the
+ * re-laid-out filter of each stride phase; wgrad for fp32 split-K partials.
+ * The caller-allocated scratch with a size query is the tensorcore Conv2D
+ * page's "Scratch sizing" convention, minus the im2col buffer.
+ */
+int conv2d_workspace_size(int op, const conv2d_problem_t *prob, int dtype,
+                          const conv2d_algo_t *algo, size_t *bytes);
+
+/* The plan the library would run for (op, prob, dtype, algo).  No device work. */
+int conv2d_plan_info(int op, const conv2d_problem_t *prob, int dtype,
+                     const conv2d_algo_t *algo, conv2d_plan_info_t *info);
+
+/*
+ * Forward convolution (tensorcore tc_conv2d_forward; burn conv_forward_nhwc:
+ * implicit GEMM for groups == 1, direct convolution otherwise).
+ *   x     device, [N][H][W][C], dtype
+ *   w     device, [K][R][S][C/G], dtype
+ *   bias  device, [K] or NULL; dtype for F16/BF16, int32 for I8
+ *   relu  0 or 1
+ *   act_scale, w_scale, out_scale  I8 only (finite, > 0); ignored otherwise
+ *   y     device, [N][P][Q][K], dtype; overwritten
+ *   workspace / workspace_bytes  as conv2d_workspace_size(CONV2D_OP_FPROP, ...)
+ */
+int conv2d_fprop(const conv2d_problem_t *prob, int dtype,
+                 const void *x, const void *w, const void *bias, int relu,
+                 double act_scale, double w_scale, double out_scale,
+                 void *y, void *workspace, size_t workspace_bytes,
+                 const conv2d_algo_t *algo, void *stream);
+
+/*
+ * Data gradient (tensorcore tc_conv2d_backward_input; burn conv_data_backward).
+ * Every element of dx is written, including positions no output reads (0).
+ *   dy  device, [N][P][Q][K], dtype (F16 or BF16)
+ *   w   device, [K][R][S][C/G], dtype
+ *   dx  device, [N][H][W][C], dtype; overwritten
+ * No bias and no ReLU.  Strided problems run one implicit GEMM per stride
+ * phase (h mod stride_h, w mod stride_w) in a single launch.
+ */
+int conv2d_dgrad(const conv2d_problem_t *prob, int dtype,
+                 const void *dy, const void *w, void *dx,
+                 void *workspace, size_t workspace_bytes,
+                 const conv2d_algo_t *algo, void *stream);
+
+/*
+ * Weight gradient (tensorcore tc_conv2d_backward_weight; burn
+ * conv_weight_backward).  The reduction runs over all N*P*Q output pixels, in
+ * fp32, cut into split_k contiguous pixel slices whose fp32 partials are
+ * summed in slice order by a second kernel (the "parallel" split-K of the
+ * CUTLASS notebook's "Split-K" section, made deterministic).
+ *   x   device, [N][H][W][C], dtype (F16 or BF16)
+ *   dy  device, [N][P][Q][K], dtype
+ *   dw  device, [K][R][S][C/G], dtype; overwritten
+ */
+int conv2d_wgrad(const conv2d_problem_t *prob, int dtype,
+                 const void *x, const void *dy, void *dw,
+                 void *workspace, size_t workspace_bytes,
+                 const conv2d_algo_t *algo, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *conv2d_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV2D_NHWC_H */

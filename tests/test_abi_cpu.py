@@ -1,0 +1,176 @@
+"""Host-side tests of the C ABI: no GPU, no kernel launches.
+
+The library must load on a machine without a GPU, export every function the
+public header declares, compute output sizes the way the oracle does (two
+independent implementations of the same formula), and reject bad arguments
+before anything could be enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from convolution_nhwc_implicit_amd import binding as B
+from convolution_nhwc_implicit_amd.workloads import WORKLOADS, problem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b(\w+)\s*\(", text, flags=re.M):
+            if m.group(1) not in ("defined",):
+                names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_header_functions_exported(lib):
+    names = declared_functions()
+    assert {"conv2d_fprop", "conv2d_dgrad", "conv2d_wgrad", "conv2d_output_size",
+            "conv2d_workspace_size", "conv2d_plan_info", "conv2d_status_string"} <= names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(0, 6):
+        s = B.conv2d_status_string(code)
+        assert isinstance(s, str) and s
+    assert B.conv2d_status_string(0) == "ok"
+
+
+def test_output_size_agrees_with_oracle():
+    n = 0
+    for inp in (1, 2, 5, 8, 13, 28, 57):
+        for pad in (0, 1, 2, 3):
+            for k in (1, 2, 3, 5):
+                for stride in (1, 2, 3):
+                    for dil in (1, 2, 3):
+                        prob = problem(1, 8, inp, inp + 1, 8, k, k, pad=(pad, pad),
+                                       stride=(stride, stride), dil=(dil, dil))
+                        exp_h = oracle.out_size(inp, pad, k, stride, dil)
+                        exp_w = oracle.out_size(inp + 1, pad, k, stride, dil)
+                        if exp_h < 1 or exp_w < 1:
+                            with pytest.raises(B.Conv2dError) as e:
+                                B.conv2d_output_size(prob)
+                            assert e.value.status == B.CONV2D_ERR_INVALID_ARGUMENT
+                        else:
+                            assert B.conv2d_output_size(prob) == (exp_h, exp_w)
+                            n += 1
+    assert n > 500
+
+
+def test_workload_output_sizes():
+    exp = {"c1_tiny": (8, 8), "c2_strided": (14, 14), "c3a_resnet3x3": (56, 56),
+           "c3b_resnet1x1": (56, 56), "c4_awkward": (27, 27), "c4g_grouped": (27, 27),
+           "c5_int8": (56, 56)}
+    for name, wl in WORKLOADS.items():
+        assert B.conv2d_output_size(wl["prob"]) == exp[name]
+        assert oracle.output_hw(wl["prob"]) == exp[name]
+
+
+@pytest.mark.parametrize("bad", [
+    dict(N=0), dict(C=0), dict(K=-1), dict(R=0), dict(pad_h=-1), dict(stride_w=0),
+    dict(dil_h=0), dict(groups=0), dict(groups=3), dict(H=1, pad_h=0),
+])
+def test_invalid_problems(bad):
+    prob = dict(problem(2, 8, 8, 8, 16, 3, 3, pad=(1, 1)), **bad)
+    for op in (0, 1, 2):
+        with pytest.raises(B.Conv2dError) as e:
+            B.conv2d_workspace_size(op, prob, "f16")
+        assert e.value.status == B.CONV2D_ERR_INVALID_ARGUMENT
+
+
+def test_unsupported_cases():
+    p = problem(2, 12, 8, 8, 16, 3, 3, pad=(1, 1))  # C % 8 != 0 on the implicit GEMM
+    with pytest.raises(B.Conv2dError) as e:
+        B.conv2d_plan_info(B.CONV2D_OP_FPROP, p, "f16")
+    assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
+    p = problem(2, 16, 8, 8, 16, 3, 3, pad=(1, 1))  # int8 needs C % 16, fprop only
+    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, p, "i8")["kernel"] == 1
+    for op in (B.CONV2D_OP_DGRAD, B.CONV2D_OP_WGRAD):
+        with pytest.raises(B.Conv2dError) as e:
+            B.conv2d_plan_info(op, p, "i8")
+        assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
+    with pytest.raises(B.Conv2dError) as e:
+        B.conv2d_plan_info(B.CONV2D_OP_FPROP, p, 7)
+    assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
+    with pytest.raises(B.Conv2dError) as e:  # tile index beyond the table
+        B.conv2d_plan_info(B.CONV2D_OP_FPROP, p, "f16", algo=dict(tile=99))
+    assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
+
+
+def test_plan_rules():
+    g = problem(2, 12, 9, 9, 12, 3, 3, pad=(1, 1), groups=3)  # grouped -> direct, any channel count
+    for op in (0, 1, 2):
+        assert B.conv2d_plan_info(op, g, "bf16")["kernel"] == 2
+    s = problem(2, 16, 9, 9, 16, 3, 3, pad=(1, 1), stride=(2, 3))
+    info = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, s, "f16")
+    assert info["kernel"] == 1 and info["phases"] == 6
+    assert info["workspace_bytes"] >= 16 * 3 * 3 * 16 * 2
+    w = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, s, "f16", algo=dict(split_k=5))
+    assert w["split_k"] == 5 and w["workspace_bytes"] >= 5 * 16 * 3 * 3 * 16 * 4
+    assert B.conv2d_plan_info(B.CONV2D_OP_WGRAD, s, "f16", algo=dict(split_k=1))["workspace_bytes"] == 0
+    # the plan is a pure function of its arguments
+    assert B.conv2d_plan_info(2, s, "f16") == B.conv2d_plan_info(2, s, "f16")
+    for t in range(1, B.conv2d_plan_info(0, s, "f16")["num_tiles"] + 1):
+        assert B.conv2d_plan_info(0, s, "f16", algo=dict(tile=t))["tile"] == t - 1
+
+
+def _raw_call(lib, fn, *args):
+    return getattr(lib, fn)(*args)
+
+
+def test_errors_return_before_enqueue(lib):
+    """Error paths return their code before any HIP call; the fake device
+    addresses below are never dereferenced."""
+    prob = B.make_problem(problem(2, 8, 8, 8, 16, 3, 3, pad=(1, 1)))
+    bad = B.make_problem(problem(2, 8, 8, 8, 16, 3, 3, pad=(1, 1), groups=3))
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    pr = ctypes.byref(prob)
+    # invalid problem
+    assert lib.conv2d_fprop(ctypes.byref(bad), 0, fake, fake, None, 0, 1.0, 1.0, 1.0, fake, None, 0,
+                            None, None) == B.CONV2D_ERR_INVALID_ARGUMENT
+    # null required pointer
+    assert lib.conv2d_fprop(pr, 0, None, fake, None, 0, 1.0, 1.0, 1.0, fake, None, 0, None,
+                            None) == B.CONV2D_ERR_INVALID_ARGUMENT
+    # relu must be 0/1
+    assert lib.conv2d_fprop(pr, 0, fake, fake, None, 3, 1.0, 1.0, 1.0, fake, None, 0, None,
+                            None) == B.CONV2D_ERR_INVALID_ARGUMENT
+    # misaligned tensor
+    assert lib.conv2d_fprop(pr, 0, odd, fake, None, 0, 1.0, 1.0, 1.0, fake, None, 0, None,
+                            None) == B.CONV2D_ERR_UNSUPPORTED
+    # int8 scales must be finite and positive
+    p16 = B.make_problem(problem(2, 16, 8, 8, 16, 3, 3, pad=(1, 1)))
+    assert lib.conv2d_fprop(ctypes.byref(p16), 2, fake, fake, None, 0, 0.0, 1.0, 1.0, fake, None, 0,
+                            None, None) == B.CONV2D_ERR_INVALID_ARGUMENT
+    # workspace too small (dgrad always needs the re-laid-out filter)
+    assert lib.conv2d_dgrad(pr, 0, fake, fake, fake, fake, 16, None,
+                            None) == B.CONV2D_ERR_WORKSPACE_TOO_SMALL
+    assert lib.conv2d_wgrad(pr, 0, fake, fake, fake, None, 0,
+                            ctypes.byref(B.Conv2dAlgo(0, 4)), None) == B.CONV2D_ERR_WORKSPACE_TOO_SMALL
+    # int8 backward passes are not offered
+    assert lib.conv2d_dgrad(ctypes.byref(p16), 2, fake, fake, fake, fake, 1 << 20, None,
+                            None) == B.CONV2D_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(2, 8, 8, 8, dtype=torch.float16)
+    w = torch.zeros(16, 3, 3, 8, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        B.fprop(x, w, padding=1)

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and medium problems are compared element by element on every output;
+they span several tiles in M, N and GEMM-K and end in ragged tails.  The full
+workloads are compared on every output where the oracle is fast enough and on
+a sample of outputs otherwise, in the launch configuration the benchmark uses
+(the library's default plan).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from convolution_nhwc_implicit_amd import binding as B
+from convolution_nhwc_implicit_amd import workloads as WL
+from convolution_nhwc_implicit_amd.workloads import problem
+
+from parity import (check, f64, oracle_fprop_out, run_dgrad, run_fprop, run_wgrad,
+                    sample_indices)
+
+pytestmark = pytest.mark.gpu
+
+
+def case_inputs(prob, dtype, dist, seed, bias=True):
+    P, Q = oracle.output_hw(prob)
+    return WL.random_case(prob, dtype, dist, seed, P, Q, bias=bias)
+
+
+# (id, problem, dtype, dist, bias, relu)
+CASES = [
+    ("ragged3x3", problem(3, 24, 17, 19, 40, 3, 3, pad=(1, 1)), "f16", "int", True, False),
+    ("ragged3x3_relu", problem(2, 32, 15, 13, 72, 3, 3, pad=(1, 1)), "f16", "int", True, True),
+    ("strided_dilated", problem(2, 16, 23, 21, 24, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2)),
+     "f16", "int", False, False),
+    ("asym", problem(2, 8, 11, 14, 16, 3, 2, pad=(1, 0), stride=(2, 1), dil=(1, 2)), "f16", "int",
+     True, False),
+    ("stride3", problem(2, 16, 13, 10, 8, 2, 2, pad=(0, 1), stride=(3, 3)), "f16", "int", False,
+     False),
+    ("pad_gt_filter", problem(2, 8, 6, 7, 16, 3, 3, pad=(3, 2)), "f16", "int", True, False),
+    ("one_by_one", problem(2, 32, 9, 13, 48, 1, 1), "f16", "int", True, True),
+    ("one_by_one_s2", problem(2, 16, 9, 13, 24, 1, 1, stride=(2, 2)), "f16", "int", False, False),
+    ("tiny_image", problem(3, 8, 1, 1, 8, 1, 1), "f16", "int", True, False),
+    ("p_is_1", problem(2, 16, 3, 3, 16, 3, 3), "f16", "int", True, False),
+    ("wide_c", problem(1, 256, 7, 6, 32, 3, 3, pad=(1, 1)), "f16", "int", True, False),
+    ("bf16_int", problem(2, 24, 12, 11, 40, 3, 3, pad=(1, 1), stride=(2, 1)), "bf16", "int", True,
+     True),
+    ("bf16_gauss", problem(3, 32, 16, 17, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", True, True),
+    ("f16_gauss", problem(2, 64, 20, 18, 136, 3, 3, pad=(1, 1)), "f16", "gauss", True, True),
+    ("f16_gauss_s2d2", problem(2, 48, 25, 23, 56, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2)),
+     "f16", "gauss", False, False),
+    ("grouped2", problem(2, 12, 9, 10, 8, 3, 3, pad=(1, 1), groups=2), "bf16", "int", True, True),
+    ("grouped4_s2d2", problem(2, 16, 13, 13, 8, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2),
+                              groups=4), "f16", "int", False, False),
+    ("depthwise", problem(2, 8, 10, 9, 8, 3, 3, pad=(1, 1), groups=8), "f16", "int", True, False),
+    ("grouped_gauss", problem(2, 24, 11, 11, 24, 3, 3, pad=(1, 1), groups=3), "bf16", "gauss",
+     True, False),
+]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,dist,bias,relu", CASES, ids=[c[0] for c in CASES])
+def test_parity_cases(cid, prob, dtype, dist, bias, relu):
+    mode = "exact" if dist == "int" else "tol"
+    x, w, b, dy = case_inputs(prob, dtype, dist, seed=zlib.crc32(cid.encode()), bias=bias)
+    y = run_fprop(prob, dtype, x, w, b, relu)
+    check(f64(y), oracle_fprop_out(prob, dtype, x, w, b, relu), dtype, mode, f"{cid} fprop")
+    dx = run_dgrad(prob, dtype, dy, w, fill=float("nan"))
+    check(f64(dx), oracle.dgrad(prob, f64(dy), f64(w)), dtype, mode, f"{cid} dgrad")
+    dw = run_wgrad(prob, dtype, x, dy)
+    check(f64(dw), oracle.wgrad(prob, f64(x), f64(dy)), dtype, mode, f"{cid} wgrad")
+
+
+INT8_CASES = [
+    ("i8_3x3", problem(2, 32, 11, 13, 48, 3, 3, pad=(1, 1)), True, True),
+    ("i8_norelu", problem(2, 16, 9, 9, 32, 3, 3, pad=(1, 1), stride=(2, 2)), True, False),
+    ("i8_nobias", problem(1, 64, 8, 7, 16, 1, 1), False, True),
+    ("i8_grouped", problem(2, 16, 7, 7, 16, 3, 3, pad=(1, 1), groups=4), True, True),
+]
+
+
+@pytest.mark.parametrize("cid,prob,bias,relu", INT8_CASES, ids=[c[0] for c in INT8_CASES])
+def test_int8_fprop_exact(cid, prob, bias, relu):
+    x, w, b, _ = case_inputs(prob, "i8", "uniform_i8", seed=zlib.crc32(cid.encode()), bias=bias)
+    scales = (0.02, 0.01, 0.05)
+    y = run_fprop(prob, "i8", x, w, b, relu, scales=scales)
+    exp = oracle_fprop_out(prob, "i8", x, w, b, relu, scales=scales)
+    got = y.cpu().numpy().reshape(-1)
+    bad = np.nonzero(got != exp)[0]
+    assert bad.size == 0, f"{bad.size} int8 codes differ, first {bad[:5]}: {got[bad[:5]]} vs {exp[bad[:5]]}"
+    if relu:
+        assert got.min() >= 0
+
+
+# ------------------------------------------------------------ tile / split sweeps
+
+def test_every_fprop_and_dgrad_tile_matches_oracle():
+    prob = problem(2, 32, 13, 11, 48, 3, 3, pad=(1, 1), stride=(2, 1))
+    x, w, b, dy = case_inputs(prob, "f16", "int", seed=42)
+    ref_y = oracle_fprop_out(prob, "f16", x, w, b, True)
+    ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
+    n = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")["num_tiles"]
+    for t in range(1, n + 1):
+        algo = dict(tile=t)
+        check(f64(run_fprop(prob, "f16", x, w, b, True, algo=algo)), ref_y, "f16", "exact", f"tile {t}")
+        check(f64(run_dgrad(prob, "f16", dy, w, algo=algo)), ref_dx, "f16", "exact", f"dgrad tile {t}")
+
+
+def test_int8_every_tile():
+    prob = problem(2, 32, 9, 10, 48, 3, 3, pad=(1, 1))
+    x, w, b, _ = case_inputs(prob, "i8", "uniform_i8", seed=43)
+    scales = (0.02, 0.01, 0.05)
+    exp = oracle_fprop_out(prob, "i8", x, w, b, True, scales=scales)
+    for t in range(1, B.conv2d_plan_info(0, prob, "i8")["num_tiles"] + 1):
+        y = run_fprop(prob, "i8", x, w, b, True, scales=scales, algo=dict(tile=t))
+        assert np.array_equal(y.cpu().numpy().reshape(-1), exp), f"tile {t}"
+
+
+@pytest.mark.parametrize("groups", [1, 2])
+def test_wgrad_split_k_bit_identical(groups):
+    prob = problem(2, 16, 14, 12, 24, 3, 3, pad=(1, 1), groups=groups)
+    x, _, _, dy = case_inputs(prob, "f16", "int", seed=44)
+    ref = oracle.wgrad(prob, f64(x), f64(dy))
+    outs = []
+    for s in (1, 2, 3, 5, 16, 200):
+        dw = run_wgrad(prob, "f16", x, dy, algo=dict(split_k=s))
+        check(f64(dw), ref, "f16", "exact", f"split {s}")
+        outs.append(dw.cpu())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_deterministic_repeats():
+    prob = problem(4, 64, 18, 18, 64, 3, 3, pad=(1, 1))
+    x, w, b, dy = case_inputs(prob, "f16", "gauss", seed=45)
+    for run in (lambda: run_fprop(prob, "f16", x, w, b, True), lambda: run_dgrad(prob, "f16", dy, w),
+                lambda: run_wgrad(prob, "f16", x, dy)):
+        a, c = run(), run()
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_nonzero_storage_offsets():
+    """Sub-tensors that start inside a larger allocation (16-byte aligned)."""
+    prob = problem(3, 16, 9, 9, 24, 3, 3, pad=(1, 1))
+    x, w, b, dy = case_inputs(prob, "f16", "int", seed=46)
+    P, Q = B.conv2d_output_size(prob)
+
+    def inside(t, off=64):
+        buf = torch.zeros(t.numel() + 2 * off, dtype=t.dtype, device="cuda")
+        v = buf[off:off + t.numel()].view(t.shape)
+        v.copy_(t.to("cuda"))
+        return v
+
+    y = inside(torch.zeros(prob["N"], P, Q, prob["K"], dtype=torch.float16))
+    B.conv2d_fprop(prob, "f16", inside(x), inside(w), inside(b), 0, 1.0, 1.0, 1.0, y, None)
+    torch.cuda.synchronize()
+    check(f64(y), oracle_fprop_out(prob, "f16", x, w, b, False), "f16", "exact", "offset fprop")
+
+
+def test_error_leaves_output_untouched():
+    prob = problem(2, 16, 8, 8, 16, 3, 3, pad=(1, 1))
+    x, w, b, dy = case_inputs(prob, "f16", "int", seed=47)
+    dx = torch.full((2, 8, 8, 16), 7.0, dtype=torch.float16, device="cuda")
+    small = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.Conv2dError) as e:
+        B.conv2d_dgrad(prob, "f16", dy.cuda(), w.cuda(), dx, small)
+    assert e.value.status == B.CONV2D_ERR_WORKSPACE_TOO_SMALL
+    torch.cuda.synchronize()
+    assert torch.all(dx == 7.0)
+
+
+# ------------------------------------------------------------- the workloads
+
+def _workload_inputs(name):
+    wl = WL.WORKLOADS[name]
+    prob = wl["prob"]
+    P, Q = B.conv2d_output_size(prob)
+    x, w = WL.make_x(name), WL.make_w(name)
+    b = WL.make_bias(name) if wl["bias"] else None
+    dy = WL.make_dy(name, P, Q) if wl["dtype"] != "i8" else None
+    return wl, prob, x, w, b, dy
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "c2_strided", "c4g_grouped"])
+def test_workload_full(name):
+    wl, prob, x, w, b, dy = _workload_inputs(name)
+    dt, mode = wl["dtype"], wl["check"]
+    y = run_fprop(prob, dt, x, w, b, wl["relu"])
+    check(f64(y), oracle_fprop_out(prob, dt, x, w, b, wl["relu"]), dt, mode, f"{name} fprop")
+    dx = run_dgrad(prob, dt, dy, w, fill=float("nan"))
+    check(f64(dx), oracle.dgrad(prob, f64(dy), f64(w)), dt, mode, f"{name} dgrad")
+    dw = run_wgrad(prob, dt, x, dy)
+    check(f64(dw), oracle.wgrad(prob, f64(x), f64(dy)), dt, mode, f"{name} wgrad")
+
+
+@pytest.mark.parametrize("name", ["c3a_resnet3x3", "c3b_resnet1x1", "c4_awkward"])
+def test_workload_sampled(name):
+    wl, prob, x, w, b, dy = _workload_inputs(name)
+    dt, mode = wl["dtype"], wl["check"]
+    xb, wb, dyb = f64(x), f64(w), f64(dy)
+    y = f64(run_fprop(prob, dt, x, w, b, wl["relu"])).reshape(-1)
+    idx = sample_indices(y.size, 4096, 1)
+    check(y[idx], oracle_fprop_out(prob, dt, x, w, b, wl["relu"], idx=idx), dt, mode, f"{name} fprop")
+    dx = run_dgrad(prob, dt, dy, w, fill=float("nan"))
+    dx = f64(dx).reshape(-1)
+    idx = sample_indices(dx.size, 4096, 2)
+    check(dx[idx], oracle.dgrad_sampled(prob, dyb, wb, idx), dt, mode, f"{name} dgrad")
+    dw = f64(run_wgrad(prob, dt, x, dy)).reshape(-1)
+    idx = sample_indices(dw.size, 1024, 3)
+    check(dw[idx], oracle.wgrad_sampled(prob, xb, dyb, idx), dt, mode, f"{name} wgrad")
+    # a property at full size: the three passes are adjoint (fp32-accumulated
+    # GPU values, so equal to within the rounding of the outputs)
+    if not wl["relu"] and b is None:
+        a1 = float(np.dot(y, dyb.reshape(-1)))
+        a2 = float(np.dot(xb.reshape(-1), dx))
+        a3 = float(np.dot(wb.reshape(-1), dw))
+        scale = np.linalg.norm(y) * np.linalg.norm(dyb)
+        assert abs(a1 - a2) <= 1e-2 * scale and abs(a1 - a3) <= 1e-2 * scale
+
+
+def test_workload_int8_sampled():
+    name = "c5_int8"
+    wl, prob, x, w, b, _ = _workload_inputs(name)
+    y = run_fprop(prob, "i8", x, w, b, wl["relu"], scales=wl["scales"]).cpu().numpy().reshape(-1)
+    idx = sample_indices(y.size, 8192, 4)
+    exp = oracle_fprop_out(prob, "i8", x, w, b, wl["relu"], scales=wl["scales"], idx=idx)
+    assert np.array_equal(y[idx], exp)
+    assert y.min() >= 0 and y.max() <= 127
