@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-images", type=int, default=0,
                     help="images of the batch the oracle runs on (0 = auto)")
+    ap.add_argument("--only", choices=["fprop", "dgrad", "wgrad"], default=None,
+                    help="profiling aid: run only this pass (prints per-pass timing, no JSON line)")
     return ap.parse_args()
 
 
@@ -94,6 +96,23 @@ def main():
         B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)
         if ev:
             ev[3].record(stream)
+
+    if args.only:
+        run = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, 1.0, 1.0, 1.0, y, ws[0], stream=stream),
+               "dgrad": lambda: B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream),
+               "wgrad": lambda: B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)}[args.only]
+        for _ in range(args.warmup):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        fl = flops(prob, P, Q)
+        print(f"{args.only} {name}: {us:.2f} us/launch, {fl / us / 1e6:.1f} TFLOP/s", flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

@@ -130,6 +130,16 @@ int choose_igemm_tile(long long m_total, long long ngemm)
     return 2;                                                                      // 64 x 64
 }
 
+// Stride-1 problems whose source channel count and filter the band kernel
+// is built for keep the filter and a ring of input rows in LDS.
+bool band_eligible(const Dims &d, int dtype, long long cin)
+{
+    return d.G == 1 && d.sh == 1 && d.sw == 1 && d.dh == d.dw && dtype != CONV2D_DTYPE_I8 &&
+           band_supported((int)d.R, (int)d.S, (int)cin, (int)d.dh);
+}
+
+constexpr int kBandTile = 5;  // tile index of the band kernel (algo tile 6)
+
 int choose_wgrad_splits(long long tiles, long long npix)
 {
     const long long steps = (npix + kWgradPixStep - 1) / kWgradPixStep;
@@ -197,16 +207,21 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         if (s > 1) pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * ncols) * sizeof(float), 256);
         return CONV2D_OK;
     }
-    pl->num_tiles = igemm_num_tiles();
+    const bool band = band_eligible(d, dtype, op == CONV2D_OP_FPROP ? d.C : d.K);
+    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0);
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
-        pl->tile = (algo && algo->tile) ? algo->tile - 1 : choose_igemm_tile(d.N * d.P * d.Q, d.K);
+        pl->tile = (algo && algo->tile) ? algo->tile - 1
+                   : band             ? kBandTile
+                                      : choose_igemm_tile(d.N * d.P * d.Q, d.K);
         return CONV2D_OK;
     }
     // dgrad
     if (d.sh * d.sw > kMaxPhases) return CONV2D_ERR_UNSUPPORTED;
     pl->phases = (int)(d.sh * d.sw);
-    pl->tile = (algo && algo->tile) ? algo->tile - 1 : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.C);
+    pl->tile = (algo && algo->tile) ? algo->tile - 1
+               : band             ? kBandTile
+                                  : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.C);
     pl->ws_bytes = round_up((size_t)d.R * d.S * d.C * d.K * elem_size(dtype), 256);
     return CONV2D_OK;
 }
@@ -219,6 +234,31 @@ void fill_phase_common(Phase &ph, int tile)
     ph.tiles_m = (int)(((long long)ph.m_total + ts.bm - 1) / ts.bm);
     ph.div_mj = make_fastdiv((uint32_t)std::max(1, ph.mj));
     ph.div_mimj = make_fastdiv((uint32_t)std::max(1LL, (long long)ph.mi * ph.mj));
+}
+
+// Rows of one image per band workgroup: enough workgroups for every CU.
+void band_rows(BandArgs &b, long long other_wgs)
+{
+    long long chunks = (kNumCUs + b.N * other_wgs - 1) / (b.N * other_wgs);
+    chunks = std::max(1LL, std::min(chunks, (long long)b.P));
+    b.rows_per_wg = (int)((b.P + chunks - 1) / chunks);
+    b.chunks_per_img = (b.P + b.rows_per_wg - 1) / b.rows_per_wg;
+}
+
+// Stride-1 convolution src [N][H][W][cin] -> dst [N][P][Q][ngemm] on the band kernel.
+int run_band(int dtype, const Dims &d, int cin, const void *src, int H, int W, const void *bmat, int flip,
+             const void *bias, int relu, void *dst, int P, int Q, int ngemm, int pad_h, int pad_w,
+             hipStream_t s)
+{
+    BandArgs b;
+    memset(&b, 0, sizeof(b));
+    b.src = src; b.bmat = bmat; b.bias = bias; b.dst = dst;
+    b.N = (int)d.N; b.H = H; b.W = W; b.P = P; b.Q = Q; b.ngemm = ngemm;
+    b.pad_h = pad_h; b.pad_w = pad_w; b.flip = flip; b.relu = relu;
+    const int seg = 64 - (int)(d.dw * (d.S - 1));
+    const int gn = (ngemm + 63) / 64, gq = (Q + seg - 1) / seg;
+    band_rows(b, (long long)gn * gq);
+    return hip_status(launch_band(dtype, (int)d.R, (int)d.S, cin, (int)d.dh, b, gn, gq, s));
 }
 
 }  // namespace
@@ -308,6 +348,10 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
         a.total = d.N * d.P * d.Q * d.K;
         return hip_status(launch_direct_fprop(dtype, a, s));
     }
+
+    if (pl.tile == kBandTile)
+        return run_band(dtype, d, (int)d.C, x, (int)d.H, (int)d.W, w, 0, bias, relu, y, (int)d.P, (int)d.Q,
+                        (int)d.K, (int)d.ph, (int)d.pw, s);
 
     IgemmArgs a;
     memset(&a, 0, sizeof(a));
@@ -399,6 +443,9 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
     if (nph == 0) return CONV2D_OK;
     hipError_t e = launch_dgrad_prep(dtype, pa, s);
     if (e != hipSuccess) return CONV2D_ERR_DEVICE;
+    if (pl.tile == kBandTile)  // stride 1: one phase holding every tap, read reversed
+        return run_band(dtype, d, (int)d.K, dy, (int)d.P, (int)d.Q, workspace, 1, nullptr, 0, dx, (int)d.H,
+                        (int)d.W, (int)d.C, (int)(d.dh * (d.R - 1) - d.ph), (int)(d.dw * (d.S - 1) - d.pw), s);
     TileShape ts = igemm_tile_shape(pl.tile);
     const int gn = (int)((d.C + ts.bn - 1) / ts.bn);
     return hip_status(launch_igemm(dtype, pl.tile, a, max_tiles, gn, s));

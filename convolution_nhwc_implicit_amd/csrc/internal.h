@@ -95,6 +95,26 @@ TileShape igemm_tile_shape(int tile);
 hipError_t launch_igemm(int dtype, int tile, const IgemmArgs &a, int grid_m, int grid_n,
                         hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// Stride-1 band kernel (band.hip): filter and a ring of input rows in LDS.
+// src [N][H][W][CIN] -> dst [N][P][Q][ngemm] with P = H + 2*pad_h - dil*(R-1)
+// (likewise Q); pad_h / pad_w may be negative.  bmat is [ngemm][R*S*CIN]; with
+// flip set, its taps are read in reverse order (dgrad).
+// ---------------------------------------------------------------------------
+struct BandArgs {
+    const void *src;
+    const void *bmat;
+    const void *bias;
+    void *dst;
+    int N, H, W, P, Q, ngemm;
+    int pad_h, pad_w;
+    int flip, relu;
+    int rows_per_wg, chunks_per_img;
+};
+bool band_supported(int R, int S, int cin, int dil);
+hipError_t launch_band(int dtype, int R, int S, int cin, int dil, const BandArgs &a, int grid_n, int grid_q,
+                       hipStream_t st);
+
 // Re-lays the filter w[K][R][S][C] out as one dense [C][taps*K] matrix per
 // dgrad stride phase (taps of the phase in (jr, js) order, K innermost).
 struct PrepPhase {

@@ -56,6 +56,17 @@ CASES = [
     ("depthwise", problem(2, 8, 10, 9, 8, 3, 3, pad=(1, 1), groups=8), "f16", "int", True, False),
     ("grouped_gauss", problem(2, 24, 11, 11, 24, 3, 3, pad=(1, 1), groups=3), "bf16", "gauss",
      True, False),
+    # stride-1 problems with 64 source channels and a 3x3 filter run on the
+    # band kernel (filter + ring of input rows in LDS): two column segments,
+    # partial N tiles, one-row and multi-group row ranges, padding 0..3
+    ("band_two_segments", problem(3, 64, 21, 70, 64, 3, 3, pad=(1, 1)), "f16", "int", True, True),
+    ("band_ntail", problem(2, 64, 19, 33, 72, 3, 3, pad=(1, 1)), "bf16", "int", True, False),
+    ("band_multigroup", problem(100, 64, 30, 6, 64, 3, 3, pad=(1, 1)), "f16", "int", True, False),
+    ("band_pad0", problem(2, 64, 12, 12, 64, 3, 3), "f16", "int", False, False),
+    ("band_pad2", problem(2, 64, 9, 9, 64, 3, 3, pad=(2, 2)), "f16", "int", True, False),
+    ("band_pad3", problem(2, 64, 8, 8, 64, 3, 3, pad=(3, 3)), "f16", "int", False, False),
+    ("band_gauss", problem(8, 64, 28, 28, 64, 3, 3, pad=(1, 1)), "f16", "gauss", True, True),
+    ("band_bf16_gauss", problem(4, 64, 17, 23, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
 ]
 
 
@@ -103,6 +114,20 @@ def test_every_fprop_and_dgrad_tile_matches_oracle():
     for t in range(1, n + 1):
         algo = dict(tile=t)
         check(f64(run_fprop(prob, "f16", x, w, b, True, algo=algo)), ref_y, "f16", "exact", f"tile {t}")
+        check(f64(run_dgrad(prob, "f16", dy, w, algo=algo)), ref_dx, "f16", "exact", f"dgrad tile {t}")
+
+
+def test_every_tile_on_band_eligible_problem():
+    prob = problem(3, 64, 14, 13, 64, 3, 3, pad=(1, 1))
+    x, w, b, dy = case_inputs(prob, "f16", "int", seed=48)
+    ref_y = oracle_fprop_out(prob, "f16", x, w, b, False)
+    ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
+    info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")
+    assert info["num_tiles"] == 6 and info["tile"] == 5  # the band kernel is the default
+    assert B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16")["tile"] == 5
+    for t in range(1, info["num_tiles"] + 1):
+        algo = dict(tile=t)
+        check(f64(run_fprop(prob, "f16", x, w, b, False, algo=algo)), ref_y, "f16", "exact", f"tile {t}")
         check(f64(run_dgrad(prob, "f16", dy, w, algo=algo)), ref_dx, "f16", "exact", f"dgrad tile {t}")
 
 
