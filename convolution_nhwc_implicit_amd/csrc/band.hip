@@ -18,9 +18,11 @@
 //     finished output row (bias, ReLU, rounding applied), which then leaves as
 //     fully coalesced 128-bit stores; the prefetched rows go into the same
 //     slots afterwards;
-//   * 16-byte channel chunks inside each pixel are XOR-swizzled by the pixel
-//     index, so the 32 consecutive pixels of an operand fragment read
-//     conflict-free; filter rows are padded by 16 bytes for the same reason.
+//   * the LDS has 64 four-byte banks and serves 16 lanes of a 128-bit read per
+//     cycle.  A 128-byte pixel covers half of the banks, so the 16-byte channel
+//     chunks of pixel `col` are XOR-swizzled by col/2: any 16 consecutive
+//     pixels of an operand fragment (at any tap shift) then hit all 64 banks.
+//     Filter rows are padded by 16 bytes, which does the same for them.
 //
 // The same kernel runs stride-1 dgrad: the source is dy, the padding is
 // dil*(R-1) - pad, and the filter (re-laid out as [C][R*S*K]) is read with its
@@ -75,7 +77,7 @@ struct BandCfg {
     static constexpr int NEW_CHUNKS = GROUP_ROWS * ROW_CHUNKS;
     static constexpr int CPR = ROW_CHUNKS / NT;         // chunks per thread per ring row
     static constexpr int NEW_CPT = GROUP_ROWS * CPR;    // prefetch chunks per thread
-    static constexpr int SWZ = (NCH >= 8 ? 8 : NCH) - 1;
+    static constexpr int SWZ = (NCH >= 8 ? 8 : NCH) - 1;  // applied to col / 2
     static_assert(ROW_CHUNKS % NT == 0, "a ring row is a whole number of chunks per thread");
     static constexpr int OUT_PIXB = BN * 2;             // staged output pixel (BN channels)
     static_assert(SEG * OUT_PIXB <= SLOTB, "a wave's output row fits in one ring slot");
@@ -106,20 +108,6 @@ __global__ __launch_bounds__(512, 1) void band_kernel(const BandArgs a)
     const elem *src = (const elem *)a.src + (size_t)img * a.H * a.W * CIN;
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    // ---- filter tile -> LDS (taps reversed for dgrad)
-    {
-        constexpr int CH_PER_ROW = C::KG / 8;
-        for (int id = tid; id < C::BN * CH_PER_ROW; id += C::NT) {
-            const int n = id / CH_PER_ROW, kc = id - n * CH_PER_ROW;
-            const int tap = kc / (CIN / 8), cc = kc - tap * (CIN / 8);
-            const int stap = a.flip ? (R * S - 1 - tap) : tap;
-            u32x4 v = zero;
-            if (n0 + n < a.ngemm)
-                v = *(const u32x4 *)((const elem *)a.bmat + (size_t)(n0 + n) * C::KG + stap * CIN + cc * 8);
-            *(u32x4 *)(filt + n * C::FROWB + kc * 16) = v;
-        }
-    }
-
     // ---- ring rows.  Thread t always moves the same (column, channel chunk)
     // positions of a row: chunk t + i*256 of the row's RCOLS*NCH chunks, so
     // a row costs CPR loads per thread and the addresses are a base plus
@@ -128,8 +116,8 @@ __global__ __launch_bounds__(512, 1) void band_kernel(const BandArgs a)
     const int my_col = tid / C::NCH;  // + i * (NT / NCH) for the i-th chunk of a row
     constexpr int COL_STEP = C::NT / C::NCH;
     const elem *my_src = src + (size_t)my_j * 8;
-    const int my_swz = ((my_j ^ (my_col & C::SWZ)) * 16) + my_col * C::PIXB;
-    static_assert((COL_STEP & C::SWZ) == 0, "column step keeps the swizzle phase");
+    const int my_swz = ((my_j ^ ((my_col >> 1) & C::SWZ)) * 16) + my_col * C::PIXB;
+    static_assert(((COL_STEP >> 1) & C::SWZ) == 0 && COL_STEP % 2 == 0, "column step keeps the swizzle phase");
     auto load_row_chunk = [&](int hrel, int i) -> u32x4 {
         const int h = h_base + hrel, w = w_base + my_col + i * COL_STEP;
         if ((unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W)
@@ -138,11 +126,6 @@ __global__ __launch_bounds__(512, 1) void band_kernel(const BandArgs a)
     };
     auto ring_chunk = [&](int hrel, int i) -> u32x4 * {
         return (u32x4 *)(ring + (hrel % C::NSLOT) * C::SLOTB + my_swz + i * COL_STEP * C::PIXB);
-    };
-    auto load_rows_sync = [&](int r0, int n) {
-        for (int rr = 0; rr < n; ++rr)
-#pragma unroll
-            for (int i = 0; i < C::CPR; ++i) *ring_chunk(r0 + rr, i) = load_row_chunk(r0 + rr, i);
     };
     u32x4 pre[C::NEW_CPT];
     auto prefetch = [&](int r0) {
@@ -158,14 +141,51 @@ __global__ __launch_bounds__(512, 1) void band_kernel(const BandArgs a)
             for (int i = 0; i < C::CPR; ++i) *ring_chunk(r0 + rr, i) = pre[rr * C::CPR + i];
     };
 
-    // prologue: halo rows, then group 0's rows
-    if (C::HALO_R > 0) load_rows_sync(0, C::HALO_R);
-    prefetch(C::HALO_R);
-    commit(C::HALO_R);
+    // ---- prologue: the filter tile (taps reversed for dgrad), the halo rows
+    // and group 0's rows are all requested before any of them is waited for
+    constexpr int F_CHUNKS = C::BN * C::KG / 8;
+    constexpr int F_CPT = (F_CHUNKS + C::NT - 1) / C::NT;
+    {
+        u32x4 freg[F_CPT];
+#pragma unroll
+        for (int i = 0; i < F_CPT; ++i) {
+            const int id = tid + i * C::NT;
+            const int n = id / (C::KG / 8), kc = id - n * (C::KG / 8);
+            const int tap = kc / (CIN / 8), cc = kc - tap * (CIN / 8);
+            const int stap = a.flip ? (R * S - 1 - tap) : tap;
+            freg[i] = zero;
+            if (id < F_CHUNKS && n0 + n < a.ngemm)
+                freg[i] = *(const u32x4 *)((const elem *)a.bmat + (size_t)(n0 + n) * C::KG + stap * CIN + cc * 8);
+        }
+        u32x4 hreg[C::HALO_R * C::CPR > 0 ? C::HALO_R * C::CPR : 1];
+#pragma unroll
+        for (int rr = 0; rr < C::HALO_R; ++rr)
+#pragma unroll
+            for (int i = 0; i < C::CPR; ++i) hreg[rr * C::CPR + i] = load_row_chunk(rr, i);
+        prefetch(C::HALO_R);
+#pragma unroll
+        for (int i = 0; i < F_CPT; ++i) {
+            const int id = tid + i * C::NT;
+            const int n = id / (C::KG / 8), kc = id - n * (C::KG / 8);
+            if (id < F_CHUNKS) *(u32x4 *)(filt + n * C::FROWB + kc * 16) = freg[i];
+        }
+#pragma unroll
+        for (int rr = 0; rr < C::HALO_R; ++rr)
+#pragma unroll
+            for (int i = 0; i < C::CPR; ++i) *ring_chunk(rr, i) = hreg[rr * C::CPR + i];
+        commit(C::HALO_R);
+    }
     __syncthreads();
 
     const int ngroups = (p_end - p_start + C::GROUP_ROWS - 1) / C::GROUP_ROWS;
     const int l32 = lane & 31, lhi = lane >> 5;
+    const unsigned char *fbase = filt + l32 * C::FROWB + lhi * 16;
+    float bias_v[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int ch = n0 + n * 32 + l32;
+        bias_v[n] = (a.bias && ch < a.ngemm) ? E::to_f32(((const elem *)a.bias)[ch]) : 0.0f;
+    }
 
     for (int g = 0; g < ngroups; ++g) {
         const bool more = g + 1 < ngroups;
@@ -180,39 +200,55 @@ __global__ __launch_bounds__(512, 1) void band_kernel(const BandArgs a)
 #pragma unroll
             for (int n = 0; n < 2; ++n) acc[m][n] = f32x16{};
         if (active) {
-            // k16 steps in (tap, channel) order; fragments of step ks+1 are
-            // loaded while the MFMAs of step ks run
+            // Taps in a rolled loop, the CIN/16 channel steps of a tap
+            // unrolled.  Two fragment buffers: while the MFMAs of one step
+            // issue, the reads of the next step are interleaved between them
+            // (one LDS read per MFMA); the first step of the next tap is read
+            // during the last step of this one (at the last tap it re-reads
+            // the same tap, so every read stays unconditional).
             constexpr int C16 = CIN / 16;
-            constexpr int KS = R * S * C16;
-            const unsigned char *fbase = filt + l32 * C::FROWB + lhi * 16;
-            auto load_frags = [&](int ks, u32x4 (&fa)[2], u32x4 (&fb)[2]) {
-                const int tap = ks / C16, c16 = ks - tap * C16;
-                const int r = tap / S, s = tap - r * S;
-                const int j = 2 * c16 + lhi;
+            static_assert(C16 % 2 == 0, "even channel steps per tap");
+            u32x4 fa0[2], fb0[2], fa1[2], fb1[2];
+            auto load_frags = [&](int tap, int c16, u32x4 (&A)[2], u32x4 (&Bf)[2]) {
+                const int r = tap / S, sx = tap - r * S;
                 const unsigned char *rowp = ring + ((pr + r * DIL) % C::NSLOT) * C::SLOTB;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int col = h * 32 + l32 + s * DIL;
-                    fa[h] = *(const u32x4 *)(rowp + col * C::PIXB + ((j ^ (col & C::SWZ)) * 16));
+                    const int col = h * 32 + l32 + sx * DIL;
+                    A[h] = *(const u32x4 *)(rowp + col * C::PIXB +
+                                            (((2 * c16 + lhi) ^ ((col >> 1) & C::SWZ)) << 4));
                 }
-#pragma unroll
-                for (int n = 0; n < 2; ++n)
-                    fb[n] = *(const u32x4 *)(fbase + n * 32 * C::FROWB + ks * 32);
+                const unsigned char *fp = fbase + tap * CIN * 2 + c16 * 32;
+                Bf[0] = *(const u32x4 *)(fp);
+                Bf[1] = *(const u32x4 *)(fp + 32 * C::FROWB);
             };
-            u32x4 fa[2], fb[2];
-            load_frags(0, fa, fb);
-#pragma unroll 2
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 na[2], nb[2];
-                if (ks + 1 < KS) load_frags(ks + 1, na, nb);
+            auto mma = [&](const u32x4 (&A)[2], const u32x4 (&Bf)[2], bool interleave) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) acc[m][n] = Mfma32<E>::run(fa[m], fb[n], acc[m][n]);
-                fa[0] = na[0];
-                fa[1] = na[1];
-                fb[0] = nb[0];
-                fb[1] = nb[1];
+                    for (int n = 0; n < 2; ++n) acc[m][n] = Mfma32<E>::run(A[m], Bf[n], acc[m][n]);
+                if (interleave) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // one LDS read
+                        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // one MFMA
+                    }
+                }
+            };
+            load_frags(0, 0, fa0, fb0);
+#pragma unroll 1
+            for (int tap = 0; tap < R * S; ++tap) {
+                const int next = tap + 1 < R * S ? tap + 1 : tap;
+#pragma unroll
+                for (int c16 = 0; c16 < C16; c16 += 2) {
+                    load_frags(tap, c16 + 1, fa1, fb1);
+                    mma(fa0, fb0, true);
+                    if (c16 + 2 < C16)
+                        load_frags(tap, c16 + 2, fa0, fb0);
+                    else
+                        load_frags(next, 0, fa0, fb0);
+                    mma(fa1, fb1, true);
+                }
             }
         }
         __syncthreads();  // every wave is done reading this group's ring rows
@@ -225,8 +261,7 @@ __global__ __launch_bounds__(512, 1) void band_kernel(const BandArgs a)
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 const int chl = n * 32 + l32;
-                const int ch = n0 + chl;
-                const float b = (a.bias && ch < a.ngemm) ? E::to_f32(((const elem *)a.bias)[ch]) : 0.0f;
+                const float b = bias_v[n];
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -238,22 +273,33 @@ __global__ __launch_bounds__(512, 1) void band_kernel(const BandArgs a)
             }
         }
         __syncthreads();
-        if (active) {
-            // the wave's row: SEG columns x BN channels, 16 bytes per lane
-            const int p = p_start + pr;
-            elem *drow = (elem *)a.dst + ((size_t)img * a.P + p) * a.Q * a.ngemm;
-            constexpr int CPP = C::OUT_PIXB / 16;  // 16-byte chunks per pixel
-            for (int id = lane; id < C::SEG * CPP; id += 64) {
-                const int ql = id / CPP, cc = id - ql * CPP;
-                const int q = q0 + ql, ch = n0 + cc * 8;
-                if (q < a.Q && ch < a.ngemm)
-                    *(u32x4 *)(drow + (size_t)q * a.ngemm + ch) = *(const u32x4 *)(stage + ql * C::OUT_PIXB + cc * 16);
-            }
+        // read the staged row back (SEG columns x BN channels, 16 bytes per
+        // lane), free the slots for the prefetched rows, then store
+        constexpr int CPP = C::OUT_PIXB / 16;  // 16-byte chunks per pixel
+        constexpr int OUT_CPL = (C::SEG * CPP + 63) / 64;
+        u32x4 outv[OUT_CPL];
+#pragma unroll
+        for (int i = 0; i < OUT_CPL; ++i) {
+            const int id = lane + i * 64;
+            const int ql = id / CPP, cc = id - ql * CPP;
+            outv[i] = (active && id < C::SEG * CPP) ? *(const u32x4 *)(stage + ql * C::OUT_PIXB + cc * 16) : zero;
         }
         __syncthreads();  // staged outputs are read back; the slots are free
         if (more) {
             commit((g + 1) * C::GROUP_ROWS + C::HALO_R);
             __syncthreads();
+        }
+        if (active) {
+            const int p = p_start + pr;
+            elem *drow = (elem *)a.dst + ((size_t)img * a.P + p) * a.Q * a.ngemm;
+#pragma unroll
+            for (int i = 0; i < OUT_CPL; ++i) {
+                const int id = lane + i * 64;
+                const int ql = id / CPP, cc = id - ql * CPP;
+                const int q = q0 + ql, ch = n0 + cc * 8;
+                if (id < C::SEG * CPP && q < a.Q && ch < a.ngemm)
+                    *(u32x4 *)(drow + (size_t)q * a.ngemm + ch) = outv[i];
+            }
         }
     }
 }
