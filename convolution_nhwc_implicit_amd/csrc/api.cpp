@@ -140,6 +140,25 @@ bool band_eligible(const Dims &d, int dtype, long long cin)
 
 constexpr int kBandTile = 5;  // tile index of the band kernel (algo tile 6)
 
+// Stride-1 wgrad with the filter shape and channel counts the wgrad band
+// kernel is built for.
+bool wgrad_band_eligible(const Dims &d, int dtype)
+{
+    return d.G == 1 && d.sh == 1 && d.sw == 1 && d.dh == d.dw && dtype != CONV2D_DTYPE_I8 &&
+           wgrad_band_supported((int)d.R, (int)d.S, (int)d.C, (int)d.K, (int)d.dh, (int)d.Q);
+}
+
+constexpr int kWgradBandTile = 1;  // wgrad tile index of the band kernel (algo tile 2)
+
+// Output rows per wgrad band workgroup: about one workgroup per CU.
+void wgrad_band_rows(const Dims &d, int *rows, int *chunks)
+{
+    long long c = (kNumCUs + d.N - 1) / d.N;
+    c = std::max(1LL, std::min(c, d.P));
+    *rows = (int)((d.P + c - 1) / c);
+    *chunks = (int)((d.P + *rows - 1) / *rows);
+}
+
 int choose_wgrad_splits(long long tiles, long long npix)
 {
     const long long steps = (npix + kWgradPixStep - 1) / kWgradPixStep;
@@ -194,11 +213,23 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     if (d.C % vec || d.K % vec) return CONV2D_ERR_UNSUPPORTED;
     pl->kernel = 1;
     if (op == CONV2D_OP_WGRAD) {
-        pl->num_tiles = wgrad_num_tiles();
+        const bool wband = wgrad_band_eligible(d, dtype);
+        pl->num_tiles = wgrad_num_tiles() + (wband ? 1 : 0);
         if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
+        // default: the band kernel when it applies and no split count is forced
+        const bool use_band = algo && algo->tile ? algo->tile - 1 == kWgradBandTile
+                                                  : wband && !(algo && algo->split_k);
+        const long long ncols = d.R * d.S * d.C;
+        if (use_band) {
+            pl->tile = kWgradBandTile;
+            int rows, chunks;
+            wgrad_band_rows(d, &rows, &chunks);
+            pl->split_k = (int)(d.N * chunks);
+            pl->ws_bytes = round_up((size_t)pl->split_k * splitk_stride(d.K * ncols) * sizeof(float), 256);
+            return CONV2D_OK;
+        }
         pl->tile = (algo && algo->tile) ? algo->tile - 1 : 0;
         TileShape ts = wgrad_tile_shape(pl->tile);
-        const long long ncols = d.R * d.S * d.C;
         const long long tiles = ((d.K + ts.bm - 1) / ts.bm) * ((ncols + ts.bn - 1) / ts.bn);
         const long long npix = d.N * d.P * d.Q;
         int s = (algo && algo->split_k) ? algo->split_k : choose_wgrad_splits(tiles, npix);
@@ -482,6 +513,20 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
         if (e != hipSuccess || pl.split_k == 1) return hip_status(e);
         return hip_status(
             launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k, a.total, a.part_stride, dw, s));
+    }
+
+    if (pl.tile == kWgradBandTile) {
+        WgradBandArgs b;
+        memset(&b, 0, sizeof(b));
+        b.x = x; b.dy = dy; b.out = workspace;
+        b.N = (int)d.N; b.H = (int)d.H; b.W = (int)d.W; b.P = (int)d.P; b.Q = (int)d.Q;
+        b.pad_h = (int)d.ph; b.pad_w = (int)d.pw;
+        wgrad_band_rows(d, &b.rows_per_wg, &b.chunks_per_img);
+        b.part_stride = splitk_stride(d.K * d.R * d.S * d.C);
+        hipError_t e = launch_wgrad_band(dtype, b, s);
+        if (e != hipSuccess) return CONV2D_ERR_DEVICE;
+        return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,
+                                               d.K * d.R * d.S * d.C, b.part_stride, dw, s));
     }
 
     WgradArgs a;

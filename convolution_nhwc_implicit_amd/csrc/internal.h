@@ -163,6 +163,23 @@ hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long 
 inline long long splitk_stride(long long count) { return (count + 3) / 4 * 4; }
 
 // ---------------------------------------------------------------------------
+// Stride-1 wgrad band kernel (wgrad_band.hip): dy and x rows in LDS rings,
+// transposing LDS reads.  One workgroup per (image, band of rows_per_wg output
+// rows); each writes fp32 partials [K][R*S*C] at out + workgroup * part_stride.
+// ---------------------------------------------------------------------------
+struct WgradBandArgs {
+    const void *x;
+    const void *dy;
+    void *out;
+    int N, H, W, P, Q;
+    int pad_h, pad_w;
+    int rows_per_wg, chunks_per_img;
+    long long part_stride;
+};
+bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q);
+hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Direct convolution for groups > 1: one thread per output element, fp32
 // (int32 for int8) accumulation in a fixed (r, s, channel) order.
 // ---------------------------------------------------------------------------

@@ -166,32 +166,66 @@ hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st)
 }
 
 // ---------------------------------------------------------------------------
-// out[i] = round(sum_{z = 0..splits-1} parts[z*stride + i]), summed in slice
-// order in fp32, four elements per thread.  stride is a multiple of 4 and at
-// least count, so the 128-bit partial loads stay inside slice z; the last
-// thread stores only the elements below count.
+// out[i] = round(sum over slices z of parts[z*stride + i]) in fp32, in a fixed
+// order: the slices are split into 16 classes z % 16; each class is summed in
+// ascending z, then the 16 class sums are added in ascending class order.
+// A workgroup owns 64 consecutive elements: thread (class c, lane e) reads
+// elements 4e..4e+3 of every slice of class c with 128-bit loads (16 lanes of
+// one slice read 256 contiguous bytes), and the class sums meet in LDS.
+// stride is a multiple of 4 and at least count; the last workgroup's lanes
+// past count read inside the slice padding and store nothing.
 // ---------------------------------------------------------------------------
 template <class E>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *parts, int splits, long long count,
                                                             long long stride, typename E::elem *out)
 {
-    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= count) return;
-    f32x4 s = *(const f32x4 *)(parts + i);
-    for (int z = 1; z < splits; ++z) {
-        const f32x4 v = *(const f32x4 *)(parts + (size_t)z * stride + i);
-        s[0] += v[0];
-        s[1] += v[1];
-        s[2] += v[2];
-        s[3] += v[3];
-    }
-    typename E::elem o[4];
+    constexpr int NCLS = 16;
+    __shared__ f32x4 part[NCLS][16];
+    const int cls = threadIdx.x >> 4, e = threadIdx.x & 15;
+    const long long i = (long long)blockIdx.x * 64 + e * 4;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if (i < stride) {
+        const float *p = parts + i;
+        int z = cls;
+        for (; z + 7 * NCLS < splits; z += 8 * NCLS) {
+            f32x4 v[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = E::from_f32(s[j]);
-    if (i + 4 <= count) {
-        *(uint2 *)(out + i) = *(const uint2 *)o;
-    } else {
-        for (int j = 0; j < 4 && i + j < count; ++j) out[i + j] = o[j];
+            for (int u = 0; u < 8; ++u) v[u] = *(const f32x4 *)(p + (size_t)(z + u * NCLS) * stride);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                s[0] += v[u][0];
+                s[1] += v[u][1];
+                s[2] += v[u][2];
+                s[3] += v[u][3];
+            }
+        }
+        for (; z < splits; z += NCLS) {
+            const f32x4 v = *(const f32x4 *)(p + (size_t)z * stride);
+            s[0] += v[0];
+            s[1] += v[1];
+            s[2] += v[2];
+            s[3] += v[3];
+        }
+    }
+    part[cls][e] = s;
+    __syncthreads();
+    if (cls == 0 && i < count) {
+        f32x4 t = part[0][e];
+        for (int c = 1; c < NCLS; ++c) {
+            const f32x4 v = part[c][e];
+            t[0] += v[0];
+            t[1] += v[1];
+            t[2] += v[2];
+            t[3] += v[3];
+        }
+        typename E::elem o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = E::from_f32(t[j]);
+        if (i + 4 <= count) {
+            *(uint2 *)(out + i) = *(const uint2 *)o;
+        } else {
+            for (int j = 0; j < 4 && i + j < count; ++j) out[i + j] = o[j];
+        }
     }
 }
 
@@ -199,8 +233,7 @@ hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long 
                                 long long stride, void *out, hipStream_t st)
 {
     if (stride % 4 || stride < count) return hipErrorInvalidValue;
-    const long long threads = (count + 3) / 4;
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    const unsigned blocks = (unsigned)((count + 63) / 64);
     if (blocks == 0) return hipSuccess;
     switch (dtype) {
     case CONV2D_DTYPE_F16:

@@ -67,6 +67,13 @@ CASES = [
     ("band_pad3", problem(2, 64, 8, 8, 64, 3, 3, pad=(3, 3)), "f16", "int", False, False),
     ("band_gauss", problem(8, 64, 28, 28, 64, 3, 3, pad=(1, 1)), "f16", "gauss", True, True),
     ("band_bf16_gauss", problem(4, 64, 17, 23, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
+    # wgrad band kernel (stride 1, 3x3, C = K = 64, Q % 4 == 0, Q <= 64):
+    # two row groups with a partial last group, and one-row bands whose pixel
+    # count is not a multiple of 16
+    ("wband_groups", problem(64, 64, 30, 8, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
+    ("wband_masked", problem(2, 64, 12, 12, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
+    ("wband_bf16", problem(16, 64, 20, 20, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
+    ("wband_wide", problem(4, 64, 9, 64, 64, 3, 3, pad=(1, 1)), "f16", "int", True, True),
 ]
 
 
@@ -139,6 +146,16 @@ def test_int8_every_tile():
     for t in range(1, B.conv2d_plan_info(0, prob, "i8")["num_tiles"] + 1):
         y = run_fprop(prob, "i8", x, w, b, True, scales=scales, algo=dict(tile=t))
         assert np.array_equal(y.cpu().numpy().reshape(-1), exp), f"tile {t}"
+
+
+def test_wgrad_band_and_generic_agree():
+    prob = problem(8, 64, 18, 16, 64, 3, 3, pad=(1, 1))
+    x, _, _, dy = case_inputs(prob, "f16", "int", seed=49)
+    ref = oracle.wgrad(prob, f64(x), f64(dy))
+    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
+    assert info["num_tiles"] == 2 and info["tile"] == 1  # band kernel is the default
+    for t in (1, 2):
+        check(f64(run_wgrad(prob, "f16", x, dy, algo=dict(tile=t))), ref, "f16", "exact", f"wgrad tile {t}")
 
 
 @pytest.mark.parametrize("groups", [1, 2])
