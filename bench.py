@@ -29,6 +29,35 @@ METRIC = "conv2d TFLOP/s (fprop/dgrad/wgrad) and % of MFMA peak, 56x56x64 3x3 fp
 # FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s), int8 5.03 POP/s, HBM3E 8 TB/s.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2}
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 64 << 20  # reference copy for the HBM byte counters
+# Measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by
+# the same counters on a plain copy) lives in this summary, keyed by a hash of
+# the kernel sources it was measured on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3a_hbm_traffic.json")
+KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "convolution_nhwc_implicit_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(pass_name):
+    """HBM bytes per launch of a pass from the committed counter summary, or
+    None when it is absent or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    p = t.get("passes", {}).get(pass_name)
+    return None if p is None else p.get("hbm_bytes")
 
 
 def parse():
@@ -40,8 +69,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-images", type=int, default=0,
                     help="images of the batch the oracle runs on (0 = auto)")
-    ap.add_argument("--only", choices=["fprop", "dgrad", "wgrad"], default=None,
-                    help="profiling aid: run only this pass (prints per-pass timing, no JSON line)")
+    ap.add_argument("--only", choices=["fprop", "dgrad", "wgrad", "copy"], default=None,
+                    help="profiling aid: run only this pass (prints its timing, no JSON line); "
+                         "'copy' runs a plain 64 MiB device copy, the reference for HBM byte counters")
     return ap.parse_args()
 
 
@@ -97,6 +127,22 @@ def main():
         if ev:
             ev[3].record(stream)
 
+    if args.only == "copy":
+        src_t = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst_t = torch.empty_like(src_t)
+        # one elementwise kernel that reads COPY_BYTES and writes COPY_BYTES
+        for _ in range(args.warmup):
+            torch.neg(src_t, out=dst_t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            torch.neg(src_t, out=dst_t)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        print(f"copy {COPY_BYTES} B: {us:.2f} us/launch, {2 * COPY_BYTES / us / 1e3:.1f} GB/s", flush=True)
+        return
     if args.only:
         run = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, 1.0, 1.0, 1.0, y, ws[0], stream=stream),
                "dgrad": lambda: B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream),
@@ -162,7 +208,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": d["alg_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(d["alg_gbs"] / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["per_launch"] = {"flop": fl, "alg_bytes": alg_bytes[dom], "avg_us": d["us_mean"]}
 
