@@ -132,10 +132,12 @@ int choose_igemm_tile(long long m_total, long long ngemm)
 
 // Stride-1 problems whose source channel count and filter the band kernel
 // is built for keep the filter and a ring of input rows in LDS.
-bool band_eligible(const Dims &d, int dtype, long long cin)
+bool band_eligible(const Dims &d, int dtype, long long cin, long long src_h, long long src_w, long long ngemm)
 {
+    // buffer offsets are 32-bit: one source image and the filter stay under 1 GiB
     return d.G == 1 && d.sh == 1 && d.sw == 1 && d.dh == d.dw && dtype != CONV2D_DTYPE_I8 &&
-           band_supported((int)d.R, (int)d.S, (int)cin, (int)d.dh);
+           band_supported((int)d.R, (int)d.S, (int)cin, (int)d.dh) && src_h * src_w * cin * 2 < (1LL << 30) &&
+           d.R * d.S * cin * ngemm * 2 < (1LL << 30);
 }
 
 constexpr int kBandTile = 5;  // tile index of the band kernel (algo tile 6)
@@ -238,7 +240,8 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         if (s > 1) pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * ncols) * sizeof(float), 256);
         return CONV2D_OK;
     }
-    const bool band = band_eligible(d, dtype, op == CONV2D_OP_FPROP ? d.C : d.K);
+    const bool band = op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K)
+                                            : band_eligible(d, dtype, d.K, d.P, d.Q, d.C);
     pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0);
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
@@ -253,7 +256,8 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     pl->tile = (algo && algo->tile) ? algo->tile - 1
                : band             ? kBandTile
                                   : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.C);
-    pl->ws_bytes = round_up((size_t)d.R * d.S * d.C * d.K * elem_size(dtype), 256);
+    // the band kernel reads the filter as it is; the others take a re-laid-out copy
+    pl->ws_bytes = pl->tile == kBandTile ? 0 : round_up((size_t)d.R * d.S * d.C * d.K * elem_size(dtype), 256);
     return CONV2D_OK;
 }
 
@@ -431,6 +435,10 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
         return hip_status(launch_direct_dgrad(dtype, a, s));
     }
 
+    if (pl.tile == kBandTile)  // stride 1: every tap, filter read reversed and transposed
+        return run_band(dtype, d, (int)d.K, dy, (int)d.P, (int)d.Q, w, 1, nullptr, 0, dx, (int)d.H, (int)d.W,
+                        (int)d.C, (int)(d.dh * (d.R - 1) - d.ph), (int)(d.dw * (d.S - 1) - d.pw), s);
+
     // One GEMM per stride phase (h mod sh, w mod sw), one launch for all.
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
@@ -474,9 +482,6 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
     if (nph == 0) return CONV2D_OK;
     hipError_t e = launch_dgrad_prep(dtype, pa, s);
     if (e != hipSuccess) return CONV2D_ERR_DEVICE;
-    if (pl.tile == kBandTile)  // stride 1: one phase holding every tap, read reversed
-        return run_band(dtype, d, (int)d.K, dy, (int)d.P, (int)d.Q, workspace, 1, nullptr, 0, dx, (int)d.H,
-                        (int)d.W, (int)d.C, (int)(d.dh * (d.R - 1) - d.ph), (int)(d.dw * (d.S - 1) - d.pw), s);
     TileShape ts = igemm_tile_shape(pl.tile);
     const int gn = (int)((d.C + ts.bn - 1) / ts.bn);
     return hip_status(launch_igemm(dtype, pl.tile, a, max_tiles, gn, s));

@@ -1,37 +1,44 @@
-// band.hip -- stride-1 implicit-GEMM convolution with the whole filter and a
-// ring of input rows resident in LDS (gfx950).
+// band.hip -- stride-1 implicit-GEMM convolution with the filter held in
+// registers and a ring of input rows in LDS filled by direct-to-LDS loads
+// (gfx950).
 //
-// For a stride-1 convolution every input pixel feeds R*S output pixels.  The
-// generic implicit-GEMM kernel gathers each GEMM row from memory once per tap;
-// this kernel instead keeps a band of input rows in LDS and forms all R*S
-// tap-shifted operand fragments from it, so each input byte leaves HBM once.
-// The filter ([Ngemm-tile 64][R*S*CIN]) stays in LDS for the life of the
-// workgroup, which walks a contiguous range of output rows of one image:
+// For a stride-1 convolution every input pixel feeds R*S output pixels.  This
+// kernel keeps a band of input rows in LDS and forms all R*S tap-shifted
+// operand fragments from it, so each input byte leaves HBM once per
+// workgroup (plus the R-1 halo rows).  A workgroup (8 waves, two per SIMD)
+// walks a contiguous range of output rows of one image, four rows per group:
 //
-//   * a group is 8 output rows; each of the 8 waves (two per SIMD) owns one
-//     row x 64 output columns x 64 output channels (a 64x64 tile of 32x32x16
-//     MFMA blocks, fp32 accumulators);
-//   * the LDS ring holds the 8 + dil*(R-1) input rows the group reads; while a
-//     group is computed, the 8 input rows of the next group are loaded into
-//     registers;
-//   * when the group is done, the 8 ring slots only it used take each wave's
-//     finished output row (bias, ReLU, rounding applied), which then leaves as
-//     fully coalesced 128-bit stores; the prefetched rows go into the same
-//     slots afterwards;
+//   * GEMM: rows = 32 output channels per wave (the A operand, the filter),
+//     columns = 64 output pixels of one row (two 32x32x16 MFMA blocks), K =
+//     (tap, channel).  The two waves of an output row take the two 32-channel
+//     halves of the workgroup's 64 channels;
+//   * the wave's 32 x (R*S*CIN) filter slice lives in VGPRs for the whole
+//     kernel, so the only LDS reads in the main loop are the pixel fragments
+//     (half of what reading both operands from LDS would cost);
+//   * input rows arrive through buffer_load ... lds (no register staging):
+//     padding comes from the buffer range check, which returns zeros.  The
+//     rows of group g+1 are in flight while group g is computed; a group's
+//     slots are refilled with the rows of group g+2 right after its barrier;
+//   * results (bias, ReLU and rounding applied) are staged in LDS, over the
+//     filter staging area that only the prologue uses, and leave as whole
+//     128-byte pixels: stores of partial lines would multiply the number of
+//     memory requests several times;
 //   * the LDS has 64 four-byte banks and serves 16 lanes of a 128-bit read per
 //     cycle.  A 128-byte pixel covers half of the banks, so the 16-byte channel
 //     chunks of pixel `col` are XOR-swizzled by col/2: any 16 consecutive
-//     pixels of an operand fragment (at any tap shift) then hit all 64 banks.
-//     Filter rows are padded by 16 bytes, which does the same for them.
+//     pixels of a fragment (at any tap shift) then hit all 64 banks.
 //
-// The same kernel runs stride-1 dgrad: the source is dy, the padding is
-// dil*(R-1) - pad, and the filter (re-laid out as [C][R*S*K]) is read with its
-// taps reversed.
+// The same kernel runs stride-1 dgrad (TRANS): the source is dy, the padding
+// is dil*(R-1) - pad, and the filter w[K][R][S][C] is read with its taps
+// reversed and K and C swapped.  The swap is done while the filter is copied
+// from LDS into registers, with the transposing read ds_read_b64_tr_b16, so
+// dgrad needs no separate re-layout pass.
 #include "device_common.h"
 
 namespace cnv {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <class E>
 struct Mfma32;
@@ -52,255 +59,293 @@ struct Mfma32<EBF16> {
     }
 };
 
-template <int R, int S, int CIN, int DIL>
+namespace band {
+constexpr unsigned kOOB = 0x7ffffff0u;        // a buffer offset past every range: reads as zero
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (CDNA)
+
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *lds, unsigned voff)
+{
+    // lane i writes 16 bytes at lds + 16*i
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0,
+                                             0);
+}
+__device__ inline s16x4 tr16(const unsigned char *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+}
+__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+__device__ inline float relu_floor(float v, float lo, uint32_t keep)
+{
+    return v > lo ? v : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & keep);
+}
+
+template <int R, int S, int CIN, int DIL, bool TRANS>
 struct BandCfg {
     static constexpr int NT = 512;
-    static constexpr int GROUP_ROWS = 8;                // output rows per group = waves
+    static constexpr int WAVES = NT / 64;
+    static constexpr int GR = WAVES / 2;                // output rows per group (two waves each)
     static constexpr int BN = 64;                       // output channels per workgroup
     static constexpr int HALO_R = DIL * (R - 1);
     static constexpr int HALO_S = DIL * (S - 1);
-    static constexpr int NSLOT = GROUP_ROWS + HALO_R;   // ring rows
+    static constexpr int NSLOT = 2 * GR + HALO_R;       // ring rows: current group + halo + next group
     static constexpr int RCOLS = 64;                    // input columns per ring row
     static constexpr int SEG = RCOLS - HALO_S;          // output columns per workgroup
     static constexpr int NCH = CIN / 8;                 // 16-byte chunks per pixel
     static constexpr int PIXB = CIN * 2;
     static constexpr int SLOTB = RCOLS * PIXB;
     static constexpr int KG = R * S * CIN;              // GEMM-K
-    static constexpr int FROWB = KG * 2 + 16;           // padded filter row
-    static constexpr int FILT_BYTES = BN * FROWB;
+    static constexpr int C16 = CIN / 16;                // k16 steps per tap
+    static constexpr int KSTEPS = KG / 16;
+    static constexpr int PF = 3;                        // pixel-fragment reads in flight (k16 steps)
     // Fragments of the last output columns of a segment read up to HALO_S
     // pixels past a ring row (those outputs are discarded); the tail pad keeps
-    // the reads of the last slot inside the allocation.
+    // the reads of the last slot inside the ring.
     static constexpr int RING_BYTES = NSLOT * SLOTB + HALO_S * PIXB;
-    static constexpr int LDS_BYTES = FILT_BYTES + RING_BYTES;
-    static constexpr int ROW_CHUNKS = RCOLS * NCH;
-    static constexpr int NEW_CHUNKS = GROUP_ROWS * ROW_CHUNKS;
-    static constexpr int CPR = ROW_CHUNKS / NT;         // chunks per thread per ring row
-    static constexpr int NEW_CPT = GROUP_ROWS * CPR;    // prefetch chunks per thread
-    static constexpr int SWZ = (NCH >= 8 ? 8 : NCH) - 1;  // applied to col / 2
-    static_assert(ROW_CHUNKS % NT == 0, "a ring row is a whole number of chunks per thread");
-    static constexpr int OUT_PIXB = BN * 2;             // staged output pixel (BN channels)
-    static_assert(SEG * OUT_PIXB <= SLOTB, "a wave's output row fits in one ring slot");
-    static_assert(CIN % 16 == 0, "k16 steps stay inside one tap");
+    // Filter staging (prologue only): FROWS rows of FROWE elements plus a pad
+    // that makes the fragment reads conflict-free: 16 bytes for the 128-bit
+    // reads of fprop (row stride = 36 banks mod 64), 64 bytes for the
+    // transposing 64-bit reads of dgrad (48 banks mod 64).
+    static constexpr int FROWS = TRANS ? CIN : BN;
+    static constexpr int FROWE = R * S * (TRANS ? BN : CIN);
+    static constexpr int FROWB = FROWE * 2 + (TRANS ? 64 : 16);
+    static constexpr int FROWCH = FROWB / 16;
+    static constexpr int FILT_BYTES = FROWS * FROWB;
+    static constexpr int FBLOCKS = FROWS * FROWCH / 64;  // 1 KB direct-to-LDS blocks
+    // Output staging (after the prologue, over the filter staging): two
+    // buffers of GR rows x RCOLS pixels x BN channels.
+    static constexpr int OSTAGE_BYTES = GR * SLOTB;
+    static constexpr int STAGE_BYTES = FILT_BYTES > 2 * OSTAGE_BYTES ? FILT_BYTES : 2 * OSTAGE_BYTES;
+    static constexpr int BIAS_BYTES = BN * 4;
+    static constexpr int LDS_BYTES = RING_BYTES + STAGE_BYTES + BIAS_BYTES;
+    static_assert(CIN == 64 && BN == 64, "pixels of 8 chunks, two 32-channel halves");
+    static_assert(BN * 2 == PIXB, "a staged output pixel has the layout of a ring pixel");
+    static_assert(RCOLS * NCH == 64 * WAVES, "one 1 KB block of each ring row per wave");
+    static_assert(FROWS * FROWCH % 64 == 0, "the filter staging is whole 1 KB blocks");
+    static_assert(FROWE == KG, "filter staging rows hold one GEMM-K row");
     static_assert(LDS_BYTES <= 163840, "fits in the 160 KB LDS");
 };
+}  // namespace band
 
-template <class E, int R, int S, int CIN, int DIL>
-__global__ __launch_bounds__(512, 1) void band_kernel(const BandArgs a)
+template <class E, int R, int S, int CIN, int DIL, bool TRANS>
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void band_kernel(const BandArgs a)
 {
-    using C = BandCfg<R, S, CIN, DIL>;
+    using C = band::BandCfg<R, S, CIN, DIL, TRANS>;
     using elem = typename E::elem;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
-    unsigned char *filt = smem;
-    unsigned char *ring = smem + C::FILT_BYTES;
+    unsigned char *ring = smem;
+    unsigned char *filt = smem + C::RING_BYTES;    // prologue only
+    unsigned char *ostage = smem + C::RING_BYTES;  // after the prologue
+    float *bias_s = (float *)(smem + C::RING_BYTES + C::STAGE_BYTES);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
     const int img = blockIdx.x / a.chunks_per_img;
     const int chunk = blockIdx.x - img * a.chunks_per_img;
     const int p_start = chunk * a.rows_per_wg;
     const int p_end = min(p_start + a.rows_per_wg, a.P);
-    if (p_start >= p_end) return;
+    if (p_start >= p_end) return;  // whole workgroup
+    const int nrows = p_end - p_start;
     const int n0 = blockIdx.y * C::BN;
     const int q0 = blockIdx.z * C::SEG;
     const int h_base = p_start - a.pad_h;  // input row of ring row 0
     const int w_base = q0 - a.pad_w;       // input column of ring column 0
 
-    const elem *src = (const elem *)a.src + (size_t)img * a.H * a.W * CIN;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-
-    // ---- ring rows.  Thread t always moves the same (column, channel chunk)
-    // positions of a row: chunk t + i*256 of the row's RCOLS*NCH chunks, so
-    // a row costs CPR loads per thread and the addresses are a base plus
-    // compile-time offsets.
-    const int my_j = tid % C::NCH;
-    const int my_col = tid / C::NCH;  // + i * (NT / NCH) for the i-th chunk of a row
-    constexpr int COL_STEP = C::NT / C::NCH;
-    const elem *my_src = src + (size_t)my_j * 8;
-    const int my_swz = ((my_j ^ ((my_col >> 1) & C::SWZ)) * 16) + my_col * C::PIXB;
-    static_assert(((COL_STEP >> 1) & C::SWZ) == 0 && COL_STEP % 2 == 0, "column step keeps the swizzle phase");
-    auto load_row_chunk = [&](int hrel, int i) -> u32x4 {
-        const int h = h_base + hrel, w = w_base + my_col + i * COL_STEP;
-        if ((unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W)
-            return *(const u32x4 *)(my_src + ((size_t)h * a.W + w) * CIN);
-        return zero;
+    // ---- ring rows by direct-to-LDS loads.  Wave w moves pixels 8w..8w+7 of
+    // each row (one 1 KB block); lane i fills stored chunk i%8 of pixel
+    // 8w + i/8, i.e. source chunk (i%8) ^ swizzle(pixel).
+    const elem *src_img = (const elem *)a.src + (size_t)img * a.H * a.W * CIN;
+    const __amdgpu_buffer_rsrc_t src_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)src_img, 0, a.H * a.W * CIN * 2, band::kRsrcWord3);
+    const unsigned row_bytes = (unsigned)(a.W * CIN * 2);
+    auto lane_src = [&](int blk) -> int {  // byte offset in a source row, or -1 past the row
+        const int col = 8 * blk + (lane >> 3);
+        const int j = (lane & 7) ^ ((col >> 1) & 7);
+        const int w = w_base + col;
+        return (unsigned)w < (unsigned)a.W ? (w * CIN + j * 8) * 2 : -1;
     };
-    auto ring_chunk = [&](int hrel, int i) -> u32x4 * {
-        return (u32x4 *)(ring + (hrel % C::NSLOT) * C::SLOTB + my_swz + i * COL_STEP * C::PIXB);
+    const int my_off = lane_src(wave);
+    auto dma_row = [&](int rr, int blk, int off) {
+        const int h = h_base + rr;
+        const bool ok = off >= 0 && (unsigned)h < (unsigned)a.H;
+        band::dma16(src_rs, ring + (rr % C::NSLOT) * C::SLOTB + blk * 1024,
+                    ok ? (unsigned)h * row_bytes + (unsigned)off : band::kOOB);
     };
-    u32x4 pre[C::NEW_CPT];
-    auto prefetch = [&](int r0) {
-#pragma unroll
-        for (int rr = 0; rr < C::GROUP_ROWS; ++rr)
-#pragma unroll
-            for (int i = 0; i < C::CPR; ++i) pre[rr * C::CPR + i] = load_row_chunk(r0 + rr, i);
+    // group g reads ring rows [g*GR, g*GR + GR + HALO_R); it brings the rows
+    // past the previous group's (all of them for g = 0)
+    auto group_rows = [&](int g, int &r0, int &r1) {
+        r0 = g == 0 ? 0 : g * C::GR + C::HALO_R;
+        r1 = min((g + 1) * C::GR + C::HALO_R, nrows + C::HALO_R);
     };
-    auto commit = [&](int r0) {
-#pragma unroll
-        for (int rr = 0; rr < C::GROUP_ROWS; ++rr)
-#pragma unroll
-            for (int i = 0; i < C::CPR; ++i) *ring_chunk(r0 + rr, i) = pre[rr * C::CPR + i];
+    auto dma_group = [&](int g) {
+        int r0, r1;
+        group_rows(g, r0, r1);
+        for (int rr = r0; rr < r1; ++rr) dma_row(rr, wave, my_off);
     };
 
-    // ---- prologue: the filter tile (taps reversed for dgrad), the halo rows
-    // and group 0's rows are all requested before any of them is waited for
-    constexpr int F_CHUNKS = C::BN * C::KG / 8;
-    constexpr int F_CPT = (F_CHUNKS + C::NT - 1) / C::NT;
+    // ---- prologue: the filter tile and group 0's rows, then group 1's rows.
+    // The first half of the waves starts well before the second, so it issues
+    // all of the prologue's loads.
+    constexpr int PW = C::WAVES / 2;
+    if (wave < PW) {
+        int r0, r1;
+        group_rows(0, r0, r1);
+        const int off2 = lane_src(wave + PW);
+        for (int rr = r0; rr < r1; ++rr) {
+            dma_row(rr, wave, my_off);
+            dma_row(rr, wave + PW, off2);
+        }
+        const int fbytes = (TRANS ? CIN * R * S * a.ngemm : a.ngemm * C::KG) * 2;
+        const __amdgpu_buffer_rsrc_t w_rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)a.bmat, 0, fbytes, band::kRsrcWord3);
+        for (int b = wave; b < C::FBLOCKS; b += PW) {
+            const int p = b * 64 + lane;
+            const int row = p / C::FROWCH, col = p - row * C::FROWCH;
+            unsigned voff = band::kOOB;
+            if (col < C::FROWE / 8) {
+                if (!TRANS) {
+                    // row = output channel, col = (tap, channel chunk)
+                    if (n0 + row < a.ngemm) voff = (unsigned)(((n0 + row) * C::KG + col * 8) * 2);
+                } else {
+                    // row = k (dy channel), col = (tap, chunk of the dx channel slice)
+                    const int tap = col / (C::BN / 8), c = n0 + (col - tap * (C::BN / 8)) * 8;
+                    if (c < a.ngemm) voff = (unsigned)(((row * R * S + tap) * a.ngemm + c) * 2);
+                }
+            }
+            band::dma16(w_rs, filt + b * 1024, voff);
+        }
+    }
     {
-        u32x4 freg[F_CPT];
-#pragma unroll
-        for (int i = 0; i < F_CPT; ++i) {
-            const int id = tid + i * C::NT;
-            const int n = id / (C::KG / 8), kc = id - n * (C::KG / 8);
-            const int tap = kc / (CIN / 8), cc = kc - tap * (CIN / 8);
-            const int stap = a.flip ? (R * S - 1 - tap) : tap;
-            freg[i] = zero;
-            if (id < F_CHUNKS && n0 + n < a.ngemm)
-                freg[i] = *(const u32x4 *)((const elem *)a.bmat + (size_t)(n0 + n) * C::KG + stap * CIN + cc * 8);
-        }
-        u32x4 hreg[C::HALO_R * C::CPR > 0 ? C::HALO_R * C::CPR : 1];
-#pragma unroll
-        for (int rr = 0; rr < C::HALO_R; ++rr)
-#pragma unroll
-            for (int i = 0; i < C::CPR; ++i) hreg[rr * C::CPR + i] = load_row_chunk(rr, i);
-        prefetch(C::HALO_R);
-#pragma unroll
-        for (int i = 0; i < F_CPT; ++i) {
-            const int id = tid + i * C::NT;
-            const int n = id / (C::KG / 8), kc = id - n * (C::KG / 8);
-            if (id < F_CHUNKS) *(u32x4 *)(filt + n * C::FROWB + kc * 16) = freg[i];
-        }
-#pragma unroll
-        for (int rr = 0; rr < C::HALO_R; ++rr)
-#pragma unroll
-            for (int i = 0; i < C::CPR; ++i) *ring_chunk(rr, i) = hreg[rr * C::CPR + i];
-        commit(C::HALO_R);
-    }
-    __syncthreads();
-
-    const int ngroups = (p_end - p_start + C::GROUP_ROWS - 1) / C::GROUP_ROWS;
-    const int l32 = lane & 31, lhi = lane >> 5;
-    const unsigned char *fbase = filt + l32 * C::FROWB + lhi * 16;
-    float bias_v[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int ch = n0 + n * 32 + l32;
-        bias_v[n] = (a.bias && ch < a.ngemm) ? E::to_f32(((const elem *)a.bias)[ch]) : 0.0f;
-    }
-
-    for (int g = 0; g < ngroups; ++g) {
-        const bool more = g + 1 < ngroups;
-        if (more) prefetch((g + 1) * C::GROUP_ROWS + C::HALO_R);
-
-        // the output row of this wave (relative to p_start)
-        const int pr = g * C::GROUP_ROWS + wave;
-        const bool active = p_start + pr < p_end;
-        f32x16 acc[2][2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) acc[m][n] = f32x16{};
-        if (active) {
-            // Taps in a rolled loop, the CIN/16 channel steps of a tap
-            // unrolled.  Two fragment buffers: while the MFMAs of one step
-            // issue, the reads of the next step are interleaved between them
-            // (one LDS read per MFMA); the first step of the next tap is read
-            // during the last step of this one (at the last tap it re-reads
-            // the same tap, so every read stays unconditional).
-            constexpr int C16 = CIN / 16;
-            static_assert(C16 % 2 == 0, "even channel steps per tap");
-            u32x4 fa0[2], fb0[2], fa1[2], fb1[2];
-            auto load_frags = [&](int tap, int c16, u32x4 (&A)[2], u32x4 (&Bf)[2]) {
-                const int r = tap / S, sx = tap - r * S;
-                const unsigned char *rowp = ring + ((pr + r * DIL) % C::NSLOT) * C::SLOTB;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int col = h * 32 + l32 + sx * DIL;
-                    A[h] = *(const u32x4 *)(rowp + col * C::PIXB +
-                                            (((2 * c16 + lhi) ^ ((col >> 1) & C::SWZ)) << 4));
-                }
-                const unsigned char *fp = fbase + tap * CIN * 2 + c16 * 32;
-                Bf[0] = *(const u32x4 *)(fp);
-                Bf[1] = *(const u32x4 *)(fp + 32 * C::FROWB);
-            };
-            auto mma = [&](const u32x4 (&A)[2], const u32x4 (&Bf)[2], bool interleave) {
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) acc[m][n] = Mfma32<E>::run(A[m], Bf[n], acc[m][n]);
-                if (interleave) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // one LDS read
-                        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // one MFMA
-                    }
-                }
-            };
-            load_frags(0, 0, fa0, fb0);
-#pragma unroll 1
-            for (int tap = 0; tap < R * S; ++tap) {
-                const int next = tap + 1 < R * S ? tap + 1 : tap;
-#pragma unroll
-                for (int c16 = 0; c16 < C16; c16 += 2) {
-                    load_frags(tap, c16 + 1, fa1, fb1);
-                    mma(fa0, fb0, true);
-                    if (c16 + 2 < C16)
-                        load_frags(tap, c16 + 2, fa0, fb0);
-                    else
-                        load_frags(next, 0, fa0, fb0);
-                    mma(fa1, fb1, true);
-                }
-            }
-        }
-        __syncthreads();  // every wave is done reading this group's ring rows
-
-        // ---- epilogue: bias, ReLU, round, staged in the ring slot of input
-        // row pr (used by this group only) as [column][channel]; 32x32 block
-        // layout: lane holds channel (lane & 31), columns 8*(i/4) + 4*(lane/32) + i%4
-        unsigned char *stage = ring + (pr % C::NSLOT) * C::SLOTB;
-        if (active) {
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int chl = n * 32 + l32;
-                const float b = bias_v[n];
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int ql = m * 32 + 8 * (i >> 2) + 4 * lhi + (i & 3);
-                        *(elem *)(stage + ql * C::OUT_PIXB + chl * 2) =
-                            E::from_f32(bias_relu_f32(acc[m][n][i], b, a.relu));
-                    }
-            }
-        }
+        if (tid < C::BN)
+            bias_s[tid] = (a.bias && n0 + tid < a.ngemm) ? E::to_f32(((const elem *)a.bias)[n0 + tid]) : 0.0f;
+        band::wait_vm_all();
         __syncthreads();
-        // read the staged row back (SEG columns x BN channels, 16 bytes per
-        // lane), free the slots for the prefetched rows, then store
-        constexpr int CPP = C::OUT_PIXB / 16;  // 16-byte chunks per pixel
-        constexpr int OUT_CPL = (C::SEG * CPP + 63) / 64;
-        u32x4 outv[OUT_CPL];
+        dma_group(1);  // into slots group 0 does not read
+    }
+
+    // ---- the wave's filter fragments (A operand): rows n0 + 32*nb + 0..31,
+    // k16 step ks = tap*C16 + c16; lane holds row l32, k = 8*lhi + 0..7
+    const int nb = wave & 1, l32 = lane & 31, lhi = lane >> 5;
+    u32x4 fr[C::KSTEPS];
+    if (!TRANS) {
+        const unsigned char *fp = filt + (nb * 32 + l32) * C::FROWB + lhi * 16;
 #pragma unroll
-        for (int i = 0; i < OUT_CPL; ++i) {
-            const int id = lane + i * 64;
-            const int ql = id / CPP, cc = id - ql * CPP;
-            outv[i] = (active && id < C::SEG * CPP) ? *(const u32x4 *)(stage + ql * C::OUT_PIXB + cc * 16) : zero;
+        for (int ks = 0; ks < C::KSTEPS; ++ks) fr[ks] = *(const u32x4 *)(fp + ks * 32);
+    } else {
+        // ds_read_b64_tr_b16: in each group of 16 lanes, lane L points at
+        // row L/4, columns 4*(L%4)..+3 of a 4 x 16 tile; lane i receives
+        // column i of the 4 rows.  Rows are k, columns the dx channels.
+        const int L = lane & 15, g16 = l32 >> 4;
+        const unsigned char *fp = filt + (L >> 2) * C::FROWB + (nb * 32 + g16 * 16 + 4 * (L & 3)) * 2;
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            const int tap = ks / C::C16, c16 = ks - tap * C::C16;
+            const int stap = R * S - 1 - tap;
+            const int kb = 16 * c16 + 8 * lhi;
+            const uint2 lo = __builtin_bit_cast(uint2, band::tr16(fp + kb * C::FROWB + stap * C::BN * 2));
+            const uint2 hi = __builtin_bit_cast(uint2, band::tr16(fp + (kb + 4) * C::FROWB + stap * C::BN * 2));
+            fr[ks] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
-        __syncthreads();  // staged outputs are read back; the slots are free
-        if (more) {
-            commit((g + 1) * C::GROUP_ROWS + C::HALO_R);
-            __syncthreads();
+    }
+
+    // ---- pixel fragments (B operand): output column mb*32 + l32 at tap
+    // column s reads ring column mb*32 + l32 + s*DIL, channel chunk
+    // 2*c16 + lhi, stored at chunk (2*c16 + lhi) ^ swizzle.  The byte offset
+    // inside a row is t_off[s] ^ (c16 << 5) (+ 32 pixels for mb = 1, which
+    // keeps the swizzle).
+    int t_off[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int col = l32 + s * DIL;
+        t_off[s] = col * C::PIXB + ((lhi ^ ((col >> 1) & 7)) << 4);
+    }
+
+    // ReLU (v <= 0, -0 and NaN included, -> +0) without lane masks:
+    // v > relu_lo ? v : v & relu_keep, with (0, 0) for ReLU and (-inf, ~0) without
+    const float relu_lo = a.relu ? 0.0f : -__builtin_inff();
+    const uint32_t relu_keep = a.relu ? 0u : ~0u;
+    const int ngroups = (nrows + C::GR - 1) / C::GR;
+    const int prw = wave >> 1;
+    __syncthreads();  // every wave holds its filter fragments: the staging area is free
+    for (int g = 0; g < ngroups; ++g) {
+        const int pr = g * C::GR + prw;  // output row of this wave, relative to p_start
+        const bool active = pr < nrows;
+        f32x16 acc[2];
+        acc[0] = f32x16{};
+        acc[1] = f32x16{};
+        if (active) {
+            int rowb[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) rowb[r] = ((pr + r * DIL) % C::NSLOT) * C::SLOTB;
+            u32x4 P[C::KSTEPS][2];
+            auto ld = [&](int ks) {
+                const int tap = ks / C::C16, c16 = ks - tap * C::C16;
+                const int r = tap / S, s = tap - r * S;
+                const unsigned char *p = ring + rowb[r] + (t_off[s] ^ (c16 << 5));
+                P[ks][0] = *(const u32x4 *)p;
+                P[ks][1] = *(const u32x4 *)(p + 32 * C::PIXB);
+            };
+#pragma unroll
+            for (int ks = 0; ks < C::PF; ++ks) ld(ks);
+#pragma unroll
+            for (int ks = 0; ks < C::KSTEPS; ++ks) {
+                if (ks + C::PF < C::KSTEPS) ld(ks + C::PF);
+                acc[0] = Mfma32<E>::run(fr[ks], P[ks][0], acc[0]);
+                acc[1] = Mfma32<E>::run(fr[ks], P[ks][1], acc[1]);
+                // keep the reads PF steps ahead of their MFMAs (the scheduler
+                // would otherwise sink each read down to its use)
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        // ---- epilogue, part 1: bias, ReLU, round, into the output staging
+        // (double-buffered) as [row][pixel][channel] with the ring's chunk
+        // swizzle.  Lane holds pixel mb*32 + l32, channels 32*nb + 8*j +
+        // 4*lhi + 0..3 in acc[mb][4j..4j+3]: 8 bytes, half lhi of chunk 4nb+j.
+        unsigned char *stage = ostage + (g & 1) * C::OSTAGE_BYTES + prw * C::SLOTB;
+        if (active) {
+            // all bias reads before any staging write (the compiler keeps LDS
+            // reads and writes in order), and ReLU as pure vector ops
+            f32x4 bv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = *(const f32x4 *)(bias_s + nb * 32 + 8 * j + 4 * lhi);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int px = mb * 32 + l32;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t v[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const uint32_t lo = E::from_f32(band::relu_floor(acc[mb][4 * j + 2 * t] + bv[j][2 * t], relu_lo, relu_keep));
+                        const uint32_t hi =
+                            E::from_f32(band::relu_floor(acc[mb][4 * j + 2 * t + 1] + bv[j][2 * t + 1], relu_lo, relu_keep));
+                        v[t] = lo | (hi << 16);
+                    }
+                    const int chunk = (4 * nb + j) ^ ((px >> 1) & 7);
+                    *(uint2 *)(stage + px * C::PIXB + chunk * 16 + lhi * 8) = uint2{v[0], v[1]};
+                }
+            }
+        }
+        band::wait_vm_all();  // the next group's rows (and this wave's older stores)
+        __syncthreads();      // every wave is done with this group's rows; the staging is complete
+
+        // ---- epilogue, part 2: whole pixels (128-byte lines) from the
+        // staging to memory.  Wave nb of a row stores pixels 32*nb..+31,
+        // 8 pixels per instruction; lane i takes stored chunk i%8 of pixel
+        // i/8, i.e. channel chunk (i%8) ^ swizzle(pixel).
         if (active) {
             const int p = p_start + pr;
-            elem *drow = (elem *)a.dst + ((size_t)img * a.P + p) * a.Q * a.ngemm;
+            elem *drow = (elem *)a.dst + ((size_t)img * a.P + p) * a.Q * a.ngemm;  // wave-uniform
 #pragma unroll
-            for (int i = 0; i < OUT_CPL; ++i) {
-                const int id = lane + i * 64;
-                const int ql = id / CPP, cc = id - ql * CPP;
-                const int q = q0 + ql, ch = n0 + cc * 8;
-                if (id < C::SEG * CPP && q < a.Q && ch < a.ngemm)
-                    *(u32x4 *)(drow + (size_t)q * a.ngemm + ch) = outv[i];
+            for (int t = 0; t < 4; ++t) {
+                const int px = nb * 32 + 8 * t + (lane >> 3);
+                const int chunk = (lane & 7) ^ ((px >> 1) & 7);
+                const u32x4 v = *(const u32x4 *)(stage + px * C::PIXB + (lane & 7) * 16);
+                const int q = q0 + px, ch = n0 + chunk * 8;
+                if (px < C::SEG && q < a.Q && ch < a.ngemm) *(u32x4 *)(drow + (unsigned)(q * a.ngemm + ch)) = v;
             }
         }
+        dma_group(g + 2);  // into the slots of the rows only this group read
     }
 }
 
@@ -314,9 +359,20 @@ hipError_t launch_band(int dtype, int R, int S, int cin, int dil, const BandArgs
 {
     if (!band_supported(R, S, cin, dil)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(a.N * a.chunks_per_img), (unsigned)grid_n, (unsigned)grid_q);
+    const bool t = a.flip != 0;
     switch (dtype) {
-    case CONV2D_DTYPE_F16: band_kernel<EF16, 3, 3, 64, 1><<<grid, 512, 0, st>>>(a); break;
-    case CONV2D_DTYPE_BF16: band_kernel<EBF16, 3, 3, 64, 1><<<grid, 512, 0, st>>>(a); break;
+    case CONV2D_DTYPE_F16:
+        if (t)
+            band_kernel<EF16, 3, 3, 64, 1, true><<<grid, 512, 0, st>>>(a);
+        else
+            band_kernel<EF16, 3, 3, 64, 1, false><<<grid, 512, 0, st>>>(a);
+        break;
+    case CONV2D_DTYPE_BF16:
+        if (t)
+            band_kernel<EBF16, 3, 3, 64, 1, true><<<grid, 512, 0, st>>>(a);
+        else
+            band_kernel<EBF16, 3, 3, 64, 1, false><<<grid, 512, 0, st>>>(a);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -96,10 +96,12 @@ hipError_t launch_igemm(int dtype, int tile, const IgemmArgs &a, int grid_m, int
                         hipStream_t st);
 
 // ---------------------------------------------------------------------------
-// Stride-1 band kernel (band.hip): filter and a ring of input rows in LDS.
-// src [N][H][W][CIN] -> dst [N][P][Q][ngemm] with P = H + 2*pad_h - dil*(R-1)
-// (likewise Q); pad_h / pad_w may be negative.  bmat is [ngemm][R*S*CIN]; with
-// flip set, its taps are read in reverse order (dgrad).
+// Stride-1 band kernel (band.hip): filter in registers, a ring of input rows
+// in LDS.  src [N][H][W][CIN] -> dst [N][P][Q][ngemm] with
+// P = H + 2*pad_h - dil*(R-1) (likewise Q); pad_h / pad_w may be negative.
+// Without flip, bmat is the fprop filter [ngemm][R][S][CIN]; with flip it is
+// the filter w[CIN][R][S][ngemm] of a dgrad, read with its taps reversed and
+// its two channel axes swapped.
 // ---------------------------------------------------------------------------
 struct BandArgs {
     const void *src;
