@@ -528,6 +528,9 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
         b.pad_h = (int)d.ph; b.pad_w = (int)d.pw;
         wgrad_band_rows(d, &b.rows_per_wg, &b.chunks_per_img);
         b.part_stride = splitk_stride(d.K * d.R * d.S * d.C);
+        b.xw = (int)(d.Q + d.dw * (d.S - 1));
+        b.div_xw = make_fastdiv((uint32_t)b.xw);
+        b.steps_per_group = wgrad_band_steps((int)d.Q);
         hipError_t e = launch_wgrad_band(dtype, b, s);
         if (e != hipSuccess) return CONV2D_ERR_DEVICE;
         return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,

@@ -177,8 +177,12 @@ struct WgradBandArgs {
     int pad_h, pad_w;
     int rows_per_wg, chunks_per_img;
     long long part_stride;
+    int xw;              // padded row pitch Q + dil*(S-1)
+    FastDiv div_xw;
+    int steps_per_group;  // wgrad_band_steps(Q)
 };
 bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q);
+int wgrad_band_steps(int Q);
 hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------

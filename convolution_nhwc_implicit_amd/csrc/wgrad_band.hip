@@ -8,20 +8,29 @@
 // ds_read_b64_tr_b16 gives exactly that from a pixel-major tile: in each group
 // of 16 lanes, lane L points at 4 channels of pixel L/4 and lane i receives
 // channel i of the 4 pixels.  So dy and x rows are copied into LDS as they are,
-// every input byte once, and all R*S tap shifts of x are just different read
-// addresses.
+// every input byte once (plus the halo rows), and all R*S tap shifts of x are
+// just different read addresses.
+//
+// Rows are laid out with the padded pitch XW = Q + dil*(S-1) in both LDS
+// buffers: dy gets XW - Q zero pixels after each row, so output pixel
+// (p, q) sits at v = p*XW + q and its tap (r, s) of x at v + r*dil*XW +
+// s*dil.  Every address is then linear in v: a 16-pixel step moves every
+// read by the same 2 KB (an immediate offset), the few padding pixels add
+// zeros, and the main loop needs no per-step index arithmetic.
 //
 // A workgroup (12 waves, three per SIMD) owns a band of output rows of one
 // image and all K x R*S*C outputs.  Output blocks are 32x32 (32x32x16 MFMA,
 // fp32 accumulators): wave w owns k-block w/6 and the three column blocks
-// 3*(w%6)..+2, over every pixel of the band.  Rows stream through two LDS
-// rings (dy: 2 groups of 4 rows, x: 4 rows + halo + 4 prefetched rows); the
-// next group's rows are loaded into registers while the current one is
-// computed.  Each workgroup writes its fp32 partial sums; the split-K
+// 3*(w%6)..+2 (which share one tap row r), over every pixel of the band.  The
+// band is walked in groups of GR output rows; each group's dy rows and its
+// GR + halo x rows are brought by direct-to-LDS loads (buffer_load ... lds;
+// pixels outside the image and the padding come from the buffer range check
+// as zeros) into one of two buffers, while the previous group is computed
+// from the other.  Each workgroup writes its fp32 partial sums; the split-K
 // reduction adds the workgroups' partials in workgroup order.
 //
-// 16-byte channel chunks of pixel `col` are stored with chunk bit 2 flipped
-// when bit 1 of col is set: the transposing reads of 4 consecutive pixels x
+// 16-byte channel chunks of pixel v are stored with chunk bit 2 flipped
+// when bit 1 of v is set: the transposing reads of 4 consecutive pixels x
 // 32 channels then cover all 64 LDS banks.
 #include "device_common.h"
 
@@ -51,32 +60,38 @@ struct Mfma32w<EBF16> {
 
 namespace wb {
 constexpr int NT = 768;          // 12 waves
+constexpr int WAVES = NT / 64;
 constexpr int CH = 64;           // C = K = 64 channels, 128 bytes per pixel
 constexpr int PIXB = CH * 2;
 constexpr int GR = 4;            // output rows per group
 constexpr int R = 3, S = 3, DIL = 1;
 constexpr int HALO = DIL * (R - 1);
-constexpr int XSLOTS = 2 * GR + HALO;
-constexpr int DSLOTS = 2 * GR;
-constexpr int QMAX = 56;         // widest output row handled (sizes the prefetch)
-constexpr int XW_MAX = QMAX + DIL * (S - 1);
-constexpr int X_BYTES = XSLOTS * XW_MAX * PIXB;
-constexpr int D_BYTES = DSLOTS * QMAX * PIXB;
-constexpr int ZERO_BYTES = PIXB;
-constexpr int LDS_BYTES = X_BYTES + D_BYTES + ZERO_BYTES;
+constexpr int BODY = 5;          // 16-pixel steps per straight-line body
+// buffer capacities in pixels (whole 1 KB direct-to-LDS blocks of 8 pixels),
+// sized for Q <= QMAX: a group covers steps*16 virtual pixels of dy (steps a
+// multiple of BODY) and those plus the tap shifts of x
+constexpr int QMAX = 56;
+constexpr int DCAP = 240;        // >= 16 * ceil_BODY(ceil(GR*(QMAX+2)/16))
+constexpr int XCAP = 360;        // >= DCAP + HALO*(QMAX+2) + DIL*(S-1)
+constexpr int D_BYTES = DCAP * PIXB, X_BYTES = XCAP * PIXB;
+constexpr int BUF_BYTES = D_BYTES + X_BYTES;
+constexpr int LDS_BYTES = 2 * BUF_BYTES;
 constexpr int NCOLB = R * S * CH / 32;   // 18 column blocks of 32 (static check below)
 constexpr int WAVE_CB = 3;               // column blocks per wave
+constexpr unsigned kOOB = 0x7ffffff0u;        // a buffer offset past every range: reads as zero
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (CDNA)
 static_assert(NCOLB == 6 * WAVE_CB, "six waves x three column blocks per k-block");
+static_assert(DCAP % 8 == 0 && XCAP % 8 == 0, "whole 1 KB blocks");
 static_assert(LDS_BYTES <= 163840, "fits in the 160 KB LDS");
-// Row loading: a group brings GR dy rows and GR x rows; each of these 2*GR rows
-// is moved by NT/(2*GR) threads, thread t owning channel chunk t%8 of columns
-// (t % TPR)/8 + i*COLS_STEP.
-constexpr int TPR = NT / (2 * GR);               // 96 threads per row
-constexpr int COLS_STEP = TPR / 8;               // 12 columns apart
-constexpr int PRE_CPT = (XW_MAX + COLS_STEP - 1) / COLS_STEP;  // chunks per thread
-static_assert(TPR % 8 == 0, "whole pixels per thread stride");
 
-__device__ inline int swz_chunk(int chunk, int col) { return chunk ^ (((col >> 1) & 1) << 2); }
+__device__ inline int swz_chunk(int chunk, int v) { return chunk ^ (((v >> 1) & 1) << 2); }
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *lds, unsigned voff)
+{
+    // lane i writes 16 bytes at lds + 16*i
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0,
+                                             0);
+}
+__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 }  // namespace wb
 
 template <class E>
@@ -85,188 +100,146 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     using namespace wb;
     using elem = typename E::elem;
     __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
-    unsigned char *xring = smem;
-    unsigned char *dring = smem + X_BYTES;
-    unsigned char *zpix = smem + X_BYTES + D_BYTES;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int img = blockIdx.x / a.chunks_per_img;
     const int chunk = blockIdx.x - img * a.chunks_per_img;
     const int p_start = chunk * a.rows_per_wg;
     const int p_end = min(p_start + a.rows_per_wg, a.P);
     const int nrows = p_end - p_start;  // >= 1 by construction of the grid
-    const int Q = a.Q;
-    const int XW = Q + DIL * (S - 1);
-    const int xslotb = XW * PIXB, dslotb = Q * PIXB;
+    const int Q = a.Q, XW = a.xw;
     const int h_base = p_start - a.pad_h;  // input row of x band row 0
-    const int w_base = -a.pad_w;           // input column of x ring column 0
-    const elem *x = (const elem *)a.x + (size_t)img * a.H * a.W * CH;
-    const elem *dy = (const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    if (tid < ZERO_BYTES / 16) *(u32x4 *)(zpix + tid * 16) = zero;
-
-    // ---- row loading (see TPR / COLS_STEP).  Thread t moves chunk my_j of
-    // columns my_col0 + i*COLS_STEP of row my_row of the group's new rows:
-    // rows 0..GR-1 are dy rows, GR..2GR-1 are x rows.
-    const int my_row = tid / TPR, my_j = tid % 8;
-    const int my_col0 = (tid % TPR) / 8;
-    const bool my_is_dy = my_row < GR;
-    const int my_rr = my_is_dy ? my_row : my_row - GR;
-    const int my_w = my_is_dy ? Q : XW;  // pixels in the row
-    u32x4 pre[PRE_CPT];
-    auto fetch = [&](int drow0, int xrow0) {
-        const int br = (my_is_dy ? drow0 : xrow0) + my_rr;
-        const int h = h_base + br;
-        const bool row_ok = my_is_dy ? br < nrows : (unsigned)h < (unsigned)a.H;
-        const elem *rowsrc = my_is_dy ? dy + (size_t)br * Q * CH : x + (size_t)h * a.W * CH;
-#pragma unroll
-        for (int i = 0; i < PRE_CPT; ++i) {
-            const int col = my_col0 + i * COLS_STEP;
-            const int w = my_is_dy ? col : w_base + col;
-            const bool ok = row_ok && col < my_w && (unsigned)w < (unsigned)(my_is_dy ? Q : a.W);
-            pre[i] = ok ? *(const u32x4 *)(rowsrc + (size_t)w * CH + my_j * 8) : zero;
-        }
-    };
-    auto store = [&](int drow0, int xrow0) {
-        const int br = (my_is_dy ? drow0 : xrow0) + my_rr;
-        unsigned char *rowdst = my_is_dy ? dring + (br % DSLOTS) * dslotb : xring + (br % XSLOTS) * xslotb;
-#pragma unroll
-        for (int i = 0; i < PRE_CPT; ++i) {
-            const int col = my_col0 + i * COLS_STEP;
-            if (col < my_w) *(u32x4 *)(rowdst + col * PIXB + swz_chunk(my_j, col) * 16) = pre[i];
+    // ---- loads.  Group g covers band rows [g*GR, g*GR + GR): dy virtual
+    // pixels [0, DCAP) and x virtual pixels [0, XCAP) of its buffer, 1 KB
+    // block b going to wave b % WAVES.  Lane i of a block fills stored chunk
+    // i%8 of pixel 8*blk + i/8, i.e. source chunk swz_chunk(i%8, pixel).
+    const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const elem *)a.x + (size_t)img * a.H * a.W * CH), 0, a.H * a.W * CH * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t d_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH), 0, nrows * Q * CH * 2, kRsrcWord3);
+    auto dma_group = [&](int g) {
+        const int d0 = g * GR;
+        if (d0 >= nrows) return;
+        const int ndy = min(GR, nrows - d0);  // dy rows of the group
+        const int nx = ndy + HALO;            // x rows it reads
+        unsigned char *buf = smem + (g & 1) * BUF_BYTES;
+        constexpr int DBLK = DCAP / 8, NBLK = (DCAP + XCAP) / 8;
+        for (int b = wave; b < NBLK; b += WAVES) {
+            const bool is_dy = b < DBLK;
+            const int v = (is_dy ? b : b - DBLK) * 8 + (lane >> 3);
+            const int row = (int)fdiv((uint32_t)v, a.div_xw), col = v - row * XW;
+            const int j = swz_chunk(lane & 7, v);
+            unsigned voff = kOOB;
+            if (is_dy) {
+                if (row < ndy && col < Q) voff = (unsigned)((((d0 + row) * Q + col) * CH + j * 8) * 2);
+            } else {
+                const int h = h_base + d0 + row, w = col - a.pad_w;
+                if (row < nx && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W)
+                    voff = (unsigned)(((h * a.W + w) * CH + j * 8) * 2);
+            }
+            dma16(is_dy ? d_rs : x_rs, buf + b * 1024, voff);
         }
     };
 
-    // prologue: x halo rows [0, HALO) (the x-row threads load them, HALO <= GR),
-    // then group 0: dy rows [0, GR), x rows [HALO, HALO + GR)
-    if (!my_is_dy && my_rr < HALO) {
-        fetch(0, 0);
-        store(0, 0);
-    }
-    fetch(0, HALO);
-    store(0, HALO);
+    dma_group(0);
+    wait_vm_all();
     __syncthreads();
+    dma_group(1);
 
-    // ---- per-wave roles
+    // ---- per-wave roles: k-block kb, column blocks cb0..cb0+2, all of tap
+    // row r (column block cb is tap cb/2 = (r, s), channel half cb&1)
     const int kb = wave / 6;
     const int cb0 = WAVE_CB * (wave % 6);
+    const int tap_r = (cb0 >> 1) / S;
     const int l32 = lane & 31, g16 = l32 >> 4, L = lane & 15, lhi = lane >> 5;
-    const int cin = 16 * g16 + 4 * (L & 3);      // channel offset inside a 32-channel block
+    const int cin = 16 * g16 + 4 * (L & 3);  // channel offset inside a 32-channel block
     const int cchunk = cin >> 3, cbyte = (cin & 7) * 2;
-    // column block -> (tap row r, tap column s, channel half): tap = cb / 2
-    int cb_r[WAVE_CB], cb_s[WAVE_CB], cb_chunk[WAVE_CB];
+
+    // ---- per-lane read offsets (step 0 of a buffer).  Read rd of a step
+    // covers pixels v = 16*t + 8*lhi + 4*rd + 0..3; this lane points at pixel
+    // v + L/4.  Steps move every read by 16 pixels, which keeps bit 1 of the
+    // pixel index and so the swizzle.
+    int doff[2], xoff[2][WAVE_CB];
 #pragma unroll
-    for (int i = 0; i < WAVE_CB; ++i) {
-        const int cb = cb0 + i, tap = cb >> 1;
-        cb_r[i] = tap / S;
-        cb_s[i] = tap - cb_r[i] * S;
-        cb_chunk[i] = (cb & 1) * 4 + cchunk;
+    for (int rd = 0; rd < 2; ++rd) {
+        const int v = 8 * lhi + 4 * rd + (L >> 2);
+        doff[rd] = v * PIXB + swz_chunk(kb * 4 + cchunk, v) * 16 + cbyte;
+#pragma unroll
+        for (int i = 0; i < WAVE_CB; ++i) {
+            const int cb = cb0 + i, tap_s = (cb >> 1) - tap_r * S;
+            const int xv = v + tap_r * DIL * XW + tap_s * DIL;
+            xoff[rd][i] = D_BYTES + xv * PIXB + swz_chunk((cb & 1) * 4 + cchunk, xv) * 16 + cbyte;
+        }
     }
 
     f32x16 acc[WAVE_CB];
 #pragma unroll
     for (int n = 0; n < WAVE_CB; ++n) acc[n] = f32x16{};
 
-    const int band_pix = nrows * Q;
-    const int nsteps = (band_pix + 15) / 16;
-    const int steps_per_group = GR * Q / 16;  // Q % 4 == 0
-    const int ngroups = (nrows + GR - 1) / GR;
-
-    auto tr = [](const unsigned char *p) -> s16x4 {
+    typedef __attribute__((address_space(3))) unsigned char lds_u8;  // 32-bit LDS addresses
+    auto tr = [](const lds_u8 *p) -> s16x4 {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
     };
-
-    // ---- per-lane read state.  Lane reads pixels f and f + 4 of each 16-pixel
-    // step (f = 16*t + 8*lhi + L/4).  Pixels only ever move by multiples of 4
-    // (16 per step, -Q on a row wrap, Q % 4 == 0), so each read's channel
-    // swizzle is fixed: its byte offsets inside a pixel are precomputed, and
-    // only the column and the ring rows are updated per step.
-    int pq[2], prr[2];
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-        pq[rd] = 8 * lhi + 4 * rd + (L >> 2);
-        prr[rd] = 0;
-        while (pq[rd] >= Q) {
-            pq[rd] -= Q;
-            ++prr[rd];
-        }
-    }
-    int aoff[2], boff[2][WAVE_CB];
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-        aoff[rd] = swz_chunk(kb * 4 + cchunk, pq[rd]) * 16 + cbyte;
-#pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i) {
-            // tap column shift plus the swizzled chunk of the shifted pixel;
-            // the current column pq is added per step
-            const int col = pq[rd] + cb_s[i] * DIL;
-            boff[rd][i] = cb_s[i] * DIL * PIXB + swz_chunk(cb_chunk[i], col) * 16 + cbyte;
-        }
-    }
-    // byte offsets of each read inside the ring (without the column pq*PIXB):
-    // dy row prr; x row prr + r_i*DIL of column block i.  Static indices only
-    // (a register array indexed by a runtime value becomes a select chain),
-    // recomputed on a row wrap.
-    int doff[2], xoff[2][WAVE_CB];
-    auto set_rows = [&](int rd) {
-        doff[rd] = X_BYTES + (prr[rd] % DSLOTS) * dslotb + aoff[rd];
-#pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i)
-            xoff[rd][i] = ((prr[rd] + cb_r[i] * DIL) % XSLOTS) * xslotb + boff[rd][i];
-    };
-    set_rows(0);
-    set_rows(1);
-    auto advance = [&]() {
+    typedef s16x4 Frag[2 + 2 * WAVE_CB];  // [0..1] dy, [2..7] x: 64-bit halves
+    // lane addresses of a body's first step; step k adds k*2 KB, which the
+    // reads take as an immediate offset
+    const lds_u8 *ad[2], *ax[2][WAVE_CB];
+    // (the empty asm keeps the compiler from re-associating base + offset +
+    // k*2 KB into one register per step)
+    auto set_body = [&](const lds_u8 *base) {
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
-            pq[rd] += 16;
-            if (pq[rd] >= Q) {
-                do {
-                    pq[rd] -= Q;
-                    ++prr[rd];
-                } while (pq[rd] >= Q);
-                set_rows(rd);
+            ad[rd] = base + doff[rd];
+            asm volatile("" : "+v"(ad[rd]));
+#pragma unroll
+            for (int i = 0; i < WAVE_CB; ++i) {
+                ax[rd][i] = base + xoff[rd][i];
+                asm volatile("" : "+v"(ax[rd][i]));
             }
         }
     };
-    const int zoff = X_BYTES + D_BYTES + cbyte;  // the zero pixel
-    auto load_step = [&](u32x4 &fa, u32x4 (&fb)[WAVE_CB]) {
-        s16x4 ra[2], rb[WAVE_CB][2];
+    auto load_step = [&](Frag &f, int k) {
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
-            const bool ok = prr[rd] < nrows;
-            const int qb = pq[rd] * PIXB;
-            ra[rd] = tr(smem + (ok ? doff[rd] + qb : zoff));
+            f[rd] = tr(ad[rd] + k * 16 * PIXB);
 #pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i) rb[i][rd] = tr(smem + (ok ? xoff[rd][i] + qb : zoff));
-        }
-        const uint2 alo = __builtin_bit_cast(uint2, ra[0]), ahi = __builtin_bit_cast(uint2, ra[1]);
-        fa = u32x4{alo.x, alo.y, ahi.x, ahi.y};
-#pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i) {
-            const uint2 lo = __builtin_bit_cast(uint2, rb[i][0]), hi = __builtin_bit_cast(uint2, rb[i][1]);
-            fb[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+            for (int i = 0; i < WAVE_CB; ++i) f[2 + 2 * i + rd] = tr(ax[rd][i] + k * 16 * PIXB);
         }
     };
-    auto mma = [&](const u32x4 &fa, const u32x4 (&fb)[WAVE_CB]) {
+    auto join = [](s16x4 lo, s16x4 hi) -> u32x4 {
+        const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+        return u32x4{l.x, l.y, h.x, h.y};
+    };
+    auto mma = [&](const Frag &f) {
+        const u32x4 fa = join(f[0], f[1]);
 #pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i) acc[i] = Mfma32w<E>::run(fa, fb[i], acc[i]);
+        for (int i = 0; i < WAVE_CB; ++i) acc[i] = Mfma32w<E>::run(fa, join(f[2 + 2 * i], f[3 + 2 * i]), acc[i]);
     };
 
+    // Steps run in straight-line bodies of BODY: the reads of step k+1 are
+    // issued before the MFMAs of step k, and nothing is in flight across
+    // bodies.  Steps past the group's pixels read zero dy pixels.
+    const int ngroups = (nrows + GR - 1) / GR;
     for (int g = 0; g < ngroups; ++g) {
-        const bool more = g + 1 < ngroups;
-        if (more) fetch((g + 1) * GR, (g + 1) * GR + HALO);
-        const int t0 = g * steps_per_group;
-        const int t1 = min(t0 + steps_per_group, nsteps);
-        for (int t = t0; t < t1; ++t) {
-            u32x4 fa, fb[WAVE_CB];
-            load_step(fa, fb);
-            advance();
-            mma(fa, fb);
+        const unsigned char *buf = smem + (g & 1) * BUF_BYTES;
+        const int nbody = a.steps_per_group / BODY;
+        for (int bd = 0; bd < nbody; ++bd) {
+            set_body((const lds_u8 *)buf + bd * BODY * 16 * PIXB);
+            Frag f[BODY];
+            load_step(f[0], 0);
+#pragma unroll
+            for (int k = 0; k < BODY; ++k) {
+                if (k + 1 < BODY) load_step(f[k + 1], k + 1);
+                __builtin_amdgcn_sched_barrier(0);  // all reads of step k+1 before the MFMAs of step k
+                mma(f[k]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        if (more) store((g + 1) * GR, (g + 1) * GR + HALO);  // slots of rows the previous group used
-        __syncthreads();
+        wait_vm_all();     // the next group's rows
+        __syncthreads();   // every wave is done with this group's buffer
+        dma_group(g + 2);  // into the buffer this group used
     }
 
     // ---- the workgroup's fp32 partials [K][R*S*C]; 32x32 block layout: lane
@@ -286,10 +259,21 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     }
 }
 
+// Steps of 16 pixels per group for output width Q, rounded up to whole
+// bodies; 0 if the group does not fit the buffers.
+int wgrad_band_steps(int Q)
+{
+    const int xw = Q + wb::DIL * (wb::S - 1);
+    int steps = (wb::GR * xw + 15) / 16;
+    steps = (steps + wb::BODY - 1) / wb::BODY * wb::BODY;
+    if (steps * 16 > wb::DCAP || steps * 16 + wb::HALO * xw + wb::DIL * (wb::S - 1) > wb::XCAP) return 0;
+    return steps;
+}
+
 bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q)
 {
     return R == wb::R && S == wb::S && C == wb::CH && K == wb::CH && dil == wb::DIL && Q % 4 == 0 &&
-           Q <= wb::QMAX && Q >= 4;
+           Q <= wb::QMAX && Q >= 4 && wgrad_band_steps(Q) > 0;
 }
 
 hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st)
