@@ -60,21 +60,10 @@ struct Mfma32<EBF16> {
 };
 
 namespace band {
-constexpr unsigned kOOB = 0x7ffffff0u;        // a buffer offset past every range: reads as zero
-constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (CDNA)
-
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *lds, unsigned voff)
-{
-    // lane i writes 16 bytes at lds + 16*i
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0,
-                                             0);
-}
 __device__ inline s16x4 tr16(const unsigned char *p)
 {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
-__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-
 __device__ inline float relu_floor(float v, float lo, uint32_t keep)
 {
     return v > lo ? v : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & keep);
@@ -155,8 +144,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // each row (one 1 KB block); lane i fills stored chunk i%8 of pixel
     // 8w + i/8, i.e. source chunk (i%8) ^ swizzle(pixel).
     const elem *src_img = (const elem *)a.src + (size_t)img * a.H * a.W * CIN;
-    const __amdgpu_buffer_rsrc_t src_rs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)src_img, 0, a.H * a.W * CIN * 2, band::kRsrcWord3);
+    const u32x4 src_rs = make_buf_rsrc(src_img, (uint32_t)(a.H * a.W * CIN * 2));
     const unsigned row_bytes = (unsigned)(a.W * CIN * 2);
     auto lane_src = [&](int blk) -> int {  // byte offset in a source row, or -1 past the row
         const int col = 8 * blk + (lane >> 3);
@@ -168,8 +156,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     auto dma_row = [&](int rr, int blk, int off) {
         const int h = h_base + rr;
         const bool ok = off >= 0 && (unsigned)h < (unsigned)a.H;
-        band::dma16(src_rs, ring + (rr % C::NSLOT) * C::SLOTB + blk * 1024,
-                    ok ? (unsigned)h * row_bytes + (unsigned)off : band::kOOB);
+        dma16(src_rs, lds_addr(ring + (rr % C::NSLOT) * C::SLOTB + blk * 1024),
+              ok ? (unsigned)h * row_bytes + (unsigned)off : kBufOOB);
     };
     // group g reads ring rows [g*GR, g*GR + GR + HALO_R); it brings the rows
     // past the previous group's (all of them for g = 0)
@@ -196,12 +184,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             dma_row(rr, wave + PW, off2);
         }
         const int fbytes = (TRANS ? CIN * R * S * a.ngemm : a.ngemm * C::KG) * 2;
-        const __amdgpu_buffer_rsrc_t w_rs =
-            __builtin_amdgcn_make_buffer_rsrc((void *)a.bmat, 0, fbytes, band::kRsrcWord3);
+        const u32x4 w_rs = make_buf_rsrc(a.bmat, (uint32_t)fbytes);
         for (int b = wave; b < C::FBLOCKS; b += PW) {
             const int p = b * 64 + lane;
             const int row = p / C::FROWCH, col = p - row * C::FROWCH;
-            unsigned voff = band::kOOB;
+            unsigned voff = kBufOOB;
             if (col < C::FROWE / 8) {
                 if (!TRANS) {
                     // row = output channel, col = (tap, channel chunk)
@@ -212,13 +199,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                     if (c < a.ngemm) voff = (unsigned)(((row * R * S + tap) * a.ngemm + c) * 2);
                 }
             }
-            band::dma16(w_rs, filt + b * 1024, voff);
+            dma16(w_rs, lds_addr(filt + b * 1024), voff);
         }
     }
     {
         if (tid < C::BN)
             bias_s[tid] = (a.bias && n0 + tid < a.ngemm) ? E::to_f32(((const elem *)a.bias)[n0 + tid]) : 0.0f;
-        band::wait_vm_all();
+        wait_vm_all();
         __syncthreads();
         dma_group(1);  // into slots group 0 does not read
     }
@@ -326,7 +313,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 }
             }
         }
-        band::wait_vm_all();  // the next group's rows (and this wave's older stores)
+        wait_vm_all();  // the next group's rows (and this wave's older stores)
         __syncthreads();      // every wave is done with this group's rows; the staging is complete
 
         // ---- epilogue, part 2: whole pixels (128-byte lines) from the

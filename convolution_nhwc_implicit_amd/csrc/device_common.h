@@ -64,6 +64,51 @@ struct EI8 {
     }
 };
 
+// ---- direct-to-LDS loads (buffer_load_dwordx4 ... lds) -------------------
+// Lane i of the wave writes its 16 bytes at LDS address lds + 16*i; the
+// global offset voff is checked against the buffer's byte range and reads
+// past it return zeros (padding without branches).  The instruction is
+// issued from inline asm so that the compiler does not track it: it would
+// otherwise wait for every such load before any later LDS access, which
+// serialises the prefetch with the compute.  Callers make the data visible
+// themselves: s_waitcnt vmcnt(0) on every wave, then a barrier.
+constexpr uint32_t kBufOOB = 0x7ffffff0u;  // an offset past every range: reads as zero
+
+// Raw buffer descriptor (base, stride 0, num_records = bytes, 32-bit data
+// format for CDNA), wave-uniform.
+__device__ inline u32x4 make_buf_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    u32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w = 0x00020000u;
+    return r;
+}
+// Wave-uniform 32-bit LDS address of a __shared__ location.
+__device__ inline uint32_t lds_addr(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char *)p);
+}
+// M0 (the LDS base of the transfer) is saved and restored around the load,
+// so the compiler's own use of M0 is untouched.
+__device__ inline void dma16(const u32x4 &rsrc, uint32_t lds, uint32_t voff)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
 // int8 requantisation of one accumulator: + bias, ReLU, * m in fp64,
 // round half to even (v_rndne_f64), saturate.
 __device__ inline int8_t requant_i8(int v, double m)

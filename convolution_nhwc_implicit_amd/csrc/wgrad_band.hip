@@ -66,32 +66,27 @@ constexpr int PIXB = CH * 2;
 constexpr int GR = 4;            // output rows per group
 constexpr int R = 3, S = 3, DIL = 1;
 constexpr int HALO = DIL * (R - 1);
-constexpr int BODY = 5;          // 16-pixel steps per straight-line body
+constexpr int BODY = 8;          // 16-pixel steps per straight-line body (per half)
+constexpr int HALVES = 2;        // the waves split a group's steps: even / odd
 // buffer capacities in pixels (whole 1 KB direct-to-LDS blocks of 8 pixels),
 // sized for Q <= QMAX: a group covers steps*16 virtual pixels of dy (steps a
-// multiple of BODY) and those plus the tap shifts of x
+// multiple of HALVES*BODY) and those plus the tap shifts of x
 constexpr int QMAX = 56;
-constexpr int DCAP = 240;        // >= 16 * ceil_BODY(ceil(GR*(QMAX+2)/16))
-constexpr int XCAP = 360;        // >= DCAP + HALO*(QMAX+2) + DIL*(S-1)
+constexpr int DCAP = 256;        // >= 16 * round_up(ceil(GR*(QMAX+2)/16), HALVES*BODY)
+constexpr int XCAP = 376;        // >= DCAP + HALO*(QMAX+2) + DIL*(S-1)
 constexpr int D_BYTES = DCAP * PIXB, X_BYTES = XCAP * PIXB;
 constexpr int BUF_BYTES = D_BYTES + X_BYTES;
 constexpr int LDS_BYTES = 2 * BUF_BYTES;
 constexpr int NCOLB = R * S * CH / 32;   // 18 column blocks of 32 (static check below)
 constexpr int WAVE_CB = 3;               // column blocks per wave
-constexpr unsigned kOOB = 0x7ffffff0u;        // a buffer offset past every range: reads as zero
-constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (CDNA)
-static_assert(NCOLB == 6 * WAVE_CB, "six waves x three column blocks per k-block");
+constexpr int WAVE_KB = 2;               // k-blocks per wave (all of K = 64)
+constexpr int NACC = WAVE_KB * WAVE_CB;
+static_assert(NCOLB == 6 * WAVE_CB && WAVES == 6 * HALVES, "six waves of three column blocks per half");
+static_assert(WAVES / HALVES * 64 * NACC * 16 * 4 <= LDS_BYTES, "one half's accumulators fit in LDS");
 static_assert(DCAP % 8 == 0 && XCAP % 8 == 0, "whole 1 KB blocks");
 static_assert(LDS_BYTES <= 163840, "fits in the 160 KB LDS");
 
 __device__ inline int swz_chunk(int chunk, int v) { return chunk ^ (((v >> 1) & 1) << 2); }
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *lds, unsigned voff)
-{
-    // lane i writes 16 bytes at lds + 16*i
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0,
-                                             0);
-}
-__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 }  // namespace wb
 
 template <class E>
@@ -115,10 +110,9 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     // pixels [0, DCAP) and x virtual pixels [0, XCAP) of its buffer, 1 KB
     // block b going to wave b % WAVES.  Lane i of a block fills stored chunk
     // i%8 of pixel 8*blk + i/8, i.e. source chunk swz_chunk(i%8, pixel).
-    const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const elem *)a.x + (size_t)img * a.H * a.W * CH), 0, a.H * a.W * CH * 2, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t d_rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH), 0, nrows * Q * CH * 2, kRsrcWord3);
+    const u32x4 x_rs = make_buf_rsrc((const elem *)a.x + (size_t)img * a.H * a.W * CH, (uint32_t)(a.H * a.W * CH * 2));
+    const u32x4 d_rs =
+        make_buf_rsrc((const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH, (uint32_t)(nrows * Q * CH * 2));
     auto dma_group = [&](int g) {
         const int d0 = g * GR;
         if (d0 >= nrows) return;
@@ -131,7 +125,7 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
             const int v = (is_dy ? b : b - DBLK) * 8 + (lane >> 3);
             const int row = (int)fdiv((uint32_t)v, a.div_xw), col = v - row * XW;
             const int j = swz_chunk(lane & 7, v);
-            unsigned voff = kOOB;
+            unsigned voff = kBufOOB;
             if (is_dy) {
                 if (row < ndy && col < Q) voff = (unsigned)((((d0 + row) * Q + col) * CH + j * 8) * 2);
             } else {
@@ -139,7 +133,7 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
                 if (row < nx && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W)
                     voff = (unsigned)(((h * a.W + w) * CH + j * 8) * 2);
             }
-            dma16(is_dy ? d_rs : x_rs, buf + b * 1024, voff);
+            dma16(is_dy ? d_rs : x_rs, lds_addr(buf + b * 1024), voff);
         }
     };
 
@@ -148,54 +142,66 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     __syncthreads();
     dma_group(1);
 
-    // ---- per-wave roles: k-block kb, column blocks cb0..cb0+2, all of tap
-    // row r (column block cb is tap cb/2 = (r, s), channel half cb&1)
-    const int kb = wave / 6;
+    // ---- per-wave roles: both k-blocks, column blocks cb0..cb0+2 (all of
+    // tap row r: column block cb is tap cb/2 = (r, s), channel half cb&1),
+    // and the steps of one parity
+    const int half = wave / 6;
     const int cb0 = WAVE_CB * (wave % 6);
     const int tap_r = (cb0 >> 1) / S;
-    const int l32 = lane & 31, g16 = l32 >> 4, L = lane & 15, lhi = lane >> 5;
-    const int cin = 16 * g16 + 4 * (L & 3);  // channel offset inside a 32-channel block
-    const int cchunk = cin >> 3, cbyte = (cin & 7) * 2;
+    const int l32 = lane & 31, lhi = lane >> 5;
 
-    // ---- per-lane read offsets (step 0 of a buffer).  Read rd of a step
-    // covers pixels v = 16*t + 8*lhi + 4*rd + 0..3; this lane points at pixel
-    // v + L/4.  Steps move every read by 16 pixels, which keeps bit 1 of the
-    // pixel index and so the swizzle.
-    int doff[2], xoff[2][WAVE_CB];
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-        const int v = 8 * lhi + 4 * rd + (L >> 2);
-        doff[rd] = v * PIXB + swz_chunk(kb * 4 + cchunk, v) * 16 + cbyte;
-#pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i) {
-            const int cb = cb0 + i, tap_s = (cb >> 1) - tap_r * S;
-            const int xv = v + tap_r * DIL * XW + tap_s * DIL;
-            xoff[rd][i] = D_BYTES + xv * PIXB + swz_chunk((cb & 1) * 4 + cchunk, xv) * 16 + cbyte;
-        }
-    }
+    // ---- per-lane read offsets (first step of this half in a buffer).  Read
+    // rd of a step covers pixels v = 16*t + 8*lhi + 4*rd + 0..3; this lane
+    // points at pixel v + L/4.  Steps move every read by a multiple of 16
+    // pixels, which keeps bit 1 of the pixel index and so the swizzle.  They
+    // are recomputed per body from an opaque copy of the lane id (holding
+    // them across the loop would cost registers the fragments need).
+    auto dy_off = [&](int ln, int rd, int kb) {
+        const int L_ = ln & 15, g_ = (ln >> 4) & 1, h_ = ln >> 5;
+        const int c_ = 16 * g_ + 4 * (L_ & 3);
+        const int v = 16 * half + 8 * h_ + 4 * rd + (L_ >> 2);
+        return v * PIXB + swz_chunk(kb * 4 + (c_ >> 3), v) * 16 + (c_ & 7) * 2;
+    };
+    auto x_off = [&](int ln, int rd, int i) {
+        const int L_ = ln & 15, g_ = (ln >> 4) & 1, h_ = ln >> 5;
+        const int c_ = 16 * g_ + 4 * (L_ & 3);
+        const int v = 16 * half + 8 * h_ + 4 * rd + (L_ >> 2);
+        const int cb = cb0 + i, tap_s = (cb >> 1) - tap_r * S;
+        const int xv = v + tap_r * DIL * XW + tap_s * DIL;
+        return D_BYTES + xv * PIXB + swz_chunk((cb & 1) * 4 + (c_ >> 3), xv) * 16 + (c_ & 7) * 2;
+    };
 
-    f32x16 acc[WAVE_CB];
+    f32x16 acc[WAVE_KB][WAVE_CB];
 #pragma unroll
-    for (int n = 0; n < WAVE_CB; ++n) acc[n] = f32x16{};
+    for (int kb = 0; kb < WAVE_KB; ++kb)
+#pragma unroll
+        for (int n = 0; n < WAVE_CB; ++n) acc[kb][n] = f32x16{};
 
     typedef __attribute__((address_space(3))) unsigned char lds_u8;  // 32-bit LDS addresses
     auto tr = [](const lds_u8 *p) -> s16x4 {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
     };
-    typedef s16x4 Frag[2 + 2 * WAVE_CB];  // [0..1] dy, [2..7] x: 64-bit halves
-    // lane addresses of a body's first step; step k adds k*2 KB, which the
-    // reads take as an immediate offset
-    const lds_u8 *ad[2], *ax[2][WAVE_CB];
-    // (the empty asm keeps the compiler from re-associating base + offset +
-    // k*2 KB into one register per step)
+    // one step's fragments as raw 64-bit halves: [2*kb + rd] dy, [4 + 2*i + rd] x
+    typedef s16x4 Frag[2 * WAVE_KB + 2 * WAVE_CB];
+    // lane addresses of a body's first step; step k (k-th of this half) adds
+    // k*HALVES*2 KB, which the reads take as an immediate offset (the empty
+    // asm keeps the compiler from re-associating base + offset + k*4 KB into
+    // one register per step)
+    constexpr int STEPB = HALVES * 16 * PIXB;
+    const lds_u8 *ad[2][WAVE_KB], *ax[2][WAVE_CB];
     auto set_body = [&](const lds_u8 *base) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
-            ad[rd] = base + doff[rd];
-            asm volatile("" : "+v"(ad[rd]));
+#pragma unroll
+            for (int kb = 0; kb < WAVE_KB; ++kb) {
+                ad[rd][kb] = base + dy_off(ln, rd, kb);
+                asm volatile("" : "+v"(ad[rd][kb]));
+            }
 #pragma unroll
             for (int i = 0; i < WAVE_CB; ++i) {
-                ax[rd][i] = base + xoff[rd][i];
+                ax[rd][i] = base + x_off(ln, rd, i);
                 asm volatile("" : "+v"(ax[rd][i]));
             }
         }
@@ -203,9 +209,10 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     auto load_step = [&](Frag &f, int k) {
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
-            f[rd] = tr(ad[rd] + k * 16 * PIXB);
 #pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i) f[2 + 2 * i + rd] = tr(ax[rd][i] + k * 16 * PIXB);
+            for (int kb = 0; kb < WAVE_KB; ++kb) f[2 * kb + rd] = tr(ad[rd][kb] + k * STEPB);
+#pragma unroll
+            for (int i = 0; i < WAVE_CB; ++i) f[2 * WAVE_KB + 2 * i + rd] = tr(ax[rd][i] + k * STEPB);
         }
     };
     auto join = [](s16x4 lo, s16x4 hi) -> u32x4 {
@@ -213,20 +220,25 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         return u32x4{l.x, l.y, h.x, h.y};
     };
     auto mma = [&](const Frag &f) {
-        const u32x4 fa = join(f[0], f[1]);
 #pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i) acc[i] = Mfma32w<E>::run(fa, join(f[2 + 2 * i], f[3 + 2 * i]), acc[i]);
+        for (int kb = 0; kb < WAVE_KB; ++kb) {
+            const u32x4 fa = join(f[2 * kb], f[2 * kb + 1]);
+#pragma unroll
+            for (int i = 0; i < WAVE_CB; ++i)
+                acc[kb][i] = Mfma32w<E>::run(fa, join(f[2 * WAVE_KB + 2 * i], f[2 * WAVE_KB + 2 * i + 1]), acc[kb][i]);
+        }
     };
 
-    // Steps run in straight-line bodies of BODY: the reads of step k+1 are
-    // issued before the MFMAs of step k, and nothing is in flight across
-    // bodies.  Steps past the group's pixels read zero dy pixels.
+    // Steps run in straight-line bodies of BODY (of one parity): the reads
+    // of step k+1 are issued before the MFMAs of step k, and nothing is in
+    // flight across bodies.  Steps past the group's pixels read zero dy
+    // pixels.
     const int ngroups = (nrows + GR - 1) / GR;
     for (int g = 0; g < ngroups; ++g) {
         const unsigned char *buf = smem + (g & 1) * BUF_BYTES;
-        const int nbody = a.steps_per_group / BODY;
+        const int nbody = a.steps_per_group / (HALVES * BODY);
         for (int bd = 0; bd < nbody; ++bd) {
-            set_body((const lds_u8 *)buf + bd * BODY * 16 * PIXB);
+            set_body((const lds_u8 *)buf + bd * BODY * STEPB);
             Frag f[BODY];
             load_step(f[0], 0);
 #pragma unroll
@@ -242,20 +254,35 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         dma_group(g + 2);  // into the buffer this group used
     }
 
-    // ---- the workgroup's fp32 partials [K][R*S*C]; 32x32 block layout: lane
-    // holds column (lane & 31), rows 8*(r/4) + 4*(lane/32) + r%4
-    {
+    // ---- the two halves' sums: half 1 parks its accumulators in LDS (the
+    // buffers are idle now), half 0 adds them (half 0 + half 1, a fixed
+    // order) and writes the workgroup's fp32 partials [K][R*S*C].
+    float *park = (float *)smem + (wave % 6) * (NACC * 16 * 64) + lane;
+    if (half == 1) {
+#pragma unroll
+        for (int kb = 0; kb < WAVE_KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < WAVE_CB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) park[((kb * WAVE_CB + i) * 16 + r) * 64] = acc[kb][i][r];
+    }
+    __syncthreads();
+    if (half == 0) {
+        // 32x32 block layout: lane holds column (lane & 31), rows
+        // 8*(r/4) + 4*(lane/32) + r%4
         constexpr int NCOLS = R * S * CH;
         float *out = (float *)a.out + (size_t)blockIdx.x * a.part_stride;
 #pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i) {
-            const int col = (cb0 + i) * 32 + l32;
+        for (int kb = 0; kb < WAVE_KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int k = kb * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-                out[(size_t)k * NCOLS + col] = acc[i][r];
+            for (int i = 0; i < WAVE_CB; ++i) {
+                const int col = (cb0 + i) * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int k = kb * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
+                    out[(size_t)k * NCOLS + col] = acc[kb][i][r] + park[((kb * WAVE_CB + i) * 16 + r) * 64];
+                }
             }
-        }
     }
 }
 
@@ -265,7 +292,8 @@ int wgrad_band_steps(int Q)
 {
     const int xw = Q + wb::DIL * (wb::S - 1);
     int steps = (wb::GR * xw + 15) / 16;
-    steps = (steps + wb::BODY - 1) / wb::BODY * wb::BODY;
+    constexpr int unit = wb::HALVES * wb::BODY;
+    steps = (steps + unit - 1) / unit * unit;
     if (steps * 16 > wb::DCAP || steps * 16 + wb::HALO * xw + wb::DIL * (wb::S - 1) > wb::XCAP) return 0;
     return steps;
 }
