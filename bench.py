@@ -5,10 +5,14 @@ One step = fprop (+bias+ReLU) + dgrad + wgrad of one batch of the workload
 through the C ABI, inputs resident in HBM before the timed region.  Prints one
 JSON line:
   value      = FLOPs of the three passes / wall time per step (TFLOP/s),
-               2*N*P*Q*K*(C/G)*R*S FLOPs per pass;
-  passes     = per-pass time (HIP events on the launch stream), TFLOP/s and
-               fraction of the dense fp16 MFMA peak, and algorithmic GB/s;
-  roofline   = the pass that takes the most time, against its bound;
+               2*N*P*Q*K*(C/G)*R*S FLOPs per pass, over K back-to-back steps
+               between two device synchronisations;
+  passes     = per-pass time per launch (K back-to-back launches of the pass
+               between two HIP events on the launch stream), TFLOP/s,
+               fraction of the dense fp16 MFMA peak, algorithmic GB/s and the
+               kernels the pass launches;
+  roofline   = the pass that takes the most time, against its bound, with
+               the measured HBM traffic of its kernels;
   cpu_baseline = the fp64 CPU oracle on a bounded sample of the same
                workload (first images of the batch), same FLOP convention.
 
@@ -29,12 +33,13 @@ METRIC = "conv2d TFLOP/s (fprop/dgrad/wgrad) and % of MFMA peak, 56x56x64 3x3 fp
 # FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s), int8 5.03 POP/s, HBM3E 8 TB/s.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2}
 PEAK_HBM_GBS = 8000.0
+BAND_TILE, WGRAD_BAND_TILE = 5, 1  # plan tile indices of the band kernels (conv2d_plan_info)
 COPY_BYTES = 64 << 20  # reference copy for the HBM byte counters
 # Measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by
 # the same counters on a plain copy) lives in this summary, keyed by a hash of
 # the kernel sources it was measured on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3a_hbm_traffic.json")
-KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp"]
+KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h"]
 
 
 def kernel_source_hash():
@@ -114,18 +119,10 @@ def main():
     ws = {op: B.workspace_for(op, prob, dt, dev) for op in (0, 1, 2)}
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def step():
         B.conv2d_fprop(prob, dt, x, w, b, relu, 1.0, 1.0, 1.0, y, ws[0], stream=stream)
-        if ev:
-            ev[1].record(stream)
         B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream)
-        if ev:
-            ev[2].record(stream)
         B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)
-        if ev:
-            ev[3].record(stream)
 
     if args.only == "copy":
         src_t = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -164,14 +161,31 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # Timed region 1: K whole steps back to back (wall clock between two
+    # device synchronisations) -> value.
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # Timed region 2: each pass alone, K back-to-back launches between two HIP
+    # events recorded on the launch stream -> per-pass time per launch (the
+    # figure rocprofv3's kernel trace reports as the kernels' duration).
+    runs = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, 1.0, 1.0, 1.0, y, ws[0], stream=stream),
+            "dgrad": lambda: B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream),
+            "wgrad": lambda: B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)}
+    pass_us = {}
+    for pname, run in runs.items():
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pass_us[pname] = e0.elapsed_time(e1) * 1e3 / args.steps
 
     fl = flops(prob, P, Q)
     esz = 2
@@ -184,20 +198,24 @@ def main():
         "wgrad": esz * (elems_x + elems_y + elems_w),
     }
     plans = {n: B.conv2d_plan_info(op, prob, dt) for op, n in enumerate(("fprop", "dgrad", "wgrad"))}
+    kernels = {
+        "fprop": ["band" if plans["fprop"]["tile"] == BAND_TILE else "implicit_gemm"],
+        "dgrad": ["band"] if plans["dgrad"]["tile"] == BAND_TILE else ["filter_relayout", "implicit_gemm"],
+        "wgrad": (["wgrad_band" if plans["wgrad"]["tile"] == WGRAD_BAND_TILE else "wgrad_gemm"]
+                  + (["splitk_reduce"] if plans["wgrad"]["split_k"] > 1 else [])),
+    }
     passes = {}
-    for j, pname in enumerate(("fprop", "dgrad", "wgrad")):
-        times = np.array([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])
-        us = float(np.mean(times)) * 1e3
+    for pname in ("fprop", "dgrad", "wgrad"):
+        us = pass_us[pname]
         passes[pname] = {
-            "us_mean": round(us, 3),
-            "us_median": round(float(np.median(times)) * 1e3, 3),
+            "us_per_launch": round(us, 3),
             "tflops": round(fl / (us * 1e-6) / 1e12, 2),
             "frac_mfma_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_TFLOPS[dt], 4),
             "alg_gbs": round(alg_bytes[pname] / (us * 1e-6) / 1e9, 1),
-            "kernels": {"fprop": 1, "dgrad": 2, "wgrad": 2 if plans[pname]["split_k"] > 1 else 1}[pname],
+            "kernels": kernels[pname],
             "plan": plans[pname],
         }
-    dom = max(passes, key=lambda k: passes[k]["us_mean"])
+    dom = max(passes, key=lambda k: passes[k]["us_per_launch"])
     d = passes[dom]
     # Compute-bound when the pass's arithmetic intensity exceeds the ridge point.
     ai = fl / alg_bytes[dom]
@@ -210,7 +228,8 @@ def main():
                 "frac": round(d["alg_gbs"] / PEAK_HBM_GBS, 4)}
     roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
-    roof["per_launch"] = {"flop": fl, "alg_bytes": alg_bytes[dom], "avg_us": d["us_mean"]}
+    roof["kernels"] = kernels[dom]
+    roof["per_launch"] = {"flop": fl, "alg_bytes": alg_bytes[dom], "avg_us": d["us_per_launch"]}
 
     total_fl = 3 * fl
     result = {

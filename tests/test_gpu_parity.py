@@ -67,12 +67,14 @@ CASES = [
     ("band_pad3", problem(2, 64, 8, 8, 64, 3, 3, pad=(3, 3)), "f16", "int", False, False),
     ("band_gauss", problem(8, 64, 28, 28, 64, 3, 3, pad=(1, 1)), "f16", "gauss", True, True),
     ("band_bf16_gauss", problem(4, 64, 17, 23, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
-    # wgrad band kernel (stride 1, 3x3, C = K = 64, Q % 4 == 0, Q <= 64):
+    # wgrad band kernel (stride 1, 3x3, C = K = 64, Q % 4 == 0, Q <= 56):
     # two row groups with a partial last group, and one-row bands whose pixel
-    # count is not a multiple of 16
+    # count is not a multiple of 16; the widest row it takes (Q = 56, several
+    # groups per band), and one just past it (Q = 64, generic path)
     ("wband_groups", problem(64, 64, 30, 8, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
     ("wband_masked", problem(2, 64, 12, 12, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
     ("wband_bf16", problem(16, 64, 20, 20, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
+    ("wband_q56", problem(2, 64, 23, 56, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
     ("wband_wide", problem(4, 64, 9, 64, 64, 3, 3, pad=(1, 1)), "f16", "int", True, True),
 ]
 
