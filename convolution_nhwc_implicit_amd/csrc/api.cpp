@@ -152,10 +152,11 @@ bool wgrad_band_eligible(const Dims &d, int dtype)
 
 constexpr int kWgradBandTile = 1;  // wgrad tile index of the band kernel (algo tile 2)
 
-// Output rows per wgrad band workgroup: about one workgroup per CU.
+// Output rows per wgrad band: about one workgroup per CU, two workgroups
+// (column halves) per band.
 void wgrad_band_rows(const Dims &d, int *rows, int *chunks)
 {
-    long long c = (kNumCUs + d.N - 1) / d.N;
+    long long c = (kNumCUs / 2 + d.N - 1) / d.N;
     c = std::max(1LL, std::min(c, d.P));
     *rows = (int)((d.P + c - 1) / c);
     *chunks = (int)((d.P + *rows - 1) / *rows);
@@ -531,6 +532,7 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
         b.xw = (int)(d.Q + d.dw * (d.S - 1));
         b.div_xw = make_fastdiv((uint32_t)b.xw);
         b.steps_per_group = wgrad_band_steps((int)d.Q);
+        b.xcd_pairs = (d.N * b.chunks_per_img) % 8 == 0;
         hipError_t e = launch_wgrad_band(dtype, b, s);
         if (e != hipSuccess) return CONV2D_ERR_DEVICE;
         return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,

@@ -180,6 +180,7 @@ struct WgradBandArgs {
     int xw;              // padded row pitch Q + dil*(S-1)
     FastDiv div_xw;
     int steps_per_group;  // wgrad_band_steps(Q)
+    int xcd_pairs;        // bands a multiple of 8: the two column halves of a band share an XCD
 };
 bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q);
 int wgrad_band_steps(int Q);

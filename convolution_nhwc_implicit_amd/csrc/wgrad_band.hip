@@ -66,23 +66,26 @@ constexpr int PIXB = CH * 2;
 constexpr int GR = 4;            // output rows per group
 constexpr int R = 3, S = 3, DIL = 1;
 constexpr int HALO = DIL * (R - 1);
-constexpr int BODY = 8;          // 16-pixel steps per straight-line body (per half)
-constexpr int HALVES = 2;        // the waves split a group's steps: even / odd
+constexpr int NCOLB = R * S * CH / 32;   // 18 column blocks of 32 in all
+constexpr int CB_WG = NCOLB / 2;         // a workgroup computes one half of them
+constexpr int WAVE_CB = 3;               // column blocks per wave
+constexpr int WAVE_KB = 2;               // k-blocks per wave (all of K = 64)
+constexpr int NACC = WAVE_KB * WAVE_CB;
+constexpr int WSETS = CB_WG / WAVE_CB;   // 3 waves cover the workgroup's columns ...
+constexpr int PHASES = WAVES / WSETS;    // ... and 4 such sets split the 16-pixel steps (t mod 4)
+constexpr int BODY = 4;                  // steps per straight-line body (per phase)
 // buffer capacities in pixels (whole 1 KB direct-to-LDS blocks of 8 pixels),
 // sized for Q <= QMAX: a group covers steps*16 virtual pixels of dy (steps a
-// multiple of HALVES*BODY) and those plus the tap shifts of x
+// multiple of PHASES*BODY) and those plus the tap shifts of x
 constexpr int QMAX = 56;
-constexpr int DCAP = 256;        // >= 16 * round_up(ceil(GR*(QMAX+2)/16), HALVES*BODY)
+constexpr int DCAP = 256;        // >= 16 * round_up(ceil(GR*(QMAX+2)/16), PHASES*BODY)
 constexpr int XCAP = 376;        // >= DCAP + HALO*(QMAX+2) + DIL*(S-1)
 constexpr int D_BYTES = DCAP * PIXB, X_BYTES = XCAP * PIXB;
 constexpr int BUF_BYTES = D_BYTES + X_BYTES;
 constexpr int LDS_BYTES = 2 * BUF_BYTES;
-constexpr int NCOLB = R * S * CH / 32;   // 18 column blocks of 32 (static check below)
-constexpr int WAVE_CB = 3;               // column blocks per wave
-constexpr int WAVE_KB = 2;               // k-blocks per wave (all of K = 64)
-constexpr int NACC = WAVE_KB * WAVE_CB;
-static_assert(NCOLB == 6 * WAVE_CB && WAVES == 6 * HALVES, "six waves of three column blocks per half");
-static_assert(WAVES / HALVES * 64 * NACC * 16 * 4 <= LDS_BYTES, "one half's accumulators fit in LDS");
+constexpr int PARK_WAVE = 64 * NACC * 16 * 4;  // one wave's accumulators
+static_assert(CB_WG == WSETS * WAVE_CB && WAVES == WSETS * PHASES && PHASES == 4, "3 x 4 waves");
+static_assert(2 * WSETS * PARK_WAVE <= LDS_BYTES, "two phases' accumulators fit in LDS");
 static_assert(DCAP % 8 == 0 && XCAP % 8 == 0, "whole 1 KB blocks");
 static_assert(LDS_BYTES <= 163840, "fits in the 160 KB LDS");
 
@@ -98,8 +101,20 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int img = blockIdx.x / a.chunks_per_img;
-    const int chunk = blockIdx.x - img * a.chunks_per_img;
+    // Workgroup -> (band, column half).  Workgroups are dealt to the 8 XCDs
+    // in turn, so the two halves of a band go 8 apart: same XCD, and the
+    // second one's row loads hit that XCD's L2.
+    int band, colh;
+    if (a.xcd_pairs) {
+        const int bid = blockIdx.x;
+        colh = (bid >> 3) & 1;
+        band = (bid & 7) + 8 * (bid >> 4);
+    } else {
+        colh = blockIdx.x & 1;
+        band = blockIdx.x >> 1;
+    }
+    const int img = band / a.chunks_per_img;
+    const int chunk = band - img * a.chunks_per_img;
     const int p_start = chunk * a.rows_per_wg;
     const int p_end = min(p_start + a.rows_per_wg, a.P);
     const int nrows = p_end - p_start;  // >= 1 by construction of the grid
@@ -113,14 +128,17 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     const u32x4 x_rs = make_buf_rsrc((const elem *)a.x + (size_t)img * a.H * a.W * CH, (uint32_t)(a.H * a.W * CH * 2));
     const u32x4 d_rs =
         make_buf_rsrc((const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH, (uint32_t)(nrows * Q * CH * 2));
-    auto dma_group = [&](int g) {
+    // (the waves of a workgroup start over a few microseconds; the first
+    // group's loads are spread over the first PW waves only)
+    constexpr int PW = 4;
+    auto dma_group = [&](int g, int nw) {
         const int d0 = g * GR;
-        if (d0 >= nrows) return;
+        if (d0 >= nrows || wave >= nw) return;
         const int ndy = min(GR, nrows - d0);  // dy rows of the group
         const int nx = ndy + HALO;            // x rows it reads
         unsigned char *buf = smem + (g & 1) * BUF_BYTES;
         constexpr int DBLK = DCAP / 8, NBLK = (DCAP + XCAP) / 8;
-        for (int b = wave; b < NBLK; b += WAVES) {
+        for (int b = wave; b < NBLK; b += nw) {
             const bool is_dy = b < DBLK;
             const int v = (is_dy ? b : b - DBLK) * 8 + (lane >> 3);
             const int row = (int)fdiv((uint32_t)v, a.div_xw), col = v - row * XW;
@@ -137,35 +155,35 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         }
     };
 
-    dma_group(0);
+    dma_group(0, PW);
     wait_vm_all();
     __syncthreads();
-    dma_group(1);
+    dma_group(1, WAVES);
 
-    // ---- per-wave roles: both k-blocks, column blocks cb0..cb0+2 (all of
-    // tap row r: column block cb is tap cb/2 = (r, s), channel half cb&1),
-    // and the steps of one parity
-    const int half = wave / 6;
-    const int cb0 = WAVE_CB * (wave % 6);
+    // ---- per-wave roles: both k-blocks, column blocks cb0..cb0+2 of the
+    // workgroup's half (all of one tap row r: column block cb is tap cb/2 =
+    // (r, s), channel half cb&1), and the steps t = phase (mod 4)
+    const int phase = wave / WSETS;
+    const int cb0 = colh * CB_WG + WAVE_CB * (wave % WSETS);
     const int tap_r = (cb0 >> 1) / S;
     const int l32 = lane & 31, lhi = lane >> 5;
 
-    // ---- per-lane read offsets (first step of this half in a buffer).  Read
-    // rd of a step covers pixels v = 16*t + 8*lhi + 4*rd + 0..3; this lane
-    // points at pixel v + L/4.  Steps move every read by a multiple of 16
+    // ---- per-lane read offsets (first step of this phase in a buffer).
+    // Read rd of a step covers pixels v = 16*t + 8*lhi + 4*rd + 0..3; this
+    // lane points at pixel v + L/4.  Steps move every read by a multiple of 16
     // pixels, which keeps bit 1 of the pixel index and so the swizzle.  They
     // are recomputed per body from an opaque copy of the lane id (holding
     // them across the loop would cost registers the fragments need).
     auto dy_off = [&](int ln, int rd, int kb) {
         const int L_ = ln & 15, g_ = (ln >> 4) & 1, h_ = ln >> 5;
         const int c_ = 16 * g_ + 4 * (L_ & 3);
-        const int v = 16 * half + 8 * h_ + 4 * rd + (L_ >> 2);
+        const int v = 16 * phase + 8 * h_ + 4 * rd + (L_ >> 2);
         return v * PIXB + swz_chunk(kb * 4 + (c_ >> 3), v) * 16 + (c_ & 7) * 2;
     };
     auto x_off = [&](int ln, int rd, int i) {
         const int L_ = ln & 15, g_ = (ln >> 4) & 1, h_ = ln >> 5;
         const int c_ = 16 * g_ + 4 * (L_ & 3);
-        const int v = 16 * half + 8 * h_ + 4 * rd + (L_ >> 2);
+        const int v = 16 * phase + 8 * h_ + 4 * rd + (L_ >> 2);
         const int cb = cb0 + i, tap_s = (cb >> 1) - tap_r * S;
         const int xv = v + tap_r * DIL * XW + tap_s * DIL;
         return D_BYTES + xv * PIXB + swz_chunk((cb & 1) * 4 + (c_ >> 3), xv) * 16 + (c_ & 7) * 2;
@@ -183,11 +201,11 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     };
     // one step's fragments as raw 64-bit halves: [2*kb + rd] dy, [4 + 2*i + rd] x
     typedef s16x4 Frag[2 * WAVE_KB + 2 * WAVE_CB];
-    // lane addresses of a body's first step; step k (k-th of this half) adds
-    // k*HALVES*2 KB, which the reads take as an immediate offset (the empty
-    // asm keeps the compiler from re-associating base + offset + k*4 KB into
+    // lane addresses of a body's first step; step k (k-th of this phase) adds
+    // k*PHASES*2 KB, which the reads take as an immediate offset (the empty
+    // asm keeps the compiler from re-associating base + offset + k*8 KB into
     // one register per step)
-    constexpr int STEPB = HALVES * 16 * PIXB;
+    constexpr int STEPB = PHASES * 16 * PIXB;
     const lds_u8 *ad[2][WAVE_KB], *ax[2][WAVE_CB];
     auto set_body = [&](const lds_u8 *base) {
         int ln = lane;
@@ -229,14 +247,14 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         }
     };
 
-    // Steps run in straight-line bodies of BODY (of one parity): the reads
-    // of step k+1 are issued before the MFMAs of step k, and nothing is in
+    // Steps run in straight-line bodies of BODY (of one phase): the reads of
+    // step k+1 are issued before the MFMAs of step k, and nothing is in
     // flight across bodies.  Steps past the group's pixels read zero dy
     // pixels.
     const int ngroups = (nrows + GR - 1) / GR;
     for (int g = 0; g < ngroups; ++g) {
         const unsigned char *buf = smem + (g & 1) * BUF_BYTES;
-        const int nbody = a.steps_per_group / (HALVES * BODY);
+        const int nbody = a.steps_per_group / (PHASES * BODY);
         for (int bd = 0; bd < nbody; ++bd) {
             set_body((const lds_u8 *)buf + bd * BODY * STEPB);
             Frag f[BODY];
@@ -251,38 +269,74 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         }
         wait_vm_all();     // the next group's rows
         __syncthreads();   // every wave is done with this group's buffer
-        dma_group(g + 2);  // into the buffer this group used
+        dma_group(g + 2, WAVES);  // into the buffer this group used
     }
 
-    // ---- the two halves' sums: half 1 parks its accumulators in LDS (the
-    // buffers are idle now), half 0 adds them (half 0 + half 1, a fixed
-    // order) and writes the workgroup's fp32 partials [K][R*S*C].
-    float *park = (float *)smem + (wave % 6) * (NACC * 16 * 64) + lane;
-    if (half == 1) {
+    // ---- the four phases' sums, in a fixed order (p0 + p2) + (p1 + p3),
+    // through LDS (the buffers are idle now): phases 2 and 3 park, phases 0
+    // and 1 add; then phase 1 parks and phase 0 adds.  A parked wave is
+    // [NACC*4][64 lanes] of 16-byte pieces (4 consecutive accumulator rows).
+    auto park_slot = [&](int slot) { return (f32x4 *)(smem + slot * PARK_WAVE) + lane; };
+    auto park = [&](f32x4 *p) {
 #pragma unroll
         for (int kb = 0; kb < WAVE_KB; ++kb)
 #pragma unroll
             for (int i = 0; i < WAVE_CB; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) park[((kb * WAVE_CB + i) * 16 + r) * 64] = acc[kb][i][r];
-    }
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16 &v = acc[kb][i];
+                    p[((kb * WAVE_CB + i) * 4 + q) * 64] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+                }
+    };
+    auto add = [&](const f32x4 *p) {
+#pragma unroll
+        for (int kb = 0; kb < WAVE_KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < WAVE_CB; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 t = p[((kb * WAVE_CB + i) * 4 + q) * 64];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[kb][i][4 * q + e] += t[e];
+                }
+    };
+    const int ws = wave % WSETS;
+    if (phase >= 2) park(park_slot((phase - 2) * WSETS + ws));
     __syncthreads();
-    if (half == 0) {
-        // 32x32 block layout: lane holds column (lane & 31), rows
-        // 8*(r/4) + 4*(lane/32) + r%4
-        constexpr int NCOLS = R * S * CH;
-        float *out = (float *)a.out + (size_t)blockIdx.x * a.part_stride;
+    if (phase < 2) add(park_slot(phase * WSETS + ws));
+    __syncthreads();
+    if (phase == 1) park(park_slot(ws));
+    __syncthreads();
+    // Phase 0 adds and lays the workgroup's partial tile out in LDS as
+    // [K][CB_WG*32] floats (32x32 block layout: lane holds column lane&31,
+    // rows 8*(r/4) + 4*(lane/32) + r%4); then every wave copies rows of it
+    // to memory with 16-byte stores.
+    constexpr int TCOLS = CB_WG * 32;
+    float *tile = (float *)smem + WSETS * (PARK_WAVE / 4);  // past phase 1's parked waves
+    static_assert(WSETS * PARK_WAVE + 64 * TCOLS * 4 <= LDS_BYTES, "tile fits after the parked waves");
+    if (phase == 0) {
+        add(park_slot(ws));
 #pragma unroll
         for (int kb = 0; kb < WAVE_KB; ++kb)
 #pragma unroll
             for (int i = 0; i < WAVE_CB; ++i) {
-                const int col = (cb0 + i) * 32 + l32;
+                const int col = (WAVE_CB * ws + i) * 32 + l32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int k = kb * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-                    out[(size_t)k * NCOLS + col] = acc[kb][i][r] + park[((kb * WAVE_CB + i) * 16 + r) * 64];
+                    tile[k * TCOLS + col] = acc[kb][i][r];
                 }
             }
+    }
+    __syncthreads();
+    {
+        constexpr int NCOLS = R * S * CH;
+        constexpr int CHUNKS = 64 * TCOLS / 4;  // 16-byte pieces of the tile
+        float *out = (float *)a.out + (size_t)band * a.part_stride + colh * TCOLS;
+        for (int c = tid; c < CHUNKS; c += NT) {
+            const int k = c / (TCOLS / 4), col = (c - k * (TCOLS / 4)) * 4;
+            *(f32x4 *)(out + (size_t)k * NCOLS + col) = *(const f32x4 *)(tile + k * TCOLS + col);
+        }
     }
 }
 
@@ -292,7 +346,7 @@ int wgrad_band_steps(int Q)
 {
     const int xw = Q + wb::DIL * (wb::S - 1);
     int steps = (wb::GR * xw + 15) / 16;
-    constexpr int unit = wb::HALVES * wb::BODY;
+    constexpr int unit = wb::PHASES * wb::BODY;
     steps = (steps + unit - 1) / unit * unit;
     if (steps * 16 > wb::DCAP || steps * 16 + wb::HALO * xw + wb::DIL * (wb::S - 1) > wb::XCAP) return 0;
     return steps;
@@ -306,7 +360,7 @@ bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q)
 
 hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st)
 {
-    dim3 grid((unsigned)(a.N * a.chunks_per_img));
+    dim3 grid((unsigned)(2 * a.N * a.chunks_per_img));  // two column halves per band
     switch (dtype) {
     case CONV2D_DTYPE_F16: wgrad_band_kernel<EF16><<<grid, wb::NT, 0, st>>>(a); break;
     case CONV2D_DTYPE_BF16: wgrad_band_kernel<EBF16><<<grid, wb::NT, 0, st>>>(a); break;
