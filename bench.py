@@ -104,23 +104,27 @@ def main():
     name = args.workload
     wl = WL.WORKLOADS[name]
     prob, dt = wl["prob"], wl["dtype"]
-    if dt == "i8":
-        print("bench.py times the fp16/bf16 three-pass step; int8 is fprop only", file=sys.stderr)
+    if dt == "i8" and args.only != "fprop":
+        print("bench.py times the fp16/bf16 three-pass step; int8 is fprop only (use --only fprop)",
+              file=sys.stderr)
         sys.exit(2)
     P, Q = B.conv2d_output_size(prob)
     x = WL.make_x(name).to(dev)
     w = WL.make_w(name).to(dev)
     b = WL.make_bias(name).to(dev) if wl["bias"] else None
-    dy = WL.make_dy(name, P, Q).to(dev)
     relu = wl["relu"]
+    sc = wl.get("scales", (1.0, 1.0, 1.0))  # int8 requantisation scales (act, w, out)
     y = torch.empty((prob["N"], P, Q, prob["K"]), dtype=x.dtype, device=dev)
-    dx = torch.empty_like(x)
-    dw = torch.empty_like(w)
-    ws = {op: B.workspace_for(op, prob, dt, dev) for op in (0, 1, 2)}
+    ops = (0,) if dt == "i8" else (0, 1, 2)
+    ws = {op: B.workspace_for(op, prob, dt, dev) for op in ops}
+    if dt != "i8":
+        dy = WL.make_dy(name, P, Q).to(dev)
+        dx = torch.empty_like(x)
+        dw = torch.empty_like(w)
     stream = torch.cuda.current_stream()
 
     def step():
-        B.conv2d_fprop(prob, dt, x, w, b, relu, 1.0, 1.0, 1.0, y, ws[0], stream=stream)
+        B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, ws[0], stream=stream)
         B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream)
         B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)
 
@@ -141,7 +145,7 @@ def main():
         print(f"copy {COPY_BYTES} B: {us:.2f} us/launch, {2 * COPY_BYTES / us / 1e3:.1f} GB/s", flush=True)
         return
     if args.only:
-        run = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, 1.0, 1.0, 1.0, y, ws[0], stream=stream),
+        run = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, ws[0], stream=stream),
                "dgrad": lambda: B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream),
                "wgrad": lambda: B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)}[args.only]
         for _ in range(args.warmup):
@@ -154,7 +158,12 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.steps
         fl = flops(prob, P, Q)
-        print(f"{args.only} {name}: {us:.2f} us/launch, {fl / us / 1e6:.1f} TFLOP/s", flush=True)
+        esz = 1 if dt == "i8" else 2
+        nx, ny = prob["N"] * prob["H"] * prob["W"] * prob["C"], prob["N"] * P * Q * prob["K"]
+        nw = prob["K"] * prob["R"] * prob["S"] * (prob["C"] // prob["groups"])
+        mb = esz * (nx + ny + nw) / 1e6  # algorithmic bytes: each tensor once
+        print(f"{args.only} {name}: {us:.2f} us/launch, {fl / us / 1e6:.1f} T{'OP' if dt == 'i8' else 'FLOP'}/s, "
+              f"{mb / us * 1e3:.1f} GB/s algorithmic ({mb:.2f} MB)", flush=True)
         return
 
     for _ in range(args.warmup):
@@ -173,7 +182,7 @@ def main():
     # Timed region 2: each pass alone, K back-to-back launches between two HIP
     # events recorded on the launch stream -> per-pass time per launch (the
     # figure rocprofv3's kernel trace reports as the kernels' duration).
-    runs = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, 1.0, 1.0, 1.0, y, ws[0], stream=stream),
+    runs = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, ws[0], stream=stream),
             "dgrad": lambda: B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream),
             "wgrad": lambda: B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)}
     pass_us = {}
@@ -198,10 +207,12 @@ def main():
         "wgrad": esz * (elems_x + elems_y + elems_w),
     }
     plans = {n: B.conv2d_plan_info(op, prob, dt) for op, n in enumerate(("fprop", "dgrad", "wgrad"))}
+    direct = plans["fprop"]["kernel"] == 2  # groups > 1
     kernels = {
-        "fprop": ["band" if plans["fprop"]["tile"] == BAND_TILE else "implicit_gemm"],
-        "dgrad": ["band"] if plans["dgrad"]["tile"] == BAND_TILE else ["filter_relayout", "implicit_gemm"],
-        "wgrad": (["wgrad_band" if plans["wgrad"]["tile"] == WGRAD_BAND_TILE else "wgrad_gemm"]
+        "fprop": ["direct" if direct else "band" if plans["fprop"]["tile"] == BAND_TILE else "implicit_gemm"],
+        "dgrad": (["direct"] if direct else ["band"] if plans["dgrad"]["tile"] == BAND_TILE
+                  else ["filter_relayout", "implicit_gemm"]),
+        "wgrad": (["direct" if direct else "wgrad_band" if plans["wgrad"]["tile"] == WGRAD_BAND_TILE else "wgrad_gemm"]
                   + (["splitk_reduce"] if plans["wgrad"]["split_k"] > 1 else [])),
     }
     passes = {}

@@ -177,6 +177,14 @@ int choose_direct_splits(long long outputs, long long npix)
     return (int)std::max(1LL, std::min(s, 4096LL));
 }
 
+int choose_direct_tiled_splits(long long wgs_per_slice, long long npix)
+{
+    // about two workgroups per CU, slices of at least 64 pixels
+    long long s = (2 * kNumCUs) / std::max(1LL, wgs_per_slice);
+    s = std::min(s, std::max(1LL, npix / 64));
+    return (int)std::max(1LL, std::min(s, 4096LL));
+}
+
 int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, Plan *pl)
 {
     int st = validate(prob, &pl->d);
@@ -197,13 +205,25 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     pl->tile = 0;
 
     if (d.G > 1) {
+        // tile 0: one thread per output; tile 1: LDS-tiled dot-product kernel
+        // (16-bit types, channel counts in 16-byte vectors, staging fits LDS)
         pl->kernel = 2;
-        pl->num_tiles = 1;
-        if (algo && algo->tile > 1) return CONV2D_ERR_UNSUPPORTED;
+        const bool tiled = op == CONV2D_OP_WGRAD
+                               ? direct_wgrad_tiled_ok(dtype, (int)d.Cg, (int)d.Kg)
+                               : direct_tiled_rows(op == CONV2D_OP_DGRAD, dtype, (int)d.R, (int)d.S, (int)d.W,
+                                                   (int)d.Q, (int)d.Cg, (int)d.Kg) > 0;
+        pl->num_tiles = tiled ? 2 : 1;
+        if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
+        pl->tile = (algo && algo->tile) ? algo->tile - 1 : pl->num_tiles - 1;
         if (op == CONV2D_OP_WGRAD) {
             const long long outputs = d.K * d.R * d.S * d.Cg;
             const long long npix = d.N * d.P * d.Q;
-            int s = (algo && algo->split_k) ? algo->split_k : choose_direct_splits(outputs, npix);
+            const long long wgs = pl->tile ? direct_wgrad_tiled_wgs((int)d.R, (int)d.S, (int)d.Cg, (int)d.Kg,
+                                                                    (int)d.G)
+                                           : 0;
+            int s = (algo && algo->split_k) ? algo->split_k
+                    : pl->tile              ? choose_direct_tiled_splits(wgs, npix)
+                                            : choose_direct_splits(outputs, npix);
             if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
             pl->split_k = s;
             if (s > 1) pl->ws_bytes = round_up((size_t)s * splitk_stride(outputs) * sizeof(float), 256);
@@ -382,6 +402,10 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
         a.dh = (int)d.dh; a.dw = (int)d.dw; a.G = (int)d.G; a.Cg = (int)d.Cg; a.Kg = (int)d.Kg;
         a.relu = relu; a.requant_m = m; a.splits = 1;
         a.total = d.N * d.P * d.Q * d.K;
+        if (pl.tile == 1) {
+            a.tiled = 1;
+            a.rows = direct_tiled_rows(0, dtype, a.R, a.S, a.W, a.Q, a.Cg, a.Kg);
+        }
         return hip_status(launch_direct_fprop(dtype, a, s));
     }
 
@@ -433,6 +457,10 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
         a.dh = (int)d.dh; a.dw = (int)d.dw; a.G = (int)d.G; a.Cg = (int)d.Cg; a.Kg = (int)d.Kg;
         a.splits = 1;
         a.total = d.N * d.H * d.W * d.C;
+        if (pl.tile == 1) {
+            a.tiled = 1;
+            a.rows = direct_tiled_rows(1, dtype, a.R, a.S, a.W, a.Q, a.Cg, a.Kg);
+        }
         return hip_status(launch_direct_dgrad(dtype, a, s));
     }
 
@@ -515,6 +543,7 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
         a.pix_per_split = (npix + pl.split_k - 1) / pl.split_k;
         a.total = d.K * d.R * d.S * d.Cg;
         a.part_stride = splitk_stride(a.total);
+        a.tiled = pl.tile == 1;
         hipError_t e = launch_direct_wgrad(dtype, a, s);
         if (e != hipSuccess || pl.split_k == 1) return hip_status(e);
         return hip_status(

@@ -204,7 +204,14 @@ struct DirectArgs {
     uint32_t npix;          // wgrad: N*P*Q
     uint32_t pix_per_split; // wgrad
     long long total;        // output elements (per split for wgrad)
+    int tiled;              // use the LDS-tiled kernel (direct_tiled_rows / direct_wgrad_tiled_ok)
+    int rows;               // fprop / dgrad tiled: output rows per workgroup
 };
+// Output rows per workgroup of the LDS-tiled direct fprop (op 0) / dgrad
+// (op 1) kernel for 16-bit types, or 0 if it does not apply.
+int direct_tiled_rows(int op, int dtype, int R, int S, int W, int Q, int Cg, int Kg);
+bool direct_wgrad_tiled_ok(int dtype, int Cg, int Kg);
+long long direct_wgrad_tiled_wgs(int R, int S, int Cg, int Kg, int G);  // workgroups per pixel slice
 hipError_t launch_direct_fprop(int dtype, const DirectArgs &a, hipStream_t st);
 hipError_t launch_direct_dgrad(int dtype, const DirectArgs &a, hipStream_t st);
 hipError_t launch_direct_wgrad(int dtype, const DirectArgs &a, hipStream_t st);

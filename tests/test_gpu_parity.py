@@ -56,6 +56,15 @@ CASES = [
     ("depthwise", problem(2, 8, 10, 9, 8, 3, 3, pad=(1, 1), groups=8), "f16", "int", True, False),
     ("grouped_gauss", problem(2, 24, 11, 11, 24, 3, 3, pad=(1, 1), groups=3), "bf16", "gauss",
      True, False),
+    # grouped problems whose channel counts take the LDS-tiled direct kernels:
+    # several output rows per workgroup with a partial last one, strides and
+    # dilations, a filter taller than wide
+    ("grouped_tiled_s2d2", problem(3, 32, 21, 17, 48, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2),
+                                   groups=2), "f16", "int", True, True),
+    ("grouped_tiled_asym", problem(2, 48, 13, 21, 48, 3, 2, pad=(1, 0), stride=(1, 2), dil=(2, 1),
+                                   groups=3), "bf16", "gauss", True, False),
+    ("grouped_tiled_wide", problem(2, 64, 9, 30, 64, 3, 3, pad=(1, 1), groups=2), "f16", "gauss",
+     False, False),
     # stride-1 problems with 64 source channels and a 3x3 filter run on the
     # band kernel (filter + ring of input rows in LDS): two column segments,
     # partial N tiles, one-row and multi-group row ranges, padding 0..3
@@ -158,6 +167,26 @@ def test_wgrad_band_and_generic_agree():
     assert info["num_tiles"] == 2 and info["tile"] == 1  # band kernel is the default
     for t in (1, 2):
         check(f64(run_wgrad(prob, "f16", x, dy, algo=dict(tile=t))), ref, "f16", "exact", f"wgrad tile {t}")
+
+
+@pytest.mark.parametrize("prob", [
+    problem(2, 16, 11, 9, 32, 3, 3, pad=(1, 1), groups=2),
+    problem(3, 64, 14, 13, 96, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2), groups=4),
+], ids=["g2", "c4g_like"])
+def test_grouped_every_tile(prob):
+    """Both direct kernels (one thread per output, LDS-tiled) against the oracle."""
+    x, w, b, dy = case_inputs(prob, "f16", "int", seed=50)
+    ref_y = oracle_fprop_out(prob, "f16", x, w, b, True)
+    ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
+    ref_dw = oracle.wgrad(prob, f64(x), f64(dy))
+    for op in (B.CONV2D_OP_FPROP, B.CONV2D_OP_DGRAD, B.CONV2D_OP_WGRAD):
+        info = B.conv2d_plan_info(op, prob, "f16")
+        assert info["kernel"] == 2 and info["num_tiles"] == 2 and info["tile"] == 1
+    for t in (1, 2):
+        algo = dict(tile=t)
+        check(f64(run_fprop(prob, "f16", x, w, b, True, algo=algo)), ref_y, "f16", "exact", f"tile {t}")
+        check(f64(run_dgrad(prob, "f16", dy, w, algo=algo)), ref_dx, "f16", "exact", f"dgrad tile {t}")
+        check(f64(run_wgrad(prob, "f16", x, dy, algo=algo)), ref_dw, "f16", "exact", f"wgrad tile {t}")
 
 
 @pytest.mark.parametrize("groups", [1, 2])
