@@ -64,10 +64,45 @@ __device__ inline s16x4 tr16(const unsigned char *p)
 {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
-__device__ inline float relu_floor(float v, float lo, uint32_t keep)
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef short s2v __attribute__((ext_vector_type(2)));
+template <class E>
+struct Pack2;
+template <>
+struct Pack2<EF16> {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    __device__ static inline uint32_t cvt(f2v v) { return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2)); }
+};
+template <>
+struct Pack2<EBF16> {
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    __device__ static inline uint32_t cvt(f2v v) { return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2)); }
+};
+// Two epilogue values to a packed pair, rounded to nearest even by one packed
+// conversion.  ReLU (v <= 0, -0 and NaN included, -> +0), which commutes with
+// the rounding: a max against 0 that maps NaN to 0 (packed fp16 after the
+// conversion; fp32 before it for bf16, which has no packed max), then an
+// int16 max of the packed halves, which turns a -0 into +0.
+template <class E, bool RELU>
+__device__ inline uint32_t out_pair(float a, float b)
 {
-    return v > lo ? v : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & keep);
+    constexpr bool F16 = E::kDtype == CONV2D_DTYPE_F16;
+    if (RELU && !F16) {
+        a = __builtin_fmaxf(a, 0.0f);
+        b = __builtin_fmaxf(b, 0.0f);
+    }
+    uint32_t p = Pack2<E>::cvt(f2v{a, b});
+    if (RELU && F16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        p = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(h2, p), h2{0, 0}));
+    }
+    if (RELU) p = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s2v, p), s2v{0, 0}));
+    return p;
 }
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
 
 template <int R, int S, int CIN, int DIL, bool TRANS>
 struct BandCfg {
@@ -165,24 +200,27 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         r0 = g == 0 ? 0 : g * C::GR + C::HALO_R;
         r1 = min((g + 1) * C::GR + C::HALO_R, nrows + C::HALO_R);
     };
+    // All global memory traffic is issued by the first half of the waves (the
+    // "I/O waves"): they start well before the second half and, being older,
+    // win the MFMA arbitration and finish each group first, so their loads
+    // and stores fill time they would otherwise spend at the group barrier.
+    // I/O wave w moves blocks w and w + PW of every ring row.
+    constexpr int PW = C::WAVES / 2;
+    const bool io_wave = wave < PW;
+    static_assert(PW == C::GR, "I/O wave w stores output row w of a group");
+    const int off2 = lane_src(wave + PW);
     auto dma_group = [&](int g) {
         int r0, r1;
         group_rows(g, r0, r1);
-        for (int rr = r0; rr < r1; ++rr) dma_row(rr, wave, my_off);
-    };
-
-    // ---- prologue: the filter tile and group 0's rows, then group 1's rows.
-    // The first half of the waves starts well before the second, so it issues
-    // all of the prologue's loads.
-    constexpr int PW = C::WAVES / 2;
-    if (wave < PW) {
-        int r0, r1;
-        group_rows(0, r0, r1);
-        const int off2 = lane_src(wave + PW);
         for (int rr = r0; rr < r1; ++rr) {
             dma_row(rr, wave, my_off);
             dma_row(rr, wave + PW, off2);
         }
+    };
+
+    // ---- prologue: the filter tile and group 0's rows, then group 1's rows.
+    if (io_wave) {
+        dma_group(0);
         const int fbytes = (TRANS ? CIN * R * S * a.ngemm : a.ngemm * C::KG) * 2;
         const u32x4 w_rs = make_buf_rsrc(a.bmat, (uint32_t)fbytes);
         for (int b = wave; b < C::FBLOCKS; b += PW) {
@@ -203,11 +241,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
     }
     {
-        if (tid < C::BN)
-            bias_s[tid] = (a.bias && n0 + tid < a.ngemm) ? E::to_f32(((const elem *)a.bias)[n0 + tid]) : 0.0f;
+        // the bias in the accumulator layout, [nb][lhi][16]: entry i of a
+        // lane's acc holds channel 32*nb + 8*(i/4) + 4*lhi + i%4
+        if (tid < C::BN) {
+            const int i = tid & 15, lh = (tid >> 4) & 1, hb = tid >> 5;
+            const int ch = n0 + 32 * hb + 8 * (i >> 2) + 4 * lh + (i & 3);
+            bias_s[tid] = (a.bias && ch < a.ngemm) ? E::to_f32(((const elem *)a.bias)[ch]) : 0.0f;
+        }
         wait_vm_all();
         __syncthreads();
-        dma_group(1);  // into slots group 0 does not read
+        if (io_wave) dma_group(1);  // into slots group 0 does not read
     }
 
     // ---- the wave's filter fragments (A operand): rows n0 + 32*nb + 0..31,
@@ -247,20 +290,35 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         t_off[s] = col * C::PIXB + ((lhi ^ ((col >> 1) & 7)) << 4);
     }
 
-    // ReLU (v <= 0, -0 and NaN included, -> +0) without lane masks:
-    // v > relu_lo ? v : v & relu_keep, with (0, 0) for ReLU and (-inf, ~0) without
-    const float relu_lo = a.relu ? 0.0f : -__builtin_inff();
-    const uint32_t relu_keep = a.relu ? 0u : ~0u;
     const int ngroups = (nrows + C::GR - 1) / C::GR;
     const int prw = wave >> 1;
+    // ---- epilogue, part 2 (I/O waves, one group later): whole pixels
+    // (128-byte lines) from the staging to memory.  I/O wave w stores row w
+    // of the group, 8 pixels per instruction; lane i takes stored chunk i%8
+    // of pixel i/8, i.e. channel chunk (i%8) ^ swizzle(pixel).
+    auto store_rows = [&](int g) {
+        const int pr = g * C::GR + wave;
+        if (pr >= nrows) return;
+        const unsigned char *stage = ostage + (g & 1) * C::OSTAGE_BYTES + wave * C::SLOTB;
+        elem *drow = (elem *)a.dst + ((size_t)img * a.P + p_start + pr) * a.Q * a.ngemm;  // wave-uniform
+#pragma unroll
+        for (int t = 0; t < C::RCOLS / 8; ++t) {
+            const int px = 8 * t + (lane >> 3);
+            const int chunk = (lane & 7) ^ ((px >> 1) & 7);
+            const u32x4 v = *(const u32x4 *)(stage + px * C::PIXB + (lane & 7) * 16);
+            const int q = q0 + px, ch = n0 + chunk * 8;
+            if (px < C::SEG && q < a.Q && ch < a.ngemm) *(u32x4 *)(drow + (unsigned)(q * a.ngemm + ch)) = v;
+        }
+    };
     __syncthreads();  // every wave holds its filter fragments: the staging area is free
     for (int g = 0; g < ngroups; ++g) {
         const int pr = g * C::GR + prw;  // output row of this wave, relative to p_start
         const bool active = pr < nrows;
         f32x16 acc[2];
-        acc[0] = f32x16{};
-        acc[1] = f32x16{};
         if (active) {
+            // the accumulators start at the bias (zero for dgrad)
+            acc[0] = *(const f32x16 *)(bias_s + (nb * 2 + lhi) * 16);
+            acc[1] = acc[0];
             int rowb[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) rowb[r] = ((pr + r * DIL) % C::NSLOT) * C::SLOTB;
@@ -284,17 +342,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // ---- epilogue, part 1: bias, ReLU, round, into the output staging
+        // ---- epilogue, part 1: ReLU, round, into the output staging
         // (double-buffered) as [row][pixel][channel] with the ring's chunk
         // swizzle.  Lane holds pixel mb*32 + l32, channels 32*nb + 8*j +
         // 4*lhi + 0..3 in acc[mb][4j..4j+3]: 8 bytes, half lhi of chunk 4nb+j.
         unsigned char *stage = ostage + (g & 1) * C::OSTAGE_BYTES + prw * C::SLOTB;
-        if (active) {
-            // all bias reads before any staging write (the compiler keeps LDS
-            // reads and writes in order), and ReLU as pure vector ops
-            f32x4 bv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = *(const f32x4 *)(bias_s + nb * 32 + 8 * j + 4 * lhi);
+        auto epilogue = [&](auto relu_c) {
+            constexpr bool RELU = decltype(relu_c)::value;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 const int px = mb * 32 + l32;
@@ -302,38 +356,27 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 for (int j = 0; j < 4; ++j) {
                     uint32_t v[2];
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const uint32_t lo = E::from_f32(band::relu_floor(acc[mb][4 * j + 2 * t] + bv[j][2 * t], relu_lo, relu_keep));
-                        const uint32_t hi =
-                            E::from_f32(band::relu_floor(acc[mb][4 * j + 2 * t + 1] + bv[j][2 * t + 1], relu_lo, relu_keep));
-                        v[t] = lo | (hi << 16);
-                    }
+                    for (int t = 0; t < 2; ++t)
+                        v[t] = band::out_pair<E, RELU>(acc[mb][4 * j + 2 * t], acc[mb][4 * j + 2 * t + 1]);
                     const int chunk = (4 * nb + j) ^ ((px >> 1) & 7);
                     *(uint2 *)(stage + px * C::PIXB + chunk * 16 + lhi * 8) = uint2{v[0], v[1]};
                 }
             }
-        }
-        wait_vm_all();  // the next group's rows (and this wave's older stores)
-        __syncthreads();      // every wave is done with this group's rows; the staging is complete
-
-        // ---- epilogue, part 2: whole pixels (128-byte lines) from the
-        // staging to memory.  Wave nb of a row stores pixels 32*nb..+31,
-        // 8 pixels per instruction; lane i takes stored chunk i%8 of pixel
-        // i/8, i.e. channel chunk (i%8) ^ swizzle(pixel).
+        };
         if (active) {
-            const int p = p_start + pr;
-            elem *drow = (elem *)a.dst + ((size_t)img * a.P + p) * a.Q * a.ngemm;  // wave-uniform
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int px = nb * 32 + 8 * t + (lane >> 3);
-                const int chunk = (lane & 7) ^ ((px >> 1) & 7);
-                const u32x4 v = *(const u32x4 *)(stage + px * C::PIXB + (lane & 7) * 16);
-                const int q = q0 + px, ch = n0 + chunk * 8;
-                if (px < C::SEG && q < a.Q && ch < a.ngemm) *(u32x4 *)(drow + (unsigned)(q * a.ngemm + ch)) = v;
-            }
+            if (a.relu)
+                epilogue(band::BoolC<true>{});
+            else
+                epilogue(band::BoolC<false>{});
         }
-        dma_group(g + 2);  // into the slots of the rows only this group read
+        if (io_wave) {
+            wait_vm_all();  // the next group's rows (and this wave's older stores)
+            if (g > 0) store_rows(g - 1);
+        }
+        __syncthreads();  // every wave is done with this group's rows; the staging is complete
+        if (io_wave) dma_group(g + 2);  // into the slots of the rows only this group read
     }
+    if (io_wave) store_rows(ngroups - 1);
 }
 
 bool band_supported(int R, int S, int cin, int dil)

@@ -76,6 +76,7 @@ CASES = [
     ("band_pad3", problem(2, 64, 8, 8, 64, 3, 3, pad=(3, 3)), "f16", "int", False, False),
     ("band_gauss", problem(8, 64, 28, 28, 64, 3, 3, pad=(1, 1)), "f16", "gauss", True, True),
     ("band_bf16_gauss", problem(4, 64, 17, 23, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
+    ("band_bf16_relu", problem(3, 64, 13, 40, 64, 3, 3, pad=(1, 1)), "bf16", "int", True, True),
     # wgrad band kernel (stride 1, 3x3, C = K = 64, Q % 4 == 0, Q <= 56):
     # two row groups with a partial last group, and one-row bands whose pixel
     # count is not a multiple of 16; the widest row it takes (Q = 56, several
@@ -94,6 +95,8 @@ def test_parity_cases(cid, prob, dtype, dist, bias, relu):
     x, w, b, dy = case_inputs(prob, dtype, dist, seed=zlib.crc32(cid.encode()), bias=bias)
     y = run_fprop(prob, dtype, x, w, b, relu)
     check(f64(y), oracle_fprop_out(prob, dtype, x, w, b, relu), dtype, mode, f"{cid} fprop")
+    if relu:  # ReLU gives +0, never -0
+        assert not bool((y.view(torch.int16) == -32768).any()), f"{cid}: -0 after ReLU"
     dx = run_dgrad(prob, dtype, dy, w, fill=float("nan"))
     check(f64(dx), oracle.dgrad(prob, f64(dy), f64(w)), dtype, mode, f"{cid} dgrad")
     dw = run_wgrad(prob, dtype, x, dy)
