@@ -200,11 +200,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         r0 = g == 0 ? 0 : g * C::GR + C::HALO_R;
         r1 = min((g + 1) * C::GR + C::HALO_R, nrows + C::HALO_R);
     };
-    // All global memory traffic is issued by the first half of the waves (the
-    // "I/O waves"): they start well before the second half and, being older,
-    // win the MFMA arbitration and finish each group first, so their loads
-    // and stores fill time they would otherwise spend at the group barrier.
-    // I/O wave w moves blocks w and w + PW of every ring row.
+    // After the prologue all global memory traffic is issued by the first
+    // half of the waves (the "I/O waves"): being older, they win the MFMA
+    // arbitration against the second half on their SIMD and finish each group
+    // first, so their loads and stores fill time they would otherwise spend
+    // at the group barrier.  I/O wave w moves blocks w and w + PW of every
+    // ring row.
     constexpr int PW = C::WAVES / 2;
     const bool io_wave = wave < PW;
     static_assert(PW == C::GR, "I/O wave w stores output row w of a group");
@@ -218,12 +219,17 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
     };
 
-    // ---- prologue: the filter tile and group 0's rows, then group 1's rows.
-    if (io_wave) {
-        dma_group(0);
+    // ---- prologue: the filter tile and group 0's rows (every wave a share),
+    // then group 1's rows.
+    {
+        {
+            int r0, r1;
+            group_rows(0, r0, r1);
+            for (int rr = r0; rr < r1; ++rr) dma_row(rr, wave, my_off);
+        }
         const int fbytes = (TRANS ? CIN * R * S * a.ngemm : a.ngemm * C::KG) * 2;
         const u32x4 w_rs = make_buf_rsrc(a.bmat, (uint32_t)fbytes);
-        for (int b = wave; b < C::FBLOCKS; b += PW) {
+        for (int b = wave; b < C::FBLOCKS; b += C::WAVES) {
             const int p = b * 64 + lane;
             const int row = p / C::FROWCH, col = p - row * C::FROWCH;
             unsigned voff = kBufOOB;

@@ -128,9 +128,6 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     const u32x4 x_rs = make_buf_rsrc((const elem *)a.x + (size_t)img * a.H * a.W * CH, (uint32_t)(a.H * a.W * CH * 2));
     const u32x4 d_rs =
         make_buf_rsrc((const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH, (uint32_t)(nrows * Q * CH * 2));
-    // (the waves of a workgroup start over a few microseconds; the first
-    // group's loads are spread over the first PW waves only)
-    constexpr int PW = 4;
     auto dma_group = [&](int g, int nw) {
         const int d0 = g * GR;
         if (d0 >= nrows || wave >= nw) return;
@@ -155,7 +152,7 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         }
     };
 
-    dma_group(0, PW);
+    dma_group(0, WAVES);
     wait_vm_all();
     __syncthreads();
     dma_group(1, WAVES);
