@@ -89,6 +89,10 @@ static_assert(2 * WSETS * PARK_WAVE <= LDS_BYTES, "two phases' accumulators fit 
 static_assert(DCAP % 8 == 0 && XCAP % 8 == 0, "whole 1 KB blocks");
 static_assert(LDS_BYTES <= 163840, "fits in the 160 KB LDS");
 
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
 __device__ inline int swz_chunk(int chunk, int v) { return chunk ^ (((v >> 1) & 1) << 2); }
 }  // namespace wb
 
@@ -270,70 +274,75 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     }
 
     // ---- the four phases' sums, in a fixed order (p0 + p2) + (p1 + p3),
-    // through LDS (the buffers are idle now): phases 2 and 3 park, phases 0
-    // and 1 add; then phase 1 parks and phase 0 adds.  A parked wave is
-    // [NACC*4][64 lanes] of 16-byte pieces (4 consecutive accumulator rows).
-    auto park_slot = [&](int slot) { return (f32x4 *)(smem + slot * PARK_WAVE) + lane; };
-    auto park = [&](f32x4 *p) {
+    // through LDS (the buffers are idle now).  Round 1: phases 2 and 3 park
+    // all their accumulators, phases 0 and 1 add them.  Round 2: phase 0
+    // keeps k-block 0 and phase 1 k-block 1; each parks the other block and
+    // adds the one parked for it, then stores its rows of the partial tile.
+    // A parked block set is [blocks*4][64 lanes] of 16-byte pieces (4
+    // consecutive accumulator rows).
+    constexpr int PARK_HALF = PARK_WAVE / WAVE_KB;  // one k-block's accumulators
+    const int ws_ = wave % WSETS;
+    auto slot = [&](int s, int bytes) { return (f32x4 *)(smem + s * bytes) + lane; };
+    // park / add k-blocks [KB0, KB0 + NKB) (compile-time, so acc stays in registers)
+    auto park = [&](f32x4 *p, auto kb0_c, auto nkb_c) {
+        constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
 #pragma unroll
-        for (int kb = 0; kb < WAVE_KB; ++kb)
+        for (int kb = KB0; kb < KB0 + NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < WAVE_CB; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f32x16 &v = acc[kb][i];
-                    p[((kb * WAVE_CB + i) * 4 + q) * 64] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+                    p[(((kb - KB0) * WAVE_CB + i) * 4 + q) * 64] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
                 }
     };
-    auto add = [&](const f32x4 *p) {
+    auto add = [&](const f32x4 *p, auto kb0_c, auto nkb_c) {
+        constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
 #pragma unroll
-        for (int kb = 0; kb < WAVE_KB; ++kb)
+        for (int kb = KB0; kb < KB0 + NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < WAVE_CB; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4 t = p[((kb * WAVE_CB + i) * 4 + q) * 64];
+                    const f32x4 t = p[(((kb - KB0) * WAVE_CB + i) * 4 + q) * 64];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[kb][i][4 * q + e] += t[e];
                 }
     };
-    const int ws = wave % WSETS;
-    if (phase >= 2) park(park_slot((phase - 2) * WSETS + ws));
-    __syncthreads();
-    if (phase < 2) add(park_slot(phase * WSETS + ws));
-    __syncthreads();
-    if (phase == 1) park(park_slot(ws));
-    __syncthreads();
-    // Phase 0 adds and lays the workgroup's partial tile out in LDS as
-    // [K][CB_WG*32] floats (32x32 block layout: lane holds column lane&31,
-    // rows 8*(r/4) + 4*(lane/32) + r%4); then every wave copies rows of it
-    // to memory with 16-byte stores.
-    constexpr int TCOLS = CB_WG * 32;
-    float *tile = (float *)smem + WSETS * (PARK_WAVE / 4);  // past phase 1's parked waves
-    static_assert(WSETS * PARK_WAVE + 64 * TCOLS * 4 <= LDS_BYTES, "tile fits after the parked waves");
-    if (phase == 0) {
-        add(park_slot(ws));
-#pragma unroll
-        for (int kb = 0; kb < WAVE_KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i) {
-                const int col = (WAVE_CB * ws + i) * 32 + l32;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int k = kb * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-                    tile[k * TCOLS + col] = acc[kb][i][r];
-                }
-            }
-    }
-    __syncthreads();
-    {
+    // the partial tile's rows k = 32*KB + 0..31 in this wave's columns: lane
+    // holds column l32, rows 8*(r/4) + 4*(lane/32) + r%4 of each block
+    auto store = [&](auto kb_c) {
+        constexpr int KB = decltype(kb_c)::value;
         constexpr int NCOLS = R * S * CH;
-        constexpr int CHUNKS = 64 * TCOLS / 4;  // 16-byte pieces of the tile
+        constexpr int TCOLS = CB_WG * 32;
         float *out = (float *)a.out + (size_t)band * a.part_stride + colh * TCOLS;
-        for (int c = tid; c < CHUNKS; c += NT) {
-            const int k = c / (TCOLS / 4), col = (c - k * (TCOLS / 4)) * 4;
-            *(f32x4 *)(out + (size_t)k * NCOLS + col) = *(const f32x4 *)(tile + k * TCOLS + col);
+#pragma unroll
+        for (int i = 0; i < WAVE_CB; ++i) {
+            const int col = (WAVE_CB * ws_ + i) * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int k = KB * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
+                out[(size_t)k * NCOLS + col] = acc[KB][i][r];
+            }
         }
+    };
+    using I0 = wb::IntC<0>;
+    using I1 = wb::IntC<1>;
+    using I2 = wb::IntC<2>;
+    if (phase >= 2) park(slot((phase - 2) * WSETS + ws_, PARK_WAVE), I0{}, I2{});
+    __syncthreads();
+    if (phase < 2) add(slot(phase * WSETS + ws_, PARK_WAVE), I0{}, I2{});
+    __syncthreads();
+    if (phase == 0) park(slot(ws_, PARK_HALF), I1{}, I1{});
+    if (phase == 1) park(slot(WSETS + ws_, PARK_HALF), I0{}, I1{});
+    __syncthreads();
+    if (phase == 0) {
+        add(slot(WSETS + ws_, PARK_HALF), I0{}, I1{});
+        store(I0{});
+    }
+    if (phase == 1) {
+        add(slot(ws_, PARK_HALF), I1{}, I1{});
+        store(I1{});
     }
 }
 
