@@ -95,8 +95,10 @@ typedef struct conv2d_problem {
  *   tile:    0 = library choice, otherwise 1 + index into the kernel's tile
  *            table (see conv2d_plan_info).  Out-of-range -> UNSUPPORTED.
  *   split_k: 0 = library choice, otherwise the number of slices the wgrad
- *            reduction over N*P*Q is cut into (partials are summed in slice
- *            order by a second kernel).  Ignored by fprop and dgrad.
+ *            reduction over N*P*Q is cut into (partials are summed in a
+ *            fixed order by a second kernel).  Ignored by fprop and dgrad.
+ *            For groups > 1, tile 1 is the one-thread-per-output direct
+ *            kernel and tile 2 (when it applies) the LDS-tiled one.
  */
 typedef struct conv2d_algo {
     int tile;
@@ -171,8 +173,10 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype,
  * Weight gradient (tensorcore tc_conv2d_backward_weight; burn
  * conv_weight_backward).  The reduction runs over all N*P*Q output pixels, in
  * fp32, cut into split_k contiguous pixel slices whose fp32 partials are
- * summed in slice order by a second kernel (the "parallel" split-K of the
- * CUTLASS notebook's "Split-K" section, made deterministic).
+ * summed in a fixed order by a second kernel (the "parallel" split-K of the
+ * CUTLASS notebook's "Split-K" section, made deterministic).  The stride-1
+ * 3x3 64-channel path cuts the pixels into row bands instead (one partial
+ * per band).
  *   x   device, [N][H][W][C], dtype (F16 or BF16)
  *   dy  device, [N][P][Q][K], dtype
  *   dw  device, [K][R][S][C/G], dtype; overwritten
