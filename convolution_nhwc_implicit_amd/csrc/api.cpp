@@ -108,12 +108,22 @@ AxisPhase axis_phase(int ph, int extent_full, int stride, int pad, int dil, int 
     return a;
 }
 
+constexpr size_t kNoBuf = ~(size_t)0;
+
 struct Plan {
     int op, dtype;
     int kernel;  // 1 implicit GEMM, 2 direct
     int tile, num_tiles, split_k, phases;
     size_t ws_bytes;
     Dims d;
+    // Channel counts that are not whole 16-byte vectors (groups == 1): the
+    // pass runs as `inner` on copies padded with zero channels, kept in the
+    // workspace after the inner pass's own (offsets, or kNoBuf when the
+    // tensor is used in place).  fprop: act = x, out = y; dgrad: act = dx,
+    // out = dy; wgrad: act = x, out = dy; filt = the padded filter (w or dw).
+    bool padded;
+    conv2d_problem_t inner;
+    size_t inner_ws, off_act, off_out, off_filt, off_bias;
 };
 
 int choose_igemm_tile(long long m_total, long long ngemm)
@@ -185,6 +195,47 @@ int choose_direct_tiled_splits(long long wgs_per_slice, long long npix)
     return (int)std::max(1LL, std::min(s, 4096LL));
 }
 
+int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, Plan *pl);
+
+// Plan of a groups == 1 problem whose C or K is not a multiple of vec: the
+// inner problem has both rounded up to vec; the workspace holds the inner
+// pass's own workspace, then the padded copies the pass needs.
+int plan_padded(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, int vec, Plan *pl)
+{
+    const Dims d = pl->d;
+    conv2d_problem_t in = *prob;
+    in.c = (int)((d.C + vec - 1) / vec * vec);
+    in.k = (int)((d.K + vec - 1) / vec * vec);
+    Plan ip;
+    int st = make_plan(op, &in, dtype, algo, &ip);
+    if (st) return st;
+    *pl = ip;
+    pl->d = d;
+    pl->padded = true;
+    pl->inner = in;
+    pl->inner_ws = ip.ws_bytes;
+    const size_t e = (size_t)elem_size(dtype);
+    const long long Cp = in.c, Kp = in.k;
+    const bool pad_c = Cp != d.C, pad_k = Kp != d.K;
+    size_t off = round_up(ip.ws_bytes, 256);
+    auto take = [&](long long elems, size_t esz) {
+        const size_t o = off;
+        off += round_up((size_t)elems * esz, 256);
+        return o;
+    };
+    pl->off_filt = take(Kp * d.R * d.S * Cp, e);
+    if (op == CONV2D_OP_FPROP) {
+        if (pad_c) pl->off_act = take(d.N * d.H * d.W * Cp, e);
+        if (pad_k) pl->off_out = take(d.N * d.P * d.Q * Kp, e);
+        if (pad_k) pl->off_bias = take(Kp, dtype == CONV2D_DTYPE_I8 ? 4 : e);
+    } else {
+        if (pad_c) pl->off_act = take(d.N * d.H * d.W * Cp, e);
+        if (pad_k) pl->off_out = take(d.N * d.P * d.Q * Kp, e);
+    }
+    pl->ws_bytes = off;
+    return CONV2D_OK;
+}
+
 int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, Plan *pl)
 {
     int st = validate(prob, &pl->d);
@@ -203,6 +254,13 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     pl->phases = 1;
     pl->ws_bytes = 0;
     pl->tile = 0;
+    pl->padded = false;
+    pl->off_act = pl->off_out = pl->off_filt = pl->off_bias = kNoBuf;
+
+    // implicit GEMM: 128-bit chunks of channels along GEMM-K and GEMM-N;
+    // other channel counts run on zero-padded copies
+    const int vec = dtype == CONV2D_DTYPE_I8 ? 16 : 8;
+    if (d.G == 1 && (d.C % vec || d.K % vec)) return plan_padded(op, prob, dtype, algo, vec, pl);
 
     if (d.G > 1) {
         // tile 0: one thread per output; tile 1: LDS-tiled dot-product kernel
@@ -231,9 +289,6 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         return CONV2D_OK;
     }
 
-    // implicit GEMM: 128-bit chunks of channels along GEMM-K and GEMM-N
-    const int vec = dtype == CONV2D_DTYPE_I8 ? 16 : 8;
-    if (d.C % vec || d.K % vec) return CONV2D_ERR_UNSUPPORTED;
     pl->kernel = 1;
     if (op == CONV2D_OP_WGRAD) {
         const bool wband = wgrad_band_eligible(d, dtype);
@@ -283,6 +338,18 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_DEVICE; }
+
+// Copy rows x src_cols of src (row pitch src_ld) into dst (dst_rows x
+// dst_cols, pitch dst_ld), zero-filling what src does not cover.
+hipError_t repack(int esz, const void *src, long long src_rows, long long src_cols, long long src_ld, void *dst,
+                  long long dst_rows, long long dst_cols, long long dst_ld, hipStream_t s)
+{
+    RepackArgs a;
+    a.src = src; a.dst = dst;
+    a.src_rows = src_rows; a.dst_rows = dst_rows;
+    a.src_cols = (int)src_cols; a.src_ld = (int)src_ld; a.dst_cols = (int)dst_cols; a.dst_ld = (int)dst_ld;
+    return launch_repack(esz, a, s);
+}
 
 void fill_phase_common(Phase &ph, int tile)
 {
@@ -390,8 +457,36 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
         m = act_scale * w_scale / out_scale;  // double, left to right
     }
     if (workspace_bytes < pl.ws_bytes) return CONV2D_ERR_WORKSPACE_TOO_SMALL;
+    if (pl.ws_bytes && (!workspace || !aligned16(workspace))) return CONV2D_ERR_INVALID_ARGUMENT;
     const Dims &d = pl.d;
     hipStream_t s = (hipStream_t)stream;
+
+    if (pl.padded) {
+        unsigned char *wsb = (unsigned char *)workspace;
+        const int e = elem_size(dtype);
+        const long long Cp = pl.inner.c, Kp = pl.inner.k, npix = d.N * d.P * d.Q;
+        const void *xp = x, *bp = bias;
+        void *yp = y;
+        if (pl.off_act != kNoBuf) {
+            xp = wsb + pl.off_act;
+            if (repack(e, x, d.N * d.H * d.W, d.C, d.C, (void *)xp, d.N * d.H * d.W, Cp, Cp, s) != hipSuccess)
+                return CONV2D_ERR_DEVICE;
+        }
+        if (repack(e, w, d.K * d.R * d.S, d.C, d.C, wsb + pl.off_filt, Kp * d.R * d.S, Cp, Cp, s) != hipSuccess)
+            return CONV2D_ERR_DEVICE;
+        if (pl.off_out != kNoBuf) {
+            yp = wsb + pl.off_out;
+            if (bias) {
+                bp = wsb + pl.off_bias;
+                if (repack(dtype == CONV2D_DTYPE_I8 ? 4 : e, bias, 1, d.K, d.K, (void *)bp, 1, Kp, Kp, s) != hipSuccess)
+                    return CONV2D_ERR_DEVICE;
+            }
+        }
+        st = conv2d_fprop(&pl.inner, dtype, xp, wsb + pl.off_filt, bp, relu, act_scale, w_scale, out_scale, yp,
+                          workspace, pl.inner_ws, algo, stream);
+        if (st || pl.off_out == kNoBuf) return st;
+        return hip_status(repack(e, yp, npix, d.K, Kp, y, npix, d.K, d.K, s));
+    }
 
     if (pl.kernel == 2) {
         DirectArgs a{};
@@ -447,6 +542,24 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
     if (pl.ws_bytes && (!workspace || !aligned16(workspace))) return CONV2D_ERR_INVALID_ARGUMENT;
     const Dims &d = pl.d;
     hipStream_t s = (hipStream_t)stream;
+
+    if (pl.padded) {
+        unsigned char *wsb = (unsigned char *)workspace;
+        const int e = elem_size(dtype);
+        const long long Cp = pl.inner.c, Kp = pl.inner.k, npix = d.N * d.P * d.Q, nin = d.N * d.H * d.W;
+        const void *dyp = dy;
+        void *dxp = dx;
+        if (pl.off_out != kNoBuf) {
+            dyp = wsb + pl.off_out;
+            if (repack(e, dy, npix, d.K, d.K, (void *)dyp, npix, Kp, Kp, s) != hipSuccess) return CONV2D_ERR_DEVICE;
+        }
+        if (repack(e, w, d.K * d.R * d.S, d.C, d.C, wsb + pl.off_filt, Kp * d.R * d.S, Cp, Cp, s) != hipSuccess)
+            return CONV2D_ERR_DEVICE;
+        if (pl.off_act != kNoBuf) dxp = wsb + pl.off_act;
+        st = conv2d_dgrad(&pl.inner, dtype, dyp, wsb + pl.off_filt, dxp, workspace, pl.inner_ws, algo, stream);
+        if (st || pl.off_act == kNoBuf) return st;
+        return hip_status(repack(e, dxp, nin, d.C, Cp, dx, nin, d.C, d.C, s));
+    }
 
     if (pl.kernel == 2) {
         DirectArgs a{};
@@ -530,6 +643,26 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
     hipStream_t s = (hipStream_t)stream;
     const uint32_t npix = (uint32_t)(d.N * d.P * d.Q);
     void *out = pl.split_k > 1 ? workspace : dw;
+
+    if (pl.padded) {
+        unsigned char *wsb = (unsigned char *)workspace;
+        const int e = elem_size(dtype);
+        const long long Cp = pl.inner.c, Kp = pl.inner.k, nin = d.N * d.H * d.W;
+        const void *xp = x, *dyp = dy;
+        if (pl.off_act != kNoBuf) {
+            xp = wsb + pl.off_act;
+            if (repack(e, x, nin, d.C, d.C, (void *)xp, nin, Cp, Cp, s) != hipSuccess) return CONV2D_ERR_DEVICE;
+        }
+        if (pl.off_out != kNoBuf) {
+            dyp = wsb + pl.off_out;
+            if (repack(e, dy, npix, d.K, d.K, (void *)dyp, npix, Kp, Kp, s) != hipSuccess) return CONV2D_ERR_DEVICE;
+        }
+        void *dwp = wsb + pl.off_filt;
+        st = conv2d_wgrad(&pl.inner, dtype, xp, dyp, dwp, workspace, pl.inner_ws, algo, stream);
+        if (st) return st;
+        // the first K*R*S rows of the padded [Kp][R][S][Cp] filter are k < K
+        return hip_status(repack(e, dwp, Kp * d.R * d.S, Cp, Cp, dw, d.K * d.R * d.S, d.C, d.C, s));
+    }
 
     if (pl.kernel == 2) {
         DirectArgs a{};

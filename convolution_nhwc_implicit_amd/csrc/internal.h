@@ -216,4 +216,16 @@ hipError_t launch_direct_fprop(int dtype, const DirectArgs &a, hipStream_t st);
 hipError_t launch_direct_dgrad(int dtype, const DirectArgs &a, hipStream_t st);
 hipError_t launch_direct_wgrad(int dtype, const DirectArgs &a, hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// Row re-layout (repack.hip): dst[r][c] = (r < src_rows && c < src_cols) ?
+// src[r][c] : 0 for r < dst_rows, c < dst_cols; rows are src_ld / dst_ld
+// elements apart.  Element size 1, 2 or 4 bytes.
+struct RepackArgs {
+    const void *src;
+    void *dst;
+    long long src_rows, dst_rows;
+    int src_cols, src_ld, dst_cols, dst_ld;
+};
+hipError_t launch_repack(int esz, const RepackArgs &a, hipStream_t st);
+
 }  // namespace cnv

@@ -94,11 +94,27 @@ def test_invalid_problems(bad):
         assert e.value.status == B.CONV2D_ERR_INVALID_ARGUMENT
 
 
+def test_padded_channel_plans():
+    """C or K not a multiple of 8 (16 for int8) runs on zero-padded copies
+    kept in the workspace after the padded problem's own workspace."""
+    N, H, W = 2, 8, 8
+    p = problem(N, 12, H, W, 16, 3, 3, pad=(1, 1))  # C % 8 != 0
+    q = problem(N, 16, H, W, 16, 3, 3, pad=(1, 1))  # the same problem padded
+    for op in (0, 1, 2):
+        info, inner = B.conv2d_plan_info(op, p, "f16"), B.conv2d_plan_info(op, q, "f16")
+        assert info["kernel"] == inner["kernel"] == 1 and info["tile"] == inner["tile"]
+        filt = 16 * 3 * 3 * 16 * 2
+        act = N * H * W * 16 * 2  # x (fprop, wgrad) or dx (dgrad), padded to 16 channels
+        up = lambda v: (v + 255) // 256 * 256
+        assert info["workspace_bytes"] == up(inner["workspace_bytes"]) + up(filt) + up(act)
+    k = problem(N, 16, H, W, 13, 3, 3, pad=(1, 1))  # K % 8 != 0: y/dy copies (and bias for fprop)
+    assert B.conv2d_plan_info(0, k, "f16")["workspace_bytes"] > 0
+    assert B.conv2d_plan_info(0, problem(N, 3, H, W, 16, 3, 3), "i8")["kernel"] == 1
+    # grouped problems keep the direct kernels for any channel count
+    assert B.conv2d_plan_info(0, problem(N, 6, H, W, 9, 3, 3, groups=3), "f16")["workspace_bytes"] == 0
+
+
 def test_unsupported_cases():
-    p = problem(2, 12, 8, 8, 16, 3, 3, pad=(1, 1))  # C % 8 != 0 on the implicit GEMM
-    with pytest.raises(B.Conv2dError) as e:
-        B.conv2d_plan_info(B.CONV2D_OP_FPROP, p, "f16")
-    assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
     p = problem(2, 16, 8, 8, 16, 3, 3, pad=(1, 1))  # int8 needs C % 16, fprop only
     assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, p, "i8")["kernel"] == 1
     for op in (B.CONV2D_OP_DGRAD, B.CONV2D_OP_WGRAD):

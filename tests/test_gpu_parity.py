@@ -86,6 +86,15 @@ CASES = [
     ("wband_bf16", problem(16, 64, 20, 20, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
     ("wband_q56", problem(2, 64, 23, 56, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
     ("wband_wide", problem(4, 64, 9, 64, 64, 3, 3, pad=(1, 1)), "f16", "int", True, True),
+    # channel counts that are not whole 16-byte vectors run on zero-padded
+    # copies: a stem-like C = 3 7x7 stride-2 layer, an odd K, both odd with
+    # stride and dilation, and C = 60 whose padded problem takes the band
+    # kernels
+    ("pad_c3_stem", problem(2, 3, 30, 30, 16, 7, 7, pad=(3, 3), stride=(2, 2)), "f16", "int", True, True),
+    ("pad_k13", problem(2, 16, 11, 13, 13, 3, 3, pad=(1, 1)), "bf16", "int", True, False),
+    ("pad_both", problem(3, 5, 9, 10, 7, 3, 2, pad=(1, 0), stride=(1, 2), dil=(2, 1)), "f16", "gauss",
+     True, True),
+    ("pad_c60_band", problem(2, 60, 10, 12, 64, 3, 3, pad=(1, 1)), "f16", "int", True, True),
 ]
 
 
@@ -108,6 +117,8 @@ INT8_CASES = [
     ("i8_norelu", problem(2, 16, 9, 9, 32, 3, 3, pad=(1, 1), stride=(2, 2)), True, False),
     ("i8_nobias", problem(1, 64, 8, 7, 16, 1, 1), False, True),
     ("i8_grouped", problem(2, 16, 7, 7, 16, 3, 3, pad=(1, 1), groups=4), True, True),
+    ("i8_pad_c3", problem(2, 3, 12, 12, 16, 3, 3, pad=(1, 1)), True, True),
+    ("i8_pad_k20", problem(2, 32, 9, 8, 20, 3, 3, pad=(1, 1)), True, False),
 ]
 
 
