@@ -280,7 +280,7 @@ def test_workload_full(name):
     check(f64(dw), oracle.wgrad(prob, f64(x), f64(dy)), dt, mode, f"{name} wgrad")
 
 
-@pytest.mark.parametrize("name", ["c3a_resnet3x3", "c3b_resnet1x1", "c4_awkward"])
+@pytest.mark.parametrize("name", ["c3a_resnet3x3", "c3b_resnet1x1", "c4_awkward", "n1_stem"])
 def test_workload_sampled(name):
     wl, prob, x, w, b, dy = _workload_inputs(name)
     dt, mode = wl["dtype"], wl["check"]
