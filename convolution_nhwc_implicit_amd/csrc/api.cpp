@@ -290,6 +290,13 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     }
 
     pl->kernel = 1;
+    {
+        // operands are read through 32-bit buffer offsets
+        const unsigned long long e = (unsigned long long)elem_size(dtype);
+        if (e * d.N * d.H * d.W * d.C > kBufMaxBytes || e * d.N * d.P * d.Q * d.K > kBufMaxBytes ||
+            e * d.K * d.R * d.S * d.C > kBufMaxBytes)
+            return CONV2D_ERR_UNSUPPORTED;
+    }
     if (op == CONV2D_OP_WGRAD) {
         const bool wband = wgrad_band_eligible(d, dtype);
         pl->num_tiles = wgrad_num_tiles() + (wband ? 1 : 0);
@@ -511,6 +518,7 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
     IgemmArgs a;
     memset(&a, 0, sizeof(a));
     a.src = x; a.bmat = w; a.bias = bias; a.dst = y;
+    a.b_elems = d.K * d.R * d.S * d.C;
     a.nimg = (int)d.N; a.hs = (int)d.H; a.ws = (int)d.W; a.cs = (int)d.C;
     a.ngemm = (int)d.K;
     a.ho = (int)d.P; a.wo = (int)d.Q; a.osh = 1; a.osw = 1;
@@ -589,6 +597,7 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
     IgemmArgs a;
     memset(&a, 0, sizeof(a));
     a.src = dy; a.bmat = workspace; a.bias = nullptr; a.dst = dx;
+    a.b_elems = d.R * d.S * d.C * d.K;
     a.nimg = (int)d.N; a.hs = (int)d.P; a.ws = (int)d.Q; a.cs = (int)d.K;
     a.ngemm = (int)d.C;
     a.ho = (int)d.H; a.wo = (int)d.W; a.osh = (int)d.sh; a.osw = (int)d.sw;

@@ -72,7 +72,10 @@ struct EI8 {
 // otherwise wait for every such load before any later LDS access, which
 // serialises the prefetch with the compute.  Callers make the data visible
 // themselves: s_waitcnt vmcnt(0) on every wave, then a barrier.
-constexpr uint32_t kBufOOB = 0x7ffffff0u;  // an offset past every range: reads as zero
+constexpr uint32_t kBufOOB = 0x7ffffff0u;  // past every range under 2 GB: reads as zero
+// Past every buffer of at most kBufMaxBytes (internal.h), the largest
+// tensor the implicit-GEMM kernels take:
+constexpr uint32_t kBufOOBFar = 0xfffffff0u;
 
 // Raw buffer descriptor (base, stride 0, num_records = bytes, 32-bit data
 // format for CDNA), wave-uniform.

@@ -30,6 +30,14 @@ using T2 = Tile<64, 64, 128, 2, 2>;
 using T3 = Tile<256, 64, 64, 4, 1>;
 using T4 = Tile<64, 32, 128, 4, 1>;
 
+// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ inline void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <class E, class TL>
 __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
 {
@@ -38,72 +46,81 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     constexpr int CH = BKB / 16;        // 16-byte chunks per tile row per k-step
     constexpr int EPC = E::EPC;
     constexpr int BK = CH * EPC;        // GEMM-K elements per k-step
-    constexpr int ROWB = BKB + 16;      // padded LDS row: conflict-free 128-bit reads
-    constexpr int A_CH = BM * CH / NT;  // A chunks per thread
-    constexpr int B_TOT = BN * CH;
-    constexpr int B_CH = (B_TOT + NT - 1) / NT;
+    constexpr int RB = 64 / CH;         // tile rows per 1 KB direct-to-LDS block
+    constexpr int SH = CH == 8 ? 1 : 2; // chunk swizzle: stored slot = chunk ^ ((row >> SH) & (CH - 1))
+    constexpr int A_BLK = BM / RB / 4;  // blocks per wave and stage
+    constexpr int B_BLK = BN / RB / 4;
+    constexpr int PER = A_BLK + B_BLK;  // direct-to-LDS loads per wave and stage
+    constexpr int NSTAGE = 3;
     constexpr int WTM = BM / TL::WM, WTN = BN / TL::WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
     constexpr int KSUB = BKB / 64;      // MFMAs along K per k-step
-    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int STAGE = (BM + BN) * BKB;
     static_assert(TL::WM * TL::WN == 4, "four waves");
-    static_assert((BM * CH) % NT == 0 && NT % CH == 0, "chunk mapping");
+    static_assert(CH == 4 || CH == 8, "64- or 128-byte tile rows");
+    static_assert((BM / RB) % 4 == 0 && (BN / RB) % 4 == 0 && A_BLK > 0 && B_BLK > 0, "whole blocks per wave");
     using elem = typename E::elem;
     using acc_t = typename E::acc;
     constexpr int OSZ = (int)sizeof(elem);
     constexpr int CROWB = BN * OSZ + 16;
-    static_assert(BM * CROWB <= 2 * STAGE, "epilogue tile fits in LDS");
+    static_assert(BM * CROWB <= NSTAGE * STAGE, "epilogue tile fits in LDS");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE * STAGE];
 
     const Phase &ph = a.ph[blockIdx.z];
     const int mt = blockIdx.x;
     if (mt >= ph.tiles_m) return;
     const int nt = blockIdx.y;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / TL::WN, wn = wave % TL::WN;
-    const int kc = tid % CH;
 
-    const elem *src = (const elem *)a.src;
     const int hs = a.hs, ws = a.ws, cs = a.cs;
     const uint32_t mi_mj = (uint32_t)ph.mi * (uint32_t)ph.mj;
 
-    // ---- per-thread A rows: image base and source coordinates of tap (0,0)
-    const elem *a_base[A_CH];
-    int a_ih[A_CH], a_iw[A_CH];
+    // ---- operand tiles arrive by direct-to-LDS loads (buffer_load ... lds):
+    // wave w fills blocks w, w+4, ... of a stage's A rows and B rows; lane i
+    // of a block fills stored slot i % CH of block row i / CH, which holds
+    // logical chunk kc = (i % CH) ^ swizzle(row).  For every block a wave
+    // fills, the swizzle of its rows depends on the lane alone, so each lane
+    // moves the same GEMM-K chunk kc of all its rows.
+    const int brow = lane / CH;  // row inside a block
+    const int kc = (lane % CH) ^ (((RB * wave + brow) >> SH) & (CH - 1));
+    const u32x4 a_rs = make_buf_rsrc(a.src, (uint32_t)((size_t)a.nimg * hs * ws * cs * sizeof(elem)));
+    const u32x4 b_rs = make_buf_rsrc(a.bmat, (uint32_t)(a.b_elems * sizeof(elem)));
+
+    // per lane: A rows (image base, source coordinates of tap (0,0))
+    uint32_t a_img[A_BLK];
+    int a_ih[A_BLK], a_iw[A_BLK];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int row = (tid + i * NT) / CH;
+    for (int t = 0; t < A_BLK; ++t) {
+        const int row = RB * (wave + 4 * t) + brow;
         const uint32_t m = (uint32_t)mt * BM + row;
         if (m < ph.m_total) {
             const uint32_t n = fdiv(m, ph.div_mimj);
             const uint32_t rem = m - n * mi_mj;
             const uint32_t ii = fdiv(rem, ph.div_mj);
             const uint32_t jj = rem - ii * ph.mj;
-            a_base[i] = src + (size_t)n * hs * ws * cs;
-            a_ih[i] = (int)ii * a.gsh + ph.th0;
-            a_iw[i] = (int)jj * a.gsw + ph.tw0;
+            a_img[t] = n * (uint32_t)(hs * ws);
+            a_ih[t] = (int)ii * a.gsh + ph.th0;
+            a_iw[t] = (int)jj * a.gsw + ph.tw0;
         } else {
-            a_base[i] = src;
-            a_ih[i] = -(1 << 29);  // never inside the image
-            a_iw[i] = -(1 << 29);
+            a_img[t] = 0;
+            a_ih[t] = -(1 << 29);  // never inside the image
+            a_iw[t] = -(1 << 29);
         }
     }
-    // ---- per-thread B rows
-    const elem *b_ptr[B_CH];
-    bool b_ok[B_CH];
+    // per lane: B rows (element offset of the row, or -1 past ngemm)
+    long long b_row[B_BLK];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int id = tid + i * NT;
-        const int row = id / CH;
-        const int n = nt * BN + row;
-        b_ok[i] = (id < B_TOT) && (n < a.ngemm);
-        b_ptr[i] = (const elem *)a.bmat + ph.b_off + (b_ok[i] ? (size_t)n * ph.kgemm + kc * EPC : 0);
+    for (int t = 0; t < B_BLK; ++t) {
+        const int n = nt * BN + RB * (wave + 4 * t) + brow;
+        b_row[t] = n < a.ngemm ? ph.b_off + (long long)n * ph.kgemm : -1;
     }
 
-    // ---- GEMM-K position of this thread's chunk: (tap tr, tap ts, channel c)
-    int c = kc * EPC, tr = 0, ts = 0;
+    // ---- GEMM-K position of this lane's chunk: (tap tr, tap ts, channel c)
+    int c = kc * EPC, tr = 0, ts = 0, kk = kc * EPC;
     auto normalize = [&]() {
         while (c >= cs) {
             c -= cs;
@@ -116,37 +133,28 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     normalize();
 
     const int KT = (ph.kgemm + BK - 1) / BK;
-    u32x4 ra[A_CH], rb[B_CH];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-
-    auto gload = [&](int kt) {
+    // issue stage kt's loads into buffer kt % NSTAGE, then advance the chunk
+    auto dma_stage = [&](int kt) {
+        unsigned char *base = smem + (kt % NSTAGE) * STAGE;
         const bool kval = tr < ph.ntr;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int h = a_ih[i] + tr * ph.tdh;
-            const int w = a_iw[i] + ts * ph.tdw;
+        for (int t = 0; t < A_BLK; ++t) {
+            const int h = a_ih[t] + tr * ph.tdh;
+            const int w = a_iw[t] + ts * ph.tdw;
             const bool ok = kval && (unsigned)h < (unsigned)hs && (unsigned)w < (unsigned)ws;
-            ra[i] = ok ? *(const u32x4 *)(a_base[i] + ((size_t)(h * ws + w) * cs + c)) : zero;
+            const uint32_t voff = ok ? ((a_img[t] + (uint32_t)(h * ws + w)) * (uint32_t)cs + (uint32_t)c) * sizeof(elem)
+                                     : kBufOOBFar;
+            dma16(a_rs, lds_addr(base + (wave + 4 * t) * 1024), voff);
         }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i)
-            rb[i] = (b_ok[i] && kval) ? *(const u32x4 *)(b_ptr[i] + (size_t)kt * BK) : zero;
-    };
-    auto sstore = [&](int stage) {
-        unsigned char *base = smem + stage * STAGE;
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int row = (tid + i * NT) / CH;
-            *(u32x4 *)(base + row * ROWB + kc * 16) = ra[i];
+        for (int t = 0; t < B_BLK; ++t) {
+            const uint32_t voff =
+                (kval && b_row[t] >= 0) ? (uint32_t)((b_row[t] + kk) * (long long)sizeof(elem)) : kBufOOBFar;
+            dma16(b_rs, lds_addr(base + BM * BKB + (wave + 4 * t) * 1024), voff);
         }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int id = tid + i * NT;
-            if (id < B_TOT) {
-                const int row = id / CH;
-                *(u32x4 *)(base + (BM + row) * ROWB + kc * 16) = rb[i];
-            }
-        }
+        c += BK;
+        kk += BK;
+        normalize();
     };
 
     acc_t acc[FM][FN];
@@ -155,38 +163,43 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
+    // fragment reads: row (lane & 15) of a 16-row block, logical chunk
+    // 4*ks + lane/16, at its swizzled slot (the swizzle of rows 16q + r is
+    // that of r)
     const int frag_row = lane & 15;
-    const int frag_k = (lane >> 4) * 16;
-    if (KT > 0) {
-        gload(0);
-        sstore(0);
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < KT) {
-                c += BK;
-                normalize();
-                gload(kt + 1);
-            }
-            const unsigned char *base = smem + cur * STAGE;
+    const int fswz = (frag_row >> SH) & (CH - 1);
+    int fofs[KSUB];
 #pragma unroll
-            for (int ks = 0; ks < KSUB; ++ks) {
-                u32x4 fa[FM], fb[FN];
+    for (int ks = 0; ks < KSUB; ++ks) fofs[ks] = frag_row * BKB + (((4 * ks + (lane >> 4)) ^ fswz) << 4);
+
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    fa[i] = *(const u32x4 *)(base + (wm * WTM + i * 16 + frag_row) * ROWB + ks * 64 + frag_k);
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < KT) dma_stage(s);
+    for (int kt = 0; kt < KT; ++kt) {
+        // stage kt has landed when at most the younger stages' loads remain
+        const int younger = min(NSTAGE - 2, KT - 1 - kt);
+        if (younger >= 1)
+            wait_vm<PER * (NSTAGE - 2)>();
+        else
+            wait_vm<0>();
+        __syncthreads();  // every wave's loads of stage kt are visible; stage kt-1 is consumed
+        if (kt + NSTAGE - 1 < KT) dma_stage(kt + NSTAGE - 1);
+        const unsigned char *base = smem + (kt % NSTAGE) * STAGE;
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    fb[j] = *(const u32x4 *)(base + (BM + wn * WTN + j * 16 + frag_row) * ROWB + ks * 64 + frag_k);
+        for (int ks = 0; ks < KSUB; ++ks) {
+            u32x4 fa[FM], fb[FN];
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i) fa[i] = *(const u32x4 *)(base + (wm * WTM + i * 16) * BKB + fofs[ks]);
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(fa[i], fb[j], acc[i][j]);
-            }
-            if (kt + 1 < KT) sstore(cur ^ 1);
-            __syncthreads();
+            for (int j = 0; j < FN; ++j)
+                fb[j] = *(const u32x4 *)(base + (BM + wn * WTN + j * 16) * BKB + fofs[ks]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(fa[i], fb[j], acc[i][j]);
         }
     }
+    __syncthreads();  // the stage buffers become the epilogue tile
 
     // ---- fused epilogue: acc -> (bias, ReLU | requant) -> element -> LDS tile
     // MFMA 16x16 result layout: lane holds column (lane & 15) and rows

@@ -56,6 +56,9 @@ __host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv &f)
 //   same set of taps reaches.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPhases = 16;
+// Largest operand (bytes) the implicit-GEMM kernels read through 32-bit
+// buffer offsets; kBufOOBFar lies past it.
+constexpr unsigned long long kBufMaxBytes = 0xffffff00ull;
 
 struct Phase {
     int mi, mj;       // sub-grid extent
@@ -73,6 +76,7 @@ struct Phase {
 struct IgemmArgs {
     const void *src;
     const void *bmat;
+    long long b_elems; // elements of bmat (all phases)
     const void *bias;  // [ngemm]; element type (float paths) or int32 (int8)
     void *dst;
     int nimg, hs, ws, cs;  // source image
