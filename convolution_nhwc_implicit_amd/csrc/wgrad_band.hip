@@ -238,19 +238,25 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
         return u32x4{l.x, l.y, h.x, h.y};
     };
-    auto mma = [&](const Frag &f) {
+    // MFMAs [m0, m1) of a step (kb-major over the WAVE_KB x WAVE_CB blocks)
+    auto mma = [&](const Frag &f, int m0, int m1) {
 #pragma unroll
         for (int kb = 0; kb < WAVE_KB; ++kb) {
             const u32x4 fa = join(f[2 * kb], f[2 * kb + 1]);
 #pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i)
-                acc[kb][i] = Mfma32w<E>::run(fa, join(f[2 * WAVE_KB + 2 * i], f[2 * WAVE_KB + 2 * i + 1]), acc[kb][i]);
+            for (int i = 0; i < WAVE_CB; ++i) {
+                const int m = kb * WAVE_CB + i;
+                if (m >= m0 && m < m1)
+                    acc[kb][i] =
+                        Mfma32w<E>::run(fa, join(f[2 * WAVE_KB + 2 * i], f[2 * WAVE_KB + 2 * i + 1]), acc[kb][i]);
+            }
         }
     };
 
     // Steps run in straight-line bodies of BODY (of one phase): the reads of
-    // step k+1 are issued before the MFMAs of step k, and nothing is in
-    // flight across bodies.  Steps past the group's pixels read zero dy
+    // step k+1 are issued right after the first MFMA of step k (so that MFMA
+    // waits for step k's reads alone), and nothing is in flight across
+    // bodies.  Steps past the group's pixels read zero dy
     // pixels.
     const int ngroups = (nrows + GR - 1) / GR;
     for (int g = 0; g < ngroups; ++g) {
@@ -262,9 +268,14 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
             load_step(f[0], 0);
 #pragma unroll
             for (int k = 0; k < BODY; ++k) {
+                // step k's first MFMA, then step k+1's reads, then the rest:
+                // the first MFMA waits for step k's reads alone
+                __builtin_amdgcn_sched_barrier(0);
+                mma(f[k], 0, 1);
+                __builtin_amdgcn_sched_barrier(0);
                 if (k + 1 < BODY) load_step(f[k + 1], k + 1);
-                __builtin_amdgcn_sched_barrier(0);  // all reads of step k+1 before the MFMAs of step k
-                mma(f[k]);
+                __builtin_amdgcn_sched_barrier(0);
+                mma(f[k], 1, NACC);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
