@@ -132,34 +132,53 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     const u32x4 x_rs = make_buf_rsrc((const elem *)a.x + (size_t)img * a.H * a.W * CH, (uint32_t)(a.H * a.W * CH * 2));
     const u32x4 d_rs =
         make_buf_rsrc((const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH, (uint32_t)(nrows * Q * CH * 2));
-    auto dma_group = [&](int g, int nw) {
+    // The pixel a lane moves in each of its wave's blocks is the same in every
+    // group (buffers start at a group's first row), so its (row, column) in
+    // the group is computed once, row << 8 | column in 16 bits, two blocks
+    // per register: block wave + WAVES*j in bits 16*(j%2) of rc[j/2].  Bit 1
+    // of the pixel index, which sets the chunk swizzle, is bit 1 of lane/8
+    // (blocks are 8 pixels).
+    constexpr int DBLK = DCAP / 8, NBLK = (DCAP + XCAP) / 8;
+    constexpr int MAXB = (NBLK + WAVES - 1) / WAVES;  // blocks per wave
+    static_assert(XCAP < 256 * 6 && QMAX + 2 < 256, "row and column fit in 8 bits");
+    uint32_t rc[(MAXB + 1) / 2] = {};
+#pragma unroll
+    for (int jb = 0; jb < MAXB; ++jb) {
+        const int b = wave + WAVES * jb;
+        const int v = (b < DBLK ? b : b - DBLK) * 8 + (lane >> 3);
+        const int row = (int)fdiv((uint32_t)v, a.div_xw);
+        rc[jb / 2] |= (((uint32_t)row << 8) | (uint32_t)(v - row * XW)) << (16 * (jb & 1));
+    }
+    const int lane_chunk16 = swz_chunk(lane & 7, lane >> 3) * 16;  // byte offset of the chunk in its pixel
+    auto dma_group = [&](int g) {
         const int d0 = g * GR;
-        if (d0 >= nrows || wave >= nw) return;
+        if (d0 >= nrows) return;
         const int ndy = min(GR, nrows - d0);  // dy rows of the group
         const int nx = ndy + HALO;            // x rows it reads
         unsigned char *buf = smem + (g & 1) * BUF_BYTES;
-        constexpr int DBLK = DCAP / 8, NBLK = (DCAP + XCAP) / 8;
-        for (int b = wave; b < NBLK; b += nw) {
-            const bool is_dy = b < DBLK;
-            const int v = (is_dy ? b : b - DBLK) * 8 + (lane >> 3);
-            const int row = (int)fdiv((uint32_t)v, a.div_xw), col = v - row * XW;
-            const int j = swz_chunk(lane & 7, v);
+#pragma unroll
+        for (int jb = 0; jb < MAXB; ++jb) {
+            const int b = wave + WAVES * jb;  // wave-uniform
+            if (b >= NBLK) break;
+            const uint32_t e = rc[jb / 2] >> (16 * (jb & 1));
+            const int row = (int)((e >> 8) & 0xffu), col = (int)(e & 0xffu);
             unsigned voff = kBufOOB;
-            if (is_dy) {
-                if (row < ndy && col < Q) voff = (unsigned)((((d0 + row) * Q + col) * CH + j * 8) * 2);
+            if (b < DBLK) {
+                if (row < ndy && col < Q) voff = (unsigned)(((d0 + row) * Q + col) * PIXB + lane_chunk16);
+                dma16(d_rs, lds_addr(buf + b * 1024), voff);
             } else {
                 const int h = h_base + d0 + row, w = col - a.pad_w;
                 if (row < nx && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W)
-                    voff = (unsigned)(((h * a.W + w) * CH + j * 8) * 2);
+                    voff = (unsigned)((h * a.W + w) * PIXB + lane_chunk16);
+                dma16(x_rs, lds_addr(buf + b * 1024), voff);
             }
-            dma16(is_dy ? d_rs : x_rs, lds_addr(buf + b * 1024), voff);
         }
     };
 
-    dma_group(0, WAVES);
+    dma_group(0);
     wait_vm_all();
     __syncthreads();
-    dma_group(1, WAVES);
+    dma_group(1);
 
     // ---- per-wave roles: both k-blocks, column blocks cb0..cb0+2 of the
     // workgroup's half (all of one tap row r: column block cb is tap cb/2 =
@@ -171,10 +190,10 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
 
     // ---- per-lane read offsets (first step of this phase in a buffer).
     // Read rd of a step covers pixels v = 16*t + 8*lhi + 4*rd + 0..3; this
-    // lane points at pixel v + L/4.  Steps move every read by a multiple of 16
-    // pixels, which keeps bit 1 of the pixel index and so the swizzle.  They
-    // are recomputed per body from an opaque copy of the lane id (holding
-    // them across the loop would cost registers the fragments need).
+    // lane points at pixel v + L/4.  Read rd = 1 and later steps move every
+    // read by a multiple of 4 pixels, which keeps bit 1 of the pixel index and
+    // so the swizzle: they are constant byte offsets (4 pixels = 512 B) from
+    // the rd = 0 offsets of the body's first step.
     auto dy_off = [&](int ln, int rd, int kb) {
         const int L_ = ln & 15, g_ = (ln >> 4) & 1, h_ = ln >> 5;
         const int c_ = 16 * g_ + 4 * (L_ & 3);
@@ -207,31 +226,31 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     // asm keeps the compiler from re-associating base + offset + k*8 KB into
     // one register per step)
     constexpr int STEPB = PHASES * 16 * PIXB;
-    const lds_u8 *ad[2][WAVE_KB], *ax[2][WAVE_CB];
+    constexpr int RDB = 4 * PIXB;  // read rd = 1: 4 pixels further
+    // The offsets are recomputed per body from an opaque copy of the lane id
+    // (holding them across the loop would cost registers the fragments need).
+    const lds_u8 *ad[WAVE_KB], *ax[WAVE_CB];
     auto set_body = [&](const lds_u8 *base) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
+        for (int kb = 0; kb < WAVE_KB; ++kb) {
+            ad[kb] = base + dy_off(ln, 0, kb);
+            asm volatile("" : "+v"(ad[kb]));
+        }
 #pragma unroll
-            for (int kb = 0; kb < WAVE_KB; ++kb) {
-                ad[rd][kb] = base + dy_off(ln, rd, kb);
-                asm volatile("" : "+v"(ad[rd][kb]));
-            }
-#pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i) {
-                ax[rd][i] = base + x_off(ln, rd, i);
-                asm volatile("" : "+v"(ax[rd][i]));
-            }
+        for (int i = 0; i < WAVE_CB; ++i) {
+            ax[i] = base + x_off(ln, 0, i);
+            asm volatile("" : "+v"(ax[i]));
         }
     };
     auto load_step = [&](Frag &f, int k) {
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
 #pragma unroll
-            for (int kb = 0; kb < WAVE_KB; ++kb) f[2 * kb + rd] = tr(ad[rd][kb] + k * STEPB);
+            for (int kb = 0; kb < WAVE_KB; ++kb) f[2 * kb + rd] = tr(ad[kb] + rd * RDB + k * STEPB);
 #pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i) f[2 * WAVE_KB + 2 * i + rd] = tr(ax[rd][i] + k * STEPB);
+            for (int i = 0; i < WAVE_CB; ++i) f[2 * WAVE_KB + 2 * i + rd] = tr(ax[i] + rd * RDB + k * STEPB);
         }
     };
     auto join = [](s16x4 lo, s16x4 hi) -> u32x4 {
@@ -281,7 +300,7 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         }
         wait_vm_all();     // the next group's rows
         __syncthreads();   // every wave is done with this group's buffer
-        dma_group(g + 2, WAVES);  // into the buffer this group used
+        dma_group(g + 2);  // into the buffer this group used
     }
 
     // ---- the four phases' sums, in a fixed order (p0 + p2) + (p1 + p3),
