@@ -188,10 +188,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         return (unsigned)w < (unsigned)a.W ? (w * CIN + j * 8) * 2 : -1;
     };
     const int my_off = lane_src(wave);
+    const uint32_t ring0 = lds_addr(ring);  // LDS byte address of the ring
     auto dma_row = [&](int rr, int blk, int off) {
         const int h = h_base + rr;
         const bool ok = off >= 0 && (unsigned)h < (unsigned)a.H;
-        dma16(src_rs, lds_addr(ring + (rr % C::NSLOT) * C::SLOTB + blk * 1024),
+        dma16(src_rs, ring0 + (uint32_t)((rr % C::NSLOT) * C::SLOTB + blk * 1024),
               ok ? (unsigned)h * row_bytes + (unsigned)off : kBufOOB);
     };
     // group g reads ring rows [g*GR, g*GR + GR + HALO_R); it brings the rows

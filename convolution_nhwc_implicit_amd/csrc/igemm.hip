@@ -89,6 +89,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     const int kc = (lane % CH) ^ (((RB * wave + brow) >> SH) & (CH - 1));
     const u32x4 a_rs = make_buf_rsrc(a.src, (uint32_t)((size_t)a.nimg * hs * ws * cs * sizeof(elem)));
     const u32x4 b_rs = make_buf_rsrc(a.bmat, (uint32_t)(a.b_elems * sizeof(elem)));
+    const uint32_t lds0 = lds_addr(smem);
 
     // per lane: A rows (image base, source coordinates of tap (0,0))
     uint32_t a_img[A_BLK];
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     const int KT = (ph.kgemm + BK - 1) / BK;
     // issue stage kt's loads into buffer kt % NSTAGE, then advance the chunk
     auto dma_stage = [&](int kt) {
-        unsigned char *base = smem + (kt % NSTAGE) * STAGE;
+        const uint32_t base = lds0 + (uint32_t)((kt % NSTAGE) * STAGE);  // LDS byte address
         const bool kval = tr < ph.ntr;
 #pragma unroll
         for (int t = 0; t < A_BLK; ++t) {
@@ -144,13 +145,13 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
             const bool ok = kval && (unsigned)h < (unsigned)hs && (unsigned)w < (unsigned)ws;
             const uint32_t voff = ok ? ((a_img[t] + (uint32_t)(h * ws + w)) * (uint32_t)cs + (uint32_t)c) * sizeof(elem)
                                      : kBufOOBFar;
-            dma16(a_rs, lds_addr(base + (wave + 4 * t) * 1024), voff);
+            dma16(a_rs, base + (wave + 4 * t) * 1024, voff);
         }
 #pragma unroll
         for (int t = 0; t < B_BLK; ++t) {
             const uint32_t voff =
                 (kval && b_row[t] >= 0) ? (uint32_t)((b_row[t] + kk) * (long long)sizeof(elem)) : kBufOOBFar;
-            dma16(b_rs, lds_addr(base + BM * BKB + (wave + 4 * t) * 1024), voff);
+            dma16(b_rs, base + BM * BKB + (wave + 4 * t) * 1024, voff);
         }
         c += BK;
         kk += BK;

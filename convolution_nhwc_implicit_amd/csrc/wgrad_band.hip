@@ -150,12 +150,13 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
         rc[jb / 2] |= (((uint32_t)row << 8) | (uint32_t)(v - row * XW)) << (16 * (jb & 1));
     }
     const int lane_chunk16 = swz_chunk(lane & 7, lane >> 3) * 16;  // byte offset of the chunk in its pixel
+    const uint32_t lds0 = lds_addr(smem);
     auto dma_group = [&](int g) {
         const int d0 = g * GR;
         if (d0 >= nrows) return;
         const int ndy = min(GR, nrows - d0);  // dy rows of the group
         const int nx = ndy + HALO;            // x rows it reads
-        unsigned char *buf = smem + (g & 1) * BUF_BYTES;
+        const uint32_t buf = lds0 + (uint32_t)((g & 1) * BUF_BYTES);  // LDS byte address
 #pragma unroll
         for (int jb = 0; jb < MAXB; ++jb) {
             const int b = wave + WAVES * jb;  // wave-uniform
@@ -165,12 +166,12 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
             unsigned voff = kBufOOB;
             if (b < DBLK) {
                 if (row < ndy && col < Q) voff = (unsigned)(((d0 + row) * Q + col) * PIXB + lane_chunk16);
-                dma16(d_rs, lds_addr(buf + b * 1024), voff);
+                dma16(d_rs, buf + b * 1024, voff);
             } else {
                 const int h = h_base + d0 + row, w = col - a.pad_w;
                 if (row < nx && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W)
                     voff = (unsigned)((h * a.W + w) * PIXB + lane_chunk16);
-                dma16(x_rs, lds_addr(buf + b * 1024), voff);
+                dma16(x_rs, buf + b * 1024, voff);
             }
         }
     };
