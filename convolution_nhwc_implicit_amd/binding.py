@@ -52,6 +52,12 @@ class Conv2dAlgo(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_int), ("split_k", ctypes.c_int)]
 
 
+class Conv2dEpilogue(ctypes.Structure):
+    """conv2d_epilogue_t: out = alpha * result + beta * C (fp32), wgrad may keep fp32."""
+    _fields_ = [("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("c", ctypes.c_void_p),
+                ("out_f32", ctypes.c_int)]
+
+
 class Conv2dPlanInfo(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("tile", ctypes.c_int), ("num_tiles", ctypes.c_int),
                 ("split_k", ctypes.c_int), ("phases", ctypes.c_int),
@@ -90,10 +96,20 @@ def load():
                                  P(Conv2dAlgo), vp]
     lib.conv2d_wgrad.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t,
                                  P(Conv2dAlgo), vp]
+    ep = P(Conv2dEpilogue)
+    lib.conv2d_workspace_size_ex.argtypes = [ctypes.c_int, P(Conv2dProblem), ctypes.c_int,
+                                             P(Conv2dAlgo), ep, P(ctypes.c_size_t)]
+    lib.conv2d_fprop_ex.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, vp, ctypes.c_int, ep,
+                                    vp, vp, ctypes.c_size_t, P(Conv2dAlgo), vp]
+    lib.conv2d_dgrad_ex.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, ep, vp, vp, ctypes.c_size_t,
+                                    P(Conv2dAlgo), vp]
+    lib.conv2d_wgrad_ex.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, ep, vp, vp, ctypes.c_size_t,
+                                    P(Conv2dAlgo), vp]
     lib.conv2d_status_string.argtypes = [ctypes.c_int]
     lib.conv2d_status_string.restype = ctypes.c_char_p
     for name in ("conv2d_output_size", "conv2d_workspace_size", "conv2d_plan_info",
-                 "conv2d_fprop", "conv2d_dgrad", "conv2d_wgrad"):
+                 "conv2d_fprop", "conv2d_dgrad", "conv2d_wgrad", "conv2d_workspace_size_ex",
+                 "conv2d_fprop_ex", "conv2d_dgrad_ex", "conv2d_wgrad_ex"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -241,6 +257,82 @@ def conv2d_wgrad(prob, dtype, x, dy, dw, workspace, algo=None, stream=None):
     st = load().conv2d_wgrad(ctypes.byref(make_problem(prob)), code, x.data_ptr(), dy.data_ptr(),
                              dw.data_ptr(), wsp, wsb, _algo(algo), _stream(stream))
     _raise(st, "conv2d_wgrad")
+
+
+def _epi(epi):
+    """A ctypes epilogue from a mapping with keys alpha, beta, c (tensor or None), out_f32."""
+    if epi is None:
+        return None, None
+    c = epi.get("c")
+    e = Conv2dEpilogue(float(epi.get("alpha", 1.0)), float(epi.get("beta", 0.0)),
+                       None if c is None else c.data_ptr(), int(bool(epi.get("out_f32", False))))
+    return e, ctypes.byref(e)
+
+
+def conv2d_workspace_size_ex(op, prob, dtype, algo=None, epi=None):
+    b = ctypes.c_size_t()
+    _, ep = _epi(epi)
+    _raise(load().conv2d_workspace_size_ex(int(op), ctypes.byref(make_problem(prob)), _dtype_code(dtype),
+                                           _algo(algo), ep, ctypes.byref(b)), "conv2d_workspace_size_ex")
+    return b.value
+
+
+def _check_c(epi, dtype, shape):
+    if epi is not None and epi.get("c") is not None:
+        _check_tensor(epi["c"], "c", dtype, shape)
+
+
+def conv2d_fprop_ex(prob, dtype, x, w, bias, relu, epi, y, workspace, algo=None, stream=None):
+    code = _dtype_code(dtype)
+    tdt = CODE_DTYPE[code]
+    xs, ws_, ys = _shapes(prob)
+    _check_tensor(x, "x", tdt, xs)
+    _check_tensor(w, "w", tdt, ws_)
+    _check_tensor(y, "y", tdt, ys)
+    _check_c(epi, tdt, ys)
+    if bias is not None:
+        _check_tensor(bias, "bias", tdt, (prob["K"],))
+    need = conv2d_workspace_size_ex(CONV2D_OP_FPROP, prob, code, algo, epi)
+    wsp, wsb = _check_workspace(workspace, need)
+    keep, ep = _epi(epi)
+    st = load().conv2d_fprop_ex(ctypes.byref(make_problem(prob)), code, x.data_ptr(), w.data_ptr(),
+                                None if bias is None else bias.data_ptr(), int(bool(relu)), ep,
+                                y.data_ptr(), wsp, wsb, _algo(algo), _stream(stream))
+    _raise(st, "conv2d_fprop_ex")
+
+
+def conv2d_dgrad_ex(prob, dtype, dy, w, epi, dx, workspace, algo=None, stream=None):
+    code = _dtype_code(dtype)
+    tdt = CODE_DTYPE[code]
+    xs, ws_, ys = _shapes(prob)
+    _check_tensor(dy, "dy", tdt, ys)
+    _check_tensor(w, "w", tdt, ws_)
+    _check_tensor(dx, "dx", tdt, xs)
+    _check_c(epi, tdt, xs)
+    need = conv2d_workspace_size_ex(CONV2D_OP_DGRAD, prob, code, algo, epi)
+    wsp, wsb = _check_workspace(workspace, need)
+    keep, ep = _epi(epi)
+    st = load().conv2d_dgrad_ex(ctypes.byref(make_problem(prob)), code, dy.data_ptr(), w.data_ptr(), ep,
+                                dx.data_ptr(), wsp, wsb, _algo(algo), _stream(stream))
+    _raise(st, "conv2d_dgrad_ex")
+
+
+def conv2d_wgrad_ex(prob, dtype, x, dy, epi, dw, workspace, algo=None, stream=None):
+    """dw is float32 when epi["out_f32"] (and so is epi["c"])."""
+    code = _dtype_code(dtype)
+    tdt = CODE_DTYPE[code]
+    xs, ws_, ys = _shapes(prob)
+    _check_tensor(x, "x", tdt, xs)
+    _check_tensor(dy, "dy", tdt, ys)
+    odt = torch.float32 if (epi is not None and epi.get("out_f32")) else tdt
+    _check_tensor(dw, "dw", odt, ws_)
+    _check_c(epi, odt, ws_)
+    need = conv2d_workspace_size_ex(CONV2D_OP_WGRAD, prob, code, algo, epi)
+    wsp, wsb = _check_workspace(workspace, need)
+    keep, ep = _epi(epi)
+    st = load().conv2d_wgrad_ex(ctypes.byref(make_problem(prob)), code, x.data_ptr(), dy.data_ptr(), ep,
+                                dw.data_ptr(), wsp, wsb, _algo(algo), _stream(stream))
+    _raise(st, "conv2d_wgrad_ex")
 
 
 # --------------------------------------------------------------- conveniences

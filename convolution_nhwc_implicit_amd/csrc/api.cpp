@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "conv2d_nhwc.h"
 #include "internal.h"
@@ -110,6 +111,15 @@ AxisPhase axis_phase(int ph, int extent_full, int stride, int pad, int dil, int 
 
 constexpr size_t kNoBuf = ~(size_t)0;
 
+// Output epilogue of a pass (conv2d_epilogue_t, checked): out = alpha * result
+// + beta * c; wgrad may store fp32.
+struct Epi {
+    bool axpby = false;  // alpha != 1 or beta != 0
+    float alpha = 1.0f, beta = 0.0f;
+    const void *c = nullptr;
+    bool out_f32 = false;
+};
+
 struct Plan {
     int op, dtype;
     int kernel;  // 1 implicit GEMM, 2 direct
@@ -195,19 +205,21 @@ int choose_direct_tiled_splits(long long wgs_per_slice, long long npix)
     return (int)std::max(1LL, std::min(s, 4096LL));
 }
 
-int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, Plan *pl);
+int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, const Epi &ep,
+              Plan *pl);
 
 // Plan of a groups == 1 problem whose C or K is not a multiple of vec: the
 // inner problem has both rounded up to vec; the workspace holds the inner
 // pass's own workspace, then the padded copies the pass needs.
-int plan_padded(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, int vec, Plan *pl)
+int plan_padded(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, const Epi &ep, int vec,
+                Plan *pl)
 {
     const Dims d = pl->d;
     conv2d_problem_t in = *prob;
     in.c = (int)((d.C + vec - 1) / vec * vec);
     in.k = (int)((d.K + vec - 1) / vec * vec);
     Plan ip;
-    int st = make_plan(op, &in, dtype, algo, &ip);
+    int st = make_plan(op, &in, dtype, algo, ep, &ip);
     if (st) return st;
     *pl = ip;
     pl->d = d;
@@ -223,7 +235,7 @@ int plan_padded(int op, const conv2d_problem_t *prob, int dtype, const conv2d_al
         off += round_up((size_t)elems * esz, 256);
         return o;
     };
-    pl->off_filt = take(Kp * d.R * d.S * Cp, e);
+    pl->off_filt = take(Kp * d.R * d.S * Cp, ep.out_f32 ? 4 : e);
     if (op == CONV2D_OP_FPROP) {
         if (pad_c) pl->off_act = take(d.N * d.H * d.W * Cp, e);
         if (pad_k) pl->off_out = take(d.N * d.P * d.Q * Kp, e);
@@ -236,7 +248,8 @@ int plan_padded(int op, const conv2d_problem_t *prob, int dtype, const conv2d_al
     return CONV2D_OK;
 }
 
-int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, Plan *pl)
+int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, const Epi &ep,
+              Plan *pl)
 {
     int st = validate(prob, &pl->d);
     if (st) return st;
@@ -248,6 +261,10 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     if (dtype == CONV2D_DTYPE_I8 && op != CONV2D_OP_FPROP) return CONV2D_ERR_UNSUPPORTED;
     if (!fits_32bit(d)) return CONV2D_ERR_UNSUPPORTED;
     if (algo && (algo->tile < 0 || algo->split_k < 0)) return CONV2D_ERR_INVALID_ARGUMENT;
+    if ((ep.axpby || ep.out_f32) && dtype == CONV2D_DTYPE_I8) return CONV2D_ERR_UNSUPPORTED;
+    if (ep.out_f32 && op != CONV2D_OP_WGRAD) return CONV2D_ERR_INVALID_ARGUMENT;
+    // the wgrad epilogue runs in the split-K reduce: partials even for one slice
+    const bool wparts = ep.axpby || ep.out_f32;
     pl->op = op;
     pl->dtype = dtype;
     pl->split_k = 1;
@@ -260,7 +277,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     // implicit GEMM: 128-bit chunks of channels along GEMM-K and GEMM-N;
     // other channel counts run on zero-padded copies
     const int vec = dtype == CONV2D_DTYPE_I8 ? 16 : 8;
-    if (d.G == 1 && (d.C % vec || d.K % vec)) return plan_padded(op, prob, dtype, algo, vec, pl);
+    if (d.G == 1 && (d.C % vec || d.K % vec)) return plan_padded(op, prob, dtype, algo, ep, vec, pl);
 
     if (d.G > 1) {
         // tile 0: one thread per output; tile 1: LDS-tiled dot-product kernel
@@ -284,7 +301,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
                                             : choose_direct_splits(outputs, npix);
             if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
             pl->split_k = s;
-            if (s > 1) pl->ws_bytes = round_up((size_t)s * splitk_stride(outputs) * sizeof(float), 256);
+            if (s > 1 || wparts) pl->ws_bytes = round_up((size_t)s * splitk_stride(outputs) * sizeof(float), 256);
         }
         return CONV2D_OK;
     }
@@ -320,11 +337,12 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         int s = (algo && algo->split_k) ? algo->split_k : choose_wgrad_splits(tiles, npix);
         if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
         pl->split_k = s;
-        if (s > 1) pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * ncols) * sizeof(float), 256);
+        if (s > 1 || wparts) pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * ncols) * sizeof(float), 256);
         return CONV2D_OK;
     }
-    const bool band = op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K)
-                                            : band_eligible(d, dtype, d.K, d.P, d.Q, d.C);
+    // the band kernels have no linear-combination epilogue
+    const bool band = !ep.axpby && (op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K)
+                                                          : band_eligible(d, dtype, d.K, d.P, d.Q, d.C));
     pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0);
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
@@ -422,7 +440,7 @@ int conv2d_workspace_size(int op, const conv2d_problem_t *prob, int dtype, const
 {
     if (!bytes) return CONV2D_ERR_INVALID_ARGUMENT;
     Plan pl;
-    int st = make_plan(op, prob, dtype, algo, &pl);
+    int st = make_plan(op, prob, dtype, algo, Epi(), &pl);
     if (st) return st;
     *bytes = pl.ws_bytes;
     return CONV2D_OK;
@@ -433,7 +451,7 @@ int conv2d_plan_info(int op, const conv2d_problem_t *prob, int dtype, const conv
 {
     if (!info) return CONV2D_ERR_INVALID_ARGUMENT;
     Plan pl;
-    int st = make_plan(op, prob, dtype, algo, &pl);
+    int st = make_plan(op, prob, dtype, algo, Epi(), &pl);
     if (st) return st;
     info->kernel = pl.kernel;
     info->tile = pl.tile;
@@ -444,12 +462,12 @@ int conv2d_plan_info(int op, const conv2d_problem_t *prob, int dtype, const conv
     return CONV2D_OK;
 }
 
-int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const void *w, const void *bias,
-                 int relu, double act_scale, double w_scale, double out_scale, void *y, void *workspace,
-                 size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, const void *w, const void *bias,
+                     int relu, double act_scale, double w_scale, double out_scale, const Epi &ep, void *y,
+                     void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
 {
     Plan pl;
-    int st = make_plan(CONV2D_OP_FPROP, prob, dtype, algo, &pl);
+    int st = make_plan(CONV2D_OP_FPROP, prob, dtype, algo, ep, &pl);
     if (st) return st;
     if (!x || !w || !y) return CONV2D_ERR_INVALID_ARGUMENT;
     if (relu != 0 && relu != 1) return CONV2D_ERR_INVALID_ARGUMENT;
@@ -481,6 +499,7 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
         }
         if (repack(e, w, d.K * d.R * d.S, d.C, d.C, wsb + pl.off_filt, Kp * d.R * d.S, Cp, Cp, s) != hipSuccess)
             return CONV2D_ERR_DEVICE;
+        Epi ei = ep;
         if (pl.off_out != kNoBuf) {
             yp = wsb + pl.off_out;
             if (bias) {
@@ -488,9 +507,13 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
                 if (repack(dtype == CONV2D_DTYPE_I8 ? 4 : e, bias, 1, d.K, d.K, (void *)bp, 1, Kp, Kp, s) != hipSuccess)
                     return CONV2D_ERR_DEVICE;
             }
+            if (ep.c) {  // C padded into the padded output, which the inner pass reads and overwrites
+                if (repack(e, ep.c, npix, d.K, d.K, yp, npix, Kp, Kp, s) != hipSuccess) return CONV2D_ERR_DEVICE;
+                ei.c = yp;
+            }
         }
-        st = conv2d_fprop(&pl.inner, dtype, xp, wsb + pl.off_filt, bp, relu, act_scale, w_scale, out_scale, yp,
-                          workspace, pl.inner_ws, algo, stream);
+        st = fprop_run(&pl.inner, dtype, xp, wsb + pl.off_filt, bp, relu, act_scale, w_scale, out_scale, ei, yp,
+                       workspace, pl.inner_ws, algo, stream);
         if (st || pl.off_out == kNoBuf) return st;
         return hip_status(repack(e, yp, npix, d.K, Kp, y, npix, d.K, d.K, s));
     }
@@ -503,6 +526,7 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
         a.pad_h = (int)d.ph; a.pad_w = (int)d.pw; a.sh = (int)d.sh; a.sw = (int)d.sw;
         a.dh = (int)d.dh; a.dw = (int)d.dw; a.G = (int)d.G; a.Cg = (int)d.Cg; a.Kg = (int)d.Kg;
         a.relu = relu; a.requant_m = m; a.splits = 1;
+        a.axpby = ep.axpby; a.alpha = ep.alpha; a.beta = ep.beta; a.cmat = ep.c;
         a.total = d.N * d.P * d.Q * d.K;
         if (pl.tile == 1) {
             a.tiled = 1;
@@ -524,6 +548,7 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
     a.ho = (int)d.P; a.wo = (int)d.Q; a.osh = 1; a.osw = 1;
     a.gsh = (int)d.sh; a.gsw = (int)d.sw;
     a.relu = relu; a.requant_m = m;
+    a.axpby = ep.axpby; a.alpha = ep.alpha; a.beta = ep.beta; a.cmat = ep.c;
     a.nphases = 1;
     Phase &ph = a.ph[0];
     ph.mi = (int)d.P; ph.mj = (int)d.Q; ph.oh0 = 0; ph.ow0 = 0;
@@ -538,11 +563,11 @@ int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const v
     return hip_status(launch_igemm(dtype, pl.tile, a, ph.tiles_m, gn, s));
 }
 
-int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const void *w, void *dx,
-                 void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, const void *w, const Epi &ep,
+                     void *dx, void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
 {
     Plan pl;
-    int st = make_plan(CONV2D_OP_DGRAD, prob, dtype, algo, &pl);
+    int st = make_plan(CONV2D_OP_DGRAD, prob, dtype, algo, ep, &pl);
     if (st) return st;
     if (!dy || !w || !dx) return CONV2D_ERR_INVALID_ARGUMENT;
     if (!aligned16(dy) || !aligned16(w) || !aligned16(dx)) return CONV2D_ERR_UNSUPPORTED;
@@ -563,8 +588,15 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
         }
         if (repack(e, w, d.K * d.R * d.S, d.C, d.C, wsb + pl.off_filt, Kp * d.R * d.S, Cp, Cp, s) != hipSuccess)
             return CONV2D_ERR_DEVICE;
-        if (pl.off_act != kNoBuf) dxp = wsb + pl.off_act;
-        st = conv2d_dgrad(&pl.inner, dtype, dyp, wsb + pl.off_filt, dxp, workspace, pl.inner_ws, algo, stream);
+        Epi ei = ep;
+        if (pl.off_act != kNoBuf) {
+            dxp = wsb + pl.off_act;
+            if (ep.c) {  // C padded into the padded dx, which the inner pass reads and overwrites
+                if (repack(e, ep.c, nin, d.C, d.C, dxp, nin, Cp, Cp, s) != hipSuccess) return CONV2D_ERR_DEVICE;
+                ei.c = dxp;
+            }
+        }
+        st = dgrad_run(&pl.inner, dtype, dyp, wsb + pl.off_filt, ei, dxp, workspace, pl.inner_ws, algo, stream);
         if (st || pl.off_act == kNoBuf) return st;
         return hip_status(repack(e, dxp, nin, d.C, Cp, dx, nin, d.C, d.C, s));
     }
@@ -577,6 +609,7 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
         a.pad_h = (int)d.ph; a.pad_w = (int)d.pw; a.sh = (int)d.sh; a.sw = (int)d.sw;
         a.dh = (int)d.dh; a.dw = (int)d.dw; a.G = (int)d.G; a.Cg = (int)d.Cg; a.Kg = (int)d.Kg;
         a.splits = 1;
+        a.axpby = ep.axpby; a.alpha = ep.alpha; a.beta = ep.beta; a.cmat = ep.c;
         a.total = d.N * d.H * d.W * d.C;
         if (pl.tile == 1) {
             a.tiled = 1;
@@ -603,6 +636,7 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
     a.ho = (int)d.H; a.wo = (int)d.W; a.osh = (int)d.sh; a.osw = (int)d.sw;
     a.gsh = 1; a.gsw = 1;
     a.relu = 0;
+    a.axpby = ep.axpby; a.alpha = ep.alpha; a.beta = ep.beta; a.cmat = ep.c;
     long long off = 0;
     int nph = 0, max_tiles = 0;
     for (int py = 0; py < d.sh; ++py)
@@ -638,11 +672,11 @@ int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const 
     return hip_status(launch_igemm(dtype, pl.tile, a, max_tiles, gn, s));
 }
 
-int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const void *dy, void *dw,
-                 void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, const void *dy, const Epi &ep,
+                     void *dw, void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
 {
     Plan pl;
-    int st = make_plan(CONV2D_OP_WGRAD, prob, dtype, algo, &pl);
+    int st = make_plan(CONV2D_OP_WGRAD, prob, dtype, algo, ep, &pl);
     if (st) return st;
     if (!x || !dy || !dw) return CONV2D_ERR_INVALID_ARGUMENT;
     if (!aligned16(x) || !aligned16(dy) || !aligned16(dw)) return CONV2D_ERR_UNSUPPORTED;
@@ -651,7 +685,11 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
     const Dims &d = pl.d;
     hipStream_t s = (hipStream_t)stream;
     const uint32_t npix = (uint32_t)(d.N * d.P * d.Q);
-    void *out = pl.split_k > 1 ? workspace : dw;
+    // the epilogue (alpha, beta, fp32 output) runs in the split-K reduce
+    const bool to_parts = ep.axpby || ep.out_f32;
+    const bool reduce = pl.split_k > 1 || to_parts;
+    void *out = reduce ? workspace : dw;
+    const ReduceEpi re{ep.alpha, ep.beta, ep.axpby ? ep.c : nullptr, ep.out_f32 ? 1 : 0};
 
     if (pl.padded) {
         unsigned char *wsb = (unsigned char *)workspace;
@@ -667,10 +705,17 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
             if (repack(e, dy, npix, d.K, d.K, (void *)dyp, npix, Kp, Kp, s) != hipSuccess) return CONV2D_ERR_DEVICE;
         }
         void *dwp = wsb + pl.off_filt;
-        st = conv2d_wgrad(&pl.inner, dtype, xp, dyp, dwp, workspace, pl.inner_ws, algo, stream);
+        const int eo = ep.out_f32 ? 4 : e;  // element size of dw (and C)
+        Epi ei = ep;
+        if (ep.c) {  // C padded into the padded dw, which the inner pass reads and overwrites
+            if (repack(eo, ep.c, d.K * d.R * d.S, d.C, d.C, dwp, Kp * d.R * d.S, Cp, Cp, s) != hipSuccess)
+                return CONV2D_ERR_DEVICE;
+            ei.c = dwp;
+        }
+        st = wgrad_run(&pl.inner, dtype, xp, dyp, ei, dwp, workspace, pl.inner_ws, algo, stream);
         if (st) return st;
         // the first K*R*S rows of the padded [Kp][R][S][Cp] filter are k < K
-        return hip_status(repack(e, dwp, Kp * d.R * d.S, Cp, Cp, dw, d.K * d.R * d.S, d.C, d.C, s));
+        return hip_status(repack(eo, dwp, Kp * d.R * d.S, Cp, Cp, dw, d.K * d.R * d.S, d.C, d.C, s));
     }
 
     if (pl.kernel == 2) {
@@ -686,10 +731,11 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
         a.total = d.K * d.R * d.S * d.Cg;
         a.part_stride = splitk_stride(a.total);
         a.tiled = pl.tile == 1;
+        a.to_parts = to_parts;
         hipError_t e = launch_direct_wgrad(dtype, a, s);
-        if (e != hipSuccess || pl.split_k == 1) return hip_status(e);
+        if (e != hipSuccess || !reduce) return hip_status(e);
         return hip_status(
-            launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k, a.total, a.part_stride, dw, s));
+            launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k, a.total, a.part_stride, dw, &re, s));
     }
 
     if (pl.tile == kWgradBandTile) {
@@ -707,7 +753,7 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
         hipError_t e = launch_wgrad_band(dtype, b, s);
         if (e != hipSuccess) return CONV2D_ERR_DEVICE;
         return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,
-                                               d.K * d.R * d.S * d.C, b.part_stride, dw, s));
+                                               d.K * d.R * d.S * d.C, b.part_stride, dw, &re, s));
     }
 
     WgradArgs a;
@@ -728,10 +774,96 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
     a.div_PQ = make_fastdiv((uint32_t)(d.P * d.Q));
     a.div_C = make_fastdiv((uint32_t)d.C);
     a.div_S = make_fastdiv((uint32_t)d.S);
+    a.to_parts = to_parts;
     hipError_t e = launch_wgrad(dtype, pl.tile, a, s);
-    if (e != hipSuccess || pl.split_k == 1) return hip_status(e);
+    if (e != hipSuccess || !reduce) return hip_status(e);
     return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,
-                                           (long long)d.K * a.ncols, a.part_stride, dw, s));
+                                           (long long)d.K * a.ncols, a.part_stride, dw, &re, s));
+}
+
+// conv2d_epilogue_t -> Epi, with its checks (before anything is enqueued)
+static int make_epi(const conv2d_epilogue_t *e, int op, Epi *ep)
+{
+    *ep = Epi();
+    if (!e) return CONV2D_OK;
+    if (!(std::fabs(e->alpha) < 1e30) || !(std::fabs(e->beta) < 1e30)) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (e->out_f32 != 0 && e->out_f32 != 1) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (e->out_f32 && op != CONV2D_OP_WGRAD) return CONV2D_ERR_INVALID_ARGUMENT;
+    ep->alpha = (float)e->alpha;
+    ep->beta = (float)e->beta;
+    ep->axpby = ep->alpha != 1.0f || ep->beta != 0.0f;
+    ep->out_f32 = e->out_f32 != 0;
+    if (ep->beta != 0.0f) {
+        if (!e->c) return CONV2D_ERR_INVALID_ARGUMENT;
+        if (!aligned16(e->c)) return CONV2D_ERR_UNSUPPORTED;
+        ep->c = e->c;
+    }
+    return CONV2D_OK;
+}
+
+int conv2d_workspace_size_ex(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo,
+                             const conv2d_epilogue_t *epi, size_t *bytes)
+{
+    if (!bytes) return CONV2D_ERR_INVALID_ARGUMENT;
+    Epi ep;
+    int st = make_epi(epi, op, &ep);
+    if (st) return st;
+    Plan pl;
+    st = make_plan(op, prob, dtype, algo, ep, &pl);
+    if (st) return st;
+    *bytes = pl.ws_bytes;
+    return CONV2D_OK;
+}
+
+int conv2d_fprop(const conv2d_problem_t *prob, int dtype, const void *x, const void *w, const void *bias,
+                 int relu, double act_scale, double w_scale, double out_scale, void *y, void *workspace,
+                 size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+{
+    return fprop_run(prob, dtype, x, w, bias, relu, act_scale, w_scale, out_scale, Epi(), y, workspace,
+                     workspace_bytes, algo, stream);
+}
+
+int conv2d_dgrad(const conv2d_problem_t *prob, int dtype, const void *dy, const void *w, void *dx,
+                 void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+{
+    return dgrad_run(prob, dtype, dy, w, Epi(), dx, workspace, workspace_bytes, algo, stream);
+}
+
+int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const void *dy, void *dw,
+                 void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
+{
+    return wgrad_run(prob, dtype, x, dy, Epi(), dw, workspace, workspace_bytes, algo, stream);
+}
+
+int conv2d_fprop_ex(const conv2d_problem_t *prob, int dtype, const void *x, const void *w, const void *bias,
+                    int relu, const conv2d_epilogue_t *epi, void *y, void *workspace, size_t workspace_bytes,
+                    const conv2d_algo_t *algo, void *stream)
+{
+    Epi ep;
+    int st = make_epi(epi, CONV2D_OP_FPROP, &ep);
+    if (st) return st;
+    if (dtype == CONV2D_DTYPE_I8) return CONV2D_ERR_UNSUPPORTED;
+    return fprop_run(prob, dtype, x, w, bias, relu, 1.0, 1.0, 1.0, ep, y, workspace, workspace_bytes, algo, stream);
+}
+
+int conv2d_dgrad_ex(const conv2d_problem_t *prob, int dtype, const void *dy, const void *w,
+                    const conv2d_epilogue_t *epi, void *dx, void *workspace, size_t workspace_bytes,
+                    const conv2d_algo_t *algo, void *stream)
+{
+    Epi ep;
+    int st = make_epi(epi, CONV2D_OP_DGRAD, &ep);
+    if (st) return st;
+    return dgrad_run(prob, dtype, dy, w, ep, dx, workspace, workspace_bytes, algo, stream);
+}
+
+int conv2d_wgrad_ex(const conv2d_problem_t *prob, int dtype, const void *x, const void *dy,
+                    const conv2d_epilogue_t *epi, void *dw, void *workspace, size_t workspace_bytes,
+                    const conv2d_algo_t *algo, void *stream)
+{
+    Epi ep;
+    int st = make_epi(epi, CONV2D_OP_WGRAD, &ep);
+    if (st) return st;
+    return wgrad_run(prob, dtype, x, dy, ep, dw, workspace, workspace_bytes, algo, stream);
 }
 
 }  // extern "C"

@@ -19,6 +19,15 @@ __device__ inline float ld_f(const typename E::elem *p)
 }
 
 // ---------------------------------------------------------------- fprop ----
+// alpha * acc + beta * cmat[idx] when the linear-combination epilogue is on
+template <class E>
+__device__ inline float axpby_at(const DirectArgs &a, float acc, size_t idx)
+{
+    if (!a.axpby) return acc;
+    const float c = a.cmat ? ld_f<E>((const typename E::elem *)a.cmat + idx) : 0.0f;
+    return a.alpha * acc + a.beta * c;
+}
+
 template <class E>
 __global__ __launch_bounds__(256) void direct_fprop_kernel(const DirectArgs a)
 {
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(256) void direct_fprop_kernel(const DirectArgs a)
             }
         }
         const float b = a.bias ? ld_f<E>((const elem *)a.bias + k) : 0.0f;
-        ((elem *)a.out)[idx] = E::from_f32(bias_relu_f32(acc, b, a.relu));
+        ((elem *)a.out)[idx] = E::from_f32(bias_relu_f32(axpby_at<E>(a, acc, idx), b, a.relu));
     }
 }
 
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(256) void direct_dgrad_kernel(const DirectArgs a)
             for (int kl = 0; kl < a.Kg; ++kl) acc += ld_f<E>(dyp + kl) * ld_f<E>(wp + kl * kstride);
         }
     }
-    ((elem *)a.out)[idx] = E::from_f32(acc);
+    ((elem *)a.out)[idx] = E::from_f32(axpby_at<E>(a, acc, idx));
 }
 
 // ---------------------------------------------------------------- wgrad ----
@@ -145,7 +154,7 @@ __global__ __launch_bounds__(256) void direct_wgrad_kernel(const DirectArgs a)
             }
         }
     }
-    if (a.splits == 1)
+    if (a.splits == 1 && !a.to_parts)
         ((elem *)a.out)[idx] = E::from_f32(acc);
     else
         ((float *)a.out)[(size_t)z * a.part_stride + idx] = acc;
@@ -242,6 +251,7 @@ __global__ __launch_bounds__(256) void direct_fprop_tiled(const DirectArgs a)
             }
         }
         const int k0 = g * a.Kg + kb * 4;
+        const size_t o = (((size_t)n * a.P + p) * a.Q + q) * a.K + k0;
         uint32_t v[2];
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
@@ -250,11 +260,11 @@ __global__ __launch_bounds__(256) void direct_fprop_tiled(const DirectArgs a)
             for (int e = 0; e < 2; ++e) {
                 const int k = k0 + 2 * e2 + e;
                 const float b = a.bias ? ld_f<E>((const elem *)a.bias + k) : 0.0f;
-                lohi[e] = E::from_f32(bias_relu_f32(acc[2 * e2 + e], b, a.relu));
+                lohi[e] = E::from_f32(bias_relu_f32(axpby_at<E>(a, acc[2 * e2 + e], o + 2 * e2 + e), b, a.relu));
             }
             v[e2] = lohi[0] | (lohi[1] << 16);
         }
-        *(uint2 *)((elem *)a.out + (((size_t)n * a.P + p) * a.Q + q) * a.K + k0) = uint2{v[0], v[1]};
+        *(uint2 *)((elem *)a.out + o) = uint2{v[0], v[1]};
     }
 }
 
@@ -319,11 +329,13 @@ __global__ __launch_bounds__(256) void direct_dgrad_tiled(const DirectArgs a)
                 }
             }
         }
+        const size_t o = (((size_t)n * a.H + h) * a.W + wc) * a.C + g * a.Cg + cb * 4;
         uint32_t v[2];
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2)
-            v[e2] = (uint32_t)E::from_f32(acc[2 * e2]) | ((uint32_t)E::from_f32(acc[2 * e2 + 1]) << 16);
-        *(uint2 *)((elem *)a.out + (((size_t)n * a.H + h) * a.W + wc) * a.C + g * a.Cg + cb * 4) = uint2{v[0], v[1]};
+            v[e2] = (uint32_t)E::from_f32(axpby_at<E>(a, acc[2 * e2], o + 2 * e2)) |
+                    ((uint32_t)E::from_f32(axpby_at<E>(a, acc[2 * e2 + 1], o + 2 * e2 + 1)) << 16);
+        *(uint2 *)((elem *)a.out + o) = uint2{v[0], v[1]};
     }
 }
 
@@ -388,7 +400,7 @@ __global__ __launch_bounds__(256) void direct_wgrad_tiled(const DirectArgs a)
     for (int e = 0; e < 4; ++e) {
         const int k = g * a.Kg + kb * 4 + e;
         const size_t o = (((size_t)k * a.R + r) * a.S + s) * a.Cg + c8 * 8;
-        if (a.splits == 1) {
+        if (a.splits == 1 && !a.to_parts) {
             uint32_t v[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)

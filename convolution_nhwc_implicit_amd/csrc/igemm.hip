@@ -228,8 +228,22 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-                    *(elem *)(smem + row * CROWB + col * OSZ) =
-                        E::from_f32(bias_relu_f32(acc[i][j][r], b, a.relu));
+                    float v = acc[i][j][r];
+                    if (a.axpby) {
+                        // linear combination with C at this output element
+                        float c = 0.0f;
+                        const uint32_t m = (uint32_t)mt * BM + row;
+                        if (a.cmat && nok && m < ph.m_total) {
+                            const uint32_t ni = fdiv(m, ph.div_mimj);
+                            const uint32_t rem = m - ni * mi_mj;
+                            const uint32_t ii = fdiv(rem, ph.div_mj);
+                            const uint32_t jj = rem - ii * ph.mj;
+                            const int oh = ph.oh0 + (int)ii * a.osh, ow = ph.ow0 + (int)jj * a.osw;
+                            c = E::to_f32(((const elem *)a.cmat)[(((size_t)ni * a.ho + oh) * a.wo + ow) * a.ngemm + n]);
+                        }
+                        v = a.alpha * v + a.beta * c;
+                    }
+                    *(elem *)(smem + row * CROWB + col * OSZ) = E::from_f32(bias_relu_f32(v, b, a.relu));
                 }
         }
     }

@@ -86,6 +86,10 @@ struct IgemmArgs {
     int gsh, gsw;          // source step per sub-grid step
     int relu;
     double requant_m;      // int8 only
+    // out = alpha * acc + beta * cmat (+ bias), cmat laid out like dst (float paths)
+    int axpby;
+    float alpha, beta;
+    const void *cmat;
     int nphases;
     Phase ph[kMaxPhases];
 };
@@ -157,14 +161,22 @@ struct WgradArgs {
     int splits;
     long long part_stride;  // elements between consecutive slices' partials
     FastDiv div_Q, div_PQ, div_C, div_S;
+    int to_parts;           // fp32 partials even for one split
 };
 
 int wgrad_num_tiles();
 TileShape wgrad_tile_shape(int tile);
 constexpr int kWgradPixStep = 64;  // pixels per main-loop step
 hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st);
+// Epilogue of the split-K sum t: out = alpha * t + beta * c (c laid out like
+// out, NULL when beta == 0), stored as fp32 when out_f32, else rounded once.
+struct ReduceEpi {
+    float alpha, beta;
+    const void *c;
+    int out_f32;
+};
 hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long long count,
-                                long long stride, void *out, hipStream_t st);
+                                long long stride, void *out, const ReduceEpi *epi, hipStream_t st);
 // Elements between consecutive slices' partials: count rounded up to 4.
 inline long long splitk_stride(long long count) { return (count + 3) / 4 * 4; }
 
@@ -210,6 +222,12 @@ struct DirectArgs {
     long long total;        // output elements (per split for wgrad)
     int tiled;              // use the LDS-tiled kernel (direct_tiled_rows / direct_wgrad_tiled_ok)
     int rows;               // fprop / dgrad tiled: output rows per workgroup
+    // fprop / dgrad: out = alpha * conv + beta * cmat (+ bias), cmat laid out
+    // like out, when axpby; wgrad: fp32 partials even for one split when to_parts
+    int axpby;
+    float alpha, beta;
+    const void *cmat;
+    int to_parts;
 };
 // Output rows per workgroup of the LDS-tiled direct fprop (op 0) / dgrad
 // (op 1) kernel for 16-bit types, or 0 if it does not apply.

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
             for (int r = 0; r < 4; ++r) {
                 const int k = mt * BM + wm * WTM + i * 16 + (lane >> 4) * 4 + r;
                 if (k >= a.K) continue;
-                if (a.splits == 1)
+                if (a.splits == 1 && !a.to_parts)
                     ((elem *)a.out)[(size_t)k * a.ncols + col] = E::from_f32(acc[i][j][r]);
                 else
                     ((float *)a.out)[(size_t)z * a.part_stride + (size_t)k * a.ncols + col] = acc[i][j][r];
@@ -177,8 +177,9 @@ hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st)
 // ---------------------------------------------------------------------------
 template <class E>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *parts, int splits, long long count,
-                                                            long long stride, typename E::elem *out)
+                                                            long long stride, void *out_, const ReduceEpi epi)
 {
+    using elem = typename E::elem;
     constexpr int NCLS = 16;
     __shared__ f32x4 part[NCLS][16];
     const int cls = threadIdx.x >> 4, e = threadIdx.x & 15;
@@ -218,30 +219,46 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *parts, 
             t[2] += v[2];
             t[3] += v[3];
         }
-        typename E::elem o[4];
+        if (epi.alpha != 1.0f || epi.beta != 0.0f) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = E::from_f32(t[j]);
-        if (i + 4 <= count) {
-            *(uint2 *)(out + i) = *(const uint2 *)o;
+            for (int j = 0; j < 4; ++j) {
+                float c = 0.0f;
+                if (epi.c && i + j < count)
+                    c = epi.out_f32 ? ((const float *)epi.c)[i + j] : E::to_f32(((const elem *)epi.c)[i + j]);
+                t[j] = epi.alpha * t[j] + epi.beta * c;
+            }
+        }
+        if (epi.out_f32) {
+            float *out = (float *)out_;
+            if (i + 4 <= count) {
+                *(f32x4 *)(out + i) = t;
+            } else {
+                for (int j = 0; j < 4 && i + j < count; ++j) out[i + j] = t[j];
+            }
         } else {
-            for (int j = 0; j < 4 && i + j < count; ++j) out[i + j] = o[j];
+            elem *out = (elem *)out_;
+            elem o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = E::from_f32(t[j]);
+            if (i + 4 <= count) {
+                *(uint2 *)(out + i) = *(const uint2 *)o;
+            } else {
+                for (int j = 0; j < 4 && i + j < count; ++j) out[i + j] = o[j];
+            }
         }
     }
 }
 
 hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long long count,
-                                long long stride, void *out, hipStream_t st)
+                                long long stride, void *out, const ReduceEpi *epi, hipStream_t st)
 {
     if (stride % 4 || stride < count) return hipErrorInvalidValue;
     const unsigned blocks = (unsigned)((count + 63) / 64);
     if (blocks == 0) return hipSuccess;
+    const ReduceEpi e = epi ? *epi : ReduceEpi{1.0f, 0.0f, nullptr, 0};
     switch (dtype) {
-    case CONV2D_DTYPE_F16:
-        splitk_reduce_kernel<EF16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, (uint16_t *)out);
-        break;
-    case CONV2D_DTYPE_BF16:
-        splitk_reduce_kernel<EBF16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, (uint16_t *)out);
-        break;
+    case CONV2D_DTYPE_F16: splitk_reduce_kernel<EF16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, out, e); break;
+    case CONV2D_DTYPE_BF16: splitk_reduce_kernel<EBF16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, out, e); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

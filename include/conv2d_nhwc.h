@@ -186,6 +186,55 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype,
                  void *workspace, size_t workspace_bytes,
                  const conv2d_algo_t *algo, void *stream);
 
+/*
+ * Linear-combination epilogue of the three passes: the CUTLASS Python
+ * notebook runs fprop, dgrad and wgrad as D = alpha * conv + beta * C with a
+ * source tensor C of the output's shape ("Run the Conv2d" and the backward
+ * sections); wgrad accumulates in fp32 whatever the output type (the TVM
+ * pull request "[CUTLASS] Add wgrad support" makes that the rule), which the
+ * out_f32 option hands back unrounded.  With an epilogue each output element is, in fp32,
+ *   v = alpha * r + beta * C[same element] (+ bias[k] for fprop)
+ * (the products rounded to fp32, then added left to right), then ReLU if
+ * set (fprop), then one rounding to the output type (none with out_f32),
+ * where r is the fp32 result of the pass.  alpha and beta are converted to
+ * fp32.  C may alias the output (each element is read before it is written).
+ * A NULL epilogue, or alpha = 1, beta = 0, out_f32 = 0, is the plain pass.
+ * F16/BF16 only (INT8 -> UNSUPPORTED).  Band kernels have no such epilogue,
+ * so fprop/dgrad with alpha != 1 or beta != 0 run on the implicit GEMM; wgrad
+ * always applies it in its split-K reduction, so it needs a workspace even
+ * for one slice (conv2d_workspace_size_ex).
+ */
+typedef struct conv2d_epilogue {
+    double alpha;    /* finite (|alpha| < 1e30) */
+    double beta;     /* finite; 0 ignores c */
+    const void *c;   /* device, laid out like the output; required (16-byte aligned) when beta != 0 */
+    int out_f32;     /* wgrad only: dw and c are fp32 (the sum is not rounded) */
+} conv2d_epilogue_t;
+
+/* conv2d_workspace_size for a pass with an epilogue (NULL = plain). */
+int conv2d_workspace_size_ex(int op, const conv2d_problem_t *prob, int dtype,
+                             const conv2d_algo_t *algo, const conv2d_epilogue_t *epi,
+                             size_t *bytes);
+
+/* conv2d_fprop with an epilogue (F16/BF16; no int8 requantisation). */
+int conv2d_fprop_ex(const conv2d_problem_t *prob, int dtype,
+                    const void *x, const void *w, const void *bias, int relu,
+                    const conv2d_epilogue_t *epi, void *y,
+                    void *workspace, size_t workspace_bytes,
+                    const conv2d_algo_t *algo, void *stream);
+
+/* conv2d_dgrad with an epilogue. */
+int conv2d_dgrad_ex(const conv2d_problem_t *prob, int dtype,
+                    const void *dy, const void *w, const conv2d_epilogue_t *epi, void *dx,
+                    void *workspace, size_t workspace_bytes,
+                    const conv2d_algo_t *algo, void *stream);
+
+/* conv2d_wgrad with an epilogue; with out_f32 dw is float32 [K][R][S][C/G]. */
+int conv2d_wgrad_ex(const conv2d_problem_t *prob, int dtype,
+                    const void *x, const void *dy, const conv2d_epilogue_t *epi, void *dw,
+                    void *workspace, size_t workspace_bytes,
+                    const conv2d_algo_t *algo, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *conv2d_status_string(int status);
 

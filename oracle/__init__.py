@@ -41,6 +41,8 @@ def _load():
         lib.oracle_fprop_sampled.argtypes = [ip, dp, dp, dp, ctypes.c_int, i64p, ctypes.c_long, dp]
         lib.oracle_dgrad_sampled.argtypes = [ip, dp, dp, i64p, ctypes.c_long, dp]
         lib.oracle_wgrad_sampled.argtypes = [ip, dp, dp, i64p, ctypes.c_long, dp]
+        lib.oracle_linear_combination.argtypes = [dp, dp, ctypes.c_long, ctypes.c_long, ctypes.c_double,
+                                                   ctypes.c_double, dp, ctypes.c_int, dp]
         lib.oracle_requant_multiplier.restype = ctypes.c_double
         lib.oracle_requant_multiplier.argtypes = [ctypes.c_double] * 3
         lib.oracle_requant.argtypes = [dp, i64p, ctypes.c_long, ctypes.c_long,
@@ -152,6 +154,24 @@ def wgrad_sampled(prob, x, dy, idx):
     dp = ctypes.c_double
     _check(_load().oracle_wgrad_sampled(_dims(prob), _ptr(x, dp), _ptr(dy, dp),
                                         _ptr(idx, ctypes.c_int64), idx.shape[0], _ptr(out, dp)))
+    return out
+
+
+def linear_combination(r, alpha=1.0, beta=0.0, c=None, bias=None, relu=False):
+    """alpha * r + beta * c (+ bias over the last axis) (ReLU), elementwise in
+    fp64: the D = alpha*conv + beta*C epilogue of the CUTLASS notebook.  r is a
+    pass's fp64 result, c an array of the same shape (or None)."""
+    r = _f64(r)
+    out = np.empty_like(r)
+    K = r.shape[-1]
+    cc = None if c is None else _f64(c)
+    if cc is not None and cc.shape != r.shape:
+        raise ValueError("c must have the result's shape")
+    b = None if bias is None else _f64(bias)
+    dp = ctypes.c_double
+    _load().oracle_linear_combination(_ptr(r, dp), None if cc is None else _ptr(cc, dp), r.size, K,
+                                      float(alpha), float(beta), None if b is None else _ptr(b, dp),
+                                      int(bool(relu)), _ptr(out, dp))
     return out
 
 

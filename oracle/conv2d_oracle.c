@@ -162,6 +162,26 @@ static double wgrad_at(const prob_t *p, const double *x, const double *dy,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Linear-combination epilogue of the CUTLASS Python notebook: every pass it  */
+/* runs (fprop "Run the Conv2d", dgrad and wgrad) produces                   */
+/* D = alpha * conv + beta * C for a source tensor C of the output's shape.  */
+/* With a bias and ReLU (fprop) the bias is added to that sum and ReLU comes */
+/* last, as in the plain epilogue below (conv, bias, ReLU).  r holds the     */
+/* pass's exact result, out[i] = relu(alpha*r[i] + beta*c[i] + bias[i % K]). */
+/* ------------------------------------------------------------------------ */
+void oracle_linear_combination(const double *r, const double *c, long count, long K, double alpha,
+                               double beta, const double *bias, int relu, double *out)
+{
+    for (long i = 0; i < count; ++i) {
+        double v = alpha * r[i];
+        if (c) v += beta * c[i];
+        if (bias) v += bias[i % K];
+        if (relu && !(v > 0.0)) v = 0.0;
+        out[i] = v;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Epilogue of the float paths: + bias, then ReLU.  The order (conv, bias,    */
 /* ReLU) is the one the quantized cuDNN conv builds in its op graph          */
 /* (apply_impl_helper, "kReluFused" page).  ReLU maps every v <= 0 to +0.    */

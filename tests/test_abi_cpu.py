@@ -190,3 +190,39 @@ def test_binding_rejects_host_tensors():
     w = torch.zeros(16, 3, 3, 8, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         B.fprop(x, w, padding=1)
+
+
+def test_epilogue_checks(lib):
+    """The linear-combination entry points check their epilogue before any
+    device work (the fake addresses below are never dereferenced)."""
+    prob = B.make_problem(problem(2, 8, 8, 8, 16, 3, 3, pad=(1, 1)))
+    p16 = B.make_problem(problem(2, 16, 8, 8, 16, 3, 3, pad=(1, 1)))
+    pr = ctypes.byref(prob)
+    fake = ctypes.c_void_p(0x10000)
+
+    def epi(alpha=1.0, beta=0.0, c=None, f32=0):
+        return ctypes.byref(B.Conv2dEpilogue(alpha, beta, c, f32))
+
+    inv, uns = B.CONV2D_ERR_INVALID_ARGUMENT, B.CONV2D_ERR_UNSUPPORTED
+    assert lib.conv2d_fprop_ex(pr, 0, fake, fake, None, 0, epi(alpha=float("nan")), fake, None, 0,
+                               None, None) == inv
+    assert lib.conv2d_fprop_ex(pr, 0, fake, fake, None, 0, epi(beta=float("inf"), c=0x10000), fake,
+                               None, 0, None, None) == inv
+    assert lib.conv2d_dgrad_ex(pr, 0, fake, fake, epi(beta=1.0), fake, fake, 1 << 20, None,
+                               None) == inv  # beta != 0 needs C
+    assert lib.conv2d_dgrad_ex(pr, 0, fake, fake, epi(beta=1.0, c=0x10008), fake, fake, 1 << 20, None,
+                               None) == uns  # C must be 16-byte aligned
+    assert lib.conv2d_fprop_ex(pr, 0, fake, fake, None, 0, epi(f32=1), fake, None, 0, None,
+                               None) == inv  # fp32 output is for wgrad only
+    assert lib.conv2d_fprop_ex(ctypes.byref(p16), 2, fake, fake, None, 0, epi(alpha=2.0), fake, None, 0,
+                               None, None) == uns  # no int8 epilogue
+    s = problem(2, 16, 9, 9, 16, 3, 3, pad=(1, 1))
+    assert B.conv2d_workspace_size(2, s, "f16", algo=dict(split_k=1)) == 0
+    # wgrad applies the epilogue in its reduction: partials even for one slice
+    n = B.conv2d_workspace_size_ex(2, s, "f16", algo=dict(split_k=1), epi=dict(out_f32=True))
+    assert n >= 16 * 3 * 3 * 16 * 4
+    assert B.conv2d_workspace_size_ex(2, s, "f16", epi=None) == B.conv2d_workspace_size(2, s, "f16")
+    # the band-shaped dgrad needs no workspace plain, the filter re-layout with an epilogue
+    band = problem(2, 64, 9, 9, 64, 3, 3, pad=(1, 1))
+    assert B.conv2d_workspace_size(1, band, "f16") == 0
+    assert B.conv2d_workspace_size_ex(1, band, "f16", epi=dict(alpha=2.0)) >= 64 * 9 * 64 * 2

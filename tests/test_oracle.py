@@ -181,6 +181,35 @@ def test_bias_and_relu_epilogue():
     assert not np.any(np.signbit(yr))  # ReLU yields +0, never -0
 
 
+def test_linear_combination_epilogue():
+    """D = alpha*conv + beta*C (the CUTLASS notebook's epilogue): the plain
+    pass at (1, 0), beta*C alone at alpha = 0, linear in (alpha, beta), bias
+    and ReLU in the plain epilogue's order (exact on integer data)."""
+    rng = np.random.default_rng(16)
+    prob = problem(2, 4, 7, 6, 5, 3, 3, pad=(1, 1))
+    x, w, dy = rand_problem_inputs(prob, rng)
+    y = oracle.fprop(prob, x, w)
+    c = ints(rng, y.shape)
+    b = ints(rng, (5,))
+    assert np.array_equal(oracle.linear_combination(y), y)
+    assert np.array_equal(oracle.linear_combination(y, bias=b, relu=True),
+                          oracle.fprop(prob, x, w, bias=b, relu=True))
+    assert np.array_equal(oracle.linear_combination(y, 0.0, 3.0, c), 3.0 * c)
+    assert np.array_equal(oracle.linear_combination(y, 0.0, 3.0, c, bias=b), 3.0 * c + b)
+    l1 = oracle.linear_combination(y, 2.0, -1.0, c)
+    l2 = oracle.linear_combination(y, -0.5, 4.0, c)
+    assert np.array_equal(l1 + l2, oracle.linear_combination(y, 1.5, 3.0, c))
+    assert np.array_equal(oracle.linear_combination(y, 2.0, 0.0, c), 2.0 * y)
+    # ReLU after the sum: where beta*C turns the sign, the result follows the sum
+    v = oracle.linear_combination(y, 1.0, -1.0, c, relu=True)
+    assert np.array_equal(v > 0, (y - c) > 0)
+    assert not np.any(np.signbit(v))
+    # dgrad / wgrad results take the same epilogue elementwise
+    dx = oracle.dgrad(prob, dy, w)
+    cx = ints(rng, dx.shape)
+    assert np.array_equal(oracle.linear_combination(dx, 1.0, 1.0, cx) - cx, dx)
+
+
 # ------------------------------------------------------------ adjoint pins
 
 ADJ_PROBLEMS = [
