@@ -208,6 +208,23 @@ int choose_direct_tiled_splits(long long wgs_per_slice, long long npix)
 int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, const Epi &ep,
               Plan *pl);
 
+// Work units of the depthwise wgrad kernel: strips of cols output columns of
+// one output row.
+static long long depthwise_units(const Dims &d)
+{
+    const int cols = direct_depthwise_wgrad_cols((int)d.N, (int)d.H, (int)d.W, (int)d.C, (int)d.P, (int)d.Q, (int)d.R, (int)d.S,
+                                               (int)d.sw, (int)d.dw);
+    return d.N * d.P * ((d.Q + cols - 1) / cols);
+}
+
+// depthwise wgrad: at most two workgroups per CU, at least 64 pixels per slice
+int choose_direct_depthwise_splits(const Dims &d)
+{
+    const int cols = direct_depthwise_wgrad_cols((int)d.N, (int)d.H, (int)d.W, (int)d.C, (int)d.P, (int)d.Q, (int)d.R, (int)d.S,
+                                               (int)d.sw, (int)d.dw);
+    return (int)std::max(1LL, std::min(2LL * kNumCUs, depthwise_units(d) * cols / 64));
+}
+
 // Plan of a groups == 1 problem whose C or K is not a multiple of vec: the
 // inner problem has both rounded up to vec; the workspace holds the inner
 // pass's own workspace, then the padded copies the pass needs.
@@ -280,28 +297,34 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     if (d.G == 1 && (d.C % vec || d.K % vec)) return plan_padded(op, prob, dtype, algo, ep, vec, pl);
 
     if (d.G > 1) {
-        // tile 0: one thread per output; tile 1: LDS-tiled dot-product kernel
-        // (16-bit types, channel counts in 16-byte vectors, staging fits LDS)
+        // tile 0: one thread per output; tile 1: the depthwise kernels
+        // (groups = C = K) or the LDS-tiled dot-product kernels (16-bit
+        // types, channel counts in 16-byte vectors, staging fits LDS)
         pl->kernel = 2;
-        const bool tiled = op == CONV2D_OP_WGRAD
-                               ? direct_wgrad_tiled_ok(dtype, (int)d.Cg, (int)d.Kg)
-                               : direct_tiled_rows(op == CONV2D_OP_DGRAD, dtype, (int)d.R, (int)d.S, (int)d.W,
-                                                   (int)d.Q, (int)d.Cg, (int)d.Kg) > 0;
+        const bool dwise = direct_depthwise_ok(dtype, (int)d.C, (int)d.Cg, (int)d.Kg, (int)d.R, (int)d.S);
+        const bool tiled = dwise || (op == CONV2D_OP_WGRAD
+                                         ? direct_wgrad_tiled_ok(dtype, (int)d.Cg, (int)d.Kg)
+                                         : direct_tiled_rows(op == CONV2D_OP_DGRAD, dtype, (int)d.R, (int)d.S,
+                                                             (int)d.W, (int)d.Q, (int)d.Cg, (int)d.Kg) > 0);
         pl->num_tiles = tiled ? 2 : 1;
         if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
         pl->tile = (algo && algo->tile) ? algo->tile - 1 : pl->num_tiles - 1;
         if (op == CONV2D_OP_WGRAD) {
             const long long outputs = d.K * d.R * d.S * d.Cg;
             const long long npix = d.N * d.P * d.Q;
-            const long long wgs = pl->tile ? direct_wgrad_tiled_wgs((int)d.R, (int)d.S, (int)d.Cg, (int)d.Kg,
-                                                                    (int)d.G)
-                                           : 0;
+            const bool dwk = pl->tile == 1 && dwise;  // one workgroup per pixel slice, always partials
+            const long long wgs = dwk        ? 1
+                                  : pl->tile ? direct_wgrad_tiled_wgs((int)d.R, (int)d.S, (int)d.Cg, (int)d.Kg,
+                                                                      (int)d.G)
+                                             : 0;
             int s = (algo && algo->split_k) ? algo->split_k
+                    : dwk                   ? choose_direct_depthwise_splits(d)
                     : pl->tile              ? choose_direct_tiled_splits(wgs, npix)
                                             : choose_direct_splits(outputs, npix);
             if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
             pl->split_k = s;
-            if (s > 1 || wparts) pl->ws_bytes = round_up((size_t)s * splitk_stride(outputs) * sizeof(float), 256);
+            if (s > 1 || wparts || dwk)
+                pl->ws_bytes = round_up((size_t)s * splitk_stride(outputs) * sizeof(float), 256);
         }
         return CONV2D_OK;
     }
@@ -528,7 +551,9 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         a.relu = relu; a.requant_m = m; a.splits = 1;
         a.axpby = ep.axpby; a.alpha = ep.alpha; a.beta = ep.beta; a.cmat = ep.c;
         a.total = d.N * d.P * d.Q * d.K;
-        if (pl.tile == 1) {
+        if (pl.tile == 1 && direct_depthwise_ok(dtype, a.C, a.Cg, a.Kg, a.R, a.S)) {
+            a.depthwise = 1;
+        } else if (pl.tile == 1) {
             a.tiled = 1;
             a.rows = direct_tiled_rows(0, dtype, a.R, a.S, a.W, a.Q, a.Cg, a.Kg);
         }
@@ -611,7 +636,9 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
         a.splits = 1;
         a.axpby = ep.axpby; a.alpha = ep.alpha; a.beta = ep.beta; a.cmat = ep.c;
         a.total = d.N * d.H * d.W * d.C;
-        if (pl.tile == 1) {
+        if (pl.tile == 1 && direct_depthwise_ok(dtype, a.C, a.Cg, a.Kg, a.R, a.S)) {
+            a.depthwise = 1;
+        } else if (pl.tile == 1) {
             a.tiled = 1;
             a.rows = direct_tiled_rows(1, dtype, a.R, a.S, a.W, a.Q, a.Cg, a.Kg);
         }
@@ -730,10 +757,19 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         a.pix_per_split = (npix + pl.split_k - 1) / pl.split_k;
         a.total = d.K * d.R * d.S * d.Cg;
         a.part_stride = splitk_stride(a.total);
-        a.tiled = pl.tile == 1;
-        a.to_parts = to_parts;
+        a.depthwise = pl.tile == 1 && direct_depthwise_ok(dtype, a.C, a.Cg, a.Kg, a.R, a.S);
+        a.tiled = pl.tile == 1 && !a.depthwise;
+        a.to_parts = to_parts || a.depthwise;
+        if (a.depthwise) {
+            a.out = workspace;  // the depthwise kernel always writes partials
+            const int cols = direct_depthwise_wgrad_cols(a.N, a.H, a.W, a.C, a.P, a.Q, a.R, a.S, a.sw, a.dw);
+            a.npix = (uint32_t)depthwise_units(d);
+            a.pix_per_split = (a.npix + pl.split_k - 1) / pl.split_k;
+            a.div_q = make_fastdiv((uint32_t)((a.Q + cols - 1) / cols));
+            a.div_p = make_fastdiv((uint32_t)a.P);
+        }
         hipError_t e = launch_direct_wgrad(dtype, a, s);
-        if (e != hipSuccess || !reduce) return hip_status(e);
+        if (e != hipSuccess || !(reduce || a.depthwise)) return hip_status(e);
         return hip_status(
             launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k, a.total, a.part_stride, dw, &re, s));
     }

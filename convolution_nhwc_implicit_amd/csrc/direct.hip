@@ -414,6 +414,485 @@ __global__ __launch_bounds__(256) void direct_wgrad_tiled(const DirectArgs a)
     }
 }
 
+// ---------------------------------------------------------- depthwise ----
+// groups = C = K (one channel per group): per-channel 2-D filters, no
+// reduction over channels.  A thread owns 8 channels (one 16-byte vector of
+// the NHWC pixel) of DWT consecutive output columns and accumulates their
+// taps in fp32, (r, s) in order.  Neighbouring threads take neighbouring
+// channel vectors, so every load of a wave is whole 16-byte pieces of
+// consecutive pixels; the re-reads of the 3x3 neighbourhood hit the caches.
+constexpr int DWT = 4;
+constexpr int DW_MAX_TAPS = 9;  // wgrad keeps one fp32 sum per tap and channel
+constexpr int DWW = 4;          // output columns per work unit of the wgrad row kernel
+
+// The row kernels: unit column stride and dilation, R and S up to 3, and
+// the tensors they read through buffer offsets under 1 GB.
+static bool rows_ok(int R, int S, int sw, int dw, long long in_bytes, long long in2_bytes)
+{
+    return R <= 3 && S <= 3 && sw == 1 && dw == 1 && in_bytes < (1LL << 30) && in2_bytes < (1LL << 30);
+}
+
+template <class E>
+__device__ inline void unpack8(u32x4 v, float *f)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = E::to_f32((typename E::elem)(w[j >> 1] >> (16 * (j & 1))));
+}
+
+// Bias of the thread's 8 channels (zeros without bias), loaded once.
+template <class E>
+__device__ inline void load_bias8(const DirectArgs &a, int c0, float *b8)
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b8[j] = a.bias ? ld_f<E>((const typename E::elem *)a.bias + c0 + j) : 0.0f;
+}
+
+// out[o .. o+7] = epilogue(v): alpha/beta with C, then bias and ReLU when b8
+// is given (fprop).
+template <class E>
+__device__ inline void store8(const DirectArgs &a, typename E::elem *dst, size_t o, const float *v,
+                              const float *b8)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2) {
+        uint32_t h[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int j = 2 * j2 + e;
+            float t = axpby_at<E>(a, v[j], o + j);
+            if (b8) t = bias_relu_f32(t, b8[j], a.relu);
+            h[e] = E::from_f32(t);
+        }
+        w[j2] = h[0] | (h[1] << 16);
+    }
+    *(u32x4 *)(dst + o) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// The filter [C][R][S] is C*R*S contiguous elements, a whole number of
+// 16-byte chunks.  It is staged per workgroup in LDS as [R*S][C] fp32 (taps
+// reversed when flip), so a thread reads its 8 channels' weight of a tap as
+// two 16-byte LDS reads.  The caller loads chunk threadIdx.x (filter_chunk)
+// before its own input loads, so the two share one trip to memory.
+template <class E>
+__device__ inline u32x4 filter_chunk(const DirectArgs &a, int i)
+{
+    return i < a.C * a.R * a.S / 8 ? *(const u32x4 *)((const typename E::elem *)a.b + (size_t)i * 8)
+                                   : u32x4{0, 0, 0, 0};
+}
+
+template <class E>
+__device__ inline void stage_filter(const DirectArgs &a, float *wsh, bool flip, u32x4 first)
+{
+    const int RS = a.R * a.S, nch = a.C * RS / 8;
+    for (int i = threadIdx.x; i < nch; i += 256) {
+        float f[8];
+        unpack8<E>(i == (int)threadIdx.x ? first : filter_chunk<E>(a, i), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int fl = i * 8 + e, c = fl / RS, k = fl - c * RS;
+            wsh[(flip ? RS - 1 - k : k) * a.C + c] = f[e];
+        }
+    }
+}
+
+__device__ inline void filter8(const float *wsh, int k, int C, int c0, float *wv)
+{
+    const f32x4 lo = *(const f32x4 *)(wsh + k * C + c0), hi = *(const f32x4 *)(wsh + k * C + c0 + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        wv[j] = lo[j];
+        wv[4 + j] = hi[j];
+    }
+}
+
+// Geometry of the row kernel: an input of ih x iw pixels, an output of oh x ow
+// pixels; output row p reads input rows p*sh - ph + r*dh, output column q reads
+// input columns q - pw + s (unit column stride and dilation).  The thread
+// index t < nthr is (row n*oh + p, column strip qt, channel vector c8),
+// c8 fastest; in_bytes is the input's size (under 2 GB).
+struct DwGeom {
+    int ih, iw, oh, ow, sh, dh, ph, pw;
+    uint32_t nthr, in_bytes;
+    FastDiv div_c8, div_qt, div_oh;
+};
+
+// Row kernel, R <= 3 and S <= 3 with unit column stride and dilation.  (R and
+// S stay run-time values: fixing them at compile time lets the compiler widen
+// every row's pixels to fp32 at once, which costs occupancy and time.)  A
+// thread's DWT outputs read
+// DWT + S - 1 input pixels of each of R input rows; they are all loaded, as
+// buffer loads whose out-of-range offsets read zeros (the padding), before
+// the filter and bias are staged, so the kernel makes one trip to memory;
+// every tap then reuses them from registers.  fprop: in = x, filter as
+// stored, bias and ReLU.  dgrad at stride 1 (FLIP): in = dy, the filter
+// reversed in r and s, pads (R-1)*dh - pad_h and (S-1) - pad_w, no bias.
+template <class E, bool FLIP>
+__global__ __launch_bounds__(256) void depthwise_rows(const DirectArgs a, const DwGeom g)
+{
+    using elem = typename E::elem;
+    extern __shared__ __attribute__((aligned(16))) float wsh[];  // [R*S][C] filter, then [C] bias
+    const int R = a.R, S = a.S;
+    const uint32_t C8 = (uint32_t)a.C / 8, QT = (uint32_t)(g.ow + DWT - 1) / DWT;
+    uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    const bool live = t < g.nthr;
+    if (!live) t = 0;
+    const uint32_t rest = fdiv(t, g.div_c8), c8 = t - rest * C8;
+    const uint32_t prow = fdiv(rest, g.div_qt), qt = rest - prow * QT;
+    const uint32_t n = fdiv(prow, g.div_oh), p = prow - n * (uint32_t)g.oh;
+    const int c0 = (int)c8 * 8, w0 = (int)qt * DWT - g.pw;
+    const uint32_t pixb = (uint32_t)a.C * 2;
+    // filter chunk and bias first: staging them waits for these loads only
+    const u32x4 fch = filter_chunk<E>(a, threadIdx.x);
+    const bool has_bias = !FLIP && a.bias;
+    const float bias0 = has_bias && (int)threadIdx.x < a.C ? ld_f<E>((const elem *)a.bias + threadIdx.x) : 0.0f;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.a, (short)0, (int)g.in_bytes, 0x00020000);
+    u32x4 raw[3][DWT + 2];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const int h = (int)p * g.sh - g.ph + r * g.dh;
+        const bool rok = live && r < R && (unsigned)h < (unsigned)g.ih;
+        const uint32_t base = rok ? ((n * (uint32_t)g.ih + (uint32_t)h) * (uint32_t)g.iw) * pixb + (uint32_t)c0 * 2 : kBufOOB;
+#pragma unroll
+        for (int u = 0; u < DWT + 2; ++u) {
+            const int wc = w0 + u;
+            const uint32_t off = (unsigned)wc < (unsigned)g.iw && u < DWT + S - 1 ? base + (uint32_t)wc * pixb : kBufOOB;
+            raw[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+        }
+    }
+    stage_filter<E>(a, wsh, FLIP, fch);
+    float *bsh = wsh + R * S * a.C;
+    if (has_bias) {
+        for (int i = threadIdx.x; i < a.C; i += 256)
+            bsh[i] = i == (int)threadIdx.x ? bias0 : ld_f<E>((const elem *)a.bias + i);
+    }
+    __syncthreads();
+    if (!live) return;
+    float acc[DWT][8];
+#pragma unroll
+    for (int i = 0; i < DWT; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        if (r >= R) break;
+        float xf[DWT + 2][8];
+#pragma unroll
+        for (int u = 0; u < DWT + 2; ++u) unpack8<E>(raw[r][u], xf[u]);
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            if (s >= S) break;
+            float wv[8];
+            filter8(wsh, r * S + s, a.C, c0, wv);
+#pragma unroll
+            for (int i = 0; i < DWT; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] += xf[i + s][j] * wv[j];
+        }
+    }
+    float b8[8];
+    if (has_bias) {
+        const f32x4 lo = *(const f32x4 *)(bsh + c0), hi = *(const f32x4 *)(bsh + c0 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b8[j] = lo[j];
+            b8[4 + j] = hi[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b8[j] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < DWT; ++i) {
+        const int q = (int)qt * DWT + i;
+        if (q < g.ow)
+            store8<E>(a, (elem *)a.out, (((size_t)n * g.oh + p) * g.ow + q) * a.C + c0, acc[i],
+                      FLIP ? nullptr : b8);
+    }
+}
+
+// General fprop (any column stride or dilation, up to 9 taps): per tap, the
+// thread's DWT output columns each load their input pixel.
+template <class E>
+__global__ __launch_bounds__(256) void depthwise_fprop(const DirectArgs a)
+{
+    using elem = typename E::elem;
+    extern __shared__ __attribute__((aligned(16))) float wsh[];  // [R*S][C]
+    const int C8 = a.C / 8, QT = (a.Q + DWT - 1) / DWT;
+    stage_filter<E>(a, wsh, false, filter_chunk<E>(a, threadIdx.x));
+    __syncthreads();
+    long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (long long)a.N * a.P * QT * C8) return;
+    const int c8 = (int)(t % C8);
+    t /= C8;
+    const int qt = (int)(t % QT);
+    t /= QT;
+    const int p = (int)(t % a.P), n = (int)(t / a.P);
+    const int c0 = c8 * 8;
+    const elem *x = (const elem *)a.a;
+    float acc[DWT][8];
+#pragma unroll
+    for (int i = 0; i < DWT; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    for (int r = 0; r < a.R; ++r) {
+        const int h = p * a.sh - a.pad_h + r * a.dh;
+        if ((unsigned)h >= (unsigned)a.H) continue;
+        const elem *xrow = x + ((size_t)n * a.H + h) * a.W * a.C + c0;
+        for (int s = 0; s < a.S; ++s) {
+            float wv[8];
+            filter8(wsh, r * a.S + s, a.C, c0, wv);
+#pragma unroll
+            for (int i = 0; i < DWT; ++i) {
+                const int q = qt * DWT + i;
+                const int wc = q * a.sw - a.pad_w + s * a.dw;
+                if (q >= a.Q || (unsigned)wc >= (unsigned)a.W) continue;
+                float xf[8];
+                unpack8<E>(*(const u32x4 *)(xrow + (size_t)wc * a.C), xf);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] += xf[j] * wv[j];
+            }
+        }
+    }
+    float b8[8];
+    load_bias8<E>(a, c0, b8);
+#pragma unroll
+    for (int i = 0; i < DWT; ++i) {
+        const int q = qt * DWT + i;
+        if (q < a.Q) store8<E>(a, (elem *)a.out, (((size_t)n * a.P + p) * a.Q + q) * a.C + c0, acc[i], b8);
+    }
+}
+
+template <class E>
+__global__ __launch_bounds__(256) void depthwise_dgrad(const DirectArgs a)
+{
+    using elem = typename E::elem;
+    extern __shared__ __attribute__((aligned(16))) float wsh[];  // [R*S][C]
+    const int C8 = a.C / 8, WT = (a.W + DWT - 1) / DWT;
+    stage_filter<E>(a, wsh, false, filter_chunk<E>(a, threadIdx.x));
+    __syncthreads();
+    long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (long long)a.N * a.H * WT * C8) return;
+    const int c8 = (int)(t % C8);
+    t /= C8;
+    const int wt = (int)(t % WT);
+    t /= WT;
+    const int h = (int)(t % a.H), n = (int)(t / a.H);
+    const int c0 = c8 * 8;
+    const elem *dy = (const elem *)a.a;
+    float acc[DWT][8];
+#pragma unroll
+    for (int i = 0; i < DWT; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    for (int r = 0; r < a.R; ++r) {
+        const int th = h + a.pad_h - r * a.dh;
+        if (th < 0 || th % a.sh) continue;
+        const int p = th / a.sh;
+        if (p >= a.P) continue;
+        const elem *drow = dy + ((size_t)n * a.P + p) * a.Q * a.C + c0;
+        for (int s = 0; s < a.S; ++s) {
+            float wv[8];
+            filter8(wsh, r * a.S + s, a.C, c0, wv);
+#pragma unroll
+            for (int i = 0; i < DWT; ++i) {
+                const int wc = wt * DWT + i;
+                const int tw = wc + a.pad_w - s * a.dw;
+                if (wc >= a.W || tw < 0 || tw % a.sw) continue;
+                const int q = tw / a.sw;
+                if (q >= a.Q) continue;
+                float df[8];
+                unpack8<E>(*(const u32x4 *)(drow + (size_t)q * a.C), df);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] += df[j] * wv[j];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < DWT; ++i) {
+        const int wc = wt * DWT + i;
+        if (wc < a.W)
+            store8<E>(a, (elem *)a.out, (((size_t)n * a.H + h) * a.W + wc) * a.C + c0, acc[i], nullptr);
+    }
+}
+
+// wgrad: dw[c,r,s] = sum over output pixels of dy[pix,c] * x[tap pixel,c].
+// Workgroup z takes pixels [z*pix_per_split, ...); its threads are (channel
+// vector c8, pixel lane pl): lane pl sums pixels pl, pl + npl, ... of the
+// slice, then the lanes' sums are added in lane order through LDS and the
+// workgroup writes one fp32 partial per (c, r, s).
+template <class E>
+__global__ __launch_bounds__(256) void depthwise_wgrad(const DirectArgs a)
+{
+    using elem = typename E::elem;
+    __shared__ float red[256][8];
+    const int C8 = a.C / 8, npl = 256 / C8, RS = a.R * a.S;
+    const int tid = threadIdx.x, c8 = tid % C8, pl = tid / C8;
+    const bool live = pl < npl;
+    const int c0 = c8 * 8;
+    const elem *x = (const elem *)a.a + c0;
+    const elem *dy = (const elem *)a.b + c0;
+    const uint32_t pbeg = (uint32_t)blockIdx.x * a.pix_per_split;
+    uint32_t pend = pbeg + a.pix_per_split;
+    if (pend > a.npix || pend < pbeg) pend = a.npix;
+    float acc[DW_MAX_TAPS][8];
+#pragma unroll
+    for (int k = 0; k < DW_MAX_TAPS; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[k][j] = 0.0f;
+    if (live) {
+        for (uint32_t pix = pbeg + pl; pix < pend; pix += npl) {
+            const uint32_t rest = fdiv(pix, a.div_q), q = pix - rest * (uint32_t)a.Q;
+            const uint32_t n = fdiv(rest, a.div_p), p = rest - n * (uint32_t)a.P;
+            float df[8];
+            unpack8<E>(*(const u32x4 *)(dy + (size_t)pix * a.C), df);
+#pragma unroll
+            for (int k = 0; k < DW_MAX_TAPS; ++k) {
+                const int r = k / a.S, s = k - r * a.S;
+                const int h = (int)p * a.sh - a.pad_h + r * a.dh;
+                const int wc = (int)q * a.sw - a.pad_w + s * a.dw;
+                if (k < RS && (unsigned)h < (unsigned)a.H && (unsigned)wc < (unsigned)a.W) {
+                    float xf[8];
+                    unpack8<E>(*(const u32x4 *)(x + (((size_t)n * a.H + h) * a.W + wc) * a.C), xf);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[k][j] += df[j] * xf[j];
+                }
+            }
+        }
+    }
+    float *part = (float *)a.out + (size_t)blockIdx.x * a.part_stride;
+#pragma unroll
+    for (int k = 0; k < DW_MAX_TAPS; ++k) {
+        if (k >= RS) continue;  // uniform
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[tid][j] = acc[k][j];
+        __syncthreads();
+        if (pl == 0) {
+            float sum[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sum[j] = 0.0f;
+            for (int l = 0; l < npl; ++l)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sum[j] += red[l * C8 + c8][j];
+            const int r = k / a.S, s = k - r * a.S;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part[((size_t)(c0 + j) * a.R + r) * a.S + s] = sum[j];
+        }
+        __syncthreads();
+    }
+}
+
+// wgrad, R <= 3 and S <= 3 with unit column stride and dilation: a work unit
+// is a strip of DWW output columns of one output row.  The thread loads the
+// strip's dy pixels and the DWW + S - 1 input pixels of each of its R input
+// rows, then adds dy[q] * x[q - pad_w + s] over the strip into its fp32 sum
+// of every tap.  Workgroup z takes units [z*units_per_split, ...), thread
+// lane sl the units sl, sl + nsl, ... of them; the lanes' sums are added in
+// lane order through LDS and the workgroup writes one fp32 partial per
+// (c, r, s).
+template <class E, int T>
+__global__ __launch_bounds__(256) void depthwise_wgrad_rows(const DirectArgs a)
+{
+    using elem = typename E::elem;
+    __shared__ float red[256][8];
+    const int C8 = a.C / 8, nsl = 256 / C8, RS = a.R * a.S;
+    const int tid = threadIdx.x, c8 = tid % C8, sl = tid / C8;
+    const int c0 = c8 * 8;
+    const elem *x = (const elem *)a.a + c0;
+    const elem *dy = (const elem *)a.b + c0;
+    const uint32_t beg = (uint32_t)blockIdx.x * a.pix_per_split;
+    uint32_t end = beg + a.pix_per_split;
+    if (end > a.npix || end < beg) end = a.npix;
+    const uint32_t QT = (uint32_t)(a.Q + T - 1) / T, pixb = (uint32_t)a.C * 2;
+    // x and dy as buffers (each under 1 GB): out-of-range offsets read zeros
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x - c0), (short)0, (int)((uint32_t)a.N * a.H * a.W * pixb), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ds = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(dy - c0), (short)0, (int)((uint32_t)a.N * a.P * a.Q * pixb), 0x00020000);
+    float acc[3][3][8];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[r][s][j] = 0.0f;
+    if (sl < nsl) {
+        for (uint32_t u = beg + sl; u < end; u += nsl) {
+            const uint32_t rest = fdiv(u, a.div_q), qt = u - rest * QT;
+            const uint32_t n = fdiv(rest, a.div_p), p = rest - n * (uint32_t)a.P;
+            const int q0 = (int)qt * T, w0 = q0 - a.pad_w;
+            const uint32_t dbase = ((n * (uint32_t)a.P + p) * (uint32_t)a.Q + (uint32_t)q0) * pixb + (uint32_t)c0 * 2;
+            u32x4 draw[T];
+#pragma unroll
+            for (int i = 0; i < T; ++i)
+                draw[i] = __builtin_amdgcn_raw_buffer_load_b128(ds, q0 + i < a.Q ? dbase + i * pixb : kBufOOB, 0, 0);
+            u32x4 xraw[3][T + 2];
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const int h = (int)p * a.sh - a.pad_h + r * a.dh;
+                const bool rok = r < a.R && (unsigned)h < (unsigned)a.H;
+                const uint32_t base = rok ? (n * (uint32_t)a.H + (uint32_t)h) * (uint32_t)a.W * pixb + (uint32_t)c0 * 2
+                                          : kBufOOB;
+#pragma unroll
+                for (int v = 0; v < T + 2; ++v) {
+                    const int wc = w0 + v;
+                    const uint32_t off =
+                        v < T + a.S - 1 && (unsigned)wc < (unsigned)a.W ? base + (uint32_t)wc * pixb : kBufOOB;
+                    xraw[r][v] = __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0);
+                }
+            }
+            float df[T][8];
+#pragma unroll
+            for (int i = 0; i < T; ++i) unpack8<E>(draw[i], df[i]);
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                if (r >= a.R) break;
+                float xf[T + 2][8];
+#pragma unroll
+                for (int v = 0; v < T + 2; ++v) unpack8<E>(xraw[r][v], xf[v]);
+#pragma unroll
+                for (int s = 0; s < 3; ++s) {
+                    if (s >= a.S) break;
+#pragma unroll
+                    for (int i = 0; i < T; ++i)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[r][s][j] += df[i][j] * xf[i + s][j];
+                }
+            }
+        }
+    }
+    float *part = (float *)a.out + (size_t)blockIdx.x * a.part_stride;
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            if (r >= a.R || s >= a.S) continue;  // uniform
+#pragma unroll
+            for (int j = 0; j < 8; ++j) red[tid][j] = acc[r][s][j];
+            __syncthreads();
+            for (int o = tid; o < C8 * 8; o += 256) {
+                const int oc8 = o >> 3, j = o & 7;
+                float sum = 0.0f;
+                for (int l = 0; l < nsl; ++l) sum += red[l * C8 + oc8][j];
+                part[(size_t)o * RS + r * a.S + s] = sum;
+            }
+            __syncthreads();
+        }
+}
+
+int direct_depthwise_wgrad_cols(int N, int H, int W, int C, int P, int Q, int R, int S, int sw, int dw)
+{
+    const long long xb = (long long)N * H * W * C * 2, dyb = (long long)N * P * Q * C * 2;
+    return rows_ok(R, S, sw, dw, xb, dyb) ? DWW : 1;
+}
+
+bool direct_depthwise_ok(int dtype, int C, int Cg, int Kg, int R, int S)
+{
+    return (dtype == CONV2D_DTYPE_F16 || dtype == CONV2D_DTYPE_BF16) && Cg == 1 && Kg == 1 && C % 8 == 0 &&
+           C / 8 <= 256 && R * S <= DW_MAX_TAPS && (size_t)R * S * C * sizeof(float) <= 64 * 1024;
+}
+
 int direct_tiled_rows(int op, int dtype, int R, int S, int W, int Q, int Cg, int Kg)
 {
     if (dtype != CONV2D_DTYPE_F16 && dtype != CONV2D_DTYPE_BF16) return 0;
@@ -444,9 +923,47 @@ long long direct_wgrad_tiled_wgs(int R, int S, int Cg, int Kg, int G)
 
 static unsigned blocks_for(long long total) { return (unsigned)((total + 255) / 256); }
 
+static DwGeom dw_geom(const DirectArgs &a, int ih, int iw, int oh, int ow, int sh, int dh, int ph, int pw,
+                      long long thr, long long in_bytes)
+{
+    DwGeom g{ih, iw, oh, ow, sh, dh, ph, pw, (uint32_t)thr, (uint32_t)in_bytes, {}, {}, {}};
+    g.div_c8 = make_fastdiv((uint32_t)(a.C / 8));
+    g.div_qt = make_fastdiv((uint32_t)((ow + DWT - 1) / DWT));
+    g.div_oh = make_fastdiv((uint32_t)oh);
+    return g;
+}
+
+template <bool FLIP>
+static hipError_t launch_rows(int dtype, const DirectArgs &a, const DwGeom &g, hipStream_t st)
+{
+    const size_t lds = ((size_t)a.R * a.S * a.C + a.C) * sizeof(float);
+    const unsigned blocks = (unsigned)((g.nthr + 255) / 256);
+    switch (dtype) {
+    case CONV2D_DTYPE_F16: depthwise_rows<EF16, FLIP><<<blocks, 256, lds, st>>>(a, g); break;
+    case CONV2D_DTYPE_BF16: depthwise_rows<EBF16, FLIP><<<blocks, 256, lds, st>>>(a, g); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_direct_fprop(int dtype, const DirectArgs &a, hipStream_t st)
 {
     if (a.total == 0) return hipSuccess;
+    if (a.depthwise) {
+        const long long thr = (long long)a.N * a.P * ((a.Q + DWT - 1) / DWT) * (a.C / 8);
+        const long long in_bytes = (long long)a.N * a.H * a.W * a.C * 2;
+        if (rows_ok(a.R, a.S, a.sw, a.dw, in_bytes, 0) && thr < (1LL << 31)) {
+            const DwGeom g = dw_geom(a, a.H, a.W, a.P, a.Q, a.sh, a.dh, a.pad_h, a.pad_w, thr, in_bytes);
+            return launch_rows<false>(dtype, a, g, st);
+        }
+        const size_t lds = (size_t)a.R * a.S * a.C * sizeof(float);
+        switch (dtype) {
+        case CONV2D_DTYPE_F16: depthwise_fprop<EF16><<<blocks_for(thr), 256, lds, st>>>(a); break;
+        case CONV2D_DTYPE_BF16: depthwise_fprop<EBF16><<<blocks_for(thr), 256, lds, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     if (a.tiled) {
         const size_t lds = ((size_t)a.Kg * a.R * a.S * a.Cg + (size_t)a.rows * a.R * a.W * a.Cg) * 2;
         dim3 grid((unsigned)(a.N * ((a.P + a.rows - 1) / a.rows)), (unsigned)a.G);
@@ -469,6 +986,23 @@ hipError_t launch_direct_fprop(int dtype, const DirectArgs &a, hipStream_t st)
 hipError_t launch_direct_dgrad(int dtype, const DirectArgs &a, hipStream_t st)
 {
     if (a.total == 0) return hipSuccess;
+    if (a.depthwise) {
+        const long long thr = (long long)a.N * a.H * ((a.W + DWT - 1) / DWT) * (a.C / 8);
+        const long long in_bytes = (long long)a.N * a.P * a.Q * a.C * 2;
+        if (a.sh == 1 && rows_ok(a.R, a.S, a.sw, a.dw, in_bytes, 0) && thr < (1LL << 31)) {
+            // stride 1: the fprop row kernel over dy with the filter reversed
+            const DwGeom g = dw_geom(a, a.P, a.Q, a.H, a.W, 1, a.dh, (a.R - 1) * a.dh - a.pad_h,
+                                     (a.S - 1) - a.pad_w, thr, in_bytes);
+            return launch_rows<true>(dtype, a, g, st);
+        }
+        const size_t lds = (size_t)a.R * a.S * a.C * sizeof(float);
+        switch (dtype) {
+        case CONV2D_DTYPE_F16: depthwise_dgrad<EF16><<<blocks_for(thr), 256, lds, st>>>(a); break;
+        case CONV2D_DTYPE_BF16: depthwise_dgrad<EBF16><<<blocks_for(thr), 256, lds, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     if (a.tiled) {
         const size_t lds = ((size_t)a.R * a.S * a.Cg * a.Kg + (size_t)a.rows * a.R * a.Q * a.Kg) * 2;
         dim3 grid((unsigned)(a.N * ((a.H + a.rows - 1) / a.rows)), (unsigned)a.G);
@@ -490,6 +1024,25 @@ hipError_t launch_direct_dgrad(int dtype, const DirectArgs &a, hipStream_t st)
 hipError_t launch_direct_wgrad(int dtype, const DirectArgs &a, hipStream_t st)
 {
     if (a.total == 0) return hipSuccess;
+    if (a.depthwise) {  // always fp32 partials, one per workgroup (grid = splits)
+        const bool rows = direct_depthwise_wgrad_cols(a.N, a.H, a.W, a.C, a.P, a.Q, a.R, a.S, a.sw, a.dw) > 1;
+        switch (dtype) {
+        case CONV2D_DTYPE_F16:
+            if (rows)
+                depthwise_wgrad_rows<EF16, DWW><<<(unsigned)a.splits, 256, 0, st>>>(a);
+            else
+                depthwise_wgrad<EF16><<<(unsigned)a.splits, 256, 0, st>>>(a);
+            break;
+        case CONV2D_DTYPE_BF16:
+            if (rows)
+                depthwise_wgrad_rows<EBF16, DWW><<<(unsigned)a.splits, 256, 0, st>>>(a);
+            else
+                depthwise_wgrad<EBF16><<<(unsigned)a.splits, 256, 0, st>>>(a);
+            break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     if (a.tiled) {
         const long long per_g = (long long)(a.Kg / 4) * a.R * a.S * (a.Cg / 8);
         dim3 grid(blocks_for(per_g), (unsigned)a.G, (unsigned)a.splits);

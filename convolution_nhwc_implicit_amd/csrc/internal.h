@@ -217,8 +217,8 @@ struct DirectArgs {
     double requant_m;
     int splits;
     long long part_stride;  // wgrad: elements between slices' partials
-    uint32_t npix;          // wgrad: N*P*Q
-    uint32_t pix_per_split; // wgrad
+    uint32_t npix;          // wgrad: N*P*Q (depthwise: work units, direct_depthwise_wgrad_cols)
+    uint32_t pix_per_split; // wgrad: pixels (depthwise: work units) per slice
     long long total;        // output elements (per split for wgrad)
     int tiled;              // use the LDS-tiled kernel (direct_tiled_rows / direct_wgrad_tiled_ok)
     int rows;               // fprop / dgrad tiled: output rows per workgroup
@@ -228,11 +228,16 @@ struct DirectArgs {
     float alpha, beta;
     const void *cmat;
     int to_parts;
+    int depthwise;          // groups = C = K: the depthwise kernels (direct_depthwise_ok)
+    FastDiv div_q, div_p;   // depthwise wgrad: work units per output row, and P
 };
 // Output rows per workgroup of the LDS-tiled direct fprop (op 0) / dgrad
 // (op 1) kernel for 16-bit types, or 0 if it does not apply.
 int direct_tiled_rows(int op, int dtype, int R, int S, int W, int Q, int Cg, int Kg);
 bool direct_wgrad_tiled_ok(int dtype, int Cg, int Kg);
+bool direct_depthwise_ok(int dtype, int C, int Cg, int Kg, int R, int S);
+// Output columns per work unit of the depthwise wgrad kernel (1: one pixel).
+int direct_depthwise_wgrad_cols(int N, int H, int W, int C, int P, int Q, int R, int S, int sw, int dw);
 long long direct_wgrad_tiled_wgs(int R, int S, int Cg, int Kg, int G);  // workgroups per pixel slice
 hipError_t launch_direct_fprop(int dtype, const DirectArgs &a, hipStream_t st);
 hipError_t launch_direct_dgrad(int dtype, const DirectArgs &a, hipStream_t st);

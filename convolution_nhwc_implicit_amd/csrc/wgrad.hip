@@ -167,23 +167,25 @@ hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st)
 
 // ---------------------------------------------------------------------------
 // out[i] = round(sum over slices z of parts[z*stride + i]) in fp32, in a fixed
-// order: the slices are split into 16 classes z % 16; each class is summed in
-// ascending z, then the 16 class sums are added in ascending class order.
-// A workgroup owns 64 consecutive elements: thread (class c, lane e) reads
-// elements 4e..4e+3 of every slice of class c with 128-bit loads (16 lanes of
-// one slice read 256 contiguous bytes), and the class sums meet in LDS.
+// order: the slices are split into NCLS classes z % NCLS; each class is summed
+// in ascending z, then the class sums are added in ascending class order.
+// A workgroup owns 4*256/NCLS consecutive elements: thread (class c, lane e)
+// reads elements 4e..4e+3 of every slice of class c with 128-bit loads, and
+// the class sums meet in LDS.  NCLS is 16 (256 contiguous bytes of a slice
+// per class) unless there are few elements and many slices, where 64 classes
+// keep more loads in flight; the choice depends only on count and splits.
 // stride is a multiple of 4 and at least count; the last workgroup's lanes
 // past count read inside the slice padding and store nothing.
 // ---------------------------------------------------------------------------
-template <class E>
+template <class E, int NCLS>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *parts, int splits, long long count,
                                                             long long stride, void *out_, const ReduceEpi epi)
 {
     using elem = typename E::elem;
-    constexpr int NCLS = 16;
-    __shared__ f32x4 part[NCLS][16];
-    const int cls = threadIdx.x >> 4, e = threadIdx.x & 15;
-    const long long i = (long long)blockIdx.x * 64 + e * 4;
+    constexpr int NL = 256 / NCLS;  // lanes per class
+    __shared__ f32x4 part[NCLS][NL];
+    const int cls = threadIdx.x / NL, e = threadIdx.x % NL;
+    const long long i = (long long)blockIdx.x * (4 * NL) + e * 4;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     if (i < stride) {
         const float *p = parts + i;
@@ -253,12 +255,23 @@ hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long 
                                 long long stride, void *out, const ReduceEpi *epi, hipStream_t st)
 {
     if (stride % 4 || stride < count) return hipErrorInvalidValue;
-    const unsigned blocks = (unsigned)((count + 63) / 64);
-    if (blocks == 0) return hipSuccess;
+    if (count == 0) return hipSuccess;
     const ReduceEpi e = epi ? *epi : ReduceEpi{1.0f, 0.0f, nullptr, 0};
+    const bool wide = (count + 63) / 64 < 256 && splits >= 128;  // fewer workgroups than CUs
+    const unsigned blocks = (unsigned)(wide ? (count + 15) / 16 : (count + 63) / 64);
     switch (dtype) {
-    case CONV2D_DTYPE_F16: splitk_reduce_kernel<EF16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, out, e); break;
-    case CONV2D_DTYPE_BF16: splitk_reduce_kernel<EBF16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, out, e); break;
+    case CONV2D_DTYPE_F16:
+        if (wide)
+            splitk_reduce_kernel<EF16, 64><<<blocks, 256, 0, st>>>(parts, splits, count, stride, out, e);
+        else
+            splitk_reduce_kernel<EF16, 16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, out, e);
+        break;
+    case CONV2D_DTYPE_BF16:
+        if (wide)
+            splitk_reduce_kernel<EBF16, 64><<<blocks, 256, 0, st>>>(parts, splits, count, stride, out, e);
+        else
+            splitk_reduce_kernel<EBF16, 16><<<blocks, 256, 0, st>>>(parts, splits, count, stride, out, e);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

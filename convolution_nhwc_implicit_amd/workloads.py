@@ -16,11 +16,13 @@ Workloads (sizes and distributions follow the pages' own examples):
                  requantised with scales act 0.02, w 0.01, out 0.05
   n1_stem        fp16 Gaussian, 32x224x224x3 -> 64, 7x7 s2 p3, bias + ReLU (a
                  three-channel image stem, the small-C case; cfg 5)
+  d1_depthwise   fp16 Gaussian, 32x56x56x128 -> 128, 3x3 s1 p1, groups 128
+                 (depthwise), bias + ReLU (cfg 6)
 
 Integer-valued data is ceil(U(-4.5, 3.5)), the draw the CUTLASS notebook uses
 so that fp16 products and fp32 sums are exact.  Its values are -4..4.
 
-Seeds: numpy PCG64(1234 + 16*cfg + tensor_index), cfg = 0..4 for c1..c5 (5 for n1_stem),
+Seeds: numpy PCG64(1234 + 16*cfg + tensor_index), cfg = 0..4 for c1..c5 (5 for n1_stem, 6 for d1_depthwise),
 tensor_index x=0, w=1, bias=2, dy=3, and 4/5/6 for the filter, bias and dy of
 the variant that shares its input with the base config (c3b, c4g).
 
@@ -73,6 +75,10 @@ WORKLOADS = {
     "n1_stem": dict(
         prob=problem(32, 3, 224, 224, 64, 7, 7, pad=(3, 3), stride=(2, 2)),
         dtype="f16", dist="gauss", cfg=5, idx=dict(x=0, w=1, bias=2, dy=3),
+        bias=True, relu=True, check="tol"),
+    "d1_depthwise": dict(
+        prob=problem(32, 128, 56, 56, 128, 3, 3, pad=(1, 1), groups=128),
+        dtype="f16", dist="gauss", cfg=6, idx=dict(x=0, w=1, bias=2, dy=3),
         bias=True, relu=True, check="tol"),
 }
 

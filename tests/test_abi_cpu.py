@@ -76,7 +76,8 @@ def test_output_size_agrees_with_oracle():
 def test_workload_output_sizes():
     exp = {"c1_tiny": (8, 8), "c2_strided": (14, 14), "c3a_resnet3x3": (56, 56),
            "c3b_resnet1x1": (56, 56), "c4_awkward": (27, 27), "c4g_grouped": (27, 27),
-           "c5_int8": (56, 56), "n1_stem": (112, 112)}
+           "c5_int8": (56, 56), "n1_stem": (112, 112),
+           "d1_depthwise": (56, 56)}
     for name, wl in WORKLOADS.items():
         assert B.conv2d_output_size(wl["prob"]) == exp[name]
         assert oracle.output_hw(wl["prob"]) == exp[name]

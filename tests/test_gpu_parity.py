@@ -54,6 +54,24 @@ CASES = [
     ("grouped4_s2d2", problem(2, 16, 13, 13, 8, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2),
                               groups=4), "f16", "int", False, False),
     ("depthwise", problem(2, 8, 10, 9, 8, 3, 3, pad=(1, 1), groups=8), "f16", "int", True, False),
+    # depthwise kernels (groups = C = K, C % 8 == 0): strides and dilation,
+    # a ragged last column strip, 24 channels (three 8-channel vectors), 1x3
+    ("dw_s2d2", problem(2, 16, 13, 11, 16, 3, 3, pad=(2, 2), stride=(2, 2), dil=(2, 2), groups=16),
+     "f16", "int", True, True),
+    ("dw_bf16_gauss", problem(3, 32, 15, 17, 32, 3, 3, pad=(1, 1), groups=32), "bf16", "gauss", True, False),
+    ("dw_c24_1x3", problem(2, 24, 9, 14, 24, 1, 3, pad=(0, 1), stride=(1, 2), groups=24), "f16", "int",
+     False, False),
+    ("dw_5x5_fallback", problem(2, 8, 9, 9, 8, 5, 5, pad=(2, 2), groups=8), "f16", "int", True, False),
+    # depthwise row kernels (unit column stride and dilation, R, S <= 3):
+    # a 3x2 filter with row stride and dilation (dgrad takes the general
+    # kernel, stride 2), and a valid 3x3 with row dilation whose stride-1
+    # dgrad runs the row kernel with pads (R-1)*dh and S-1; ragged strips
+    ("dw_rows_3x2_s21", problem(3, 16, 14, 11, 16, 3, 2, pad=(0, 1), stride=(2, 1), dil=(2, 1), groups=16),
+     "f16", "int", True, True),
+    ("dw_rows_valid_d2", problem(2, 40, 12, 13, 40, 3, 3, pad=(0, 0), dil=(2, 1), groups=40),
+     "bf16", "int", False, False),
+    ("dw_rows_2x1_gauss", problem(2, 64, 7, 19, 64, 2, 1, pad=(1, 0), groups=64), "f16", "gauss",
+     True, False),
     ("grouped_gauss", problem(2, 24, 11, 11, 24, 3, 3, pad=(1, 1), groups=3), "bf16", "gauss",
      True, False),
     # grouped problems whose channel counts take the LDS-tiled direct kernels:
@@ -268,7 +286,7 @@ def _workload_inputs(name):
     return wl, prob, x, w, b, dy
 
 
-@pytest.mark.parametrize("name", ["c1_tiny", "c2_strided", "c4g_grouped"])
+@pytest.mark.parametrize("name", ["c1_tiny", "c2_strided", "c4g_grouped", "d1_depthwise"])
 def test_workload_full(name):
     wl, prob, x, w, b, dy = _workload_inputs(name)
     dt, mode = wl["dtype"], wl["check"]
