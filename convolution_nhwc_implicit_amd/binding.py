@@ -105,11 +105,15 @@ def load():
                                     P(Conv2dAlgo), vp]
     lib.conv2d_wgrad_ex.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, ep, vp, vp, ctypes.c_size_t,
                                     P(Conv2dAlgo), vp]
+    lib.conv2d_bias_grad_workspace_size.argtypes = [P(Conv2dProblem), ctypes.c_int, P(ctypes.c_size_t)]
+    lib.conv2d_bias_grad.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, ctypes.c_int, vp,
+                                     ctypes.c_size_t, vp]
     lib.conv2d_status_string.argtypes = [ctypes.c_int]
     lib.conv2d_status_string.restype = ctypes.c_char_p
     for name in ("conv2d_output_size", "conv2d_workspace_size", "conv2d_plan_info",
                  "conv2d_fprop", "conv2d_dgrad", "conv2d_wgrad", "conv2d_workspace_size_ex",
-                 "conv2d_fprop_ex", "conv2d_dgrad_ex", "conv2d_wgrad_ex"):
+                 "conv2d_fprop_ex", "conv2d_dgrad_ex", "conv2d_wgrad_ex",
+                 "conv2d_bias_grad_workspace_size", "conv2d_bias_grad"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -335,6 +339,28 @@ def conv2d_wgrad_ex(prob, dtype, x, dy, epi, dw, workspace, algo=None, stream=No
     _raise(st, "conv2d_wgrad_ex")
 
 
+def conv2d_bias_grad_workspace_size(prob, dtype):
+    n = ctypes.c_size_t(0)
+    st = load().conv2d_bias_grad_workspace_size(ctypes.byref(make_problem(prob)), _dtype_code(dtype),
+                                                 ctypes.byref(n))
+    _raise(st, "conv2d_bias_grad_workspace_size")
+    return n.value
+
+
+def conv2d_bias_grad(prob, dtype, dy, db, workspace, out_f32=False, stream=None):
+    """db[K] = sum of dy[N,P,Q,K] over N, P, Q; float32 when out_f32."""
+    code = _dtype_code(dtype)
+    tdt = CODE_DTYPE[code]
+    _, _, ys = _shapes(prob)
+    _check_tensor(dy, "dy", tdt, ys)
+    _check_tensor(db, "db", torch.float32 if out_f32 else tdt, (prob["K"],))
+    need = conv2d_bias_grad_workspace_size(prob, code)
+    wsp, wsb = _check_workspace(workspace, need)
+    st = load().conv2d_bias_grad(ctypes.byref(make_problem(prob)), code, dy.data_ptr(), db.data_ptr(),
+                                 int(bool(out_f32)), wsp, wsb, _stream(stream))
+    _raise(st, "conv2d_bias_grad")
+
+
 # --------------------------------------------------------------- conveniences
 
 def _pair(v):
@@ -377,6 +403,17 @@ def dgrad(dy, w, input_hw, stride=1, padding=0, dilation=1, groups=1, algo=None)
     wsb = workspace_for(CONV2D_OP_DGRAD, prob, dy.dtype, dy.device, algo)
     conv2d_dgrad(prob, dy.dtype, dy, w, dx, wsb, algo)
     return dx
+
+
+def bias_grad(dy, out_f32=False):
+    """db[K] = sum of dy[N,P,Q,K] over N, P, Q."""
+    N, P, Q, K = dy.shape
+    prob = problem_from((N, P, Q, K), (K, 1, 1, K))
+    db = torch.empty((K,), dtype=torch.float32 if out_f32 else dy.dtype, device=dy.device)
+    n = conv2d_bias_grad_workspace_size(prob, dy.dtype)
+    wsb = torch.empty(n, dtype=torch.uint8, device=dy.device) if n else None
+    conv2d_bias_grad(prob, dy.dtype, dy, db, wsb, out_f32)
+    return db
 
 
 def wgrad(x, dy, filter_rs, stride=1, padding=0, dilation=1, groups=1, algo=None):

@@ -139,14 +139,17 @@ struct Plan {
 int choose_igemm_tile(long long m_total, long long ngemm)
 {
     // Prefer the widest N tile the problem fills; shrink M until the grid has
-    // enough workgroups for 256 CUs.
+    // enough workgroups for 256 CUs.  With a 64-wide N, 64 x 64 tiles unless
+    // they would make more than 16 workgroups per CU (measured: the 1x1
+    // 64x56x56x256 -> 64 dgrad takes 28 us on 64 x 64 against 33 us on
+    // 128 x 64; larger grids gain nothing from the smaller tile).
     if (ngemm <= 32) return 4;  // 64 x 32
     auto tiles = [&](int t) {
         TileShape s = igemm_tile_shape(t);
         return ((m_total + s.bm - 1) / s.bm) * ((ngemm + s.bn - 1) / s.bn);
     };
     if (ngemm >= 128 && ngemm % 128 == 0 && tiles(1) >= 2 * kNumCUs) return 1;  // 128 x 128
-    if (tiles(0) >= 2 * kNumCUs) return 0;                                        // 128 x 64
+    if (tiles(0) >= 2 * kNumCUs && tiles(2) > 16 * kNumCUs) return 0;           // 128 x 64
     return 2;                                                                      // 64 x 64
 }
 
@@ -433,6 +436,23 @@ int run_band(int dtype, const Dims &d, int cin, const void *src, int H, int W, c
 }
 
 }  // namespace
+
+// Bias gradient: column sums of dy [N*P*Q][K] over row slices, about two
+// workgroups per CU and at least 64 rows per slice, then the split-K reduce.
+static int bias_grad_plan(const conv2d_problem_t *prob, int dtype, Dims *d, int *splits, size_t *ws)
+{
+    int st = validate(prob, d);
+    if (st) return st;
+    if (dtype != CONV2D_DTYPE_F16 && dtype != CONV2D_DTYPE_BF16) return CONV2D_ERR_UNSUPPORTED;
+    const long long rows = d->N * d->P * d->Q;
+    if (rows * d->K > kMaxElems) return CONV2D_ERR_UNSUPPORTED;
+    const long long cb = ((d->K + 7) / 8 + kColsumVecsPerWg - 1) / kColsumVecsPerWg;
+    long long s = std::min(std::max(1LL, 2LL * kNumCUs / cb), std::max(1LL, rows / 64));
+    s = std::min(s, 65535LL);
+    *splits = (int)s;
+    *ws = round_up((size_t)s * splitk_stride(d->K) * sizeof(float), 256);
+    return CONV2D_OK;
+}
 
 extern "C" {
 
@@ -890,6 +910,41 @@ int conv2d_dgrad_ex(const conv2d_problem_t *prob, int dtype, const void *dy, con
     int st = make_epi(epi, CONV2D_OP_DGRAD, &ep);
     if (st) return st;
     return dgrad_run(prob, dtype, dy, w, ep, dx, workspace, workspace_bytes, algo, stream);
+}
+
+int conv2d_bias_grad_workspace_size(const conv2d_problem_t *prob, int dtype, size_t *bytes)
+{
+    if (!bytes) return CONV2D_ERR_INVALID_ARGUMENT;
+    Dims d;
+    int splits;
+    return bias_grad_plan(prob, dtype, &d, &splits, bytes);
+}
+
+int conv2d_bias_grad(const conv2d_problem_t *prob, int dtype, const void *dy, void *db, int out_f32,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    Dims d;
+    int splits;
+    size_t ws;
+    int st = bias_grad_plan(prob, dtype, &d, &splits, &ws);
+    if (st) return st;
+    if (!dy || !db || (out_f32 != 0 && out_f32 != 1)) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (!aligned16(dy) || !aligned16(db)) return CONV2D_ERR_UNSUPPORTED;
+    if (workspace_bytes < ws) return CONV2D_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned16(workspace)) return CONV2D_ERR_INVALID_ARGUMENT;
+    const uint32_t rows = (uint32_t)(d.N * d.P * d.Q);
+    ColsumArgs a;
+    a.src = dy;
+    a.parts = (float *)workspace;
+    a.rows = rows;
+    a.rows_per_split = (rows + splits - 1) / splits;
+    a.K = (int)d.K;
+    a.vec = d.K % 8 == 0;
+    a.part_stride = splitk_stride(d.K);
+    hipStream_t s = (hipStream_t)stream;
+    if (launch_colsum(dtype, a, splits, s) != hipSuccess) return CONV2D_ERR_DEVICE;
+    const ReduceEpi re{1.0f, 0.0f, nullptr, out_f32};
+    return hip_status(launch_splitk_reduce(dtype, a.parts, splits, d.K, a.part_stride, db, &re, s));
 }
 
 int conv2d_wgrad_ex(const conv2d_problem_t *prob, int dtype, const void *x, const void *dy,

@@ -180,6 +180,21 @@ hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long 
 // Elements between consecutive slices' partials: count rounded up to 4.
 inline long long splitk_stride(long long count) { return (count + 3) / 4 * 4; }
 
+// Column sums of a row-major [rows][K] fp16/bf16 matrix into fp32 partials,
+// one per row slice: parts[z*part_stride + k] = sum over rows r of slice z of
+// src[r][k], in a fixed order (wgrad.hip, colsum_kernel).  The bias gradient
+// is this over dy viewed as [N*P*Q][K], then the split-K reduce.
+struct ColsumArgs {
+    const void *src;
+    float *parts;
+    uint32_t rows, rows_per_split;
+    int K;
+    int vec;                // K % 8 == 0: 16-byte row pieces (src 16-byte aligned)
+    long long part_stride;
+};
+constexpr int kColsumVecsPerWg = 256;  // 8-column vectors per workgroup (grid.y = column blocks)
+hipError_t launch_colsum(int dtype, const ColsumArgs &a, int splits, hipStream_t st);
+
 // ---------------------------------------------------------------------------
 // Stride-1 wgrad band kernel (wgrad_band.hip): dy and x rows in LDS rings,
 // transposing LDS reads.  One workgroup per (image, band of rows_per_wg output

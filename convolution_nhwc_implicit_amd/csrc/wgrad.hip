@@ -277,4 +277,89 @@ hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Column sums (bias gradient).  Workgroup (z, y) takes rows [z*rows_per_split,
+// ...) and the 8-column vectors [256*y, 256*y + ncv).  Thread (row lane rl,
+// vector cv) adds rows rl, rl + nrl, ... of the slice in ascending order in
+// fp32; the nrl lane sums of a column are then added in lane order through
+// LDS, and the workgroup writes one fp32 partial per column.  A wave reads
+// whole consecutive rows, 16 bytes a lane (K % 8 == 0), else element by
+// element.
+// ---------------------------------------------------------------------------
+template <class E, bool VEC>
+__global__ __launch_bounds__(256) void colsum_kernel(const ColsumArgs a)
+{
+    using elem = typename E::elem;
+    __shared__ float red[256][8];
+    const int K8 = (a.K + 7) / 8, cb = blockIdx.y * kColsumVecsPerWg;
+    const int ncv = min(K8 - cb, kColsumVecsPerWg), nrl = 256 / ncv;
+    const int tid = threadIdx.x, cv = tid % ncv, rl = tid / ncv;
+    const int k0 = (cb + cv) * 8;
+    const uint32_t r0 = blockIdx.x * a.rows_per_split;
+    uint32_t r1 = r0 + a.rows_per_split;
+    if (r1 > a.rows || r1 < r0) r1 = a.rows;
+    float s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = 0.0f;
+    if (rl < nrl) {
+        const elem *src = (const elem *)a.src + k0;
+        uint32_t r = r0 + rl;
+        if (VEC) {
+            // eight rows in flight per step (rows past the slice read as
+            // zeros, which leave the sums unchanged); each added in order
+            for (; r < r1; r += 8 * (uint32_t)nrl) {
+                u32x4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    v[u] = r + u * nrl < r1 ? *(const u32x4 *)(src + (size_t)(r + u * nrl) * a.K)
+                                            : u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) s[j] += E::to_f32((elem)(w[j >> 1] >> (16 * (j & 1))));
+                }
+            }
+        } else {
+            for (; r < r1; r += nrl) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (k0 + j < a.K) s[j] += E::to_f32(src[(size_t)r * a.K + j]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[tid][j] = s[j];
+    __syncthreads();
+    float *part = a.parts + (size_t)blockIdx.x * a.part_stride;
+    for (int o = tid; o < ncv * 8; o += 256) {
+        const int oc = o >> 3, j = o & 7, k = (cb + oc) * 8 + j;
+        float sum = 0.0f;
+        for (int l = 0; l < nrl; ++l) sum += red[l * ncv + oc][j];
+        if (k < a.K) part[k] = sum;
+    }
+}
+
+hipError_t launch_colsum(int dtype, const ColsumArgs &a, int splits, hipStream_t st)
+{
+    if (a.K < 1 || splits < 1 || (a.vec && a.K % 8)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)splits, (unsigned)(((a.K + 7) / 8 + kColsumVecsPerWg - 1) / kColsumVecsPerWg));
+    switch (dtype) {
+    case CONV2D_DTYPE_F16:
+        if (a.vec)
+            colsum_kernel<EF16, true><<<grid, 256, 0, st>>>(a);
+        else
+            colsum_kernel<EF16, false><<<grid, 256, 0, st>>>(a);
+        break;
+    case CONV2D_DTYPE_BF16:
+        if (a.vec)
+            colsum_kernel<EBF16, true><<<grid, 256, 0, st>>>(a);
+        else
+            colsum_kernel<EBF16, false><<<grid, 256, 0, st>>>(a);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace cnv

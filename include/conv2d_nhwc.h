@@ -235,6 +235,28 @@ int conv2d_wgrad_ex(const conv2d_problem_t *prob, int dtype,
                     void *workspace, size_t workspace_bytes,
                     const conv2d_algo_t *algo, void *stream);
 
+/*
+ * Bias gradient.  The forward pass adds bias[k] to every output pixel of
+ * channel k (the tensorcore Conv2D page, forward algorithm, step 3; the burn
+ * conv module's `bias` argument, "added to each channel"), so the gradient of
+ * the loss with respect to the bias is the adjoint of that broadcast:
+ *   db[k] = sum over n < N, p < P, q < Q of dy[n][p][q][k],
+ * summed in fp32 in a fixed order (row slices of the N*P*Q pixels, each in
+ * ascending pixel order, then the slices in ascending order), then rounded
+ * once to dtype, or handed back as fp32 with out_f32 = 1.  Bit-identical run
+ * to run.  Only N, K and P, Q (from the problem) matter; groups do not.
+ *   dy  device, [N][P][Q][K], dtype F16/BF16 (INT8 -> UNSUPPORTED), 16-byte aligned
+ *   db  device, [K], dtype (fp32 with out_f32), 16-byte aligned; overwritten
+ *   workspace / workspace_bytes  as conv2d_bias_grad_workspace_size; fp32
+ *       partials [slices][K rounded up to 4]
+ * Errors: INVALID_ARGUMENT (bad problem, null dy/db/workspace, out_f32 not
+ * 0/1), UNSUPPORTED (dtype, alignment, more than 2^31 - 1 elements of dy),
+ * WORKSPACE_TOO_SMALL; nothing is enqueued on error.
+ */
+int conv2d_bias_grad_workspace_size(const conv2d_problem_t *prob, int dtype, size_t *bytes);
+int conv2d_bias_grad(const conv2d_problem_t *prob, int dtype, const void *dy, void *db, int out_f32,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *conv2d_status_string(int status);
 

@@ -38,6 +38,7 @@ def _load():
             getattr(lib, name).argtypes = [ip, dp, dp, dp, ctypes.c_int, dp]
         lib.oracle_dgrad.argtypes = [ip, dp, dp, dp]
         lib.oracle_wgrad.argtypes = [ip, dp, dp, dp]
+        lib.oracle_bias_grad.argtypes = [ip, dp, dp]
         lib.oracle_fprop_sampled.argtypes = [ip, dp, dp, dp, ctypes.c_int, i64p, ctypes.c_long, dp]
         lib.oracle_dgrad_sampled.argtypes = [ip, dp, dp, i64p, ctypes.c_long, dp]
         lib.oracle_wgrad_sampled.argtypes = [ip, dp, dp, i64p, ctypes.c_long, dp]
@@ -52,7 +53,7 @@ def _load():
         lib.oracle_round_f16.argtypes = [dp, ctypes.c_long, u16p]
         lib.oracle_round_bf16.argtypes = [dp, ctypes.c_long, u16p]
         for name in ("oracle_fprop", "oracle_dgrad", "oracle_wgrad", "oracle_fprop_sampled",
-                     "oracle_dgrad_sampled", "oracle_wgrad_sampled"):
+                     "oracle_dgrad_sampled", "oracle_wgrad_sampled", "oracle_bias_grad"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -119,6 +120,15 @@ def wgrad(prob, x, dy):
     dp = ctypes.c_double
     _check(_load().oracle_wgrad(_dims(prob), _ptr(x, dp), _ptr(dy, dp), _ptr(dw, dp)))
     return dw
+
+
+def bias_grad(prob, dy):
+    """db[k] = sum of dy[n,p,q,k] over n, p, q (adjoint of the bias add); shape [K]."""
+    dy = _f64(dy)
+    db = np.empty((prob["K"],), dtype=np.float64)
+    dp = ctypes.c_double
+    _check(_load().oracle_bias_grad(_dims(prob), _ptr(dy, dp), _ptr(db, dp)))
+    return db
 
 
 def _idx(idx):

@@ -241,6 +241,27 @@ int oracle_wgrad(const int *d, const double *x, const double *dy, double *dw)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Bias gradient.  fprop adds bias[k] to every output pixel of channel k     */
+/* (the tensorcore Conv2D page, forward algorithm, step 3), so the gradient  */
+/* with respect to the bias is the adjoint of that broadcast:                */
+/* db[k] = sum over all n, p, q of dy[n,p,q,k].  One fp64 sum per channel,   */
+/* pixels in ascending order.                                                */
+/* ------------------------------------------------------------------------ */
+int oracle_bias_grad(const int *d, const double *dy, double *db)
+{
+    prob_t p;
+    if (load_prob(d, &p)) return -1;
+    long total = p.N * p.P * p.Q;
+#pragma omp parallel for schedule(static)
+    for (long k = 0; k < p.K; ++k) {
+        double acc = 0.0;
+        for (long pix = 0; pix < total; ++pix) acc += dy[pix * p.K + k];
+        db[k] = acc;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Sampled outputs: idx holds `count` flat output indices (row-major in the  */
 /* output layout); out[i] receives the value at idx[i].  Used to check       */
 /* full-size problems at a sample of points.                                 */

@@ -227,3 +227,24 @@ def test_epilogue_checks(lib):
     band = problem(2, 64, 9, 9, 64, 3, 3, pad=(1, 1))
     assert B.conv2d_workspace_size(1, band, "f16") == 0
     assert B.conv2d_workspace_size_ex(1, band, "f16", epi=dict(alpha=2.0)) >= 64 * 9 * 64 * 2
+
+
+def test_bias_grad_checks(lib):
+    """The bias gradient validates and plans before any device work (the fake
+    addresses below are never dereferenced)."""
+    prob = problem(4, 8, 10, 10, 24, 3, 3, pad=(1, 1))
+    pr = ctypes.byref(B.make_problem(prob))
+    fake = ctypes.c_void_p(0x10000)
+    n = B.conv2d_bias_grad_workspace_size(prob, "f16")
+    # one fp32 partial of K (rounded up to 4) per row slice; 400 rows make 6 slices
+    assert n >= 6 * 24 * 4 and n % 256 == 0
+    inv, uns = B.CONV2D_ERR_INVALID_ARGUMENT, B.CONV2D_ERR_UNSUPPORTED
+    assert lib.conv2d_bias_grad(pr, 0, None, fake, 0, fake, n, None) == inv
+    assert lib.conv2d_bias_grad(pr, 0, fake, fake, 2, fake, n, None) == inv  # out_f32 is 0 or 1
+    assert lib.conv2d_bias_grad(pr, 2, fake, fake, 0, fake, n, None) == uns  # no int8
+    assert lib.conv2d_bias_grad(pr, 0, ctypes.c_void_p(0x10008), fake, 0, fake, n, None) == uns
+    assert lib.conv2d_bias_grad(pr, 0, fake, fake, 0, fake, n - 256, None) == B.CONV2D_ERR_WORKSPACE_TOO_SMALL
+    assert lib.conv2d_bias_grad(pr, 0, fake, fake, 0, None, n, None) == inv
+    bad = B.make_problem(problem(4, 8, 10, 10, 24, 3, 3, pad=(1, 1), groups=3))
+    bad.c = 7  # C % groups != 0
+    assert lib.conv2d_bias_grad(ctypes.byref(bad), 0, fake, fake, 0, fake, n, None) == inv

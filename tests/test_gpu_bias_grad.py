@@ -1,0 +1,62 @@
+"""GPU parity of the bias gradient, db[k] = sum of dy[n,p,q,k] over n, p, q,
+against the oracle, through the C ABI: the 16-byte path (K % 8 == 0) on the
+benchmark's full-size dy, a K that is not a multiple of 8 (element loads),
+more than 256 eight-channel vectors (two column blocks), fewer rows than one
+slice, a strided problem, fp32 output, and bit-identical repeats.  Integer
+data sums exactly in fp32 (every partial sum is an integer below 2^24), so
+those results must equal the oracle's rounded once."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from convolution_nhwc_implicit_amd import binding as B
+from convolution_nhwc_implicit_amd import workloads as WL
+from convolution_nhwc_implicit_amd.workloads import problem
+
+from parity import DEV, check, f64
+
+pytestmark = pytest.mark.gpu
+
+C3A = WL.WORKLOADS["c3a_resnet3x3"]["prob"]
+CASES = [
+    ("c3a_gauss", C3A, "f16", "gauss"),
+    ("c3a_int", C3A, "f16", "int"),
+    ("k13_bf16", problem(3, 8, 9, 10, 13, 3, 3, pad=(1, 1)), "bf16", "int"),
+    ("k2056_two_blocks", problem(1, 8, 8, 8, 2056, 1, 1), "f16", "gauss"),
+    ("rows_lt_64", problem(1, 8, 5, 6, 40, 3, 3, pad=(1, 1)), "f16", "int"),
+    ("strided_bf16", problem(4, 16, 23, 19, 72, 3, 3, pad=(1, 1), stride=(2, 2)), "bf16", "gauss"),
+]
+
+
+def make_dy(cid, prob, dtype, dist):
+    P, Q = oracle.output_hw(prob)
+    rng = np.random.Generator(np.random.PCG64(zlib.crc32(cid.encode())))
+    return WL.draw((prob["N"], P, Q, prob["K"]), dtype, dist, rng)
+
+
+def run(prob, dtype, dy, out_f32=False):
+    db = torch.empty((prob["K"],), dtype=torch.float32 if out_f32 else dy.dtype, device=DEV)
+    n = B.conv2d_bias_grad_workspace_size(prob, dtype)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV) if n else None
+    B.conv2d_bias_grad(prob, dtype, dy, db, ws, out_f32=out_f32)
+    torch.cuda.synchronize()
+    return db
+
+
+@pytest.mark.parametrize("cid,prob,dtype,dist", CASES, ids=[c[0] for c in CASES])
+def test_bias_grad(cid, prob, dtype, dist):
+    dy = make_dy(cid, prob, dtype, dist)
+    ref = oracle.bias_grad(prob, f64(dy))
+    dyg = dy.to(DEV)
+    db = run(prob, dtype, dyg)
+    check(f64(db), ref, dtype, "exact" if dist == "int" else "tol", f"{cid} db")
+    db32 = run(prob, dtype, dyg, out_f32=True)
+    g = db32.cpu().numpy().astype(np.float64)
+    if dist == "int":
+        assert np.array_equal(g, ref), f"{cid} db fp32: {np.count_nonzero(g != ref)} differ"
+    else:
+        assert np.max(np.abs(g - ref)) <= 1e-5 * np.max(np.abs(ref)), f"{cid} db fp32"
+    assert torch.equal(run(prob, dtype, dyg), db), f"{cid}: repeat differs"

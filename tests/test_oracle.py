@@ -234,6 +234,34 @@ def test_adjoint_identities_exact(prob):
     assert a == b == c
 
 
+@pytest.mark.parametrize("prob", ADJ_PROBLEMS)
+def test_bias_grad_adjoint_exact(prob):
+    """db is the adjoint of the bias add: with a zero filter fprop is the
+    broadcast of the bias, so <fprop(x, 0, b), dy> = <b, db>, exactly on
+    integer data."""
+    rng = np.random.default_rng(9)
+    x, w, dy = rand_problem_inputs(prob, rng)
+    b = rng.integers(-4, 5, size=prob["K"]).astype(np.float64)
+    y = oracle.fprop(prob, x, np.zeros_like(w), bias=b)
+    db = oracle.bias_grad(prob, dy)
+    assert float(np.sum(y * dy)) == float(np.sum(b * db))
+
+
+@pytest.mark.parametrize("prob", ADJ_PROBLEMS[:3])
+def test_bias_grad_brute_force(prob):
+    """The map bias -> fprop(x, 0, bias), built column by column from unit
+    bias vectors; bias_grad must be its exact transpose."""
+    rng = np.random.default_rng(10)
+    x, w, dy = rand_problem_inputs(prob, rng)
+    K = prob["K"]
+    V = np.empty((dy.size, K))
+    for k in range(K):
+        e = np.zeros(K)
+        e[k] = 1.0
+        V[:, k] = oracle.fprop(prob, x, np.zeros_like(w), bias=e).reshape(-1)
+    assert np.array_equal(oracle.bias_grad(prob, dy), V.T @ dy.reshape(-1))
+
+
 @pytest.mark.parametrize("prob", ADJ_PROBLEMS[:3])
 def test_dense_operator_brute_force(prob):
     """Build the linear maps x -> fprop(x, w) and w -> fprop(x, w) column by
