@@ -7,8 +7,10 @@
 // scratch size is the cost this kernel avoids).  Each 16-byte chunk of a GEMM
 // row is 8 (16-bit types) or 16 (int8) consecutive channels of one filter tap,
 // so every global load is a 128-bit load of contiguous NHWC memory or zero for
-// a padding tap.  Tiles are staged in LDS in two buffers and fed to 16x16x32
-// (f16/bf16) or 16x16x64 (int8) MFMA with fp32 / int32 accumulation.  The
+// a padding tap.  Tiles arrive in LDS by direct-to-LDS loads into a ring of
+// three stages (two k-steps in flight while the third is computed; padding
+// reads zeros through the buffer range check) and feed 16x16x32 (f16/bf16)
+// or 16x16x64 (int8) MFMA with fp32 / int32 accumulation.  The
 // epilogue (bias, ReLU, int8 requantisation, rounding) is fused and the tile
 // leaves through LDS as 128-bit stores.
 //
