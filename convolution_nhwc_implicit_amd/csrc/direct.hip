@@ -8,6 +8,8 @@
 // own consecutive channels, so the NHWC / KRSC reads and the writes coalesce.
 // wgrad cuts its long pixel sum into slices whose fp32 partials are reduced in
 // slice order by the same split-K reduction as the implicit-GEMM wgrad.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace cnv {
@@ -440,6 +442,30 @@ __device__ inline void unpack8(u32x4 v, float *f)
     for (int j = 0; j < 8; ++j) f[j] = E::to_f32((typename E::elem)(w[j >> 1] >> (16 * (j & 1))));
 }
 
+// acc + (fp16 in the low / high half of x2, widened exactly) * w, one rounding.
+__device__ inline float fma_mix_lo(uint32_t x2, float w, float acc)
+{
+    asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(x2), "v"(w));
+    return acc;
+}
+__device__ inline float fma_mix_hi(uint32_t x2, float w, float acc)
+{
+    asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(x2), "v"(w));
+    return acc;
+}
+
+// acc + a * b for the fp16 pair in the low / high halves of a2 and b2.
+__device__ inline float fma_mix2_lo(uint32_t a2, uint32_t b2, float acc)
+{
+    asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+    return acc;
+}
+__device__ inline float fma_mix2_hi(uint32_t a2, uint32_t b2, float acc)
+{
+    asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+    return acc;
+}
+
 // Bias of the thread's 8 channels (zeros without bias), loaded once.
 template <class E>
 __device__ inline void load_bias8(const DirectArgs &a, int c0, float *b8)
@@ -577,18 +603,40 @@ __global__ __launch_bounds__(256) void depthwise_rows(const DirectArgs a, const 
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
         if (r >= R) break;
-        float xf[DWT + 2][8];
+        if constexpr (std::is_same<E, EF16>::value) {
+            // fp16 pixels feed v_fma_mix_f32 straight from their packed
+            // words (exact widening, one rounding: the same result as
+            // converting first), which saves a conversion per element
 #pragma unroll
-        for (int u = 0; u < DWT + 2; ++u) unpack8<E>(raw[r][u], xf[u]);
+            for (int s = 0; s < 3; ++s) {
+                if (s >= S) break;
+                float wv[8];
+                filter8(wsh, r * S + s, a.C, c0, wv);
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-            if (s >= S) break;
-            float wv[8];
-            filter8(wsh, r * S + s, a.C, c0, wv);
+                for (int i = 0; i < DWT; ++i) {
+                    const u32x4 v = raw[r][i + s];
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int i = 0; i < DWT; ++i)
+                    for (int j = 0; j < 8; j += 2) {
+                        acc[i][j] = fma_mix_lo(w4[j >> 1], wv[j], acc[i][j]);
+                        acc[i][j + 1] = fma_mix_hi(w4[j >> 1], wv[j + 1], acc[i][j + 1]);
+                    }
+                }
+            }
+        } else {
+            float xf[DWT + 2][8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] += xf[i + s][j] * wv[j];
+            for (int u = 0; u < DWT + 2; ++u) unpack8<E>(raw[r][u], xf[u]);
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                if (s >= S) break;
+                float wv[8];
+                filter8(wsh, r * S + s, a.C, c0, wv);
+#pragma unroll
+                for (int i = 0; i < DWT; ++i)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[i][j] += xf[i + s][j] * wv[j];
+            }
         }
     }
     float b8[8];
@@ -842,22 +890,46 @@ __global__ __launch_bounds__(256) void depthwise_wgrad_rows(const DirectArgs a)
                     xraw[r][v] = __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0);
                 }
             }
-            float df[T][8];
+            if constexpr (std::is_same<E, EF16>::value) {
+                // both operands fp16: v_fma_mix_f32 takes them from their
+                // packed words (exact products' widening, one rounding)
 #pragma unroll
-            for (int i = 0; i < T; ++i) unpack8<E>(draw[i], df[i]);
+                for (int r = 0; r < 3; ++r) {
+                    if (r >= a.R) break;
 #pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                if (r >= a.R) break;
-                float xf[T + 2][8];
+                    for (int s = 0; s < 3; ++s) {
+                        if (s >= a.S) break;
 #pragma unroll
-                for (int v = 0; v < T + 2; ++v) unpack8<E>(xraw[r][v], xf[v]);
+                        for (int i = 0; i < T; ++i) {
+                            const uint32_t d4[4] = {draw[i].x, draw[i].y, draw[i].z, draw[i].w};
+                            const u32x4 xv = xraw[r][i + s];
+                            const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-                for (int s = 0; s < 3; ++s) {
-                    if (s >= a.S) break;
+                            for (int j = 0; j < 8; j += 2) {
+                                acc[r][s][j] = fma_mix2_lo(d4[j >> 1], x4[j >> 1], acc[r][s][j]);
+                                acc[r][s][j + 1] = fma_mix2_hi(d4[j >> 1], x4[j >> 1], acc[r][s][j + 1]);
+                            }
+                        }
+                    }
+                }
+            } else {
+                float df[T][8];
 #pragma unroll
-                    for (int i = 0; i < T; ++i)
+                for (int i = 0; i < T; ++i) unpack8<E>(draw[i], df[i]);
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[r][s][j] += df[i][j] * xf[i + s][j];
+                for (int r = 0; r < 3; ++r) {
+                    if (r >= a.R) break;
+                    float xf[T + 2][8];
+#pragma unroll
+                    for (int v = 0; v < T + 2; ++v) unpack8<E>(xraw[r][v], xf[v]);
+#pragma unroll
+                    for (int s = 0; s < 3; ++s) {
+                        if (s >= a.S) break;
+#pragma unroll
+                        for (int i = 0; i < T; ++i)
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) acc[r][s][j] += df[i][j] * xf[i + s][j];
+                    }
                 }
             }
         }
