@@ -122,6 +122,42 @@ __device__ inline int8_t requant_i8(int v, double m)
     return (int8_t)(int)t;
 }
 
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef short s2v __attribute__((ext_vector_type(2)));
+template <class E>
+struct Pack2;
+template <>
+struct Pack2<EF16> {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    __device__ static inline uint32_t cvt(f2v v) { return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2)); }
+};
+template <>
+struct Pack2<EBF16> {
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    __device__ static inline uint32_t cvt(f2v v) { return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2)); }
+};
+// Two epilogue values to a packed pair, rounded to nearest even by one packed
+// conversion.  ReLU (v <= 0, -0 and NaN included, -> +0), which commutes with
+// the rounding: a max against 0 that maps NaN to 0 (packed fp16 after the
+// conversion; fp32 before it for bf16, which has no packed max), then an
+// int16 max of the packed halves, which turns a -0 into +0.
+template <class E, bool RELU>
+__device__ inline uint32_t out_pair(float a, float b)
+{
+    constexpr bool F16 = E::kDtype == CONV2D_DTYPE_F16;
+    if (RELU && !F16) {
+        a = __builtin_fmaxf(a, 0.0f);
+        b = __builtin_fmaxf(b, 0.0f);
+    }
+    uint32_t p = Pack2<E>::cvt(f2v{a, b});
+    if (RELU && F16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        p = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(h2, p), h2{0, 0}));
+    }
+    if (RELU) p = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s2v, p), s2v{0, 0}));
+    return p;
+}
+
 // Float epilogue value: acc + bias, then ReLU (v <= 0, including -0, -> +0).
 __device__ inline float bias_relu_f32(float v, float b, int relu)
 {

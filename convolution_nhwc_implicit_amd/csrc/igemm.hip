@@ -196,57 +196,90 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 fb[j] = *(const u32x4 *)(base + (BM + wn * WTN + j * 16) * BKB + fofs[ks]);
+            // filter fragment as the MFMA's A operand, pixels as B: each lane
+            // of a result block then holds 4 consecutive channels of a pixel
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(fa[i], fb[j], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(fb[j], fa[i], acc[i][j]);
         }
     }
     __syncthreads();  // the stage buffers become the epilogue tile
 
-    // ---- fused epilogue: acc -> (bias, ReLU | requant) -> element -> LDS tile
-    // MFMA 16x16 result layout: lane holds column (lane & 15) and rows
-    // 4*(lane >> 4) + 0..3 of each 16x16 block.
+    // ---- fused epilogue: acc -> (bias, ReLU | requant) -> LDS tile -> HBM
+    // MFMA 16x16 result layout (A = channels, B = pixels): lane holds pixel
+    // (lane & 15) and channels 4*(lane >> 4) + 0..3 of each 16x16 block, so
+    // a lane packs its 4 channels of a pixel into one LDS write.  ngemm is a
+    // multiple of 8 (16 for int8), so those 4 channels are all in range or
+    // all past it.  fprop writes one output image in pixel order, where the
+    // address of GEMM row m is m*ngemm (contig); dgrad phases decompose m.
+    const bool contig = ph.oh0 == 0 && ph.ow0 == 0 && a.osh == 1 && a.osw == 1 && ph.mi == a.ho && ph.mj == a.wo;
+    auto out_offset = [&](uint32_t m) -> size_t {
+        if (contig) return (size_t)m * a.ngemm;
+        const uint32_t n = fdiv(m, ph.div_mimj);
+        const uint32_t rem = m - n * mi_mj;
+        const uint32_t ii = fdiv(rem, ph.div_mj);
+        const uint32_t jj = rem - ii * ph.mj;
+        const int oh = ph.oh0 + (int)ii * a.osh, ow = ph.ow0 + (int)jj * a.osw;
+        return (((size_t)n * a.ho + oh) * a.wo + ow) * a.ngemm;
+    };
+    const int prow = lane & 15, cq = 4 * (lane >> 4);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int col = wn * WTN + j * 16 + (lane & 15);
+        const int col = wn * WTN + j * 16 + cq;
         const int n = nt * BN + col;
         const bool nok = n < a.ngemm;
         if constexpr (E::kDtype == CONV2D_DTYPE_I8) {
-            const int b = (a.bias && nok) ? ((const int32_t *)a.bias)[n] : 0;
+            int b[4];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int r = 0; r < 4; ++r) b[r] = (a.bias && nok) ? ((const int32_t *)a.bias)[n + r] : 0;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * WTM + i * 16 + prow;
+                uint32_t word = 0;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-                    int v = acc[i][j][r] + b;
+                    int v = acc[i][j][r] + b[r];
                     if (a.relu && v < 0) v = 0;
-                    *(int8_t *)(smem + row * CROWB + col) = requant_i8(v, a.requant_m);
+                    word |= (uint32_t)(uint8_t)requant_i8(v, a.requant_m) << (8 * r);
                 }
+                *(uint32_t *)(smem + row * CROWB + col) = word;
+            }
         } else {
-            const float b = (a.bias && nok) ? E::to_f32(((const elem *)a.bias)[n]) : 0.0f;
+            float b[4];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int r = 0; r < 4; ++r) b[r] = (a.bias && nok) ? E::to_f32(((const elem *)a.bias)[n + r]) : 0.0f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-                    float v = acc[i][j][r];
-                    if (a.axpby) {
-                        // linear combination with C at this output element
-                        float c = 0.0f;
-                        const uint32_t m = (uint32_t)mt * BM + row;
-                        if (a.cmat && nok && m < ph.m_total) {
-                            const uint32_t ni = fdiv(m, ph.div_mimj);
-                            const uint32_t rem = m - ni * mi_mj;
-                            const uint32_t ii = fdiv(rem, ph.div_mj);
-                            const uint32_t jj = rem - ii * ph.mj;
-                            const int oh = ph.oh0 + (int)ii * a.osh, ow = ph.ow0 + (int)jj * a.osw;
-                            c = E::to_f32(((const elem *)a.cmat)[(((size_t)ni * a.ho + oh) * a.wo + ow) * a.ngemm + n]);
-                        }
-                        v = a.alpha * v + a.beta * c;
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * WTM + i * 16 + prow;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r];
+                if (a.axpby) {
+                    // linear combination with C at these output elements
+                    float c[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const uint32_t m = (uint32_t)mt * BM + row;
+                    if (a.cmat && nok && m < ph.m_total) {
+                        const uint2 cv = *(const uint2 *)((const elem *)a.cmat + out_offset(m) + n);
+                        const uint32_t cw[2] = {cv.x, cv.y};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) c[r] = E::to_f32((elem)(cw[r >> 1] >> (16 * (r & 1))));
                     }
-                    *(elem *)(smem + row * CROWB + col * OSZ) = E::from_f32(bias_relu_f32(v, b, a.relu));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = a.alpha * v[r] + a.beta * c[r];
                 }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] += b[r];
+                uint2 p;
+                if (a.relu) {
+                    p.x = out_pair<E, true>(v[0], v[1]);
+                    p.y = out_pair<E, true>(v[2], v[3]);
+                } else {
+                    p.x = out_pair<E, false>(v[0], v[1]);
+                    p.y = out_pair<E, false>(v[2], v[3]);
+                }
+                *(uint2 *)(smem + row * CROWB + col * OSZ) = p;
+            }
         }
     }
     __syncthreads();
@@ -259,14 +292,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
         const uint32_t m = (uint32_t)mt * BM + row;
         const int n0 = nt * BN + cc * EPO;
         if (m >= ph.m_total || n0 >= a.ngemm) continue;
-        const uint32_t n = fdiv(m, ph.div_mimj);
-        const uint32_t rem = m - n * mi_mj;
-        const uint32_t ii = fdiv(rem, ph.div_mj);
-        const uint32_t jj = rem - ii * ph.mj;
-        const int oh = ph.oh0 + (int)ii * a.osh;
-        const int ow = ph.ow0 + (int)jj * a.osw;
-        *(u32x4 *)(dst + (((size_t)n * a.ho + oh) * a.wo + ow) * a.ngemm + n0) =
-            *(const u32x4 *)(smem + row * CROWB + cc * 16);
+        *(u32x4 *)(dst + out_offset(m) + n0) = *(const u32x4 *)(smem + row * CROWB + cc * 16);
     }
 }
 
