@@ -158,9 +158,10 @@ int choose_igemm_tile(long long m_total, long long ngemm)
 bool band_eligible(const Dims &d, int dtype, long long cin, long long src_h, long long src_w, long long ngemm)
 {
     // buffer offsets are 32-bit: one source image and the filter stay under 1 GiB
-    return d.G == 1 && d.sh == 1 && d.sw == 1 && d.dh == d.dw && dtype != CONV2D_DTYPE_I8 &&
-           band_supported((int)d.R, (int)d.S, (int)cin, (int)d.dh) && src_h * src_w * cin * 2 < (1LL << 30) &&
-           d.R * d.S * cin * ngemm * 2 < (1LL << 30);
+    const long long e = elem_size(dtype);
+    return d.G == 1 && d.sh == 1 && d.sw == 1 && d.dh == d.dw &&
+           band_supported(dtype, (int)d.R, (int)d.S, (int)cin, (int)d.dh) && src_h * src_w * cin * e < (1LL << 30) &&
+           d.R * d.S * cin * ngemm * e < (1LL << 30);
 }
 
 constexpr int kBandTile = 5;  // tile index of the band kernel (algo tile 6)
@@ -421,14 +422,14 @@ void band_rows(BandArgs &b, long long other_wgs)
 
 // Stride-1 convolution src [N][H][W][cin] -> dst [N][P][Q][ngemm] on the band kernel.
 int run_band(int dtype, const Dims &d, int cin, const void *src, int H, int W, const void *bmat, int flip,
-             const void *bias, int relu, void *dst, int P, int Q, int ngemm, int pad_h, int pad_w,
-             hipStream_t s)
+             const void *bias, int relu, double requant_m, void *dst, int P, int Q, int ngemm, int pad_h,
+             int pad_w, hipStream_t s)
 {
     BandArgs b;
     memset(&b, 0, sizeof(b));
     b.src = src; b.bmat = bmat; b.bias = bias; b.dst = dst;
     b.N = (int)d.N; b.H = H; b.W = W; b.P = P; b.Q = Q; b.ngemm = ngemm;
-    b.pad_h = pad_h; b.pad_w = pad_w; b.flip = flip; b.relu = relu;
+    b.pad_h = pad_h; b.pad_w = pad_w; b.flip = flip; b.relu = relu; b.requant_m = requant_m;
     const int seg = 64 - (int)(d.dw * (d.S - 1));
     const int gn = (ngemm + 63) / 64, gq = (Q + seg - 1) / seg;
     band_rows(b, (long long)gn * gq);
@@ -581,7 +582,7 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     }
 
     if (pl.tile == kBandTile)
-        return run_band(dtype, d, (int)d.C, x, (int)d.H, (int)d.W, w, 0, bias, relu, y, (int)d.P, (int)d.Q,
+        return run_band(dtype, d, (int)d.C, x, (int)d.H, (int)d.W, w, 0, bias, relu, m, y, (int)d.P, (int)d.Q,
                         (int)d.K, (int)d.ph, (int)d.pw, s);
 
     IgemmArgs a;
@@ -666,7 +667,7 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
     }
 
     if (pl.tile == kBandTile)  // stride 1: every tap, filter read reversed and transposed
-        return run_band(dtype, d, (int)d.K, dy, (int)d.P, (int)d.Q, w, 1, nullptr, 0, dx, (int)d.H, (int)d.W,
+        return run_band(dtype, d, (int)d.K, dy, (int)d.P, (int)d.Q, w, 1, nullptr, 0, 0.0, dx, (int)d.H, (int)d.W,
                         (int)d.C, (int)(d.dh * (d.R - 1) - d.ph), (int)(d.dw * (d.S - 1) - d.pw), s);
 
     // One GEMM per stride phase (h mod sh, w mod sw), one launch for all.

@@ -28,6 +28,13 @@
 //     chunks of pixel `col` are XOR-swizzled by col/2: any 16 consecutive
 //     pixels of a fragment (at any tap shift) then hit all 64 banks.
 //
+// int8 (the quantised fprop) runs the same data movement: a pixel of 128
+// int8 channels is the 128 bytes of 64 fp16 ones, and the 32x32x32 int8 MFMA
+// takes 16 bytes a lane like the 32x32x16 fp16 one, so only the MFMA, the
+// int32 accumulators (started at the int32 bias) and the epilogue (ReLU,
+// requantisation in fp64, 64 bytes per staged pixel) differ.  CIN counts
+// 2-byte units.
+//
 // The same kernel runs stride-1 dgrad (TRANS): the source is dy, the padding
 // is dil*(R-1) - pad, and the filter w[K][R][S][C] is read with its taps
 // reversed and K and C swapped.  The swap is done while the filter is copied
@@ -38,12 +45,14 @@
 namespace cnv {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <class E>
 struct Mfma32;
 template <>
 struct Mfma32<EF16> {
+    using acc = f32x16;
     __device__ static inline f32x16 run(u32x4 a, u32x4 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -52,10 +61,20 @@ struct Mfma32<EF16> {
 };
 template <>
 struct Mfma32<EBF16> {
+    using acc = f32x16;
     __device__ static inline f32x16 run(u32x4 a, u32x4 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                         __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma32<EI8> {
+    using acc = i32x16;
+    __device__ static inline i32x16 run(u32x4 a, u32x4 b, i32x16 c)
+    {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b),
+                                                      c, 0, 0, 0);
     }
 };
 
@@ -121,6 +140,10 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 {
     using C = band::BandCfg<R, S, CIN, DIL, TRANS>;
     using elem = typename E::elem;
+    using acc_t = typename Mfma32<E>::acc;
+    constexpr bool I8 = E::kDtype == CONV2D_DTYPE_I8;
+    static_assert(!(I8 && TRANS), "int8 is fprop only");
+    constexpr int EPC16 = 16 / (int)sizeof(elem);  // output channels per 16-byte chunk
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
     unsigned char *ring = smem;
     unsigned char *filt = smem + C::RING_BYTES;    // prologue only
@@ -143,8 +166,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // ---- ring rows by direct-to-LDS loads.  Wave w moves pixels 8w..8w+7 of
     // each row (one 1 KB block); lane i fills stored chunk i%8 of pixel
     // 8w + i/8, i.e. source chunk (i%8) ^ swizzle(pixel).
-    const elem *src_img = (const elem *)a.src + (size_t)img * a.H * a.W * CIN;
-    const u32x4 src_rs = make_buf_rsrc(src_img, (uint32_t)(a.H * a.W * CIN * 2));
+    const unsigned char *src_img = (const unsigned char *)a.src + (size_t)img * a.H * a.W * C::PIXB;
+    const u32x4 src_rs = make_buf_rsrc(src_img, (uint32_t)(a.H * a.W * C::PIXB));
     const unsigned row_bytes = (unsigned)(a.W * CIN * 2);
     auto lane_src = [&](int blk) -> int {  // byte offset in a source row, or -1 past the row
         const int col = 8 * blk + (lane >> 3);
@@ -218,7 +241,10 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         if (tid < C::BN) {
             const int i = tid & 15, lh = (tid >> 4) & 1, hb = tid >> 5;
             const int ch = n0 + 32 * hb + 8 * (i >> 2) + 4 * lh + (i & 3);
-            bias_s[tid] = (a.bias && ch < a.ngemm) ? E::to_f32(((const elem *)a.bias)[ch]) : 0.0f;
+            if constexpr (I8)
+                ((int32_t *)bias_s)[tid] = (a.bias && ch < a.ngemm) ? ((const int32_t *)a.bias)[ch] : 0;
+            else
+                bias_s[tid] = (a.bias && ch < a.ngemm) ? E::to_f32(((const elem *)a.bias)[ch]) : 0.0f;
         }
         wait_vm_all();
         __syncthreads();
@@ -278,18 +304,19 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             const int px = 8 * t + (lane >> 3);
             const int chunk = (lane & 7) ^ ((px >> 1) & 7);
             const u32x4 v = *(const u32x4 *)(stage + px * C::PIXB + (lane & 7) * 16);
-            const int q = q0 + px, ch = n0 + chunk * 8;
-            if (px < C::SEG && q < a.Q && ch < a.ngemm) *(u32x4 *)(drow + (unsigned)(q * a.ngemm + ch)) = v;
+            const int q = q0 + px, ch = n0 + chunk * EPC16;
+            if (chunk < C::BN / EPC16 && px < C::SEG && q < a.Q && ch < a.ngemm)
+                *(u32x4 *)(drow + (unsigned)(q * a.ngemm + ch)) = v;
         }
     };
     __syncthreads();  // every wave holds its filter fragments: the staging area is free
     for (int g = 0; g < ngroups; ++g) {
         const int pr = g * C::GR + prw;  // output row of this wave, relative to p_start
         const bool active = pr < nrows;
-        f32x16 acc[2];
+        acc_t acc[2];
         if (active) {
             // the accumulators start at the bias (zero for dgrad)
-            acc[0] = *(const f32x16 *)(bias_s + (nb * 2 + lhi) * 16);
+            acc[0] = *(const acc_t *)(bias_s + (nb * 2 + lhi) * 16);
             acc[1] = acc[0];
             int rowb[R];
 #pragma unroll
@@ -335,8 +362,30 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 }
             }
         };
+        // int8: lane's 4 channels -> ReLU, requantise (fp64), 4 bytes at byte
+        // 8*(j&1) + 4*lhi of logical chunk 2*nb + j/2 (16 channels a chunk)
+        auto epilogue_i8 = [&]() {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int px = mb * 32 + l32;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        int v = (int)acc[mb][4 * j + r];
+                        if (a.relu && v < 0) v = 0;
+                        word |= (uint32_t)(uint8_t)requant_i8(v, a.requant_m) << (8 * r);
+                    }
+                    const int chunk = (2 * nb + (j >> 1)) ^ ((px >> 1) & 7);
+                    *(uint32_t *)(stage + px * C::PIXB + chunk * 16 + 8 * (j & 1) + 4 * lhi) = word;
+                }
+            }
+        };
         if (active) {
-            if (a.relu)
+            if constexpr (I8)
+                epilogue_i8();
+            else if (a.relu)
                 epilogue(band::BoolC<true>{});
             else
                 epilogue(band::BoolC<false>{});
@@ -351,15 +400,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     if (io_wave) store_rows(ngroups - 1);
 }
 
-bool band_supported(int R, int S, int cin, int dil)
+bool band_supported(int dtype, int R, int S, int cin, int dil)
 {
-    return R == 3 && S == 3 && cin == 64 && dil == 1;
+    // pixels of 128 bytes: 64 fp16/bf16 channels, or 128 int8 ones
+    return R == 3 && S == 3 && dil == 1 && (dtype == CONV2D_DTYPE_I8 ? cin == 128 : cin == 64);
 }
 
 hipError_t launch_band(int dtype, int R, int S, int cin, int dil, const BandArgs &a, int grid_n, int grid_q,
                        hipStream_t st)
 {
-    if (!band_supported(R, S, cin, dil)) return hipErrorInvalidValue;
+    if (!band_supported(dtype, R, S, cin, dil)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(a.N * a.chunks_per_img), (unsigned)grid_n, (unsigned)grid_q);
     const bool t = a.flip != 0;
     switch (dtype) {
@@ -374,6 +424,10 @@ hipError_t launch_band(int dtype, int R, int S, int cin, int dil, const BandArgs
             band_kernel<EBF16, 3, 3, 64, 1, true><<<grid, 512, 0, st>>>(a);
         else
             band_kernel<EBF16, 3, 3, 64, 1, false><<<grid, 512, 0, st>>>(a);
+        break;
+    case CONV2D_DTYPE_I8:
+        if (t) return hipErrorInvalidValue;
+        band_kernel<EI8, 3, 3, 64, 1, false><<<grid, 512, 0, st>>>(a);
         break;
     default: return hipErrorInvalidValue;
     }

@@ -119,9 +119,10 @@ struct BandArgs {
     int N, H, W, P, Q, ngemm;
     int pad_h, pad_w;
     int flip, relu;
+    double requant_m;  // int8: output code = requant(acc + bias) with this multiplier
     int rows_per_wg, chunks_per_img;
 };
-bool band_supported(int R, int S, int cin, int dil);
+bool band_supported(int dtype, int R, int S, int cin, int dil);
 hipError_t launch_band(int dtype, int R, int S, int cin, int dil, const BandArgs &a, int grid_n, int grid_q,
                        hipStream_t st);
 

@@ -137,6 +137,13 @@ INT8_CASES = [
     ("i8_grouped", problem(2, 16, 7, 7, 16, 3, 3, pad=(1, 1), groups=4), True, True),
     ("i8_pad_c3", problem(2, 3, 12, 12, 16, 3, 3, pad=(1, 1)), True, True),
     ("i8_pad_k20", problem(2, 32, 9, 8, 20, 3, 3, pad=(1, 1)), True, False),
+    # 3x3 stride-1 int8 with 128 channels runs the band kernel: ragged row
+    # bands, a K that fills part of a 64-channel slice, two column segments,
+    # pads 0 and 2
+    ("i8_band", problem(2, 128, 11, 13, 128, 3, 3, pad=(1, 1)), True, True),
+    ("i8_band_k48_w70", problem(1, 128, 5, 70, 48, 3, 3, pad=(1, 1)), True, False),
+    ("i8_band_pad0_k192", problem(2, 128, 9, 9, 192, 3, 3), False, True),
+    ("i8_band_pad2", problem(1, 128, 6, 7, 64, 3, 3, pad=(2, 2)), True, True),
 ]
 
 
@@ -154,6 +161,20 @@ def test_int8_fprop_exact(cid, prob, bias, relu):
 
 
 # ------------------------------------------------------------ tile / split sweeps
+
+def test_int8_every_tile_matches_oracle():
+    """Every implicit-GEMM tile and the band kernel give the same int8 codes."""
+    prob = problem(2, 128, 10, 12, 64, 3, 3, pad=(1, 1))
+    x, w, b, _ = case_inputs(prob, "i8", "uniform_i8", seed=77, bias=True)
+    scales = (0.02, 0.01, 0.05)
+    exp = oracle_fprop_out(prob, "i8", x, w, b, True, scales=scales)
+    info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "i8")
+    assert info["num_tiles"] == 6 and info["tile"] == 5, info  # the band kernel is the default
+    for t in range(1, info["num_tiles"] + 1):
+        y = run_fprop(prob, "i8", x, w, b, True, scales=scales, algo=dict(tile=t))
+        got = y.cpu().numpy().reshape(-1)
+        assert np.array_equal(got, exp), f"tile {t}: {np.count_nonzero(got != exp)} codes differ"
+
 
 def test_every_fprop_and_dgrad_tile_matches_oracle():
     prob = problem(2, 32, 13, 11, 48, 3, 3, pad=(1, 1), stride=(2, 1))
