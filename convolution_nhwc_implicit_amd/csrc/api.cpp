@@ -174,7 +174,7 @@ bool wgrad_band_eligible(const Dims &d, int dtype)
            wgrad_band_supported((int)d.R, (int)d.S, (int)d.C, (int)d.K, (int)d.dh, (int)d.Q);
 }
 
-constexpr int kWgradBandTile = 1;  // wgrad tile index of the band kernel (algo tile 2)
+constexpr int kWgradBandTile = 2;  // wgrad tile index of the band kernel (algo tile 3), after the generic ones
 
 // Output rows per wgrad band: about one workgroup per CU, two workgroups
 // (column halves) per band.
@@ -186,11 +186,12 @@ void wgrad_band_rows(const Dims &d, int *rows, int *chunks)
     *chunks = (int)((d.P + *rows - 1) / *rows);
 }
 
-int choose_wgrad_splits(long long tiles, long long npix)
+int choose_wgrad_splits(long long tiles, long long npix, long long min_steps)
 {
+    // about three workgroups per CU, at least min_steps main-loop steps per slice
     const long long steps = (npix + kWgradPixStep - 1) / kWgradPixStep;
     long long s = (3 * kNumCUs) / std::max(1LL, tiles);
-    s = std::min(s, std::max(1LL, steps / 8));
+    s = std::min(s, std::max(1LL, steps / min_steps));
     return (int)std::max(1LL, std::min(s, 4096LL));
 }
 
@@ -357,11 +358,17 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
             pl->ws_bytes = round_up((size_t)pl->split_k * splitk_stride(d.K * ncols) * sizeof(float), 256);
             return CONV2D_OK;
         }
-        pl->tile = (algo && algo->tile) ? algo->tile - 1 : 0;
+        // default: 128 x 128 tiles when they give the chip at least 16 tiles,
+        // else the 64 x 64 kernel, whose extra tiles need fewer slices (and
+        // fewer fp32 partials) on small problems
+        const TileShape big = wgrad_tile_shape(0);
+        const long long big_tiles = ((d.K + big.bm - 1) / big.bm) * ((ncols + big.bn - 1) / big.bn);
+        pl->tile = (algo && algo->tile) ? algo->tile - 1 : (big_tiles >= 16 ? 0 : 1);
+        if (pl->tile == kWgradBandTile) return CONV2D_ERR_UNSUPPORTED;
         TileShape ts = wgrad_tile_shape(pl->tile);
         const long long tiles = ((d.K + ts.bm - 1) / ts.bm) * ((ncols + ts.bn - 1) / ts.bn);
         const long long npix = d.N * d.P * d.Q;
-        int s = (algo && algo->split_k) ? algo->split_k : choose_wgrad_splits(tiles, npix);
+        int s = (algo && algo->split_k) ? algo->split_k : choose_wgrad_splits(tiles, npix, pl->tile == 0 ? 2 : 8);
         if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
         pl->split_k = s;
         if (s > 1 || wparts) pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * ncols) * sizeof(float), 256);

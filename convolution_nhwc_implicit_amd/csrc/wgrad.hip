@@ -1,24 +1,213 @@
-// wgrad.hip -- weight-gradient implicit GEMM for gfx950, and the fixed-order
-// split-K reduction.
+// wgrad.hip -- weight-gradient implicit GEMM for gfx950, the fixed-order
+// split-K reduction, and column sums (bias gradient).
 //
 // dw[k][r][s][c] = sum over output pixels (n,p,q) of
 //                  dy[n,p,q,k] * x[n, p*sh-ph+r*dh, q*sw-pw+s*dw, c].
 // As a GEMM: rows k, columns (r,s,c), reduction over the N*P*Q pixels -- the
 // very long GEMM-K the TVM CUTLASS wgrad pull request names as the reason
-// split-K is needed.  Both operands arrive pixel-major (NHWC), while MFMA wants
-// the reduction index inside each lane's registers, so each thread loads two
-// neighbouring pixels' 8-channel chunks and interleaves them into
-// channel-major LDS rows (pixels innermost).  The reduction over pixels is cut
-// into contiguous slices; each slice writes fp32 partials and a second kernel
-// sums them in slice order (the CUTLASS notebook's "parallel" split-K, with a
-// fixed order instead of atomics, so results are identical run to run).
-// Accumulation is fp32 throughout, as the TVM pull request requires for wgrad.
+// split-K is needed.  The reduction over pixels is cut into contiguous slices;
+// each slice writes fp32 partials and a second kernel sums them in slice
+// order (the CUTLASS notebook's "parallel" split-K, with a fixed order instead
+// of atomics, so results are identical run to run).  Accumulation is fp32
+// throughout, as the TVM pull request requires for wgrad.
+//
+// A workgroup computes a 128 x 128 tile (dy channels x columns) over its
+// slice, 32 pixels per stage.  Both operands arrive pixel-major (NHWC) by
+// direct-to-LDS loads, one 256-byte LDS row per pixel: dy rows are 128
+// consecutive channels, x rows are gathered 16-byte pieces (8 channels of one
+// tap each; C % 8 == 0).  The MFMA wants 8 consecutive pixels of one channel
+// per lane, which the transposing LDS read ds_read_b64_tr_b16 delivers from
+// the pixel-major rows, so no registers or VALU work go into re-laying the
+// operands out.  16-byte chunk c of row r is stored at chunk c ^ 2*(r % 4):
+// the 4 rows of a transposing read then fall on different banks.  Three
+// stages in flight (two loading while one is computed), four waves in a 2 x 2
+// arrangement of 64 x 64 wave tiles (2 x 2 blocks of 32x32x16 MFMA).
 #include "device_common.h"
 
 namespace cnv {
 
-template <class E, int BM, int BN>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (the fragment reads of wgrad_kernel)
+__device__ inline s16x4 tr16(const unsigned char *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+}
+template <class E>
+struct Mfma32x16 {
+    __device__ static inline f32x16 run(u32x4 a, u32x4 b, f32x16 c)
+    {
+        if constexpr (E::kDtype == CONV2D_DTYPE_F16)
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                           c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                            __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ inline void wait_vm_n()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <class E>
 __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
+{
+    constexpr int BM = 128, BN = 128, SP = 32, NSTAGE = 3;
+    constexpr int ROWB = 256;
+    constexpr int TILE = SP * ROWB;      // 8 KB: 8 direct-to-LDS blocks of 4 rows
+    constexpr int STAGE = 2 * TILE;      // dy tile, then x tile
+    constexpr int PER = 4;               // direct-to-LDS loads per wave and stage
+    using elem = typename E::elem;
+    static_assert(SP * 2 == kWgradPixStep, "slices are whole pairs of stages");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE * STAGE];
+
+    const int mt = blockIdx.x, nt = blockIdx.y, z = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const uint32_t pbeg = (uint32_t)z * a.pix_per_split;
+    uint32_t pend = pbeg + a.pix_per_split;
+    if (pend > a.npix || pend < pbeg) pend = a.npix;
+    const int KT = pend > pbeg ? (int)((pend - pbeg + SP - 1) / SP) : 0;
+
+    // ---- direct-to-LDS loads.  Wave w fills blocks w and w + 4 of each tile;
+    // lane i fills row 4*blk + i/16, stored chunk i%16, i.e. logical chunk lc.
+    const int lc = (lane & 15) ^ (2 * ((lane >> 4) & 3));
+    const uint32_t lds0 = lds_addr(smem);
+    const u32x4 dy_rs = make_buf_rsrc(a.dy, (uint32_t)((size_t)a.npix * a.K * sizeof(elem)));
+    const u32x4 x_rs = make_buf_rsrc(a.x, (uint32_t)((size_t)a.N * a.H * a.W * a.C * sizeof(elem)));
+    // dy: channel k of this lane's chunk (whole chunk valid or not, K % 8 == 0)
+    const int k = mt * BM + 8 * lc;
+    const bool kval = k < a.K;
+    // x: column (tap, channel) of this lane's chunk
+    const int col = nt * BN + 8 * lc;
+    const bool cval = col < a.ncols;
+    const uint32_t tap = fdiv((uint32_t)(cval ? col : 0), a.div_C);
+    const int cch = (cval ? col : 0) - (int)tap * a.C;
+    const uint32_t tr = fdiv(tap, a.div_S);
+    const int hoff = (int)tr * a.dh - a.pad_h;
+    const int woff = ((int)tap - (int)tr * a.S) * a.dw - a.pad_w;
+    // the lane's pixel in each of its two blocks: pixel index and (n, p, q),
+    // advanced by SP per stage in mixed radix (Q, P)
+    const uint32_t PQ = (uint32_t)a.P * (uint32_t)a.Q;
+    const uint32_t dn = SP / PQ, dp = (SP / (uint32_t)a.Q) % (uint32_t)a.P, dq = SP % (uint32_t)a.Q;
+    uint32_t pix[2], pn[2], pp[2], pq[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        pix[t] = pbeg + 4 * (wave + 4 * t) + (lane >> 4);
+        const uint32_t v = pix[t] < a.npix ? pix[t] : 0;
+        pn[t] = fdiv(v, a.div_PQ);
+        const uint32_t rem = v - pn[t] * PQ;
+        pp[t] = fdiv(rem, a.div_Q);
+        pq[t] = rem - pp[t] * (uint32_t)a.Q;
+    }
+    auto dma_stage = [&](int kt) {
+        const uint32_t base = lds0 + (uint32_t)((kt % NSTAGE) * STAGE);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bool ok = pix[t] < pend;
+            const uint32_t blk = (uint32_t)(wave + 4 * t) * 1024;
+            dma16(dy_rs, base + blk,
+                  (ok && kval) ? (uint32_t)(((size_t)pix[t] * a.K + k) * sizeof(elem)) : kBufOOBFar);
+            const int h = (int)pp[t] * a.sh + hoff, w = (int)pq[t] * a.sw + woff;
+            const bool okx = ok && cval && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W;
+            dma16(x_rs, base + TILE + blk,
+                  okx ? (uint32_t)(((((size_t)pn[t] * a.H + h) * a.W + w) * a.C + cch) * sizeof(elem)) : kBufOOBFar);
+            // the lane's pixel of the next stage
+            pix[t] += SP;
+            pq[t] += dq;
+            const uint32_t c1 = pq[t] >= (uint32_t)a.Q;
+            if (c1) pq[t] -= a.Q;
+            pp[t] += dp + c1;
+            const uint32_t c2 = pp[t] >= (uint32_t)a.P;
+            if (c2) pp[t] -= a.P;
+            pn[t] += dn + c2;
+        }
+    };
+
+    // ---- fragments by transposing reads: lane l gets column l%32 of a 32-wide
+    // block (dy channel or x column) for pixels 8*(l/32) + 0..7 of a 16-pixel
+    // k-step; in each 16-lane group lane L addresses row L/4, columns
+    // 4*(L%4)..+3 of a 4 x 16 piece.
+    const int fcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column offset in a 32-wide block
+    const int frow = 8 * (lane >> 5) + ((lane & 15) >> 2);      // pixel row in a k-step (+4: second read)
+    auto frag = [&](const unsigned char *tile, int colb, int ks) -> u32x4 {
+        const int c = colb + fcol;  // first of this lane's 4 columns
+        const int r0 = 16 * ks + frow, r1 = r0 + 4;
+        const int ch = c >> 3, cb = (c & 7) * 2;
+        const uint2 lo = __builtin_bit_cast(uint2, tr16(tile + r0 * ROWB + ((ch ^ (2 * (r0 & 3))) << 4) + cb));
+        const uint2 hi = __builtin_bit_cast(uint2, tr16(tile + r1 * ROWB + ((ch ^ (2 * (r1 & 3))) << 4) + cb));
+        return u32x4{lo.x, lo.y, hi.x, hi.y};
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+#pragma unroll
+    for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+        if (s0 < KT) dma_stage(s0);
+    for (int kt = 0; kt < KT; ++kt) {
+        // stage kt has landed when at most the younger stage's loads remain
+        if (kt + 1 < KT)
+            wait_vm_n<PER * (NSTAGE - 2)>();
+        else
+            wait_vm_n<0>();
+        __syncthreads();  // every wave's loads of stage kt are visible; stage kt-1 is consumed
+        if (kt + NSTAGE - 1 < KT) dma_stage(kt + NSTAGE - 1);
+        const unsigned char *ta = smem + (kt % NSTAGE) * STAGE;
+        const unsigned char *tb = ta + TILE;
+#pragma unroll
+        for (int ks = 0; ks < SP / 16; ++ks) {
+            u32x4 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[i] = frag(ta, wm * 64 + 32 * i, ks);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) fb[j] = frag(tb, wn * 64 + 32 * j, ks);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = Mfma32x16<E>::run(fa[i], fb[j], acc[i][j]);
+        }
+    }
+
+    // result block layout: lane holds column l%32, rows 8*(e/4) + 4*(l/32) + e%4
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = nt * BN + wn * 64 + 32 * j + (lane & 31);
+            if (c >= a.ncols) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int kk = mt * BM + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (kk >= a.K) continue;
+                if (a.splits == 1 && !a.to_parts)
+                    ((elem *)a.out)[(size_t)kk * a.ncols + c] = E::from_f32(acc[i][j][e]);
+                else
+                    ((float *)a.out)[(size_t)z * a.part_stride + (size_t)kk * a.ncols + c] = acc[i][j][e];
+            }
+        }
+}
+
+// Small problems: 64 x 64 tiles, 64 pixels per step.  Each thread loads two
+// neighbouring pixels' 8-channel chunks of dy and x into registers and
+// interleaves them into channel-major LDS rows (pixels innermost), which the
+// 16x16x32 MFMA reads directly.  More tiles per problem than the 128 x 128
+// kernel, so fewer slices (and fewer partials) fill the chip.
+template <class E, int BM, int BN>
+__global__ __launch_bounds__(256) void wgrad_interleave_kernel(const WgradArgs a)
 {
     constexpr int NT = 256;
     constexpr int BKP = kWgradPixStep;  // pixels per step
@@ -146,20 +335,32 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
         }
 }
 
-int wgrad_num_tiles() { return 1; }
+// tile 0: the transposing-read kernel (128 x 128), tile 1: the interleaving
+// kernel (64 x 64)
+int wgrad_num_tiles() { return 2; }
 TileShape wgrad_tile_shape(int tile)
 {
-    (void)tile;
-    return {64, 64};
+    return tile == 0 ? TileShape{128, 128} : TileShape{64, 64};
 }
 
 hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st)
 {
-    if (tile != 0) return hipErrorInvalidValue;
-    dim3 grid((unsigned)((a.K + 63) / 64), (unsigned)((a.ncols + 63) / 64), (unsigned)a.splits);
+    if (tile < 0 || tile >= wgrad_num_tiles()) return hipErrorInvalidValue;
+    const TileShape ts = wgrad_tile_shape(tile);
+    dim3 grid((unsigned)((a.K + ts.bm - 1) / ts.bm), (unsigned)((a.ncols + ts.bn - 1) / ts.bn), (unsigned)a.splits);
     switch (dtype) {
-    case CONV2D_DTYPE_F16: wgrad_kernel<EF16, 64, 64><<<grid, 256, 0, st>>>(a); break;
-    case CONV2D_DTYPE_BF16: wgrad_kernel<EBF16, 64, 64><<<grid, 256, 0, st>>>(a); break;
+    case CONV2D_DTYPE_F16:
+        if (tile == 0)
+            wgrad_kernel<EF16><<<grid, 256, 0, st>>>(a);
+        else
+            wgrad_interleave_kernel<EF16, 64, 64><<<grid, 256, 0, st>>>(a);
+        break;
+    case CONV2D_DTYPE_BF16:
+        if (tile == 0)
+            wgrad_kernel<EBF16><<<grid, 256, 0, st>>>(a);
+        else
+            wgrad_interleave_kernel<EBF16, 64, 64><<<grid, 256, 0, st>>>(a);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

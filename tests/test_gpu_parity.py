@@ -217,8 +217,8 @@ def test_wgrad_band_and_generic_agree():
     x, _, _, dy = case_inputs(prob, "f16", "int", seed=49)
     ref = oracle.wgrad(prob, f64(x), f64(dy))
     info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
-    assert info["num_tiles"] == 2 and info["tile"] == 1  # band kernel is the default
-    for t in (1, 2):
+    assert info["num_tiles"] == 3 and info["tile"] == 2  # band kernel is the default
+    for t in (1, 2, 3):
         check(f64(run_wgrad(prob, "f16", x, dy, algo=dict(tile=t))), ref, "f16", "exact", f"wgrad tile {t}")
 
 
