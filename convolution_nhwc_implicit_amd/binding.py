@@ -53,9 +53,10 @@ class Conv2dAlgo(ctypes.Structure):
 
 
 class Conv2dEpilogue(ctypes.Structure):
-    """conv2d_epilogue_t: out = alpha * result + beta * C (fp32), wgrad may keep fp32."""
+    """conv2d_epilogue_t: out = alpha * result + beta * C (fp32), wgrad may keep fp32 and
+    also produce the bias gradient db."""
     _fields_ = [("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("c", ctypes.c_void_p),
-                ("out_f32", ctypes.c_int)]
+                ("out_f32", ctypes.c_int), ("db", ctypes.c_void_p)]
 
 
 class Conv2dPlanInfo(ctypes.Structure):
@@ -267,9 +268,10 @@ def _epi(epi):
     """A ctypes epilogue from a mapping with keys alpha, beta, c (tensor or None), out_f32."""
     if epi is None:
         return None, None
-    c = epi.get("c")
+    c, db = epi.get("c"), epi.get("db")
     e = Conv2dEpilogue(float(epi.get("alpha", 1.0)), float(epi.get("beta", 0.0)),
-                       None if c is None else c.data_ptr(), int(bool(epi.get("out_f32", False))))
+                       None if c is None else c.data_ptr(), int(bool(epi.get("out_f32", False))),
+                       None if db is None else db.data_ptr())
     return e, ctypes.byref(e)
 
 
@@ -322,7 +324,8 @@ def conv2d_dgrad_ex(prob, dtype, dy, w, epi, dx, workspace, algo=None, stream=No
 
 
 def conv2d_wgrad_ex(prob, dtype, x, dy, epi, dw, workspace, algo=None, stream=None):
-    """dw is float32 when epi["out_f32"] (and so is epi["c"])."""
+    """dw is float32 when epi["out_f32"] (and so are epi["c"] and epi["db"]); epi["db"], if given,
+    receives the bias gradient."""
     code = _dtype_code(dtype)
     tdt = CODE_DTYPE[code]
     xs, ws_, ys = _shapes(prob)
@@ -331,6 +334,8 @@ def conv2d_wgrad_ex(prob, dtype, x, dy, epi, dw, workspace, algo=None, stream=No
     odt = torch.float32 if (epi is not None and epi.get("out_f32")) else tdt
     _check_tensor(dw, "dw", odt, ws_)
     _check_c(epi, odt, ws_)
+    if epi is not None and epi.get("db") is not None:
+        _check_tensor(epi["db"], "db", odt, (prob["K"],))
     need = conv2d_workspace_size_ex(CONV2D_OP_WGRAD, prob, code, algo, epi)
     wsp, wsb = _check_workspace(workspace, need)
     keep, ep = _epi(epi)

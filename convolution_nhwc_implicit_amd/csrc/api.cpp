@@ -118,6 +118,7 @@ struct Epi {
     float alpha = 1.0f, beta = 0.0f;
     const void *c = nullptr;
     bool out_f32 = false;
+    void *db = nullptr;  // wgrad: bias gradient output
 };
 
 struct Plan {
@@ -862,6 +863,32 @@ static int make_epi(const conv2d_epilogue_t *e, int op, Epi *ep)
         if (!aligned16(e->c)) return CONV2D_ERR_UNSUPPORTED;
         ep->c = e->c;
     }
+    if (e->db) {
+        if (op != CONV2D_OP_WGRAD) return CONV2D_ERR_INVALID_ARGUMENT;
+        if (!aligned16(e->db)) return CONV2D_ERR_UNSUPPORTED;
+        ep->db = e->db;
+    }
+    return CONV2D_OK;
+}
+
+// Workspace of wgrad_ex: the pass's own, then (with db) the bias-gradient
+// partials at the next 256-byte boundary.
+static int wgrad_ex_workspace(const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, const Epi &ep,
+                              size_t *pass_bytes, size_t *total)
+{
+    Plan pl;
+    int st = make_plan(CONV2D_OP_WGRAD, prob, dtype, algo, ep, &pl);
+    if (st) return st;
+    *pass_bytes = pl.ws_bytes;
+    *total = pl.ws_bytes;
+    if (ep.db) {
+        Dims d;
+        int splits;
+        size_t bws;
+        st = bias_grad_plan(prob, dtype, &d, &splits, &bws);
+        if (st) return st;
+        *total = round_up(pl.ws_bytes, 256) + bws;
+    }
     return CONV2D_OK;
 }
 
@@ -872,6 +899,10 @@ int conv2d_workspace_size_ex(int op, const conv2d_problem_t *prob, int dtype, co
     Epi ep;
     int st = make_epi(epi, op, &ep);
     if (st) return st;
+    if (op == CONV2D_OP_WGRAD) {
+        size_t pass;
+        return wgrad_ex_workspace(prob, dtype, algo, ep, &pass, bytes);
+    }
     Plan pl;
     st = make_plan(op, prob, dtype, algo, ep, &pl);
     if (st) return st;
@@ -962,7 +993,19 @@ int conv2d_wgrad_ex(const conv2d_problem_t *prob, int dtype, const void *x, cons
     Epi ep;
     int st = make_epi(epi, CONV2D_OP_WGRAD, &ep);
     if (st) return st;
-    return wgrad_run(prob, dtype, x, dy, ep, dw, workspace, workspace_bytes, algo, stream);
+    if (!ep.db) return wgrad_run(prob, dtype, x, dy, ep, dw, workspace, workspace_bytes, algo, stream);
+    // with the bias gradient: check everything of both parts before enqueuing either
+    size_t pass, total;
+    st = wgrad_ex_workspace(prob, dtype, algo, ep, &pass, &total);
+    if (st) return st;
+    if (!x || !dy || !dw) return CONV2D_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dw)) return CONV2D_ERR_UNSUPPORTED;
+    if (workspace_bytes < total) return CONV2D_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned16(workspace)) return CONV2D_ERR_INVALID_ARGUMENT;
+    st = wgrad_run(prob, dtype, x, dy, ep, dw, pass ? workspace : nullptr, pass, algo, stream);
+    if (st) return st;
+    unsigned char *bws = (unsigned char *)workspace + round_up(pass, 256);
+    return conv2d_bias_grad(prob, dtype, dy, ep.db, ep.out_f32 ? 1 : 0, bws, total - round_up(pass, 256), stream);
 }
 
 }  // extern "C"

@@ -209,6 +209,9 @@ typedef struct conv2d_epilogue {
     double beta;     /* finite; 0 ignores c */
     const void *c;   /* device, laid out like the output; required (16-byte aligned) when beta != 0 */
     int out_f32;     /* wgrad only: dw and c are fp32 (the sum is not rounded) */
+    void *db;        /* wgrad only, may be NULL: also the bias gradient db[K] = sum of dy over N, P, Q
+                        (as conv2d_bias_grad; fp32 with out_f32, else dtype; 16-byte aligned; alpha and
+                        beta do not apply to it).  The workspace then also holds its partials. */
 } conv2d_epilogue_t;
 
 /* conv2d_workspace_size for a pass with an epilogue (NULL = plain). */

@@ -223,6 +223,17 @@ def test_epilogue_checks(lib):
     n = B.conv2d_workspace_size_ex(2, s, "f16", algo=dict(split_k=1), epi=dict(out_f32=True))
     assert n >= 16 * 3 * 3 * 16 * 4
     assert B.conv2d_workspace_size_ex(2, s, "f16", epi=None) == B.conv2d_workspace_size(2, s, "f16")
+    # the bias gradient beside wgrad: its partials follow the pass's workspace
+    fake_db = type("T", (), {"data_ptr": lambda self: 0x20000})()
+    n0 = B.conv2d_workspace_size_ex(2, s, "f16", epi=dict(alpha=2.0))
+    n1 = B.conv2d_workspace_size_ex(2, s, "f16", epi=dict(alpha=2.0, db=fake_db))
+    assert n1 >= n0 + 16 * 4 and n1 % 256 == 0
+    ep = B.Conv2dEpilogue(1.0, 0.0, None, 0, 0x20000)
+    assert lib.conv2d_fprop_ex(pr, 0, fake, fake, None, 0, ctypes.byref(ep), fake, None, 0, None,
+                               None) == inv  # db is for wgrad only
+    ep = B.Conv2dEpilogue(1.0, 0.0, None, 0, 0x20008)
+    assert lib.conv2d_wgrad_ex(pr, 0, fake, fake, ctypes.byref(ep), fake, fake, 1 << 20, None,
+                               None) == uns  # db must be 16-byte aligned
     # the band-shaped dgrad needs no workspace plain, the filter re-layout with an epilogue
     band = problem(2, 64, 9, 9, 64, 3, 3, pad=(1, 1))
     assert B.conv2d_workspace_size(1, band, "f16") == 0

@@ -72,25 +72,32 @@ def test_epilogue_all_passes(cid, prob, dtype, dist):
     torch.cuda.synchronize()
     ref = oracle.linear_combination(oracle.dgrad(prob, f64(dy), f64(w)), alpha, beta, f64(cx))
     check(f64(dx), ref, dtype, mode, f"{cid} dgrad")
-    # wgrad, rounded to the filter type
-    epi = dict(alpha=alpha, beta=beta, c=gpu(cw))
+    # wgrad, rounded to the filter type, with the bias gradient beside it
+    db = torch.full((prob["K"],), float("nan"), dtype=x.dtype, device=DEV)
+    epi = dict(alpha=alpha, beta=beta, c=gpu(cw), db=db)
     dw = torch.empty_like(gpu(w))
     B.conv2d_wgrad_ex(prob, dtype, gpu(x), gpu(dy), epi, dw, ws_for(B.CONV2D_OP_WGRAD, prob, dtype, epi))
     torch.cuda.synchronize()
     dw_ref = oracle.wgrad(prob, f64(x), f64(dy))
+    db_ref = oracle.bias_grad(prob, f64(dy))
     check(f64(dw), oracle.linear_combination(dw_ref, alpha, beta, f64(cw)), dtype, mode, f"{cid} wgrad")
-    # wgrad kept in fp32, with an fp32 C
+    check(f64(db), db_ref, dtype, mode, f"{cid} db")  # alpha and beta do not apply to db
+    # wgrad kept in fp32, with an fp32 C (and an fp32 db)
     cw32 = gpu(cw).float()
-    epi = dict(alpha=alpha, beta=beta, c=cw32, out_f32=True)
+    db32 = torch.full((prob["K"],), float("nan"), dtype=torch.float32, device=DEV)
+    epi = dict(alpha=alpha, beta=beta, c=cw32, out_f32=True, db=db32)
     dw32 = torch.empty(dw.shape, dtype=torch.float32, device=DEV)
     B.conv2d_wgrad_ex(prob, dtype, gpu(x), gpu(dy), epi, dw32, ws_for(B.CONV2D_OP_WGRAD, prob, dtype, epi))
     torch.cuda.synchronize()
     g = dw32.cpu().numpy().astype(np.float64).reshape(-1)
     r = oracle.linear_combination(dw_ref, alpha, beta, f64(cw)).reshape(-1)
+    gb = db32.cpu().numpy().astype(np.float64)
     if mode == "exact":  # integer partial sums below 2^24: exact in fp32
         assert np.array_equal(g, r), f"{cid} wgrad fp32: {np.count_nonzero(g != r)} differ"
+        assert np.array_equal(gb, db_ref), f"{cid} db fp32"
     else:
         assert np.max(np.abs(g - r)) <= 1e-5 * np.max(np.abs(r)), f"{cid} wgrad fp32"
+        assert np.max(np.abs(gb - db_ref)) <= 1e-5 * np.max(np.abs(db_ref)), f"{cid} db fp32"
 
 
 def test_epilogue_in_place_and_plain():
