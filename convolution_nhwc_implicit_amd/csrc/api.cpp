@@ -356,7 +356,9 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
             int rows, chunks;
             wgrad_band_rows(d, &rows, &chunks);
             pl->split_k = (int)(d.N * chunks);
-            pl->ws_bytes = round_up((size_t)pl->split_k * splitk_stride(d.K * ncols) * sizeof(float), 256);
+            // with the bias gradient each slice also holds the band's K dy column sums
+            const long long per = d.K * ncols + (ep.db ? d.K : 0);
+            pl->ws_bytes = round_up((size_t)pl->split_k * splitk_stride(per) * sizeof(float), 256);
             return CONV2D_OK;
         }
         // default: 128 x 128 tiles when they give the chip at least 16 tiles,
@@ -763,6 +765,7 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         void *dwp = wsb + pl.off_filt;
         const int eo = ep.out_f32 ? 4 : e;  // element size of dw (and C)
         Epi ei = ep;
+        ei.db = nullptr;  // the bias gradient of the padded problem is not the caller's
         if (ep.c) {  // C padded into the padded dw, which the inner pass reads and overwrites
             if (repack(eo, ep.c, d.K * d.R * d.S, d.C, d.C, dwp, Kp * d.R * d.S, Cp, Cp, s) != hipSuccess)
                 return CONV2D_ERR_DEVICE;
@@ -810,15 +813,22 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         b.N = (int)d.N; b.H = (int)d.H; b.W = (int)d.W; b.P = (int)d.P; b.Q = (int)d.Q;
         b.pad_h = (int)d.ph; b.pad_w = (int)d.pw;
         wgrad_band_rows(d, &b.rows_per_wg, &b.chunks_per_img);
-        b.part_stride = splitk_stride(d.K * d.R * d.S * d.C);
+        const long long kcols = d.K * d.R * d.S * d.C;
+        b.with_db = ep.db != nullptr;  // the bias gradient rides along in the slices
+        b.part_stride = splitk_stride(kcols + (b.with_db ? d.K : 0));
         b.xw = (int)(d.Q + d.dw * (d.S - 1));
         b.div_xw = make_fastdiv((uint32_t)b.xw);
         b.steps_per_group = wgrad_band_steps((int)d.Q);
         b.xcd_pairs = (d.N * b.chunks_per_img) % 8 == 0;
         hipError_t e = launch_wgrad_band(dtype, b, s);
         if (e != hipSuccess) return CONV2D_ERR_DEVICE;
+        ReduceEpi rb = re;
+        if (b.with_db) {
+            rb.out2 = ep.db;
+            rb.count1 = kcols;
+        }
         return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,
-                                               d.K * d.R * d.S * d.C, b.part_stride, dw, &re, s));
+                                               kcols + (b.with_db ? d.K : 0), b.part_stride, dw, &rb, s));
     }
 
     WgradArgs a;
@@ -871,17 +881,19 @@ static int make_epi(const conv2d_epilogue_t *e, int op, Epi *ep)
     return CONV2D_OK;
 }
 
-// Workspace of wgrad_ex: the pass's own, then (with db) the bias-gradient
-// partials at the next 256-byte boundary.
+// Workspace of wgrad_ex: the pass's own, then (with db, unless the wgrad band
+// kernel sums dy in its own slices) the bias-gradient partials at the next
+// 256-byte boundary.  *fused tells which.
 static int wgrad_ex_workspace(const conv2d_problem_t *prob, int dtype, const conv2d_algo_t *algo, const Epi &ep,
-                              size_t *pass_bytes, size_t *total)
+                              size_t *pass_bytes, size_t *total, bool *fused)
 {
     Plan pl;
     int st = make_plan(CONV2D_OP_WGRAD, prob, dtype, algo, ep, &pl);
     if (st) return st;
     *pass_bytes = pl.ws_bytes;
     *total = pl.ws_bytes;
-    if (ep.db) {
+    *fused = ep.db && !pl.padded && pl.kernel == 1 && pl.tile == kWgradBandTile;
+    if (ep.db && !*fused) {
         Dims d;
         int splits;
         size_t bws;
@@ -901,7 +913,8 @@ int conv2d_workspace_size_ex(int op, const conv2d_problem_t *prob, int dtype, co
     if (st) return st;
     if (op == CONV2D_OP_WGRAD) {
         size_t pass;
-        return wgrad_ex_workspace(prob, dtype, algo, ep, &pass, bytes);
+        bool fused;
+        return wgrad_ex_workspace(prob, dtype, algo, ep, &pass, bytes, &fused);
     }
     Plan pl;
     st = make_plan(op, prob, dtype, algo, ep, &pl);
@@ -996,13 +1009,17 @@ int conv2d_wgrad_ex(const conv2d_problem_t *prob, int dtype, const void *x, cons
     if (!ep.db) return wgrad_run(prob, dtype, x, dy, ep, dw, workspace, workspace_bytes, algo, stream);
     // with the bias gradient: check everything of both parts before enqueuing either
     size_t pass, total;
-    st = wgrad_ex_workspace(prob, dtype, algo, ep, &pass, &total);
+    bool fused;
+    st = wgrad_ex_workspace(prob, dtype, algo, ep, &pass, &total, &fused);
     if (st) return st;
+    if (fused) return wgrad_run(prob, dtype, x, dy, ep, dw, workspace, workspace_bytes, algo, stream);
     if (!x || !dy || !dw) return CONV2D_ERR_INVALID_ARGUMENT;
     if (!aligned16(x) || !aligned16(dy) || !aligned16(dw)) return CONV2D_ERR_UNSUPPORTED;
     if (workspace_bytes < total) return CONV2D_ERR_WORKSPACE_TOO_SMALL;
     if (!workspace || !aligned16(workspace)) return CONV2D_ERR_INVALID_ARGUMENT;
-    st = wgrad_run(prob, dtype, x, dy, ep, dw, pass ? workspace : nullptr, pass, algo, stream);
+    Epi en = ep;
+    en.db = nullptr;  // the bias gradient runs on its own below
+    st = wgrad_run(prob, dtype, x, dy, en, dw, pass ? workspace : nullptr, pass, algo, stream);
     if (st) return st;
     unsigned char *bws = (unsigned char *)workspace + round_up(pass, 256);
     return conv2d_bias_grad(prob, dtype, dy, ep.db, ep.out_f32 ? 1 : 0, bws, total - round_up(pass, 256), stream);

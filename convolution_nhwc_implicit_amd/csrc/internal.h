@@ -175,6 +175,10 @@ struct ReduceEpi {
     float alpha, beta;
     const void *c;
     int out_f32;
+    // elements [count1, count) go to out2[i - count1] with no alpha/beta/c
+    // (the bias gradient reduced with the weight gradient); count1 % 4 == 0
+    void *out2;
+    long long count1;
 };
 hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long long count,
                                 long long stride, void *out, const ReduceEpi *epi, hipStream_t st);
@@ -213,6 +217,7 @@ struct WgradBandArgs {
     FastDiv div_xw;
     int steps_per_group;  // wgrad_band_steps(Q)
     int xcd_pairs;        // bands a multiple of 8: the two column halves of a band share an XCD
+    int with_db;          // also the band's dy column sums at [K*R*S*C, +K) of its slice
 };
 bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q);
 int wgrad_band_steps(int Q);

@@ -422,31 +422,37 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *parts, 
             t[2] += v[2];
             t[3] += v[3];
         }
-        if (epi.alpha != 1.0f || epi.beta != 0.0f) {
+        // [0, count1) (all of it without out2) -> out with the linear
+        // combination; [count1, count) -> out2 as is
+        const bool second = epi.out2 && i >= epi.count1;
+        const long long base = second ? epi.count1 : 0;
+        const long long end = (epi.out2 && !second) ? epi.count1 : count;
+        if (!second && (epi.alpha != 1.0f || epi.beta != 0.0f)) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float c = 0.0f;
-                if (epi.c && i + j < count)
+                if (epi.c && i + j < end)
                     c = epi.out_f32 ? ((const float *)epi.c)[i + j] : E::to_f32(((const elem *)epi.c)[i + j]);
                 t[j] = epi.alpha * t[j] + epi.beta * c;
             }
         }
+        const long long o0 = i - base, n = end - base;  // o0 % 4 == 0
         if (epi.out_f32) {
-            float *out = (float *)out_;
-            if (i + 4 <= count) {
-                *(f32x4 *)(out + i) = t;
+            float *out = (float *)(second ? epi.out2 : out_);
+            if (o0 + 4 <= n) {
+                *(f32x4 *)(out + o0) = t;
             } else {
-                for (int j = 0; j < 4 && i + j < count; ++j) out[i + j] = t[j];
+                for (int j = 0; j < 4 && o0 + j < n; ++j) out[o0 + j] = t[j];
             }
         } else {
-            elem *out = (elem *)out_;
+            elem *out = (elem *)(second ? epi.out2 : out_);
             elem o[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) o[j] = E::from_f32(t[j]);
-            if (i + 4 <= count) {
-                *(uint2 *)(out + i) = *(const uint2 *)o;
+            if (o0 + 4 <= n) {
+                *(uint2 *)(out + o0) = *(const uint2 *)o;
             } else {
-                for (int j = 0; j < 4 && i + j < count; ++j) out[i + j] = o[j];
+                for (int j = 0; j < 4 && o0 + j < n; ++j) out[o0 + j] = o[j];
             }
         }
     }
@@ -457,7 +463,8 @@ hipError_t launch_splitk_reduce(int dtype, const float *parts, int splits, long 
 {
     if (stride % 4 || stride < count) return hipErrorInvalidValue;
     if (count == 0) return hipSuccess;
-    const ReduceEpi e = epi ? *epi : ReduceEpi{1.0f, 0.0f, nullptr, 0};
+    const ReduceEpi e = epi ? *epi : ReduceEpi{1.0f, 0.0f, nullptr, 0, nullptr, 0};
+    if (e.out2 && (e.count1 % 4 || e.count1 <= 0 || e.count1 >= count)) return hipErrorInvalidValue;
     const bool wide = (count + 63) / 64 < 256 && splits >= 128;  // fewer workgroups than CUs
     const unsigned blocks = (unsigned)(wide ? (count + 15) / 16 : (count + 63) / 64);
     switch (dtype) {

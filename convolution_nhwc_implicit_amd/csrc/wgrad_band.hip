@@ -96,6 +96,27 @@ struct IntC {
 __device__ inline int swz_chunk(int chunk, int v) { return chunk ^ (((v >> 1) & 1) << 2); }
 }  // namespace wb
 
+// acc + (both 16-bit values of the packed pair w), in fp32: a two-element
+// dot product with (1, 1) (exact products, one fp32 accumulation)
+template <class E>
+struct DotOne;
+template <>
+struct DotOne<EF16> {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    __device__ static inline float add(uint32_t w, float acc)
+    {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), h2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+    }
+};
+template <>
+struct DotOne<EBF16> {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    __device__ static inline float add(uint32_t w, float acc)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), b2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+    }
+};
+
 template <class E>
 __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs a)
 {
@@ -215,6 +236,12 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     for (int kb = 0; kb < WAVE_KB; ++kb)
 #pragma unroll
         for (int n = 0; n < WAVE_CB; ++n) acc[kb][n] = f32x16{};
+    // bias gradient (with_db): the first column set of each phase in the
+    // first column half adds up the dy values its fragments hold (every dy
+    // pixel of the band exactly once); lane holds channel 32*kb + l32, the
+    // pixels of half lhi of each step
+    const bool dbw = a.with_db && colh == 0 && wave % WSETS == 0;  // wave-uniform
+    float dbacc[WAVE_KB] = {};
 
     typedef __attribute__((address_space(3))) unsigned char lds_u8;  // 32-bit LDS addresses
     auto tr = [](const lds_u8 *p) -> s16x4 {
@@ -296,6 +323,16 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
                 if (k + 1 < BODY) load_step(f[k + 1], k + 1);
                 __builtin_amdgcn_sched_barrier(0);
                 mma(f[k], 1, NACC);
+                if (dbw) {
+#pragma unroll
+                    for (int kb = 0; kb < WAVE_KB; ++kb)
+#pragma unroll
+                        for (int rd = 0; rd < 2; ++rd) {
+                            const uint2 u = __builtin_bit_cast(uint2, f[k][2 * kb + rd]);
+                            dbacc[kb] = DotOne<E>::add(u.x, dbacc[kb]);
+                            dbacc[kb] = DotOne<E>::add(u.y, dbacc[kb]);
+                        }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -374,6 +411,28 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     if (phase == 1) {
         add(slot(ws_, PARK_HALF), I1{}, I1{});
         store(I1{});
+    }
+    if (a.with_db) {  // uniform: the barriers are reached by every wave
+        // the bias-gradient partial of the band: lanes l32 and l32 + 32 of a
+        // summing wave hold the two pixel halves of a channel; the four
+        // phases' sums are added in phase order through LDS
+        float *dbs = (float *)smem;  // [PHASES][CH]
+        __syncthreads();             // every wave is done with the slots
+        if (dbw) {
+#pragma unroll
+            for (int kb = 0; kb < WAVE_KB; ++kb) {
+                const float v = dbacc[kb] + __shfl_xor(dbacc[kb], 32);
+                if (lhi == 0) dbs[phase * CH + kb * 32 + l32] = v;
+            }
+        }
+        __syncthreads();
+        if (colh == 0 && wave == 0) {
+            constexpr int NCOLS = R * S * CH;
+            float s = dbs[lane];
+#pragma unroll
+            for (int p = 1; p < PHASES; ++p) s += dbs[p * CH + lane];
+            ((float *)a.out)[(size_t)band * a.part_stride + (size_t)CH * NCOLS + lane] = s;
+        }
     }
 }
 

@@ -60,3 +60,22 @@ def test_bias_grad(cid, prob, dtype, dist):
     else:
         assert np.max(np.abs(g - ref)) <= 1e-5 * np.max(np.abs(ref)), f"{cid} db fp32"
     assert torch.equal(run(prob, dtype, dyg), db), f"{cid}: repeat differs"
+
+
+def test_wgrad_with_fused_bias_grad_full_size():
+    """On the benchmark shape the wgrad band kernel sums dy in its own slices:
+    dw stays bit-identical to the plain pass, db matches the oracle."""
+    prob = C3A
+    assert B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")["tile"] == 2  # the wgrad band kernel
+    x = WL.make_x("c3a_resnet3x3").to(DEV)
+    dy = WL.make_dy("c3a_resnet3x3", 56, 56).to(DEV)
+    dw0 = torch.empty((64, 3, 3, 64), dtype=torch.float16, device=DEV)
+    B.conv2d_wgrad(prob, "f16", x, dy, dw0, B.workspace_for(B.CONV2D_OP_WGRAD, prob, "f16", DEV))
+    db = torch.full((64,), float("nan"), dtype=torch.float16, device=DEV)
+    epi = dict(db=db)
+    n = B.conv2d_workspace_size_ex(B.CONV2D_OP_WGRAD, prob, "f16", epi=epi)
+    dw = torch.empty_like(dw0)
+    B.conv2d_wgrad_ex(prob, "f16", x, dy, epi, dw, torch.empty(n, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(dw, dw0), "dw changed by the fused bias gradient"
+    check(f64(db), oracle.bias_grad(prob, f64(dy)), "f16", "tol", "fused db")

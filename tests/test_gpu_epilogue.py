@@ -24,6 +24,10 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("igemm", problem(2, 32, 13, 11, 48, 3, 3, pad=(1, 1), stride=(2, 1)), "f16", "int"),
     ("band_shape", problem(3, 64, 12, 14, 64, 3, 3, pad=(1, 1)), "f16", "int"),
+    # the wgrad band kernel (Q a multiple of 4): the bias gradient is summed
+    # inside it and reduced with the weight gradient
+    ("wband_shape", problem(2, 64, 10, 12, 64, 3, 3, pad=(1, 1)), "bf16", "int"),
+    ("wband_gauss", problem(3, 64, 9, 16, 64, 3, 3, pad=(1, 1)), "f16", "gauss"),
     ("grouped_tiled", problem(2, 32, 11, 9, 48, 3, 3, pad=(1, 1), groups=2), "f16", "int"),
     ("grouped_naive", problem(2, 12, 9, 10, 8, 3, 3, pad=(1, 1), groups=2), "bf16", "int"),
     ("padded_c3_k13", problem(2, 3, 17, 15, 13, 5, 5, pad=(2, 2), stride=(2, 2)), "f16", "int"),
