@@ -374,7 +374,10 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         int s = (algo && algo->split_k) ? algo->split_k : choose_wgrad_splits(tiles, npix, pl->tile == 0 ? 2 : 8);
         if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
         pl->split_k = s;
-        if (s > 1 || wparts) pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * ncols) * sizeof(float), 256);
+        // with the bias gradient, tile 0 carries dy's column sums in its slices
+        const bool gdb = ep.db && pl->tile == 0;
+        if (s > 1 || wparts || gdb)
+            pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * ncols + (gdb ? d.K : 0)) * sizeof(float), 256);
         return CONV2D_OK;
     }
     // the band kernels have no linear-combination epilogue
@@ -850,10 +853,22 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     a.div_C = make_fastdiv((uint32_t)d.C);
     a.div_S = make_fastdiv((uint32_t)d.S);
     a.to_parts = to_parts;
+    a.with_db = ep.db && pl.tile == 0;
+    if (a.with_db) {  // dy's column sums ride along in the slices: always partials
+        a.to_parts = 1;
+        a.out = workspace;
+        a.part_stride = splitk_stride((long long)d.K * a.ncols + d.K);
+    }
     hipError_t e = launch_wgrad(dtype, pl.tile, a, s);
-    if (e != hipSuccess || !reduce) return hip_status(e);
+    if (e != hipSuccess || !(reduce || a.with_db)) return hip_status(e);
+    ReduceEpi rg = re;
+    if (a.with_db) {
+        rg.out2 = ep.db;
+        rg.count1 = (long long)d.K * a.ncols;
+    }
     return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,
-                                           (long long)d.K * a.ncols, a.part_stride, dw, &re, s));
+                                           (long long)d.K * a.ncols + (a.with_db ? d.K : 0), a.part_stride, dw,
+                                           &rg, s));
 }
 
 // conv2d_epilogue_t -> Epi, with its checks (before anything is enqueued)
@@ -892,7 +907,7 @@ static int wgrad_ex_workspace(const conv2d_problem_t *prob, int dtype, const con
     if (st) return st;
     *pass_bytes = pl.ws_bytes;
     *total = pl.ws_bytes;
-    *fused = ep.db && !pl.padded && pl.kernel == 1 && pl.tile == kWgradBandTile;
+    *fused = ep.db && !pl.padded && pl.kernel == 1 && (pl.tile == kWgradBandTile || pl.tile == 0);
     if (ep.db && !*fused) {
         Dims d;
         int splits;

@@ -158,6 +158,21 @@ __device__ inline uint32_t out_pair(float a, float b)
     return p;
 }
 
+// acc + (both 16-bit values of the packed pair w), in fp32: a two-element
+// dot product with (1, 1) (exact products, one fp32 accumulation)
+template <class E>
+struct DotOne {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    __device__ static inline float add(uint32_t w, float acc)
+    {
+        if constexpr (E::kDtype == CONV2D_DTYPE_F16)
+            return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), h2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+        else
+            return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), b2{(__bf16)1.0f, (__bf16)1.0f}, acc,
+                                                   false);
+    }
+};
 // Float epilogue value: acc + bias, then ReLU (v <= 0, including -0, -> +0).
 __device__ inline float bias_relu_f32(float v, float b, int relu)
 {

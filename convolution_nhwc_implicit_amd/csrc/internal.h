@@ -163,6 +163,7 @@ struct WgradArgs {
     long long part_stride;  // elements between consecutive slices' partials
     FastDiv div_Q, div_PQ, div_C, div_S;
     int to_parts;           // fp32 partials even for one split
+    int with_db;            // wgrad_kernel (tile 0): also dy's column sums at [K*ncols, +K) of each slice
 };
 
 int wgrad_num_tiles();

@@ -154,6 +154,11 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    // bias gradient (with_db): the waves of the first column tile's left
+    // half add up the dy values their fragments hold (every dy element of
+    // the slice once); lane holds channel wm*64 + 32*i + l%32
+    const bool dbw = a.with_db && nt == 0 && wn == 0;  // wave-uniform
+    float dbacc[2] = {0.0f, 0.0f};
 
 #pragma unroll
     for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
@@ -179,6 +184,22 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) acc[i][j] = Mfma32x16<E>::run(fa[i], fb[j], acc[i][j]);
+            if (dbw) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) dbacc[i] = DotOne<E>::add(fa[i][q], dbacc[i]);
+            }
+        }
+    }
+    if (dbw) {
+        // lanes l and l + 32 hold the two pixel halves of a channel
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+            const int kk = mt * BM + wm * 64 + 32 * i + lane;
+            if (lane < 32 && kk < a.K)
+                ((float *)a.out)[(size_t)z * a.part_stride + (size_t)a.K * a.ncols + kk] = v;
         }
     }
 

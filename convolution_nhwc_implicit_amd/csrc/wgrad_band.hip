@@ -96,26 +96,6 @@ struct IntC {
 __device__ inline int swz_chunk(int chunk, int v) { return chunk ^ (((v >> 1) & 1) << 2); }
 }  // namespace wb
 
-// acc + (both 16-bit values of the packed pair w), in fp32: a two-element
-// dot product with (1, 1) (exact products, one fp32 accumulation)
-template <class E>
-struct DotOne;
-template <>
-struct DotOne<EF16> {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    __device__ static inline float add(uint32_t w, float acc)
-    {
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), h2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
-    }
-};
-template <>
-struct DotOne<EBF16> {
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    __device__ static inline float add(uint32_t w, float acc)
-    {
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), b2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
-    }
-};
 
 template <class E>
 __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs a)

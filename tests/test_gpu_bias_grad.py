@@ -79,3 +79,30 @@ def test_wgrad_with_fused_bias_grad_full_size():
     torch.cuda.synchronize()
     assert torch.equal(dw, dw0), "dw changed by the fused bias gradient"
     check(f64(db), oracle.bias_grad(prob, f64(dy)), "f16", "tol", "fused db")
+
+
+@pytest.mark.parametrize("prob", [
+    problem(2, 64, 10, 12, 64, 3, 3, pad=(1, 1)),                       # all three wgrad kernels
+    problem(3, 32, 11, 9, 136, 5, 3, pad=(2, 1), stride=(2, 1), dil=(1, 2)),
+], ids=["wband_shape", "strided"])
+def test_wgrad_db_every_tile(prob):
+    """db beside wgrad on every wgrad kernel (fused into the 128x128 and band
+    kernels, a second launch after the 64x64 one): dw is bit-identical to the
+    plain pass of the same tile, db equals the oracle's (integer data)."""
+    P, Q = oracle.output_hw(prob)
+    x, _, _, dy = WL.random_case(prob, "f16", "int", zlib.crc32(b"db-tiles"), P, Q, bias=False)
+    x, dy = x.to(DEV), dy.to(DEV)
+    ref = oracle.bias_grad(prob, f64(dy))
+    wshape = (prob["K"], prob["R"], prob["S"], prob["C"])
+    for t in range(1, B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")["num_tiles"] + 1):
+        algo = dict(tile=t)
+        dw0 = torch.empty(wshape, dtype=torch.float16, device=DEV)
+        B.conv2d_wgrad(prob, "f16", x, dy, dw0, B.workspace_for(B.CONV2D_OP_WGRAD, prob, "f16", DEV, algo), algo)
+        db = torch.full((prob["K"],), float("nan"), dtype=torch.float16, device=DEV)
+        epi = dict(db=db)
+        n = B.conv2d_workspace_size_ex(B.CONV2D_OP_WGRAD, prob, "f16", algo=algo, epi=epi)
+        dw = torch.empty_like(dw0)
+        B.conv2d_wgrad_ex(prob, "f16", x, dy, epi, dw, torch.empty(max(n, 1), dtype=torch.uint8, device=DEV), algo)
+        torch.cuda.synchronize()
+        assert torch.equal(dw, dw0), f"tile {t}: dw changed"
+        check(f64(db), ref, "f16", "exact", f"tile {t} db")
