@@ -87,8 +87,8 @@ def flops(prob, P, Q):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the data-parallel sharding across GPUs is described, not built)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(data-parallel sharding across GPUs is a design, not an implementation)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
