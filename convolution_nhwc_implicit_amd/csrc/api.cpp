@@ -302,7 +302,10 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     const int vec = dtype == CONV2D_DTYPE_I8 ? 16 : 8;
     if (d.G == 1 && (d.C % vec || d.K % vec)) return plan_padded(op, prob, dtype, algo, ep, vec, pl);
 
-    if (d.G > 1) {
+    // grouped fprop whose channels per group come in 128-bit chunks: the
+    // implicit GEMM, one GEMM per group (grid.y = groups x N tiles)
+    const bool grouped_gemm = d.G > 1 && op == CONV2D_OP_FPROP && d.Cg % vec == 0 && d.Kg % vec == 0;
+    if (d.G > 1 && !grouped_gemm) {
         // tile 0: one thread per output; tile 1: the depthwise kernels
         // (groups = C = K) or the LDS-tiled dot-product kernels (16-bit
         // types, channel counts in 16-byte vectors, staging fits LDS)
@@ -388,7 +391,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     if (op == CONV2D_OP_FPROP) {
         pl->tile = (algo && algo->tile) ? algo->tile - 1
                    : band             ? kBandTile
-                                      : choose_igemm_tile(d.N * d.P * d.Q, d.K);
+                                      : choose_igemm_tile(d.N * d.P * d.Q, d.Kg);
         return CONV2D_OK;
     }
     // dgrad
@@ -601,9 +604,10 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     IgemmArgs a;
     memset(&a, 0, sizeof(a));
     a.src = x; a.bmat = w; a.bias = bias; a.dst = y;
-    a.b_elems = d.K * d.R * d.S * d.C;
+    a.b_elems = d.K * d.R * d.S * d.Cg;
     a.nimg = (int)d.N; a.hs = (int)d.H; a.ws = (int)d.W; a.cs = (int)d.C;
     a.ngemm = (int)d.K;
+    a.cg = (int)d.Cg; a.kg = (int)d.Kg;
     a.ho = (int)d.P; a.wo = (int)d.Q; a.osh = 1; a.osw = 1;
     a.gsh = (int)d.sh; a.gsw = (int)d.sw;
     a.relu = relu; a.requant_m = m;
@@ -613,13 +617,13 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     ph.mi = (int)d.P; ph.mj = (int)d.Q; ph.oh0 = 0; ph.ow0 = 0;
     ph.th0 = -(int)d.ph; ph.tw0 = -(int)d.pw; ph.tdh = (int)d.dh; ph.tdw = (int)d.dw;
     ph.ntr = (int)d.R; ph.nts = (int)d.S;
-    ph.kgemm = (int)(d.R * d.S * d.C);
+    ph.kgemm = (int)(d.R * d.S * d.Cg);
     ph.m_total = (uint32_t)(d.N * d.P * d.Q);
     ph.b_off = 0;
     fill_phase_common(ph, pl.tile);
     TileShape ts = igemm_tile_shape(pl.tile);
-    const int gn = (int)((d.K + ts.bn - 1) / ts.bn);
-    return hip_status(launch_igemm(dtype, pl.tile, a, ph.tiles_m, gn, s));
+    a.ntiles_g = (int)((d.Kg + ts.bn - 1) / ts.bn);
+    return hip_status(launch_igemm(dtype, pl.tile, a, ph.tiles_m, (int)d.G * a.ntiles_g, s));
 }
 
 static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, const void *w, const Epi &ep,
@@ -694,6 +698,7 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
     a.b_elems = d.R * d.S * d.C * d.K;
     a.nimg = (int)d.N; a.hs = (int)d.P; a.ws = (int)d.Q; a.cs = (int)d.K;
     a.ngemm = (int)d.C;
+    a.cg = (int)d.K; a.kg = (int)d.C;  // dense
     a.ho = (int)d.H; a.wo = (int)d.W; a.osh = (int)d.sh; a.osw = (int)d.sw;
     a.gsh = 1; a.gsw = 1;
     a.relu = 0;
@@ -730,6 +735,7 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
     if (e != hipSuccess) return CONV2D_ERR_DEVICE;
     TileShape ts = igemm_tile_shape(pl.tile);
     const int gn = (int)((d.C + ts.bn - 1) / ts.bn);
+    a.ntiles_g = gn;
     return hip_status(launch_igemm(dtype, pl.tile, a, max_tiles, gn, s));
 }
 

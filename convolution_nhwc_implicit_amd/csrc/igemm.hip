@@ -72,7 +72,11 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     const Phase &ph = a.ph[blockIdx.z];
     const int mt = blockIdx.x;
     if (mt >= ph.tiles_m) return;
-    const int nt = blockIdx.y;
+    // N tile ntl of group gi: output channels gi*kg + ntl*BN + (0..BN-1), of
+    // which the first kg - ntl*BN exist
+    const int gi = blockIdx.y / a.ntiles_g, ntl = blockIdx.y - gi * a.ntiles_g;
+    const int ncol0 = gi * a.kg + ntl * BN;       // first output channel of the tile
+    const int nvalid = min(BN, a.kg - ntl * BN);  // channels of the tile in the group
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,15 +122,15 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     long long b_row[B_BLK];
 #pragma unroll
     for (int t = 0; t < B_BLK; ++t) {
-        const int n = nt * BN + RB * (wave + 4 * t) + brow;
-        b_row[t] = n < a.ngemm ? ph.b_off + (long long)n * ph.kgemm : -1;
+        const int nl = RB * (wave + 4 * t) + brow;
+        b_row[t] = nl < nvalid ? ph.b_off + (long long)(ncol0 + nl) * ph.kgemm : -1;
     }
 
     // ---- GEMM-K position of this lane's chunk: (tap tr, tap ts, channel c)
     int c = kc * EPC, tr = 0, ts = 0, kk = kc * EPC;
     auto normalize = [&]() {
-        while (c >= cs) {
-            c -= cs;
+        while (c >= a.cg) {
+            c -= a.cg;
             if (++ts == ph.nts) {
                 ts = 0;
                 ++tr;
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
             const int h = a_ih[t] + tr * ph.tdh;
             const int w = a_iw[t] + ts * ph.tdw;
             const bool ok = kval && (unsigned)h < (unsigned)hs && (unsigned)w < (unsigned)ws;
-            const uint32_t voff = ok ? ((a_img[t] + (uint32_t)(h * ws + w)) * (uint32_t)cs + (uint32_t)c) * sizeof(elem)
+            const uint32_t voff = ok ? ((a_img[t] + (uint32_t)(h * ws + w)) * (uint32_t)cs + (uint32_t)(gi * a.cg + c)) * sizeof(elem)
                                      : kBufOOBFar;
             dma16(a_rs, base + (wave + 4 * t) * 1024, voff);
         }
@@ -227,8 +231,8 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int col = wn * WTN + j * 16 + cq;
-        const int n = nt * BN + col;
-        const bool nok = n < a.ngemm;
+        const int n = ncol0 + col;
+        const bool nok = col < nvalid;
         if constexpr (E::kDtype == CONV2D_DTYPE_I8) {
             int b[4];
 #pragma unroll
@@ -290,9 +294,8 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     for (int id = tid; id < BM * OCH; id += NT) {
         const int row = id / OCH, cc = id % OCH;
         const uint32_t m = (uint32_t)mt * BM + row;
-        const int n0 = nt * BN + cc * EPO;
-        if (m >= ph.m_total || n0 >= a.ngemm) continue;
-        *(u32x4 *)(dst + out_offset(m) + n0) = *(const u32x4 *)(smem + row * CROWB + cc * 16);
+        if (m >= ph.m_total || cc * EPO >= nvalid) continue;
+        *(u32x4 *)(dst + out_offset(m) + ncol0 + cc * EPO) = *(const u32x4 *)(smem + row * CROWB + cc * 16);
     }
 }
 

@@ -79,8 +79,12 @@ struct IgemmArgs {
     long long b_elems; // elements of bmat (all phases)
     const void *bias;  // [ngemm]; element type (float paths) or int32 (int8)
     void *dst;
-    int nimg, hs, ws, cs;  // source image
+    int nimg, hs, ws, cs;  // source image (cs: channels per pixel)
     int ngemm;
+    // groups (fprop): GEMM-K runs over cg channels per tap starting at
+    // g*cg, GEMM-N over kg output channels starting at g*kg; grid.y =
+    // groups * ntiles_g.  Dense: cg = cs, kg = ngemm, ntiles_g = grid.y.
+    int cg, kg, ntiles_g;
     int ho, wo;            // full output image extent
     int osh, osw;          // output step of the sub-grid
     int gsh, gsw;          // source step per sub-grid step

@@ -135,6 +135,7 @@ INT8_CASES = [
     ("i8_norelu", problem(2, 16, 9, 9, 32, 3, 3, pad=(1, 1), stride=(2, 2)), True, False),
     ("i8_nobias", problem(1, 64, 8, 7, 16, 1, 1), False, True),
     ("i8_grouped", problem(2, 16, 7, 7, 16, 3, 3, pad=(1, 1), groups=4), True, True),
+    ("i8_grouped_gemm", problem(2, 64, 9, 8, 96, 3, 3, pad=(1, 1), stride=(2, 1), groups=2), True, True),
     ("i8_pad_c3", problem(2, 3, 12, 12, 16, 3, 3, pad=(1, 1)), True, True),
     ("i8_pad_k20", problem(2, 32, 9, 8, 20, 3, 3, pad=(1, 1)), True, False),
     # 3x3 stride-1 int8 with 128 channels runs the band kernel: ragged row
@@ -227,17 +228,23 @@ def test_wgrad_band_and_generic_agree():
     problem(3, 64, 14, 13, 96, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2), groups=4),
 ], ids=["g2", "c4g_like"])
 def test_grouped_every_tile(prob):
-    """Both direct kernels (one thread per output, LDS-tiled) against the oracle."""
+    """Grouped problems whose channels per group come in 16-byte chunks: fprop
+    on every implicit-GEMM tile (one GEMM per group), dgrad and wgrad on both
+    direct kernels (one thread per output, LDS-tiled), against the oracle."""
     x, w, b, dy = case_inputs(prob, "f16", "int", seed=50)
     ref_y = oracle_fprop_out(prob, "f16", x, w, b, True)
     ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
     ref_dw = oracle.wgrad(prob, f64(x), f64(dy))
-    for op in (B.CONV2D_OP_FPROP, B.CONV2D_OP_DGRAD, B.CONV2D_OP_WGRAD):
+    info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")
+    assert info["kernel"] == 1 and info["num_tiles"] == 5
+    for op in (B.CONV2D_OP_DGRAD, B.CONV2D_OP_WGRAD):
         info = B.conv2d_plan_info(op, prob, "f16")
         assert info["kernel"] == 2 and info["num_tiles"] == 2 and info["tile"] == 1
-    for t in (1, 2):
+    for t in range(1, 6):
         algo = dict(tile=t)
         check(f64(run_fprop(prob, "f16", x, w, b, True, algo=algo)), ref_y, "f16", "exact", f"tile {t}")
+    for t in (1, 2):
+        algo = dict(tile=t)
         check(f64(run_dgrad(prob, "f16", dy, w, algo=algo)), ref_dx, "f16", "exact", f"dgrad tile {t}")
         check(f64(run_wgrad(prob, "f16", x, dy, algo=algo)), ref_dw, "f16", "exact", f"wgrad tile {t}")
 
