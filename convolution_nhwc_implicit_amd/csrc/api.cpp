@@ -304,7 +304,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
 
     // grouped fprop whose channels per group come in 128-bit chunks: the
     // implicit GEMM, one GEMM per group (grid.y = groups x N tiles)
-    const bool grouped_gemm = d.G > 1 && op == CONV2D_OP_FPROP && d.Cg % vec == 0 && d.Kg % vec == 0;
+    const bool grouped_gemm = d.G > 1 && op != CONV2D_OP_WGRAD && d.Cg % vec == 0 && d.Kg % vec == 0;
     if (d.G > 1 && !grouped_gemm) {
         // tile 0: one thread per output; tile 1: the depthwise kernels
         // (groups = C = K) or the LDS-tiled dot-product kernels (16-bit
@@ -399,9 +399,9 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     pl->phases = (int)(d.sh * d.sw);
     pl->tile = (algo && algo->tile) ? algo->tile - 1
                : band             ? kBandTile
-                                  : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.C);
+                                  : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.Cg);
     // the band kernel reads the filter as it is; the others take a re-laid-out copy
-    pl->ws_bytes = pl->tile == kBandTile ? 0 : round_up((size_t)d.R * d.S * d.C * d.K * elem_size(dtype), 256);
+    pl->ws_bytes = pl->tile == kBandTile ? 0 : round_up((size_t)d.R * d.S * d.C * d.Kg * elem_size(dtype), 256);
     return CONV2D_OK;
 }
 
@@ -692,13 +692,14 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
     memset(&pa, 0, sizeof(pa));
     pa.w = w; pa.wt = workspace;
     pa.K = (int)d.K; pa.R = (int)d.R; pa.S = (int)d.S; pa.C = (int)d.C;
+    pa.Kg = (int)d.Kg; pa.Cg = (int)d.Cg;
     IgemmArgs a;
     memset(&a, 0, sizeof(a));
     a.src = dy; a.bmat = workspace; a.bias = nullptr; a.dst = dx;
-    a.b_elems = d.R * d.S * d.C * d.K;
+    a.b_elems = d.R * d.S * d.C * d.Kg;
     a.nimg = (int)d.N; a.hs = (int)d.P; a.ws = (int)d.Q; a.cs = (int)d.K;
     a.ngemm = (int)d.C;
-    a.cg = (int)d.K; a.kg = (int)d.C;  // dense
+    a.cg = (int)d.Kg; a.kg = (int)d.Cg;  // one GEMM per group: Kg dy channels in, Cg dx channels out
     a.ho = (int)d.H; a.wo = (int)d.W; a.osh = (int)d.sh; a.osw = (int)d.sw;
     a.gsh = 1; a.gsw = 1;
     a.relu = 0;
@@ -714,7 +715,7 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
             ph.mi = ay.extent; ph.mj = ax.extent; ph.oh0 = py; ph.ow0 = px;
             ph.th0 = ay.o0; ph.tw0 = ax.o0; ph.tdh = ay.dstep; ph.tdw = ax.dstep;
             ph.ntr = ay.ntap; ph.nts = ax.ntap;
-            ph.kgemm = (int)(ay.ntap * ax.ntap * d.K);
+            ph.kgemm = (int)(ay.ntap * ax.ntap * d.Kg);
             ph.m_total = (uint32_t)(d.N * ay.extent * ax.extent);
             ph.b_off = off;
             fill_phase_common(ph, pl.tile);
@@ -723,7 +724,7 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
             pp.r0 = ay.r0; pp.rstep = ay.step; pp.ntr = ay.ntap;
             pp.s0 = ax.r0; pp.sstep = ax.step; pp.nts = ax.ntap;
             pp.off = off;
-            const long long elems = d.C * ay.ntap * ax.ntap * d.K;
+            const long long elems = d.C * ay.ntap * ax.ntap * d.Kg;
             pa.max_elems = (int)std::max<long long>(pa.max_elems, elems);
             off += elems;
             ++nph;
@@ -734,9 +735,8 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
     hipError_t e = launch_dgrad_prep(dtype, pa, s);
     if (e != hipSuccess) return CONV2D_ERR_DEVICE;
     TileShape ts = igemm_tile_shape(pl.tile);
-    const int gn = (int)((d.C + ts.bn - 1) / ts.bn);
-    a.ntiles_g = gn;
-    return hip_status(launch_igemm(dtype, pl.tile, a, max_tiles, gn, s));
+    a.ntiles_g = (int)((d.Cg + ts.bn - 1) / ts.bn);
+    return hip_status(launch_igemm(dtype, pl.tile, a, max_tiles, (int)d.G * a.ntiles_g, s));
 }
 
 static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, const void *dy, const Epi &ep,

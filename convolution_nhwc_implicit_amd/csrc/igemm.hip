@@ -339,24 +339,26 @@ hipError_t launch_igemm(int dtype, int tile, const IgemmArgs &a, int grid_m, int
 
 // ---------------------------------------------------------------------------
 // dgrad filter re-layout: for each stride phase, wt[c][tap][k] =
-// w[k][r0 + jr*rstep][s0 + js*sstep][c] with tap = jr*nts + js.
+// w[g*Kg + k][r0 + jr*rstep][s0 + js*sstep][c - g*Cg] with tap = jr*nts + js
+// and g = c / Cg the dx channel's group (one group: w[k][r][s][c]).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void dgrad_prep_kernel(const PrepArgs a)
 {
     const PrepPhase &p = a.ph[blockIdx.y];
     const int ntap = p.ntr * p.nts;
-    const int total = a.C * ntap * a.K;
+    const int total = a.C * ntap * a.Kg;
     const T *w = (const T *)a.w;
     T *wt = (T *)a.wt + p.off;
     for (int idx = blockIdx.x * 256 + threadIdx.x; idx < total; idx += gridDim.x * 256) {
-        const int k = idx % a.K;
-        const int t = idx / a.K;
+        const int k = idx % a.Kg;  // dy channel within the group
+        const int t = idx / a.Kg;
         const int tap = t % ntap;
-        const int c = t / ntap;
+        const int c = t / ntap;    // dx channel
+        const int g = c / a.Cg;
         const int r = p.r0 + (tap / p.nts) * p.rstep;
         const int s = p.s0 + (tap % p.nts) * p.sstep;
-        wt[idx] = w[(((size_t)k * a.R + r) * a.S + s) * a.C + c];
+        wt[idx] = w[((((size_t)g * a.Kg + k) * a.R + r) * a.S + s) * a.Cg + (c - g * a.Cg)];
     }
 }
 

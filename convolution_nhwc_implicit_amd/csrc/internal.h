@@ -130,8 +130,9 @@ bool band_supported(int dtype, int R, int S, int cin, int dil);
 hipError_t launch_band(int dtype, int R, int S, int cin, int dil, const BandArgs &a, int grid_n, int grid_q,
                        hipStream_t st);
 
-// Re-lays the filter w[K][R][S][C] out as one dense [C][taps*K] matrix per
-// dgrad stride phase (taps of the phase in (jr, js) order, K innermost).
+// Re-lays the filter w[K][R][S][C/G] out as one [C][taps*K/G] matrix per
+// dgrad stride phase (taps of the phase in (jr, js) order, the dx channel's
+// group's dy channels innermost).
 struct PrepPhase {
     int r0, rstep, ntr;
     int s0, sstep, nts;
@@ -141,6 +142,7 @@ struct PrepArgs {
     const void *w;
     void *wt;
     int K, R, S, C;
+    int Kg, Cg;     // per group (dense: K, C); dx channel c reads the Kg dy channels of its group
     int nphases;
     int max_elems;  // largest C*ntr*nts*K over phases
     PrepPhase ph[kMaxPhases];

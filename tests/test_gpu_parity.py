@@ -229,23 +229,25 @@ def test_wgrad_band_and_generic_agree():
 ], ids=["g2", "c4g_like"])
 def test_grouped_every_tile(prob):
     """Grouped problems whose channels per group come in 16-byte chunks: fprop
-    on every implicit-GEMM tile (one GEMM per group), dgrad and wgrad on both
-    direct kernels (one thread per output, LDS-tiled), against the oracle."""
+    and dgrad (every stride phase) on every implicit-GEMM tile, one GEMM per
+    group; wgrad on both direct kernels (one thread per output, LDS-tiled);
+    against the oracle."""
     x, w, b, dy = case_inputs(prob, "f16", "int", seed=50)
     ref_y = oracle_fprop_out(prob, "f16", x, w, b, True)
     ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
     ref_dw = oracle.wgrad(prob, f64(x), f64(dy))
-    info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")
-    assert info["kernel"] == 1 and info["num_tiles"] == 5
-    for op in (B.CONV2D_OP_DGRAD, B.CONV2D_OP_WGRAD):
+    for op in (B.CONV2D_OP_FPROP, B.CONV2D_OP_DGRAD):
         info = B.conv2d_plan_info(op, prob, "f16")
-        assert info["kernel"] == 2 and info["num_tiles"] == 2 and info["tile"] == 1
+        assert info["kernel"] == 1 and info["num_tiles"] == 5
+    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
+    assert info["kernel"] == 2 and info["num_tiles"] == 2 and info["tile"] == 1
     for t in range(1, 6):
         algo = dict(tile=t)
         check(f64(run_fprop(prob, "f16", x, w, b, True, algo=algo)), ref_y, "f16", "exact", f"tile {t}")
+        check(f64(run_dgrad(prob, "f16", dy, w, algo=algo, fill=float("nan"))), ref_dx, "f16", "exact",
+              f"dgrad tile {t}")
     for t in (1, 2):
         algo = dict(tile=t)
-        check(f64(run_dgrad(prob, "f16", dy, w, algo=algo)), ref_dx, "f16", "exact", f"dgrad tile {t}")
         check(f64(run_wgrad(prob, "f16", x, dy, algo=algo)), ref_dw, "f16", "exact", f"wgrad tile {t}")
 
 
