@@ -304,7 +304,8 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
 
     // grouped fprop whose channels per group come in 128-bit chunks: the
     // implicit GEMM, one GEMM per group (grid.y = groups x N tiles)
-    const bool grouped_gemm = d.G > 1 && op != CONV2D_OP_WGRAD && d.Cg % vec == 0 && d.Kg % vec == 0;
+    const bool grouped_gemm = d.G > 1 && d.Cg % vec == 0 && d.Kg % vec == 0 &&
+                              (op != CONV2D_OP_WGRAD || dtype != CONV2D_DTYPE_I8);
     if (d.G > 1 && !grouped_gemm) {
         // tile 0: one thread per output; tile 1: the depthwise kernels
         // (groups = C = K) or the LDS-tiled dot-product kernels (16-bit
@@ -353,7 +354,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         // default: the band kernel when it applies and no split count is forced
         const bool use_band = algo && algo->tile ? algo->tile - 1 == kWgradBandTile
                                                   : wband && !(algo && algo->split_k);
-        const long long ncols = d.R * d.S * d.C;
+        const long long ncols = d.R * d.S * d.Cg;  // per group
         if (use_band) {
             pl->tile = kWgradBandTile;
             int rows, chunks;
@@ -368,11 +369,11 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         // else the 64 x 64 kernel, whose extra tiles need fewer slices (and
         // fewer fp32 partials) on small problems
         const TileShape big = wgrad_tile_shape(0);
-        const long long big_tiles = ((d.K + big.bm - 1) / big.bm) * ((ncols + big.bn - 1) / big.bn);
+        const long long big_tiles = d.G * ((d.Kg + big.bm - 1) / big.bm) * ((ncols + big.bn - 1) / big.bn);
         pl->tile = (algo && algo->tile) ? algo->tile - 1 : (big_tiles >= 16 ? 0 : 1);
         if (pl->tile == kWgradBandTile) return CONV2D_ERR_UNSUPPORTED;
         TileShape ts = wgrad_tile_shape(pl->tile);
-        const long long tiles = ((d.K + ts.bm - 1) / ts.bm) * ((ncols + ts.bn - 1) / ts.bn);
+        const long long tiles = d.G * ((d.Kg + ts.bm - 1) / ts.bm) * ((ncols + ts.bn - 1) / ts.bn);
         const long long npix = d.N * d.P * d.Q;
         int s = (algo && algo->split_k) ? algo->split_k : choose_wgrad_splits(tiles, npix, pl->tile == 0 ? 2 : 8);
         if (s > 65535) return CONV2D_ERR_UNSUPPORTED;
@@ -847,7 +848,9 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     a.R = (int)d.R; a.S = (int)d.S; a.P = (int)d.P; a.Q = (int)d.Q;
     a.pad_h = (int)d.ph; a.pad_w = (int)d.pw; a.sh = (int)d.sh; a.sw = (int)d.sw;
     a.dh = (int)d.dh; a.dw = (int)d.dw;
-    a.ncols = (int)(d.R * d.S * d.C);
+    a.ncols = (int)(d.R * d.S * d.Cg);  // per group
+    a.Kg = (int)d.Kg; a.Cg = (int)d.Cg;
+    a.mtiles_g = (int)((d.Kg + wgrad_tile_shape(pl.tile).bm - 1) / wgrad_tile_shape(pl.tile).bm);
     a.npix = npix;
     // slices are whole main-loop steps
     const uint32_t steps = (npix + kWgradPixStep - 1) / kWgradPixStep;
@@ -856,7 +859,7 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     a.part_stride = splitk_stride((long long)d.K * a.ncols);
     a.div_Q = make_fastdiv((uint32_t)d.Q);
     a.div_PQ = make_fastdiv((uint32_t)(d.P * d.Q));
-    a.div_C = make_fastdiv((uint32_t)d.C);
+    a.div_C = make_fastdiv((uint32_t)d.Cg);
     a.div_S = make_fastdiv((uint32_t)d.S);
     a.to_parts = to_parts;
     a.with_db = ep.db && pl.tile == 0;

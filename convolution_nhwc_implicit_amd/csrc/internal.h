@@ -170,6 +170,10 @@ struct WgradArgs {
     FastDiv div_Q, div_PQ, div_C, div_S;
     int to_parts;           // fp32 partials even for one split
     int with_db;            // wgrad_kernel (tile 0): also dy's column sums at [K*ncols, +K) of each slice
+    // groups: one GEMM per group, rows g*Kg + (0..Kg-1), columns (r, s, c')
+    // over the group's Cg channels (ncols = R*S*Cg, div_C divides by Cg);
+    // grid.x = groups * mtiles_g.  Dense: Kg = K, Cg = C.
+    int Kg, Cg, mtiles_g;
 };
 
 int wgrad_num_tiles();

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE * STAGE];
 
-    const int mt = blockIdx.x, nt = blockIdx.y, z = blockIdx.z;
+    const int nt = blockIdx.y, z = blockIdx.z;
+    const int gi = blockIdx.x / a.mtiles_g, mt = blockIdx.x - gi * a.mtiles_g;  // group, row tile in it
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -83,14 +84,15 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
     const uint32_t lds0 = lds_addr(smem);
     const u32x4 dy_rs = make_buf_rsrc(a.dy, (uint32_t)((size_t)a.npix * a.K * sizeof(elem)));
     const u32x4 x_rs = make_buf_rsrc(a.x, (uint32_t)((size_t)a.N * a.H * a.W * a.C * sizeof(elem)));
-    // dy: channel k of this lane's chunk (whole chunk valid or not, K % 8 == 0)
-    const int k = mt * BM + 8 * lc;
-    const bool kval = k < a.K;
-    // x: column (tap, channel) of this lane's chunk
+    // dy: channel k of this lane's chunk (whole chunk valid or not, Kg % 8 == 0)
+    const int kl = mt * BM + 8 * lc;  // within the group
+    const bool kval = kl < a.Kg;
+    const int k = gi * a.Kg + kl;
+    // x: column (tap, channel of the group) of this lane's chunk
     const int col = nt * BN + 8 * lc;
     const bool cval = col < a.ncols;
     const uint32_t tap = fdiv((uint32_t)(cval ? col : 0), a.div_C);
-    const int cch = (cval ? col : 0) - (int)tap * a.C;
+    const int cch = gi * a.Cg + (cval ? col : 0) - (int)tap * a.Cg;
     const uint32_t tr = fdiv(tap, a.div_S);
     const int hoff = (int)tr * a.dh - a.pad_h;
     const int woff = ((int)tap - (int)tr * a.S) * a.dw - a.pad_w;
@@ -197,9 +199,9 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
-            const int kk = mt * BM + wm * 64 + 32 * i + lane;
-            if (lane < 32 && kk < a.K)
-                ((float *)a.out)[(size_t)z * a.part_stride + (size_t)a.K * a.ncols + kk] = v;
+            const int kl2 = mt * BM + wm * 64 + 32 * i + lane;
+            if (lane < 32 && kl2 < a.Kg)
+                ((float *)a.out)[(size_t)z * a.part_stride + (size_t)a.K * a.ncols + gi * a.Kg + kl2] = v;
         }
     }
 
@@ -212,8 +214,9 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
             if (c >= a.ncols) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int kk = mt * BM + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (kk >= a.K) continue;
+                const int kl2 = mt * BM + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (kl2 >= a.Kg) continue;
+                const int kk = gi * a.Kg + kl2;
                 if (a.splits == 1 && !a.to_parts)
                     ((elem *)a.out)[(size_t)kk * a.ncols + c] = E::from_f32(acc[i][j][e]);
                 else
@@ -243,19 +246,20 @@ __global__ __launch_bounds__(256) void wgrad_interleave_kernel(const WgradArgs a
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
 
-    const int mt = blockIdx.x, nt = blockIdx.y, z = blockIdx.z;
+    const int nt = blockIdx.y, z = blockIdx.z;
+    const int gi = blockIdx.x / a.mtiles_g, mt = blockIdx.x - gi * a.mtiles_g;  // group, row tile in it
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int pp = tid % PAIRS, ch = tid / PAIRS;
 
-    // this thread's dy chunk: channels k0..k0+7
-    const int k0 = mt * BM + ch * 8;
-    const bool kval = k0 < a.K;
-    // this thread's x chunk: columns col0..col0+7, all in one tap (C % 8 == 0)
+    // this thread's dy chunk: channels k0..k0+7 (of the group's Kg)
+    const int k0 = gi * a.Kg + mt * BM + ch * 8;
+    const bool kval = mt * BM + ch * 8 < a.Kg;
+    // this thread's x chunk: columns col0..col0+7, all in one tap (Cg % 8 == 0)
     const int col0 = nt * BN + ch * 8;
     const bool cval = col0 < a.ncols;
     const uint32_t tap = fdiv((uint32_t)(cval ? col0 : 0), a.div_C);
-    const int cch = (cval ? col0 : 0) - (int)tap * a.C;
+    const int cch = gi * a.Cg + (cval ? col0 : 0) - (int)tap * a.Cg;
     const uint32_t tr = fdiv(tap, a.div_S);
     const int ts = (int)tap - (int)tr * a.S;
     const int hoff = (int)tr * a.dh - a.pad_h;
@@ -346,8 +350,9 @@ __global__ __launch_bounds__(256) void wgrad_interleave_kernel(const WgradArgs a
             if (col >= a.ncols) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int k = mt * BM + wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-                if (k >= a.K) continue;
+                const int kl = mt * BM + wm * WTM + i * 16 + (lane >> 4) * 4 + r;
+                if (kl >= a.Kg) continue;
+                const int k = gi * a.Kg + kl;
                 if (a.splits == 1 && !a.to_parts)
                     ((elem *)a.out)[(size_t)k * a.ncols + col] = E::from_f32(acc[i][j][r]);
                 else
@@ -368,7 +373,8 @@ hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st)
 {
     if (tile < 0 || tile >= wgrad_num_tiles()) return hipErrorInvalidValue;
     const TileShape ts = wgrad_tile_shape(tile);
-    dim3 grid((unsigned)((a.K + ts.bm - 1) / ts.bm), (unsigned)((a.ncols + ts.bn - 1) / ts.bn), (unsigned)a.splits);
+    if (a.mtiles_g != (a.Kg + ts.bm - 1) / ts.bm || a.K % a.Kg) return hipErrorInvalidValue;
+    dim3 grid((unsigned)(a.K / a.Kg * a.mtiles_g), (unsigned)((a.ncols + ts.bn - 1) / ts.bn), (unsigned)a.splits);
     switch (dtype) {
     case CONV2D_DTYPE_F16:
         if (tile == 0)
