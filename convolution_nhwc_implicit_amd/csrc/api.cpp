@@ -757,7 +757,7 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     const bool to_parts = ep.axpby || ep.out_f32;
     const bool reduce = pl.split_k > 1 || to_parts;
     void *out = reduce ? workspace : dw;
-    const ReduceEpi re{ep.alpha, ep.beta, ep.axpby ? ep.c : nullptr, ep.out_f32 ? 1 : 0};
+    const ReduceEpi re{ep.alpha, ep.beta, ep.axpby ? ep.c : nullptr, ep.out_f32 ? 1 : 0, nullptr, 0};
 
     if (pl.padded) {
         unsigned char *wsb = (unsigned char *)workspace;
@@ -1019,7 +1019,7 @@ int conv2d_bias_grad(const conv2d_problem_t *prob, int dtype, const void *dy, vo
     a.part_stride = splitk_stride(d.K);
     hipStream_t s = (hipStream_t)stream;
     if (launch_colsum(dtype, a, splits, s) != hipSuccess) return CONV2D_ERR_DEVICE;
-    const ReduceEpi re{1.0f, 0.0f, nullptr, out_f32};
+    const ReduceEpi re{1.0f, 0.0f, nullptr, out_f32, nullptr, 0};
     return hip_status(launch_splitk_reduce(dtype, a.parts, splits, d.K, a.part_stride, db, &re, s));
 }
 
