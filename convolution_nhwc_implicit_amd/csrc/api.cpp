@@ -156,13 +156,15 @@ int choose_igemm_tile(long long m_total, long long ngemm)
 
 // Stride-1 problems whose source channel count and filter the band kernel
 // is built for keep the filter and a ring of input rows in LDS.
-bool band_eligible(const Dims &d, int dtype, long long cin, long long src_h, long long src_w, long long ngemm)
+bool band_eligible(const Dims &d, int dtype, long long cin, long long src_h, long long src_w, long long ngemm,
+                   long long dst_h, long long dst_w)
 {
-    // buffer offsets are 32-bit: one source image and the filter stay under 1 GiB
+    // buffer offsets are 32-bit: one source image, one output image and the
+    // filter stay under 1 GiB
     const long long e = elem_size(dtype);
     return d.G == 1 && d.sh == 1 && d.sw == 1 && d.dh == d.dw &&
            band_supported(dtype, (int)d.R, (int)d.S, (int)cin, (int)d.dh) && src_h * src_w * cin * e < (1LL << 30) &&
-           d.R * d.S * cin * ngemm * e < (1LL << 30);
+           dst_h * dst_w * ngemm * e < (1LL << 30) && d.R * d.S * cin * ngemm * e < (1LL << 30);
 }
 
 constexpr int kBandTile = 5;  // tile index of the band kernel (algo tile 6)
@@ -385,8 +387,8 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         return CONV2D_OK;
     }
     // the band kernels have no linear-combination epilogue
-    const bool band = !ep.axpby && (op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K)
-                                                          : band_eligible(d, dtype, d.K, d.P, d.Q, d.C));
+    const bool band = !ep.axpby && (op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K, d.P, d.Q)
+                                                          : band_eligible(d, dtype, d.K, d.P, d.Q, d.C, d.H, d.W));
     pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0);
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {

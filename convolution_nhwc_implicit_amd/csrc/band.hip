@@ -20,9 +20,10 @@
 //     rows of group g+1 are in flight while group g is computed; a group's
 //     slots are refilled with the rows of group g+2 right after its barrier;
 //   * results (bias, ReLU and rounding applied) are staged in LDS, over the
-//     filter staging area that only the prologue uses, and leave as whole
-//     128-byte pixels: stores of partial lines would multiply the number of
-//     memory requests several times;
+//     filter staging area that only the prologue uses, and each wave stores
+//     its own results from there as 64-byte half pixels (four lanes each):
+//     stores straight from the accumulators would be 8-byte pieces, four
+//     times as many memory requests;
 //   * the LDS has 64 four-byte banks and serves 16 lanes of a 128-bit read per
 //     cycle.  A 128-byte pixel covers half of the banks, so the 16-byte channel
 //     chunks of pixel `col` are XOR-swizzled by col/2: any 16 consecutive
@@ -120,10 +121,10 @@ struct BandCfg {
     static constexpr int FROWCH = FROWB / 16;
     static constexpr int FILT_BYTES = FROWS * FROWB;
     static constexpr int FBLOCKS = FROWS * FROWCH / 64;  // 1 KB direct-to-LDS blocks
-    // Output staging (after the prologue, over the filter staging): two
-    // buffers of GR rows x RCOLS pixels x BN channels.
+    // Output staging (after the prologue, over the filter staging): GR rows
+    // x RCOLS pixels x BN channels.
     static constexpr int OSTAGE_BYTES = GR * SLOTB;
-    static constexpr int STAGE_BYTES = FILT_BYTES > 2 * OSTAGE_BYTES ? FILT_BYTES : 2 * OSTAGE_BYTES;
+    static constexpr int STAGE_BYTES = FILT_BYTES > OSTAGE_BYTES ? FILT_BYTES : OSTAGE_BYTES;
     static constexpr int BIAS_BYTES = BN * 4;
     static constexpr int LDS_BYTES = RING_BYTES + STAGE_BYTES + BIAS_BYTES;
     static_assert(CIN == 64 && BN == 64, "pixels of 8 chunks, two 32-channel halves");
@@ -189,15 +190,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         r0 = g == 0 ? 0 : g * C::GR + C::HALO_R;
         r1 = min((g + 1) * C::GR + C::HALO_R, nrows + C::HALO_R);
     };
-    // After the prologue all global memory traffic is issued by the first
-    // half of the waves (the "I/O waves"): being older, they win the MFMA
-    // arbitration against the second half on their SIMD and finish each group
-    // first, so their loads and stores fill time they would otherwise spend
-    // at the group barrier.  I/O wave w moves blocks w and w + PW of every
-    // ring row.
+    // After the prologue all row loads are issued by the first half of the
+    // waves (the "I/O waves"): being older, they win the MFMA arbitration
+    // against the second half on their SIMD and finish each group first, so
+    // the loads fill time they would otherwise spend at the group barrier.
+    // I/O wave w moves blocks w and w + PW of every ring row.
     constexpr int PW = C::WAVES / 2;
     const bool io_wave = wave < PW;
-    static_assert(PW == C::GR, "I/O wave w stores output row w of a group");
     const int off2 = lane_src(wave + PW);
     auto dma_group = [&](int g) {
         int r0, r1;
@@ -294,26 +293,100 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // (128-byte lines) from the staging to memory.  I/O wave w stores row w
     // of the group, 8 pixels per instruction; lane i takes stored chunk i%8
     // of pixel i/8, i.e. channel chunk (i%8) ^ swizzle(pixel).
-    auto store_rows = [&](int g) {
-        const int pr = g * C::GR + wave;
-        if (pr >= nrows) return;
-        const unsigned char *stage = ostage + (g & 1) * C::OSTAGE_BYTES + wave * C::SLOTB;
-        elem *drow = (elem *)a.dst + ((size_t)img * a.P + p_start + pr) * a.Q * a.ngemm;  // wave-uniform
+    // 32-bit offsets from the start of the output image (its size is checked
+    // on the host); stores past a row's valid pixels or channels go to an
+    // offset past the range, which the buffer range check drops
+    const __amdgpu_buffer_rsrc_t dst_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((elem *)a.dst + (size_t)img * a.P * a.Q * a.ngemm), (short)0,
+        (int)((size_t)a.P * a.Q * a.ngemm * sizeof(elem)), 0x00020000);
+    // Each wave stages its own 64 pixels x 32 channels in its row of the
+    // staging area and stores them from there itself, so no wave waits on
+    // another for its results.
+    unsigned char *stage = ostage + prw * C::SLOTB;
+
+    // ---- epilogue, part 1: ReLU, round, into the staging as [pixel][channel]
+    // with the ring's chunk swizzle.  Lane holds pixel mb*32 + l32, channels
+    // 32*nb + 8*j + 4*lhi + 0..3 in acc[mb][4j..4j+3]: 8 bytes, half lhi of
+    // chunk 4nb+j.
+    acc_t acc[2];
+    auto epilogue = [&](auto relu_c) {
+        constexpr bool RELU = decltype(relu_c)::value;
 #pragma unroll
-        for (int t = 0; t < C::RCOLS / 8; ++t) {
-            const int px = 8 * t + (lane >> 3);
-            const int chunk = (lane & 7) ^ ((px >> 1) & 7);
-            const u32x4 v = *(const u32x4 *)(stage + px * C::PIXB + (lane & 7) * 16);
-            const int q = q0 + px, ch = n0 + chunk * EPC16;
-            if (chunk < C::BN / EPC16 && px < C::SEG && q < a.Q && ch < a.ngemm)
-                *(u32x4 *)(drow + (unsigned)(q * a.ngemm + ch)) = v;
+        for (int mb = 0; mb < 2; ++mb) {
+            const int px = mb * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t v[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    v[t] = out_pair<E, RELU>(acc[mb][4 * j + 2 * t], acc[mb][4 * j + 2 * t + 1]);
+                const int chunk = (4 * nb + j) ^ ((px >> 1) & 7);
+                *(uint2 *)(stage + px * C::PIXB + chunk * 16 + lhi * 8) = uint2{v[0], v[1]};
+            }
         }
     };
+    // int8: lane's 4 channels -> ReLU, requantise (fp64), 4 bytes at byte
+    // 8*(j&1) + 4*lhi of logical chunk 2*nb + j/2 (16 channels a chunk)
+    auto epilogue_i8 = [&]() {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int px = mb * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    int v = (int)acc[mb][4 * j + r];
+                    if (a.relu && v < 0) v = 0;
+                    word |= (uint32_t)(uint8_t)requant_i8(v, a.requant_m) << (8 * r);
+                }
+                const int chunk = (2 * nb + (j >> 1)) ^ ((px >> 1) & 7);
+                *(uint32_t *)(stage + px * C::PIXB + chunk * 16 + 8 * (j & 1) + 4 * lhi) = word;
+            }
+        }
+    };
+    auto stage_rows = [&]() {
+        if constexpr (I8)
+            epilogue_i8();
+        else if (a.relu)
+            epilogue(band::BoolC<true>{});
+        else
+            epilogue(band::BoolC<false>{});
+    };
+    // ---- epilogue, part 2: the wave's 16-byte chunks back from the staging
+    // (its own writes: LDS runs a wave's accesses in order) and out, four
+    // lanes (64 contiguous bytes) per pixel for fp16/bf16, two for int8.
+    // fp16/bf16 lane order: pixels {2u, 2u+1, 2u+8, 2u+9} of a quarter-wave
+    // cover all 64 banks under the swizzle.
+    auto store_rows = [&](int g) {
+        const int qrow = (p_start + g * C::GR + prw) * a.Q + q0;  // wave-uniform
+        asm volatile("" ::: "memory");  // the reads stay after the staging writes
+        constexpr int LPP = I8 ? 2 : 4;  // lanes per pixel
+#pragma unroll
+        for (int t = 0; t < C::RCOLS * LPP / 64; ++t) {
+            const int u = lane / LPP, c = lane % LPP;
+            const int px = I8 ? 32 * t + u : 16 * t + (u & 1) + 8 * ((u >> 1) & 1) + 2 * (u >> 2);
+            const int chunk = LPP * nb + c;
+            const u32x4 v = *(const u32x4 *)(stage + px * C::PIXB + ((chunk ^ ((px >> 1) & 7)) << 4));
+            const int ch = n0 + chunk * EPC16;
+            const bool ok = px < C::SEG && q0 + px < a.Q && ch < a.ngemm;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v, dst_rs, ok ? (uint32_t)(((qrow + px) * a.ngemm + ch) * (int)sizeof(elem)) : kBufOOB, 0, 0);
+        }
+    };
+    // The compute waves finish a group's MFMAs after the I/O waves (which win
+    // the MFMA arbitration), so they stage and store group g's results after
+    // the barrier that ends the group, while the I/O waves already run group
+    // g+1's MFMAs.  The I/O waves stage right after their MFMAs, while the
+    // compute waves still run theirs.
     __syncthreads();  // every wave holds its filter fragments: the staging area is free
     for (int g = 0; g < ngroups; ++g) {
+        if (!io_wave && g > 0 && (g - 1) * C::GR + prw < nrows) {
+            stage_rows();
+            store_rows(g - 1);
+        }
         const int pr = g * C::GR + prw;  // output row of this wave, relative to p_start
         const bool active = pr < nrows;
-        acc_t acc[2];
         if (active) {
             // the accumulators start at the bias (zero for dgrad)
             acc[0] = *(const acc_t *)(bias_s + (nb * 2 + lhi) * 16);
@@ -341,63 +414,20 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // ---- epilogue, part 1: ReLU, round, into the output staging
-        // (double-buffered) as [row][pixel][channel] with the ring's chunk
-        // swizzle.  Lane holds pixel mb*32 + l32, channels 32*nb + 8*j +
-        // 4*lhi + 0..3 in acc[mb][4j..4j+3]: 8 bytes, half lhi of chunk 4nb+j.
-        unsigned char *stage = ostage + (g & 1) * C::OSTAGE_BYTES + prw * C::SLOTB;
-        auto epilogue = [&](auto relu_c) {
-            constexpr bool RELU = decltype(relu_c)::value;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int px = mb * 32 + l32;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t v[2];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-                        v[t] = out_pair<E, RELU>(acc[mb][4 * j + 2 * t], acc[mb][4 * j + 2 * t + 1]);
-                    const int chunk = (4 * nb + j) ^ ((px >> 1) & 7);
-                    *(uint2 *)(stage + px * C::PIXB + chunk * 16 + lhi * 8) = uint2{v[0], v[1]};
-                }
-            }
-        };
-        // int8: lane's 4 channels -> ReLU, requantise (fp64), 4 bytes at byte
-        // 8*(j&1) + 4*lhi of logical chunk 2*nb + j/2 (16 channels a chunk)
-        auto epilogue_i8 = [&]() {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int px = mb * 32 + l32;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        int v = (int)acc[mb][4 * j + r];
-                        if (a.relu && v < 0) v = 0;
-                        word |= (uint32_t)(uint8_t)requant_i8(v, a.requant_m) << (8 * r);
-                    }
-                    const int chunk = (2 * nb + (j >> 1)) ^ ((px >> 1) & 7);
-                    *(uint32_t *)(stage + px * C::PIXB + chunk * 16 + 8 * (j & 1) + 4 * lhi) = word;
-                }
-            }
-        };
-        if (active) {
-            if constexpr (I8)
-                epilogue_i8();
-            else if (a.relu)
-                epilogue(band::BoolC<true>{});
-            else
-                epilogue(band::BoolC<false>{});
-        }
         if (io_wave) {
-            wait_vm_all();  // the next group's rows (and this wave's older stores)
-            if (g > 0) store_rows(g - 1);
+            if (active) stage_rows();
+            // the next group's rows (and this wave's older stores), before the
+            // stores below join the count
+            wait_vm_all();
+            if (active) store_rows(g);
         }
-        __syncthreads();  // every wave is done with this group's rows; the staging is complete
+        __syncthreads();  // every wave is done with this group's rows
         if (io_wave) dma_group(g + 2);  // into the slots of the rows only this group read
     }
-    if (io_wave) store_rows(ngroups - 1);
+    if (!io_wave && (ngroups - 1) * C::GR + prw < nrows) {
+        stage_rows();
+        store_rows(ngroups - 1);
+    }
 }
 
 bool band_supported(int dtype, int R, int S, int cin, int dil)
