@@ -190,31 +190,30 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         r0 = g == 0 ? 0 : g * C::GR + C::HALO_R;
         r1 = min((g + 1) * C::GR + C::HALO_R, nrows + C::HALO_R);
     };
-    // After the prologue all row loads are issued by the first half of the
-    // waves (the "I/O waves"): being older, they win the MFMA arbitration
-    // against the second half on their SIMD and finish each group first, so
-    // the loads fill time they would otherwise spend at the group barrier.
-    // I/O wave w moves blocks w and w + PW of every ring row.
+    // The first half of the waves (the "leading waves") are older: they win
+    // the MFMA arbitration against the second half (the "trailing waves") on
+    // their SIMD and finish each group's MFMAs first.  So the leading waves
+    // start a group's MFMAs right after its barrier, and the trailing waves
+    // first store the previous group's results and issue the row loads of
+    // the group after next (blocks w and w ^ PW of every ring row), which
+    // they wait for before the next barrier.
     constexpr int PW = C::WAVES / 2;
-    const bool io_wave = wave < PW;
-    const int off2 = lane_src(wave + PW);
+    const bool lead = wave < PW;
+    const int off2 = lane_src(wave ^ PW);
     auto dma_group = [&](int g) {
         int r0, r1;
         group_rows(g, r0, r1);
         for (int rr = r0; rr < r1; ++rr) {
             dma_row(rr, wave, my_off);
-            dma_row(rr, wave + PW, off2);
+            dma_row(rr, wave ^ PW, off2);
         }
     };
 
-    // ---- prologue: the filter tile and group 0's rows (every wave a share),
-    // then group 1's rows.
+    // ---- prologue: the filter tile, then group 0's rows (every wave a
+    // share).  The filter is read into registers as soon as it has landed,
+    // while the rows are still on their way.
+    int nrow0;
     {
-        {
-            int r0, r1;
-            group_rows(0, r0, r1);
-            for (int rr = r0; rr < r1; ++rr) dma_row(rr, wave, my_off);
-        }
         const int fbytes = (TRANS ? CIN * R * S * a.ngemm : a.ngemm * C::KG) * 2;
         const u32x4 w_rs = make_buf_rsrc(a.bmat, (uint32_t)fbytes);
         for (int b = wave; b < C::FBLOCKS; b += C::WAVES) {
@@ -233,23 +232,24 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
             dma16(w_rs, lds_addr(filt + b * 1024), voff);
         }
+        int r0, r1;
+        group_rows(0, r0, r1);
+        for (int rr = r0; rr < r1; ++rr) dma_row(rr, wave, my_off);
+        nrow0 = r1 - r0;
     }
-    {
-        // the bias in the accumulator layout, [nb][lhi][16]: entry i of a
-        // lane's acc holds channel 32*nb + 8*(i/4) + 4*lhi + i%4
-        if (tid < C::BN) {
-            const int i = tid & 15, lh = (tid >> 4) & 1, hb = tid >> 5;
-            const int ch = n0 + 32 * hb + 8 * (i >> 2) + 4 * lh + (i & 3);
-            if constexpr (I8)
-                ((int32_t *)bias_s)[tid] = (a.bias && ch < a.ngemm) ? ((const int32_t *)a.bias)[ch] : 0;
-            else
-                bias_s[tid] = (a.bias && ch < a.ngemm) ? E::to_f32(((const elem *)a.bias)[ch]) : 0.0f;
-        }
-        wait_vm_all();
-        __syncthreads();
-        if (io_wave) dma_group(1);  // into slots group 0 does not read
+    // loads complete in issue order: with only the row loads outstanding,
+    // this wave's share of the filter is in LDS
+    static_assert(C::GR + C::HALO_R <= 6, "row loads of group 0 the wait below covers");
+    switch (nrow0) {
+    case 6: wait_vm_n<6>(); break;
+    case 5: wait_vm_n<5>(); break;
+    case 4: wait_vm_n<4>(); break;
+    case 3: wait_vm_n<3>(); break;
+    case 2: wait_vm_n<2>(); break;
+    case 1: wait_vm_n<1>(); break;
+    default: wait_vm_all(); break;
     }
-
+    __syncthreads();  // the filter staging is complete
     // ---- the wave's filter fragments (A operand): rows n0 + 32*nb + 0..31,
     // k16 step ks = tap*C16 + c16; lane holds row l32, k = 8*lhi + 0..7
     const int nb = wave & 1, l32 = lane & 31, lhi = lane >> 5;
@@ -273,6 +273,22 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             const uint2 hi = __builtin_bit_cast(uint2, band::tr16(fp + (kb + 4) * C::FROWB + stap * C::BN * 2));
             fr[ks] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
+    }
+
+    {
+        // the bias in the accumulator layout, [nb][lhi][16]: entry i of a
+        // lane's acc holds channel 32*nb + 8*(i/4) + 4*lhi + i%4
+        if (tid < C::BN) {
+            const int i = tid & 15, lh = (tid >> 4) & 1, hb = tid >> 5;
+            const int ch = n0 + 32 * hb + 8 * (i >> 2) + 4 * lh + (i & 3);
+            if constexpr (I8)
+                ((int32_t *)bias_s)[tid] = (a.bias && ch < a.ngemm) ? ((const int32_t *)a.bias)[ch] : 0;
+            else
+                bias_s[tid] = (a.bias && ch < a.ngemm) ? E::to_f32(((const elem *)a.bias)[ch]) : 0.0f;
+        }
+        wait_vm_all();    // group 0's rows
+        __syncthreads();  // rows and bias visible; every wave holds its filter fragments
+        if (!lead) dma_group(1);  // into slots group 0 does not read
     }
 
     // ---- pixel fragments (B operand): output column mb*32 + l32 at tap
@@ -374,14 +390,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 v, dst_rs, ok ? (uint32_t)(((qrow + px) * a.ngemm + ch) * (int)sizeof(elem)) : kBufOOB, 0, 0);
         }
     };
-    // The compute waves finish a group's MFMAs after the I/O waves (which win
-    // the MFMA arbitration), so they stage and store group g's results after
-    // the barrier that ends the group, while the I/O waves already run group
-    // g+1's MFMAs.  The I/O waves stage right after their MFMAs, while the
-    // compute waves still run theirs.
-    __syncthreads();  // every wave holds its filter fragments: the staging area is free
+    // The trailing waves stage and store group g's results after the barrier
+    // that ends the group, while the leading waves already run group g+1's
+    // MFMAs; the leading waves stage theirs right after their MFMAs, while
+    // the trailing waves still run their own.
     for (int g = 0; g < ngroups; ++g) {
-        if (!io_wave && g > 0 && (g - 1) * C::GR + prw < nrows) {
+        if (!lead && g > 0 && (g - 1) * C::GR + prw < nrows) {
             stage_rows();
             store_rows(g - 1);
         }
@@ -414,17 +428,18 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (io_wave) {
-            if (active) stage_rows();
-            // the next group's rows (and this wave's older stores), before the
-            // stores below join the count
-            wait_vm_all();
-            if (active) store_rows(g);
+        if (lead) {
+            if (active) {
+                stage_rows();
+                store_rows(g);
+            }
+        } else {
+            wait_vm_all();  // the next group's rows (and this wave's older stores)
         }
         __syncthreads();  // every wave is done with this group's rows
-        if (io_wave) dma_group(g + 2);  // into the slots of the rows only this group read
+        if (!lead) dma_group(g + 2);  // into the slots of the rows only this group read
     }
-    if (!io_wave && (ngroups - 1) * C::GR + prw < nrows) {
+    if (!lead && (ngroups - 1) * C::GR + prw < nrows) {
         stage_rows();
         store_rows(ngroups - 1);
     }

@@ -111,6 +111,13 @@ __device__ inline void dma16(const u32x4 &rsrc, uint32_t lds, uint32_t voff)
         : "memory");
 }
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ inline void wait_vm_n()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // int8 requantisation of one accumulator: + bias, ReLU, * m in fp64,
 // round half to even (v_rndne_f64), saturate.

@@ -46,13 +46,6 @@ struct Mfma32x16 {
                                                             __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
 };
-// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ inline void wait_vm_n()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 template <class E>
 __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
