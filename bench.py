@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3a_resnet3x3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (default: also replay captured HIP graphs)")
     ap.add_argument("--cpu-sample-images", type=int, default=0,
                     help="images of the batch the oracle runs on (0 = auto)")
     ap.add_argument("--only", choices=["fprop", "dgrad", "wgrad", "copy"], default=None,
@@ -123,10 +125,10 @@ def main():
         dw = torch.empty_like(w)
     stream = torch.cuda.current_stream()
 
-    def step():
-        B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, ws[0], stream=stream)
-        B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream)
-        B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)
+    def step(st=stream):
+        B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, ws[0], stream=st)
+        B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=st)
+        B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=st)
 
     if args.only == "copy":
         src_t = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -171,30 +173,68 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region 1: K whole steps back to back (wall clock between two
-    # device synchronisations) -> value.
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # device synchronisations), launched eagerly -> value.  The same step
+    # replayed from a captured HIP graph (the library makes no allocation,
+    # copy, memset or synchronisation call, so a step captures as its kernel
+    # launches) is reported beside it.
+    def wall(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    eager_ms = wall(step)
+    cap = torch.cuda.Stream()  # default priority
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            step(cap)
+        stream.wait_stream(cap)
+        for _ in range(args.warmup):
+            graph.replay()
+        graph_ms = wall(graph.replay)
+    ms_per_step = eager_ms
 
     # Timed region 2: each pass alone, K back-to-back launches between two HIP
     # events recorded on the launch stream -> per-pass time per launch (the
-    # figure rocprofv3's kernel trace reports as the kernels' duration).
-    runs = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, ws[0], stream=stream),
-            "dgrad": lambda: B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream),
-            "wgrad": lambda: B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)}
-    pass_us = {}
-    for pname, run in runs.items():
-        run()
+    # figure rocprofv3's kernel trace reports as the kernels' duration); the K
+    # launches are replayed from one captured graph unless --eager.
+    runs = {"fprop": lambda st: B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, ws[0], stream=st),
+            "dgrad": lambda st: B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=st),
+            "wgrad": lambda st: B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=st)}
+
+    def events(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(args.steps):
-            run()
+        fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        pass_us[pname] = e0.elapsed_time(e1) * 1e3 / args.steps
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    pass_us, eager_us = {}, {}
+    for pname, run in runs.items():
+        run(stream)
+
+        def eager_k():
+            for _ in range(args.steps):
+                run(stream)
+
+        eager_us[pname] = events(eager_k)
+        if graph is not None:
+            g = torch.cuda.CUDAGraph()
+            cap.wait_stream(stream)
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(args.steps):
+                    run(cap)
+            stream.wait_stream(cap)
+            g.replay()
+            pass_us[pname] = events(g.replay)
+        else:
+            pass_us[pname] = eager_us[pname]
 
     fl = flops(prob, P, Q)
     esz = 2
@@ -223,6 +263,7 @@ def main():
             "tflops": round(fl / (us * 1e-6) / 1e12, 2),
             "frac_mfma_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_TFLOPS[dt], 4),
             "alg_gbs": round(alg_bytes[pname] / (us * 1e-6) / 1e9, 1),
+            "eager_us_per_launch": round(eager_us[pname], 3),
             "kernels": kernels[pname],
             "plan": plans[pname],
         }
@@ -251,6 +292,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "timing": "step: eager launches; passes: " + ("eager launches" if args.eager else
+                                                      "HIP graph replay of K launches"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -263,6 +306,8 @@ def main():
         "passes": passes,
         "roofline": roof,
     }
+    if graph is not None:
+        result["graph_ms_per_step"] = round(graph_ms, 5)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(name, prob, P, Q, args.cpu_sample_images)
