@@ -95,6 +95,7 @@ CASES = [
     ("band_gauss", problem(8, 64, 28, 28, 64, 3, 3, pad=(1, 1)), "f16", "gauss", True, True),
     ("band_bf16_gauss", problem(4, 64, 17, 23, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
     ("band_bf16_relu", problem(3, 64, 13, 40, 64, 3, 3, pad=(1, 1)), "bf16", "int", True, True),
+    ("band_one_row", problem(3, 64, 1, 9, 64, 3, 3, pad=(1, 1)), "f16", "int", True, True),
     # wgrad band kernel (stride 1, 3x3, C = K = 64, Q % 4 == 0, Q <= 56):
     # two row groups with a partial last group, and one-row bands whose pixel
     # count is not a multiple of 16; the widest row it takes (Q = 56, several
@@ -145,6 +146,7 @@ INT8_CASES = [
     ("i8_band_k48_w70", problem(1, 128, 5, 70, 48, 3, 3, pad=(1, 1)), True, False),
     ("i8_band_pad0_k192", problem(2, 128, 9, 9, 192, 3, 3), False, True),
     ("i8_band_pad2", problem(1, 128, 6, 7, 64, 3, 3, pad=(2, 2)), True, True),
+    ("i8_band_two_rows", problem(2, 128, 2, 5, 128, 3, 3, pad=(1, 1)), True, True),
 ]
 
 
