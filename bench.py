@@ -33,7 +33,7 @@ METRIC = "conv2d TFLOP/s (fprop/dgrad/wgrad) and % of MFMA peak, 56x56x64 3x3 fp
 # FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s), int8 5.03 POP/s, HBM3E 8 TB/s.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2}
 PEAK_HBM_GBS = 8000.0
-BAND_TILE, WGRAD_BAND_TILE = 5, 1  # plan tile indices of the band kernels (conv2d_plan_info)
+BAND_TILE, WGRAD_BAND_TILE = 5, 2  # plan tile indices of the band kernels (conv2d_plan_info)
 COPY_BYTES = 64 << 20  # reference copy for the HBM byte counters
 # Measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by
 # the same counters on a plain copy) lives in this summary, keyed by a hash of

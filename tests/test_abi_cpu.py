@@ -259,3 +259,15 @@ def test_bias_grad_checks(lib):
     bad = B.make_problem(problem(4, 8, 10, 10, 24, 3, 3, pad=(1, 1), groups=3))
     bad.c = 7  # C % groups != 0
     assert lib.conv2d_bias_grad(ctypes.byref(bad), 0, fake, fake, 0, fake, n, None) == inv
+
+
+def test_bench_names_the_band_kernels():
+    """bench.py names the kernels of a pass from the plan's tile index; its
+    constants must be the band kernels' indices in the library's plans."""
+    import bench
+    from convolution_nhwc_implicit_amd import workloads as WL
+
+    c3a = WL.WORKLOADS["c3a_resnet3x3"]["prob"]
+    assert B.conv2d_plan_info(0, c3a, "f16")["tile"] == bench.BAND_TILE
+    assert B.conv2d_plan_info(1, c3a, "f16")["tile"] == bench.BAND_TILE
+    assert B.conv2d_plan_info(2, c3a, "f16")["tile"] == bench.WGRAD_BAND_TILE
