@@ -6,6 +6,8 @@ test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 The arithmetic lives in ``conv2d_oracle.c`` (plain C, double precision, one
 output element at a time).  This module only marshals numpy arrays to it.
+``oracle.winograd`` (numpy, fp64) writes out the Winograd F(2x2, 3x3) steps
+for stride-1 3x3 layers and the per-output bound on its rounding error.
 
 A problem is a mapping with the keys N, C, H, W, K, R, S, pad_h, pad_w,
 stride_h, stride_w, dil_h, dil_w, groups.  Tensors are float64 numpy arrays in

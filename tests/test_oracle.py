@@ -429,3 +429,41 @@ def test_round_overflow_to_inf():
     got = oracle.round_bf16(np.array([3.4e38, 3.39e38, -1e39]))
     assert math.isinf(bf16_value(got[2])) and bf16_value(got[2]) < 0
     assert np.isfinite(bf16_value(got[1]))
+
+
+# ---- Winograd F(2x2, 3x3) (oracle.winograd), pinned to the direct definition
+WINO_CASES = [(2, 5, 7, 9, 3, 1), (1, 3, 6, 6, 4, 0), (2, 4, 5, 8, 2, 2), (1, 2, 1, 1, 3, 1), (3, 8, 12, 11, 5, 1)]
+
+
+@pytest.mark.parametrize("N,C,H,W,K,pad", WINO_CASES)
+def test_winograd_matches_direct(N, C, H, W, K, pad):
+    """The transforms, products and inverse transform reproduce the direct
+    convolution (odd P and Q leave partial 2x2 blocks; pads 0, 1, 2)."""
+    from oracle import winograd as WG
+    prob = problem(N, C, H, W, K, 3, 3, pad=(pad, pad))
+    rng = np.random.default_rng(N * 1000 + C * 100 + H)
+    x, w, b = rng.standard_normal((N, H, W, C)), rng.standard_normal((K, 3, 3, C)), rng.standard_normal(K)
+    yd = oracle.fprop(prob, x, w, bias=b, relu=True)
+    yw = WG.fprop(prob, x, w, bias=b, relu=True)
+    assert yw.shape == yd.shape
+    assert np.max(np.abs(yw - yd)) <= 1e-12 * np.max(np.abs(yd))
+    # every output is a signed sum of the terms S adds up in absolute value
+    assert np.all(np.abs(oracle.fprop(prob, x, w)) <= WG.abs_terms(prob, x, w) * (1 + 1e-12))
+
+
+def test_winograd_single_tap_and_errors():
+    """A filter with one nonzero tap gives the shifted input times that tap;
+    other problem shapes are refused."""
+    from oracle import winograd as WG
+    prob = problem(1, 2, 5, 6, 2, 3, 3, pad=(1, 1))
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 5, 6, 2))
+    w = np.zeros((2, 3, 3, 2))
+    w[0, 2, 0, 1] = 3.0  # y[p, q, 0] = 3 x[p + 1, q - 1, 1]
+    y = WG.fprop(prob, x, w)
+    want = np.zeros((1, 5, 6))
+    want[0, :4, 1:] = 3.0 * x[0, 1:, :5, 1]
+    assert np.allclose(y[..., 0], want, rtol=0, atol=1e-13)
+    assert np.all(y[..., 1] == 0)
+    with pytest.raises(ValueError):
+        WG.fprop(problem(1, 2, 5, 6, 2, 3, 3, pad=(1, 1), stride=(2, 2)), x, w)
