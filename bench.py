@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3a_resnet3x3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile", type=int, default=0,
+                    help="with --only: algorithm tile override (1-based, conv2d_plan_info order; 0 = library choice)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: also replay captured HIP graphs)")
     ap.add_argument("--cpu-sample-images", type=int, default=0,
@@ -147,9 +149,13 @@ def main():
         print(f"copy {COPY_BYTES} B: {us:.2f} us/launch, {2 * COPY_BYTES / us / 1e3:.1f} GB/s", flush=True)
         return
     if args.only:
-        run = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, ws[0], stream=stream),
-               "dgrad": lambda: B.conv2d_dgrad(prob, dt, dy, w, dx, ws[1], stream=stream),
-               "wgrad": lambda: B.conv2d_wgrad(prob, dt, x, dy, dw, ws[2], stream=stream)}[args.only]
+        al = dict(tile=args.tile) if args.tile else None
+        op = {"fprop": 0, "dgrad": 1, "wgrad": 2}[args.only]
+        wso = B.workspace_for(op, prob, dt, dev, al) if al else ws.get(op)
+        run = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, wso, al,
+                                               stream=stream),
+               "dgrad": lambda: B.conv2d_dgrad(prob, dt, dy, w, dx, wso, al, stream=stream),
+               "wgrad": lambda: B.conv2d_wgrad(prob, dt, x, dy, dw, wso, al, stream=stream)}[args.only]
         for _ in range(args.warmup):
             run()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -164,7 +170,8 @@ def main():
         nx, ny = prob["N"] * prob["H"] * prob["W"] * prob["C"], prob["N"] * P * Q * prob["K"]
         nw = prob["K"] * prob["R"] * prob["S"] * (prob["C"] // prob["groups"])
         mb = esz * (nx + ny + nw) / 1e6  # algorithmic bytes: each tensor once
-        print(f"{args.only} {name}: {us:.2f} us/launch, {fl / us / 1e6:.1f} T{'OP' if dt == 'i8' else 'FLOP'}/s, "
+        tl = f" tile {args.tile}" if args.tile else ""
+        print(f"{args.only}{tl} {name}: {us:.2f} us/launch, {fl / us / 1e6:.1f} T{'OP' if dt == 'i8' else 'FLOP'}/s, "
               f"{mb / us * 1e3:.1f} GB/s algorithmic ({mb:.2f} MB)", flush=True)
         return
 

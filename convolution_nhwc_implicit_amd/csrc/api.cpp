@@ -168,6 +168,16 @@ bool band_eligible(const Dims &d, int dtype, long long cin, long long src_h, lon
 }
 
 constexpr int kBandTile = 5;  // tile index of the band kernel (algo tile 6)
+constexpr int kWinoTile = 6;  // fprop: Winograd F(2x2,3x3) (algo tile 7), only when asked for
+
+// Winograd F(2x2, 3x3) fprop: a band-eligible problem (stride 1, 3x3,
+// dilation 1, buffer sizes) with 64 input channels and a multiple of 16
+// output channels.  Never the library's own choice: its rounding differs
+// from the direct sum's.
+bool wino_eligible(const Dims &d, int dtype)
+{
+    return wino_supported(dtype, (int)d.R, (int)d.S, (int)d.C, (int)d.dh) && d.K % 16 == 0;
+}
 
 // Stride-1 wgrad with the filter shape and channel counts the wgrad band
 // kernel is built for.
@@ -389,12 +399,14 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     // the band kernels have no linear-combination epilogue
     const bool band = !ep.axpby && (op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K, d.P, d.Q)
                                                           : band_eligible(d, dtype, d.K, d.P, d.Q, d.C, d.H, d.W));
-    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0);
+    const bool wino = band && op == CONV2D_OP_FPROP && wino_eligible(d, dtype);
+    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0);
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
         pl->tile = (algo && algo->tile) ? algo->tile - 1
                    : band             ? kBandTile
                                       : choose_igemm_tile(d.N * d.P * d.Q, d.Kg);
+        if (pl->tile == kWinoTile) pl->kernel = 3;
         return CONV2D_OK;
     }
     // dgrad
@@ -603,6 +615,25 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     if (pl.tile == kBandTile)
         return run_band(dtype, d, (int)d.C, x, (int)d.H, (int)d.W, w, 0, bias, relu, m, y, (int)d.P, (int)d.Q,
                         (int)d.K, (int)d.ph, (int)d.pw, s);
+    if (pl.tile == kWinoTile) {
+        WinoArgs wa;
+        memset(&wa, 0, sizeof(wa));
+        wa.src = x; wa.w = w; wa.bias = bias; wa.dst = y;
+        wa.N = (int)d.N; wa.H = (int)d.H; wa.W = (int)d.W; wa.P = (int)d.P; wa.Q = (int)d.Q;
+        wa.ngemm = (int)d.K; wa.pad_h = (int)d.ph; wa.pad_w = (int)d.pw; wa.relu = relu;
+        wa.tile_rows = (int)((d.P + 1) / 2);
+        wa.tiles_q = (int)((d.Q + 63) / 64);
+        const long long batches = d.N * wa.tile_rows * wa.tiles_q;
+        if (batches > INT32_MAX) return CONV2D_ERR_UNSUPPORTED;
+        wa.batches = (int)batches;
+        // persistent: about one workgroup per CU over the channel slices,
+        // a multiple of 8 (one share per XCD) when there are that many batches
+        const long long slices = (d.K + 63) / 64;
+        long long gx = std::max(1LL, (long long)kNumCUs / slices);
+        gx = std::min(gx, batches);
+        if (gx >= 8) gx -= gx % 8;
+        return hip_status(launch_wino_fprop(dtype, wa, (int)gx, s));
+    }
 
     IgemmArgs a;
     memset(&a, 0, sizeof(a));

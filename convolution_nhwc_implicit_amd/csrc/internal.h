@@ -130,6 +130,25 @@ bool band_supported(int dtype, int R, int S, int cin, int dil);
 hipError_t launch_band(int dtype, int R, int S, int cin, int dil, const BandArgs &a, int grid_n, int grid_q,
                        hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// Winograd F(2x2, 3x3) fprop (wino.hip): stride 1, 3x3, 64 input channels,
+// src [N][H][W][64], filter w [ngemm][3][3][64], dst [N][P][Q][ngemm],
+// ngemm % 16 == 0.  Batches of 32 tiles (2 output rows x 64 columns):
+// tile_rows = ceil(P/2), tiles_q = ceil(Q/64), batches = N*tile_rows*tiles_q.
+// ---------------------------------------------------------------------------
+struct WinoArgs {
+    const void *src;
+    const void *w;
+    const void *bias;
+    void *dst;
+    int N, H, W, P, Q, ngemm;
+    int pad_h, pad_w;
+    int relu;
+    int tile_rows, tiles_q, batches;
+};
+bool wino_supported(int dtype, int R, int S, int cin, int dil);
+hipError_t launch_wino_fprop(int dtype, const WinoArgs &a, int grid_x, hipStream_t st);
+
 // Re-lays the filter w[K][R][S][C/G] out as one [C][taps*K/G] matrix per
 // dgrad stride phase (taps of the phase in (jr, js) order, the dx channel's
 // group's dy channels innermost).

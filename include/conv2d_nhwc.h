@@ -99,6 +99,16 @@ typedef struct conv2d_problem {
  *            fixed order by a second kernel).  Ignored by fprop and dgrad.
  *            For groups > 1, tile 1 is the one-thread-per-output direct
  *            kernel and tile 2 (when it applies) the LDS-tiled one.
+ *            fprop of a stride-1, dilation-1 3x3 problem with 64 input
+ *            channels and a multiple of 16 output channels (fp16/bf16, no
+ *            linear-combination epilogue) also offers, as its last tile,
+ *            Winograd F(2x2, 3x3), the faster 3x3 stride-1 path the
+ *            tensorcore "Conv2D" page plans ("What's not done in v0.1").  It
+ *            is never the library's choice: it rounds the transformed filter
+ *            and input tiles to the 16-bit type before the products, so its
+ *            results differ from the direct sum by a few units of that
+ *            type's rounding of the transformed terms (exact on
+ *            integer-valued data whose transforms are exact).
  */
 typedef struct conv2d_algo {
     int tile;
@@ -107,7 +117,7 @@ typedef struct conv2d_algo {
 
 /* What the library will launch for a problem (diagnostics and tests). */
 typedef struct conv2d_plan_info {
-    int kernel;        /* 1 = implicit GEMM, 2 = direct (groups > 1) */
+    int kernel;        /* 1 = implicit GEMM, 2 = direct (groups > 1), 3 = Winograd F(2x2,3x3) */
     int tile;          /* index of the tile configuration used (0-based) */
     int num_tiles;     /* number of tile configurations available for this op/dtype */
     int split_k;       /* reduction slices (wgrad), 1 otherwise */

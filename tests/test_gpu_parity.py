@@ -197,12 +197,16 @@ def test_every_tile_on_band_eligible_problem():
     ref_y = oracle_fprop_out(prob, "f16", x, w, b, False)
     ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
     info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")
-    assert info["num_tiles"] == 6 and info["tile"] == 5  # the band kernel is the default
-    assert B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16")["tile"] == 5
+    # the band kernel is the default; fprop's last tile is Winograd F(2x2,3x3),
+    # exact here because the transformed integer operands are exact in fp16
+    assert info["num_tiles"] == 7 and info["tile"] == 5
+    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16", algo=dict(tile=7))["kernel"] == 3
+    dinfo = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16")
+    assert dinfo["num_tiles"] == 6 and dinfo["tile"] == 5
     for t in range(1, info["num_tiles"] + 1):
-        algo = dict(tile=t)
-        check(f64(run_fprop(prob, "f16", x, w, b, False, algo=algo)), ref_y, "f16", "exact", f"tile {t}")
-        check(f64(run_dgrad(prob, "f16", dy, w, algo=algo)), ref_dx, "f16", "exact", f"dgrad tile {t}")
+        check(f64(run_fprop(prob, "f16", x, w, b, False, algo=dict(tile=t))), ref_y, "f16", "exact", f"tile {t}")
+    for t in range(1, dinfo["num_tiles"] + 1):
+        check(f64(run_dgrad(prob, "f16", dy, w, algo=dict(tile=t))), ref_dx, "f16", "exact", f"dgrad tile {t}")
 
 
 def test_int8_every_tile():

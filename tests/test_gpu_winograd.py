@@ -1,0 +1,113 @@
+"""GPU parity of the Winograd F(2x2, 3x3) fprop (fprop's last tile on
+stride-1 3x3 problems with 64 input channels), through the C ABI.
+
+Integer-valued inputs in [-4, 3]: the transformed filter values are
+quarter-integers below 10 and the transformed input values integers below 17,
+all exact in fp16 and bf16, and every later sum is exact in fp32, so the
+result must equal the direct definition rounded once (the oracle's fprop).
+
+Gaussian inputs: the kernel rounds U = G g G^T and V = B^T d B once to the
+16-bit type u_op before the products; everything else runs in fp32, then one
+rounding to the output type.  Every output must lie within
+oracle.winograd.error_bound (2 u_op + u_op^2 + (2C+40) 2^-24 times the sum of
+the absolute values of the terms) of the exact value, plus the output
+rounding.  That is the tolerance this path is held to, derived from its
+arithmetic; the max_rel / rms_scaled figures of the direct kernels' check
+are reported, not asserted."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import winograd as WGO
+from convolution_nhwc_implicit_amd import binding as B
+from convolution_nhwc_implicit_amd import workloads as WL
+from convolution_nhwc_implicit_amd.workloads import problem
+
+from parity import check, f64, run_fprop
+
+pytestmark = pytest.mark.gpu
+
+U_TYPE = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def wino_tile(prob, dtype):
+    info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype)
+    algo = dict(tile=info["num_tiles"])
+    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype, algo=algo)["kernel"] == 3
+    return algo
+
+
+EXACT = [
+    # partial 2x2 blocks (odd P, Q), two 64-column segments, bias + ReLU
+    ("odd_two_segments", problem(2, 64, 13, 71, 64, 3, 3, pad=(1, 1)), "f16", True, True),
+    ("pad0_k16", problem(3, 64, 9, 10, 16, 3, 3), "f16", True, False),
+    ("pad2_k48", problem(2, 64, 7, 8, 48, 3, 3, pad=(2, 2)), "bf16", False, True),
+    ("k128_two_slices", problem(2, 64, 12, 20, 128, 3, 3, pad=(1, 1)), "bf16", True, True),
+    ("one_row", problem(3, 64, 1, 5, 32, 3, 3, pad=(1, 1)), "f16", True, False),
+    ("many_batches", problem(40, 64, 10, 12, 64, 3, 3, pad=(1, 1)), "f16", True, True),
+]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,bias,relu", EXACT, ids=[c[0] for c in EXACT])
+def test_winograd_exact_on_integers(cid, prob, dtype, bias, relu):
+    P, Q = oracle.output_hw(prob)
+    x, w, b, _ = WL.random_case(prob, dtype, "int", 7000 + len(cid), P, Q, bias=bias)
+    y = run_fprop(prob, dtype, x, w, b, relu, algo=wino_tile(prob, dtype))
+    ref = oracle.fprop(prob, f64(x), f64(w), bias=None if b is None else f64(b), relu=relu)
+    check(f64(y), ref, dtype, "exact", cid)
+
+
+def within_bound(g, prob, x, w, b, relu, dtype, what):
+    """Every output within the derived bound; returns (max_rel, rms_scaled)."""
+    xf, wf = f64(x), f64(w)
+    bf = None if b is None else f64(b)
+    y = oracle.fprop(prob, xf, wf, bias=bf, relu=relu)
+    E = WGO.error_bound(prob, xf, wf, U_TYPE[dtype])
+    u_out = U_TYPE[dtype]
+    babs = 0.0 if bf is None else np.abs(bf)
+    tol = E * 1.001 + u_out * (np.abs(y) + E) + 2.0 ** -23 * (np.abs(y) + babs) + 1e-7
+    err = np.abs(f64(g) - y)
+    bad = np.nonzero(err > tol)
+    assert bad[0].size == 0, (f"{what}: {bad[0].size} outputs outside the bound; worst err/tol "
+                              f"{np.max(err / tol):.3f}")
+    ref_out = oracle.bits_to_f64(oracle.round_to(y, dtype), dtype)
+    max_rel = float(np.max(err) / np.max(np.abs(y)))
+    rms = float(np.linalg.norm(f64(g) - ref_out) / np.linalg.norm(ref_out))
+    return max_rel, rms, float(np.max(err / tol))
+
+
+GAUSS = [
+    ("gauss_f16", problem(4, 64, 17, 23, 64, 3, 3, pad=(1, 1)), "f16", True, True),
+    ("gauss_bf16", problem(4, 64, 17, 23, 64, 3, 3, pad=(1, 1)), "bf16", True, False),
+    ("gauss_f16_k96_pad0", problem(2, 64, 15, 66, 96, 3, 3), "f16", False, False),
+]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,bias,relu", GAUSS, ids=[c[0] for c in GAUSS])
+def test_winograd_within_derived_bound(cid, prob, dtype, bias, relu):
+    P, Q = oracle.output_hw(prob)
+    x, w, b, _ = WL.random_case(prob, dtype, "gauss", 7100 + len(cid), P, Q, bias=bias)
+    y = run_fprop(prob, dtype, x, w, b, relu, algo=wino_tile(prob, dtype))
+    max_rel, rms, worst = within_bound(y, prob, x, w, b, relu, dtype, cid)
+    print(f"{cid}: max_rel {max_rel:.2e} rms_scaled {rms:.2e} worst err/bound {worst:.3f}")
+
+
+def test_winograd_full_size_c3a():
+    """The benchmark shape (64x56x56x64 -> 64, Gaussian, bias + ReLU) on the
+    Winograd tile: two whole images against the bound (the first and the
+    last, so the first and last batches of the persistent grid), and the
+    same inputs' direct-kernel result for comparison."""
+    name = "c3a_resnet3x3"
+    prob = WL.WORKLOADS[name]["prob"]
+    x, w, b = WL.make_x(name), WL.make_w(name), WL.make_bias(name)
+    y = run_fprop(prob, "f16", x, w, b, True, algo=wino_tile(prob, "f16"))
+    sub = dict(prob, N=1)
+    for n in (0, prob["N"] - 1):
+        mr, rms, worst = within_bound(y[n:n + 1], sub, x[n:n + 1], w, b, True, "f16", f"image {n}")
+        print(f"c3a image {n}: max_rel {mr:.2e} rms_scaled {rms:.2e} worst err/bound {worst:.3f}")
+    yd = run_fprop(prob, "f16", x, w, b, True)
+    d = (y.float() - yd.float()).abs()
+    assert torch.isfinite(y.float()).all()
+    print(f"c3a Winograd vs band kernel: max |diff| {d.max().item():.3e}, "
+          f"rms {d.pow(2).mean().sqrt().item():.3e}")
