@@ -305,13 +305,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
     const int ngroups = (nrows + C::GR - 1) / C::GR;
     const int prw = wave >> 1;
-    // ---- epilogue, part 2 (I/O waves, one group later): whole pixels
-    // (128-byte lines) from the staging to memory.  I/O wave w stores row w
-    // of the group, 8 pixels per instruction; lane i takes stored chunk i%8
-    // of pixel i/8, i.e. channel chunk (i%8) ^ swizzle(pixel).
-    // 32-bit offsets from the start of the output image (its size is checked
-    // on the host); stores past a row's valid pixels or channels go to an
-    // offset past the range, which the buffer range check drops
+    // Output stores use 32-bit offsets from the start of the output image
+    // (its size is checked on the host); stores past a row's valid pixels or
+    // channels go to an offset past the range, which the range check drops.
     const __amdgpu_buffer_rsrc_t dst_rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)((elem *)a.dst + (size_t)img * a.P * a.Q * a.ngemm), (short)0,
         (int)((size_t)a.P * a.Q * a.ngemm * sizeof(elem)), 0x00020000);
