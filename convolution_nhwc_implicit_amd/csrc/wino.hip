@@ -81,6 +81,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
         for (int cs = 0; cs < 2; ++cs) {
             const int c0 = 32 * cs + 8 * (lane >> 4);
+            // the 8 channels of each tap: one 16-byte load per tap
+            u32x4 gv[9];
+#pragma unroll
+            for (int tap = 0; tap < 9; ++tap)
+                gv[tap] = kok ? *(const u32x4 *)(wk + tap * wn::CIN + c0) : u32x4{0, 0, 0, 0};
             uint32_t packed[wn::XI][4];
 #pragma unroll
             for (int hp = 0; hp < 4; ++hp) {  // channel pairs c0 + 2hp, +1
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                     for (int r = 0; r < 3; ++r)
 #pragma unroll
                         for (int s = 0; s < 3; ++s)
-                            g[r][s] = kok ? E::to_f32(wk[(r * 3 + s) * wn::CIN + c0 + 2 * hp + e]) : 0.0f;
+                            g[r][s] = E::to_f32((elem)(gv[r * 3 + s][hp] >> (16 * e)));
                     float t[4][3];  // G g
 #pragma unroll
                     for (int s = 0; s < 3; ++s) {
@@ -144,15 +149,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int vr_off = tm * wn::VROW;
     const int vr_swz = (tm >> 1) & 7;
 
-    for (int b = L; b < a.batches; b += G) {
-        const int n = b / per_img, rem = b - n * per_img;
+    // ---- input window of batch bb (thread: tile tt, channels 4jc..): 16
+    // 8-byte loads into raw, issued one batch ahead so that their latency
+    // overlaps the previous batch's MFMAs and epilogue
+    uint2 raw[4][4];
+    auto load_windows = [&](int bb) {
+        const int n = bb / per_img, rem = bb - n * per_img;
         const int tr = rem / a.tiles_q, ts = rem - tr * a.tiles_q;
         const int p0 = 2 * tr, q0 = 64 * ts;
-
-        // ---- input window loads (issued before the barrier that frees V)
         const __amdgpu_buffer_rsrc_t src_rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const elem *)a.src + (size_t)n * img_in), (short)0, (int)(img_in * sizeof(elem)), 0x00020000);
-        uint2 raw[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = p0 - a.pad_h + i;
@@ -164,6 +170,14 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 raw[i][j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src_rs, off, 0, 0));
             }
         }
+    };
+    if (L < a.batches) load_windows(L);
+
+    for (int b = L; b < a.batches; b += G) {
+        const int n = b / per_img, rem = b - n * per_img;
+        const int tr = rem / a.tiles_q, ts = rem - tr * a.tiles_q;
+        const int p0 = 2 * tr, q0 = 64 * ts;
+
         __syncthreads();  // the previous batch's MFMAs are done with V
 
         // ---- V = B^T d B, two channels at a time, B^T = [1 0 -1 0; 0 1 1 0;
@@ -204,6 +218,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 *(uint32_t *)(vbuf + xi * wn::TB * wn::VROW + vw_off + 4 * hp) = vout[xi];
         }
         __syncthreads();  // V complete
+        if (b + G < a.batches) load_windows(b + G);  // raw is free again
 
         // ---- 16 GEMMs: M_xi [16 channels x 16 tiles] over 64 input channels
         f32x4 acc[wn::XI];
