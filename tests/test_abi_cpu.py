@@ -271,3 +271,33 @@ def test_bench_names_the_band_kernels():
     assert B.conv2d_plan_info(0, c3a, "f16")["tile"] == bench.BAND_TILE
     assert B.conv2d_plan_info(1, c3a, "f16")["tile"] == bench.BAND_TILE
     assert B.conv2d_plan_info(2, c3a, "f16")["tile"] == bench.WGRAD_BAND_TILE
+
+
+def test_winograd_tile_offered_only_where_it_applies():
+    """fprop's Winograd tile (plan kernel 3) exists for stride-1, dilation-1
+    3x3 problems with 64 input channels and a multiple of 16 output channels,
+    fp16/bf16, without the linear-combination epilogue; it is never the
+    default, needs no workspace, and dgrad does not offer it."""
+    base = problem(2, 64, 10, 12, 64, 3, 3, pad=(1, 1))
+    for dt in ("f16", "bf16"):
+        info = B.conv2d_plan_info(0, base, dt)
+        assert info["num_tiles"] == 7 and info["tile"] == 5 and info["kernel"] == 1
+        w = B.conv2d_plan_info(0, base, dt, algo=dict(tile=7))
+        assert w["kernel"] == 3 and w["tile"] == 6 and w["workspace_bytes"] == 0
+    assert B.conv2d_plan_info(1, base, "f16")["num_tiles"] == 6
+    others = [(base, "i8"),
+              (problem(2, 32, 10, 12, 64, 3, 3, pad=(1, 1)), "f16"),
+              (problem(2, 64, 10, 12, 40, 3, 3, pad=(1, 1)), "f16"),
+              (problem(2, 64, 10, 12, 64, 3, 3, pad=(1, 1), stride=(2, 2)), "f16"),
+              (problem(2, 64, 10, 12, 64, 3, 3, pad=(2, 2), dil=(2, 2)), "bf16"),
+              (problem(2, 64, 10, 12, 64, 5, 5, pad=(2, 2)), "f16")]
+    for prob, dt in others:
+        n = B.conv2d_plan_info(0, prob, dt)["num_tiles"]
+        assert n <= 6, (prob, dt)
+        assert all(B.conv2d_plan_info(0, prob, dt, algo=dict(tile=t))["kernel"] != 3 for t in range(1, n + 1))
+        with pytest.raises(B.Conv2dError) as e:
+            B.conv2d_plan_info(0, prob, dt, algo=dict(tile=7))
+        assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
+    with pytest.raises(B.Conv2dError) as e:
+        B.conv2d_workspace_size_ex(0, base, "f16", algo=dict(tile=7), epi=dict(alpha=2.0, beta=0.0))
+    assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
