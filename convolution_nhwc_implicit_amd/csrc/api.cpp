@@ -170,13 +170,16 @@ bool band_eligible(const Dims &d, int dtype, long long cin, long long src_h, lon
 constexpr int kBandTile = 5;  // tile index of the band kernel (algo tile 6)
 constexpr int kWinoTile = 6;  // fprop: Winograd F(2x2,3x3) (algo tile 7), only when asked for
 
-// Winograd F(2x2, 3x3) fprop: a band-eligible problem (stride 1, 3x3,
-// dilation 1, buffer sizes) with 64 input channels and a multiple of 16
-// output channels.  Never the library's own choice: its rounding differs
-// from the direct sum's.
-bool wino_eligible(const Dims &d, int dtype)
+// Winograd F(2x2, 3x3): a band-eligible problem (stride 1, 3x3, dilation 1,
+// buffer sizes) whose source has 64 channels and whose output channels are a
+// multiple of 16: fprop (x -> y), or dgrad (dy -> dx, the forward
+// convolution of dy padded by 2 - pad, so pad <= 2).  Never the library's
+// own choice: its rounding differs from the direct sum's.
+bool wino_eligible(const Dims &d, int dtype, int op)
 {
-    return wino_supported(dtype, (int)d.R, (int)d.S, (int)d.C, (int)d.dh) && d.K % 16 == 0;
+    if (op == CONV2D_OP_FPROP) return wino_supported(dtype, (int)d.R, (int)d.S, (int)d.C, (int)d.dh) && d.K % 16 == 0;
+    return wino_supported(dtype, (int)d.R, (int)d.S, (int)d.K, (int)d.dh) && d.C % 16 == 0 && d.ph <= 2 &&
+           d.pw <= 2;
 }
 
 // Stride-1 wgrad with the filter shape and channel counts the wgrad band
@@ -399,7 +402,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     // the band kernels have no linear-combination epilogue
     const bool band = !ep.axpby && (op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K, d.P, d.Q)
                                                           : band_eligible(d, dtype, d.K, d.P, d.Q, d.C, d.H, d.W));
-    const bool wino = band && op == CONV2D_OP_FPROP && wino_eligible(d, dtype);
+    const bool wino = band && wino_eligible(d, dtype, op);
     pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0);
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
@@ -415,8 +418,14 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     pl->tile = (algo && algo->tile) ? algo->tile - 1
                : band             ? kBandTile
                                   : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.Cg);
-    // the band kernel reads the filter as it is; the others take a re-laid-out copy
-    pl->ws_bytes = pl->tile == kBandTile ? 0 : round_up((size_t)d.R * d.S * d.C * d.Kg * elem_size(dtype), 256);
+    // the band kernel reads the filter as it is; Winograd takes its transform,
+    // the implicit GEMM a re-laid-out copy
+    if (pl->tile == kWinoTile) {
+        pl->kernel = 3;
+        pl->ws_bytes = round_up((size_t)16 * d.C * d.K * elem_size(dtype), 256);
+    } else {
+        pl->ws_bytes = pl->tile == kBandTile ? 0 : round_up((size_t)d.R * d.S * d.C * d.Kg * elem_size(dtype), 256);
+    }
     return CONV2D_OK;
 }
 
@@ -465,6 +474,23 @@ int run_band(int dtype, const Dims &d, int cin, const void *src, int H, int W, c
     const int gn = (ngemm + 63) / 64, gq = (Q + seg - 1) / seg;
     band_rows(b, (long long)gn * gq);
     return hip_status(launch_band(dtype, (int)d.R, (int)d.S, cin, (int)d.dh, b, gn, gq, s));
+}
+
+// Winograd launch: batches of 2 output rows x 64 columns over a persistent
+// grid of about one workgroup per CU across the 64-channel slices, a multiple
+// of 8 (one share per XCD) when there are that many batches.
+int run_wino(int dtype, const Dims &d, WinoArgs &wa, hipStream_t s)
+{
+    wa.tile_rows = (wa.P + 1) / 2;
+    wa.tiles_q = (wa.Q + 63) / 64;
+    const long long batches = d.N * wa.tile_rows * wa.tiles_q;
+    if (batches > INT32_MAX) return CONV2D_ERR_UNSUPPORTED;
+    wa.batches = (int)batches;
+    const long long slices = (wa.ngemm + 63) / 64;
+    long long gx = std::max(1LL, (long long)kNumCUs / slices);
+    gx = std::min(gx, batches);
+    if (gx >= 8) gx -= gx % 8;
+    return hip_status(launch_wino_fprop(dtype, wa, (int)gx, s));
 }
 
 }  // namespace
@@ -618,21 +644,10 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     if (pl.tile == kWinoTile) {
         WinoArgs wa;
         memset(&wa, 0, sizeof(wa));
-        wa.src = x; wa.w = w; wa.bias = bias; wa.dst = y;
+        wa.src = x; wa.w = w; wa.u = nullptr; wa.bias = bias; wa.dst = y;
         wa.N = (int)d.N; wa.H = (int)d.H; wa.W = (int)d.W; wa.P = (int)d.P; wa.Q = (int)d.Q;
         wa.ngemm = (int)d.K; wa.pad_h = (int)d.ph; wa.pad_w = (int)d.pw; wa.relu = relu;
-        wa.tile_rows = (int)((d.P + 1) / 2);
-        wa.tiles_q = (int)((d.Q + 63) / 64);
-        const long long batches = d.N * wa.tile_rows * wa.tiles_q;
-        if (batches > INT32_MAX) return CONV2D_ERR_UNSUPPORTED;
-        wa.batches = (int)batches;
-        // persistent: about one workgroup per CU over the channel slices,
-        // a multiple of 8 (one share per XCD) when there are that many batches
-        const long long slices = (d.K + 63) / 64;
-        long long gx = std::max(1LL, (long long)kNumCUs / slices);
-        gx = std::min(gx, batches);
-        if (gx >= 8) gx -= gx % 8;
-        return hip_status(launch_wino_fprop(dtype, wa, (int)gx, s));
+        return run_wino(dtype, d, wa, s);
     }
 
     IgemmArgs a;
@@ -717,6 +732,14 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
         return hip_status(launch_direct_dgrad(dtype, a, s));
     }
 
+    if (pl.tile == kWinoTile) {  // the forward Winograd kernel on dy, with the flipped, transposed filter
+        WinoArgs wa;
+        memset(&wa, 0, sizeof(wa));
+        wa.src = dy; wa.w = w; wa.u = workspace; wa.bias = nullptr; wa.dst = dx;
+        wa.N = (int)d.N; wa.H = (int)d.P; wa.W = (int)d.Q; wa.P = (int)d.H; wa.Q = (int)d.W;
+        wa.ngemm = (int)d.C; wa.pad_h = (int)(2 - d.ph); wa.pad_w = (int)(2 - d.pw); wa.relu = 0;
+        return run_wino(dtype, d, wa, s);
+    }
     if (pl.tile == kBandTile)  // stride 1: every tap, filter read reversed and transposed
         return run_band(dtype, d, (int)d.K, dy, (int)d.P, (int)d.Q, w, 1, nullptr, 0, 0.0, dx, (int)d.H, (int)d.W,
                         (int)d.C, (int)(d.dh * (d.R - 1) - d.ph), (int)(d.dw * (d.S - 1) - d.pw), s);

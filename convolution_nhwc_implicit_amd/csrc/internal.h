@@ -138,7 +138,8 @@ hipError_t launch_band(int dtype, int R, int S, int cin, int dil, const BandArgs
 // ---------------------------------------------------------------------------
 struct WinoArgs {
     const void *src;
-    const void *w;
+    const void *w;  // filter [ngemm][3][3][64] (fprop) or [64][3][3][ngemm] (dgrad)
+    void *u;        // dgrad: workspace for the transformed filter U[16][ngemm][64]; null for fprop
     const void *bias;
     void *dst;
     int N, H, W, P, Q, ngemm;

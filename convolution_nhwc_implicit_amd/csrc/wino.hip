@@ -1,5 +1,7 @@
-// wino.hip -- Winograd F(2x2, 3x3) forward convolution for stride-1 3x3
-// layers with 64 input channels, on 16x16x32 MFMAs (gfx950).
+// wino.hip -- Winograd F(2x2, 3x3) for stride-1 3x3 layers with 64 input
+// channels, on 16x16x32 MFMAs (gfx950): fprop, and dgrad as the forward
+// convolution of dy (64 channels) with the filter's taps reversed and its
+// channel axes swapped, padded by 2 - pad.
 //
 // The tensorcore "Conv2D" page ("What's not done in v0.1") names a Winograd
 // path for 3x3 stride-1 layers as a later priority.  F(2x2, 3x3) (Lavin and
@@ -58,7 +60,46 @@ constexpr int VROW = CIN * 2;           // bytes of one (point, tile) row of V
 constexpr int V_BYTES = XI * TB * VROW;  // 64 KB
 }  // namespace wn
 
+// dgrad: the transformed filter of the equivalent forward convolution of dy,
+// whose filter is w'[c][r][s][k] = w[k][2-r][2-s][c] (taps reversed, channel
+// axes swapped): U[xi][c][k] = (G w'_ck G^T)[xi] for every dx channel
+// c < ngemm and dy channel k < 64, in fp32, rounded once, into the workspace.
+// One thread per (k, c), c fastest, so the filter reads are coalesced.
 template <class E>
+__global__ __launch_bounds__(256) void wino_dgrad_filter_kernel(const void *w, void *u, int ngemm)
+{
+    using elem = typename E::elem;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= ngemm * wn::CIN) return;
+    const int k = i / ngemm, c = i - k * ngemm;
+    const elem *wk = (const elem *)w + (size_t)k * 9 * ngemm + c;
+    float g[3][3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int s = 0; s < 3; ++s) g[r][s] = E::to_f32(wk[((2 - r) * 3 + (2 - s)) * ngemm]);
+    float t[4][3];  // G g
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        t[0][s] = g[0][s];
+        t[1][s] = 0.5f * (g[0][s] + g[1][s] + g[2][s]);
+        t[2][s] = 0.5f * (g[0][s] - g[1][s] + g[2][s]);
+        t[3][s] = g[2][s];
+    }
+    elem *uo = (elem *)u + (size_t)c * wn::CIN + k;
+    const size_t pstride = (size_t)ngemm * wn::CIN;  // between points
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // (G g) G^T
+        uo[(4 * r + 0) * pstride] = E::from_f32(t[r][0]);
+        uo[(4 * r + 1) * pstride] = E::from_f32(0.5f * (t[r][0] + t[r][1] + t[r][2]));
+        uo[(4 * r + 2) * pstride] = E::from_f32(0.5f * (t[r][0] - t[r][1] + t[r][2]));
+        uo[(4 * r + 3) * pstride] = E::from_f32(t[r][2]);
+    }
+}
+
+// UWS: U comes ready from the workspace (dgrad) instead of being formed from
+// the filter in the prologue (fprop).
+template <class E, bool UWS>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void wino_fprop_kernel(
     const WinoArgs a)
 {
@@ -74,7 +115,17 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // 32cs + 8(lane >> 4) + 0..7.  U = G g G^T with G = [1 0 0; h h h; h -h h;
     // 0 0 1], h = 1/2, computed in fp32 and rounded once.
     u32x4 uf[wn::XI][2];
-    {
+    if constexpr (UWS) {
+        // U[xi][k][c] from the workspace, one 16-byte load per fragment
+        const int kr = k0 + 16 * kg + (lane & 15);
+        const bool kok = kr < a.ngemm;
+        const elem *uk = (const elem *)a.u + (size_t)(kok ? kr : 0) * wn::CIN + 8 * (lane >> 4);
+#pragma unroll
+        for (int xi = 0; xi < wn::XI; ++xi)
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs)
+                uf[xi][cs] = kok ? *(const u32x4 *)(uk + (size_t)xi * a.ngemm * wn::CIN + 32 * cs) : u32x4{0, 0, 0, 0};
+    } else {
         const int kr = k0 + 16 * kg + (lane & 15);
         const bool kok = kr < a.ngemm;
         const elem *wk = (const elem *)a.w + (size_t)(kok ? kr : 0) * 9 * wn::CIN;
@@ -282,9 +333,24 @@ bool wino_supported(int dtype, int R, int S, int cin, int dil)
 hipError_t launch_wino_fprop(int dtype, const WinoArgs &a, int grid_x, hipStream_t st)
 {
     dim3 grid((unsigned)grid_x, (unsigned)((a.ngemm + wn::BK - 1) / wn::BK));
+    const unsigned fblocks = (unsigned)((a.ngemm * wn::CIN + 255) / 256);
     switch (dtype) {
-    case CONV2D_DTYPE_F16: wino_fprop_kernel<EF16><<<grid, wn::NT, 0, st>>>(a); break;
-    case CONV2D_DTYPE_BF16: wino_fprop_kernel<EBF16><<<grid, wn::NT, 0, st>>>(a); break;
+    case CONV2D_DTYPE_F16:
+        if (a.u) {
+            wino_dgrad_filter_kernel<EF16><<<fblocks, 256, 0, st>>>(a.w, a.u, a.ngemm);
+            wino_fprop_kernel<EF16, true><<<grid, wn::NT, 0, st>>>(a);
+        } else {
+            wino_fprop_kernel<EF16, false><<<grid, wn::NT, 0, st>>>(a);
+        }
+        break;
+    case CONV2D_DTYPE_BF16:
+        if (a.u) {
+            wino_dgrad_filter_kernel<EBF16><<<fblocks, 256, 0, st>>>(a.w, a.u, a.ngemm);
+            wino_fprop_kernel<EBF16, true><<<grid, wn::NT, 0, st>>>(a);
+        } else {
+            wino_fprop_kernel<EBF16, false><<<grid, wn::NT, 0, st>>>(a);
+        }
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -197,12 +197,12 @@ def test_every_tile_on_band_eligible_problem():
     ref_y = oracle_fprop_out(prob, "f16", x, w, b, False)
     ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
     info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")
-    # the band kernel is the default; fprop's last tile is Winograd F(2x2,3x3),
+    # the band kernel is the default; the last tile is Winograd F(2x2,3x3),
     # exact here because the transformed integer operands are exact in fp16
     assert info["num_tiles"] == 7 and info["tile"] == 5
     assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16", algo=dict(tile=7))["kernel"] == 3
     dinfo = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16")
-    assert dinfo["num_tiles"] == 6 and dinfo["tile"] == 5
+    assert dinfo["num_tiles"] == 7 and dinfo["tile"] == 5  # dgrad's last tile is Winograd too
     for t in range(1, info["num_tiles"] + 1):
         check(f64(run_fprop(prob, "f16", x, w, b, False, algo=dict(tile=t))), ref_y, "f16", "exact", f"tile {t}")
     for t in range(1, dinfo["num_tiles"] + 1):

@@ -24,7 +24,7 @@ from convolution_nhwc_implicit_amd import binding as B
 from convolution_nhwc_implicit_amd import workloads as WL
 from convolution_nhwc_implicit_amd.workloads import problem
 
-from parity import check, f64, run_fprop
+from parity import check, f64, run_dgrad, run_fprop
 
 pytestmark = pytest.mark.gpu
 
@@ -111,3 +111,50 @@ def test_winograd_full_size_c3a():
     assert torch.isfinite(y.float()).all()
     print(f"c3a Winograd vs band kernel: max |diff| {d.max().item():.3e}, "
           f"rms {d.pow(2).mean().sqrt().item():.3e}")
+
+
+# ---- dgrad: the forward Winograd kernel on dy (K = 64 channels) with the
+# filter's taps reversed and channel axes swapped, padded by 2 - pad
+def dgrad_as_fprop(prob, w):
+    """The forward problem and filter w'[c][r][s][k] = w[k][2-r][2-s][c] whose
+    fprop of dy is dgrad(dy, w) for a stride-1 3x3 problem."""
+    P, Q = oracle.output_hw(prob)
+    fp = problem(prob["N"], prob["K"], P, Q, prob["C"], 3, 3, pad=(2 - prob["pad_h"], 2 - prob["pad_w"]))
+    wf = np.ascontiguousarray(np.transpose(f64(w)[:, ::-1, ::-1, :], (3, 1, 2, 0)))
+    return fp, torch.from_numpy(wf)
+
+
+def run_dgrad_wino(prob, dtype, dy, w):
+    algo = dict(tile=B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, dtype)["num_tiles"])
+    assert B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, dtype, algo=algo)["kernel"] == 3
+    return run_dgrad(prob, dtype, dy, w, algo=algo, fill=float("nan"))
+
+
+EXACT_D = [
+    ("d_odd_two_segments", problem(2, 64, 13, 71, 64, 3, 3, pad=(1, 1)), "f16"),
+    ("d_pad0_c16", problem(3, 16, 9, 10, 64, 3, 3), "bf16"),
+    ("d_pad2_c48", problem(2, 48, 7, 8, 64, 3, 3, pad=(2, 2)), "f16"),
+    ("d_c128_two_slices", problem(2, 128, 12, 20, 64, 3, 3, pad=(1, 1)), "bf16"),
+]
+
+
+@pytest.mark.parametrize("cid,prob,dtype", EXACT_D, ids=[c[0] for c in EXACT_D])
+def test_winograd_dgrad_exact_on_integers(cid, prob, dtype):
+    P, Q = oracle.output_hw(prob)
+    _, w, _, dy = WL.random_case(prob, dtype, "int", 7200 + len(cid), P, Q, bias=False)
+    dx = run_dgrad_wino(prob, dtype, dy, w)
+    check(f64(dx), oracle.dgrad(prob, f64(dy), f64(w)), dtype, "exact", cid)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_winograd_dgrad_within_derived_bound(dtype):
+    prob = problem(4, 64, 17, 23, 64, 3, 3, pad=(1, 1))
+    P, Q = oracle.output_hw(prob)
+    _, w, _, dy = WL.random_case(prob, dtype, "gauss", 7300, P, Q, bias=False)
+    dx = run_dgrad_wino(prob, dtype, dy, w)
+    fp, wf = dgrad_as_fprop(prob, w)
+    # the equivalent forward problem reproduces the direct dgrad
+    ref = oracle.dgrad(prob, f64(dy), f64(w))
+    assert np.max(np.abs(oracle.fprop(fp, f64(dy), f64(wf)) - ref)) <= 1e-12 * np.max(np.abs(ref))
+    max_rel, rms, worst = within_bound(dx, fp, dy, wf, None, False, dtype, f"dgrad {dtype}")
+    print(f"dgrad {dtype}: max_rel {max_rel:.2e} rms_scaled {rms:.2e} worst err/bound {worst:.3f}")
