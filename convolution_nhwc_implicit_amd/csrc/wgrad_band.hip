@@ -322,8 +322,8 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     }
 
     // ---- the four phases' sums, in a fixed order (p0 + p2) + (p1 + p3),
-    // through LDS (the buffers are idle now).  Round 1: phases 2 and 3 park
-    // all their accumulators, phases 0 and 1 add them.  Round 2: phase 0
+    // through LDS (the buffers are idle now).  Step 1: phases 2 and 3 park
+    // all their accumulators, phases 0 and 1 add them.  Step 2: phase 0
     // keeps k-block 0 and phase 1 k-block 1; each parks the other block and
     // adds the one parked for it, then stores its rows of the partial tile.
     // A parked block set is [blocks*4][64 lanes] of 16-byte pieces (4
