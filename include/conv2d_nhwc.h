@@ -99,12 +99,14 @@ typedef struct conv2d_problem {
  *            fixed order by a second kernel).  Ignored by fprop and dgrad.
  *            For groups > 1, tile 1 is the one-thread-per-output direct
  *            kernel and tile 2 (when it applies) the LDS-tiled one.
- *            fprop of a stride-1, dilation-1 3x3 problem with 64 input
- *            channels and a multiple of 16 output channels (fp16/bf16, no
- *            linear-combination epilogue) also offers, as its last tile,
- *            Winograd F(2x2, 3x3), the faster 3x3 stride-1 path the
- *            tensorcore "Conv2D" page plans ("What's not done in v0.1").  It
- *            is never the library's choice: it rounds the transformed filter
+ *            A stride-1, dilation-1 3x3 problem (fp16/bf16, no
+ *            linear-combination epilogue) also offers, as the last tile of
+ *            fprop when C = 64 and K % 16 == 0, and of dgrad when K = 64,
+ *            C % 16 == 0 and pad <= 2, Winograd F(2x2, 3x3), the faster 3x3
+ *            stride-1 path the tensorcore "Conv2D" page plans ("What's not
+ *            done in v0.1").  dgrad then needs workspace for the transformed
+ *            filter (16*C*K elements).  It is never the library's choice: it
+ *            rounds the transformed filter
  *            and input tiles to the 16-bit type before the products, so its
  *            results differ from the direct sum by a few units of that
  *            type's rounding of the transformed terms (exact on
