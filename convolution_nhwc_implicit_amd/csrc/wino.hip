@@ -104,7 +104,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const WinoArgs a)
 {
     using elem = typename E::elem;
-    __shared__ __attribute__((aligned(16))) unsigned char vbuf[wn::V_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char vbuf[2 * wn::V_BYTES];  // V double-buffered
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = wave & 3, tg = wave >> 2;
@@ -222,54 +222,63 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
         }
     };
-    if (L < a.batches) load_windows(L);
+    auto transform = [&](unsigned char *vb) {
+    // ---- V = B^T d B, two channels at a time, B^T = [1 0 -1 0; 0 1 1 0;
+    // 0 -1 1 0; 0 1 0 -1]
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+        float d[2][4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t word = hp ? raw[i][j].y : raw[i][j].x;
+                d[0][i][j] = E::to_f32((elem)(word & 0xffffu));
+                d[1][i][j] = E::to_f32((elem)(word >> 16));
+            }
+        uint32_t vout[wn::XI];
+#pragma unroll
+        for (int xi = 0; xi < wn::XI; ++xi) vout[xi] = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float t[4][4];  // B^T d
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                t[0][j] = d[e][0][j] - d[e][2][j];
+                t[1][j] = d[e][1][j] + d[e][2][j];
+                t[2][j] = d[e][2][j] - d[e][1][j];
+                t[3][j] = d[e][1][j] - d[e][3][j];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {  // (B^T d) B
+                const float v[4] = {t[r][0] - t[r][2], t[r][1] + t[r][2], t[r][2] - t[r][1], t[r][1] - t[r][3]};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vout[4 * r + c] |= (uint32_t)E::from_f32(v[c]) << (16 * e);
+            }
+        }
+#pragma unroll
+        for (int xi = 0; xi < wn::XI; ++xi)
+            *(uint32_t *)(vb + xi * wn::TB * wn::VROW + vw_off + 4 * hp) = vout[xi];
+    }
+    };
+    if (L < a.batches) {
+        load_windows(L);
+        transform(vbuf);
+        if (L + G < a.batches) load_windows(L + G);
+    }
+    __syncthreads();  // the first batch's V is complete
 
-    for (int b = L; b < a.batches; b += G) {
+    for (int b = L, it = 0; b < a.batches; b += G, ++it) {
         const int n = b / per_img, rem = b - n * per_img;
         const int tr = rem / a.tiles_q, ts = rem - tr * a.tiles_q;
         const int p0 = 2 * tr, q0 = 64 * ts;
 
-        __syncthreads();  // the previous batch's MFMAs are done with V
-
-        // ---- V = B^T d B, two channels at a time, B^T = [1 0 -1 0; 0 1 1 0;
-        // 0 -1 1 0; 0 1 0 -1]
-#pragma unroll
-        for (int hp = 0; hp < 2; ++hp) {
-            float d[2][4][4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t word = hp ? raw[i][j].y : raw[i][j].x;
-                    d[0][i][j] = E::to_f32((elem)(word & 0xffffu));
-                    d[1][i][j] = E::to_f32((elem)(word >> 16));
-                }
-            uint32_t vout[wn::XI];
-#pragma unroll
-            for (int xi = 0; xi < wn::XI; ++xi) vout[xi] = 0;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                float t[4][4];  // B^T d
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    t[0][j] = d[e][0][j] - d[e][2][j];
-                    t[1][j] = d[e][1][j] + d[e][2][j];
-                    t[2][j] = d[e][2][j] - d[e][1][j];
-                    t[3][j] = d[e][1][j] - d[e][3][j];
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {  // (B^T d) B
-                    const float v[4] = {t[r][0] - t[r][2], t[r][1] + t[r][2], t[r][2] - t[r][1], t[r][1] - t[r][3]};
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) vout[4 * r + c] |= (uint32_t)E::from_f32(v[c]) << (16 * e);
-                }
-            }
-#pragma unroll
-            for (int xi = 0; xi < wn::XI; ++xi)
-                *(uint32_t *)(vbuf + xi * wn::TB * wn::VROW + vw_off + 4 * hp) = vout[xi];
+        // the next batch's V into the other buffer, then this batch's MFMAs
+        if (b + G < a.batches) {
+            transform(vbuf + ((it + 1) & 1) * wn::V_BYTES);
+            if (b + 2 * G < a.batches) load_windows(b + 2 * G);  // raw is free again
         }
-        __syncthreads();  // V complete
-        if (b + G < a.batches) load_windows(b + G);  // raw is free again
+        const unsigned char *vcur = vbuf + (it & 1) * wn::V_BYTES;
 
         // ---- 16 GEMMs: M_xi [16 channels x 16 tiles] over 64 input channels
         f32x4 acc[wn::XI];
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
             for (int cs = 0; cs < 2; ++cs) {
                 const int ch = ((4 * cs + (lane >> 4)) ^ vr_swz) << 4;
-                const u32x4 vf = *(const u32x4 *)(vbuf + xi * wn::TB * wn::VROW + vr_off + ch);
+                const u32x4 vf = *(const u32x4 *)(vcur + xi * wn::TB * wn::VROW + vr_off + ch);
                 acc[xi] = E::mfma(uf[xi][cs], vf, acc[xi]);
             }
         }
@@ -321,6 +330,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             store(BoolConst<true>{});
         else
             store(BoolConst<false>{});
+        // the next batch's V is complete; this batch's buffer is free for the
+        // batch after next
+        __syncthreads();
     }
 }
 
