@@ -26,6 +26,9 @@
 //     for every batch; only V goes through LDS.  The grid is persistent (one
 //     workgroup per CU and channel slice) so the filter is transformed once
 //     per CU.
+//   * V is double-buffered in LDS (2 x 64 KB): each batch step forms the next
+//     batch's V, then runs this batch's MFMAs and epilogue, one barrier per
+//     batch, so the two waves of a SIMD overlap transform and MFMA work.
 //   * V: thread (tile t, channels 4j..4j+3) reads its 4x4 input window from
 //     HBM/L2 (8-byte loads; padding from the buffer range check), forms
 //     B^T d B in fp32 two channels at a time, rounds once and writes V into
