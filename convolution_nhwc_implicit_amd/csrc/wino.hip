@@ -225,44 +225,41 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
         }
     };
+    // ---- V = B^T d B of this thread's tile and 4 channels, into buffer vb:
+    // two channels at a time in fp32, each pair rounded once by one packed
+    // conversion.  B^T = [1 0 -1 0; 0 1 1 0; 0 -1 1 0; 0 1 0 -1].
     auto transform = [&](unsigned char *vb) {
-    // ---- V = B^T d B, two channels at a time, B^T = [1 0 -1 0; 0 1 1 0;
-    // 0 -1 1 0; 0 1 0 -1]
 #pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {
-        float d[2][4][4];
+        for (int hp = 0; hp < 2; ++hp) {
+            float v[2][wn::XI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int e = 0; e < 2; ++e) {
+                float d[4][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t word = hp ? raw[i][j].y : raw[i][j].x;
-                d[0][i][j] = E::to_f32((elem)(word & 0xffffu));
-                d[1][i][j] = E::to_f32((elem)(word >> 16));
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        d[i][j] = E::to_f32((elem)(((hp ? raw[i][j].y : raw[i][j].x) >> (16 * e)) & 0xffffu));
+                float t[4][4];  // B^T d
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    t[0][j] = d[0][j] - d[2][j];
+                    t[1][j] = d[1][j] + d[2][j];
+                    t[2][j] = d[2][j] - d[1][j];
+                    t[3][j] = d[1][j] - d[3][j];
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {  // (B^T d) B
+                    v[e][4 * r + 0] = t[r][0] - t[r][2];
+                    v[e][4 * r + 1] = t[r][1] + t[r][2];
+                    v[e][4 * r + 2] = t[r][2] - t[r][1];
+                    v[e][4 * r + 3] = t[r][1] - t[r][3];
+                }
             }
-        uint32_t vout[wn::XI];
 #pragma unroll
-        for (int xi = 0; xi < wn::XI; ++xi) vout[xi] = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            float t[4][4];  // B^T d
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                t[0][j] = d[e][0][j] - d[e][2][j];
-                t[1][j] = d[e][1][j] + d[e][2][j];
-                t[2][j] = d[e][2][j] - d[e][1][j];
-                t[3][j] = d[e][1][j] - d[e][3][j];
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {  // (B^T d) B
-                const float v[4] = {t[r][0] - t[r][2], t[r][1] + t[r][2], t[r][2] - t[r][1], t[r][1] - t[r][3]};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) vout[4 * r + c] |= (uint32_t)E::from_f32(v[c]) << (16 * e);
-            }
+            for (int xi = 0; xi < wn::XI; ++xi)
+                *(uint32_t *)(vb + xi * wn::TB * wn::VROW + vw_off + 4 * hp) = Pack2<E>::cvt(f2v{v[0][xi], v[1][xi]});
         }
-#pragma unroll
-        for (int xi = 0; xi < wn::XI; ++xi)
-            *(uint32_t *)(vb + xi * wn::TB * wn::VROW + vw_off + 4 * hp) = vout[xi];
-    }
     };
     if (L < a.batches) {
         load_windows(L);
