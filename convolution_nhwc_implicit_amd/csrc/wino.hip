@@ -20,7 +20,7 @@
 // points: sixteen 16x16 accumulators, so the inverse transform needs no
 // exchange between lanes (a lane holds one tile and four channels of each).
 //
-//   * U: the wave's 16 channels x 64 input channels x 16 points in fp16/bf16
+//   * U: the wave's 16 channels x 64 input channels x 16 points in fp16
 //     are 32 A fragments of 16 bytes a lane (128 VGPRs), computed once per
 //     workgroup from the filter (in fp32, rounded once) and kept in registers
 //     for every batch; only V goes through LDS.  The grid is persistent (one
@@ -38,8 +38,9 @@
 //   * Epilogue: A^T M A in fp32 per lane, + bias, ReLU, one rounding; each
 //     lane stores its four channels (8 bytes) of four output pixels.
 //
-// Numerics differ from the direct convolution: U and V are rounded to the
-// 16-bit type before the products, so each product carries up to ~2 units
+// fp16 only (bf16's 8-bit significand would leave rms_scaled near 4e-3).
+// Numerics differ from the direct convolution: U and V are rounded to fp16
+// before the products, so each product carries up to ~2 units
 // of that type's rounding of the transformed terms.  Integer-valued data
 // small enough that U (quarter-integers) and V are exact give exactly the
 // direct result.
@@ -336,10 +337,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
 }
 
+// fp16 only: with bf16's 8-bit significand, the one rounding of U and V
+// before the products leaves rms_scaled near 4e-3 on Gaussian data, above the
+// 1e-3 every other path meets, so bf16 problems are not offered this tile.
 bool wino_supported(int dtype, int R, int S, int cin, int dil)
 {
-    return (dtype == CONV2D_DTYPE_F16 || dtype == CONV2D_DTYPE_BF16) && R == 3 && S == 3 && dil == 1 &&
-           cin == wn::CIN;
+    return dtype == CONV2D_DTYPE_F16 && R == 3 && S == 3 && dil == 1 && cin == wn::CIN;
 }
 
 hipError_t launch_wino_fprop(int dtype, const WinoArgs &a, int grid_x, hipStream_t st)
@@ -353,14 +356,6 @@ hipError_t launch_wino_fprop(int dtype, const WinoArgs &a, int grid_x, hipStream
             wino_fprop_kernel<EF16, true><<<grid, wn::NT, 0, st>>>(a);
         } else {
             wino_fprop_kernel<EF16, false><<<grid, wn::NT, 0, st>>>(a);
-        }
-        break;
-    case CONV2D_DTYPE_BF16:
-        if (a.u) {
-            wino_dgrad_filter_kernel<EBF16><<<fblocks, 256, 0, st>>>(a.w, a.u, a.ngemm);
-            wino_fprop_kernel<EBF16, true><<<grid, wn::NT, 0, st>>>(a);
-        } else {
-            wino_fprop_kernel<EBF16, false><<<grid, wn::NT, 0, st>>>(a);
         }
         break;
     default: return hipErrorInvalidValue;

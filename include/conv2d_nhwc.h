@@ -97,19 +97,23 @@ typedef struct conv2d_problem {
  *   split_k: 0 = library choice, otherwise the number of slices the wgrad
  *            reduction over N*P*Q is cut into (partials are summed in a
  *            fixed order by a second kernel).  Ignored by fprop and dgrad.
- *            For groups > 1, tile 1 is the one-thread-per-output direct
- *            kernel and tile 2 (when it applies) the LDS-tiled one.
- *            A stride-1, dilation-1 3x3 problem (fp16/bf16, no
+ *            For groups > 1 whose channels per group are not whole 16-byte
+ *            vectors (C/G or K/G not a multiple of 8; 16 for int8), tile 1
+ *            is the one-thread-per-output direct kernel and tile 2 (when it
+ *            applies) the LDS-tiled or depthwise one; other grouped problems
+ *            run one implicit GEMM per group on the implicit-GEMM tiles.
+ *            A stride-1, dilation-1 3x3 fp16 problem (no
  *            linear-combination epilogue) also offers, as the last tile of
  *            fprop when C = 64 and K % 16 == 0, and of dgrad when K = 64,
  *            C % 16 == 0 and pad <= 2, Winograd F(2x2, 3x3), the faster 3x3
  *            stride-1 path the tensorcore "Conv2D" page plans ("What's not
  *            done in v0.1").  dgrad then needs workspace for the transformed
- *            filter (16*C*K elements).  It is never the library's choice: it
- *            rounds the transformed filter
- *            and input tiles to the 16-bit type before the products, so its
- *            results differ from the direct sum by a few units of that
- *            type's rounding of the transformed terms (exact on
+ *            filter (16*C*K elements).  bf16 problems are not offered it
+ *            (its rounding of the transformed operands to bf16 would leave
+ *            rms_scaled near 4e-3).  It is never the library's choice: it
+ *            rounds the transformed filter and input tiles to fp16 before
+ *            the products, so its results differ from the direct sum by a
+ *            few units of fp16 rounding of the transformed terms (exact on
  *            integer-valued data whose transforms are exact).
  */
 typedef struct conv2d_algo {

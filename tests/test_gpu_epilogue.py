@@ -3,8 +3,8 @@ beta * C, and wgrad's fp32 output) against the oracle, through the C ABI, on
 every kernel family: the implicit GEMM (fprop, strided dgrad phases, generic
 wgrad), shapes the band kernels would take (fprop/dgrad then run on the
 implicit GEMM; wgrad keeps the band kernel and applies the epilogue in its
-reduction), the tiled and one-thread-per-output direct kernels, and the
-zero-padded channel path.  Integer-valued data with alpha = 2, beta = -1 is
+reduction), the grouped implicit GEMM, the LDS-tiled and
+one-thread-per-output direct kernels, and the zero-padded channel path.  Integer-valued data with alpha = 2, beta = -1 is
 exact in fp32, so those outputs must equal the oracle's rounded once."""
 import zlib
 
@@ -28,7 +28,11 @@ CASES = [
     # inside it and reduced with the weight gradient
     ("wband_shape", problem(2, 64, 10, 12, 64, 3, 3, pad=(1, 1)), "bf16", "int"),
     ("wband_gauss", problem(3, 64, 9, 16, 64, 3, 3, pad=(1, 1)), "f16", "gauss"),
-    ("grouped_tiled", problem(2, 32, 11, 9, 48, 3, 3, pad=(1, 1), groups=2), "f16", "int"),
+    ("grouped_gemm", problem(2, 32, 11, 9, 48, 3, 3, pad=(1, 1), groups=2), "f16", "int"),
+    # LDS-tiled direct kernels: fprop and wgrad (C/G = 8, K/G = 4), dgrad (C/G = 4, K/G = 8)
+    ("direct_tiled_fw", problem(2, 16, 9, 10, 8, 3, 3, pad=(1, 1), groups=2), "f16", "int"),
+    ("direct_tiled_d", problem(2, 8, 11, 9, 16, 3, 3, pad=(1, 1), groups=2), "bf16", "int"),
+    ("direct_tiled_gauss", problem(2, 24, 12, 13, 12, 3, 3, pad=(1, 1), groups=3), "bf16", "gauss"),
     ("grouped_naive", problem(2, 12, 9, 10, 8, 3, 3, pad=(1, 1), groups=2), "bf16", "int"),
     ("padded_c3_k13", problem(2, 3, 17, 15, 13, 5, 5, pad=(2, 2), stride=(2, 2)), "f16", "int"),
     ("gauss", problem(2, 24, 12, 11, 40, 3, 3, pad=(1, 1)), "bf16", "gauss"),
@@ -56,6 +60,11 @@ def ws_for(op, prob, dtype, epi):
 
 @pytest.mark.parametrize("cid,prob,dtype,dist", CASES, ids=[c[0] for c in CASES])
 def test_epilogue_all_passes(cid, prob, dtype, dist):
+    if cid.startswith("direct_tiled"):  # the kernels under test are the ones planned
+        ops = (B.CONV2D_OP_DGRAD,) if cid == "direct_tiled_d" else (B.CONV2D_OP_FPROP, B.CONV2D_OP_WGRAD)
+        for op in ops:
+            info = B.conv2d_plan_info(op, prob, dtype)
+            assert info["kernel"] == 2 and info["tile"] == 1, (op, info)
     mode = "exact" if dist == "int" else "tol"
     alpha, beta = coefs(dist)
     x, w, b, dy, cy, cx, cw = inputs(cid, prob, dtype, dist)

@@ -31,10 +31,20 @@ def draw_problem(rng, kind):
         C, K = (8 * int(v) for v in rng.integers(1, 13, size=2))
     elif kind == "dense_odd":
         C, K = (int(v) for v in rng.integers(1, 41, size=2))
-    elif kind == "grouped":  # half with whole 16-byte channel vectors per group (LDS-tiled kernels)
+    elif kind == "grouped":
+        # a third each: whole 16-byte channel vectors per group (one implicit
+        # GEMM per group); 8-channel vectors on one side and an odd multiple
+        # of 4 channels on the other (the LDS-tiled direct kernels); any
+        # counts (the one-thread-per-output kernel)
         G = int(rng.integers(2, 5))
-        vec = 8 if rng.integers(0, 2) == 0 else 1
-        C, K = (G * vec * int(v) for v in rng.integers(1, 25 if vec == 1 else 5, size=2))
+        mode = int(rng.integers(0, 3))
+        if mode == 0:
+            C, K = (G * 8 * int(v) for v in rng.integers(1, 5, size=2))
+        elif mode == 1:
+            a, b = 8 * int(rng.integers(1, 4)), 4 * (2 * int(rng.integers(0, 3)) + 1)
+            C, K = (G * a, G * b) if rng.integers(0, 2) == 0 else (G * b, G * a)
+        else:
+            C, K = (G * int(v) for v in rng.integers(1, 25, size=2))
     elif kind == "stem":  # few input channels, a wide filter, stride 2 (zero-padded channels)
         C, K = int(rng.integers(1, 8)), 8 * int(rng.integers(1, 9))
         R = S = int(rng.choice([3, 5, 7]))

@@ -467,3 +467,64 @@ def test_winograd_single_tap_and_errors():
     assert np.all(y[..., 1] == 0)
     with pytest.raises(ValueError):
         WG.fprop(problem(1, 2, 5, 6, 2, 3, 3, pad=(1, 1), stride=(2, 2)), x, w)
+
+
+# ---- oracle.winograd.error_bound pinned from both sides by a simulation of
+# the rounded arithmetic: U = G g G^T and V = B^T d B formed in fp32 and
+# rounded once to the 16-bit type, fp32 products and sums over the channels
+# in order, the inverse transform in fp32 (no output rounding).  The bound must
+# hold for every output, and must not be loose: with one channel (few terms,
+# little cancellation of rounding errors) the worst output reaches a quarter of
+# it, with 64 channels (the kernel's shape) a twenty-fifth.
+def _wino_rounded_sim(prob, x, w, dtype):
+    from oracle import winograd as WG
+    f32 = np.float32
+
+    def r16(a):
+        return oracle.bits_to_f64(oracle.round_to(np.asarray(a, dtype=np.float64), dtype), dtype).astype(f32)
+
+    d, P, Q = WG._tiles(prob, x)
+    G, BT, AT = WG.G.astype(f32), WG.BT.astype(f32), WG.AT.astype(f32)
+    U = np.einsum("kasc,bs->kabc", np.einsum("ar,krsc->kasc", G, w.astype(f32)).astype(f32), G).astype(f32)
+    V = np.einsum("ntqajc,bj->ntqabc", np.einsum("ai,ntqijc->ntqajc", BT, d.astype(f32)).astype(f32),
+                  BT).astype(f32)
+    U, V = r16(U), r16(V)
+    M = np.zeros(V.shape[:5] + (w.shape[0],), dtype=f32)
+    for c in range(x.shape[-1]):
+        M = (M + np.einsum("kab,ntqab->ntqabk", U[..., c], V[..., c]).astype(f32)).astype(f32)
+    Yb = np.einsum("ntqybk,xb->ntqyxk", np.einsum("ya,ntqabk->ntqybk", AT, M).astype(f32), AT).astype(f32)
+    N, TP, TQ = Yb.shape[:3]
+    return Yb.transpose(0, 1, 3, 2, 4, 5).reshape(N, 2 * TP, 2 * TQ, -1)[:, :P, :Q, :].astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype,u", [("f16", 2.0 ** -11), ("bf16", 2.0 ** -8)])
+@pytest.mark.parametrize("C,floor", [(1, 0.25), (64, 0.04)])
+def test_winograd_error_bound_holds_and_is_tight(dtype, u, C, floor):
+    from oracle import winograd as WG
+    from convolution_nhwc_implicit_amd.workloads import draw
+    prob = problem(2, C, 9, 11, 8, 3, 3, pad=(1, 1))
+    rng = np.random.default_rng(900 + C)
+    x = draw((2, 9, 11, C), dtype, "gauss", rng).to(torch.float64).numpy()
+    w = draw((8, 3, 3, C), dtype, "gauss", rng, std=1.0 / np.sqrt(9 * C)).to(torch.float64).numpy()
+    y = oracle.fprop(prob, x, w)
+    ratio = np.abs(_wino_rounded_sim(prob, x, w, dtype) - y) / WG.error_bound(prob, x, w, u)
+    assert ratio.max() <= 1.0, f"simulated rounding exceeds the bound: {ratio.max():.3f}"
+    assert ratio.max() >= floor, f"bound loose: worst simulated error is {ratio.max():.3f} of it"
+
+
+def test_winograd_error_bound_catches_a_dropped_rounding():
+    """The simulation must separate a right bound from a wrong one: rounding
+    only V (the filter transform left exact) gives a bound that the full
+    rounding exceeds on some output."""
+    from oracle import winograd as WG
+    from convolution_nhwc_implicit_amd.workloads import draw
+    prob = problem(2, 1, 9, 11, 8, 3, 3, pad=(1, 1))
+    rng = np.random.default_rng(901)
+    x = draw((2, 9, 11, 1), "f16", "gauss", rng).to(torch.float64).numpy()
+    w = draw((8, 3, 3, 1), "f16", "gauss", rng, std=1.0 / 3).to(torch.float64).numpy()
+    u = 2.0 ** -11
+    y = oracle.fprop(prob, x, w)
+    err = np.abs(_wino_rounded_sim(prob, x, w, "f16") - y)
+    half = 1.01 * (u + 42 * 2.0 ** -24) * WG.abs_terms(prob, x, w)  # one operand's rounding only
+    assert np.any(err > half)
+    assert np.all(err <= WG.error_bound(prob, x, w, u))
