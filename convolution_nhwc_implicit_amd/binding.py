@@ -24,6 +24,8 @@ CONV2D_ERR_INVALID_ARGUMENT = 1
 CONV2D_ERR_UNSUPPORTED = 2
 CONV2D_ERR_WORKSPACE_TOO_SMALL = 3
 CONV2D_ERR_DEVICE = 4
+CONV2D_ERR_SCRATCH_LIMIT = 5
+CONV2D_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 CONV2D_DTYPE_F16 = 0
 CONV2D_DTYPE_BF16 = 1
@@ -97,6 +99,7 @@ def load():
                                  P(Conv2dAlgo), vp]
     lib.conv2d_wgrad.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t,
                                  P(Conv2dAlgo), vp]
+    lib.conv2d_wgrad_noalloc.argtypes = [P(Conv2dProblem), ctypes.c_int, vp, vp, vp, P(Conv2dAlgo), vp]
     ep = P(Conv2dEpilogue)
     lib.conv2d_workspace_size_ex.argtypes = [ctypes.c_int, P(Conv2dProblem), ctypes.c_int,
                                              P(Conv2dAlgo), ep, P(ctypes.c_size_t)]
@@ -114,7 +117,7 @@ def load():
     for name in ("conv2d_output_size", "conv2d_workspace_size", "conv2d_plan_info",
                  "conv2d_fprop", "conv2d_dgrad", "conv2d_wgrad", "conv2d_workspace_size_ex",
                  "conv2d_fprop_ex", "conv2d_dgrad_ex", "conv2d_wgrad_ex",
-                 "conv2d_bias_grad_workspace_size", "conv2d_bias_grad"):
+                 "conv2d_bias_grad_workspace_size", "conv2d_bias_grad", "conv2d_wgrad_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -262,6 +265,19 @@ def conv2d_wgrad(prob, dtype, x, dy, dw, workspace, algo=None, stream=None):
     st = load().conv2d_wgrad(ctypes.byref(make_problem(prob)), code, x.data_ptr(), dy.data_ptr(),
                              dw.data_ptr(), wsp, wsb, _algo(algo), _stream(stream))
     _raise(st, "conv2d_wgrad")
+
+
+def conv2d_wgrad_noalloc(prob, dtype, x, dy, dw, algo=None, stream=None):
+    """conv2d_wgrad with the partials in the library's static device scratch."""
+    code = _dtype_code(dtype)
+    tdt = CODE_DTYPE[code]
+    xs, ws_, ys = _shapes(prob)
+    _check_tensor(x, "x", tdt, xs)
+    _check_tensor(dy, "dy", tdt, ys)
+    _check_tensor(dw, "dw", tdt, ws_)
+    st = load().conv2d_wgrad_noalloc(ctypes.byref(make_problem(prob)), code, x.data_ptr(), dy.data_ptr(),
+                                     dw.data_ptr(), _algo(algo), _stream(stream))
+    _raise(st, "conv2d_wgrad_noalloc")
 
 
 def _epi(epi):

@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "conv2d_nhwc.h"
 #include "internal.h"
@@ -512,6 +513,42 @@ static int bias_grad_plan(const conv2d_problem_t *prob, int dtype, Dims *d, int 
     return CONV2D_OK;
 }
 
+// ---- scratch of the no-allocation wgrad entry point -------------------------
+// For callers that cannot allocate, the wgrad partials go to this file-scope
+// device array instead of a caller workspace.  Every device the library runs
+// on holds its own copy (CONV2D_NOALLOC_SCRATCH_BYTES) until the process
+// ends.  The array's name is a host-side stand-in, not a device address: its
+// address on a device comes from hipGetSymbolAddress with that device
+// current, taken once per device and kept in scratch_ptr; only that pointer
+// is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[CONV2D_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+static void *scratch_ptr[kMaxDevices];
+static std::mutex scratch_mu;
+
+// The scratch address on the device the stream belongs to (the current device
+// for the null stream).
+static int scratch_for_stream(hipStream_t s, void **out)
+{
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return CONV2D_ERR_DEVICE;
+    dev = cur;
+    if (s && hipStreamGetDevice(s, &dev) != hipSuccess) return CONV2D_ERR_DEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return CONV2D_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return CONV2D_ERR_DEVICE;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return CONV2D_ERR_DEVICE;
+        if (e != hipSuccess || !p) return CONV2D_ERR_DEVICE;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return CONV2D_OK;
+}
+
 extern "C" {
 
 const char *conv2d_status_string(int status)
@@ -522,6 +559,8 @@ const char *conv2d_status_string(int status)
     case CONV2D_ERR_UNSUPPORTED: return "unsupported problem, dtype or alignment";
     case CONV2D_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case CONV2D_ERR_DEVICE: return "device (HIP) error";
+    case CONV2D_ERR_SCRATCH_LIMIT:
+        return "the pass needs more scratch than the no-allocation entry point's static buffer holds";
     default: return "unknown status";
     }
 }
@@ -1021,6 +1060,22 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype, const void *x, const v
                  void *workspace, size_t workspace_bytes, const conv2d_algo_t *algo, void *stream)
 {
     return wgrad_run(prob, dtype, x, dy, Epi(), dw, workspace, workspace_bytes, algo, stream);
+}
+
+int conv2d_wgrad_noalloc(const conv2d_problem_t *prob, int dtype, const void *x, const void *dy, void *dw,
+                         const conv2d_algo_t *algo, void *stream)
+{
+    Plan pl;
+    int st = make_plan(CONV2D_OP_WGRAD, prob, dtype, algo, Epi(), &pl);
+    if (st) return st;
+    if (pl.ws_bytes > (size_t)CONV2D_NOALLOC_SCRATCH_BYTES) return CONV2D_ERR_SCRATCH_LIMIT;
+    void *ws = nullptr;
+    if (pl.ws_bytes) {
+        st = scratch_for_stream((hipStream_t)stream, &ws);
+        if (st) return st;
+    }
+    return wgrad_run(prob, dtype, x, dy, Epi(), dw, ws, pl.ws_bytes ? (size_t)CONV2D_NOALLOC_SCRATCH_BYTES : 0,
+                     algo, stream);
 }
 
 int conv2d_fprop_ex(const conv2d_problem_t *prob, int dtype, const void *x, const void *w, const void *bias,

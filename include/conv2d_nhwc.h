@@ -62,6 +62,7 @@ extern "C" {
 #define CONV2D_ERR_UNSUPPORTED          2  /* dtype/op pair, alignment, channel multiple */
 #define CONV2D_ERR_WORKSPACE_TOO_SMALL  3
 #define CONV2D_ERR_DEVICE               4  /* a HIP launch failed */
+#define CONV2D_ERR_SCRATCH_LIMIT        5  /* conv2d_wgrad_noalloc: the pass needs more than its static scratch */
 
 /* Element types. */
 #define CONV2D_DTYPE_F16   0
@@ -201,6 +202,28 @@ int conv2d_wgrad(const conv2d_problem_t *prob, int dtype,
                  const void *x, const void *dy, void *dw,
                  void *workspace, size_t workspace_bytes,
                  const conv2d_algo_t *algo, void *stream);
+
+/*
+ * conv2d_wgrad without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same problem, arguments, plan, kernels and
+ * results (bit for bit) as conv2d_wgrad; the split-K partials go to a static
+ * device buffer of CONV2D_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  It calls no allocating
+ * routine.
+ *   Errors: as conv2d_wgrad, plus CONV2D_ERR_SCRATCH_LIMIT when the plan's
+ *   workspace (conv2d_workspace_size) exceeds the buffer; nothing is enqueued
+ *   then.  CONV2D_ERR_DEVICE if the buffer's address cannot be found on the
+ *   stream's device.
+ *   Concurrency: every call on one GPU shares that GPU's buffer, which keeps
+ *   the last call's contents.  Calls whose work overlaps on one GPU (two
+ *   streams, or two host threads) race and give undefined results; calls in
+ *   order on one stream are safe.
+ */
+#define CONV2D_NOALLOC_SCRATCH_BYTES (64u << 20)
+int conv2d_wgrad_noalloc(const conv2d_problem_t *prob, int dtype,
+                         const void *x, const void *dy, void *dw,
+                         const conv2d_algo_t *algo, void *stream);
 
 /*
  * Linear-combination epilogue of the three passes: the CUTLASS Python
