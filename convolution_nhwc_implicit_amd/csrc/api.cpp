@@ -923,7 +923,6 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         b.part_stride = splitk_stride(kcols + (b.with_db ? d.K : 0));
         b.xw = (int)(d.Q + d.dw * (d.S - 1));
         b.div_xw = make_fastdiv((uint32_t)b.xw);
-        b.steps_per_group = wgrad_band_steps((int)d.Q);
         b.xcd_pairs = (d.N * b.chunks_per_img) % 8 == 0;
         hipError_t e = launch_wgrad_band(dtype, b, s);
         if (e != hipSuccess) return CONV2D_ERR_DEVICE;

@@ -97,8 +97,16 @@ __device__ inline uint32_t lds_addr(const void *p)
 }
 // M0 (the LDS base of the transfer) is saved and restored around the load,
 // so the compiler's own use of M0 is untouched.
-__device__ inline void dma16(const u32x4 &rsrc, uint32_t lds, uint32_t voff)
+// rsrc and lds must be wave-uniform; they are read from the first lane so
+// that they sit in scalar registers whatever the compiler inferred.
+__device__ inline void dma16(const u32x4 &rsrc_in, uint32_t lds_in, uint32_t voff)
 {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+    u32x4 rsrc;
+    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc_in.x);
+    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc_in.y);
+    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc_in.z);
+    rsrc.w = __builtin_amdgcn_readfirstlane(rsrc_in.w);
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"

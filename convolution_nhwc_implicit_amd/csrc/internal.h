@@ -232,9 +232,10 @@ constexpr int kColsumVecsPerWg = 256;  // 8-column vectors per workgroup (grid.y
 hipError_t launch_colsum(int dtype, const ColsumArgs &a, int splits, hipStream_t st);
 
 // ---------------------------------------------------------------------------
-// Stride-1 wgrad band kernel (wgrad_band.hip): dy and x rows in LDS rings,
-// transposing LDS reads.  One workgroup per (image, band of rows_per_wg output
-// rows); each writes fp32 partials [K][R*S*C] at out + workgroup * part_stride.
+// Stride-1 3x3 wgrad band kernel (wgrad_band.hip): dy and x pixels in LDS,
+// transposing LDS reads.  Two workgroups (column halves) per (image, band of
+// rows_per_wg output rows); band b's fp32 partial [K][R*S*C] goes to
+// out + b * part_stride.
 // ---------------------------------------------------------------------------
 struct WgradBandArgs {
     const void *x;
@@ -246,12 +247,10 @@ struct WgradBandArgs {
     long long part_stride;
     int xw;              // padded row pitch Q + dil*(S-1)
     FastDiv div_xw;
-    int steps_per_group;  // wgrad_band_steps(Q)
     int xcd_pairs;        // bands a multiple of 8: the two column halves of a band share an XCD
     int with_db;          // also the band's dy column sums at [K*R*S*C, +K) of its slice
 };
 bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q);
-int wgrad_band_steps(int Q);
 hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------

@@ -1,5 +1,5 @@
-// wgrad_band.hip -- stride-1 weight gradient with dy and x rows resident in
-// LDS and transposing LDS reads (gfx950).
+// wgrad_band.hip -- stride-1 3x3 weight gradient with dy and x pixels resident
+// in LDS and transposing LDS reads (gfx950).
 //
 // dw[k][r][s][c] = sum over output pixels (p,q) of dy[p,q,k] * x[p-ph+r*d, q-pw+s*d, c]
 // is a GEMM with rows k, columns (r,s,c) and a reduction over pixels.  Both
@@ -7,31 +7,44 @@
 // consecutive reduction elements (pixels) per lane.  gfx950's
 // ds_read_b64_tr_b16 gives exactly that from a pixel-major tile: in each group
 // of 16 lanes, lane L points at 4 channels of pixel L/4 and lane i receives
-// channel i of the 4 pixels.  So dy and x rows are copied into LDS as they are,
-// every input byte once (plus the halo rows), and all R*S tap shifts of x are
-// just different read addresses.
+// channel i of the 4 pixels.  So dy and x pixels are copied into LDS as they
+// are, and all R*S tap shifts of x are just different read addresses.
 //
-// Rows are laid out with the padded pitch XW = Q + dil*(S-1) in both LDS
-// buffers: dy gets XW - Q zero pixels after each row, so output pixel
-// (p, q) sits at v = p*XW + q and its tap (r, s) of x at v + r*dil*XW +
-// s*dil.  Every address is then linear in v: a 16-pixel step moves every
-// read by the same 2 KB (an immediate offset), the few padding pixels add
-// zeros, and the main loop needs no per-step index arithmetic.
+// Pixels are numbered with the padded pitch XW = Q + dil*(S-1): output pixel
+// (p, q) of the band is v = p*XW + q, and its tap (r, s) of x is v + r*dil*XW
+// + s*dil.  dy is zero at the XW - Q padding columns, so the band is one
+// linear stream of rows*XW pixels, cut into steps of 16 (one MFMA's
+// reduction) and groups of 16 steps that ignore row boundaries.  Steps past
+// the band's end read zero dy pixels (their loads fall outside the band's
+// rows) and add exact zeros.
 //
-// A workgroup (12 waves, three per SIMD) owns a band of output rows of one
-// image and all K x R*S*C outputs.  Output blocks are 32x32 (32x32x16 MFMA,
-// fp32 accumulators): wave w owns k-block w/6 and the three column blocks
-// 3*(w%6)..+2 (which share one tap row r), over every pixel of the band.  The
-// band is walked in groups of GR output rows; each group's dy rows and its
-// GR + halo x rows are brought by direct-to-LDS loads (buffer_load ... lds;
-// pixels outside the image and the padding come from the buffer range check
-// as zeros) into one of two buffers, while the previous group is computed
-// from the other.  Each workgroup writes its fp32 partial sums; the split-K
-// reduction adds the workgroups' partials in workgroup order.
+// A workgroup (8 waves, two per SIMD) owns a band of output rows of one image
+// and one half of the R*S*C columns (9 column blocks of 32), all of K.  Waves
+// 0-3 hold column blocks 0-4 and waves 4-7 blocks 5-8 of the half, both
+// k-blocks (32x32x16 MFMA accumulators, 160 or 128 fp32 registers); wave w
+// takes the steps t = w (mod 4).  The two waves of a SIMD work on the same
+// steps, so each SIMD does 18 MFMAs per step, and per step a wave reads its 2
+// dy fragments and one x fragment per column block: 13 fragments for 18
+// MFMAs per SIMD.  Two waves per SIMD keep twice as many transposing reads in
+// flight as one, and the LDS read rate grows with the reads in flight.  The
+// four waves' sums of each column set are added at the end in a fixed order.
 //
-// 16-byte channel chunks of pixel v are stored with chunk bit 2 flipped
-// when bit 1 of v is set: the transposing reads of 4 consecutive pixels x
-// 32 channels then cover all 64 LDS banks.
+// Each group's dy pixels and x window (the group's pixels plus the tap
+// shifts) arrive by direct-to-LDS loads (buffer_load ... lds; pixels outside
+// the image and the padding come from the buffer range check as zeros) into
+// one of two buffers while the previous group is computed from the other.
+// The barrier between groups sits inside a wave's last step of a group: once
+// that step's fragments are in registers, the wave waits for its share of the
+// next group's loads, meets the others, reads the next group's first
+// fragments during the last step's MFMAs and issues the loads of the group
+// after next, a few blocks at a time, between them.  Each workgroup writes
+// its fp32 partial sums; the split-K reduction adds the workgroups' partials
+// in order.
+//
+// 16-byte channel chunks of buffer pixel v are stored with chunk bit 2
+// flipped when bit 1 of v is set: the transposing reads of 4 consecutive
+// pixels x 32 channels then cover all 64 LDS banks.  Groups, steps and the
+// second read of a fragment move by multiples of 4 pixels, which keep bit 1.
 #include "device_common.h"
 
 namespace cnv {
@@ -59,56 +72,66 @@ struct Mfma32w<EBF16> {
 };
 
 namespace wb {
-constexpr int NT = 768;          // 12 waves
+constexpr int NT = 512;                   // 8 waves, two per SIMD
 constexpr int WAVES = NT / 64;
-constexpr int CH = 64;           // C = K = 64 channels, 128 bytes per pixel
+constexpr int PHASES = 4;                 // wave w takes the steps t = w (mod 4)
+constexpr int CH = 64;                    // C = K = 64 channels, 128 bytes per pixel
 constexpr int PIXB = CH * 2;
-constexpr int GR = 4;            // output rows per group
 constexpr int R = 3, S = 3, DIL = 1;
-constexpr int HALO = DIL * (R - 1);
-constexpr int NCOLB = R * S * CH / 32;   // 18 column blocks of 32 in all
-constexpr int CB_WG = NCOLB / 2;         // a workgroup computes one half of them
-constexpr int WAVE_CB = 3;               // column blocks per wave
-constexpr int WAVE_KB = 2;               // k-blocks per wave (all of K = 64)
-constexpr int NACC = WAVE_KB * WAVE_CB;
-constexpr int WSETS = CB_WG / WAVE_CB;   // 3 waves cover the workgroup's columns ...
-constexpr int PHASES = WAVES / WSETS;    // ... and 4 such sets split the 16-pixel steps (t mod 4)
-constexpr int BODY = 4;                  // steps per straight-line body (per phase)
-// buffer capacities in pixels (whole 1 KB direct-to-LDS blocks of 8 pixels),
-// sized for Q <= QMAX: a group covers steps*16 virtual pixels of dy (steps a
-// multiple of PHASES*BODY) and those plus the tap shifts of x
+constexpr int NCOLS = R * S * CH;         // 576 columns (r, s, c)
+constexpr int CB_WG = NCOLS / 32 / 2;     // a workgroup computes 9 of the 18 column blocks
+constexpr int NCB_A = 5, NCB_B = CB_WG - NCB_A;  // column blocks of waves 0-3 and of waves 4-7
+constexpr int KB = CH / 32;               // k-blocks
+constexpr int GSTEPS = 16;                // steps of 16 pixels per group
+constexpr int GPIX = GSTEPS * 16;         // dy pixels per group
+constexpr int SLOTS = GSTEPS / PHASES;    // steps per wave per group
 constexpr int QMAX = 56;
-constexpr int DCAP = 256;        // >= 16 * round_up(ceil(GR*(QMAX+2)/16), PHASES*BODY)
-constexpr int XCAP = 376;        // >= DCAP + HALO*(QMAX+2) + DIL*(S-1)
+constexpr int XWMAX = QMAX + DIL * (S - 1);
+constexpr int HALO = DIL * (R - 1) * XWMAX + DIL * (S - 1);  // x pixels past a group's dy pixels
+constexpr int DCAP = GPIX;
+constexpr int XCAP = (GPIX + HALO + 63) / 64 * 64;  // whole 1 KB blocks for each of the 8 waves
 constexpr int D_BYTES = DCAP * PIXB, X_BYTES = XCAP * PIXB;
 constexpr int BUF_BYTES = D_BYTES + X_BYTES;
 constexpr int LDS_BYTES = 2 * BUF_BYTES;
-constexpr int PARK_WAVE = 64 * NACC * 16 * 4;  // one wave's accumulators
-static_assert(CB_WG == WSETS * WAVE_CB && WAVES == WSETS * PHASES && PHASES == 4, "3 x 4 waves");
-static_assert(2 * WSETS * PARK_WAVE <= LDS_BYTES, "two phases' accumulators fit in LDS");
-static_assert(DCAP % 8 == 0 && XCAP % 8 == 0, "whole 1 KB blocks");
+constexpr int DBLK = DCAP / 8, XBLK = XCAP / 8;  // 1 KB direct-to-LDS blocks of 8 pixels
+constexpr int NB_WAVE = (DBLK + XBLK) / WAVES;   // blocks per wave per group
+constexpr int STEPB = PHASES * 16 * PIXB;  // a wave's next step in a group: 64 pixels on
+constexpr int RDB = 4 * PIXB;              // the second read of a fragment: 4 pixels on
+constexpr int TILE_BYTES = 64 * 16 * 4;    // one 32x32 fp32 accumulator block, all lanes
+static_assert(DBLK % WAVES == 0 && XBLK % WAVES == 0, "every wave loads the same blocks of each tensor");
+static_assert(GSTEPS % PHASES == 0 && SLOTS == 4, "four steps per wave per group");
 static_assert(LDS_BYTES <= 163840, "fits in the 160 KB LDS");
+static_assert(2 * KB * CB_WG * TILE_BYTES <= LDS_BYTES, "two phases' blocks of both sets fit in LDS");
+static_assert((SLOTS - 1) * STEPB + RDB + 32 < 65536, "read offsets fit the 16-bit immediate");
 
 template <int V>
 struct IntC {
     static constexpr int value = V;
 };
+// f(IntC<B>{}), f(IntC<B + 1>{}), ..., f(IntC<E - 1>{})
+template <int B, int E, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(IntC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 __device__ inline int swz_chunk(int chunk, int v) { return chunk ^ (((v >> 1) & 1) << 2); }
 }  // namespace wb
 
-
-template <class E>
-__global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs a)
+// The work of one wave: NCB column blocks from block CB0 of the half, the
+// steps t = phase (mod 4); then the set's sums and the partial's stores.
+template <class E, bool DB, int NCB, int CB0>
+__device__ __attribute__((always_inline)) inline void wgrad_band_wave(const WgradBandArgs &a, unsigned char *smem,
+                                                                     const int wave, const int lane)
 {
     using namespace wb;
     using elem = typename E::elem;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int phase = wave & (PHASES - 1);
     // Workgroup -> (band, column half).  Workgroups are dealt to the 8 XCDs
     // in turn, so the two halves of a band go 8 apart: same XCD, and the
-    // second one's row loads hit that XCD's L2.
+    // second one's loads hit that XCD's L2.
     int band, colh;
     if (a.xcd_pairs) {
         const int bid = blockIdx.x;
@@ -124,290 +147,285 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     const int p_end = min(p_start + a.rows_per_wg, a.P);
     const int nrows = p_end - p_start;  // >= 1 by construction of the grid
     const int Q = a.Q, XW = a.xw;
-    const int h_base = p_start - a.pad_h;  // input row of x band row 0
+    const int h_base = p_start - a.pad_h;  // input row of band row 0, tap row 0
+    const int nsteps = (nrows * XW + 15) >> 4;
+    const int ngroups = (nsteps + GSTEPS - 1) / GSTEPS;
 
-    // ---- loads.  Group g covers band rows [g*GR, g*GR + GR): dy virtual
-    // pixels [0, DCAP) and x virtual pixels [0, XCAP) of its buffer, 1 KB
-    // block b going to wave b % WAVES.  Lane i of a block fills stored chunk
-    // i%8 of pixel 8*blk + i/8, i.e. source chunk swz_chunk(i%8, pixel).
+    // ---- loads.  Group g covers the band's pixels [g*GPIX, g*GPIX + DCAP)
+    // of dy and [g*GPIX, g*GPIX + XCAP) of x.  Lane i of a 1 KB block fills
+    // stored chunk i%8 of buffer pixel 8*blk + i/8 with source chunk
+    // swz_chunk(i%8, pixel); the lane's pixel within a block and its chunk
+    // are the same in every block (bit 1 of the pixel index is bit 1 of
+    // i/8).  The per-block arithmetic is redone in each call from an opaque
+    // copy of them, so that the compiler does not keep every block's
+    // addresses in registers across the loop.
     const u32x4 x_rs = make_buf_rsrc((const elem *)a.x + (size_t)img * a.H * a.W * CH, (uint32_t)(a.H * a.W * CH * 2));
     const u32x4 d_rs =
         make_buf_rsrc((const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH, (uint32_t)(nrows * Q * CH * 2));
-    // The pixel a lane moves in each of its wave's blocks is the same in every
-    // group (buffers start at a group's first row), so its (row, column) in
-    // the group is computed once, row << 8 | column in 16 bits, two blocks
-    // per register: block wave + WAVES*j in bits 16*(j%2) of rc[j/2].  Bit 1
-    // of the pixel index, which sets the chunk swizzle, is bit 1 of lane/8
-    // (blocks are 8 pixels).
-    constexpr int DBLK = DCAP / 8, NBLK = (DCAP + XCAP) / 8;
-    constexpr int MAXB = (NBLK + WAVES - 1) / WAVES;  // blocks per wave
-    static_assert(XCAP < 256 * 6 && QMAX + 2 < 256, "row and column fit in 8 bits");
-    uint32_t rc[(MAXB + 1) / 2] = {};
-#pragma unroll
-    for (int jb = 0; jb < MAXB; ++jb) {
-        const int b = wave + WAVES * jb;
-        const int v = (b < DBLK ? b : b - DBLK) * 8 + (lane >> 3);
-        const int row = (int)fdiv((uint32_t)v, a.div_xw);
-        rc[jb / 2] |= (((uint32_t)row << 8) | (uint32_t)(v - row * XW)) << (16 * (jb & 1));
-    }
-    const int lane_chunk16 = swz_chunk(lane & 7, lane >> 3) * 16;  // byte offset of the chunk in its pixel
     const uint32_t lds0 = lds_addr(smem);
-    auto dma_group = [&](int g) {
-        const int d0 = g * GR;
-        if (d0 >= nrows) return;
-        const int ndy = min(GR, nrows - d0);  // dy rows of the group
-        const int nx = ndy + HALO;            // x rows it reads
-        const uint32_t buf = lds0 + (uint32_t)((g & 1) * BUF_BYTES);  // LDS byte address
-#pragma unroll
-        for (int jb = 0; jb < MAXB; ++jb) {
-            const int b = wave + WAVES * jb;  // wave-uniform
-            if (b >= NBLK) break;
-            const uint32_t e = rc[jb / 2] >> (16 * (jb & 1));
-            const int row = (int)((e >> 8) & 0xffu), col = (int)(e & 0xffu);
-            unsigned voff = kBufOOB;
-            if (b < DBLK) {
-                if (row < ndy && col < Q) voff = (unsigned)(((d0 + row) * Q + col) * PIXB + lane_chunk16);
-                dma16(d_rs, buf + b * 1024, voff);
-            } else {
-                const int h = h_base + d0 + row, w = col - a.pad_w;
-                if (row < nx && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W)
-                    voff = (unsigned)((h * a.W + w) * PIXB + lane_chunk16);
-                dma16(x_rs, buf + b * 1024, voff);
-            }
+    const int lane_px = lane >> 3;
+    const int lane_chunk16 = swz_chunk(lane & 7, lane_px) * 16;
+    // block jb (0 .. NB_WAVE-1) of this wave's share of group g: dy blocks
+    // first, then x blocks; nothing for a group past the band
+    auto dma_block = [&](int g, int px, int ch, auto jb_c) __attribute__((always_inline)) {
+        constexpr int JB = decltype(jb_c)::value;
+        if (g >= ngroups) return;
+        const uint32_t buf = lds0 + (uint32_t)((g & 1) * BUF_BYTES);
+        if constexpr (JB < DBLK / WAVES) {
+            const int b = wave + WAVES * JB;
+            const int v = px + b * 8;  // band pixel of this lane
+            const int row = (int)fdiv((uint32_t)v, a.div_xw), col = v - row * XW;
+            const bool in = row < nrows && col < Q;
+            dma16(d_rs, buf + b * 1024, in ? (unsigned)((row * Q + col) * PIXB + ch) : kBufOOB);
+        } else {
+            const int b = wave + WAVES * (JB - DBLK / WAVES);
+            const int v = px + b * 8;
+            const int row = (int)fdiv((uint32_t)v, a.div_xw), col = v - row * XW;
+            const int h = h_base + row, w = col - a.pad_w;
+            const bool in = (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W;
+            dma16(x_rs, buf + D_BYTES + b * 1024, in ? (unsigned)((h * a.W + w) * PIXB + ch) : kBufOOB);
         }
     };
+    auto dma_lane = [&](int g, int &px, int &ch) __attribute__((always_inline)) {
+        px = g * GPIX + lane_px;
+        ch = lane_chunk16;
+        asm volatile("" : "+v"(px), "+v"(ch));
+    };
 
-    dma_group(0);
-    wait_vm_all();
-    __syncthreads();
-    dma_group(1);
-
-    // ---- per-wave roles: both k-blocks, column blocks cb0..cb0+2 of the
-    // workgroup's half (all of one tap row r: column block cb is tap cb/2 =
-    // (r, s), channel half cb&1), and the steps t = phase (mod 4)
-    const int phase = wave / WSETS;
-    const int cb0 = colh * CB_WG + WAVE_CB * (wave % WSETS);
-    const int tap_r = (cb0 >> 1) / S;
+    // ---- fragment reads.  Read rd of a fragment covers pixels v = 16*t +
+    // 8*(lane/32) + 4*rd + 0..3 of step t; this lane points at pixel
+    // v + L/4 (L = lane%16), channels 4*(L%4)..+3 of its 16-channel group.
+    // Column block cb (of the 18) is tap cb/2 = (r, s), channel half cb%2.
     const int l32 = lane & 31, lhi = lane >> 5;
-
-    // ---- per-lane read offsets (first step of this phase in a buffer).
-    // Read rd of a step covers pixels v = 16*t + 8*lhi + 4*rd + 0..3; this
-    // lane points at pixel v + L/4.  Read rd = 1 and later steps move every
-    // read by a multiple of 4 pixels, which keeps bit 1 of the pixel index and
-    // so the swizzle: they are constant byte offsets (4 pixels = 512 B) from
-    // the rd = 0 offsets of the body's first step.
-    auto dy_off = [&](int ln, int rd, int kb) {
-        const int L_ = ln & 15, g_ = (ln >> 4) & 1, h_ = ln >> 5;
+    auto dy_off = [&](int kb) {
+        const int L_ = lane & 15, g_ = (lane >> 4) & 1;
         const int c_ = 16 * g_ + 4 * (L_ & 3);
-        const int v = 16 * phase + 8 * h_ + 4 * rd + (L_ >> 2);
+        const int v = 16 * phase + 8 * lhi + (L_ >> 2);
         return v * PIXB + swz_chunk(kb * 4 + (c_ >> 3), v) * 16 + (c_ & 7) * 2;
     };
-    auto x_off = [&](int ln, int rd, int i) {
-        const int L_ = ln & 15, g_ = (ln >> 4) & 1, h_ = ln >> 5;
+    auto x_off = [&](int cb) {
+        const int L_ = lane & 15, g_ = (lane >> 4) & 1;
         const int c_ = 16 * g_ + 4 * (L_ & 3);
-        const int v = 16 * phase + 8 * h_ + 4 * rd + (L_ >> 2);
-        const int cb = cb0 + i, tap_s = (cb >> 1) - tap_r * S;
-        const int xv = v + tap_r * DIL * XW + tap_s * DIL;
+        const int v = 16 * phase + 8 * lhi + (L_ >> 2);
+        const int tap = cb >> 1, tr_ = tap / S, ts_ = tap - tr_ * S;
+        const int xv = v + tr_ * DIL * XW + ts_ * DIL;
         return D_BYTES + xv * PIXB + swz_chunk((cb & 1) * 4 + (c_ >> 3), xv) * 16 + (c_ & 7) * 2;
     };
-
-    f32x16 acc[WAVE_KB][WAVE_CB];
-#pragma unroll
-    for (int kb = 0; kb < WAVE_KB; ++kb)
-#pragma unroll
-        for (int n = 0; n < WAVE_CB; ++n) acc[kb][n] = f32x16{};
-    // bias gradient (with_db): the first column set of each phase in the
-    // first column half adds up the dy values its fragments hold (every dy
-    // pixel of the band exactly once); lane holds channel 32*kb + l32, the
-    // pixels of half lhi of each step
-    const bool dbw = a.with_db && colh == 0 && wave % WSETS == 0;  // wave-uniform
-    float dbacc[WAVE_KB] = {};
-
     typedef __attribute__((address_space(3))) unsigned char lds_u8;  // 32-bit LDS addresses
     auto tr = [](const lds_u8 *p) -> s16x4 {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
     };
-    // one step's fragments as raw 64-bit halves: [2*kb + rd] dy, [4 + 2*i + rd] x
-    typedef s16x4 Frag[2 * WAVE_KB + 2 * WAVE_CB];
-    // lane addresses of a body's first step; step k (k-th of this phase) adds
-    // k*PHASES*2 KB, which the reads take as an immediate offset (the empty
-    // asm keeps the compiler from re-associating base + offset + k*8 KB into
-    // one register per step)
-    constexpr int STEPB = PHASES * 16 * PIXB;
-    constexpr int RDB = 4 * PIXB;  // read rd = 1: 4 pixels further
-    // The offsets are recomputed per body from an opaque copy of the lane id
-    // (holding them across the loop would cost registers the fragments need).
-    const lds_u8 *ad[WAVE_KB], *ax[WAVE_CB];
-    auto set_body = [&](const lds_u8 *base) {
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
+    // Lane addresses of this wave's step of slot 0 in the current buffer; slot
+    // J and the second read of a fragment are immediate offsets, and the
+    // other buffer is BUF_BYTES away.  The empty asm keeps the compiler from
+    // folding the offsets into one address register per slot.
+    const lds_u8 *ad[KB], *ax[NCB];
+    auto pin = [](const lds_u8 *&p) __attribute__((always_inline)) { asm volatile("" : "+v"(p)); };
 #pragma unroll
-        for (int kb = 0; kb < WAVE_KB; ++kb) {
-            ad[kb] = base + dy_off(ln, 0, kb);
-            asm volatile("" : "+v"(ad[kb]));
+    for (int kb = 0; kb < KB; ++kb) ad[kb] = (const lds_u8 *)smem + dy_off(kb);
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) ax[i] = (const lds_u8 *)smem + x_off(colh * CB_WG + CB0 + i);
+    auto switch_buffer = [&](int delta) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            ad[kb] += delta;
+            pin(ad[kb]);
         }
 #pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i) {
-            ax[i] = base + x_off(ln, 0, i);
-            asm volatile("" : "+v"(ax[i]));
+        for (int i = 0; i < NCB; ++i) {
+            ax[i] += delta;
+            pin(ax[i]);
         }
     };
-    auto load_step = [&](Frag &f, int k) {
+    typedef s16x4 DyFrag[KB][2];
+    s16x4 fx[NCB][2];  // x fragments, read in place
+    auto read_dy = [&](DyFrag &d, auto j_c) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_c)::value;
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < WAVE_KB; ++kb) f[2 * kb + rd] = tr(ad[kb] + rd * RDB + k * STEPB);
+            for (int rd = 0; rd < 2; ++rd) d[kb][rd] = tr(ad[kb] + rd * RDB + J * STEPB);
+    };
+    auto read_x = [&](int i, auto j_c) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_c)::value;
 #pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i) f[2 * WAVE_KB + 2 * i + rd] = tr(ax[i] + rd * RDB + k * STEPB);
-        }
+        for (int rd = 0; rd < 2; ++rd) fx[i][rd] = tr(ax[i] + rd * RDB + J * STEPB);
     };
     auto join = [](s16x4 lo, s16x4 hi) -> u32x4 {
         const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
         return u32x4{l.x, l.y, h.x, h.y};
     };
-    // MFMAs [m0, m1) of a step (kb-major over the WAVE_KB x WAVE_CB blocks)
-    auto mma = [&](const Frag &f, int m0, int m1) {
+
+    f32x16 acc[KB][NCB];
 #pragma unroll
-        for (int kb = 0; kb < WAVE_KB; ++kb) {
-            const u32x4 fa = join(f[2 * kb], f[2 * kb + 1]);
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i) {
-                const int m = kb * WAVE_CB + i;
-                if (m >= m0 && m < m1)
-                    acc[kb][i] =
-                        Mfma32w<E>::run(fa, join(f[2 * WAVE_KB + 2 * i], f[2 * WAVE_KB + 2 * i + 1]), acc[kb][i]);
+        for (int i = 0; i < NCB; ++i) acc[kb][i] = f32x16{};
+    // bias gradient (DB): the first column half's waves 0-3 add up the dy
+    // values of their fragments (every dy pixel of the band exactly once);
+    // the lane holds channel 32*kb + l32, the pixels of half lhi
+    constexpr bool DBW = DB && CB0 == 0;
+    float dbacc[KB] = {};
+
+    // One slot (one step): column block by column block, its two MFMAs (one
+    // per k-block), then the next slot's read of that block's x fragment into
+    // the same registers, and extra(i); the next dy fragments go to the other
+    // set, read after the first block.  Every fragment is read NCB - 1 MFMA
+    // pairs of this wave (and as many of its SIMD partner's) before its first
+    // use.  No MFMA and no read is conditional: a branch around MFMAs makes
+    // the compiler shuffle the accumulators between register files, one
+    // around reads makes it drain every outstanding read before each slot.
+    auto slot = [&](const DyFrag &od, DyFrag &nod, auto j_c, auto &&extra) __attribute__((always_inline)) {
+        u32x4 a_[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) a_[kb] = join(od[kb][0], od[kb][1]);
+#pragma unroll
+        for (int i = 0; i < NCB; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 b = join(fx[i][0], fx[i][1]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) acc[kb][i] = Mfma32w<E>::run(a_[kb], b, acc[kb][i]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i == 0) read_dy(nod, j_c);
+            read_x(i, j_c);
+            extra(i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DBW) {
+            if (colh == 0) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const u32x4 u = a_[kb];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dbacc[kb] = DotOne<E>::add(u[e], dbacc[kb]);
+                }
             }
         }
     };
+    using J0 = IntC<0>;
+    using J1 = IntC<1>;
+    using J2 = IntC<2>;
+    using J3 = IntC<3>;
+    auto none = [](int) __attribute__((always_inline)) {};
 
-    // Steps run in straight-line bodies of BODY (of one phase): the reads of
-    // step k+1 are issued right after the first MFMA of step k (so that MFMA
-    // waits for step k's reads alone), and nothing is in flight across
-    // bodies.  Steps past the group's pixels read zero dy
-    // pixels.
-    const int ngroups = (nrows + GR - 1) / GR;
+    DyFrag odA, odB;
+    {
+        int px, ch;
+        dma_lane(0, px, ch);
+        static_for<0, NB_WAVE>([&](auto jb) __attribute__((always_inline)) { dma_block(0, px, ch, jb); });
+    }
+    wait_vm_all();
+    __syncthreads();
+    {
+        int px, ch;
+        dma_lane(1, px, ch);
+        static_for<0, NB_WAVE>([&](auto jb) __attribute__((always_inline)) { dma_block(1, px, ch, jb); });
+    }
+    read_dy(odA, J0{});
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) read_x(i, J0{});
     for (int g = 0; g < ngroups; ++g) {
-        const unsigned char *buf = smem + (g & 1) * BUF_BYTES;
-        const int nbody = a.steps_per_group / (PHASES * BODY);
-        for (int bd = 0; bd < nbody; ++bd) {
-            set_body((const lds_u8 *)buf + bd * BODY * STEPB);
-            Frag f[BODY];
-            load_step(f[0], 0);
-#pragma unroll
-            for (int k = 0; k < BODY; ++k) {
-                // step k's first MFMA, then step k+1's reads, then the rest:
-                // the first MFMA waits for step k's reads alone
-                __builtin_amdgcn_sched_barrier(0);
-                mma(f[k], 0, 1);
-                __builtin_amdgcn_sched_barrier(0);
-                if (k + 1 < BODY) load_step(f[k + 1], k + 1);
-                __builtin_amdgcn_sched_barrier(0);
-                mma(f[k], 1, NACC);
-                if (dbw) {
-#pragma unroll
-                    for (int kb = 0; kb < WAVE_KB; ++kb)
-#pragma unroll
-                        for (int rd = 0; rd < 2; ++rd) {
-                            const uint2 u = __builtin_bit_cast(uint2, f[k][2 * kb + rd]);
-                            dbacc[kb] = DotOne<E>::add(u.x, dbacc[kb]);
-                            dbacc[kb] = DotOne<E>::add(u.y, dbacc[kb]);
-                        }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        slot(odA, odB, J1{}, none);
+        slot(odB, odA, J2{}, none);
+        slot(odA, odB, J3{}, none);
+        // Last slot of the group.  The barrier (which waits for this wave's
+        // LDS reads, this slot's fragments included, and for its loads of
+        // group g + 1) frees this group's buffer for group g + 2 and makes
+        // group g + 1 visible; the next group's first fragments are then read
+        // during this slot (after the last group: slot 0 again, unused), and
+        // the loads of group g + 2 are issued a few blocks at a time between
+        // its MFMAs (dma_block does nothing past the band).
+        int px = 0, ch = 0;
+        if (g + 1 < ngroups) {  // workgroup-uniform
+            wait_vm_all();
+            __syncthreads();
+            switch_buffer(g & 1 ? -BUF_BYTES : BUF_BYTES);
+            dma_lane(g + 2, px, ch);
         }
-        wait_vm_all();     // the next group's rows
-        __syncthreads();   // every wave is done with this group's buffer
-        dma_group(g + 2);  // into the buffer this group used
+        const int gd = g + 1 < ngroups ? g + 2 : ngroups;
+        slot(odB, odA, J0{}, [&](int i) __attribute__((always_inline)) {  // i: 0 .. NCB - 1, unrolled
+            static_for<0, NB_WAVE>([&](auto jb) __attribute__((always_inline)) {
+                if (decltype(jb)::value * NCB / NB_WAVE == i) dma_block(gd, px, ch, jb);
+            });
+        });
     }
 
-    // ---- the four phases' sums, in a fixed order (p0 + p2) + (p1 + p3),
-    // through LDS (the buffers are idle now).  Step 1: phases 2 and 3 park
-    // all their accumulators, phases 0 and 1 add them.  Step 2: phase 0
-    // keeps k-block 0 and phase 1 k-block 1; each parks the other block and
-    // adds the one parked for it, then stores its rows of the partial tile.
-    // A parked block set is [blocks*4][64 lanes] of 16-byte pieces (4
-    // consecutive accumulator rows).
-    constexpr int PARK_HALF = PARK_WAVE / WAVE_KB;  // one k-block's accumulators
-    const int ws_ = wave % WSETS;
-    auto slot = [&](int s, int bytes) { return (f32x4 *)(smem + s * bytes) + lane; };
-    // park / add k-blocks [KB0, KB0 + NKB) (compile-time, so acc stays in registers)
-    auto park = [&](f32x4 *p, auto kb0_c, auto nkb_c) {
-        constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
+    // ---- the four phases' sums of each column set, in a fixed order
+    // (p0 + p2) + (p1 + p3), through LDS (idle after the barrier): phases 2
+    // and 3 park their blocks and phases 0 and 1 add them; then phase 0
+    // keeps k-block 0 and phase 1 k-block 1, each parks the other k-block
+    // and adds the one parked for it, and stores its rows of the partial.
+    // A parked block is [4][64 lanes] of 16-byte pieces (4 consecutive
+    // accumulator rows); the lane holds column l32 of its block, rows
+    // 8*(r/4) + 4*(lane/32) + r%4.
+    constexpr int NT_ = KB * NCB;  // this set's blocks
+    constexpr int SET_BASE = CB0 == 0 ? 0 : 2 * KB * NCB_A * TILE_BYTES;
+    f32x4 *const lds4 = (f32x4 *)smem + lane;
+    auto part = [&](int h) { return lds4 + (SET_BASE + h * NT_ * TILE_BYTES) / 16; };
+    auto park = [&](f32x4 *p, int t, const f32x16 &v) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = KB0; kb < KB0 + NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x16 &v = acc[kb][i];
-                    p[(((kb - KB0) * WAVE_CB + i) * 4 + q) * 64] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-                }
+        for (int q = 0; q < 4; ++q) p[(t * 4 + q) * 64] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
     };
-    auto add = [&](const f32x4 *p, auto kb0_c, auto nkb_c) {
-        constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
+    auto add = [&](const f32x4 *p, int t, f32x16 &v) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);  // one block at a time
 #pragma unroll
-        for (int kb = KB0; kb < KB0 + NKB; ++kb)
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 u = p[(t * 4 + q) * 64];
 #pragma unroll
-            for (int i = 0; i < WAVE_CB; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 t = p[(((kb - KB0) * WAVE_CB + i) * 4 + q) * 64];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[kb][i][4 * q + e] += t[e];
-                }
-    };
-    // the partial tile's rows k = 32*KB + 0..31 in this wave's columns: lane
-    // holds column l32, rows 8*(r/4) + 4*(lane/32) + r%4 of each block
-    auto store = [&](auto kb_c) {
-        constexpr int KB = decltype(kb_c)::value;
-        constexpr int NCOLS = R * S * CH;
-        constexpr int TCOLS = CB_WG * 32;
-        float *out = (float *)a.out + (size_t)band * a.part_stride + colh * TCOLS;
-#pragma unroll
-        for (int i = 0; i < WAVE_CB; ++i) {
-            const int col = (WAVE_CB * ws_ + i) * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int k = KB * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-                out[(size_t)k * NCOLS + col] = acc[KB][i][r];
-            }
+            for (int e = 0; e < 4; ++e) v[4 * q + e] += u[e];
         }
     };
-    using I0 = wb::IntC<0>;
-    using I1 = wb::IntC<1>;
-    using I2 = wb::IntC<2>;
-    if (phase >= 2) park(slot((phase - 2) * WSETS + ws_, PARK_WAVE), I0{}, I2{});
-    __syncthreads();
-    if (phase < 2) add(slot(phase * WSETS + ws_, PARK_WAVE), I0{}, I2{});
-    __syncthreads();
-    if (phase == 0) park(slot(ws_, PARK_HALF), I1{}, I1{});
-    if (phase == 1) park(slot(WSETS + ws_, PARK_HALF), I0{}, I1{});
-    __syncthreads();
-    if (phase == 0) {
-        add(slot(WSETS + ws_, PARK_HALF), I0{}, I1{});
-        store(I0{});
-    }
-    if (phase == 1) {
-        add(slot(ws_, PARK_HALF), I1{}, I1{});
-        store(I1{});
-    }
-    if (a.with_db) {  // uniform: the barriers are reached by every wave
-        // the bias-gradient partial of the band: lanes l32 and l32 + 32 of a
-        // summing wave hold the two pixel halves of a channel; the four
-        // phases' sums are added in phase order through LDS
-        float *dbs = (float *)smem;  // [PHASES][CH]
-        __syncthreads();             // every wave is done with the slots
-        if (dbw) {
+    __syncthreads();  // every wave is done with the buffers
+    if (phase >= 2) {
 #pragma unroll
-            for (int kb = 0; kb < WAVE_KB; ++kb) {
+        for (int t = 0; t < NT_; ++t) park(part(phase - 2), t, acc[t / NCB][t % NCB]);
+    }
+    __syncthreads();
+    if (phase < 2) {
+#pragma unroll
+        for (int t = 0; t < NT_; ++t) add(part(phase), t, acc[t / NCB][t % NCB]);
+    }
+    __syncthreads();
+    // (the k-block indices are compile-time: a runtime index would put the
+    // accumulators in scratch memory)
+    auto keep = [&](auto kb_c) __attribute__((always_inline)) {  // park the other k-block
+        constexpr int KEEP = decltype(kb_c)::value;
+#pragma unroll
+        for (int i = 0; i < NCB; ++i) park(part(KEEP), i, acc[1 - KEEP][i]);
+    };
+    auto finish = [&](auto kb_c) __attribute__((always_inline)) {  // add the parked one, store
+        constexpr int KEEP = decltype(kb_c)::value;
+        float *const out = (float *)a.out + (size_t)band * a.part_stride + colh * (CB_WG * 32);
+#pragma unroll
+        for (int i = 0; i < NCB; ++i) {
+            f32x16 &v = acc[KEEP][i];
+            add(part(1 - KEEP), i, v);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                out[(size_t)(KEEP * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3)) * NCOLS + (CB0 + i) * 32 + l32] = v[r];
+        }
+    };
+    if (phase == 0) keep(IntC<0>{});
+    if (phase == 1) keep(IntC<1>{});
+    __syncthreads();
+    if (phase == 0) finish(IntC<0>{});
+    if (phase == 1) finish(IntC<1>{});
+    if constexpr (DB) {
+        // the bias-gradient partial of the band: lanes l32 and l32 + 32 hold
+        // the two pixel halves of a channel; the four phases' sums are added
+        // in phase order through LDS
+        float *dbs = (float *)smem;  // [PHASES][CH]
+        __syncthreads();             // every wave is done with the parked blocks
+        if (DBW && colh == 0) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
                 const float v = dbacc[kb] + __shfl_xor(dbacc[kb], 32);
                 if (lhi == 0) dbs[phase * CH + kb * 32 + l32] = v;
             }
         }
         __syncthreads();
         if (colh == 0 && wave == 0) {
-            constexpr int NCOLS = R * S * CH;
             float s = dbs[lane];
 #pragma unroll
             for (int p = 1; p < PHASES; ++p) s += dbs[p * CH + lane];
@@ -416,30 +434,40 @@ __global__ __launch_bounds__(768, 1) void wgrad_band_kernel(const WgradBandArgs 
     }
 }
 
-// Steps of 16 pixels per group for output width Q, rounded up to whole
-// bodies; 0 if the group does not fit the buffers.
-int wgrad_band_steps(int Q)
+template <class E, bool DB>
+__global__ __launch_bounds__(512) void wgrad_band_kernel(const WgradBandArgs a)
 {
-    const int xw = Q + wb::DIL * (wb::S - 1);
-    int steps = (wb::GR * xw + 15) / 16;
-    constexpr int unit = wb::PHASES * wb::BODY;
-    steps = (steps + unit - 1) / unit * unit;
-    if (steps * 16 > wb::DCAP || steps * 16 + wb::HALO * xw + wb::DIL * (wb::S - 1) > wb::XCAP) return 0;
-    return steps;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[wb::LDS_BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // waves 0-3 (one per SIMD) and 4-7 (the second of each SIMD) take the two column sets
+    if (wave < wb::PHASES)
+        wgrad_band_wave<E, DB, wb::NCB_A, 0>(a, smem, wave, lane);
+    else
+        wgrad_band_wave<E, DB, wb::NCB_B, wb::NCB_A>(a, smem, wave, lane);
 }
 
 bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q)
 {
-    return R == wb::R && S == wb::S && C == wb::CH && K == wb::CH && dil == wb::DIL && Q % 4 == 0 &&
-           Q <= wb::QMAX && Q >= 4 && wgrad_band_steps(Q) > 0;
+    return R == wb::R && S == wb::S && C == wb::CH && K == wb::CH && dil == wb::DIL && Q >= 1 && Q <= wb::QMAX;
 }
 
 hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st)
 {
     dim3 grid((unsigned)(2 * a.N * a.chunks_per_img));  // two column halves per band
     switch (dtype) {
-    case CONV2D_DTYPE_F16: wgrad_band_kernel<EF16><<<grid, wb::NT, 0, st>>>(a); break;
-    case CONV2D_DTYPE_BF16: wgrad_band_kernel<EBF16><<<grid, wb::NT, 0, st>>>(a); break;
+    case CONV2D_DTYPE_F16:
+        if (a.with_db)
+            wgrad_band_kernel<EF16, true><<<grid, wb::NT, 0, st>>>(a);
+        else
+            wgrad_band_kernel<EF16, false><<<grid, wb::NT, 0, st>>>(a);
+        break;
+    case CONV2D_DTYPE_BF16:
+        if (a.with_db)
+            wgrad_band_kernel<EBF16, true><<<grid, wb::NT, 0, st>>>(a);
+        else
+            wgrad_band_kernel<EBF16, false><<<grid, wb::NT, 0, st>>>(a);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
