@@ -8,9 +8,12 @@ JSON line:
                2*N*P*Q*K*(C/G)*R*S FLOPs per pass, over K back-to-back steps
                between two device synchronisations;
   passes     = per-pass time per launch (K back-to-back launches of the pass
-               between two HIP events on the launch stream), TFLOP/s,
-               fraction of the dense fp16 MFMA peak, algorithmic GB/s and the
-               kernels the pass launches;
+               between two HIP events on the launch stream, median of 5
+               trials), TFLOP/s, fraction of the dense fp16 MFMA peak (and of
+               the peak at the clock the kernel ran at, from the committed
+               counter summary), algorithmic GB/s, a cold-cache time (single
+               launches after a 512 MiB flush) and the kernels the pass
+               launches;
   roofline   = the pass that takes the most time, against its bound, with
                the measured HBM traffic of its kernels;
   cpu_baseline = the fp64 CPU oracle on a bounded sample of the same
@@ -33,6 +36,10 @@ METRIC = "conv2d TFLOP/s (fprop/dgrad/wgrad) and % of MFMA peak, 56x56x64 3x3 fp
 # FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s), int8 5.03 POP/s, HBM3E 8 TB/s.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2}
 PEAK_HBM_GBS = 8000.0
+SPEC_CLOCK_GHZ = 2.4
+TRIALS = 5            # timed trials per pass (median reported)
+COLD_LAUNCHES = 7     # single cold-cache launches per pass (median reported)
+FLUSH_BYTES = 512 << 20
 BAND_TILE, WGRAD_BAND_TILE = 5, 2  # plan tile indices of the band kernels (conv2d_plan_info)
 COPY_BYTES = 64 << 20  # reference copy for the HBM byte counters
 # Measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by
@@ -63,6 +70,35 @@ def measured_traffic(pass_name):
         return None
     p = t.get("passes", {}).get(pass_name)
     return None if p is None else p.get("hbm_bytes")
+
+
+COUNTER_FILE = os.path.join(ROOT, "profiles", "c3a_mfma_counters.json")
+
+
+def measured_clock(pass_name):
+    """Average shader clock (GHz) of the pass's main kernel under rocprofv3,
+    from the committed counter summary, while the kernel sources are the
+    ones it was taken on; else None."""
+    try:
+        with open(COUNTER_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    p = t.get("passes", {}).get(pass_name)
+    return None if p is None else p.get("clock_ghz")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parse():
@@ -222,7 +258,9 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / args.steps
 
-    pass_us, eager_us = {}, {}
+    # Each pass is timed in TRIALS trials of K launches; the median is the
+    # figure, min and max are reported beside it.
+    pass_us, eager_us, pass_trials = {}, {}, {}
     for pname, run in runs.items():
         run(stream)
 
@@ -230,7 +268,7 @@ def main():
             for _ in range(args.steps):
                 run(stream)
 
-        eager_us[pname] = events(eager_k)
+        eager_us[pname] = float(np.median([events(eager_k) for _ in range(TRIALS)]))
         if graph is not None:
             g = torch.cuda.CUDAGraph()
             cap.wait_stream(stream)
@@ -239,9 +277,28 @@ def main():
                     run(cap)
             stream.wait_stream(cap)
             g.replay()
-            pass_us[pname] = events(g.replay)
+            trials = [events(g.replay) for _ in range(TRIALS)]
         else:
-            pass_us[pname] = eager_us[pname]
+            trials = [events(eager_k) for _ in range(TRIALS)]
+        pass_trials[pname] = trials
+        pass_us[pname] = float(np.median(trials))
+
+    # Cold cache: single launches, each after a 512 MiB write that evicts the
+    # 256 MB MALL and the L2s, timed by events around the launch alone.
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    cold_us = {}
+    for pname, run in runs.items():
+        t = []
+        for _ in range(COLD_LAUNCHES):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e3)
+        cold_us[pname] = float(np.median(t))
+    del flush
 
     fl = flops(prob, P, Q)
     esz = 2
@@ -267,13 +324,22 @@ def main():
         us = pass_us[pname]
         passes[pname] = {
             "us_per_launch": round(us, 3),
+            "us_trials": {"n": TRIALS, "median": round(us, 3), "min": round(min(pass_trials[pname]), 3),
+                          "max": round(max(pass_trials[pname]), 3)},
             "tflops": round(fl / (us * 1e-6) / 1e12, 2),
             "frac_mfma_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_TFLOPS[dt], 4),
             "alg_gbs": round(alg_bytes[pname] / (us * 1e-6) / 1e9, 1),
             "eager_us_per_launch": round(eager_us[pname], 3),
+            "cold_us_per_launch": round(cold_us[pname], 3),
+            "cold_tflops": round(fl / (cold_us[pname] * 1e-6) / 1e12, 2),
             "kernels": kernels[pname],
             "plan": plans[pname],
         }
+        clk = measured_clock(pname)
+        if clk is not None:  # the dense MFMA rate at the clock the kernels ran at under the profiler
+            peak_clk = PEAK_TFLOPS[dt] * clk / SPEC_CLOCK_GHZ
+            passes[pname]["clock_ghz"] = clk
+            passes[pname]["frac_mfma_peak_at_clock"] = round(fl / (us * 1e-6) / 1e12 / peak_clk, 4)
     dom = max(passes, key=lambda k: passes[k]["us_per_launch"])
     d = passes[dom]
     # Compute-bound when the pass's arithmetic intensity exceeds the ridge point.
@@ -286,6 +352,9 @@ def main():
         roof = {"bound": "hbm", "achieved": d["alg_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(d["alg_gbs"] / PEAK_HBM_GBS, 4)}
     roof["traffic"] = measured_traffic(dom)
+    if "frac_mfma_peak_at_clock" in d and roof["bound"] == "mfma":
+        roof["clock_ghz"] = d["clock_ghz"]
+        roof["frac_at_clock"] = d["frac_mfma_peak_at_clock"]
     roof["kernel"] = dom
     roof["kernels"] = kernels[dom]
     roof["per_launch"] = {"flop": fl, "alg_bytes": alg_bytes[dom], "avg_us": d["us_per_launch"]}
@@ -345,7 +414,7 @@ def cpu_baseline(name, prob, P, Q, n_img):
     secs = time.perf_counter() - t0
     fl = 3 * flops(sub, P, Q)
     return {"value": round(fl / secs / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"fprop+dgrad+wgrad on images 0..{n_img - 1} of {prob['N']} "
                       f"({fl / 1e9:.2f} GFLOP, {secs:.1f} s)",
             "seconds": round(secs, 2)}

@@ -304,28 +304,52 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
 
     const int ngroups = (nrows + C::GR - 1) / C::GR;
-    const int prw = wave >> 1;
+    // A wave's unit of a group: output row pr (of the band) and its blocks
+    // [c0, c0 + 32*nblk) of 32 columns, for the channel half nb.  In a whole
+    // group the two waves of each row take the two channel halves over both
+    // column blocks; a group with at most GR/2 rows (the last group of a
+    // band) gives each wave one block, so all waves work on it.
+    struct Unit {
+        int pr, slot, c0, nblk;
+        bool active;
+    };
+    auto unit = [&](int g) {
+        const int rows_g = min(C::GR, nrows - g * C::GR);
+        Unit u;
+        if (rows_g <= C::GR / 2) {
+            u.slot = (wave >> 1) & (C::GR / 2 - 1);
+            u.c0 = 32 * (wave / C::GR);
+            u.nblk = 1;
+        } else {
+            u.slot = wave >> 1;
+            u.c0 = 0;
+            u.nblk = 2;
+        }
+        u.pr = g * C::GR + u.slot;
+        u.active = u.slot < rows_g;
+        return u;
+    };
     // Output stores use 32-bit offsets from the start of the output image
     // (its size is checked on the host); stores past a row's valid pixels or
     // channels go to an offset past the range, which the range check drops.
     const __amdgpu_buffer_rsrc_t dst_rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)((elem *)a.dst + (size_t)img * a.P * a.Q * a.ngemm), (short)0,
         (int)((size_t)a.P * a.Q * a.ngemm * sizeof(elem)), 0x00020000);
-    // Each wave stages its own 64 pixels x 32 channels in its row of the
-    // staging area and stores them from there itself, so no wave waits on
-    // another for its results.
-    unsigned char *stage = ostage + prw * C::SLOTB;
 
-    // ---- epilogue, part 1: ReLU, round, into the staging as [pixel][channel]
-    // with the ring's chunk swizzle.  Lane holds pixel mb*32 + l32, channels
-    // 32*nb + 8*j + 4*lhi + 0..3 in acc[mb][4j..4j+3]: 8 bytes, half lhi of
-    // chunk 4nb+j.
+    // ---- epilogue, part 1: ReLU, round, into the staging row of the unit
+    // as [pixel][channel] with the ring's chunk swizzle.  Lane holds pixel
+    // c0 + mb*32 + l32, channels 32*nb + 8*j + 4*lhi + 0..3 in
+    // acc[mb][4j..4j+3]: 8 bytes, half lhi of chunk 4nb+j.  Each wave stages
+    // and stores its own pixels, so no wave waits on another for its
+    // results.
     acc_t acc[2];
-    auto epilogue = [&](auto relu_c) {
+    auto epilogue = [&](const Unit &u, auto relu_c) {
         constexpr bool RELU = decltype(relu_c)::value;
+        unsigned char *stage = ostage + u.slot * C::SLOTB;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const int px = mb * 32 + l32;
+            if (mb >= u.nblk) break;
+            const int px = u.c0 + mb * 32 + l32;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint32_t v[2];
@@ -339,10 +363,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     };
     // int8: lane's 4 channels -> ReLU, requantise (fp64), 4 bytes at byte
     // 8*(j&1) + 4*lhi of logical chunk 2*nb + j/2 (16 channels a chunk)
-    auto epilogue_i8 = [&]() {
+    auto epilogue_i8 = [&](const Unit &u) {
+        unsigned char *stage = ostage + u.slot * C::SLOTB;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const int px = mb * 32 + l32;
+            if (mb >= u.nblk) break;
+            const int px = u.c0 + mb * 32 + l32;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint32_t word = 0;
@@ -357,27 +383,30 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
         }
     };
-    auto stage_rows = [&]() {
+    auto stage_rows = [&](const Unit &u) {
         if constexpr (I8)
-            epilogue_i8();
+            epilogue_i8(u);
         else if (a.relu)
-            epilogue(band::BoolC<true>{});
+            epilogue(u, band::BoolC<true>{});
         else
-            epilogue(band::BoolC<false>{});
+            epilogue(u, band::BoolC<false>{});
     };
     // ---- epilogue, part 2: the wave's 16-byte chunks back from the staging
     // (its own writes: LDS runs a wave's accesses in order) and out, four
     // lanes (64 contiguous bytes) per pixel for fp16/bf16, two for int8.
     // fp16/bf16 lane order: pixels {2u, 2u+1, 2u+8, 2u+9} of a quarter-wave
     // cover all 64 banks under the swizzle.
-    auto store_rows = [&](int g) {
-        const int qrow = (p_start + g * C::GR + prw) * a.Q + q0;  // wave-uniform
+    auto store_rows = [&](const Unit &u) {
+        const unsigned char *stage = ostage + u.slot * C::SLOTB;
+        const int qrow = (p_start + u.pr) * a.Q + q0;  // wave-uniform
         asm volatile("" ::: "memory");  // the reads stay after the staging writes
         constexpr int LPP = I8 ? 2 : 4;  // lanes per pixel
+        constexpr int PPI = 64 / LPP;    // pixels per store instruction
 #pragma unroll
-        for (int t = 0; t < C::RCOLS * LPP / 64; ++t) {
-            const int u = lane / LPP, c = lane % LPP;
-            const int px = I8 ? 32 * t + u : 16 * t + (u & 1) + 8 * ((u >> 1) & 1) + 2 * (u >> 2);
+        for (int t = 0; t < C::RCOLS / PPI; ++t) {
+            if (t * PPI >= 32 * u.nblk) break;
+            const int uu = lane / LPP, c = lane % LPP;
+            const int px = u.c0 + (I8 ? PPI * t + uu : 16 * t + (uu & 1) + 8 * ((uu >> 1) & 1) + 2 * (uu >> 2));
             const int chunk = LPP * nb + c;
             const u32x4 v = *(const u32x4 *)(stage + px * C::PIXB + ((chunk ^ ((px >> 1) & 7)) << 4));
             const int ch = n0 + chunk * EPC16;
@@ -391,43 +420,53 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // MFMAs; the leading waves stage theirs right after their MFMAs, while
     // the trailing waves still run their own.
     for (int g = 0; g < ngroups; ++g) {
-        if (!lead && g > 0 && (g - 1) * C::GR + prw < nrows) {
-            stage_rows();
-            store_rows(g - 1);
+        if (!lead && g > 0) {
+            const Unit up = unit(g - 1);
+            if (up.active) {
+                stage_rows(up);
+                store_rows(up);
+            }
         }
-        const int pr = g * C::GR + prw;  // output row of this wave, relative to p_start
-        const bool active = pr < nrows;
-        if (active) {
+        const Unit u = unit(g);
+        if (u.active) {
             // the accumulators start at the bias (zero for dgrad)
             acc[0] = *(const acc_t *)(bias_s + (nb * 2 + lhi) * 16);
             acc[1] = acc[0];
             int rowb[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) rowb[r] = ((pr + r * DIL) % C::NSLOT) * C::SLOTB;
-            u32x4 P[C::KSTEPS][2];
-            auto ld = [&](int ks) {
-                const int tap = ks / C::C16, c16 = ks - tap * C::C16;
-                const int r = tap / S, s = tap - r * S;
-                const unsigned char *p = ring + rowb[r] + (t_off[s] ^ (c16 << 5));
-                P[ks][0] = *(const u32x4 *)p;
-                P[ks][1] = *(const u32x4 *)(p + 32 * C::PIXB);
+            for (int r = 0; r < R; ++r) rowb[r] = ((u.pr + r * DIL) % C::NSLOT) * C::SLOTB;
+            const int cb = u.c0 * C::PIXB;  // the unit's first column (keeps the swizzle)
+            auto mma = [&](auto two_c) {
+                constexpr int NB = decltype(two_c)::value ? 2 : 1;
+                u32x4 P[C::KSTEPS][NB];
+                auto ld = [&](int ks) {
+                    const int tap = ks / C::C16, c16 = ks - tap * C::C16;
+                    const int r = tap / S, s = tap - r * S;
+                    const unsigned char *p = ring + rowb[r] + cb + (t_off[s] ^ (c16 << 5));
+#pragma unroll
+                    for (int mb = 0; mb < NB; ++mb) P[ks][mb] = *(const u32x4 *)(p + mb * 32 * C::PIXB);
+                };
+#pragma unroll
+                for (int ks = 0; ks < C::PF; ++ks) ld(ks);
+#pragma unroll
+                for (int ks = 0; ks < C::KSTEPS; ++ks) {
+                    if (ks + C::PF < C::KSTEPS) ld(ks + C::PF);
+#pragma unroll
+                    for (int mb = 0; mb < NB; ++mb) acc[mb] = Mfma32<E>::run(fr[ks], P[ks][mb], acc[mb]);
+                    // keep the reads PF steps ahead of their MFMAs (the
+                    // scheduler would otherwise sink each read down to its use)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             };
-#pragma unroll
-            for (int ks = 0; ks < C::PF; ++ks) ld(ks);
-#pragma unroll
-            for (int ks = 0; ks < C::KSTEPS; ++ks) {
-                if (ks + C::PF < C::KSTEPS) ld(ks + C::PF);
-                acc[0] = Mfma32<E>::run(fr[ks], P[ks][0], acc[0]);
-                acc[1] = Mfma32<E>::run(fr[ks], P[ks][1], acc[1]);
-                // keep the reads PF steps ahead of their MFMAs (the scheduler
-                // would otherwise sink each read down to its use)
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            if (u.nblk == 2)
+                mma(band::BoolC<true>{});
+            else
+                mma(band::BoolC<false>{});
         }
         if (lead) {
-            if (active) {
-                stage_rows();
-                store_rows(g);
+            if (u.active) {
+                stage_rows(u);
+                store_rows(u);
             }
         } else {
             wait_vm_all();  // the next group's rows (and this wave's older stores)
@@ -435,9 +474,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         __syncthreads();  // every wave is done with this group's rows
         if (!lead) dma_group(g + 2);  // into the slots of the rows only this group read
     }
-    if (!lead && (ngroups - 1) * C::GR + prw < nrows) {
-        stage_rows();
-        store_rows(ngroups - 1);
+    if (!lead) {
+        const Unit up = unit(ngroups - 1);
+        if (up.active) {
+            stage_rows(up);
+            store_rows(up);
+        }
     }
 }
 
