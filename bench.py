@@ -75,10 +75,13 @@ def measured_traffic(pass_name):
 COUNTER_FILE = os.path.join(ROOT, "profiles", "c3a_mfma_counters.json")
 
 
-def measured_clock(pass_name):
-    """Average shader clock (GHz) of the pass's main kernel under rocprofv3,
-    from the committed counter summary, while the kernel sources are the
-    ones it was taken on; else None."""
+def measured_counters(pass_name):
+    """(clock GHz, MFMA-busy fraction) of the pass's main kernel under
+    rocprofv3, from the committed counter summary, while the kernel sources
+    are the ones it was taken on; else None.  The clock is SQ_BUSY_CYCLES per
+    shader engine over the kernel's duration (the clock weighted by the time
+    the engines were busy, so a lower bound), the fraction the matrix cores'
+    busy cycles over all SIMD cycles counted in that clock."""
     try:
         with open(COUNTER_FILE) as f:
             t = json.load(f)
@@ -87,7 +90,7 @@ def measured_clock(pass_name):
     if t.get("source_hash") != kernel_source_hash():
         return None
     p = t.get("passes", {}).get(pass_name)
-    return None if p is None else p.get("clock_ghz")
+    return None if p is None else (p.get("clock_ghz"), p.get("mfma_busy_frac"))
 
 
 def cpu_model():
@@ -335,11 +338,14 @@ def main():
             "kernels": kernels[pname],
             "plan": plans[pname],
         }
-        clk = measured_clock(pname)
-        if clk is not None:  # the dense MFMA rate at the clock the kernels ran at under the profiler
-            peak_clk = PEAK_TFLOPS[dt] * clk / SPEC_CLOCK_GHZ
-            passes[pname]["clock_ghz"] = clk
+        mc = measured_counters(pname) if name == "c3a_resnet3x3" else None
+        if mc is not None and mc[0]:
+            # the dense MFMA rate at the (lower-bound) clock the kernel ran at
+            # under the profiler, so this fraction is an upper bound
+            peak_clk = PEAK_TFLOPS[dt] * mc[0] / SPEC_CLOCK_GHZ
+            passes[pname]["clock_ghz_counters"] = mc[0]
             passes[pname]["frac_mfma_peak_at_clock"] = round(fl / (us * 1e-6) / 1e12 / peak_clk, 4)
+            passes[pname]["mfma_busy_frac_counters"] = mc[1]
     dom = max(passes, key=lambda k: passes[k]["us_per_launch"])
     d = passes[dom]
     # Compute-bound when the pass's arithmetic intensity exceeds the ridge point.
@@ -353,8 +359,9 @@ def main():
                 "frac": round(d["alg_gbs"] / PEAK_HBM_GBS, 4)}
     roof["traffic"] = measured_traffic(dom)
     if "frac_mfma_peak_at_clock" in d and roof["bound"] == "mfma":
-        roof["clock_ghz"] = d["clock_ghz"]
+        roof["clock_ghz_counters"] = d["clock_ghz_counters"]
         roof["frac_at_clock"] = d["frac_mfma_peak_at_clock"]
+        roof["mfma_busy_frac_counters"] = d["mfma_busy_frac_counters"]
     roof["kernel"] = dom
     roof["kernels"] = kernels[dom]
     roof["per_launch"] = {"flop": fl, "alg_bytes": alg_bytes[dom], "avg_us": d["us_per_launch"]}
