@@ -318,23 +318,30 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     const int vec = dtype == CONV2D_DTYPE_I8 ? 16 : 8;
     if (d.G == 1 && (d.C % vec || d.K % vec)) return plan_padded(op, prob, dtype, algo, ep, vec, pl);
 
-    // grouped fprop whose channels per group come in 128-bit chunks: the
-    // implicit GEMM, one GEMM per group (grid.y = groups x N tiles)
+    // grouped problems whose channels per group come in 128-bit chunks: the
+    // implicit GEMM, one GEMM per group (grid.y = groups x N tiles); the
+    // direct kernels follow its tiles in the table
     const bool grouped_gemm = d.G > 1 && d.Cg % vec == 0 && d.Kg % vec == 0 &&
                               (op != CONV2D_OP_WGRAD || dtype != CONV2D_DTYPE_I8);
-    if (d.G > 1 && !grouped_gemm) {
-        // tile 0: one thread per output; tile 1: the depthwise kernels
-        // (groups = C = K) or the LDS-tiled dot-product kernels (16-bit
-        // types, channel counts in 16-byte vectors, staging fits LDS)
-        pl->kernel = 2;
-        const bool dwise = direct_depthwise_ok(dtype, (int)d.C, (int)d.Cg, (int)d.Kg, (int)d.R, (int)d.S);
+    const int n_gemm = grouped_gemm ? (op == CONV2D_OP_WGRAD ? wgrad_num_tiles() : igemm_num_tiles()) : 0;
+    // direct kernels (groups > 1): tile 0 one thread per output; tile 1 the
+    // depthwise kernels (groups = C = K) or the LDS-tiled dot-product kernels
+    // (16-bit types, channel counts in 16-byte vectors, staging fits LDS)
+    int n_direct = 0;
+    bool dwise = false;
+    if (d.G > 1) {
+        dwise = direct_depthwise_ok(dtype, (int)d.C, (int)d.Cg, (int)d.Kg, (int)d.R, (int)d.S);
         const bool tiled = dwise || (op == CONV2D_OP_WGRAD
                                          ? direct_wgrad_tiled_ok(dtype, (int)d.Cg, (int)d.Kg)
                                          : direct_tiled_rows(op == CONV2D_OP_DGRAD, dtype, (int)d.R, (int)d.S,
                                                              (int)d.W, (int)d.Q, (int)d.Cg, (int)d.Kg) > 0);
-        pl->num_tiles = tiled ? 2 : 1;
+        n_direct = tiled ? 2 : 1;
+    }
+    if (d.G > 1 && (!grouped_gemm || (algo && algo->tile > n_gemm))) {
+        pl->kernel = 2;
+        pl->num_tiles = n_gemm + n_direct;
         if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
-        pl->tile = (algo && algo->tile) ? algo->tile - 1 : pl->num_tiles - 1;
+        pl->tile = (algo && algo->tile) ? algo->tile - 1 - n_gemm : n_direct - 1;
         if (op == CONV2D_OP_WGRAD) {
             const long long outputs = d.K * d.R * d.S * d.Cg;
             const long long npix = d.N * d.P * d.Q;
@@ -365,7 +372,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     }
     if (op == CONV2D_OP_WGRAD) {
         const bool wband = wgrad_band_eligible(d, dtype);
-        pl->num_tiles = wgrad_num_tiles() + (wband ? 1 : 0);
+        pl->num_tiles = wgrad_num_tiles() + (wband ? 1 : 0) + n_direct;
         if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
         // default: the band kernel when it applies and no split count is forced
         const bool use_band = algo && algo->tile ? algo->tile - 1 == kWgradBandTile
@@ -404,7 +411,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     const bool band = !ep.axpby && (op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K, d.P, d.Q)
                                                           : band_eligible(d, dtype, d.K, d.P, d.Q, d.C, d.H, d.W));
     const bool wino = band && wino_eligible(d, dtype, op);
-    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0);
+    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0) + n_direct;
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
         pl->tile = (algo && algo->tile) ? algo->tile - 1

@@ -102,7 +102,8 @@ typedef struct conv2d_problem {
  *            vectors (C/G or K/G not a multiple of 8; 16 for int8), tile 1
  *            is the one-thread-per-output direct kernel and tile 2 (when it
  *            applies) the LDS-tiled or depthwise one; other grouped problems
- *            run one implicit GEMM per group on the implicit-GEMM tiles.
+ *            run one implicit GEMM per group on the implicit-GEMM tiles, and
+ *            offer the same direct kernels as the tiles after those.
  *            A stride-1, dilation-1 3x3 fp16 problem (no
  *            linear-combination epilogue) also offers, as the last tile of
  *            fprop when C = 64 and K % 16 == 0, and of dgrad when K = 64,

@@ -232,24 +232,28 @@ def test_wgrad_band_and_generic_agree():
     problem(3, 64, 14, 13, 96, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2), groups=4),
 ], ids=["g2", "c4g_like"])
 def test_grouped_every_tile(prob):
-    """Grouped problems whose channels per group come in 16-byte chunks: fprop
-    and dgrad (every stride phase) on every implicit-GEMM tile, wgrad on both
-    generic wgrad kernels, one GEMM per group; against the oracle."""
+    """Grouped problems whose channels per group come in 16-byte chunks:
+    fprop and dgrad (every stride phase) on every implicit-GEMM tile, wgrad
+    on both generic wgrad kernels, one GEMM per group; then the direct
+    kernels, which follow the GEMM tiles in the table; against the oracle."""
     x, w, b, dy = case_inputs(prob, "f16", "int", seed=50)
     ref_y = oracle_fprop_out(prob, "f16", x, w, b, True)
     ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
     ref_dw = oracle.wgrad(prob, f64(x), f64(dy))
-    for op in (B.CONV2D_OP_FPROP, B.CONV2D_OP_DGRAD):
+    for op, n_gemm in ((B.CONV2D_OP_FPROP, 5), (B.CONV2D_OP_DGRAD, 5), (B.CONV2D_OP_WGRAD, 2)):
         info = B.conv2d_plan_info(op, prob, "f16")
-        assert info["kernel"] == 1 and info["num_tiles"] == 5
-    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
-    assert info["kernel"] == 1 and info["num_tiles"] == 2
-    for t in range(1, 6):
+        assert info["kernel"] == 1 and n_gemm < info["num_tiles"] <= n_gemm + 2, info
+        kinds = [B.conv2d_plan_info(op, prob, "f16", algo=dict(tile=t))["kernel"]
+                 for t in range(1, info["num_tiles"] + 1)]
+        assert kinds == [1] * n_gemm + [2] * (info["num_tiles"] - n_gemm), kinds
+    for t in range(1, B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")["num_tiles"] + 1):
         algo = dict(tile=t)
         check(f64(run_fprop(prob, "f16", x, w, b, True, algo=algo)), ref_y, "f16", "exact", f"tile {t}")
+    for t in range(1, B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16")["num_tiles"] + 1):
+        algo = dict(tile=t)
         check(f64(run_dgrad(prob, "f16", dy, w, algo=algo, fill=float("nan"))), ref_dx, "f16", "exact",
               f"dgrad tile {t}")
-    for t in (1, 2):
+    for t in range(1, B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")["num_tiles"] + 1):
         algo = dict(tile=t)
         check(f64(run_wgrad(prob, "f16", x, dy, algo=algo)), ref_dw, "f16", "exact", f"wgrad tile {t}")
 
@@ -392,6 +396,27 @@ def test_workload_full(name):
         a3 = float(np.dot(wb.reshape(-1), dw.reshape(-1)))
         scale = np.linalg.norm(yr) * np.linalg.norm(dyb)
         assert abs(a1 - a2) <= 2e-3 * scale and abs(a1 - a3) <= 2e-3 * scale, (a1, a2, a3, scale)
+
+
+def test_workload_c4g_direct_full():
+    """The grouped variant of the awkward workload (16x57x57x96 -> 96, 5x5
+    s2 p2 d2, groups 4, bf16) runs on the grouped implicit GEMM by default;
+    here every pass runs it on the direct kernels (the last tile of each
+    table), every output against the oracle."""
+    name = "c4g_grouped"
+    wl, prob, x, w, b, dy = _workload_inputs(name)
+    dt, mode = wl["dtype"], wl["check"]
+    algos = {}
+    for op in (B.CONV2D_OP_FPROP, B.CONV2D_OP_DGRAD, B.CONV2D_OP_WGRAD):
+        n = B.conv2d_plan_info(op, prob, dt)["num_tiles"]
+        algos[op] = dict(tile=n)
+        assert B.conv2d_plan_info(op, prob, dt, algo=algos[op])["kernel"] == 2
+    y = run_fprop(prob, dt, x, w, b, wl["relu"], algo=algos[B.CONV2D_OP_FPROP])
+    check(f64(y), oracle_fprop_out(prob, dt, x, w, b, wl["relu"]), dt, mode, "c4g direct fprop")
+    dx = run_dgrad(prob, dt, dy, w, algo=algos[B.CONV2D_OP_DGRAD], fill=float("nan"))
+    check(f64(dx), oracle.dgrad(prob, f64(dy), f64(w)), dt, mode, "c4g direct dgrad")
+    dw = run_wgrad(prob, dt, x, dy, algo=algos[B.CONV2D_OP_WGRAD])
+    check(f64(dw), oracle.wgrad(prob, f64(x), f64(dy)), dt, mode, "c4g direct wgrad")
 
 
 def test_workload_int8_full():
