@@ -134,6 +134,7 @@ struct Plan {
     // tensor is used in place).  fprop: act = x, out = y; dgrad: act = dx,
     // out = dy; wgrad: act = x, out = dy; filt = the padded filter (w or dw).
     bool padded;
+    int tile_shift;  // the padded path's tiles follow the few-channel kernel's: inner tile = tile - tile_shift
     conv2d_problem_t inner;
     size_t inner_ws, off_act, off_out, off_filt, off_bias;
 };
@@ -201,6 +202,57 @@ void wgrad_band_rows(const Dims &d, int *rows, int *chunks)
     c = std::max(1LL, std::min(c, d.P));
     *rows = (int)((d.P + c - 1) / c);
     *chunks = (int)((d.P + *rows - 1) / *rows);
+}
+
+// Few-channel fprop (fewchan.hip): the window layout of each filter row
+// (delta elements before its S*C taps, Lw elements in all), the padded input
+// row in LDS (image element 0 at element `left`, room on the right for the
+// last pixel's window) and the output rows per workgroup: about two
+// workgroups per CU, as long as the rows and the staging fit 64 KB of LDS.
+// Returns false when the kernel does not apply.
+bool fewchan_layout(const Dims &d, int dtype, FewArgs *f)
+{
+    if (d.G != 1 || !fewchan_supported(dtype, (int)d.C, (int)d.K, (int)d.S, (int)d.sw, (int)d.dw, (int)d.W))
+        return false;
+    const long long e = elem_size(dtype);
+    if (e * d.N * d.H * d.W * d.C > kBufMaxBytes) return false;
+    const long long SC = d.S * d.C;
+    const long long delta = (d.pw * d.C) & 1;
+    const long long lw = (delta + SC + 7) / 8 * 8;
+    const int nst = fewchan_steps((int)d.R, (int)lw);
+    if (!nst) return false;
+    const long long left = (d.pw * d.C + delta + 7) / 8 * 8;
+    const long long win0 = left - d.pw * d.C - delta;  // window start of pixel 0
+    const long long emax = win0 + (d.Q - 1) * d.sw * d.C + lw - 1;
+    const long long pitch_e = (std::max(left + d.W * d.C, emax + 1) + 7) / 8 * 8;
+    const long long pitch = pitch_e * 2;
+    const long long stage = std::max(d.K * (32LL * nst + 16), 4LL * 32 * (2 * d.K + 16));
+    auto buf_for = [&](long long rows) { return ((rows - 1) * d.sh + (d.R - 1) * d.dh + 1) * pitch; };
+    constexpr long long kLds = 65536 - 256;
+    long long rows = std::max(1LL, std::min(d.P, d.N * d.P / (2 * kNumCUs)));
+    while (rows > 1 && (buf_for(rows) + 1023) / 1024 * 1024 + stage > kLds) --rows;
+    const long long buf = (buf_for(rows) + 1023) / 1024 * 1024;
+    if (buf + stage > kLds) return false;
+    if (!f) return true;
+    f->N = (int)d.N; f->H = (int)d.H; f->WC = (int)(d.W * d.C); f->P = (int)d.P; f->Q = (int)d.Q;
+    f->K = (int)d.K; f->R = (int)d.R; f->SC = (int)SC;
+    f->pad_h = (int)d.ph; f->sh = (int)d.sh; f->dh = (int)d.dh;
+    f->rows_per_wg = (int)rows;
+    f->bands = (int)((d.P + rows - 1) / rows);
+    f->nrows = (int)((rows - 1) * d.sh + (d.R - 1) * d.dh + 1);
+    f->pitch = (int)pitch;
+    f->cpr = (int)(pitch_e / 8);
+    f->left = (int)left;
+    f->delta = (int)delta;
+    f->lw = (int)lw;
+    f->win0 = (int)win0;
+    f->qstep = (int)(d.sw * d.C);
+    f->buf_bytes = (int)buf;
+    f->stage_bytes = (int)stage;
+    f->x_bytes = (uint32_t)(e * d.N * d.H * d.W * d.C);
+    f->div_cpr = make_fastdiv((uint32_t)f->cpr);
+    f->div_q = make_fastdiv((uint32_t)d.Q);
+    return true;
 }
 
 int choose_wgrad_splits(long long tiles, long long npix, long long min_steps)
@@ -311,12 +363,36 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     pl->ws_bytes = 0;
     pl->tile = 0;
     pl->padded = false;
+    pl->tile_shift = 0;
     pl->off_act = pl->off_out = pl->off_filt = pl->off_bias = kNoBuf;
 
     // implicit GEMM: 128-bit chunks of channels along GEMM-K and GEMM-N;
     // other channel counts run on zero-padded copies
     const int vec = dtype == CONV2D_DTYPE_I8 ? 16 : 8;
-    if (d.G == 1 && (d.C % vec || d.K % vec)) return plan_padded(op, prob, dtype, algo, ep, vec, pl);
+    if (d.G == 1 && (d.C % vec || d.K % vec)) {
+        // fprop with few input channels: tile 0 is the few-channel kernel
+        // (the default), the padded path's tiles follow it
+        if (op != CONV2D_OP_FPROP || ep.axpby || !fewchan_layout(d, dtype, nullptr))
+            return plan_padded(op, prob, dtype, algo, ep, vec, pl);
+        conv2d_algo_t ia = algo ? *algo : conv2d_algo_t{0, 0};
+        const bool few = ia.tile <= 1;
+        ia.tile = few ? 0 : ia.tile - 1;
+        Plan pp;
+        pp.d = d;
+        st = plan_padded(op, prob, dtype, &ia, ep, vec, &pp);
+        if (!few) {
+            if (st) return st;
+            *pl = pp;
+            pl->tile += 1;
+            pl->num_tiles += 1;
+            pl->tile_shift = 1;
+            return CONV2D_OK;
+        }
+        pl->kernel = 4;
+        pl->tile = 0;
+        pl->num_tiles = 1 + (st ? 0 : pp.num_tiles);
+        return CONV2D_OK;
+    }
 
     // grouped problems whose channels per group come in 128-bit chunks: the
     // implicit GEMM, one GEMM per group (grid.y = groups x N tiles); the
@@ -633,11 +709,25 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     const Dims &d = pl.d;
     hipStream_t s = (hipStream_t)stream;
 
+    if (pl.kernel == 4) {
+        FewArgs f;
+        memset(&f, 0, sizeof(f));
+        if (!fewchan_layout(d, dtype, &f)) return CONV2D_ERR_UNSUPPORTED;
+        f.x = x; f.w = w; f.bias = bias; f.y = y; f.relu = relu;
+        return hip_status(launch_fewchan_fprop(dtype, f, s));
+    }
+
     if (pl.padded) {
         unsigned char *wsb = (unsigned char *)workspace;
         const int e = elem_size(dtype);
         const long long Cp = pl.inner.c, Kp = pl.inner.k, npix = d.N * d.P * d.Q;
         const void *xp = x, *bp = bias;
+        conv2d_algo_t ia;
+        if (pl.tile_shift && algo) {
+            ia = *algo;
+            ia.tile -= pl.tile_shift;
+            algo = &ia;
+        }
         void *yp = y;
         if (pl.off_act != kNoBuf) {
             xp = wsb + pl.off_act;

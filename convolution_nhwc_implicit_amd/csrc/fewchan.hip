@@ -1,0 +1,249 @@
+// fewchan.hip -- forward convolution of inputs with few channels (C not a
+// multiple of 8: the 3-channel RGB stem of the tensorcore "Conv2D" page's
+// 224 -> 112 example), without padding the channels.
+//
+// The GEMM view (tensorcore page, "Conv2D vs GEMM tradeoffs"; CUTLASS
+// notebook, "Iterator Algorithm", few/fixed channels) has rows = output
+// channels, columns = output pixels and a reduction over (r, s, c).  With C
+// this small an output pixel's patch is short and, within one filter row r,
+// contiguous in the NHWC input row: taps s = 0..S-1 of pixel q cover the S*C
+// elements from ((q*sw - pw)*C) on.  So the reduction is laid out per filter
+// row as a window of Lw elements (a multiple of 8) that starts delta elements
+// before that run, and a pixel's 8-element operand chunk is one 16-byte read
+// of the input row as it sits in LDS: no im2col, no zero channels.  The filter
+// is re-laid out to match (zero where a window position is not one of the
+// row's S*C taps), so window positions outside the run multiply zeros.
+// delta (0 or 1) keeps every chunk 4-byte aligned in LDS, which needs
+// stride_w*C even.
+//
+// A workgroup (4 waves) owns a band of output rows of one image:
+//   * the input rows the band reads arrive by direct-to-LDS loads into one
+//     contiguous buffer of padded rows, and the left/right padding and rows
+//     outside the image come from the buffer range check as zeros;
+//   * the filter, re-laid out, is staged in LDS and held in VGPRs (the A
+//     operand, one or two blocks of 32 output channels);
+//   * the band's pixels, numbered row by row, are cut into blocks of 32 (the
+//     B operand columns of one 32x32x16 MFMA); wave w takes blocks w, w+4, ...
+//     Each block adds bias, applies ReLU, rounds, and is staged in LDS so
+//     that its 32 output pixels -- contiguous in y -- leave as 16-byte
+//     stores.
+#include "device_common.h"
+
+namespace cnv {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace fc {
+constexpr int NT = 256;
+constexpr int WAVES = NT / 64;
+
+template <class E>
+__device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ inline f32x16 mfma32<EF16>(u32x4 a, u32x4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                   0, 0, 0);
+}
+template <>
+__device__ inline f32x16 mfma32<EBF16>(u32x4 a, u32x4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                    c, 0, 0, 0);
+}
+}  // namespace fc
+
+// KB blocks of 32 output channels (K = 32*KB); NST 16-element reduction
+// steps (2*NST chunks of 8 >= R*Lw/8; chunks past R*Lw have a zero filter).
+template <class E, int KB, int NST>
+__global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
+{
+    using elem = typename E::elem;
+    constexpr int K = 32 * KB;
+    constexpr int TW = 16 * NST;          // reduction length held per output channel
+    constexpr int FPITCH = TW * 2 + 16;   // staged filter row (bytes), padded against bank conflicts
+    constexpr int OPITCH = K * 2 + 16;    // staged output pixel (bytes)
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char *rows = smem;                             // a.buf_bytes
+    unsigned char *stage = smem + a.buf_bytes;              // filter, then output staging
+    float *bias_s = (float *)(smem + a.buf_bytes + a.stage_bytes);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int img = blockIdx.x / a.bands;
+    const int band = blockIdx.x - img * a.bands;
+    const int p0 = band * a.rows_per_wg;
+    const int rows_out = min(a.rows_per_wg, a.P - p0);
+    const int npix = rows_out * a.Q;
+    const int h0 = p0 * a.sh - a.pad_h;  // input row of buffer row 0
+
+    // ---- input rows: 16-byte chunk u of the buffer is row u / cpr, element
+    // (u % cpr)*8 - left of that row; everything outside the image reads zero
+    {
+        const u32x4 xr = make_buf_rsrc(a.x, a.x_bytes);
+        const uint32_t rows_lds = lds_addr(rows);
+        const int nblk = a.buf_bytes >> 10;
+        for (int blk = wave; blk < nblk; blk += fc::WAVES) {
+            const uint32_t u = (uint32_t)(blk * 64 + lane);
+            const uint32_t rr = fdiv(u, a.div_cpr);
+            const int e0 = (int)(u - rr * (uint32_t)a.cpr) * 8 - a.left;
+            const int h = h0 + (int)rr;
+            const bool in = (int)rr < a.nrows && (unsigned)h < (unsigned)a.H && e0 >= 0 && e0 < a.WC;
+            dma16(xr, rows_lds + (uint32_t)(blk * 1024),
+                  in ? ((uint32_t)(img * a.H + h) * (uint32_t)a.WC + (uint32_t)e0) * 2u : kBufOOBFar);
+        }
+    }
+    // ---- the filter, re-laid out: staged row m holds, for t < R*Lw, window
+    // position kk = t % Lw of filter row r = t / Lw, i.e. w[m][r][kk - delta]
+    // when 0 <= kk - delta < S*C, else zero
+    {
+        const elem *w = (const elem *)a.w;
+        const int SC = a.SC;
+        for (int idx = tid; idx < K * (TW / 8); idx += fc::NT) {
+            const int m = idx / (TW / 8), c = idx - m * (TW / 8);
+            const int t0 = c * 8;
+            const int r = t0 / a.lw, kk0 = t0 - r * a.lw;
+            uint32_t v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t pair = 0;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int sc = kk0 + 2 * i + j - a.delta;
+                    const uint32_t e = (r < a.R && sc >= 0 && sc < SC) ? (uint32_t)w[(m * a.R + r) * SC + sc] : 0u;
+                    pair |= e << (16 * j);
+                }
+                v[i] = pair;
+            }
+            *(u32x4 *)(stage + m * FPITCH + c * 16) = u32x4{v[0], v[1], v[2], v[3]};
+        }
+        if (tid < K) bias_s[tid] = a.bias ? E::to_f32(((const elem *)a.bias)[tid]) : 0.0f;
+    }
+    wait_vm_all();    // this wave's row loads
+    __syncthreads();  // rows, filter and bias visible to every wave
+
+    // ---- A operand: output channels 32*mb + l32, chunk 2*j + lhi of the
+    // reduction (lane holds k = 8*lhi + 0..7 of step j)
+    const int l32 = lane & 31, lhi = lane >> 5;
+    u32x4 fa[KB][NST];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NST; ++j)
+            fa[mb][j] = *(const u32x4 *)(stage + (32 * mb + l32) * FPITCH + (2 * j + lhi) * 16);
+    // per step, the byte offset of this lane's chunk from its pixel's window
+    // start in buffer row pl*sh: filter row r = t/Lw (dh*r rows down) and
+    // window position kk0 = t % Lw; chunks past the filter read the window
+    // start (their filter is zero)
+    uint32_t coff[NST];
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+        const int t0 = (2 * j + lhi) * 8;
+        const int r = t0 / a.lw, kk0 = t0 - r * a.lw;
+        coff[j] = r < a.R ? (uint32_t)(r * a.dh * a.pitch + kk0 * 2) : 0u;
+    }
+    // the bias in the accumulator layout
+    float bv[KB][16];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bv[mb][i] = bias_s[32 * mb + 8 * (i >> 2) + 4 * lhi + (i & 3)];
+    __syncthreads();  // the filter staging is free for the outputs
+
+    unsigned char *ost = stage + wave * 32 * OPITCH;
+    const int nblocks = (npix + 31) >> 5;
+    elem *ybase = (elem *)a.y + ((size_t)img * a.P + p0) * a.Q * K;
+    for (int blk = wave; blk < nblocks; blk += fc::WAVES) {
+        const int v = min(blk * 32 + l32, npix - 1);
+        const int pl = (int)fdiv((uint32_t)v, a.div_q);
+        const int q = v - pl * a.Q;
+        // window start of pixel (pl, q) in buffer row pl*sh: element
+        // left + (q*sw - pw)*C - delta, 4-byte aligned
+        const unsigned char *pb = rows + pl * a.sh * a.pitch + (a.win0 + q * a.qstep) * 2;
+        // all of the block's pixel chunks first (2-dword reads: the chunks
+        // are 4-byte aligned), then the MFMAs
+        u32x4 bf[NST];
+#pragma unroll
+        for (int j = 0; j < NST; ++j) {
+            const uint32_t *p = (const uint32_t *)(pb + coff[j]);
+            bf[j] = u32x4{p[0], p[1], p[2], p[3]};
+        }
+        f32x16 acc[KB];
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb) acc[mb] = f32x16{};
+#pragma unroll
+        for (int j = 0; j < NST; ++j)
+#pragma unroll
+            for (int mb = 0; mb < KB; ++mb) acc[mb] = fc::mfma32<E>(fa[mb][j], bf[j], acc[mb]);
+        // epilogue: lane holds pixel l32, channels 32*mb + 8*g + 4*lhi + 0..3
+        // in acc[mb][4*g + 0..3]
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = bias_relu_f32(acc[mb][4 * g + i], bv[mb][4 * g + i], a.relu);
+                const uint2 pk = {out_pair<E, false>(o[0], o[1]), out_pair<E, false>(o[2], o[3])};
+                *(uint2 *)(ost + l32 * OPITCH + (32 * mb + 8 * g + 4 * lhi) * 2) = pk;
+            }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's staging writes are done
+        __builtin_amdgcn_wave_barrier();
+        // 32 pixels x K channels, contiguous in y from pixel blk*32
+        const int npx = min(32, npix - blk * 32);
+#pragma unroll
+        for (int it = 0; it < 32 * K * 2 / 1024; ++it) {
+            const int o = it * 1024 + lane * 16;
+            const int px = o / (K * 2), off = o - px * (K * 2);
+            const u32x4 val = *(const u32x4 *)(ost + px * OPITCH + off);
+            if (px < npx) *(u32x4 *)((unsigned char *)(ybase + (size_t)(blk * 32 + px) * K) + off) = val;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+bool fewchan_supported(int dtype, int C, int K, int S, int sw, int dw, int W)
+{
+    if (dtype != CONV2D_DTYPE_F16 && dtype != CONV2D_DTYPE_BF16) return false;
+    if (C % 8 == 0 || dw != 1 || (sw * C) % 2 || (W * C) % 8) return false;
+    if (K != 32 && K != 64) return false;
+    return true;
+}
+
+// Reduction steps (of 16) the kernels are built for.
+static int fewchan_nst(int need)
+{
+    static const int kSteps[] = {4, 8, 11, 12, 16};
+    for (int s : kSteps)
+        if (s >= need) return s;
+    return 0;
+}
+int fewchan_steps(int R, int lw) { return fewchan_nst((R * lw + 15) / 16); }
+
+template <class E, int KB>
+static hipError_t launch_kb(int nst, const FewArgs &a, hipStream_t st)
+{
+    const dim3 grid((unsigned)(a.N * a.bands)), block(fc::NT);
+    const size_t lds = (size_t)a.buf_bytes + a.stage_bytes + 64 * sizeof(float);
+    switch (nst) {
+    case 4: fewchan_fprop_kernel<E, KB, 4><<<grid, block, lds, st>>>(a); break;
+    case 8: fewchan_fprop_kernel<E, KB, 8><<<grid, block, lds, st>>>(a); break;
+    case 11: fewchan_fprop_kernel<E, KB, 11><<<grid, block, lds, st>>>(a); break;
+    case 12: fewchan_fprop_kernel<E, KB, 12><<<grid, block, lds, st>>>(a); break;
+    case 16: fewchan_fprop_kernel<E, KB, 16><<<grid, block, lds, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fewchan_fprop(int dtype, const FewArgs &a, hipStream_t st)
+{
+    const int nst = fewchan_steps(a.R, a.lw);
+    if (a.K == 64)
+        return dtype == CONV2D_DTYPE_F16 ? launch_kb<EF16, 2>(nst, a, st) : launch_kb<EBF16, 2>(nst, a, st);
+    if (a.K == 32)
+        return dtype == CONV2D_DTYPE_F16 ? launch_kb<EF16, 1>(nst, a, st) : launch_kb<EBF16, 1>(nst, a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace cnv

@@ -254,6 +254,32 @@ bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q);
 hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Few-channel fprop (fewchan.hip): groups == 1, C not a multiple of 8,
+// stride_w*C even, dil_w == 1, K = 32 or 64, fp16/bf16.  Each filter row's
+// S*C taps are read as a window of lw elements (a multiple of 8) starting
+// delta elements before them.  A workgroup computes rows_per_wg output rows
+// of one image from nrows padded input rows in LDS (pitch bytes each, cpr
+// 16-byte chunks, the image row's first element at element `left`).
+// ---------------------------------------------------------------------------
+struct FewArgs {
+    const void *x, *w, *bias;
+    void *y;
+    int N, H, WC, P, Q, K, R, SC;
+    int pad_h, sh, dh;
+    int relu;
+    int rows_per_wg, bands;   // output rows per workgroup, workgroups per image
+    int nrows, pitch, cpr, left;
+    int delta, lw;
+    int win0, qstep;          // window start of pixel q: element win0 + q*qstep of its row
+    int buf_bytes, stage_bytes;
+    uint32_t x_bytes;
+    FastDiv div_cpr, div_q;
+};
+bool fewchan_supported(int dtype, int C, int K, int S, int sw, int dw, int W);
+int fewchan_steps(int R, int lw);  // reduction steps of the kernel built for R*lw, 0 if none
+hipError_t launch_fewchan_fprop(int dtype, const FewArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Direct convolution for groups > 1: one thread per output element, fp32
 // (int32 for int8) accumulation in a fixed (r, s, channel) order.
 // ---------------------------------------------------------------------------

@@ -16,7 +16,7 @@ from convolution_nhwc_implicit_amd import binding as B
 from convolution_nhwc_implicit_amd import workloads as WL
 from convolution_nhwc_implicit_amd.workloads import problem
 
-from parity import check, f64, oracle_fprop_out, run_dgrad, run_fprop, run_wgrad
+from parity import DEV, check, f64, gpu, oracle_fprop_out, run_dgrad, run_fprop, run_wgrad
 
 pytestmark = pytest.mark.gpu
 
@@ -359,6 +359,49 @@ def test_direct_tiled_kernels(cid, prob, dtype, dist, bias, relu, tiled):
     for algo in (None, dict(tile=1)) + ((dict(tile=2), dict(tile=2, split_k=3)) if "wgrad" in tiled else ()):
         tag = f"{cid} tile {algo['tile'] if algo else 'default'}"
         check(f64(run_wgrad(prob, dtype, x, dy, algo=algo)), ref_dw, dtype, mode, f"{tag} wgrad")
+
+
+# ---------------------------------------------------- few input channels
+
+# C not a multiple of 8 with stride_w*C even, W*C a multiple of 8 and K = 32
+# or 64: the few-channel fprop kernel (the default), each filter row's S*C
+# taps read as one window of the input row.  Window lengths 8..32 (reduction
+# steps 1..14 of the built 4, 8, 11, 12, 16), odd and even pads (the window
+# starts one element early when pad_w*C is odd), row dilation, 1x1, and a
+# ragged last band (P = 25 over bands of 3 rows).
+FEW_CASES = [
+    ("few_stem", problem(2, 3, 32, 32, 64, 7, 7, pad=(3, 3), stride=(2, 2)), "f16", "int", True, True),
+    ("few_stem_ragged", problem(64, 3, 50, 32, 64, 7, 7, pad=(3, 3), stride=(2, 2)), "f16", "gauss", True, True),
+    ("few_c4_k32", problem(2, 4, 17, 22, 32, 3, 3, pad=(1, 1)), "bf16", "gauss", True, False),
+    ("few_c2_dil", problem(2, 2, 19, 20, 64, 5, 5, pad=(2, 2), dil=(2, 1)), "f16", "int", False, False),
+    ("few_c1_s2", problem(3, 1, 25, 24, 32, 3, 3, stride=(2, 2)), "f16", "int", True, True),
+    ("few_c6", problem(3, 6, 9, 12, 64, 3, 3, pad=(1, 1)), "bf16", "int", True, False),
+    ("few_c5_1x1", problem(2, 5, 8, 16, 32, 1, 1, stride=(2, 2)), "f16", "int", True, False),
+    ("few_c3_asym", problem(2, 3, 11, 40, 64, 2, 5, pad=(0, 2), stride=(1, 2)), "f16", "int", True, True),
+    ("few_c4_7x7", problem(2, 4, 20, 22, 64, 7, 7, pad=(3, 3)), "f16", "int", True, True),
+    ("few_c3_8x7", problem(2, 3, 21, 24, 32, 8, 7, pad=(3, 3), stride=(2, 2)), "bf16", "int", True, False),
+]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,dist,bias,relu", FEW_CASES, ids=[c[0] for c in FEW_CASES])
+def test_fewchan_fprop(cid, prob, dtype, dist, bias, relu):
+    info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype)
+    assert info["kernel"] == 4 and info["tile"] == 0 and info["workspace_bytes"] == 0, info
+    mode = "exact" if dist == "int" else "tol"
+    x, w, b, _ = case_inputs(prob, dtype, dist, seed=zlib.crc32(cid.encode()), bias=bias)
+    ref = oracle_fprop_out(prob, dtype, x, w, b, relu)
+    P, Q = B.conv2d_output_size(prob)
+    y = torch.full((prob["N"], P, Q, prob["K"]), float("nan"), dtype=x.dtype, device=DEV)
+    B.conv2d_fprop(prob, dtype, gpu(x), gpu(w), gpu(b), relu, 1.0, 1.0, 1.0, y, None)
+    torch.cuda.synchronize()
+    check(f64(y), ref, dtype, mode, f"{cid} few-channel")
+    if relu:
+        assert not bool((y.view(torch.int16) == -32768).any()), f"{cid}: -0 after ReLU"
+    # the padded path's first tile gives the same answer
+    yp = run_fprop(prob, dtype, x, w, b, relu, algo=dict(tile=2))
+    check(f64(yp), ref, dtype, mode, f"{cid} padded tile")
+    if mode == "exact":
+        assert torch.equal(y.view(torch.int16), yp.view(torch.int16))
 
 
 # ------------------------------------------------------------- the workloads
