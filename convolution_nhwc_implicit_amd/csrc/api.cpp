@@ -226,7 +226,9 @@ bool fewchan_layout(const Dims &d, int dtype, FewArgs *f)
     const long long emax = win0 + (d.Q - 1) * d.sw * d.C + lw - 1;
     const long long pitch_e = (std::max(left + d.W * d.C, emax + 1) + 7) / 8 * 8;
     const long long pitch = pitch_e * 2;
-    const long long stage = std::max(d.K * (32LL * nst + 16), 4LL * 32 * (2 * d.K + 16));
+    // the filter as it is (whole 1 KB blocks, and room for window reads up to
+    // lw elements past it), then the output staging of the four waves
+    const long long stage = std::max((d.K * d.R * SC * e + 2 * lw + 1023) / 1024 * 1024, 4LL * 32 * (2 * d.K + 16));
     auto buf_for = [&](long long rows) { return ((rows - 1) * d.sh + (d.R - 1) * d.dh + 1) * pitch; };
     constexpr long long kLds = 65536 - 256;
     long long rows = std::max(1LL, std::min(d.P, d.N * d.P / (2 * kNumCUs)));
@@ -252,6 +254,22 @@ bool fewchan_layout(const Dims &d, int dtype, FewArgs *f)
     f->x_bytes = (uint32_t)(e * d.N * d.H * d.W * d.C);
     f->div_cpr = make_fastdiv((uint32_t)f->cpr);
     f->div_q = make_fastdiv((uint32_t)d.Q);
+    for (int j = 0; j < kFewMaxSteps; ++j)
+        for (int h = 0; h < 2; ++h) {
+            const long long t0 = 8LL * (2 * j + h), r = t0 / lw, kk0 = t0 - r * lw;
+            FewStep &st = f->step[j];
+            const bool rok = j < nst && r < d.R;
+            st.fbase[h] = rok ? (int)(r * SC + kk0 - delta) : 0;
+            st.coff[h] = rok ? (uint32_t)(r * d.dh * pitch + kk0 * 2) : 0u;
+            for (int p = 0; p < 4; ++p) {
+                uint32_t m = 0;
+                for (int k = 0; k < 2; ++k) {
+                    const long long sc = kk0 + 2 * p + k - delta;
+                    if (rok && sc >= 0 && sc < SC) m |= 0xffffu << (16 * k);
+                }
+                st.mask[h][p] = m;
+            }
+        }
     return true;
 }
 

@@ -412,7 +412,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             const int ch = n0 + chunk * EPC16;
             const bool ok = px < C::SEG && q0 + px < a.Q && ch < a.ngemm;
             __builtin_amdgcn_raw_buffer_store_b128(
-                v, dst_rs, ok ? (uint32_t)(((qrow + px) * a.ngemm + ch) * (int)sizeof(elem)) : kBufOOB, 0, 0);
+                v, dst_rs, ok ? (uint32_t)(((qrow + px) * a.ngemm + ch) * (int)sizeof(elem)) : kBufOOB, 0, 2);
         }
     };
     // The trailing waves stage and store group g's results after the barrier

@@ -11,7 +11,7 @@
 // row as a window of Lw elements (a multiple of 8) that starts delta elements
 // before that run, and a pixel's 8-element operand chunk is one 16-byte read
 // of the input row as it sits in LDS: no im2col, no zero channels.  The filter
-// is re-laid out to match (zero where a window position is not one of the
+// is read in the same layout (zero where a window position is not one of the
 // row's S*C taps), so window positions outside the run multiply zeros.
 // delta (0 or 1) keeps every chunk 4-byte aligned in LDS, which needs
 // stride_w*C even.
@@ -20,8 +20,8 @@
 //   * the input rows the band reads arrive by direct-to-LDS loads into one
 //     contiguous buffer of padded rows, and the left/right padding and rows
 //     outside the image come from the buffer range check as zeros;
-//   * the filter, re-laid out, is staged in LDS and held in VGPRs (the A
-//     operand, one or two blocks of 32 output channels);
+//   * the filter is loaded into LDS as it is and read into VGPRs in the
+//     window layout (the A operand, one or two blocks of 32 output channels);
 //   * the band's pixels, numbered row by row, are cut into blocks of 32 (the
 //     B operand columns of one 32x32x16 MFMA); wave w takes blocks w, w+4, ...
 //     Each block adds bias, applies ReLU, rounds, and is staged in LDS so
@@ -60,12 +60,10 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
 {
     using elem = typename E::elem;
     constexpr int K = 32 * KB;
-    constexpr int TW = 16 * NST;          // reduction length held per output channel
-    constexpr int FPITCH = TW * 2 + 16;   // staged filter row (bytes), padded against bank conflicts
     constexpr int OPITCH = K * 2 + 16;    // staged output pixel (bytes)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *rows = smem;                             // a.buf_bytes
-    unsigned char *stage = smem + a.buf_bytes;              // filter, then output staging
+    unsigned char *stage = smem + a.buf_bytes;              // the filter, then output staging
     float *bias_s = (float *)(smem + a.buf_bytes + a.stage_bytes);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -93,61 +91,63 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
                   in ? ((uint32_t)(img * a.H + h) * (uint32_t)a.WC + (uint32_t)e0) * 2u : kBufOOBFar);
         }
     }
-    // ---- the filter, re-laid out: staged row m holds, for t < R*Lw, window
-    // position kk = t % Lw of filter row r = t / Lw, i.e. w[m][r][kk - delta]
-    // when 0 <= kk - delta < S*C, else zero
+    // ---- the filter as it is ([K][R][S*C], K*R*S*C a multiple of 8
+    // elements) by direct-to-LDS loads into the staging area
+    const int fchunks = K * a.R * a.SC / 8;
     {
-        const elem *w = (const elem *)a.w;
-        const int SC = a.SC;
-        for (int idx = tid; idx < K * (TW / 8); idx += fc::NT) {
-            const int m = idx / (TW / 8), c = idx - m * (TW / 8);
-            const int t0 = c * 8;
-            const int r = t0 / a.lw, kk0 = t0 - r * a.lw;
-            uint32_t v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t pair = 0;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int sc = kk0 + 2 * i + j - a.delta;
-                    const uint32_t e = (r < a.R && sc >= 0 && sc < SC) ? (uint32_t)w[(m * a.R + r) * SC + sc] : 0u;
-                    pair |= e << (16 * j);
-                }
-                v[i] = pair;
-            }
-            *(u32x4 *)(stage + m * FPITCH + c * 16) = u32x4{v[0], v[1], v[2], v[3]};
+        const u32x4 wr = make_buf_rsrc(a.w, (uint32_t)fchunks * 16u);
+        const uint32_t st_lds = lds_addr(stage);
+        for (int blk = wave; blk * 64 < fchunks; blk += fc::WAVES) {
+            const int u = blk * 64 + lane;
+            dma16(wr, st_lds + (uint32_t)(blk * 1024), u < fchunks ? (uint32_t)u * 16u : kBufOOB);
         }
         if (tid < K) bias_s[tid] = a.bias ? E::to_f32(((const elem *)a.bias)[tid]) : 0.0f;
     }
-    wait_vm_all();    // this wave's row loads
+    wait_vm_all();    // this wave's row and filter loads
     __syncthreads();  // rows, filter and bias visible to every wave
 
-    // ---- A operand: output channels 32*mb + l32, chunk 2*j + lhi of the
-    // reduction (lane holds k = 8*lhi + 0..7 of step j)
+    // ---- A operand: output channel m = 32*mb + l32, chunk 2*j + lhi of the
+    // reduction (lane holds k = 8*lhi + 0..7 of step j): the 8 consecutive
+    // filter elements of row m from a.step[j].fbase[lhi], with the halves
+    // outside the filter row's S*C taps masked to zero (reads past the
+    // filter stay inside the staging area, which has room past it).  B
+    // operand chunks sit a.step[j].coff[lhi] bytes from a pixel's window.
     const int l32 = lane & 31, lhi = lane >> 5;
     u32x4 fa[KB][NST];
-#pragma unroll
-    for (int mb = 0; mb < KB; ++mb)
-#pragma unroll
-        for (int j = 0; j < NST; ++j)
-            fa[mb][j] = *(const u32x4 *)(stage + (32 * mb + l32) * FPITCH + (2 * j + lhi) * 16);
-    // per step, the byte offset of this lane's chunk from its pixel's window
-    // start in buffer row pl*sh: filter row r = t/Lw (dh*r rows down) and
-    // window position kk0 = t % Lw; chunks past the filter read the window
-    // start (their filter is zero)
     uint32_t coff[NST];
+    {
+        const int RSC = a.R * a.SC;
 #pragma unroll
-    for (int j = 0; j < NST; ++j) {
-        const int t0 = (2 * j + lhi) * 8;
-        const int r = t0 / a.lw, kk0 = t0 - r * a.lw;
-        coff[j] = r < a.R ? (uint32_t)(r * a.dh * a.pitch + kk0 * 2) : 0u;
+        for (int j = 0; j < NST; ++j) {
+            const FewStep &st = a.step[j];
+            const int base = lhi ? st.fbase[1] : st.fbase[0];
+            coff[j] = lhi ? st.coff[1] : st.coff[0];
+            uint32_t mk[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) mk[p] = lhi ? st.mask[1][p] : st.mask[0][p];
+#pragma unroll
+            for (int mb = 0; mb < KB; ++mb) {
+                // 16 bytes at a 2-byte aligned offset: five aligned dwords,
+                // shifted into place
+                const uint32_t off = (uint32_t)((32 * mb + l32) * RSC + base) * 2u;
+                const uint32_t *d4 = (const uint32_t *)(stage + (off & ~3u));
+                const uint32_t sh = (off & 2u) * 8u;
+                uint32_t d[5];
+#pragma unroll
+                for (int i = 0; i < 5; ++i) d[i] = d4[i];
+                uint32_t v[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) v[p] = __builtin_amdgcn_alignbit(d[p + 1], d[p], sh) & mk[p];
+                fa[mb][j] = u32x4{v[0], v[1], v[2], v[3]};
+            }
+        }
     }
     // the bias in the accumulator layout
-    float bv[KB][16];
+    f32x4 bv[KB][4];
 #pragma unroll
     for (int mb = 0; mb < KB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) bv[mb][i] = bias_s[32 * mb + 8 * (i >> 2) + 4 * lhi + (i & 3)];
+        for (int g = 0; g < 4; ++g) bv[mb][g] = *(const f32x4 *)(bias_s + 32 * mb + 8 * g + 4 * lhi);
     __syncthreads();  // the filter staging is free for the outputs
 
     unsigned char *ost = stage + wave * 32 * OPITCH;
@@ -168,6 +168,7 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
             const uint32_t *p = (const uint32_t *)(pb + coff[j]);
             bf[j] = u32x4{p[0], p[1], p[2], p[3]};
         }
+        __builtin_amdgcn_sched_barrier(0);  // every read in flight before the first MFMA
         f32x16 acc[KB];
 #pragma unroll
         for (int mb = 0; mb < KB; ++mb) acc[mb] = f32x16{};
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
             for (int g = 0; g < 4; ++g) {
                 float o[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = bias_relu_f32(acc[mb][4 * g + i], bv[mb][4 * g + i], a.relu);
+                for (int i = 0; i < 4; ++i) o[i] = bias_relu_f32(acc[mb][4 * g + i], bv[mb][g][i], a.relu);
                 const uint2 pk = {out_pair<E, false>(o[0], o[1]), out_pair<E, false>(o[2], o[3])};
                 *(uint2 *)(ost + l32 * OPITCH + (32 * mb + 8 * g + 4 * lhi) * 2) = pk;
             }
@@ -196,7 +197,8 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
             const int o = it * 1024 + lane * 16;
             const int px = o / (K * 2), off = o - px * (K * 2);
             const u32x4 val = *(const u32x4 *)(ost + px * OPITCH + off);
-            if (px < npx) *(u32x4 *)((unsigned char *)(ybase + (size_t)(blk * 32 + px) * K) + off) = val;
+            if (px < npx)  // streaming stores: y is not read again here
+                __builtin_nontemporal_store(val, (u32x4 *)((unsigned char *)(ybase + (size_t)(blk * 32 + px) * K) + off));
         }
         __builtin_amdgcn_wave_barrier();
     }

@@ -295,7 +295,8 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
         const int row = id / OCH, cc = id % OCH;
         const uint32_t m = (uint32_t)mt * BM + row;
         if (m >= ph.m_total || cc * EPO >= nvalid) continue;
-        *(u32x4 *)(dst + out_offset(m) + ncol0 + cc * EPO) = *(const u32x4 *)(smem + row * CROWB + cc * 16);
+        __builtin_nontemporal_store(*(const u32x4 *)(smem + row * CROWB + cc * 16),
+                                    (u32x4 *)(dst + out_offset(m) + ncol0 + cc * EPO));
     }
 }
 

@@ -261,6 +261,18 @@ hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st);
 // of one image from nrows padded input rows in LDS (pitch bytes each, cpr
 // 16-byte chunks, the image row's first element at element `left`).
 // ---------------------------------------------------------------------------
+// Per reduction step j and lane half h (chunk c = 2*j + h, t0 = 8*c in filter
+// row r = t0 / Lw at window position kk0 = t0 % Lw): the filter element
+// offset within an output channel's R*S*C (r*S*C + kk0 - delta), the masks of
+// the chunk's valid 16-bit halves (kk0 + i - delta in [0, S*C), r < R), and
+// the chunk's byte offset from a pixel's window start in LDS (r*dh rows down,
+// kk0 elements on).  Chunks past the filter: mask 0, offsets 0.
+constexpr int kFewMaxSteps = 16;
+struct FewStep {
+    int fbase[2];
+    uint32_t mask[2][4];
+    uint32_t coff[2];
+};
 struct FewArgs {
     const void *x, *w, *bias;
     void *y;
@@ -274,6 +286,7 @@ struct FewArgs {
     int buf_bytes, stage_bytes;
     uint32_t x_bytes;
     FastDiv div_cpr, div_q;
+    FewStep step[kFewMaxSteps];
 };
 bool fewchan_supported(int dtype, int C, int K, int S, int sw, int dw, int W);
 int fewchan_steps(int R, int lw);  // reduction steps of the kernel built for R*lw, 0 if none

@@ -403,7 +403,8 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
             add(part(1 - KEEP), i, v);
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                out[(size_t)(KEEP * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3)) * NCOLS + (CB0 + i) * 32 + l32] = v[r];
+                __builtin_nontemporal_store(
+                    v[r], &out[(size_t)(KEEP * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3)) * NCOLS + (CB0 + i) * 32 + l32]);
         }
     };
     if (phase == 0) keep(IntC<0>{});
