@@ -230,7 +230,7 @@ bool fewchan_layout(const Dims &d, int dtype, FewArgs *f)
     // lw elements past it), then the output staging of the four waves
     const long long stage = std::max((d.K * d.R * SC * e + 2 * lw + 1023) / 1024 * 1024, 4LL * 32 * (2 * d.K + 16));
     auto buf_for = [&](long long rows) { return ((rows - 1) * d.sh + (d.R - 1) * d.dh + 1) * pitch; };
-    constexpr long long kLds = 65536 - 256;
+    constexpr long long kLds = 65536 - 1024;  // the last 1 KB holds the bias
     long long rows = std::max(1LL, std::min(d.P, d.N * d.P / (2 * kNumCUs)));
     while (rows > 1 && (buf_for(rows) + 1023) / 1024 * 1024 + stage > kLds) --rows;
     const long long buf = (buf_for(rows) + 1023) / 1024 * 1024;

@@ -493,7 +493,7 @@ __device__ inline void store8(const DirectArgs &a, typename E::elem *dst, size_t
         }
         w[j2] = h[0] | (h[1] << 16);
     }
-    *(u32x4 *)(dst + o) = u32x4{w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4 *)(dst + o));  // streamed out
 }
 
 // The filter [C][R][S] is C*R*S contiguous elements, a whole number of

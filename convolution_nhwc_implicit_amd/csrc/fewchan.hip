@@ -64,7 +64,7 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *rows = smem;                             // a.buf_bytes
     unsigned char *stage = smem + a.buf_bytes;              // the filter, then output staging
-    float *bias_s = (float *)(smem + a.buf_bytes + a.stage_bytes);
+    unsigned char *bias_raw = smem + a.buf_bytes + a.stage_bytes;  // 1 KB: the bias, then zeros
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,9 +75,29 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
     const int npix = rows_out * a.Q;
     const int h0 = p0 * a.sh - a.pad_h;  // input row of buffer row 0
 
-    // ---- input rows: 16-byte chunk u of the buffer is row u / cpr, element
-    // (u % cpr)*8 - left of that row; everything outside the image reads zero
+    // ---- direct-to-LDS loads, in the order they are needed: the filter as it
+    // is ([K][R][S*C], K*R*S*C a multiple of 8 elements) into the staging
+    // area, the bias (raw elements; zeros without one), then the input rows.
+    // Input row chunk u of the buffer is row u / cpr, element (u % cpr)*8 -
+    // left of that row; everything outside the image reads zero.
+    const int fchunks = K * a.R * a.SC / 8;
+    int nrow_ops = 0;  // this wave's row loads, issued last
     {
+        const u32x4 wr = make_buf_rsrc(a.w, (uint32_t)fchunks * 16u);
+        const uint32_t st_lds = lds_addr(stage);
+        for (int blk = wave; blk * 64 < fchunks; blk += fc::WAVES) {
+            const int u = blk * 64 + lane;
+            dma16(wr, st_lds + (uint32_t)(blk * 1024), u < fchunks ? (uint32_t)u * 16u : kBufOOB);
+        }
+        if (wave == 0) {
+            // whole 16-byte chunks from the boundary at or below the bias (the
+            // range check zeroes a chunk that is partly out of range; a chunk
+            // never crosses a page)
+            const uint32_t bshift = (uint32_t)((uintptr_t)a.bias & 15u);
+            const u32x4 br = make_buf_rsrc((const unsigned char *)a.bias - bshift,
+                                           a.bias ? (bshift + (uint32_t)(K * sizeof(elem)) + 15u) & ~15u : 0u);
+            dma16(br, lds_addr(bias_raw), (uint32_t)lane * 16u);
+        }
         const u32x4 xr = make_buf_rsrc(a.x, a.x_bytes);
         const uint32_t rows_lds = lds_addr(rows);
         const int nblk = a.buf_bytes >> 10;
@@ -89,22 +109,31 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
             const bool in = (int)rr < a.nrows && (unsigned)h < (unsigned)a.H && e0 >= 0 && e0 < a.WC;
             dma16(xr, rows_lds + (uint32_t)(blk * 1024),
                   in ? ((uint32_t)(img * a.H + h) * (uint32_t)a.WC + (uint32_t)e0) * 2u : kBufOOBFar);
+            ++nrow_ops;
         }
     }
-    // ---- the filter as it is ([K][R][S*C], K*R*S*C a multiple of 8
-    // elements) by direct-to-LDS loads into the staging area
-    const int fchunks = K * a.R * a.SC / 8;
-    {
-        const u32x4 wr = make_buf_rsrc(a.w, (uint32_t)fchunks * 16u);
-        const uint32_t st_lds = lds_addr(stage);
-        for (int blk = wave; blk * 64 < fchunks; blk += fc::WAVES) {
-            const int u = blk * 64 + lane;
-            dma16(wr, st_lds + (uint32_t)(blk * 1024), u < fchunks ? (uint32_t)u * 16u : kBufOOB);
-        }
-        if (tid < K) bias_s[tid] = a.bias ? E::to_f32(((const elem *)a.bias)[tid]) : 0.0f;
+    // loads complete in issue order: with only the row loads outstanding,
+    // this wave's share of the filter and the bias has landed
+    switch (nrow_ops) {
+    case 0: wait_vm_all(); break;
+    case 1: wait_vm_n<1>(); break;
+    case 2: wait_vm_n<2>(); break;
+    case 3: wait_vm_n<3>(); break;
+    case 4: wait_vm_n<4>(); break;
+    case 5: wait_vm_n<5>(); break;
+    case 6: wait_vm_n<6>(); break;
+    case 7: wait_vm_n<7>(); break;
+    case 8: wait_vm_n<8>(); break;
+    case 9: wait_vm_n<9>(); break;
+    case 10: wait_vm_n<10>(); break;
+    case 11: wait_vm_n<11>(); break;
+    case 12: wait_vm_n<12>(); break;
+    case 13: wait_vm_n<13>(); break;
+    case 14: wait_vm_n<14>(); break;
+    case 15: wait_vm_n<15>(); break;
+    default: wait_vm_all(); break;
     }
-    wait_vm_all();    // this wave's row and filter loads
-    __syncthreads();  // rows, filter and bias visible to every wave
+    __syncthreads();  // the filter and bias visible to every wave; the rows still on their way
 
     // ---- A operand: output channel m = 32*mb + l32, chunk 2*j + lhi of the
     // reduction (lane holds k = 8*lhi + 0..7 of step j): the 8 consecutive
@@ -142,13 +171,17 @@ __global__ __launch_bounds__(fc::NT) void fewchan_fprop_kernel(const FewArgs a)
             }
         }
     }
-    // the bias in the accumulator layout
+    // the bias in the accumulator layout: channels 32*mb + 8*g + 4*lhi + 0..3
     f32x4 bv[KB][4];
 #pragma unroll
     for (int mb = 0; mb < KB; ++mb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) bv[mb][g] = *(const f32x4 *)(bias_s + 32 * mb + 8 * g + 4 * lhi);
-    __syncthreads();  // the filter staging is free for the outputs
+        for (int g = 0; g < 4; ++g) {
+            const elem *bp = (const elem *)(bias_raw + ((uintptr_t)a.bias & 15u)) + 32 * mb + 8 * g + 4 * lhi;
+            bv[mb][g] = f32x4{E::to_f32(bp[0]), E::to_f32(bp[1]), E::to_f32(bp[2]), E::to_f32(bp[3])};
+        }
+    wait_vm_all();    // this wave's row loads
+    __syncthreads();  // the rows visible to every wave; the filter staging is free for the outputs
 
     unsigned char *ost = stage + wave * 32 * OPITCH;
     const int nblocks = (npix + 31) >> 5;
@@ -226,7 +259,7 @@ template <class E, int KB>
 static hipError_t launch_kb(int nst, const FewArgs &a, hipStream_t st)
 {
     const dim3 grid((unsigned)(a.N * a.bands)), block(fc::NT);
-    const size_t lds = (size_t)a.buf_bytes + a.stage_bytes + 64 * sizeof(float);
+    const size_t lds = (size_t)a.buf_bytes + a.stage_bytes + 1024;
     switch (nst) {
     case 4: fewchan_fprop_kernel<E, KB, 4><<<grid, block, lds, st>>>(a); break;
     case 8: fewchan_fprop_kernel<E, KB, 8><<<grid, block, lds, st>>>(a); break;

@@ -404,6 +404,23 @@ def test_fewchan_fprop(cid, prob, dtype, dist, bias, relu):
         assert torch.equal(y.view(torch.int16), yp.view(torch.int16))
 
 
+def test_fewchan_bias_at_2_byte_offset():
+    """The bias may start at any 2-byte boundary (the boundary's own rule);
+    the few-channel kernel reads it from the 16-byte boundary below."""
+    prob = problem(2, 3, 20, 32, 64, 7, 7, pad=(3, 3), stride=(2, 2))
+    x, w, b, _ = case_inputs(prob, "f16", "int", seed=4711, bias=True)
+    ref = oracle_fprop_out(prob, "f16", x, w, b, True)
+    P, Q = B.conv2d_output_size(prob)
+    for off in (1, 3, 7):
+        buf = torch.zeros(prob["K"] + 16, dtype=torch.float16, device=DEV)
+        bv = buf[off:off + prob["K"]]
+        bv.copy_(b.to(DEV))
+        y = torch.full((prob["N"], P, Q, prob["K"]), float("nan"), dtype=torch.float16, device=DEV)
+        B.conv2d_fprop(prob, "f16", gpu(x), gpu(w), bv, 1, 1.0, 1.0, 1.0, y, None)
+        torch.cuda.synchronize()
+        check(f64(y), ref, "f16", "exact", f"bias at element offset {off}")
+
+
 # ------------------------------------------------------------- the workloads
 
 def _workload_inputs(name):
