@@ -273,6 +273,78 @@ bool fewchan_layout(const Dims &d, int dtype, FewArgs *f)
     return true;
 }
 
+// Few-channel wgrad (fewchan_wgrad.hip): the window layout of each filter
+// row (delta makes the even pixels' windows 8-byte aligned; when sw*C is 2
+// mod 4 the odd pixels read a copy of the rows shifted by 4 bytes), the
+// group buffers (two output rows a group, two buffers in the kernel's LDS)
+// and the bands: about one workgroup per CU.  Returns false when the kernel
+// does not apply.
+bool fewchan_wgrad_layout(const Dims &d, int dtype, FewWgradArgs *f)
+{
+    if (d.G != 1 ||
+        !fewchan_wgrad_supported(dtype, (int)d.C, (int)d.K, (int)d.S, (int)d.sw, (int)d.dw, (int)d.W))
+        return false;
+    const long long e = elem_size(dtype);
+    if (e * d.N * d.H * d.W * d.C > kBufMaxBytes || e * d.N * d.P * d.Q * d.K > kBufMaxBytes) return false;
+    const long long SC = d.S * d.C;
+    const long long delta = (4 - (d.pw * d.C) % 4) % 4;
+    const long long lw = (delta + SC + 3) / 4 * 4;
+    long long ncb = (d.R * lw + 31) / 32;
+    if (ncb > 6) return false;
+    ncb = std::max(ncb, 2LL);
+    const long long left = (d.pw * d.C + delta + 7) / 8 * 8;
+    const long long win0 = left - d.pw * d.C - delta;  // a multiple of 4
+    const long long qstep = d.sw * d.C;
+    const bool odd_shift = qstep % 4 == 2;
+    const long long spc = (d.Q + 31) / 32, dq = 32 * spc;
+    const long long emax = win0 + (dq - 1) * qstep + lw - 1;
+    const long long pitch_e = (std::max(left + d.W * d.C, emax + 3) + 7) / 8 * 8;
+    const long long pitch = 2 * pitch_e, cpr = pitch_e / 8;
+    long long grw = 2, nxr = 0, nblk_dy = 0, nblk_x = 0, xa = 0, xb = 0, buf = 0;
+    for (; grw >= 1; --grw) {
+        nxr = (grw - 1) * d.sh + (d.R - 1) * d.dh + 1;
+        nblk_dy = grw * dq / 8;
+        nblk_x = (nxr * cpr + 63) / 64;
+        xa = nblk_x * 1024;
+        xb = odd_shift ? (nxr * pitch + 16 + 1023) / 1024 * 1024 : 0;
+        buf = nblk_dy * 1024 + xa + xb;
+        if (2 * buf <= fewchan_wgrad_lds_bytes()) break;
+    }
+    if (grw < 1) return false;
+    if (!f) return true;
+    const long long rows = std::max(1LL, std::min(d.P, (d.N * d.P + kNumCUs / 2) / kNumCUs));
+    f->N = (int)d.N; f->H = (int)d.H; f->WC = (int)(d.W * d.C); f->P = (int)d.P; f->Q = (int)d.Q;
+    f->R = (int)d.R; f->SC = (int)SC;
+    f->pad_h = (int)d.ph; f->sh = (int)d.sh; f->dh = (int)d.dh;
+    f->rows_per_wg = (int)rows;
+    f->bands = (int)((d.P + rows - 1) / rows);
+    f->grw = (int)grw;
+    f->spc = (int)spc;
+    f->dq = (int)dq;
+    f->lw = (int)lw;
+    f->delta = (int)delta;
+    f->win0 = (int)win0;
+    f->qstep = (int)qstep;
+    f->nxr = (int)nxr;
+    f->pitch = (int)pitch;
+    f->cpr = (int)cpr;
+    f->left = (int)left;
+    f->odd_shift = odd_shift ? 1 : 0;
+    f->nblk_dy = (int)nblk_dy;
+    f->nblk_x = (int)nblk_x;
+    f->xa_off = (int)(nblk_dy * 1024);
+    f->xb_off = (int)(nblk_dy * 1024 + xa);
+    f->buf_bytes = (int)buf;
+    f->xcopy_chunks = (int)(nxr * pitch / 16);
+    f->ncb = (int)ncb;
+    f->ncba = (int)((ncb + 1) / 2);
+    f->x_bytes = (uint32_t)(e * d.N * d.H * d.W * d.C);
+    f->dy_bytes = (uint32_t)(e * d.N * d.P * d.Q * d.K);
+    f->part_stride = splitk_stride(d.K * d.R * SC);
+    f->div_cpr = make_fastdiv((uint32_t)cpr);
+    return true;
+}
+
 int choose_wgrad_splits(long long tiles, long long npix, long long min_steps)
 {
     // about three workgroups per CU, at least min_steps main-loop steps per slice
@@ -388,10 +460,13 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     // other channel counts run on zero-padded copies
     const int vec = dtype == CONV2D_DTYPE_I8 ? 16 : 8;
     if (d.G == 1 && (d.C % vec || d.K % vec)) {
-        // fprop with few input channels: tile 0 is the few-channel kernel
-        // (the default), the padded path's tiles follow it
-        if (op != CONV2D_OP_FPROP || ep.axpby || !fewchan_layout(d, dtype, nullptr))
-            return plan_padded(op, prob, dtype, algo, ep, vec, pl);
+        // fprop and wgrad with few input channels: tile 0 is the
+        // few-channel kernel (the default), the padded path's tiles follow it
+        FewWgradArgs fw;
+        const bool fewk = op == CONV2D_OP_FPROP   ? !ep.axpby && fewchan_layout(d, dtype, nullptr)
+                          : op == CONV2D_OP_WGRAD ? fewchan_wgrad_layout(d, dtype, &fw)
+                                                  : false;
+        if (!fewk) return plan_padded(op, prob, dtype, algo, ep, vec, pl);
         conv2d_algo_t ia = algo ? *algo : conv2d_algo_t{0, 0};
         const bool few = ia.tile <= 1;
         ia.tile = few ? 0 : ia.tile - 1;
@@ -409,6 +484,10 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         pl->kernel = 4;
         pl->tile = 0;
         pl->num_tiles = 1 + (st ? 0 : pp.num_tiles);
+        if (op == CONV2D_OP_WGRAD) {  // one fp32 partial per band, then the split-K reduce
+            pl->split_k = (int)(d.N * fw.bands);
+            pl->ws_bytes = round_up((size_t)pl->split_k * (size_t)fw.part_stride * sizeof(float), 256);
+        }
         return CONV2D_OK;
     }
 
@@ -969,11 +1048,27 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
     void *out = reduce ? workspace : dw;
     const ReduceEpi re{ep.alpha, ep.beta, ep.axpby ? ep.c : nullptr, ep.out_f32 ? 1 : 0, nullptr, 0};
 
+    if (pl.kernel == 4) {
+        FewWgradArgs f;
+        memset(&f, 0, sizeof(f));
+        if (!fewchan_wgrad_layout(d, dtype, &f)) return CONV2D_ERR_UNSUPPORTED;
+        f.x = x; f.dy = dy; f.out = workspace;
+        if (launch_fewchan_wgrad(dtype, f, s) != hipSuccess) return CONV2D_ERR_DEVICE;
+        return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k, d.K * d.R * d.S * d.C,
+                                               f.part_stride, dw, &re, s));
+    }
+
     if (pl.padded) {
         unsigned char *wsb = (unsigned char *)workspace;
         const int e = elem_size(dtype);
         const long long Cp = pl.inner.c, Kp = pl.inner.k, nin = d.N * d.H * d.W;
         const void *xp = x, *dyp = dy;
+        conv2d_algo_t ia;
+        if (pl.tile_shift && algo) {
+            ia = *algo;
+            ia.tile -= pl.tile_shift;
+            algo = &ia;
+        }
         if (pl.off_act != kNoBuf) {
             xp = wsb + pl.off_act;
             if (repack(e, x, nin, d.C, d.C, (void *)xp, nin, Cp, Cp, s) != hipSuccess) return CONV2D_ERR_DEVICE;

@@ -293,6 +293,38 @@ int fewchan_steps(int R, int lw);  // reduction steps of the kernel built for R*
 hipError_t launch_fewchan_fprop(int dtype, const FewArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Few-channel wgrad (fewchan_wgrad.hip): groups == 1, C not a multiple of 8,
+// stride_w*C even, dil_w == 1, W*C % 8 == 0, K == 64, fp16/bf16.  Column t of
+// the window layout is window position t % lw of filter row t / lw, i.e. tap
+// s*C + c = t % lw - delta.  A workgroup owns rows_per_wg output rows of one
+// image, taken grw at a time; buffer g & 1 (buf_bytes) holds a group's dy
+// rows (dq pixel slots each, 128 bytes a pixel), its nxr input rows at xa_off
+// (pitch bytes each, image element 0 at element `left`) and, when odd_shift,
+// the same rows shifted by 4 bytes at xb_off.  Each workgroup writes the fp32
+// partial [K][R*S*C] of its band at out + blockIdx.x * part_stride.
+// ---------------------------------------------------------------------------
+struct FewWgradArgs {
+    const void *x, *dy;
+    void *out;
+    int N, H, WC, P, Q, R, SC;
+    int pad_h, sh, dh;
+    int rows_per_wg, bands, grw;
+    int spc, dq;              // steps per class and row, dy pixel slots per row (32 * spc)
+    int lw, delta, win0, qstep;
+    int nxr, pitch, cpr, left;
+    int odd_shift;            // the odd pixels' windows are read from the shifted copy
+    int nblk_dy, nblk_x;      // 1 KB loads per group
+    int xa_off, xb_off, buf_bytes, xcopy_chunks;
+    int ncb, ncba;            // column blocks, and those of the first set
+    uint32_t x_bytes, dy_bytes;
+    long long part_stride;
+    FastDiv div_cpr;
+};
+bool fewchan_wgrad_supported(int dtype, int C, int K, int S, int sw, int dw, int W);
+int fewchan_wgrad_lds_bytes();
+hipError_t launch_fewchan_wgrad(int dtype, const FewWgradArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Direct convolution for groups > 1: one thread per output element, fp32
 // (int32 for int8) accumulation in a fixed (r, s, channel) order.
 // ---------------------------------------------------------------------------

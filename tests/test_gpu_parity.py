@@ -421,6 +421,56 @@ def test_fewchan_bias_at_2_byte_offset():
         check(f64(y), ref, "f16", "exact", f"bias at element offset {off}")
 
 
+# The few-channel wgrad kernel (K = 64): window columns read with transposing
+# LDS reads; when stride_w*C is 2 mod 4 the odd pixels come from the rows'
+# copy shifted by 4 bytes.  Both alignments, one to three steps per pixel
+# class, row dilation, bands of 3 rows (groups of 2 and 1), bf16 Gaussian.
+FEW_WGRAD_CASES = [
+    ("fw_c4_s1", problem(2, 4, 15, 18, 64, 3, 3, pad=(1, 1)), "f16", "int"),
+    ("fw_c2_s2_wide", problem(2, 2, 9, 80, 64, 3, 3, pad=(1, 1), stride=(2, 2)), "f16", "int"),
+    ("fw_c3_wide_s2", problem(3, 3, 11, 136, 64, 7, 7, pad=(3, 3), stride=(2, 2)), "f16", "int"),
+    ("fw_c6_dil_bf16", problem(2, 6, 13, 20, 64, 3, 2, pad=(2, 1), dil=(2, 1)), "bf16", "gauss"),
+    ("fw_c1_s4", problem(2, 1, 17, 64, 64, 5, 5, pad=(2, 2), stride=(4, 4)), "f16", "int"),
+    ("fw_c3_bands3", problem(24, 3, 66, 32, 64, 7, 7, pad=(3, 3), stride=(2, 2)), "f16", "gauss"),
+] + [(c[0], c[1], c[2], c[3]) for c in FEW_CASES if c[1]["K"] == 64 and c[0] != "few_c4_7x7"]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,dist", FEW_WGRAD_CASES, ids=[c[0] for c in FEW_WGRAD_CASES])
+def test_fewchan_wgrad(cid, prob, dtype, dist):
+    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, dtype)
+    assert info["kernel"] == 4 and info["tile"] == 0, info
+    mode = "exact" if dist == "int" else "tol"
+    x, _, _, dy = case_inputs(prob, dtype, dist, seed=zlib.crc32(cid.encode()), bias=False)
+    ref = oracle.wgrad(prob, f64(x), f64(dy))
+    dw = run_wgrad(prob, dtype, x, dy)
+    check(f64(dw), ref, dtype, mode, f"{cid} few-channel wgrad")
+    again = run_wgrad(prob, dtype, x, dy)
+    assert torch.equal(again.view(torch.int16), dw.view(torch.int16)), f"{cid}: repeat differs"
+    # the padded path's first tile gives the same answer
+    dwp = run_wgrad(prob, dtype, x, dy, algo=dict(tile=2))
+    check(f64(dwp), ref, dtype, mode, f"{cid} padded tile")
+
+
+def test_fewchan_wgrad_epilogue():
+    """alpha/beta with C and an fp32 dw, and the bias gradient, on the
+    few-channel wgrad plan (the epilogue runs in the split-K reduce, the bias
+    gradient as its own column sums)."""
+    prob = problem(2, 3, 20, 32, 64, 7, 7, pad=(3, 3), stride=(2, 2))
+    x, _, _, dy = case_inputs(prob, "f16", "int", seed=4242, bias=False)
+    assert B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")["kernel"] == 4
+    ref = oracle.wgrad(prob, f64(x), f64(dy))
+    c = torch.randint(-3, 4, ref.shape, dtype=torch.float32)
+    dw = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=DEV)
+    db = torch.full((prob["K"],), float("nan"), dtype=torch.float32, device=DEV)
+    epi = dict(alpha=2.0, beta=-1.0, c=c.to(DEV), out_f32=1, db=db)
+    n = B.conv2d_workspace_size_ex(B.CONV2D_OP_WGRAD, prob, "f16", epi=epi)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV) if n else None
+    B.conv2d_wgrad_ex(prob, "f16", gpu(x), gpu(dy), epi, dw, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(dw), 2.0 * ref - c.numpy().astype(np.float64))
+    assert np.array_equal(f64(db), f64(dy).reshape(-1, prob["K"]).sum(axis=0))
+
+
 # ------------------------------------------------------------- the workloads
 
 def _workload_inputs(name):
