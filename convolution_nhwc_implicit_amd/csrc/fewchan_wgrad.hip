@@ -76,15 +76,6 @@ __device__ inline u32x4 join(s16x4 lo, s16x4 hi)
 // pixels of a transposing read (q, q+2, q+4, q+6 of one class) then cover
 // eight different chunk slots, i.e. all 32 banks of their 128 bytes
 __device__ inline int swz(int q) { return ((q >> 1) & 3) << 1; }
-
-template <int B, int E_, class F>
-__device__ __attribute__((always_inline)) inline void static_for(F &&f)
-{
-    if constexpr (B < E_) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E_>(f);
-    }
-}
 }  // namespace fw
 
 template <class E, int NCBW, int CB0>
@@ -182,30 +173,54 @@ __device__ __attribute__((always_inline)) inline void fewchan_wgrad_wave(const F
 #pragma unroll
         for (int i = 0; i < NCBW; ++i) acc[kb][i] = f32x16{};
 
-    // one step: 16 pixels of one class of output row gr of the group
-    auto step = [&](const unsigned char *buf, int t) __attribute__((always_inline)) {
+    // one step: 16 pixels of one class of output row gr of the group; its
+    // fragments are read one step ahead of their MFMAs
+    struct Frags {
+        s16x4 d[KB][2], x[NCBW][2];
+    };
+    auto read = [&](const unsigned char *buf, int t, Frags &f) __attribute__((always_inline)) {
         const int gr = t / nsteps_row, rem = t - gr * nsteps_row;
         const int cls = rem >= a.spc ? 1 : 0, j = rem - cls * a.spc;
         const lds_u8 *dyp = (const lds_u8 *)buf + gr * DQ * PIXB;
         const lds_u8 *xp = (const lds_u8 *)buf + (cls && a.odd_shift ? a.xb_off + 4 : a.xa_off) +
                            gr * a.sh * a.pitch + 2 * a.win0;
-        s16x4 fd[KB][2], fx[NCBW][2];
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
             const int q = 2 * (16 * j + 8 * lhi + 4 * rd + psub) + cls;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) fd[kb][rd] = tr(dyp + q * PIXB + dyc[kb]);
+            for (int kb = 0; kb < KB; ++kb) f.d[kb][rd] = tr(dyp + q * PIXB + dyc[kb]);
 #pragma unroll
-            for (int i = 0; i < NCBW; ++i) fx[i][rd] = tr(xp + 2 * q * a.qstep + xo[i]);
+            for (int i = 0; i < NCBW; ++i) f.x[i][rd] = tr(xp + 2 * q * a.qstep + xo[i]);
         }
+    };
+    auto mma = [&](const Frags &f) __attribute__((always_inline)) {
         u32x4 fa[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) fa[kb] = join(fd[kb][0], fd[kb][1]);
+        for (int kb = 0; kb < KB; ++kb) fa[kb] = join(f.d[kb][0], f.d[kb][1]);
 #pragma unroll
         for (int i = 0; i < NCBW; ++i) {
-            const u32x4 fb = join(fx[i][0], fx[i][1]);
+            const u32x4 fb = join(f.x[i][0], f.x[i][1]);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) acc[kb][i] = mfma<E>(fa[kb], fb, acc[kb][i]);
+        }
+    };
+    // this wave's steps t = phase, phase + 4, ... < nst of a group; the reads
+    // past the last step (clamped to it) are discarded
+    auto steps = [&](const unsigned char *buf, int nst) __attribute__((always_inline)) {
+        if (phase >= nst) return;
+        const int last = nst - 1;
+        Frags f0, f1;
+        int t = phase;
+        read(buf, t, f0);
+        while (true) {
+            read(buf, min(t + PHASES, last), f1);
+            mma(f0);
+            t += PHASES;
+            if (t >= nst) break;
+            read(buf, min(t + PHASES, last), f0);
+            mma(f1);
+            t += PHASES;
+            if (t >= nst) break;
         }
     };
 
@@ -231,7 +246,7 @@ __device__ __attribute__((always_inline)) inline void fewchan_wgrad_wave(const F
             __syncthreads();
         }
         const int grows = min(a.grw, nrows - g * a.grw);
-        for (int t = phase; t < grows * nsteps_row; t += PHASES) step(buf, t);
+        steps(buf, grows * nsteps_row);
         __syncthreads();  // every wave is done with buffer g & 1
         nxt = dma_group(g + 2);
     }
