@@ -46,7 +46,7 @@ COPY_BYTES = 64 << 20  # reference copy for the HBM byte counters
 # the same counters on a plain copy) lives in this summary, keyed by a hash of
 # the kernel sources it was measured on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3a_hbm_traffic.json")
-KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip"]
+KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip"]
 
 
 def kernel_source_hash():

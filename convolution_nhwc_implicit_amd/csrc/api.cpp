@@ -345,6 +345,60 @@ bool fewchan_wgrad_layout(const Dims &d, int dtype, FewWgradArgs *f)
     return true;
 }
 
+// Few-channel dgrad (fewchan_dgrad.hip): the dy offsets a 2x2 output block
+// reads (over both stride phases of each axis), the ring of dy rows, and
+// the bands of super-rows: about one workgroup per CU.  Returns false when
+// the kernel does not apply.
+static void fewchan_dgrad_offsets(long long pad, long long R, long long *lo, long long *n)
+{
+    long long mn = 1LL << 40, mx = -(1LL << 40);
+    for (long long a = 0; a < 2; ++a)
+        for (long long r = 0; r < R; ++r) {
+            const long long t = a + pad - r;
+            if (((t % 2) + 2) % 2) continue;
+            mn = std::min(mn, t / 2);
+            mx = std::max(mx, t / 2);
+        }
+    *lo = mn;
+    *n = mx - mn + 1;
+}
+bool fewchan_dgrad_layout(const Dims &d, int dtype, FewDgradArgs *f)
+{
+    if (d.G != 1 || !fewchan_dgrad_supported(dtype, (int)d.C, (int)d.K, (int)d.sh, (int)d.sw, (int)d.dh, (int)d.dw,
+                                             (int)d.W))
+        return false;
+    const long long e = elem_size(dtype);
+    if (e * d.N * d.H * d.W * d.C > kBufMaxBytes || e * d.N * d.P * d.Q * d.K > kBufMaxBytes) return false;
+    long long dp_min, ndh, dq_min, ndw;
+    fewchan_dgrad_offsets(d.ph, d.R, &dp_min, &ndh);
+    fewchan_dgrad_offsets(d.pw, d.S, &dq_min, &ndw);
+    const long long mx = fewchan_dgrad_max_offsets();
+    if (ndh < 2 || ndh > mx || ndw < 2 || ndw > mx) return false;
+    const long long HS = (d.H + 1) / 2, WS = (d.W + 1) / 2;
+    const long long nblk_r = (WS + 15) / 16;
+    const long long rsl = (16 * nblk_r + ndw - 1 + 7) / 8 * 8;  // pixel slots of a dy row in LDS
+    const long long rowb = rsl * 128;
+    const long long nslot = ndh + 3;
+    const long long ring = nslot * rowb;
+    const long long filt = (d.K * d.R * d.S * d.C * e + 1023) / 1024 * 1024;
+    const long long stage_wave = 2 * 32 * d.C * e;
+    if (ring + filt + 8 * stage_wave > fewchan_dgrad_lds_bytes()) return false;
+    if (!f) return true;
+    const long long rows = std::max(1LL, std::min(HS, (d.N * HS + kNumCUs / 2) / kNumCUs));
+    f->N = (int)d.N; f->H = (int)d.H; f->W = (int)d.W; f->C = (int)d.C; f->P = (int)d.P; f->Q = (int)d.Q;
+    f->R = (int)d.R; f->S = (int)d.S;
+    f->pad_h = (int)d.ph; f->pad_w = (int)d.pw;
+    f->HS = (int)HS; f->WS = (int)WS;
+    f->rows_per_wg = (int)rows;
+    f->bands = (int)((HS + rows - 1) / rows);
+    f->nblk_r = (int)nblk_r;
+    f->dp_min = (int)dp_min; f->ndh = (int)ndh; f->dq_min = (int)dq_min; f->ndw = (int)ndw;
+    f->rsl = (int)rsl; f->rowb = (int)rowb; f->nslot = (int)nslot;
+    f->ring_bytes = (int)ring; f->filt_bytes = (int)filt; f->stage_wave = (int)stage_wave;
+    f->dy_bytes = (uint32_t)(e * d.N * d.P * d.Q * d.K);
+    return true;
+}
+
 int choose_wgrad_splits(long long tiles, long long npix, long long min_steps)
 {
     // about three workgroups per CU, at least min_steps main-loop steps per slice
@@ -465,7 +519,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         FewWgradArgs fw;
         const bool fewk = op == CONV2D_OP_FPROP   ? !ep.axpby && fewchan_layout(d, dtype, nullptr)
                           : op == CONV2D_OP_WGRAD ? fewchan_wgrad_layout(d, dtype, &fw)
-                                                  : false;
+                                                  : !ep.axpby && fewchan_dgrad_layout(d, dtype, nullptr);
         if (!fewk) return plan_padded(op, prob, dtype, algo, ep, vec, pl);
         conv2d_algo_t ia = algo ? *algo : conv2d_algo_t{0, 0};
         const bool few = ia.tile <= 1;
@@ -921,12 +975,26 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
     const Dims &d = pl.d;
     hipStream_t s = (hipStream_t)stream;
 
+    if (pl.kernel == 4) {
+        FewDgradArgs f;
+        memset(&f, 0, sizeof(f));
+        if (!fewchan_dgrad_layout(d, dtype, &f)) return CONV2D_ERR_UNSUPPORTED;
+        f.dy = dy; f.w = w; f.dx = dx;
+        return hip_status(launch_fewchan_dgrad(dtype, f, s));
+    }
+
     if (pl.padded) {
         unsigned char *wsb = (unsigned char *)workspace;
         const int e = elem_size(dtype);
         const long long Cp = pl.inner.c, Kp = pl.inner.k, npix = d.N * d.P * d.Q, nin = d.N * d.H * d.W;
         const void *dyp = dy;
         void *dxp = dx;
+        conv2d_algo_t ia;
+        if (pl.tile_shift && algo) {
+            ia = *algo;
+            ia.tile -= pl.tile_shift;
+            algo = &ia;
+        }
         if (pl.off_out != kNoBuf) {
             dyp = wsb + pl.off_out;
             if (repack(e, dy, npix, d.K, d.K, (void *)dyp, npix, Kp, Kp, s) != hipSuccess) return CONV2D_ERR_DEVICE;

@@ -325,6 +325,30 @@ int fewchan_wgrad_lds_bytes();
 hipError_t launch_fewchan_wgrad(int dtype, const FewWgradArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Few-channel dgrad (fewchan_dgrad.hip): groups == 1, C <= 4 (not a multiple
+// of 8), stride 2, dilation 1, K == 64, W*C % 8 == 0, fp16/bf16.  Super-pixel
+// (i, j) = the 2x2 output pixels (2i + a, 2j + b); it reads dy pixels
+// (i + dp, j + dq) for dp in [dp_min, dp_min + ndh), dq likewise (ndh and
+// ndw in 2..4).  A workgroup owns rows_per_wg super-rows of one image (HS = ceil(H/2)
+// of them, WS = ceil(W/2) super-pixels each, nblk_r blocks of 16); its dy rows
+// sit in a ring of nslot rows of rsl pixel slots (rowb bytes).
+// ---------------------------------------------------------------------------
+struct FewDgradArgs {
+    const void *dy, *w;
+    void *dx;
+    int N, H, W, C, P, Q, R, S;
+    int pad_h, pad_w;
+    int HS, WS, rows_per_wg, bands, nblk_r;
+    int dp_min, ndh, dq_min, ndw;
+    int rsl, rowb, nslot, ring_bytes, filt_bytes, stage_wave;
+    uint32_t dy_bytes;
+};
+bool fewchan_dgrad_supported(int dtype, int C, int K, int sh, int sw, int dh, int dw, int W);
+int fewchan_dgrad_lds_bytes();
+int fewchan_dgrad_max_offsets();
+hipError_t launch_fewchan_dgrad(int dtype, const FewDgradArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Direct convolution for groups > 1: one thread per output element, fp32
 // (int32 for int8) accumulation in a fixed (r, s, channel) order.
 // ---------------------------------------------------------------------------

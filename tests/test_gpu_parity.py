@@ -471,6 +471,35 @@ def test_fewchan_wgrad_epilogue():
     assert np.array_equal(f64(db), f64(dy).reshape(-1, prob["K"]).sum(axis=0))
 
 
+# The few-channel dgrad kernel (C <= 4, stride 2, K = 64): 2x2 output blocks
+# as GEMM rows.  Filters that read 2, 3 and 4 dy offsets per axis, an odd H
+# (the last block row half outside), a last block of 16 super-pixels that
+# ends inside the row, bands of several row pairs, bf16 Gaussian.
+FEW_DGRAD_CASES = [
+    ("fd_c4_3x3", problem(2, 4, 18, 20, 64, 3, 3, pad=(1, 1), stride=(2, 2)), "f16", "int"),
+    ("fd_c2_5x5_oddH", problem(2, 2, 17, 24, 64, 5, 5, pad=(2, 2), stride=(2, 2)), "f16", "int"),
+    ("fd_c1_4x4_p0", problem(3, 1, 16, 32, 64, 4, 4, stride=(2, 2)), "f16", "int"),
+    ("fd_c3_wide_bf16", problem(2, 3, 12, 72, 64, 7, 7, pad=(3, 3), stride=(2, 2)), "bf16", "gauss"),
+    ("fd_c3_bands", problem(40, 3, 26, 16, 64, 7, 7, pad=(3, 3), stride=(2, 2)), "f16", "gauss"),
+] + [(c[0], c[1], c[2], c[3]) for c in FEW_CASES if c[0] in ("few_stem", "few_stem_ragged")]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,dist", FEW_DGRAD_CASES, ids=[c[0] for c in FEW_DGRAD_CASES])
+def test_fewchan_dgrad(cid, prob, dtype, dist):
+    info = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, dtype)
+    assert info["kernel"] == 4 and info["tile"] == 0 and info["workspace_bytes"] == 0, info
+    mode = "exact" if dist == "int" else "tol"
+    _, w, _, dy = case_inputs(prob, dtype, dist, seed=zlib.crc32(cid.encode()), bias=False)
+    ref = oracle.dgrad(prob, f64(dy), f64(w))
+    dx = run_dgrad(prob, dtype, dy, w, fill=float("nan"))
+    check(f64(dx), ref, dtype, mode, f"{cid} few-channel dgrad")
+    again = run_dgrad(prob, dtype, dy, w)
+    assert torch.equal(again.view(torch.int16), dx.view(torch.int16)), f"{cid}: repeat differs"
+    # the padded path's first tile gives the same answer
+    dxp = run_dgrad(prob, dtype, dy, w, algo=dict(tile=2), fill=float("nan"))
+    check(f64(dxp), ref, dtype, mode, f"{cid} padded tile")
+
+
 # ------------------------------------------------------------- the workloads
 
 def _workload_inputs(name):
