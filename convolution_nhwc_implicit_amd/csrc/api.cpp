@@ -382,7 +382,8 @@ bool fewchan_dgrad_layout(const Dims &d, int dtype, FewDgradArgs *f)
     const long long ring = nslot * rowb;
     const long long filt = (d.K * d.R * d.S * d.C * e + 1023) / 1024 * 1024;
     const long long stage_wave = 2 * 32 * d.C * e;
-    if (ring + filt + 8 * stage_wave > fewchan_dgrad_lds_bytes()) return false;
+    const long long bmat = 2 * ndh * ndw * 64 * 16;  // the B fragments
+    if (ring + filt + bmat + 8 * stage_wave > fewchan_dgrad_lds_bytes()) return false;
     if (!f) return true;
     const long long rows = std::max(1LL, std::min(HS, (d.N * HS + kNumCUs / 2) / kNumCUs));
     f->N = (int)d.N; f->H = (int)d.H; f->W = (int)d.W; f->C = (int)d.C; f->P = (int)d.P; f->Q = (int)d.Q;

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(fd::NT) void fewchan_dgrad_kernel(const FewDgradArg
     __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
     unsigned char *ring = smem;                                   // nslot dy rows of rowb bytes
     unsigned char *filt = smem + a.ring_bytes;                    // the filter as it is
-    unsigned char *stage = smem + a.ring_bytes + a.filt_bytes;    // per wave: 2 x 32 x C outputs
+    unsigned char *bmat = smem + a.ring_bytes + a.filt_bytes;     // the B fragments, 16 B each
+    unsigned char *stage = bmat + NSTEPS * 64 * 16;               // per wave: 2 x 32 x C outputs
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -91,22 +92,25 @@ __global__ __launch_bounds__(fd::NT) void fewchan_dgrad_kernel(const FewDgradArg
     __syncthreads();
     if (niter > 1) dma_rows(NDH + 1, 2);
 
-    // ---- B in VGPRs: lane holds column n = lane % 16 = (a, b, c) and K
-    // values 8*(lane/16) + 0..7 of each step; step st covers K values
-    // [32*st, 32*st + 32) = dy pixel (dp, dq) = pair st/2, channels
-    // 32*(st%2) + 0..31
+    // ---- B: lane holds column n = lane % 16 = (a, b, c) and K values
+    // 8*(lane/16) + 0..7 of each step; step st covers K values [32*st,
+    // 32*st + 32) = dy pixel (dp, dq) = pair st/2, channels 32*(st%2) +
+    // 0..31.  Every wave holds the same B, so the workgroup builds it once in
+    // LDS (fragment (st, lane) at 16*(64*st + lane)) and each wave reads its
+    // copy into VGPRs.
     const int n = lane & 15, kq = lane >> 4;
     u32x4 fb[NSTEPS];
     {
         const elem *fs = (const elem *)filt;
-        const int ca = n / (2 * a.C), cb = (n / a.C) & 1, cc = n % a.C;
         const int RSC = a.R * a.S * a.C;
-#pragma unroll
-        for (int st = 0; st < NSTEPS; ++st) {
-            const int pair = st >> 1, k0 = 32 * (st & 1) + 8 * kq;
+        for (int f = tid; f < NSTEPS * 64; f += NT) {
+            const int st = f >> 6, fl = f & 63;
+            const int fn = fl & 15, fk = fl >> 4;
+            const int ca = fn / (2 * a.C), cb = (fn / a.C) & 1, cc = fn % a.C;
+            const int pair = st >> 1, k0 = 32 * (st & 1) + 8 * fk;
             const int dpi = pair / NDW, dqi = pair % NDW;
             const int r = ca + a.pad_h - 2 * (a.dp_min + dpi), s = cb + a.pad_w - 2 * (a.dq_min + dqi);
-            const bool ok = n < 4 * a.C && (unsigned)r < (unsigned)a.R && (unsigned)s < (unsigned)a.S;
+            const bool ok = fn < 4 * a.C && (unsigned)r < (unsigned)a.R && (unsigned)s < (unsigned)a.S;
             const int base = ok ? (k0 * a.R + r) * a.S * a.C + s * a.C + cc : 0;
             uint32_t v[4];
 #pragma unroll
@@ -114,9 +118,11 @@ __global__ __launch_bounds__(fd::NT) void fewchan_dgrad_kernel(const FewDgradArg
                 const uint32_t lo = fs[base + (2 * e) * RSC], hi = fs[base + (2 * e + 1) * RSC];
                 v[e] = ok ? (lo | hi << 16) : 0u;
             }
-            fb[st] = u32x4{v[0], v[1], v[2], v[3]};
-            __builtin_amdgcn_sched_barrier(0);  // one step's reads at a time: bounded registers
+            *(u32x4 *)(bmat + 16 * f) = u32x4{v[0], v[1], v[2], v[3]};
         }
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < NSTEPS; ++st) fb[st] = *(const u32x4 *)(bmat + 16 * (64 * st + lane));
     }
     // the A read of step st: ring row rel0 + dp_index, pixel slot j0 + m +
     // dq_index, chunk 4*(st%2) + kq at its swizzled place (the swizzle of slot
