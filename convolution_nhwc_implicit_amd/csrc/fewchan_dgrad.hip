@@ -15,7 +15,8 @@
 // with B[(dp, dq, k)][(a, b, c)] = w[k][a + ph - 2dp][b + pw - 2dq][c] (zero
 // where the tap does not exist).  A rows are 16 consecutive dy pixels of one
 // dy row, 32 channels at a time: plain 128-bit LDS reads of the NHWC dy rows,
-// no transposition; B (at most 32 steps of 16x16x32) lives in VGPRs.  The
+// no transposition; B (at most 32 steps of 16x16x32) is built once per
+// workgroup in LDS from the filter and then lives in every wave's VGPRs.  The
 // phase decomposition of the pages' col2im picture is folded into B, and
 // every dx element is written once, with no atomics.
 //
