@@ -402,10 +402,17 @@ bool fewchan_dgrad_layout(const Dims &d, int dtype, FewDgradArgs *f)
 
 int choose_wgrad_splits(long long tiles, long long npix, long long min_steps)
 {
-    // about three workgroups per CU, at least min_steps main-loop steps per slice
+    // about three workgroups per CU, at least min_steps main-loop steps per
+    // slice; with few tiles per slice, from 8 slices on a multiple of 8, so
+    // that every XCD gets as many slices (the kernels then put all tiles of a
+    // slice on one XCD)
     const long long steps = (npix + kWgradPixStep - 1) / kWgradPixStep;
-    long long s = (3 * kNumCUs) / std::max(1LL, tiles);
-    s = std::min(s, std::max(1LL, steps / min_steps));
+    const long long cap = std::max(1LL, steps / min_steps);
+    long long s = std::min((3 * kNumCUs) / std::max(1LL, tiles), cap);
+    if (tiles <= kWgradXcdTiles && s >= 8) {
+        const long long r = (s + 4) / 8 * 8;
+        s = r <= cap ? r : s / 8 * 8;
+    }
     return (int)std::max(1LL, std::min(s, 4096LL));
 }
 

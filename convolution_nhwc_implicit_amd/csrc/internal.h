@@ -199,6 +199,7 @@ struct WgradArgs {
 int wgrad_num_tiles();
 TileShape wgrad_tile_shape(int tile);
 constexpr int kWgradPixStep = 64;  // pixels per main-loop step
+constexpr int kWgradXcdTiles = 8;  // up to this many tiles per pixel slice, a slice's tiles share an XCD
 hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st);
 // Epilogue of the split-K sum t: out = alpha * t + beta * c (c laid out like
 // out, NULL when beta == 0), stored as fp32 when out_f32, else rounded once.

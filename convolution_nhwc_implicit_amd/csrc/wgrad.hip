@@ -34,6 +34,31 @@ __device__ inline s16x4 tr16(const unsigned char *p)
 {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
+// Workgroup -> (row tile gx = group * mtiles_g + row tile, column tile nt,
+// pixel slice z) of the generic wgrad kernels.  With few tiles per slice
+// (T = gxn * gyn <= kWgradXcdTiles) the tiles of a slice, which read the
+// same dy and x pixels, share an XCD's L2: the grid is one-dimensional,
+// workgroups are dealt to the 8 XCDs in turn, and workgroup 8q + u takes
+// tile q % T of slice u + 8 * (q / T) (slices past the last -- the grid is
+// rounded up to 8 of them -- have no work).  Otherwise the grid is
+// (gxn, gyn, slices).
+struct WgradTileId {
+    int gx, nt, z;
+};
+__device__ inline WgradTileId wgrad_tile_id(int gxn, int gyn)
+{
+    const int T = gxn * gyn;
+    if (T > kWgradXcdTiles) return WgradTileId{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+    const int L = blockIdx.x, u = L & 7, q = L >> 3, qt = q / T;
+    const int t = q - qt * T, nt = t / gxn;
+    return WgradTileId{t - nt * gxn, nt, u + 8 * qt};
+}
+inline dim3 wgrad_grid(int gxn, int gyn, int splits)
+{
+    if (gxn * gyn > kWgradXcdTiles) return dim3((unsigned)gxn, (unsigned)gyn, (unsigned)splits);
+    return dim3((unsigned)(gxn * gyn * ((splits + 7) / 8 * 8)));
+}
+
 template <class E>
 struct Mfma32x16 {
     __device__ static inline f32x16 run(u32x4 a, u32x4 b, f32x16 c)
@@ -60,8 +85,10 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE * STAGE];
 
-    const int nt = blockIdx.y, z = blockIdx.z;
-    const int gi = blockIdx.x / a.mtiles_g, mt = blockIdx.x - gi * a.mtiles_g;  // group, row tile in it
+    const WgradTileId id = wgrad_tile_id(a.K / a.Kg * a.mtiles_g, (a.ncols + BN - 1) / BN);
+    if (id.z >= a.splits) return;  // the whole workgroup
+    const int nt = id.nt, z = id.z;
+    const int gi = id.gx / a.mtiles_g, mt = id.gx - gi * a.mtiles_g;  // group, row tile in it
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -239,8 +266,10 @@ __global__ __launch_bounds__(256) void wgrad_interleave_kernel(const WgradArgs a
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
 
-    const int nt = blockIdx.y, z = blockIdx.z;
-    const int gi = blockIdx.x / a.mtiles_g, mt = blockIdx.x - gi * a.mtiles_g;  // group, row tile in it
+    const WgradTileId id = wgrad_tile_id(a.K / a.Kg * a.mtiles_g, (a.ncols + BN - 1) / BN);
+    if (id.z >= a.splits) return;  // the whole workgroup
+    const int nt = id.nt, z = id.z;
+    const int gi = id.gx / a.mtiles_g, mt = id.gx - gi * a.mtiles_g;  // group, row tile in it
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int pp = tid % PAIRS, ch = tid / PAIRS;
@@ -367,7 +396,7 @@ hipError_t launch_wgrad(int dtype, int tile, const WgradArgs &a, hipStream_t st)
     if (tile < 0 || tile >= wgrad_num_tiles()) return hipErrorInvalidValue;
     const TileShape ts = wgrad_tile_shape(tile);
     if (a.mtiles_g != (a.Kg + ts.bm - 1) / ts.bm || a.K % a.Kg) return hipErrorInvalidValue;
-    dim3 grid((unsigned)(a.K / a.Kg * a.mtiles_g), (unsigned)((a.ncols + ts.bn - 1) / ts.bn), (unsigned)a.splits);
+    const dim3 grid(wgrad_grid(a.K / a.Kg * a.mtiles_g, (a.ncols + ts.bn - 1) / ts.bn, a.splits));
     switch (dtype) {
     case CONV2D_DTYPE_F16:
         if (tile == 0)
