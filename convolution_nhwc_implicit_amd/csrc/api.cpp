@@ -110,6 +110,26 @@ AxisPhase axis_phase(int ph, int extent_full, int stride, int pad, int dil, int 
     return a;
 }
 
+// dgrad on the implicit GEMM reads the filter as it is (transposing LDS
+// reads of B) unless a stride phase has GEMM-K rows longer than this: there
+// the reads (two 8-byte reads per fragment instead of one 16-byte read) cost
+// more than re-laying the filter out first (measured: 16x57x57x96 -> 192,
+// 5x5 s2 d2, 4800-long rows, 57.7 against 50.5 us; 1x1 64x56x56x256 -> 64,
+// 256-long rows, 26.8 against 29.0 us).
+constexpr int kDgradTransMaxK = 2048;
+bool dgrad_relayout(const Dims &d)
+{
+    long long kmax = 0;
+    for (int py = 0; py < d.sh; ++py)
+        for (int px = 0; px < d.sw; ++px) {
+            AxisPhase ay = axis_phase(py, (int)d.H, (int)d.sh, (int)d.ph, (int)d.dh, (int)d.R);
+            AxisPhase ax = axis_phase(px, (int)d.W, (int)d.sw, (int)d.pw, (int)d.dw, (int)d.S);
+            if (ay.extent == 0 || ax.extent == 0) continue;
+            kmax = std::max(kmax, (long long)ay.ntap * ax.ntap * d.Kg);
+        }
+    return kmax > kDgradTransMaxK;
+}
+
 constexpr size_t kNoBuf = ~(size_t)0;
 
 // Output epilogue of a pass (conv2d_epilogue_t, checked): out = alpha * result
@@ -661,13 +681,14 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     pl->tile = (algo && algo->tile) ? algo->tile - 1
                : band             ? kBandTile
                                   : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.Cg);
-    // the band kernel reads the filter as it is; Winograd takes its transform,
-    // the implicit GEMM a re-laid-out copy
+    // the band kernel reads the filter as it is, and so does the implicit
+    // GEMM unless its GEMM-K rows are long (then a re-laid-out copy);
+    // Winograd takes its transform
     if (pl->tile == kWinoTile) {
         pl->kernel = 3;
         pl->ws_bytes = round_up((size_t)16 * d.C * d.K * elem_size(dtype), 256);
-    } else {
-        pl->ws_bytes = pl->tile == kBandTile ? 0 : round_up((size_t)d.R * d.S * d.C * d.Kg * elem_size(dtype), 256);
+    } else if (pl->tile != kBandTile && dgrad_relayout(d)) {
+        pl->ws_bytes = round_up((size_t)d.R * d.S * d.C * d.Kg * elem_size(dtype), 256);
     }
     return CONV2D_OK;
 }
@@ -1054,6 +1075,9 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
                         (int)d.C, (int)(d.dh * (d.R - 1) - d.ph), (int)(d.dw * (d.S - 1) - d.pw), s);
 
     // One GEMM per stride phase (h mod sh, w mod sw), one launch for all.
+    // B is the filter as it lies in memory, read transposed in LDS, or for
+    // long GEMM-K rows a copy re-laid out per phase by a first kernel.
+    const bool relayout = dgrad_relayout(d);
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
     pa.w = w; pa.wt = workspace;
@@ -1061,8 +1085,15 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
     pa.Kg = (int)d.Kg; pa.Cg = (int)d.Cg;
     IgemmArgs a;
     memset(&a, 0, sizeof(a));
-    a.src = dy; a.bmat = workspace; a.bias = nullptr; a.dst = dx;
-    a.b_elems = d.R * d.S * d.C * d.Kg;
+    a.src = dy; a.bias = nullptr; a.dst = dx;
+    if (relayout) {
+        a.bmat = workspace;
+        a.b_elems = d.R * d.S * d.C * d.Kg;
+    } else {
+        a.bmat = w;
+        a.b_elems = d.K * d.R * d.S * d.Cg;
+        a.b_trans = 1; a.filt_r = (int)d.R; a.filt_s = (int)d.S;
+    }
     a.nimg = (int)d.N; a.hs = (int)d.P; a.ws = (int)d.Q; a.cs = (int)d.K;
     a.ngemm = (int)d.C;
     a.cg = (int)d.Kg; a.kg = (int)d.Cg;  // one GEMM per group: Kg dy channels in, Cg dx channels out
@@ -1083,6 +1114,7 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
             ph.ntr = ay.ntap; ph.nts = ax.ntap;
             ph.kgemm = (int)(ay.ntap * ax.ntap * d.Kg);
             ph.m_total = (uint32_t)(d.N * ay.extent * ax.extent);
+            ph.r0 = ay.r0; ph.rstep = ay.step; ph.s0 = ax.r0; ph.sstep = ax.step;
             ph.b_off = off;
             fill_phase_common(ph, pl.tile);
             max_tiles = std::max(max_tiles, ph.tiles_m);
@@ -1098,8 +1130,7 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
     a.nphases = nph;
     pa.nphases = nph;
     if (nph == 0) return CONV2D_OK;
-    hipError_t e = launch_dgrad_prep(dtype, pa, s);
-    if (e != hipSuccess) return CONV2D_ERR_DEVICE;
+    if (relayout && launch_dgrad_prep(dtype, pa, s) != hipSuccess) return CONV2D_ERR_DEVICE;
     TileShape ts = igemm_tile_shape(pl.tile);
     a.ntiles_g = (int)((d.Cg + ts.bn - 1) / ts.bn);
     return hip_status(launch_igemm(dtype, pl.tile, a, max_tiles, (int)d.G * a.ntiles_g, s));

@@ -40,7 +40,19 @@ __device__ inline void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <class E, class TL>
+// TB (dgrad, 16-bit types): the B tile is staged as BK rows (tap, dy
+// channel) of BN dx channels straight from w[K][R][S][C], 16-byte chunks of
+// row k swizzled by btswz(k), and read with ds_read_b64_tr_b16.
+template <int BROWCH>
+__device__ inline int btswz(int row)
+{
+    const int b3 = ((row >> 3) & 1) << 1;
+    if constexpr (BROWCH == 4) return b3;
+    if constexpr (BROWCH == 8) return (((row >> 1) & 1) << 2) | b3;
+    return ((row & 3) << 2) | b3;
+}
+
+template <class E, class TL, bool TB>
 __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
 {
     constexpr int NT = 256;
@@ -61,6 +73,10 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     static_assert(TL::WM * TL::WN == 4, "four waves");
     static_assert(CH == 4 || CH == 8, "64- or 128-byte tile rows");
     static_assert((BM / RB) % 4 == 0 && (BN / RB) % 4 == 0 && A_BLK > 0 && B_BLK > 0, "whole blocks per wave");
+    constexpr int BROWCH = BN / 8;      // TB: 16-byte chunks per B row
+    constexpr int RPB = 64 / BROWCH;    // TB: B rows per 1 KB block
+    static_assert(!TB || (EPC == 8 && (BROWCH == 4 || BROWCH == 8 || BROWCH == 16) && 4 * B_BLK * RPB == BK),
+                  "transposed B: 16-bit types, 32- to 128-wide N tiles");
     using elem = typename E::elem;
     using acc_t = typename E::acc;
     constexpr int OSZ = (int)sizeof(elem);
@@ -120,10 +136,36 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     }
     // per lane: B rows (element offset of the row, or -1 past ngemm)
     long long b_row[B_BLK];
+    // TB: per block t, the lane's B row is GEMM-K index (tap (bjr, bjs), dy
+    // channel bk) and its chunk column bcol (dx channel within the group),
+    // or -1 past the tile's valid channels
+    int bk[B_BLK], bjs[B_BLK], bjr[B_BLK], bcol[B_BLK];
 #pragma unroll
     for (int t = 0; t < B_BLK; ++t) {
-        const int nl = RB * (wave + 4 * t) + brow;
-        b_row[t] = nl < nvalid ? ph.b_off + (long long)(ncol0 + nl) * ph.kgemm : -1;
+        if constexpr (!TB) {
+            const int nl = RB * (wave + 4 * t) + brow;
+            b_row[t] = nl < nvalid ? ph.b_off + (long long)(ncol0 + nl) * ph.kgemm : -1;
+        } else {
+            const int row = RPB * (wave + 4 * t) + lane / BROWCH;  // B row in the stage
+            const int cs = (lane % BROWCH) ^ btswz<BROWCH>(row);   // source chunk of the stored one
+            bcol[t] = 8 * cs < nvalid ? ntl * BN + 8 * cs : -1;
+            bk[t] = row;
+            bjs[t] = 0;
+            bjr[t] = 0;
+        }
+    }
+    auto normalize_b = [&](int t) {
+        while (bk[t] >= a.cg) {
+            bk[t] -= a.cg;
+            if (++bjs[t] == ph.nts) {
+                bjs[t] = 0;
+                ++bjr[t];
+            }
+        }
+    };
+    if constexpr (TB) {
+#pragma unroll
+        for (int t = 0; t < B_BLK; ++t) normalize_b(t);
     }
 
     // ---- GEMM-K position of this lane's chunk: (tap tr, tap ts, channel c)
@@ -155,9 +197,22 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
         }
 #pragma unroll
         for (int t = 0; t < B_BLK; ++t) {
-            const uint32_t voff =
-                (kval && b_row[t] >= 0) ? (uint32_t)((b_row[t] + kk) * (long long)sizeof(elem)) : kBufOOBFar;
-            dma16(b_rs, base + BM * BKB + (wave + 4 * t) * 1024, voff);
+            if constexpr (!TB) {
+                const uint32_t voff =
+                    (kval && b_row[t] >= 0) ? (uint32_t)((b_row[t] + kk) * (long long)sizeof(elem)) : kBufOOBFar;
+                dma16(b_rs, base + BM * BKB + (wave + 4 * t) * 1024, voff);
+            } else {
+                // w[gi*Kg + k][r][s][col]
+                const int r = ph.r0 + bjr[t] * ph.rstep, s = ph.s0 + bjs[t] * ph.sstep;
+                const bool ok = bjr[t] < ph.ntr && bcol[t] >= 0;
+                const uint32_t voff =
+                    ok ? (uint32_t)((((gi * a.cg + bk[t]) * a.filt_r + r) * a.filt_s + s) * a.kg + bcol[t]) *
+                             (uint32_t)sizeof(elem)
+                       : kBufOOBFar;
+                dma16(b_rs, base + BM * BKB + (wave + 4 * t) * 1024, voff);
+                bk[t] += BK;
+                normalize_b(t);
+            }
         }
         c += BK;
         kk += BK;
@@ -178,6 +233,21 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
     int fofs[KSUB];
 #pragma unroll
     for (int ks = 0; ks < KSUB; ++ks) fofs[ks] = frag_row * BKB + (((4 * ks + (lane >> 4)) ^ fswz) << 4);
+    // TB: ds_read_b64_tr_b16 -- in each group of 16 lanes, lane L points at
+    // row L/4, columns 4*(L%4)..+3 of a 4 x 16 tile and receives column L of
+    // the 4 rows.  Lane group q reads B rows 32*ks + 8q + 4t + L/4 (t = 0, 1:
+    // the fragment's 8 k values), columns n0 + 4*(L%4) of block j; the row's
+    // swizzle depends on the lane only (rows move by multiples of 4 and 32).
+    int bofs[FN];
+    if constexpr (TB) {
+        const int L = lane & 15, rl = 8 * (lane >> 4) + (L >> 2);
+        const int sw = btswz<BROWCH>(rl);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int chunk = (wn * WTN + j * 16) / 8 + ((L & 3) >> 1);
+            bofs[j] = BM * BKB + rl * BN * 2 + ((chunk ^ sw) << 4) + (L & 1) * 8;
+        }
+    }
 
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
@@ -198,8 +268,21 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a)
 #pragma unroll
             for (int i = 0; i < FM; ++i) fa[i] = *(const u32x4 *)(base + (wm * WTM + i * 16) * BKB + fofs[ks]);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[j] = *(const u32x4 *)(base + (BM + wn * WTN + j * 16) * BKB + fofs[ks]);
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (!TB) {
+                    fb[j] = *(const u32x4 *)(base + (BM + wn * WTN + j * 16) * BKB + fofs[ks]);
+                } else {
+                    typedef short s16x4 __attribute__((ext_vector_type(4)));
+                    uint2 h[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        h[t] = __builtin_bit_cast(
+                            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) s16x4 *)(base + bofs[j] +
+                                                                                    (32 * ks + 4 * t) * BN * 2)));
+                    fb[j] = u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
+                }
+            }
             // filter fragment as the MFMA's A operand, pixels as B: each lane
             // of a result block then holds 4 consecutive channels of a pixel
 #pragma unroll
@@ -313,16 +396,16 @@ TileShape igemm_tile_shape(int tile)
     }
 }
 
-template <class E>
+template <class E, bool TB>
 static hipError_t launch_e(int tile, const IgemmArgs &a, int gm, int gn, hipStream_t st)
 {
     dim3 grid((unsigned)gm, (unsigned)gn, (unsigned)a.nphases);
     switch (tile) {
-    case 0: igemm_kernel<E, T0><<<grid, 256, 0, st>>>(a); break;
-    case 1: igemm_kernel<E, T1><<<grid, 256, 0, st>>>(a); break;
-    case 2: igemm_kernel<E, T2><<<grid, 256, 0, st>>>(a); break;
-    case 3: igemm_kernel<E, T3><<<grid, 256, 0, st>>>(a); break;
-    case 4: igemm_kernel<E, T4><<<grid, 256, 0, st>>>(a); break;
+    case 0: igemm_kernel<E, T0, TB><<<grid, 256, 0, st>>>(a); break;
+    case 1: igemm_kernel<E, T1, TB><<<grid, 256, 0, st>>>(a); break;
+    case 2: igemm_kernel<E, T2, TB><<<grid, 256, 0, st>>>(a); break;
+    case 3: igemm_kernel<E, T3, TB><<<grid, 256, 0, st>>>(a); break;
+    case 4: igemm_kernel<E, T4, TB><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -331,9 +414,15 @@ static hipError_t launch_e(int tile, const IgemmArgs &a, int gm, int gn, hipStre
 hipError_t launch_igemm(int dtype, int tile, const IgemmArgs &a, int grid_m, int grid_n, hipStream_t st)
 {
     switch (dtype) {
-    case CONV2D_DTYPE_F16: return launch_e<EF16>(tile, a, grid_m, grid_n, st);
-    case CONV2D_DTYPE_BF16: return launch_e<EBF16>(tile, a, grid_m, grid_n, st);
-    case CONV2D_DTYPE_I8: return launch_e<EI8>(tile, a, grid_m, grid_n, st);
+    case CONV2D_DTYPE_F16:
+        return a.b_trans ? launch_e<EF16, true>(tile, a, grid_m, grid_n, st)
+                         : launch_e<EF16, false>(tile, a, grid_m, grid_n, st);
+    case CONV2D_DTYPE_BF16:
+        return a.b_trans ? launch_e<EBF16, true>(tile, a, grid_m, grid_n, st)
+                         : launch_e<EBF16, false>(tile, a, grid_m, grid_n, st);
+    case CONV2D_DTYPE_I8:
+        if (a.b_trans) return hipErrorInvalidValue;
+        return launch_e<EI8, false>(tile, a, grid_m, grid_n, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -71,6 +71,9 @@ struct Phase {
     uint32_t m_total; // nimg * mi * mj
     long long b_off;  // element offset of this phase's B matrix
     FastDiv div_mj, div_mimj;
+    // dgrad with the filter read as it is (IgemmArgs.b_trans): filter tap
+    // (r0 + jr*rstep, s0 + js*sstep) for tap index (jr, js)
+    int r0, rstep, s0, sstep;
 };
 
 struct IgemmArgs {
@@ -95,6 +98,10 @@ struct IgemmArgs {
     float alpha, beta;
     const void *cmat;
     int nphases;
+    // dgrad: B is the filter w[K][R][S][C] itself (no re-layout pass): its
+    // GEMM-K rows (tap, dy channel) are staged as they lie in w, dx channels
+    // along the row, and the fragments are read with transposing LDS reads
+    int b_trans, filt_r, filt_s;
     Phase ph[kMaxPhases];
 };
 
@@ -150,8 +157,9 @@ struct WinoArgs {
 bool wino_supported(int dtype, int R, int S, int cin, int dil);
 hipError_t launch_wino_fprop(int dtype, const WinoArgs &a, int grid_x, hipStream_t st);
 
+
 // Re-lays the filter w[K][R][S][C/G] out as one [C][taps*K/G] matrix per
-// dgrad stride phase (taps of the phase in (jr, js) order, the dx channel's
+// dgrad stride phase, for the implicit GEMM on long GEMM-K rows (taps of the phase in (jr, js) order, the dx channel's
 // group's dy channels innermost).
 struct PrepPhase {
     int r0, rstep, ntr;

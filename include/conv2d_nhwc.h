@@ -144,8 +144,10 @@ int conv2d_output_size(const conv2d_problem_t *prob, int *P, int *Q);
 
 /*
  * Workspace bytes the caller must pass to the given op (0 is a valid answer).
- * A pure function of its arguments.  dgrad uses the workspace for the
- * re-laid-out filter of each stride phase; wgrad for fp32 split-K partials.
+ * A pure function of its arguments.  wgrad uses the workspace for fp32
+ * split-K partials; dgrad needs none except on the Winograd tile (its
+ * transformed filter); the channel-padded path (C or K off the 16-byte
+ * grid) for its zero-padded copies.
  * The caller-allocated scratch with a size query is the tensorcore Conv2D
  * page's "Scratch sizing" convention, minus the im2col buffer.
  */

@@ -189,6 +189,24 @@ def test_every_fprop_and_dgrad_tile_matches_oracle():
         check(f64(run_dgrad(prob, "f16", dy, w, algo=algo)), ref_dx, "f16", "exact", f"dgrad tile {t}")
 
 
+@pytest.mark.parametrize("cid,prob,dtype,relayout", [
+    # GEMM-K rows of 3200 per stride phase: the filter is re-laid out first
+    ("long_k", problem(2, 16, 12, 13, 128, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2)), "f16", True),
+    # rows of 1152: B read straight from the filter with transposing LDS reads
+    ("short_k_grouped", problem(2, 48, 11, 9, 96, 3, 3, pad=(1, 1), stride=(2, 2), groups=2), "bf16", False),
+], ids=["long_k", "short_k_grouped"])
+def test_dgrad_filter_paths_every_tile(cid, prob, dtype, relayout):
+    """The implicit-GEMM dgrad with the filter re-laid out (a workspace) and
+    read as it is (none), every tile, integer data: exact."""
+    _, w, _, dy = case_inputs(prob, dtype, "int", seed=zlib.crc32(cid.encode()), bias=False)
+    ref = oracle.dgrad(prob, f64(dy), f64(w))
+    info = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, dtype)
+    assert info["kernel"] == 1 and (info["workspace_bytes"] > 0) == relayout, info
+    for t in range(1, info["num_tiles"] + 1):
+        dx = run_dgrad(prob, dtype, dy, w, algo=dict(tile=t), fill=float("nan"))
+        check(f64(dx), ref, dtype, "exact", f"{cid} dgrad tile {t}")
+
+
 def test_every_tile_on_band_eligible_problem():
     prob = problem(3, 64, 14, 13, 64, 3, 3, pad=(1, 1))
     x, w, b, dy = case_inputs(prob, "f16", "int", seed=48)
@@ -300,15 +318,16 @@ def test_nonzero_storage_offsets():
 
 
 def test_error_leaves_output_untouched():
+    # wgrad split four ways needs room for its fp32 partials
     prob = problem(2, 16, 8, 8, 16, 3, 3, pad=(1, 1))
     x, w, b, dy = case_inputs(prob, "f16", "int", seed=47)
-    dx = torch.full((2, 8, 8, 16), 7.0, dtype=torch.float16, device="cuda")
+    dw = torch.full((16, 3, 3, 16), 7.0, dtype=torch.float16, device="cuda")
     small = torch.empty(8, dtype=torch.uint8, device="cuda")
     with pytest.raises(B.Conv2dError) as e:
-        B.conv2d_dgrad(prob, "f16", dy.cuda(), w.cuda(), dx, small)
+        B.conv2d_wgrad(prob, "f16", x.cuda(), dy.cuda(), dw, small, algo=dict(split_k=4))
     assert e.value.status == B.CONV2D_ERR_WORKSPACE_TOO_SMALL
     torch.cuda.synchronize()
-    assert torch.all(dx == 7.0)
+    assert torch.all(dw == 7.0)
 
 
 # ------------------------------------------- the LDS-tiled direct kernels
