@@ -46,7 +46,7 @@ COPY_BYTES = 64 << 20  # reference copy for the HBM byte counters
 # the same counters on a plain copy) lives in this summary, keyed by a hash of
 # the kernel sources it was measured on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3a_hbm_traffic.json")
-KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip"]
+KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip", "pointwise.hip"]
 
 
 def kernel_source_hash():
@@ -315,10 +315,14 @@ def main():
     }
     plans = {n: B.conv2d_plan_info(op, prob, dt) for op, n in enumerate(("fprop", "dgrad", "wgrad"))}
     direct = plans["fprop"]["kernel"] == 2  # groups > 1
+    def main_kernel(pl):
+        return ("direct" if direct else "pointwise" if pl["kernel"] == 5 else "few_channel" if pl["kernel"] == 4
+                else "band" if pl["tile"] == BAND_TILE else "implicit_gemm")
+
     kernels = {
-        "fprop": ["direct" if direct else "band" if plans["fprop"]["tile"] == BAND_TILE else "implicit_gemm"],
-        "dgrad": (["direct"] if direct else ["band"] if plans["dgrad"]["tile"] == BAND_TILE
-                  else ["filter_relayout", "implicit_gemm"]),
+        "fprop": [main_kernel(plans["fprop"])],
+        "dgrad": ((["filter_relayout"] if plans["dgrad"]["workspace_bytes"] > 0 and plans["dgrad"]["kernel"] == 1
+                   else []) + [main_kernel(plans["dgrad"])]),
         "wgrad": (["direct" if direct else "wgrad_band" if plans["wgrad"]["tile"] == WGRAD_BAND_TILE else "wgrad_gemm"]
                   + (["splitk_reduce"] if plans["wgrad"]["split_k"] > 1 else [])),
     }

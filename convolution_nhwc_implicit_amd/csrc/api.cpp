@@ -117,6 +117,18 @@ AxisPhase axis_phase(int ph, int extent_full, int stride, int pad, int dil, int 
 // 5x5 s2 d2, 4800-long rows, 57.7 against 50.5 us; 1x1 64x56x56x256 -> 64,
 // 256-long rows, 26.8 against 29.0 us).
 constexpr int kDgradTransMaxK = 2048;
+
+// 1x1 stride-1 problems without padding (fprop and dgrad, 16-bit types, no
+// linear combination) whose GEMM-K and output channel counts the pointwise
+// kernel takes.
+bool pointwise_eligible(const Dims &d, int dtype, int op, bool axpby)
+{
+    if (axpby || d.G != 1 || d.R != 1 || d.S != 1 || d.sh != 1 || d.sw != 1 || d.ph != 0 || d.pw != 0) return false;
+    const long long gk = op == CONV2D_OP_FPROP ? d.C : d.K, nout = op == CONV2D_OP_FPROP ? d.K : d.C;
+    const long long npix = d.N * d.H * d.W;
+    if (npix * gk * 2 > kBufMaxBytes || gk * nout * 2 > kBufMaxBytes) return false;
+    return pointwise_supported(dtype, (int)gk, (int)nout);
+}
 bool dgrad_relayout(const Dims &d)
 {
     long long kmax = 0;
@@ -190,6 +202,7 @@ bool band_eligible(const Dims &d, int dtype, long long cin, long long src_h, lon
 }
 
 constexpr int kBandTile = 5;  // tile index of the band kernel (algo tile 6)
+constexpr int kPwTile = 5;    // 1x1 problems (never band-eligible): the pointwise kernel in that place
 constexpr int kWinoTile = 6;  // fprop: Winograd F(2x2,3x3) (algo tile 7), only when asked for
 
 // Winograd F(2x2, 3x3): a band-eligible problem (stride 1, 3x3, dilation 1,
@@ -666,21 +679,29 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     const bool band = !ep.axpby && (op == CONV2D_OP_FPROP ? band_eligible(d, dtype, d.C, d.H, d.W, d.K, d.P, d.Q)
                                                           : band_eligible(d, dtype, d.K, d.P, d.Q, d.C, d.H, d.W));
     const bool wino = band && wino_eligible(d, dtype, op);
-    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0) + n_direct;
+    const bool pw = pointwise_eligible(d, dtype, op, ep.axpby);  // 1x1: never with band
+    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0) + (pw ? 1 : 0) + n_direct;
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
         pl->tile = (algo && algo->tile) ? algo->tile - 1
+                   : pw               ? kPwTile
                    : band             ? kBandTile
                                       : choose_igemm_tile(d.N * d.P * d.Q, d.Kg);
         if (pl->tile == kWinoTile) pl->kernel = 3;
+        if (pw && pl->tile == kPwTile) pl->kernel = 5;
         return CONV2D_OK;
     }
     // dgrad
     if (d.sh * d.sw > kMaxPhases) return CONV2D_ERR_UNSUPPORTED;
     pl->phases = (int)(d.sh * d.sw);
     pl->tile = (algo && algo->tile) ? algo->tile - 1
+               : pw               ? kPwTile
                : band             ? kBandTile
                                   : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.Cg);
+    if (pw && pl->tile == kPwTile) {
+        pl->kernel = 5;
+        return CONV2D_OK;
+    }
     // the band kernel reads the filter as it is, and so does the implicit
     // GEMM unless its GEMM-K rows are long (then a re-laid-out copy);
     // Winograd takes its transform
@@ -896,6 +917,15 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         f.x = x; f.w = w; f.bias = bias; f.y = y; f.relu = relu;
         return hip_status(launch_fewchan_fprop(dtype, f, s));
     }
+    if (pl.kernel == 5) {
+        PwArgs p;
+        memset(&p, 0, sizeof(p));
+        p.src = x; p.w = w; p.bias = bias; p.dst = y;
+        p.npix = (int)(d.N * d.H * d.W); p.gk = (int)d.C; p.nout = (int)d.K;
+        p.src_bytes = (long long)p.npix * d.C * 2; p.w_bytes = d.K * d.C * 2;
+        p.relu = relu;
+        return hip_status(launch_pointwise(dtype, p, s));
+    }
 
     if (pl.padded) {
         unsigned char *wsb = (unsigned char *)workspace;
@@ -1010,6 +1040,15 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
         if (!fewchan_dgrad_layout(d, dtype, &f)) return CONV2D_ERR_UNSUPPORTED;
         f.dy = dy; f.w = w; f.dx = dx;
         return hip_status(launch_fewchan_dgrad(dtype, f, s));
+    }
+    if (pl.kernel == 5) {
+        PwArgs p;
+        memset(&p, 0, sizeof(p));
+        p.src = dy; p.w = w; p.bias = nullptr; p.dst = dx;
+        p.npix = (int)(d.N * d.H * d.W); p.gk = (int)d.K; p.nout = (int)d.C;
+        p.src_bytes = (long long)p.npix * d.K * 2; p.w_bytes = d.K * d.C * 2;
+        p.trans = 1;
+        return hip_status(launch_pointwise(dtype, p, s));
     }
 
     if (pl.padded) {

@@ -158,6 +158,24 @@ bool wino_supported(int dtype, int R, int S, int cin, int dil);
 hipError_t launch_wino_fprop(int dtype, const WinoArgs &a, int grid_x, hipStream_t st);
 
 
+// 1x1 stride-1 convolution without padding as a streaming GEMM over the
+// pixels (fprop; dgrad with the filter read transposed): src [npix][gk] ->
+// dst [npix][nout].  fprop: w [nout][gk], bias [nout] or NULL; dgrad (trans):
+// w [gk][nout], no bias.
+struct PwArgs {
+    const void *src;
+    const void *w;
+    const void *bias;
+    void *dst;
+    long long src_bytes, w_bytes;  // both under 2^31 (32-bit buffer offsets)
+    int npix, gk, nout;
+    int trans, relu;
+};
+bool pointwise_supported(int dtype, int gk, int nout);
+int pointwise_nwg(int gk, int nout);  // output channels per workgroup, 0 if none fits
+int pointwise_pixels_per_wg(int gk);
+hipError_t launch_pointwise(int dtype, const PwArgs &a, hipStream_t st);
+
 // Re-lays the filter w[K][R][S][C/G] out as one [C][taps*K/G] matrix per
 // dgrad stride phase, for the implicit GEMM on long GEMM-K rows (taps of the phase in (jr, js) order, the dx channel's
 // group's dy channels innermost).

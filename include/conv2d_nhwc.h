@@ -104,6 +104,12 @@ typedef struct conv2d_problem {
  *            applies) the LDS-tiled or depthwise one; other grouped problems
  *            run one implicit GEMM per group on the implicit-GEMM tiles, and
  *            offer the same direct kernels as the tiles after those.
+ *            An ungrouped 1x1 problem with stride 1 and no padding (16-bit
+ *            types, no linear-combination epilogue; the summed channel count,
+ *            C for fprop and K for dgrad, 64, 128 or 256 and the other a
+ *            multiple of 64) has the pointwise kernel as tile 6, the
+ *            library's choice: a GEMM over pixels whose filter slice stays in
+ *            registers.
  *            A stride-1, dilation-1 3x3 fp16 problem (no
  *            linear-combination epilogue) also offers, as the last tile of
  *            fprop when C = 64 and K % 16 == 0, and of dgrad when K = 64,
@@ -125,7 +131,9 @@ typedef struct conv2d_algo {
 
 /* What the library will launch for a problem (diagnostics and tests). */
 typedef struct conv2d_plan_info {
-    int kernel;        /* 1 = implicit GEMM, 2 = direct (groups > 1), 3 = Winograd F(2x2,3x3) */
+    int kernel;        /* 1 = implicit GEMM (or band kernel), 2 = direct (groups > 1),
+                          3 = Winograd F(2x2,3x3), 4 = few-channel kernels (C or K
+                          off the 16-byte grid), 5 = pointwise (1x1, stride 1) */
     int tile;          /* index of the tile configuration used (0-based) */
     int num_tiles;     /* number of tile configurations available for this op/dtype */
     int split_k;       /* reduction slices (wgrad), 1 otherwise */
@@ -146,7 +154,9 @@ int conv2d_output_size(const conv2d_problem_t *prob, int *P, int *Q);
  * Workspace bytes the caller must pass to the given op (0 is a valid answer).
  * A pure function of its arguments.  wgrad uses the workspace for fp32
  * split-K partials; dgrad needs none except on the Winograd tile (its
- * transformed filter); the channel-padded path (C or K off the 16-byte
+ * transformed filter) and on the implicit-GEMM tiles when a stride phase
+ * sums over more than 2048 (filter tap, K channel) pairs (a filter copy laid
+ * out for those long rows); the channel-padded path (C or K off the 16-byte
  * grid) for its zero-padded copies.
  * The caller-allocated scratch with a size query is the tensorcore Conv2D
  * page's "Scratch sizing" convention, minus the im2col buffer.

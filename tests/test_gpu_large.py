@@ -1,6 +1,6 @@
 """Tensors past 2^31 bytes: the buffer and element offsets of the band kernels
-(per image) and the implicit GEMM (whole tensor) near the 32-bit limits the
-host plan allows.  x is 8 x 1536 x 1536 x 64 fp16 (2.4 GB, 1.2e9 elements);
+(per image), the pointwise kernel and the implicit GEMM (whole tensor) near
+the 32-bit limits the host plan allows.  x is 8 x 1536 x 1536 x 64 fp16 (2.4 GB, 1.2e9 elements);
 integer-valued data in -4..4, so every sum is exact.  Outputs are checked at
 sampled points against the oracle run on the sampled point's receptive field
 (a 3x3 patch, zero outside the image) as a one-pixel problem."""
@@ -63,16 +63,18 @@ def test_large_tensors_band_and_igemm():
         ref = oracle.fprop(one, patch(x, n, h, ww), w64).reshape(-1)
         check(y[n, h, ww].double().cpu().numpy(), ref, "f16", "exact", f"fprop band at {(n, h, ww)}")
     del y
-    print("fprop 1x1 (implicit GEMM)", flush=True)
     p1 = problem(N, C, H, W, K, 1, 1)
-    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, p1, "f16")["kernel"] == 1
+    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, p1, "f16")["kernel"] == 5  # pointwise
     y1 = torch.empty((N, H, W, K), dtype=torch.float16, device="cuda")
-    B.conv2d_fprop(p1, "f16", x, w1, None, False, 1.0, 1.0, 1.0, y1, None)
-    torch.cuda.synchronize()
-    for (n, h, ww) in sample_points(904):
-        ref = oracle.fprop(problem(1, C, 1, 1, K, 1, 1), x[n, h, ww].double().cpu().numpy().reshape(1, 1, 1, C),
-                           w164).reshape(-1)
-        check(y1[n, h, ww].double().cpu().numpy(), ref, "f16", "exact", f"fprop 1x1 at {(n, h, ww)}")
+    for algo, name in ((None, "pointwise"), (dict(tile=1), "implicit GEMM")):
+        print(f"fprop 1x1 ({name})", flush=True)
+        y1.fill_(float("nan"))
+        B.conv2d_fprop(p1, "f16", x, w1, None, False, 1.0, 1.0, 1.0, y1, None, algo)
+        torch.cuda.synchronize()
+        for (n, h, ww) in sample_points(904):
+            ref = oracle.fprop(problem(1, C, 1, 1, K, 1, 1),
+                               x[n, h, ww].double().cpu().numpy().reshape(1, 1, 1, C), w164).reshape(-1)
+            check(y1[n, h, ww].double().cpu().numpy(), ref, "f16", "exact", f"fprop 1x1 {name} at {(n, h, ww)}")
     del y1, x
     print("drawing dy, dgrad 3x3 (band)", flush=True)
     dy = big_int_tensor((N, H, W, K), 905)

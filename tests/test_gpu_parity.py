@@ -207,6 +207,54 @@ def test_dgrad_filter_paths_every_tile(cid, prob, dtype, relayout):
         check(f64(dx), ref, dtype, "exact", f"{cid} dgrad tile {t}")
 
 
+# 1x1 stride-1 problems without padding run the pointwise kernel (kernel 5):
+# GEMM-K 64, 128 and 256, 64 to 256 output channels per workgroup, pixel
+# counts that end in a partial sub-tile and a partial workgroup
+POINTWISE = [
+    ("pw_64_256", problem(3, 64, 9, 13, 256, 1, 1), "f16", "int", True, True),
+    ("pw_128_128", problem(2, 128, 17, 11, 128, 1, 1), "bf16", "int", True, False),
+    ("pw_256_64", problem(2, 256, 7, 19, 64, 1, 1), "f16", "int", False, True),
+    ("pw_64_192", problem(4, 64, 15, 15, 192, 1, 1), "bf16", "gauss", True, True),
+    ("pw_128_512", problem(2, 128, 5, 23, 512, 1, 1), "f16", "gauss", True, False),
+    ("pw_dil", problem(2, 64, 10, 10, 64, 1, 1, dil=(2, 2)), "f16", "int", True, True),
+]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,dist,bias,relu", POINTWISE, ids=[c[0] for c in POINTWISE])
+def test_pointwise(cid, prob, dtype, dist, bias, relu):
+    mode = "exact" if dist == "int" else "tol"
+    x, w, b, dy = case_inputs(prob, dtype, dist, seed=zlib.crc32(cid.encode()), bias=bias)
+    fi = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype)
+    di = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, dtype)
+    fp_pw, dg_pw = fi["kernel"] == 5, di["kernel"] == 5
+    assert fp_pw and fi["workspace_bytes"] == 0, fi
+    ref_y = oracle_fprop_out(prob, dtype, x, w, b, relu)
+    y = run_fprop(prob, dtype, x, w, b, relu)
+    check(f64(y), ref_y, dtype, mode, f"{cid} pointwise fprop")
+    if relu:
+        assert not bool((y.view(torch.int16) == -32768).any()), f"{cid}: -0 after ReLU"
+    check(f64(run_fprop(prob, dtype, x, w, b, relu, algo=dict(tile=1))), ref_y, dtype, mode, f"{cid} tile 1")
+    ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
+    if dg_pw:
+        assert di["workspace_bytes"] == 0, di
+    dx = run_dgrad(prob, dtype, dy, w, fill=float("nan"))
+    check(f64(dx), ref_dx, dtype, mode, f"{cid} pointwise dgrad")
+    check(f64(run_dgrad(prob, dtype, dy, w, algo=dict(tile=3))), ref_dx, dtype, mode, f"{cid} dgrad tile 3")
+
+
+def test_pointwise_plans():
+    """Which 1x1 problems the pointwise kernel takes."""
+    on = [(64, 256), (256, 64), (128, 128), (64, 64), (128, 512)]
+    for c, k in on:
+        prob = problem(2, c, 8, 8, k, 1, 1)
+        assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")["kernel"] == 5, (c, k)
+    for prob in (problem(2, 64, 8, 8, 256, 1, 1, pad=(1, 1)), problem(2, 64, 8, 8, 256, 1, 1, stride=(2, 2)),
+                 problem(2, 32, 8, 8, 256, 1, 1), problem(2, 64, 8, 8, 96, 1, 1),
+                 problem(2, 64, 8, 8, 256, 1, 1, groups=2)):
+        assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")["kernel"] != 5, prob
+    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, problem(2, 64, 8, 8, 256, 1, 1), "i8")["kernel"] != 5
+
+
 def test_every_tile_on_band_eligible_problem():
     prob = problem(3, 64, 14, 13, 64, 3, 3, pad=(1, 1))
     x, w, b, dy = case_inputs(prob, "f16", "int", seed=48)
