@@ -16,7 +16,8 @@
 // linear stream of rows*XW pixels, cut into steps of 16 (one MFMA's
 // reduction) and groups of 16 steps that ignore row boundaries.  Steps past
 // the band's end read zero dy pixels (their loads fall outside the band's
-// rows) and add exact zeros.
+// rows) and add exact zeros; the last group runs only the steps per wave
+// that its band pixels need.
 //
 // A workgroup (8 waves, two per SIMD) owns a band of output rows of one image
 // and one half of the R*S*C columns (9 column blocks of 32), all of K.  Waves
@@ -324,7 +325,10 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
     read_dy(odA, J0{});
 #pragma unroll
     for (int i = 0; i < NCB; ++i) read_x(i, J0{});
-    for (int g = 0; g < ngroups; ++g) {
+    // A last group of at most 8 steps computes only its first two slots.
+    const bool half = nsteps - (ngroups - 1) * GSTEPS <= GSTEPS / 2;
+    const int nfull = half ? ngroups - 1 : ngroups;
+    for (int g = 0; g < nfull; ++g) {
         slot(odA, odB, J1{}, none);
         slot(odB, odA, J2{}, none);
         slot(odA, odB, J3{}, none);
@@ -348,6 +352,12 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
                 if (decltype(jb)::value * NCB / NB_WAVE == i) dma_block(gd, px, ch, jb);
             });
         });
+    }
+    // the short last group (its slot-0 fragments are in odA and fx); the
+    // reads of its second slot fetch fragments nothing uses
+    if (half) {
+        slot(odA, odB, J1{}, none);
+        slot(odB, odA, J1{}, none);
     }
 
     // ---- the four phases' sums of each column set, in a fixed order
