@@ -46,7 +46,7 @@ COPY_BYTES = 64 << 20  # reference copy for the HBM byte counters
 # the same counters on a plain copy) lives in this summary, keyed by a hash of
 # the kernel sources it was measured on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3a_hbm_traffic.json")
-KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip", "pointwise.hip"]
+KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip", "pointwise.hip", "pointwise_wgrad.hip"]
 
 
 def kernel_source_hash():
@@ -113,6 +113,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", type=int, default=0,
                     help="with --only: algorithm tile override (1-based, conv2d_plan_info order; 0 = library choice)")
+    ap.add_argument("--split-k", type=int, default=0,
+                    help="with --only wgrad: reduction slices override (0 = library choice)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: also replay captured HIP graphs)")
     ap.add_argument("--cpu-sample-images", type=int, default=0,
@@ -188,7 +190,7 @@ def main():
         print(f"copy {COPY_BYTES} B: {us:.2f} us/launch, {2 * COPY_BYTES / us / 1e3:.1f} GB/s", flush=True)
         return
     if args.only:
-        al = dict(tile=args.tile) if args.tile else None
+        al = dict(tile=args.tile, split_k=args.split_k) if (args.tile or args.split_k) else None
         op = {"fprop": 0, "dgrad": 1, "wgrad": 2}[args.only]
         wso = B.workspace_for(op, prob, dt, dev, al) if al else ws.get(op)
         run = {"fprop": lambda: B.conv2d_fprop(prob, dt, x, w, b, relu, sc[0], sc[1], sc[2], y, wso, al,
@@ -209,7 +211,7 @@ def main():
         nx, ny = prob["N"] * prob["H"] * prob["W"] * prob["C"], prob["N"] * P * Q * prob["K"]
         nw = prob["K"] * prob["R"] * prob["S"] * (prob["C"] // prob["groups"])
         mb = esz * (nx + ny + nw) / 1e6  # algorithmic bytes: each tensor once
-        tl = f" tile {args.tile}" if args.tile else ""
+        tl = (f" tile {args.tile}" if args.tile else "") + (f" split {args.split_k}" if args.split_k else "")
         print(f"{args.only}{tl} {name}: {us:.2f} us/launch, {fl / us / 1e6:.1f} T{'OP' if dt == 'i8' else 'FLOP'}/s, "
               f"{mb / us * 1e3:.1f} GB/s algorithmic ({mb:.2f} MB)", flush=True)
         return
@@ -323,7 +325,9 @@ def main():
         "fprop": [main_kernel(plans["fprop"])],
         "dgrad": ((["filter_relayout"] if plans["dgrad"]["workspace_bytes"] > 0 and plans["dgrad"]["kernel"] == 1
                    else []) + [main_kernel(plans["dgrad"])]),
-        "wgrad": (["direct" if direct else "wgrad_band" if plans["wgrad"]["tile"] == WGRAD_BAND_TILE else "wgrad_gemm"]
+        "wgrad": (["direct" if direct else "pointwise_wgrad" if plans["wgrad"]["kernel"] == 5
+                   else "few_channel_wgrad" if plans["wgrad"]["kernel"] == 4
+                   else "wgrad_band" if plans["wgrad"]["tile"] == WGRAD_BAND_TILE else "wgrad_gemm"]
                   + (["splitk_reduce"] if plans["wgrad"]["split_k"] > 1 else [])),
     }
     passes = {}

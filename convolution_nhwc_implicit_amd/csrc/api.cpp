@@ -129,6 +129,30 @@ bool pointwise_eligible(const Dims &d, int dtype, int op, bool axpby)
     if (npix * gk * 2 > kBufMaxBytes || gk * nout * 2 > kBufMaxBytes) return false;
     return pointwise_supported(dtype, (int)gk, (int)nout);
 }
+// wgrad of the same problems when K and C are 64, 128 or 256 with K*C <=
+// 16384 (the pointwise wgrad kernel), and its pixels per slice: whole groups
+// of 64, short enough for 32-bit offsets into the slice.
+bool pointwise_wgrad_eligible(const Dims &d, int dtype)
+{
+    if (d.G != 1 || d.R != 1 || d.S != 1 || d.sh != 1 || d.sw != 1 || d.ph != 0 || d.pw != 0) return false;
+    return pointwise_wgrad_supported(dtype, (int)d.K, (int)d.C);
+}
+long long pointwise_wgrad_pps(const Dims &d, int splits)
+{
+    const long long npix = d.N * d.H * d.W;
+    return ((npix + splits - 1) / splits + 63) / 64 * 64;
+}
+bool pointwise_wgrad_fits(const Dims &d, int splits)
+{
+    const long long npix = d.N * d.H * d.W;
+    return npix < (1LL << 32) && pointwise_wgrad_pps(d, splits) * 2 * std::max(d.K, d.C) < (1LL << 31);
+}
+// One slice per CU, and at least 8 groups of 64 pixels per slice.
+int choose_pointwise_wgrad_splits(const Dims &d)
+{
+    const long long npix = d.N * d.H * d.W;
+    return (int)std::max(1LL, std::min((long long)kNumCUs, npix / 512));
+}
 bool dgrad_relayout(const Dims &d)
 {
     long long kmax = 0;
@@ -640,8 +664,20 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     }
     if (op == CONV2D_OP_WGRAD) {
         const bool wband = wgrad_band_eligible(d, dtype);
-        pl->num_tiles = wgrad_num_tiles() + (wband ? 1 : 0) + n_direct;
+        // 1x1 problems (never band-eligible): the pointwise wgrad kernel in
+        // the band kernel's place, the default whatever the split count
+        const bool pww = pointwise_wgrad_eligible(d, dtype);
+        pl->num_tiles = wgrad_num_tiles() + (wband || pww ? 1 : 0) + n_direct;
         if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
+        if (pww && (!(algo && algo->tile) || algo->tile - 1 == kWgradBandTile)) {
+            const int s = (algo && algo->split_k) ? algo->split_k : choose_pointwise_wgrad_splits(d);
+            if (s > 65535 || !pointwise_wgrad_fits(d, s)) return CONV2D_ERR_UNSUPPORTED;
+            pl->kernel = 5;
+            pl->tile = kWgradBandTile;
+            pl->split_k = s;
+            pl->ws_bytes = round_up((size_t)s * splitk_stride(d.K * d.C + (ep.db ? d.K : 0)) * sizeof(float), 256);
+            return CONV2D_OK;
+        }
         // default: the band kernel when it applies and no split count is forced
         const bool use_band = algo && algo->tile ? algo->tile - 1 == kWgradBandTile
                                                   : wband && !(algo && algo->split_k);
@@ -1267,6 +1303,27 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
             launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k, a.total, a.part_stride, dw, &re, s));
     }
 
+    if (pl.kernel == 5) {
+        PwWgradArgs p;
+        memset(&p, 0, sizeof(p));
+        p.x = x; p.dy = dy; p.out = workspace;
+        p.npix = npix;
+        p.K = (int)d.K; p.C = (int)d.C;
+        p.splits = pl.split_k;
+        p.pix_per_split = (int)pointwise_wgrad_pps(d, pl.split_k);
+        p.with_db = ep.db != nullptr;  // the bias gradient rides along in the slices
+        const long long kc = d.K * d.C;
+        p.part_stride = splitk_stride(kc + (p.with_db ? d.K : 0));
+        if (launch_pointwise_wgrad(dtype, p, s) != hipSuccess) return CONV2D_ERR_DEVICE;
+        ReduceEpi rp = re;
+        if (p.with_db) {
+            rp.out2 = ep.db;
+            rp.count1 = kc;
+        }
+        return hip_status(launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k,
+                                               kc + (p.with_db ? d.K : 0), p.part_stride, dw, &rp, s));
+    }
+
     if (pl.tile == kWgradBandTile) {
         WgradBandArgs b;
         memset(&b, 0, sizeof(b));
@@ -1366,7 +1423,8 @@ static int wgrad_ex_workspace(const conv2d_problem_t *prob, int dtype, const con
     if (st) return st;
     *pass_bytes = pl.ws_bytes;
     *total = pl.ws_bytes;
-    *fused = ep.db && !pl.padded && pl.kernel == 1 && (pl.tile == kWgradBandTile || pl.tile == 0);
+    *fused = ep.db && !pl.padded &&
+             ((pl.kernel == 1 && (pl.tile == kWgradBandTile || pl.tile == 0)) || pl.kernel == 5);
     if (ep.db && !*fused) {
         Dims d;
         int splits;

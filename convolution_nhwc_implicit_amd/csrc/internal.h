@@ -176,6 +176,22 @@ int pointwise_nwg(int gk, int nout);  // output channels per workgroup, 0 if non
 int pointwise_pixels_per_wg(int gk);
 hipError_t launch_pointwise(int dtype, const PwArgs &a, hipStream_t st);
 
+// pointwise_wgrad.hip: 1x1 stride-1 weight gradient, one workgroup per pixel
+// slice holding the whole K x C tile; fp32 partial per slice ([K][C], then K
+// dy column sums with_db), summed by the split-K reduce
+struct PwWgradArgs {
+    const void *x, *dy;
+    void *out;
+    uint32_t npix;
+    int pix_per_split;  // a multiple of 64
+    int splits;
+    long long part_stride;
+    int K, C;
+    int with_db;
+};
+bool pointwise_wgrad_supported(int dtype, int K, int C);
+hipError_t launch_pointwise_wgrad(int dtype, const PwWgradArgs &a, hipStream_t st);
+
 // Re-lays the filter w[K][R][S][C/G] out as one [C][taps*K/G] matrix per
 // dgrad stride phase, for the implicit GEMM on long GEMM-K rows (taps of the phase in (jr, js) order, the dx channel's
 // group's dy channels innermost).

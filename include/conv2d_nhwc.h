@@ -109,7 +109,10 @@ typedef struct conv2d_problem {
  *            C for fprop and K for dgrad, 64, 128 or 256 and the other a
  *            multiple of 64) has the pointwise kernel as tile 6, the
  *            library's choice: a GEMM over pixels whose filter slice stays in
- *            registers.
+ *            registers.  Its wgrad, when K and C are 64, 128 or 256 with K*C
+ *            <= 16384, runs by default on the pointwise wgrad kernel (tile 3;
+ *            each of split_k workgroups streams one slice of pixels and
+ *            writes one fp32 partial of dw).
  *            A stride-1, dilation-1 3x3 fp16 problem (no
  *            linear-combination epilogue) also offers, as the last tile of
  *            fprop when C = 64 and K % 16 == 0, and of dgrad when K = 64,
@@ -133,7 +136,8 @@ typedef struct conv2d_algo {
 typedef struct conv2d_plan_info {
     int kernel;        /* 1 = implicit GEMM (or band kernel), 2 = direct (groups > 1),
                           3 = Winograd F(2x2,3x3), 4 = few-channel kernels (C or K
-                          off the 16-byte grid), 5 = pointwise (1x1, stride 1) */
+                          off the 16-byte grid), 5 = pointwise (1x1, stride 1;
+                          fprop, dgrad and wgrad) */
     int tile;          /* index of the tile configuration used (0-based) */
     int num_tiles;     /* number of tile configurations available for this op/dtype */
     int split_k;       /* reduction slices (wgrad), 1 otherwise */

@@ -147,6 +147,35 @@ def test_plan_rules():
         assert B.conv2d_plan_info(0, s, "f16", algo=dict(tile=t))["tile"] == t - 1
 
 
+def test_pointwise_wgrad_plan():
+    """1x1 stride-1 wgrad with K and C in {64, 128, 256}, K*C <= 16384: the
+    pointwise wgrad kernel (kernel 5, in the band kernel's tile 2), one fp32
+    partial of K*C (+ K with the bias gradient) per pixel slice."""
+    prob = problem(64, 64, 56, 56, 256, 1, 1)
+    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
+    assert info["kernel"] == 5 and info["tile"] == 2 and info["num_tiles"] == 3
+    assert info["split_k"] == 256
+    assert info["workspace_bytes"] == 256 * 256 * 64 * 4  # slices are whole 256-byte multiples here
+    forced = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "bf16", algo=dict(split_k=7))
+    assert forced["kernel"] == 5 and forced["split_k"] == 7
+    class FakeDb:  # only its address is taken; nothing is enqueued
+        def data_ptr(self):
+            return 0x10000
+
+    with_db = B.conv2d_workspace_size_ex(B.CONV2D_OP_WGRAD, prob, "f16", epi=dict(db=FakeDb()))
+    assert with_db == 256 * (256 * 64 + 256) * 4  # the bias gradient rides in the slices
+    small = problem(2, 64, 5, 5, 64, 1, 1)  # 50 pixels: one slice
+    assert B.conv2d_plan_info(B.CONV2D_OP_WGRAD, small, "f16")["split_k"] == 1
+    # the generic tiles stay selectable
+    assert B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16", algo=dict(tile=1))["kernel"] == 1
+    for other in (problem(2, 64, 8, 8, 512, 1, 1), problem(2, 32, 8, 8, 64, 1, 1),
+                  problem(2, 64, 8, 8, 256, 1, 1, stride=(2, 2)), problem(2, 64, 8, 8, 64, 1, 1, pad=(1, 1)),
+                  problem(2, 64, 8, 8, 64, 1, 1, groups=2), problem(2, 192, 8, 8, 64, 1, 1)):
+        assert B.conv2d_plan_info(B.CONV2D_OP_WGRAD, other, "f16")["kernel"] != 5, other
+    with pytest.raises(B.Conv2dError):  # int8 backward passes are not offered
+        B.conv2d_plan_info(B.CONV2D_OP_WGRAD, problem(2, 64, 8, 8, 64, 1, 1), "i8")
+
+
 def _raw_call(lib, fn, *args):
     return getattr(lib, fn)(*args)
 

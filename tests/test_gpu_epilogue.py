@@ -3,7 +3,7 @@ beta * C, and wgrad's fp32 output) against the oracle, through the C ABI, on
 every kernel family: the implicit GEMM (fprop, strided dgrad phases, generic
 wgrad), shapes the band kernels would take (fprop/dgrad then run on the
 implicit GEMM; wgrad keeps the band kernel and applies the epilogue in its
-reduction), the grouped implicit GEMM, the LDS-tiled and
+reduction), the pointwise wgrad kernel (1x1), the grouped implicit GEMM, the LDS-tiled and
 one-thread-per-output direct kernels, and the zero-padded channel path.  Integer-valued data with alpha = 2, beta = -1 is
 exact in fp32, so those outputs must equal the oracle's rounded once."""
 import zlib
@@ -36,6 +36,10 @@ CASES = [
     ("grouped_naive", problem(2, 12, 9, 10, 8, 3, 3, pad=(1, 1), groups=2), "bf16", "int"),
     ("padded_c3_k13", problem(2, 3, 17, 15, 13, 5, 5, pad=(2, 2), stride=(2, 2)), "f16", "int"),
     ("gauss", problem(2, 24, 12, 11, 40, 3, 3, pad=(1, 1)), "bf16", "gauss"),
+    # 1x1 stride 1: wgrad on the pointwise wgrad kernel (bias gradient in its
+    # slices, the epilogue in the reduce); one and four pixel phases
+    ("pointwise_k256", problem(3, 64, 9, 13, 256, 1, 1), "f16", "int"),
+    ("pointwise_k64_gauss", problem(2, 64, 12, 11, 64, 1, 1), "bf16", "gauss"),
 ]
 
 

@@ -255,6 +255,40 @@ def test_pointwise_plans():
     assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, problem(2, 64, 8, 8, 256, 1, 1), "i8")["kernel"] != 5
 
 
+# The pointwise wgrad kernel (1x1 stride 1, K and C in {64, 128, 256}, K*C <=
+# 16384): every wave layout (one, two and four pixel phases), pixel counts
+# that end inside a 64-pixel group, and split counts from one slice to more
+# slices than groups (empty slices write zero partials).
+PW_WGRAD = [
+    ("pww_c64_k256", problem(3, 64, 9, 13, 256, 1, 1), "f16", "int"),
+    ("pww_c256_k64", problem(2, 256, 7, 19, 64, 1, 1), "bf16", "int"),
+    ("pww_c128_k128", problem(2, 128, 17, 11, 128, 1, 1), "f16", "int"),
+    ("pww_c64_k128", problem(2, 64, 11, 9, 128, 1, 1), "bf16", "int"),
+    ("pww_c128_k64", problem(2, 128, 9, 9, 64, 1, 1), "f16", "int"),
+    ("pww_c64_k64", problem(3, 64, 10, 10, 64, 1, 1), "f16", "int"),
+    ("pww_gauss", problem(4, 64, 15, 15, 256, 1, 1), "bf16", "gauss"),
+    ("pww_dil_gauss", problem(2, 64, 10, 10, 64, 1, 1, dil=(2, 2)), "f16", "gauss"),
+]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,dist", PW_WGRAD, ids=[c[0] for c in PW_WGRAD])
+def test_pointwise_wgrad(cid, prob, dtype, dist):
+    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, dtype)
+    assert info["kernel"] == 5 and info["tile"] == 2, info
+    mode = "exact" if dist == "int" else "tol"
+    x, _, _, dy = case_inputs(prob, dtype, dist, seed=zlib.crc32(cid.encode()), bias=False)
+    ref = oracle.wgrad(prob, f64(x), f64(dy))
+    dw = run_wgrad(prob, dtype, x, dy)
+    check(f64(dw), ref, dtype, mode, f"{cid} pointwise wgrad")
+    again = run_wgrad(prob, dtype, x, dy)
+    assert torch.equal(again.view(torch.int16), dw.view(torch.int16)), f"{cid}: repeat differs"
+    groups = (prob["N"] * prob["H"] * prob["W"] + 63) // 64
+    for s in (1, 3, groups + 5):
+        check(f64(run_wgrad(prob, dtype, x, dy, algo=dict(tile=3, split_k=s))), ref, dtype, mode,
+              f"{cid} split {s}")
+    check(f64(run_wgrad(prob, dtype, x, dy, algo=dict(tile=1))), ref, dtype, mode, f"{cid} generic tile 1")
+
+
 def test_every_tile_on_band_eligible_problem():
     prob = problem(3, 64, 14, 13, 64, 3, 3, pad=(1, 1))
     x, w, b, dy = case_inputs(prob, "f16", "int", seed=48)
