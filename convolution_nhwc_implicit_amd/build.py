@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libconv2d_nhwc.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "igemm.hip", "band.hip", "wino.hip", "wgrad.hip", "wgrad_band.hip", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip", "pointwise.hip", "pointwise_wgrad.hip"]
+SOURCES = ["api.cpp", "igemm.hip", "band.hip", "wino.hip", "wgrad.hip", "wgrad_band.hip", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip", "pointwise.hip", "pointwise_wgrad.hip", "patch.hip"]
 
 COMMON_FLAGS = [
     "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

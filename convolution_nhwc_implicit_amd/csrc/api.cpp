@@ -241,6 +241,68 @@ bool wino_eligible(const Dims &d, int dtype, int op)
            d.pw <= 2;
 }
 
+// Patch kernel (fprop): the lattice of input rows and columns the taps read,
+// the output tile (TP rows x TQ columns, at most 128 pixels) and its patch of
+// lattice pixels, which must fit in LDS beside the filter rings.  nb: output
+// channels per workgroup in blocks of 32.  Returns false when the kernel does
+// not apply.
+bool patch_layout(const Dims &d, int dtype, PatchArgs *pa, int *nb_out, int *u_out)
+{
+    if (d.G != 1 || (dtype != CONV2D_DTYPE_F16 && dtype != CONV2D_DTYPE_BF16)) return false;
+    if (d.C % 16 || d.K % 32) return false;
+    const int nb = d.K % 96 == 0 ? 3 : d.K % 64 == 0 ? 2 : 1;
+    auto gcd = [](long long u, long long v) {
+        while (v) {
+            const long long r = u % v;
+            u = v;
+            v = r;
+        }
+        return u;
+    };
+    const long long gh = gcd(d.sh, d.dh), gw = gcd(d.sw, d.dw);
+    const long long sh1 = d.sh / gh, sw1 = d.sw / gw, dh1 = d.dh / gh, dw1 = d.dw / gw;
+    const long long TQ = std::min<long long>(d.Q, 128);
+    const long long tp_max = std::min<long long>(d.P, 128 / TQ);
+    const long long cpp = d.C / 8;
+    const long long PP = cpp % 2 ? cpp : cpp + 1;
+    const long long PW = (TQ - 1) * sw1 + (d.S - 1) * dw1 + 1;
+    // the longest filter super-step (u 16-channel steps, u | C/16) whose ring
+    // leaves room for the most output rows
+    long long TP = 0;
+    int u = 0;
+    for (int uc : {4, 2, 1}) {
+        if ((d.C / 16) % uc) continue;
+        const long long budget = patch_lds_bytes() - patch_ring_bytes(nb, uc);
+        for (long long tp = tp_max; tp > TP; --tp) {
+            const long long ph = (tp - 1) * sh1 + (d.R - 1) * dh1 + 1;
+            if ((ph * PW * PP + 63) / 64 * 1024 <= budget) {
+                TP = tp;
+                u = uc;
+                break;
+            }
+        }
+    }
+    if (TP == 0) return false;
+    const long long PH = (TP - 1) * sh1 + (d.R - 1) * dh1 + 1;
+    if (pa) {
+        pa->N = (int)d.N; pa->H = (int)d.H; pa->W = (int)d.W; pa->C = (int)d.C;
+        pa->P = (int)d.P; pa->Q = (int)d.Q; pa->K = (int)d.K; pa->R = (int)d.R; pa->S = (int)d.S;
+        pa->gh = (int)gh; pa->gw = (int)gw; pa->pad_h = (int)d.ph; pa->pad_w = (int)d.pw;
+        pa->sh1 = (int)sh1; pa->sw1 = (int)sw1; pa->dh1 = (int)dh1; pa->dw1 = (int)dw1;
+        pa->TP = (int)TP; pa->TQ = (int)TQ;
+        pa->tiles_q = (int)((d.Q + TQ - 1) / TQ);
+        pa->tiles_img = (int)((d.P + TP - 1) / TP) * pa->tiles_q;
+        pa->PH = (int)PH; pa->PW = (int)PW; pa->PP = (int)PP;
+        pa->patch_slots = (int)(PH * PW * PP);
+        pa->div_pp = make_fastdiv((uint32_t)PP);
+        pa->div_pw = make_fastdiv((uint32_t)PW);
+        pa->div_tq = make_fastdiv((uint32_t)TQ);
+    }
+    if (nb_out) *nb_out = nb;
+    if (u_out) *u_out = u;
+    return true;
+}
+
 // Stride-1 wgrad with the filter shape and channel counts the wgrad band
 // kernel is built for.
 bool wgrad_band_eligible(const Dims &d, int dtype)
@@ -716,15 +778,27 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
                                                           : band_eligible(d, dtype, d.K, d.P, d.Q, d.C, d.H, d.W));
     const bool wino = band && wino_eligible(d, dtype, op);
     const bool pw = pointwise_eligible(d, dtype, op, ep.axpby);  // 1x1: never with band
-    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0) + (pw ? 1 : 0) + n_direct;
+    int patch_nb = 1;
+    // fprop: the patch kernel's tile follows the others; the default for
+    // filters with more than one tap when its grid takes at most two
+    // workgroups per CU (each workgroup pays for loading its patch and
+    // adding its four partial tiles, which many small tiles would repeat)
+    PatchArgs pa;
+    const bool patch = op == CONV2D_OP_FPROP && !ep.axpby && patch_layout(d, dtype, &pa, &patch_nb, nullptr);
+    const int patch_tile = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0) + (pw ? 1 : 0);
+    const bool patch_default =
+        patch && !band && !pw && d.R * d.S > 1 && d.N * pa.tiles_img * (d.K / (32 * patch_nb)) <= 2 * kNumCUs;
+    pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0) + (pw ? 1 : 0) + (patch ? 1 : 0) + n_direct;
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
         pl->tile = (algo && algo->tile) ? algo->tile - 1
                    : pw               ? kPwTile
                    : band             ? kBandTile
+                   : patch_default    ? patch_tile
                                       : choose_igemm_tile(d.N * d.P * d.Q, d.Kg);
-        if (pl->tile == kWinoTile) pl->kernel = 3;
+        if (pl->tile == kWinoTile && wino) pl->kernel = 3;
         if (pw && pl->tile == kPwTile) pl->kernel = 5;
+        if (patch && pl->tile == patch_tile) pl->kernel = 6;
         return CONV2D_OK;
     }
     // dgrad
@@ -1020,6 +1094,14 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         return hip_status(launch_direct_fprop(dtype, a, s));
     }
 
+    if (pl.kernel == 6) {
+        PatchArgs pa;
+        memset(&pa, 0, sizeof(pa));
+        int nb = 0, u = 0;
+        if (!patch_layout(d, dtype, &pa, &nb, &u)) return CONV2D_ERR_UNSUPPORTED;
+        pa.src = x; pa.filt = w; pa.bias = bias; pa.dst = y; pa.relu = relu;
+        return hip_status(launch_patch_fprop(dtype, nb, u, pa, s));
+    }
     if (pl.tile == kBandTile)
         return run_band(dtype, d, (int)d.C, x, (int)d.H, (int)d.W, w, 0, bias, relu, m, y, (int)d.P, (int)d.Q,
                         (int)d.K, (int)d.ph, (int)d.pw, s);

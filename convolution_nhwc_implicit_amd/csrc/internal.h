@@ -115,6 +115,32 @@ hipError_t launch_igemm(int dtype, int tile, const IgemmArgs &a, int grid_m, int
                         hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Patch kernel (patch.hip): fprop with the workgroup's input patch in LDS.
+// Along each axis the input rows a convolution reads lie on a lattice of
+// step g = gcd(stride, dil) (lattice row i is input row g*i - pad); on it the
+// convolution has stride sh1 = stride / g and dilation dh1 = dil / g.  A
+// workgroup computes TP x TQ output pixels (TP*TQ <= 128) of one image and
+// 32*nb output channels from PH x PW lattice pixels held at a pitch of PP
+// 16-byte slots (PP odd, PP >= C/8); groups == 1, C % 16 == 0, K % (32*nb) == 0.
+// ---------------------------------------------------------------------------
+struct PatchArgs {
+    const void *src;   // x [N][H][W][C]
+    const void *filt;  // w [K][R][S][C]
+    const void *bias;  // [K] or null
+    void *dst;         // y [N][P][Q][K]
+    int N, H, W, C, P, Q, K, R, S;
+    int gh, gw, pad_h, pad_w, sh1, sw1, dh1, dw1;
+    int TP, TQ, tiles_q, tiles_img;
+    int PH, PW, PP, patch_slots;
+    int relu;
+    FastDiv div_pp, div_pw, div_tq;
+};
+// u: 16-channel steps per super-step of the filter stream (1, 2 or 4; divides C/16)
+int patch_ring_bytes(int nb, int u);
+int patch_lds_bytes();
+hipError_t launch_patch_fprop(int dtype, int nb, int u, const PatchArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Stride-1 band kernel (band.hip): filter in registers, a ring of input rows
 // in LDS.  src [N][H][W][CIN] -> dst [N][P][Q][ngemm] with
 // P = H + 2*pad_h - dil*(R-1) (likewise Q); pad_h / pad_w may be negative.

@@ -310,13 +310,16 @@ def test_winograd_tile_offered_only_where_it_applies():
     workspace."""
     base = problem(2, 64, 10, 12, 64, 3, 3, pad=(1, 1))
     info = B.conv2d_plan_info(0, base, "f16")
-    assert info["num_tiles"] == 7 and info["tile"] == 5 and info["kernel"] == 1
+    # fprop table: 5 implicit-GEMM tiles, the band kernel, Winograd, the patch kernel
+    assert info["num_tiles"] == 8 and info["tile"] == 5 and info["kernel"] == 1
     w = B.conv2d_plan_info(0, base, "f16", algo=dict(tile=7))
     assert w["kernel"] == 3 and w["tile"] == 6 and w["workspace_bytes"] == 0
-    # bf16: the band kernel is still the default, and the table ends before Winograd
+    assert B.conv2d_plan_info(0, base, "f16", algo=dict(tile=8))["kernel"] == 6
+    # bf16: the band kernel is still the default, and no Winograd tile
+    # (fprop: the patch kernel follows the band kernel)
     for op in (0, 1):
         info = B.conv2d_plan_info(op, base, "bf16")
-        assert info["num_tiles"] == 6 and info["tile"] == 5 and info["kernel"] == 1
+        assert info["num_tiles"] == 6 + (op == 0) and info["tile"] == 5 and info["kernel"] == 1
     # dgrad: the forward Winograd kernel on dy with the flipped, transposed
     # filter, whose transform goes to the workspace (16 x C x K elements)
     d = B.conv2d_plan_info(1, base, "f16")
@@ -334,10 +337,10 @@ def test_winograd_tile_offered_only_where_it_applies():
               (problem(2, 64, 10, 12, 64, 5, 5, pad=(2, 2)), "f16")]
     for prob, dt in others:
         n = B.conv2d_plan_info(0, prob, dt)["num_tiles"]
-        assert n <= 6, (prob, dt)
+        assert n <= 7, (prob, dt)
         assert all(B.conv2d_plan_info(0, prob, dt, algo=dict(tile=t))["kernel"] != 3 for t in range(1, n + 1))
         with pytest.raises(B.Conv2dError) as e:
-            B.conv2d_plan_info(0, prob, dt, algo=dict(tile=7))
+            B.conv2d_plan_info(0, prob, dt, algo=dict(tile=n + 1))
         assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
     with pytest.raises(B.Conv2dError) as e:
         B.conv2d_workspace_size_ex(0, base, "f16", algo=dict(tile=7), epi=dict(alpha=2.0, beta=0.0))

@@ -295,10 +295,12 @@ def test_every_tile_on_band_eligible_problem():
     ref_y = oracle_fprop_out(prob, "f16", x, w, b, False)
     ref_dx = oracle.dgrad(prob, f64(dy), f64(w))
     info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16")
-    # the band kernel is the default; the last tile is Winograd F(2x2,3x3),
-    # exact here because the transformed integer operands are exact in fp16
-    assert info["num_tiles"] == 7 and info["tile"] == 5
+    # the band kernel is the default; tile 7 is Winograd F(2x2,3x3), exact
+    # here because the transformed integer operands are exact in fp16, and
+    # the last fprop tile the patch kernel
+    assert info["num_tiles"] == 8 and info["tile"] == 5
     assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16", algo=dict(tile=7))["kernel"] == 3
+    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16", algo=dict(tile=8))["kernel"] == 6
     dinfo = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16")
     assert dinfo["num_tiles"] == 7 and dinfo["tile"] == 5  # dgrad's last tile is Winograd too
     for t in range(1, info["num_tiles"] + 1):

@@ -31,10 +31,13 @@ U_TYPE = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
 def wino_tile(prob, dtype):
+    """The fprop Winograd tile: the one plan kernel 3 runs (the patch kernel's
+    tile follows it where that kernel applies)."""
     info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype)
-    algo = dict(tile=info["num_tiles"])
-    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype, algo=algo)["kernel"] == 3
-    return algo
+    tiles = [t for t in range(1, info["num_tiles"] + 1)
+             if B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype, algo=dict(tile=t))["kernel"] == 3]
+    assert len(tiles) == 1, tiles
+    return dict(tile=tiles[0])
 
 
 EXACT = [
@@ -167,5 +170,5 @@ def test_winograd_refuses_bf16():
         n = B.conv2d_plan_info(op, prob, "bf16")["num_tiles"]
         assert all(B.conv2d_plan_info(op, prob, "bf16", algo=dict(tile=t))["kernel"] != 3 for t in range(1, n + 1))
         with pytest.raises(B.Conv2dError) as e:
-            B.conv2d_plan_info(op, prob, "bf16", algo=dict(tile=7))
+            B.conv2d_plan_info(op, prob, "bf16", algo=dict(tile=n + 1))
         assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
