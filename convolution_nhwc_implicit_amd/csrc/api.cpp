@@ -241,16 +241,22 @@ bool wino_eligible(const Dims &d, int dtype, int op)
            d.pw <= 2;
 }
 
-// Patch kernel (fprop): the lattice of input rows and columns the taps read,
-// the output tile (TP rows x TQ columns, at most 128 pixels) and its patch of
-// lattice pixels, which must fit in LDS beside the filter rings.  nb: output
-// channels per workgroup in blocks of 32.  Returns false when the kernel does
-// not apply.
-bool patch_layout(const Dims &d, int dtype, PatchArgs *pa, int *nb_out, int *u_out)
+// Patch kernel: the lattice of source rows and columns the taps read, the
+// output tile (TP lattice rows x TQ columns, at most 128 pixels) and its
+// patch of lattice pixels, which must fit in LDS beside the filter rings.
+// fprop reads x on the lattice of step gcd(stride, dil).  dgrad applies when
+// the stride divides the dilation on both axes: dx is nonzero only on the
+// rows h = -pad (mod stride) (likewise columns), where it is a stride-1
+// correlation of dy with the flipped filter (dilation dil/stride).  nb:
+// output channels per workgroup in blocks of 32; u: 16-channel steps per
+// filter super-step.  Returns false when the kernel does not apply.
+bool patch_layout(int op, const Dims &d, int dtype, PatchArgs *pa, int *nb_out)
 {
     if (d.G != 1 || (dtype != CONV2D_DTYPE_F16 && dtype != CONV2D_DTYPE_BF16)) return false;
-    if (d.C % 16 || d.K % 32) return false;
-    const int nb = d.K % 96 == 0 ? 3 : d.K % 64 == 0 ? 2 : 1;
+    if (op != CONV2D_OP_FPROP && op != CONV2D_OP_DGRAD) return false;
+    const bool dg = op == CONV2D_OP_DGRAD;
+    const long long SC = dg ? d.K : d.C, OC = dg ? d.C : d.K;
+    if (SC % 16 || OC % 32) return false;
     auto gcd = [](long long u, long long v) {
         while (v) {
             const long long r = u % v;
@@ -259,47 +265,102 @@ bool patch_layout(const Dims &d, int dtype, PatchArgs *pa, int *nb_out, int *u_o
         }
         return u;
     };
-    const long long gh = gcd(d.sh, d.dh), gw = gcd(d.sw, d.dw);
-    const long long sh1 = d.sh / gh, sw1 = d.sw / gw, dh1 = d.dh / gh, dw1 = d.dw / gw;
-    const long long TQ = std::min<long long>(d.Q, 128);
-    const long long tp_max = std::min<long long>(d.P, 128 / TQ);
-    const long long cpp = d.C / 8;
+    // source lattice, output lattice and extents per axis
+    long long gh, gw, sh1, sw1, dh1, dw1, padh, padw, ogh = 1, ogw = 1, oh0 = 0, ow0 = 0, LP, LQ, SH, SW;
+    if (!dg) {
+        gh = gcd(d.sh, d.dh);
+        gw = gcd(d.sw, d.dw);
+        sh1 = d.sh / gh; sw1 = d.sw / gw; dh1 = d.dh / gh; dw1 = d.dw / gw;
+        padh = d.ph; padw = d.pw;
+        LP = d.P; LQ = d.Q; SH = d.H; SW = d.W;
+    } else {
+        if (d.dh % d.sh || d.dw % d.sw) return false;
+        auto axis = [](long long s, long long dil, long long pad, long long R, long long extent, long long *o0,
+                       long long *n, long long *pe) {
+            *o0 = ((-pad) % s + s) % s;               // first row h >= 0 with h + pad = 0 (mod s)
+            *n = extent > *o0 ? (extent - *o0 + s - 1) / s : 0;
+            *pe = (R - 1) * (dil / s) - (*o0 + pad) / s;  // padding of the flipped stride-1 correlation
+        };
+        axis(d.sh, d.dh, d.ph, d.R, d.H, &oh0, &LP, &padh);
+        axis(d.sw, d.dw, d.pw, d.S, d.W, &ow0, &LQ, &padw);
+        if (LP == 0 || LQ == 0) return false;
+        ogh = d.sh; ogw = d.sw;
+        gh = gw = 1; sh1 = sw1 = 1;
+        dh1 = d.dh / d.sh; dw1 = d.dw / d.sw;
+        SH = d.P; SW = d.Q;
+    }
+    const long long cpp = SC / 8;
     const long long PP = cpp % 2 ? cpp : cpp + 1;
-    const long long PW = (TQ - 1) * sw1 + (d.S - 1) * dw1 + 1;
-    // the longest filter super-step (u 16-channel steps, u | C/16) whose ring
-    // leaves room for the most output rows
-    long long TP = 0;
-    int u = 0;
-    for (int uc : {4, 2, 1}) {
-        if ((d.C / 16) % uc) continue;
-        const long long budget = patch_lds_bytes() - patch_ring_bytes(nb, uc);
-        for (long long tp = tp_max; tp > TP; --tp) {
-            const long long ph = (tp - 1) * sh1 + (d.R - 1) * dh1 + 1;
-            if ((ph * PW * PP + 63) / 64 * 1024 <= budget) {
-                TP = tp;
-                u = uc;
-                break;
+    // Candidates: pixel blocks of 32 per workgroup (mb = 4 or 2), output
+    // channels per workgroup (32*nb, nb | OC/32), the filter stream's
+    // super-step (fprop: u 16-channel steps, u | SC/16; dgrad: 1) and ring
+    // depth (fprop: set by nb and u; dgrad: 8 or 4).  Each takes the most
+    // output rows whose patch fits beside its rings; the cheapest by a simple
+    // model wins: rounds of 256 workgroups times (the main loop's cycles per
+    // wave, steps * mb * nb MFMAs at about 12 cycles each per wave, plus a
+    // prologue and epilogue of about 6000 + 600 * mb * nb cycles); ties go to
+    // the larger tiles and deeper rings.
+    const long long steps = d.R * d.S * (SC / 16);
+    long long best = -1, TP = 0, TQ = 0, PW = 0;
+    int nb = 0, u = 0, nsb = 0, mb = 0;
+    for (int mbc : {4, 2}) {
+        const long long tq = std::min<long long>(LQ, 32 * mbc);
+        const long long tp_max = std::min<long long>(LP, 32 * mbc / tq);
+        const long long pw = (tq - 1) * sw1 + (d.S - 1) * dw1 + 1;
+        for (int nbc : {3, 2, 1}) {
+            if (OC % (32 * nbc)) continue;
+            for (int uc : {4, 2, 1}) {
+                if ((SC / 16) % uc || (dg && uc != 1)) continue;
+                for (int sc : {8, 4}) {
+                    if (!dg && sc == 4) continue;  // one ring depth per (nb, u) for fprop
+                    const int ns = dg ? sc : patch_ring_stages(nbc, uc);
+                    const long long budget = patch_lds_bytes() - 4LL * ns * nbc * uc * 1024;
+                    long long tp = tp_max;
+                    for (; tp > 0; --tp) {
+                        const long long ph = (tp - 1) * sh1 + (d.R - 1) * dh1 + 1;
+                        if ((ph * pw * PP + 63) / 64 * 1024 <= budget) break;
+                    }
+                    if (tp == 0) continue;
+                    const long long wgs = d.N * ((LP + tp - 1) / tp) * ((LQ + tq - 1) / tq) * (OC / (32 * nbc));
+                    const long long cost = (wgs + kNumCUs - 1) / kNumCUs *
+                                           (steps * mbc * nbc * 12 + 6000 + 600 * mbc * nbc);
+                    if (best < 0 || cost < best) {
+                        best = cost;
+                        TP = tp;
+                        TQ = tq;
+                        PW = pw;
+                        nb = nbc;
+                        u = uc;
+                        nsb = ns;
+                        mb = mbc;
+                    }
+                }
             }
         }
     }
     if (TP == 0) return false;
     const long long PH = (TP - 1) * sh1 + (d.R - 1) * dh1 + 1;
     if (pa) {
-        pa->N = (int)d.N; pa->H = (int)d.H; pa->W = (int)d.W; pa->C = (int)d.C;
-        pa->P = (int)d.P; pa->Q = (int)d.Q; pa->K = (int)d.K; pa->R = (int)d.R; pa->S = (int)d.S;
-        pa->gh = (int)gh; pa->gw = (int)gw; pa->pad_h = (int)d.ph; pa->pad_w = (int)d.pw;
+        pa->N = (int)d.N; pa->H = (int)SH; pa->W = (int)SW; pa->SC = (int)SC;
+        pa->OH = (int)(dg ? d.H : d.P); pa->OW = (int)(dg ? d.W : d.Q); pa->OC = (int)OC;
+        pa->P = (int)LP; pa->Q = (int)LQ; pa->R = (int)d.R; pa->S = (int)d.S;
+        pa->gh = (int)gh; pa->gw = (int)gw; pa->pad_h = (int)padh; pa->pad_w = (int)padw;
         pa->sh1 = (int)sh1; pa->sw1 = (int)sw1; pa->dh1 = (int)dh1; pa->dw1 = (int)dw1;
+        pa->ogh = (int)ogh; pa->ogw = (int)ogw; pa->oh0 = (int)oh0; pa->ow0 = (int)ow0;
         pa->TP = (int)TP; pa->TQ = (int)TQ;
-        pa->tiles_q = (int)((d.Q + TQ - 1) / TQ);
-        pa->tiles_img = (int)((d.P + TP - 1) / TP) * pa->tiles_q;
+        pa->tiles_q = (int)((LQ + TQ - 1) / TQ);
+        pa->tiles_img = (int)((LP + TP - 1) / TP) * pa->tiles_q;
         pa->PH = (int)PH; pa->PW = (int)PW; pa->PP = (int)PP;
         pa->patch_slots = (int)(PH * PW * PP);
         pa->div_pp = make_fastdiv((uint32_t)PP);
         pa->div_pw = make_fastdiv((uint32_t)PW);
         pa->div_tq = make_fastdiv((uint32_t)TQ);
+        pa->nb = nb;
+        pa->u = u;
+        pa->nsb = nsb;
+        pa->mb = mb;
     }
     if (nb_out) *nb_out = nb;
-    if (u_out) *u_out = u;
     return true;
 }
 
@@ -779,15 +840,15 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
     const bool wino = band && wino_eligible(d, dtype, op);
     const bool pw = pointwise_eligible(d, dtype, op, ep.axpby);  // 1x1: never with band
     int patch_nb = 1;
-    // fprop: the patch kernel's tile follows the others; the default for
-    // filters with more than one tap when its grid takes at most two
-    // workgroups per CU (each workgroup pays for loading its patch and
-    // adding its four partial tiles, which many small tiles would repeat)
+    // the patch kernel's tile follows the others; the default for filters
+    // with more than one tap when its grid takes at most two workgroups per
+    // CU (each workgroup pays for loading its patch and adding its four
+    // partial tiles, which many small tiles would repeat)
     PatchArgs pa;
-    const bool patch = op == CONV2D_OP_FPROP && !ep.axpby && patch_layout(d, dtype, &pa, &patch_nb, nullptr);
+    const bool patch = !ep.axpby && patch_layout(op, d, dtype, &pa, &patch_nb);
     const int patch_tile = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0) + (pw ? 1 : 0);
     const bool patch_default =
-        patch && !band && !pw && d.R * d.S > 1 && d.N * pa.tiles_img * (d.K / (32 * patch_nb)) <= 2 * kNumCUs;
+        patch && !band && !pw && d.R * d.S > 1 && d.N * pa.tiles_img * (pa.OC / (32 * patch_nb)) <= 2 * kNumCUs;
     pl->num_tiles = igemm_num_tiles() + (band ? 1 : 0) + (wino ? 1 : 0) + (pw ? 1 : 0) + (patch ? 1 : 0) + n_direct;
     if (algo && algo->tile > pl->num_tiles) return CONV2D_ERR_UNSUPPORTED;
     if (op == CONV2D_OP_FPROP) {
@@ -802,12 +863,18 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         return CONV2D_OK;
     }
     // dgrad
-    if (d.sh * d.sw > kMaxPhases) return CONV2D_ERR_UNSUPPORTED;
-    pl->phases = (int)(d.sh * d.sw);
     pl->tile = (algo && algo->tile) ? algo->tile - 1
                : pw               ? kPwTile
                : band             ? kBandTile
-                                  : choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.Cg);
+               : patch_default    ? patch_tile
+                                  : -1;
+    if (patch && pl->tile == patch_tile) {
+        pl->kernel = 6;
+        return CONV2D_OK;
+    }
+    if (d.sh * d.sw > kMaxPhases) return CONV2D_ERR_UNSUPPORTED;
+    pl->phases = (int)(d.sh * d.sw);
+    if (pl->tile < 0) pl->tile = choose_igemm_tile(d.N * d.H * d.W / pl->phases, d.Cg);
     if (pw && pl->tile == kPwTile) {
         pl->kernel = 5;
         return CONV2D_OK;
@@ -1027,7 +1094,7 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         f.x = x; f.w = w; f.bias = bias; f.y = y; f.relu = relu;
         return hip_status(launch_fewchan_fprop(dtype, f, s));
     }
-    if (pl.kernel == 5) {
+    if (pl.kernel == 5 && !pl.padded) {  // (a padded plan carries its inner plan's kernel)
         PwArgs p;
         memset(&p, 0, sizeof(p));
         p.src = x; p.w = w; p.bias = bias; p.dst = y;
@@ -1094,13 +1161,12 @@ static int fprop_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         return hip_status(launch_direct_fprop(dtype, a, s));
     }
 
-    if (pl.kernel == 6) {
+    if (pl.kernel == 6 && !pl.padded) {
         PatchArgs pa;
         memset(&pa, 0, sizeof(pa));
-        int nb = 0, u = 0;
-        if (!patch_layout(d, dtype, &pa, &nb, &u)) return CONV2D_ERR_UNSUPPORTED;
+        if (!patch_layout(CONV2D_OP_FPROP, d, dtype, &pa, nullptr)) return CONV2D_ERR_UNSUPPORTED;
         pa.src = x; pa.filt = w; pa.bias = bias; pa.dst = y; pa.relu = relu;
-        return hip_status(launch_patch_fprop(dtype, nb, u, pa, s));
+        return hip_status(launch_patch(dtype, pa, false, s));
     }
     if (pl.tile == kBandTile)
         return run_band(dtype, d, (int)d.C, x, (int)d.H, (int)d.W, w, 0, bias, relu, m, y, (int)d.P, (int)d.Q,
@@ -1159,7 +1225,7 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
         f.dy = dy; f.w = w; f.dx = dx;
         return hip_status(launch_fewchan_dgrad(dtype, f, s));
     }
-    if (pl.kernel == 5) {
+    if (pl.kernel == 5 && !pl.padded) {  // (a padded plan carries its inner plan's kernel)
         PwArgs p;
         memset(&p, 0, sizeof(p));
         p.src = dy; p.w = w; p.bias = nullptr; p.dst = dx;
@@ -1167,6 +1233,13 @@ static int dgrad_run(const conv2d_problem_t *prob, int dtype, const void *dy, co
         p.src_bytes = (long long)p.npix * d.K * 2; p.w_bytes = d.K * d.C * 2;
         p.trans = 1;
         return hip_status(launch_pointwise(dtype, p, s));
+    }
+    if (pl.kernel == 6 && !pl.padded) {  // (a padded plan carries its inner plan's kernel)
+        PatchArgs pa;
+        memset(&pa, 0, sizeof(pa));
+        if (!patch_layout(CONV2D_OP_DGRAD, d, dtype, &pa, nullptr)) return CONV2D_ERR_UNSUPPORTED;
+        pa.src = dy; pa.filt = w; pa.bias = nullptr; pa.dst = dx; pa.relu = 0;
+        return hip_status(launch_patch(dtype, pa, true, s));
     }
 
     if (pl.padded) {
@@ -1385,7 +1458,7 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
             launch_splitk_reduce(dtype, (const float *)workspace, pl.split_k, a.total, a.part_stride, dw, &re, s));
     }
 
-    if (pl.kernel == 5) {
+    if (pl.kernel == 5 && !pl.padded) {  // (a padded plan carries its inner plan's kernel)
         PwWgradArgs p;
         memset(&p, 0, sizeof(p));
         p.x = x; p.dy = dy; p.out = workspace;

@@ -115,30 +115,43 @@ hipError_t launch_igemm(int dtype, int tile, const IgemmArgs &a, int grid_m, int
                         hipStream_t st);
 
 // ---------------------------------------------------------------------------
-// Patch kernel (patch.hip): fprop with the workgroup's input patch in LDS.
-// Along each axis the input rows a convolution reads lie on a lattice of
-// step g = gcd(stride, dil) (lattice row i is input row g*i - pad); on it the
+// Patch kernel (patch.hip): the workgroup's source patch in LDS.  Along each
+// axis the source rows a convolution reads lie on a lattice of step
+// g = gcd(stride, dil) (lattice row i is source row g*i - pad); on it the
 // convolution has stride sh1 = stride / g and dilation dh1 = dil / g.  A
-// workgroup computes TP x TQ output pixels (TP*TQ <= 128) of one image and
-// 32*nb output channels from PH x PW lattice pixels held at a pitch of PP
-// 16-byte slots (PP odd, PP >= C/8); groups == 1, C % 16 == 0, K % (32*nb) == 0.
+// workgroup computes TP x TQ output lattice pixels (TP*TQ <= 128) of one
+// image and 32*nb output channels from PH x PW lattice pixels held at a pitch
+// of PP 16-byte slots (PP odd, PP >= SC/8); TP*TQ <= 32*mb.  Output lattice pixel (p, q) is
+// destination pixel (oh0 + ogh*p, ow0 + ogw*q).
+// fprop: src = x (SC = C), dst = y, lattice extents P x Q, ogh = ogw = 1.
+// dgrad (stride dividing dilation): src = dy (SC = K, g = 1, sh1 = 1,
+//   dh1 = dil/stride, pad = the flipped filter's), dst = dx (OC = C), ogh =
+//   the stride; the dx pixels off the lattice are written as zeros.
+// groups == 1, SC % 16 == 0, OC % (32*nb) == 0.
 // ---------------------------------------------------------------------------
 struct PatchArgs {
-    const void *src;   // x [N][H][W][C]
+    const void *src;
     const void *filt;  // w [K][R][S][C]
-    const void *bias;  // [K] or null
-    void *dst;         // y [N][P][Q][K]
-    int N, H, W, C, P, Q, K, R, S;
+    const void *bias;  // fprop: [K] or null
+    void *dst;
+    int N, H, W, SC;   // source tensor
+    int OH, OW, OC;    // destination tensor
+    int P, Q;          // output lattice extents
+    int R, S;
     int gh, gw, pad_h, pad_w, sh1, sw1, dh1, dw1;
+    int ogh, ogw, oh0, ow0;
     int TP, TQ, tiles_q, tiles_img;
     int PH, PW, PP, patch_slots;
     int relu;
+    int nb, u, nsb, mb;  // output-channel blocks, super-step, ring depth, pixel blocks (2 or 4)
     FastDiv div_pp, div_pw, div_tq;
 };
-// u: 16-channel steps per super-step of the filter stream (1, 2 or 4; divides C/16)
-int patch_ring_bytes(int nb, int u);
+// u: 16-channel steps per super-step of the filter stream (1, 2 or 4;
+// divides SC/16); nsb: filter ring stages per wave (fprop:
+// patch_ring_stages(nb, u); dgrad: u = 1 and 4 or 8 stages)
+int patch_ring_stages(int nb, int u);
 int patch_lds_bytes();
-hipError_t launch_patch_fprop(int dtype, int nb, int u, const PatchArgs &a, hipStream_t st);
+hipError_t launch_patch(int dtype, const PatchArgs &a, bool dgrad, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Stride-1 band kernel (band.hip): filter in registers, a ring of input rows

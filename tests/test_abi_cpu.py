@@ -319,16 +319,23 @@ def test_winograd_tile_offered_only_where_it_applies():
     # (fprop: the patch kernel follows the band kernel)
     for op in (0, 1):
         info = B.conv2d_plan_info(op, base, "bf16")
-        assert info["num_tiles"] == 6 + (op == 0) and info["tile"] == 5 and info["kernel"] == 1
+        assert info["num_tiles"] == 7 and info["tile"] == 5 and info["kernel"] == 1
+        assert B.conv2d_plan_info(op, base, "bf16", algo=dict(tile=7))["kernel"] == 6
     # dgrad: the forward Winograd kernel on dy with the flipped, transposed
     # filter, whose transform goes to the workspace (16 x C x K elements)
+    # (the patch kernel's tile follows it: stride 1 divides any dilation)
     d = B.conv2d_plan_info(1, base, "f16")
-    assert d["num_tiles"] == 7 and d["tile"] == 5
+    assert d["num_tiles"] == 8 and d["tile"] == 5
     dw = B.conv2d_plan_info(1, base, "f16", algo=dict(tile=7))
     assert dw["kernel"] == 3 and dw["workspace_bytes"] == 16 * 64 * 64 * 2
-    assert B.conv2d_plan_info(1, problem(2, 64, 10, 12, 64, 3, 3, pad=(3, 3)), "f16")["num_tiles"] <= 6
-    assert B.conv2d_plan_info(1, problem(2, 48, 10, 12, 64, 3, 3, pad=(1, 1)), "f16")["num_tiles"] == 7
-    assert B.conv2d_plan_info(1, problem(2, 40, 10, 12, 64, 3, 3, pad=(1, 1)), "f16")["num_tiles"] <= 6
+    assert B.conv2d_plan_info(1, base, "f16", algo=dict(tile=8))["kernel"] == 6
+
+    def has_wino(prob):
+        n = B.conv2d_plan_info(1, prob, "f16")["num_tiles"]
+        return any(B.conv2d_plan_info(1, prob, "f16", algo=dict(tile=t))["kernel"] == 3 for t in range(1, n + 1))
+    assert not has_wino(problem(2, 64, 10, 12, 64, 3, 3, pad=(3, 3)))
+    assert has_wino(problem(2, 48, 10, 12, 64, 3, 3, pad=(1, 1)))
+    assert not has_wino(problem(2, 40, 10, 12, 64, 3, 3, pad=(1, 1)))
     others = [(base, "i8"), (base, "bf16"),
               (problem(2, 32, 10, 12, 64, 3, 3, pad=(1, 1)), "f16"),
               (problem(2, 64, 10, 12, 40, 3, 3, pad=(1, 1)), "f16"),

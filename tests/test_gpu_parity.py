@@ -112,6 +112,12 @@ CASES = [
     ("pad_both", problem(3, 5, 9, 10, 7, 3, 2, pad=(1, 0), stride=(1, 2), dil=(2, 1)), "f16", "gauss",
      True, True),
     ("pad_c60_band", problem(2, 60, 10, 12, 64, 3, 3, pad=(1, 1)), "f16", "int", True, True),
+    # padded problems whose padded copies take the pointwise kernels (1x1,
+    # 64 channels) and the patch kernel (dgrad: stride 2 divides dilation 2)
+    ("pad_c60_1x1", problem(2, 60, 9, 10, 64, 1, 1), "f16", "int", True, True),
+    ("pad_k60_1x1", problem(3, 64, 7, 9, 60, 1, 1), "bf16", "int", True, False),
+    ("pad_c29_patch", problem(2, 29, 9, 12, 12, 2, 2, pad=(0, 1), stride=(2, 1), dil=(2, 2)), "f16", "int",
+     False, False),
 ]
 
 
@@ -302,7 +308,9 @@ def test_every_tile_on_band_eligible_problem():
     assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16", algo=dict(tile=7))["kernel"] == 3
     assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, "f16", algo=dict(tile=8))["kernel"] == 6
     dinfo = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16")
-    assert dinfo["num_tiles"] == 7 and dinfo["tile"] == 5  # dgrad's last tile is Winograd too
+    assert dinfo["num_tiles"] == 8 and dinfo["tile"] == 5  # dgrad: Winograd too, then the patch kernel
+    assert B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16", algo=dict(tile=7))["kernel"] == 3
+    assert B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16", algo=dict(tile=8))["kernel"] == 6
     for t in range(1, info["num_tiles"] + 1):
         check(f64(run_fprop(prob, "f16", x, w, b, False, algo=dict(tile=t))), ref_y, "f16", "exact", f"tile {t}")
     for t in range(1, dinfo["num_tiles"] + 1):

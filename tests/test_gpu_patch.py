@@ -1,11 +1,16 @@
-"""The patch kernel (fprop with the workgroup's input patch in LDS, plan
-kernel 6) against the fp64 oracle, through the C ABI: exact on integer data,
-within max_rel / rms_scaled on Gaussian data.  The cases cover the lattice
-reading of strides and dilations (gcd(stride, dil) > 1 on an axis, and 1),
-asymmetric strides, dilations and padding, ragged last row and column tiles,
-several channel counts per 16-channel step (1, 3, 4, 6 steps per tap), the
-three output-channel block widths (32, 64, 96) and patches that limit the
-tile's row count."""
+"""The patch kernel (the workgroup's source patch in LDS, plan kernel 6)
+against the fp64 oracle, through the C ABI: exact on integer data, within
+max_rel / rms_scaled on Gaussian data.
+
+fprop cases cover the lattice reading of strides and dilations
+(gcd(stride, dil) > 1 on an axis, and 1), asymmetric strides, dilations and
+padding, ragged last row and column tiles, several channel counts per
+16-channel step (1, 3, 4, 6 steps per tap), the three output-channel block
+widths (32, 64, 96) and patches that limit the tile's row count.  dgrad cases
+(stride dividing dilation) cover stride 1 with and without dilation, stride 2
+and 3 with the dx rows and columns off the lattice (which the kernel writes
+as zeros: dx is pre-filled with NaN), a lattice that starts at row 1, and
+asymmetric filters."""
 import numpy as np
 import pytest
 
@@ -14,19 +19,20 @@ from convolution_nhwc_implicit_amd import binding as B
 from convolution_nhwc_implicit_amd import workloads as WL
 from convolution_nhwc_implicit_amd.workloads import problem
 
-from parity import check, f64, oracle_fprop_out, run_fprop
+from parity import check, f64, oracle_fprop_out, run_dgrad, run_fprop
 
 pytestmark = pytest.mark.gpu
 
 PATCH_KERNEL = 6
 
 
-def patch_tile(prob, dtype):
-    """1-based algo tile of the patch kernel (the last tile of the table)."""
-    info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype)
-    t = info["num_tiles"]
-    assert B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype, algo=dict(tile=t))["kernel"] == PATCH_KERNEL
-    return t
+def patch_tile(prob, dtype, op=B.CONV2D_OP_FPROP):
+    """1-based algo tile of the patch kernel in the pass's table."""
+    info = B.conv2d_plan_info(op, prob, dtype)
+    tiles = [t for t in range(1, info["num_tiles"] + 1)
+             if B.conv2d_plan_info(op, prob, dtype, algo=dict(tile=t))["kernel"] == PATCH_KERNEL]
+    assert len(tiles) == 1, tiles
+    return tiles[0]
 
 
 CASES = [
@@ -76,3 +82,36 @@ def test_patch_deterministic_and_matches_default_exactly():
     ya = run_fprop(prob, "f16", xi, wi, bi, True, algo=dict(tile=t))
     yb = run_fprop(prob, "f16", xi, wi, bi, True, algo=dict(tile=1))
     assert np.array_equal(f64(ya), f64(yb))
+
+
+DGRAD_CASES = [
+    # (id, problem, dtype, dist)
+    ("dg_s2d2_5x5", problem(2, 32, 23, 25, 96, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2)), "f16", "int"),
+    ("dg_s1_5x5", problem(2, 64, 17, 19, 64, 5, 5, pad=(2, 2)), "bf16", "int"),
+    ("dg_s1_d2", problem(2, 32, 15, 16, 32, 3, 3, pad=(2, 2), dil=(2, 2)), "f16", "int"),
+    ("dg_s2d4_pad3", problem(2, 32, 21, 22, 32, 3, 3, pad=(3, 3), stride=(2, 2), dil=(4, 4)), "f16", "int"),
+    ("dg_asym_s3", problem(1, 64, 20, 25, 48, 2, 3, pad=(1, 2), stride=(3, 1), dil=(3, 2)), "f16", "int"),
+    ("dg_even_hw", problem(3, 96, 16, 18, 64, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2)), "bf16", "int"),
+    ("dg_gauss_s2d2", problem(4, 96, 25, 25, 192, 5, 5, pad=(2, 2), stride=(2, 2), dil=(2, 2)), "bf16", "gauss"),
+    ("dg_gauss_s1", problem(2, 128, 20, 21, 96, 3, 3, pad=(1, 1)), "f16", "gauss"),
+]
+
+
+@pytest.mark.parametrize("cid,prob,dtype,dist", DGRAD_CASES, ids=[c[0] for c in DGRAD_CASES])
+def test_patch_dgrad(cid, prob, dtype, dist):
+    P, Q = oracle.output_hw(prob)
+    _, w, _, dy = WL.random_case(prob, dtype, dist, zlib_seed(cid), P, Q, bias=False)
+    ref = oracle.dgrad(prob, f64(dy), f64(w))
+    dx = run_dgrad(prob, dtype, dy, w, algo=dict(tile=patch_tile(prob, dtype, B.CONV2D_OP_DGRAD)),
+                   fill=float("nan"))
+    check(f64(dx), ref, dtype, "exact" if dist == "int" else "tol", cid)
+
+
+def test_patch_dgrad_refused_where_stride_does_not_divide_dilation():
+    """Stride 2 with dilation 1 leaves dx rows of both parities with taps:
+    the dgrad table has no patch kernel; fprop still has it."""
+    prob = problem(2, 64, 28, 28, 128, 3, 3, pad=(1, 1), stride=(2, 2))
+    n = B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16")["num_tiles"]
+    assert all(B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, "f16", algo=dict(tile=t))["kernel"] != PATCH_KERNEL
+               for t in range(1, n + 1))
+    patch_tile(prob, "f16")

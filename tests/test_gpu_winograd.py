@@ -30,12 +30,12 @@ pytestmark = pytest.mark.gpu
 U_TYPE = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
-def wino_tile(prob, dtype):
-    """The fprop Winograd tile: the one plan kernel 3 runs (the patch kernel's
-    tile follows it where that kernel applies)."""
-    info = B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype)
+def wino_tile(prob, dtype, op=B.CONV2D_OP_FPROP):
+    """The Winograd tile of a pass: the one plan kernel 3 runs (the patch
+    kernel's tile follows it where that kernel applies)."""
+    info = B.conv2d_plan_info(op, prob, dtype)
     tiles = [t for t in range(1, info["num_tiles"] + 1)
-             if B.conv2d_plan_info(B.CONV2D_OP_FPROP, prob, dtype, algo=dict(tile=t))["kernel"] == 3]
+             if B.conv2d_plan_info(op, prob, dtype, algo=dict(tile=t))["kernel"] == 3]
     assert len(tiles) == 1, tiles
     return dict(tile=tiles[0])
 
@@ -128,9 +128,7 @@ def dgrad_as_fprop(prob, w):
 
 
 def run_dgrad_wino(prob, dtype, dy, w):
-    algo = dict(tile=B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, dtype)["num_tiles"])
-    assert B.conv2d_plan_info(B.CONV2D_OP_DGRAD, prob, dtype, algo=algo)["kernel"] == 3
-    return run_dgrad(prob, dtype, dy, w, algo=algo, fill=float("nan"))
+    return run_dgrad(prob, dtype, dy, w, algo=wino_tile(prob, dtype, B.CONV2D_OP_DGRAD), fill=float("nan"))
 
 
 EXACT_D = [
