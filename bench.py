@@ -46,7 +46,7 @@ COPY_BYTES = 64 << 20  # reference copy for the HBM byte counters
 # the same counters on a plain copy) lives in this summary, keyed by a hash of
 # the kernel sources it was measured on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3a_hbm_traffic.json")
-KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip", "pointwise.hip", "pointwise_wgrad.hip"]
+KERNEL_SOURCES = ["band.hip", "wgrad_band.hip", "wgrad.hip", "igemm.hip", "api.cpp", "device_common.h", "internal.h", "direct.hip", "repack.hip", "fewchan.hip", "fewchan_wgrad.hip", "fewchan_dgrad.hip", "pointwise.hip", "pointwise_wgrad.hip", "patch.hip"]
 
 
 def kernel_source_hash():
@@ -319,7 +319,7 @@ def main():
     direct = plans["fprop"]["kernel"] == 2  # groups > 1
     def main_kernel(pl):
         return ("direct" if direct else "pointwise" if pl["kernel"] == 5 else "few_channel" if pl["kernel"] == 4
-                else "band" if pl["tile"] == BAND_TILE else "implicit_gemm")
+                else "patch" if pl["kernel"] == 6 else "band" if pl["tile"] == BAND_TILE else "implicit_gemm")
 
     kernels = {
         "fprop": [main_kernel(plans["fprop"])],
