@@ -374,14 +374,33 @@ bool wgrad_band_eligible(const Dims &d, int dtype)
 
 constexpr int kWgradBandTile = 2;  // wgrad tile index of the band kernel (algo tile 3), after the generic ones
 
-// Output rows per wgrad band: about one workgroup per CU, two workgroups
-// (column halves) per band.
-void wgrad_band_rows(const Dims &d, int *rows, int *chunks)
+// Bands of the wgrad band kernel, about one workgroup per CU.  With at least
+// 8 rows per band, bands of the stacked rows of all images, three
+// workgroups (filter rows) each: 85 bands of at most P rows, 255
+// workgroups, fp32 partials of 85 slices.  Otherwise bands within one image,
+// two workgroups (column halves) each.
+struct WgradBandLayout {
+    int nsplit;
+    int rows, chunks;      // nsplit = 2: rows per band, bands per image
+    int nbands;            // partial slices
+};
+WgradBandLayout wgrad_band_layout(const Dims &d)
 {
+    WgradBandLayout l = {};
+    const long long rows_total = d.N * d.P;
+    const long long nb3 = kNumCUs / 3;
+    if (rows_total >= 8 * nb3 && (rows_total + nb3 - 1) / nb3 <= d.P && rows_total < (1LL << 30)) {
+        l.nsplit = 3;
+        l.nbands = (int)nb3;
+        return l;
+    }
     long long c = (kNumCUs / 2 + d.N - 1) / d.N;
     c = std::max(1LL, std::min(c, d.P));
-    *rows = (int)((d.P + c - 1) / c);
-    *chunks = (int)((d.P + *rows - 1) / *rows);
+    l.nsplit = 2;
+    l.rows = (int)((d.P + c - 1) / c);
+    l.chunks = (int)((d.P + l.rows - 1) / l.rows);
+    l.nbands = (int)(d.N * l.chunks);
+    return l;
 }
 
 // Few-channel fprop (fewchan.hip): the window layout of each filter row
@@ -807,9 +826,7 @@ int make_plan(int op, const conv2d_problem_t *prob, int dtype, const conv2d_algo
         const long long ncols = d.R * d.S * d.Cg;  // per group
         if (use_band) {
             pl->tile = kWgradBandTile;
-            int rows, chunks;
-            wgrad_band_rows(d, &rows, &chunks);
-            pl->split_k = (int)(d.N * chunks);
+            pl->split_k = wgrad_band_layout(d).nbands;
             // with the bias gradient each slice also holds the band's K dy column sums
             const long long per = d.K * ncols + (ep.db ? d.K : 0);
             pl->ws_bytes = round_up((size_t)pl->split_k * splitk_stride(per) * sizeof(float), 256);
@@ -1485,13 +1502,20 @@ static int wgrad_run(const conv2d_problem_t *prob, int dtype, const void *x, con
         b.x = x; b.dy = dy; b.out = workspace;
         b.N = (int)d.N; b.H = (int)d.H; b.W = (int)d.W; b.P = (int)d.P; b.Q = (int)d.Q;
         b.pad_h = (int)d.ph; b.pad_w = (int)d.pw;
-        wgrad_band_rows(d, &b.rows_per_wg, &b.chunks_per_img);
+        const WgradBandLayout bl = wgrad_band_layout(d);
+        b.nsplit = bl.nsplit;
+        b.rows_per_wg = bl.rows;
+        b.chunks_per_img = bl.chunks;
+        b.nbands = bl.nbands;
+        b.rows_total = (int)(d.N * d.P);
+        b.band_f = (3 * bl.nbands) / 24;
+        b.div_p = make_fastdiv((uint32_t)d.P);
         const long long kcols = d.K * d.R * d.S * d.C;
         b.with_db = ep.db != nullptr;  // the bias gradient rides along in the slices
         b.part_stride = splitk_stride(kcols + (b.with_db ? d.K : 0));
         b.xw = (int)(d.Q + d.dw * (d.S - 1));
         b.div_xw = make_fastdiv((uint32_t)b.xw);
-        b.xcd_pairs = (d.N * b.chunks_per_img) % 8 == 0;
+        b.xcd_pairs = bl.nsplit == 2 && (d.N * b.chunks_per_img) % 8 == 0;
         hipError_t e = launch_wgrad_band(dtype, b, s);
         if (e != hipSuccess) return CONV2D_ERR_DEVICE;
         ReduceEpi rb = re;

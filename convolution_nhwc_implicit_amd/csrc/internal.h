@@ -315,8 +315,12 @@ hipError_t launch_colsum(int dtype, const ColsumArgs &a, int splits, hipStream_t
 
 // ---------------------------------------------------------------------------
 // Stride-1 3x3 wgrad band kernel (wgrad_band.hip): dy and x pixels in LDS,
-// transposing LDS reads.  Two workgroups (column halves) per (image, band of
-// rows_per_wg output rows); band b's fp32 partial [K][R*S*C] goes to
+// transposing LDS reads.  nsplit workgroups per band of output rows, each
+// with 1/nsplit of the R*S*C columns: nsplit = 2 (column halves), bands of
+// rows_per_wg rows of one image, chunks_per_img per image; nsplit = 3 (one
+// filter row each), nbands bands of the stacked rows of all images (row
+// n*P + p), band b = rows [b*rows_total/nbands, (b+1)*rows_total/nbands),
+// at most P rows.  Band b's fp32 partial [K][R*S*C] goes to
 // out + b * part_stride.
 // ---------------------------------------------------------------------------
 struct WgradBandArgs {
@@ -325,7 +329,10 @@ struct WgradBandArgs {
     void *out;
     int N, H, W, P, Q;
     int pad_h, pad_w;
-    int rows_per_wg, chunks_per_img;
+    int nsplit;
+    int rows_per_wg, chunks_per_img;  // nsplit = 2
+    int nbands, rows_total, band_f;   // nsplit = 3; band_f = (3 * nbands) / 24
+    FastDiv div_p;                    // nsplit = 3: divides by P
     long long part_stride;
     int xw;              // padded row pitch Q + dil*(S-1)
     FastDiv div_xw;

@@ -439,11 +439,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *parts, 
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     if (i < stride) {
         const float *p = parts + i;
-        int z = cls;
-        for (; z + 7 * NCLS < splits; z += 8 * NCLS) {
+        // eight slices of the class in flight; past the last slice a load
+        // gives +0, which leaves the sum unchanged
+        for (int z = cls; z < splits; z += 8 * NCLS) {
             f32x4 v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *(const f32x4 *)(p + (size_t)(z + u * NCLS) * stride);
+            for (int u = 0; u < 8; ++u)
+                v[u] = z + u * NCLS < splits ? *(const f32x4 *)(p + (size_t)(z + u * NCLS) * stride)
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 s[0] += v[u][0];
@@ -451,13 +454,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *parts, 
                 s[2] += v[u][2];
                 s[3] += v[u][3];
             }
-        }
-        for (; z < splits; z += NCLS) {
-            const f32x4 v = *(const f32x4 *)(p + (size_t)z * stride);
-            s[0] += v[0];
-            s[1] += v[1];
-            s[2] += v[2];
-            s[3] += v[3];
         }
     }
     part[cls][e] = s;

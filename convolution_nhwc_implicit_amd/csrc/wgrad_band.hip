@@ -12,23 +12,35 @@
 //
 // Pixels are numbered with the padded pitch XW = Q + dil*(S-1): output pixel
 // (p, q) of the band is v = p*XW + q, and its tap (r, s) of x is v + r*dil*XW
-// + s*dil.  dy is zero at the XW - Q padding columns, so the band is one
+// + s*dil (with one filter row a workgroup, v + s*dil of that row's window).  dy is zero at the XW - Q padding columns, so the band is one
 // linear stream of rows*XW pixels, cut into steps of 16 (one MFMA's
 // reduction) and groups of 16 steps that ignore row boundaries.  Steps past
 // the band's end read zero dy pixels (their loads fall outside the band's
 // rows) and add exact zeros; the last group runs only the steps per wave
 // that its band pixels need.
 //
-// A workgroup (8 waves, two per SIMD) owns a band of output rows of one image
-// and one half of the R*S*C columns (9 column blocks of 32), all of K.  Waves
-// 0-3 hold column blocks 0-4 and waves 4-7 blocks 5-8 of the half, both
-// k-blocks (32x32x16 MFMA accumulators, 160 or 128 fp32 registers); wave w
+// A workgroup (8 waves, two per SIMD) owns a band of output rows and a set of
+// column blocks of 32, all of K, and writes the band's fp32 partial for its
+// columns; the split-K reduction adds the bands' partials in order.  Two
+// splits of the 18 column blocks:
+//   * column halves (9 blocks each), bands within one image, two workgroups
+//     a band; the x window holds the group's pixels plus R-1 rows of halo;
+//   * filter rows (6 blocks each: the S taps x two channel halves of one r),
+//     three workgroups a band, for problems with at least 8 rows a band: 85
+//     bands (255 workgroups) of the stacked rows of all images (row n*P + p;
+//     a band crosses at most one image boundary).  Window row i is x row
+//     p + r - pad of dy row i's image, gathered row by row, so the x window
+//     is the dy window plus S-1 pixels and the partials are two thirds of
+//     the halves' (85 slices of the whole filter against 128 on 64x56x56).
+// Waves 0-3 hold the first ceil(n/2) of the workgroup's n column blocks and
+// waves 4-7 the rest, both k-blocks (32x32x16 MFMA accumulators); wave w
 // takes the steps t = w (mod 4).  The two waves of a SIMD work on the same
-// steps, so each SIMD does 18 MFMAs per step, and per step a wave reads its 2
-// dy fragments and one x fragment per column block: 13 fragments for 18
-// MFMAs per SIMD.  Two waves per SIMD keep twice as many transposing reads in
-// flight as one, and the LDS read rate grows with the reads in flight.  The
-// four waves' sums of each column set are added at the end in a fixed order.
+// steps: with halves each SIMD does 18 MFMAs per step and per step a wave
+// reads its 2 dy fragments and one x fragment per column block, 13 fragments
+// for 18 MFMAs per SIMD (filter rows: 10 for 12).  Two waves per SIMD keep
+// twice as many transposing reads in flight as one, and the LDS read rate
+// grows with the reads in flight.  The four waves' sums of each column set
+// are added at the end in a fixed order.
 //
 // Each group's dy pixels and x window (the group's pixels plus the tap
 // shifts) arrive by direct-to-LDS loads (buffer_load ... lds; pixels outside
@@ -38,9 +50,7 @@
 // that step's fragments are in registers, the wave waits for its share of the
 // next group's loads, meets the others, reads the next group's first
 // fragments during the last step's MFMAs and issues the loads of the group
-// after next, a few blocks at a time, between them.  Each workgroup writes
-// its fp32 partial sums; the split-K reduction adds the workgroups' partials
-// in order.
+// after next, a few blocks at a time, between them.
 //
 // 16-byte channel chunks of buffer pixel v are stored with chunk bit 2
 // flipped when bit 1 of v is set: the transposing reads of 4 consecutive
@@ -80,30 +90,45 @@ constexpr int CH = 64;                    // C = K = 64 channels, 128 bytes per 
 constexpr int PIXB = CH * 2;
 constexpr int R = 3, S = 3, DIL = 1;
 constexpr int NCOLS = R * S * CH;         // 576 columns (r, s, c)
-constexpr int CB_WG = NCOLS / 32 / 2;     // a workgroup computes 9 of the 18 column blocks
-constexpr int NCB_A = 5, NCB_B = CB_WG - NCB_A;  // column blocks of waves 0-3 and of waves 4-7
 constexpr int KB = CH / 32;               // k-blocks
 constexpr int GSTEPS = 16;                // steps of 16 pixels per group
 constexpr int GPIX = GSTEPS * 16;         // dy pixels per group
 constexpr int SLOTS = GSTEPS / PHASES;    // steps per wave per group
 constexpr int QMAX = 56;
 constexpr int XWMAX = QMAX + DIL * (S - 1);
-constexpr int HALO = DIL * (R - 1) * XWMAX + DIL * (S - 1);  // x pixels past a group's dy pixels
 constexpr int DCAP = GPIX;
-constexpr int XCAP = (GPIX + HALO + 63) / 64 * 64;  // whole 1 KB blocks for each of the 8 waves
-constexpr int D_BYTES = DCAP * PIXB, X_BYTES = XCAP * PIXB;
-constexpr int BUF_BYTES = D_BYTES + X_BYTES;
-constexpr int LDS_BYTES = 2 * BUF_BYTES;
-constexpr int DBLK = DCAP / 8, XBLK = XCAP / 8;  // 1 KB direct-to-LDS blocks of 8 pixels
-constexpr int NB_WAVE = (DBLK + XBLK) / WAVES;   // blocks per wave per group
+constexpr int D_BYTES = DCAP * PIXB;
+constexpr int DBLK = DCAP / 8;             // 1 KB direct-to-LDS blocks of 8 pixels
 constexpr int STEPB = PHASES * 16 * PIXB;  // a wave's next step in a group: 64 pixels on
 constexpr int RDB = 4 * PIXB;              // the second read of a fragment: 4 pixels on
 constexpr int TILE_BYTES = 64 * 16 * 4;    // one 32x32 fp32 accumulator block, all lanes
-static_assert(DBLK % WAVES == 0 && XBLK % WAVES == 0, "every wave loads the same blocks of each tensor");
+static_assert(DBLK % WAVES == 0, "every wave loads the same dy blocks");
 static_assert(GSTEPS % PHASES == 0 && SLOTS == 4, "four steps per wave per group");
-static_assert(LDS_BYTES <= 163840, "fits in the 160 KB LDS");
-static_assert(2 * KB * CB_WG * TILE_BYTES <= LDS_BYTES, "two phases' blocks of both sets fit in LDS");
-static_assert((SLOTS - 1) * STEPB + RDB + 32 < 65536, "read offsets fit the 16-bit immediate");
+
+// The column split: NSPLIT workgroups share a band's pixels, each with
+// NCOLS / NSPLIT columns.  NSPLIT = 2: column halves, the x window holds the
+// R tap rows.  NSPLIT = 3: one filter row r per workgroup (its S taps, all
+// channels); its x window is the band's rows shifted by r, so a window row
+// lines up with its dy row and only the S - 1 column shifts reach past it.
+template <int NSPLIT>
+struct Cfg {
+    static constexpr int CB_WG = NCOLS / 32 / NSPLIT;  // column blocks per workgroup: 9 or 6
+    static constexpr int NCB_A = (CB_WG + 1) / 2;       // column blocks of waves 0-3
+    static constexpr int NCB_B = CB_WG - NCB_A;         // and of waves 4-7
+    static constexpr int HALO = (NSPLIT == 2 ? DIL * (R - 1) * XWMAX : 0) + DIL * (S - 1);  // x pixels past a group's dy pixels
+    static constexpr int XCAP = (GPIX + HALO + 63) / 64 * 64;  // whole 1 KB blocks for each of the 8 waves
+    static constexpr int X_BYTES = XCAP * PIXB;
+    static constexpr int BUF_BYTES = D_BYTES + X_BYTES;
+    static constexpr int LDS_BYTES = 2 * BUF_BYTES;
+    static constexpr int XBLK = XCAP / 8;
+    static constexpr int NB_WAVE = (DBLK + XBLK) / WAVES;  // blocks per wave per group
+    static_assert(NSPLIT == 2 || NSPLIT == 3, "column halves or filter rows");
+    static_assert(NSPLIT == 2 || R == 3, "one filter row per workgroup of three");
+    static_assert(XBLK % WAVES == 0, "every wave loads the same x blocks");
+    static_assert(LDS_BYTES <= 163840, "fits in the 160 KB LDS");
+    static_assert(2 * KB * CB_WG * TILE_BYTES <= LDS_BYTES, "two phases' blocks of both sets fit in LDS");
+    static_assert((SLOTS - 1) * STEPB + RDB + 32 < 65536, "read offsets fit the 16-bit immediate");
+};
 
 template <int V>
 struct IntC {
@@ -121,34 +146,58 @@ __device__ __attribute__((always_inline)) inline void static_for(F &&f)
 __device__ inline int swz_chunk(int chunk, int v) { return chunk ^ (((v >> 1) & 1) << 2); }
 }  // namespace wb
 
-// The work of one wave: NCB column blocks from block CB0 of the half, the
-// steps t = phase (mod 4); then the set's sums and the partial's stores.
-template <class E, bool DB, int NCB, int CB0>
+// The work of one wave: NCB column blocks from block CB0 of the workgroup's
+// columns, the steps t = phase (mod 4); then the set's sums and the
+// partial's stores.
+template <class E, bool DB, int NSPLIT, int NCB, int CB0>
 __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const WgradBandArgs &a, unsigned char *smem,
                                                                      const int wave, const int lane)
 {
     using namespace wb;
     using elem = typename E::elem;
+    using Cf = Cfg<NSPLIT>;
+    constexpr int CB_WG = Cf::CB_WG, NB_WAVE = Cf::NB_WAVE, BUF_BYTES = Cf::BUF_BYTES;
     const int phase = wave & (PHASES - 1);
-    // Workgroup -> (band, column half).  Workgroups are dealt to the 8 XCDs
-    // in turn, so the two halves of a band go 8 apart: same XCD, and the
-    // second one's loads hit that XCD's L2.
-    int band, colh;
-    if (a.xcd_pairs) {
-        const int bid = blockIdx.x;
-        colh = (bid >> 3) & 1;
-        band = (bid & 7) + 8 * (bid >> 4);
+    // Workgroup -> (band, column set colh).  A band is output rows [t0, t0 +
+    // nrows) of the stack of all images' rows (row n*P + p is row p of image
+    // n).  Workgroups are dealt to the 8 XCDs in turn; the column sets of a
+    // band go 8 apart where the grid allows, so they share an XCD and the
+    // later ones' loads hit that XCD's L2.
+    int band, colh, t0, nrows, img;
+    if constexpr (NSPLIT == 2) {
+        // bands within one image: chunks_per_img bands of rows_per_wg rows
+        if (a.xcd_pairs) {
+            const int bid = blockIdx.x;
+            colh = (bid >> 3) & 1;
+            band = (bid & 7) + 8 * (bid >> 4);
+        } else {
+            colh = blockIdx.x & 1;
+            band = blockIdx.x >> 1;
+        }
+        img = band / a.chunks_per_img;
+        const int p_start = (band - img * a.chunks_per_img) * a.rows_per_wg;
+        nrows = min(p_start + a.rows_per_wg, a.P) - p_start;  // >= 1 by construction of the grid
+        t0 = img * a.P + p_start;
     } else {
-        colh = blockIdx.x & 1;
-        band = blockIdx.x >> 1;
+        // nbands bands of about rows_total / nbands rows (at most P, so a
+        // band spans at most two images).  XCD x takes the three filter rows
+        // of bands x*F .. x*F + F - 1 (F = band_f) in its first 3F
+        // workgroups; the rest of the grid deals the last bands in order.
+        const int bid = blockIdx.x, xcd = bid & 7, m = bid >> 3, F = a.band_f;
+        if (m < 3 * F) {
+            band = xcd * F + m / 3;
+            colh = m - (m / 3) * 3;
+        } else {
+            const int idx = (m - 3 * F) * 8 + xcd;
+            band = 8 * F + idx / 3;
+            colh = idx - (idx / 3) * 3;
+        }
+        t0 = (int)(((long long)band * a.rows_total) / a.nbands);
+        nrows = (int)(((long long)(band + 1) * a.rows_total) / a.nbands) - t0;
+        img = t0 / a.P;
     }
-    const int img = band / a.chunks_per_img;
-    const int chunk = band - img * a.chunks_per_img;
-    const int p_start = chunk * a.rows_per_wg;
-    const int p_end = min(p_start + a.rows_per_wg, a.P);
-    const int nrows = p_end - p_start;  // >= 1 by construction of the grid
     const int Q = a.Q, XW = a.xw;
-    const int h_base = p_start - a.pad_h;  // input row of band row 0, tap row 0
+    const int h_base = t0 - img * a.P - a.pad_h;  // column halves: input row of band row 0, tap row 0
     const int nsteps = (nrows * XW + 15) >> 4;
     const int ngroups = (nsteps + GSTEPS - 1) / GSTEPS;
 
@@ -160,9 +209,12 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
     // i/8).  The per-block arithmetic is redone in each call from an opaque
     // copy of them, so that the compiler does not keep every block's
     // addresses in registers across the loop.
-    const u32x4 x_rs = make_buf_rsrc((const elem *)a.x + (size_t)img * a.H * a.W * CH, (uint32_t)(a.H * a.W * CH * 2));
-    const u32x4 d_rs =
-        make_buf_rsrc((const elem *)a.dy + ((size_t)img * a.P + p_start) * Q * CH, (uint32_t)(nrows * Q * CH * 2));
+    // x: the band's image (and the next one, which a band of filter rows may
+    // reach into); offsets past the range read zeros
+    const int ximgs = NSPLIT == 2 ? 1 : min(2, a.N - img);
+    const u32x4 x_rs =
+        make_buf_rsrc((const elem *)a.x + (size_t)img * a.H * a.W * CH, (uint32_t)ximgs * (uint32_t)(a.H * a.W * CH * 2));
+    const u32x4 d_rs = make_buf_rsrc((const elem *)a.dy + (size_t)t0 * Q * CH, (uint32_t)(nrows * Q * CH * 2));
     const uint32_t lds0 = lds_addr(smem);
     const int lane_px = lane >> 3;
     const int lane_chunk16 = swz_chunk(lane & 7, lane_px) * 16;
@@ -182,9 +234,20 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
             const int b = wave + WAVES * (JB - DBLK / WAVES);
             const int v = px + b * 8;
             const int row = (int)fdiv((uint32_t)v, a.div_xw), col = v - row * XW;
-            const int h = h_base + row, w = col - a.pad_w;
-            const bool in = (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W;
-            dma16(x_rs, buf + D_BYTES + b * 1024, in ? (unsigned)((h * a.W + w) * PIXB + ch) : kBufOOB);
+            // window pixels past the last one a fragment reads are not fetched
+            const int w = b * 8 + lane_px < GPIX + Cf::HALO ? col - a.pad_w : -1;
+            if constexpr (NSPLIT == 2) {
+                const int h = h_base + row;
+                const bool in = (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W;
+                dma16(x_rs, buf + D_BYTES + b * 1024, in ? (unsigned)((h * a.W + w) * PIXB + ch) : kBufOOB);
+            } else {
+                // window row `row` is dy row t0 + row of image n, shifted by the filter row
+                const int t = t0 + row, n = (int)fdiv((uint32_t)t, a.div_p);
+                const int h = t - n * a.P - a.pad_h + colh * DIL;
+                const bool in = (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W && n - img < ximgs;
+                dma16(x_rs, buf + D_BYTES + b * 1024,
+                      in ? (unsigned)((((n - img) * a.H + h) * a.W + w) * PIXB + ch) : kBufOOB);
+            }
         }
     };
     auto dma_lane = [&](int g, int &px, int &ch) __attribute__((always_inline)) {
@@ -209,7 +272,7 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
         const int c_ = 16 * g_ + 4 * (L_ & 3);
         const int v = 16 * phase + 8 * lhi + (L_ >> 2);
         const int tap = cb >> 1, tr_ = tap / S, ts_ = tap - tr_ * S;
-        const int xv = v + tr_ * DIL * XW + ts_ * DIL;
+        const int xv = v + (NSPLIT == 2 ? tr_ * DIL * XW : 0) + ts_ * DIL;  // filter rows: the row is in the window
         return D_BYTES + xv * PIXB + swz_chunk((cb & 1) * 4 + (c_ >> 3), xv) * 16 + (c_ & 7) * 2;
     };
     typedef __attribute__((address_space(3))) unsigned char lds_u8;  // 32-bit LDS addresses
@@ -325,9 +388,13 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
     read_dy(odA, J0{});
 #pragma unroll
     for (int i = 0; i < NCB; ++i) read_x(i, J0{});
-    // A last group of at most 8 steps computes only its first two slots.
-    const bool half = nsteps - (ngroups - 1) * GSTEPS <= GSTEPS / 2;
-    const int nfull = half ? ngroups - 1 : ngroups;
+    // A last group of at most 12 steps computes only the slots its steps
+    // need, two or three (the steps of a slot are its four phases).
+    // (Column halves: two slots or the whole group; a third tail shape makes
+    // the compiler spill their ten accumulator blocks.)
+    int tail_slots = (nsteps - (ngroups - 1) * GSTEPS + PHASES - 1) / PHASES;  // 1 .. 4
+    if (NSPLIT == 2 && tail_slots == 3) tail_slots = SLOTS;
+    const int nfull = tail_slots == SLOTS ? ngroups : ngroups - 1;
     for (int g = 0; g < nfull; ++g) {
         slot(odA, odB, J1{}, none);
         slot(odB, odA, J2{}, none);
@@ -354,10 +421,14 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
         });
     }
     // the short last group (its slot-0 fragments are in odA and fx); the
-    // reads of its second slot fetch fragments nothing uses
-    if (half) {
+    // reads of its last slot fetch fragments nothing uses
+    if (tail_slots <= 2) {
         slot(odA, odB, J1{}, none);
         slot(odB, odA, J1{}, none);
+    } else if (NSPLIT == 3 && tail_slots == 3) {
+        slot(odA, odB, J1{}, none);
+        slot(odB, odA, J2{}, none);
+        slot(odA, odB, J2{}, none);
     }
 
     // ---- the four phases' sums of each column set, in a fixed order
@@ -369,7 +440,7 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
     // accumulator rows); the lane holds column l32 of its block, rows
     // 8*(r/4) + 4*(lane/32) + r%4.
     constexpr int NT_ = KB * NCB;  // this set's blocks
-    constexpr int SET_BASE = CB0 == 0 ? 0 : 2 * KB * NCB_A * TILE_BYTES;
+    constexpr int SET_BASE = CB0 == 0 ? 0 : 2 * KB * Cf::NCB_A * TILE_BYTES;
     f32x4 *const lds4 = (f32x4 *)smem + lane;
     auto part = [&](int h) { return lds4 + (SET_BASE + h * NT_ * TILE_BYTES) / 16; };
     auto park = [&](f32x4 *p, int t, const f32x16 &v) __attribute__((always_inline)) {
@@ -445,17 +516,18 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
     }
 }
 
-template <class E, bool DB>
+template <class E, bool DB, int NSPLIT>
 __global__ __launch_bounds__(512) void wgrad_band_kernel(const WgradBandArgs a)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[wb::LDS_BYTES];
+    using Cf = wb::Cfg<NSPLIT>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::LDS_BYTES];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // waves 0-3 (one per SIMD) and 4-7 (the second of each SIMD) take the two column sets
     if (wave < wb::PHASES)
-        wgrad_band_wave<E, DB, wb::NCB_A, 0>(a, smem, wave, lane);
+        wgrad_band_wave<E, DB, NSPLIT, Cf::NCB_A, 0>(a, smem, wave, lane);
     else
-        wgrad_band_wave<E, DB, wb::NCB_B, wb::NCB_A>(a, smem, wave, lane);
+        wgrad_band_wave<E, DB, NSPLIT, Cf::NCB_B, Cf::NCB_A>(a, smem, wave, lane);
 }
 
 bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q)
@@ -463,21 +535,30 @@ bool wgrad_band_supported(int R, int S, int C, int K, int dil, int Q)
     return R == wb::R && S == wb::S && C == wb::CH && K == wb::CH && dil == wb::DIL && Q >= 1 && Q <= wb::QMAX;
 }
 
+template <class E, bool DB>
+static void launch_wgrad_band_e(const WgradBandArgs &a, hipStream_t st)
+{
+    if (a.nsplit == 3)
+        wgrad_band_kernel<E, DB, 3><<<dim3((unsigned)(3 * a.nbands)), wb::NT, 0, st>>>(a);
+    else
+        wgrad_band_kernel<E, DB, 2><<<dim3((unsigned)(2 * a.N * a.chunks_per_img)), wb::NT, 0, st>>>(a);
+}
+
 hipError_t launch_wgrad_band(int dtype, const WgradBandArgs &a, hipStream_t st)
 {
-    dim3 grid((unsigned)(2 * a.N * a.chunks_per_img));  // two column halves per band
+    if (a.nsplit != 2 && a.nsplit != 3) return hipErrorInvalidValue;
     switch (dtype) {
     case CONV2D_DTYPE_F16:
         if (a.with_db)
-            wgrad_band_kernel<EF16, true><<<grid, wb::NT, 0, st>>>(a);
+            launch_wgrad_band_e<EF16, true>(a, st);
         else
-            wgrad_band_kernel<EF16, false><<<grid, wb::NT, 0, st>>>(a);
+            launch_wgrad_band_e<EF16, false>(a, st);
         break;
     case CONV2D_DTYPE_BF16:
         if (a.with_db)
-            wgrad_band_kernel<EBF16, true><<<grid, wb::NT, 0, st>>>(a);
+            launch_wgrad_band_e<EBF16, true>(a, st);
         else
-            wgrad_band_kernel<EBF16, false><<<grid, wb::NT, 0, st>>>(a);
+            launch_wgrad_band_e<EBF16, false>(a, st);
         break;
     default: return hipErrorInvalidValue;
     }

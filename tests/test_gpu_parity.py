@@ -103,6 +103,14 @@ CASES = [
     ("wband_bf16", problem(16, 64, 20, 20, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
     ("wband_q56", problem(2, 64, 23, 56, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
     ("wband_wide", problem(4, 64, 9, 64, 64, 3, 3, pad=(1, 1)), "f16", "int", True, True),
+    # with at least 8 * 85 output rows over all images the wgrad band kernel
+    # splits the columns by filter row over 85 bands of the stacked rows:
+    # bands of 8-9 rows across image boundaries, no padding, padding 2, and
+    # Gaussian bf16 (the short last groups of 1-3 slots come up per band)
+    ("wband3_cross", problem(13, 64, 56, 20, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
+    ("wband3_pad0", problem(24, 64, 32, 16, 64, 3, 3), "f16", "int", False, False),
+    ("wband3_pad2", problem(20, 64, 34, 12, 64, 3, 3, pad=(2, 2)), "f16", "int", False, False),
+    ("wband3_bf16", problem(12, 64, 60, 24, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
     # channel counts that are not whole 16-byte vectors run on zero-padded
     # copies: a stem-like C = 3 7x7 stride-2 layer, an odd K, both odd with
     # stride and dilation, and C = 60 whose padded problem takes the band
@@ -325,6 +333,17 @@ def test_int8_every_tile():
     for t in range(1, B.conv2d_plan_info(0, prob, "i8")["num_tiles"] + 1):
         y = run_fprop(prob, "i8", x, w, b, True, scales=scales, algo=dict(tile=t))
         assert np.array_equal(y.cpu().numpy().reshape(-1), exp), f"tile {t}"
+
+
+@pytest.mark.parametrize("prob,split", [
+    (problem(8, 64, 18, 16, 64, 3, 3, pad=(1, 1)), 8 * 9),    # column halves: 9 bands of 2 rows per image
+    (problem(13, 64, 56, 20, 64, 3, 3, pad=(1, 1)), 85),      # filter rows: 85 bands
+    (problem(64, 64, 56, 56, 64, 3, 3, pad=(1, 1)), 85),
+], ids=["halves", "rows_small", "rows_c3a"])
+def test_wgrad_band_split(prob, split):
+    """The band kernel's partial slices: one per band."""
+    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
+    assert info["tile"] == 2 and info["split_k"] == split, info
 
 
 def test_wgrad_band_and_generic_agree():

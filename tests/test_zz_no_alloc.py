@@ -30,7 +30,7 @@ def noalloc(prob, dtype, x, dy, algo=None):
 
 
 CALLS = [
-    # the wgrad band kernel, 16 images (64 band slices of partials)
+    # the wgrad band kernel, 16 images (85 band slices of partials, one filter row per workgroup)
     ("band", problem(16, 64, 56, 56, 64, 3, 3, pad=(1, 1)), "f16", "int", None),
     # a smaller problem on the generic 64 x 64 wgrad kernel with 7 slices
     ("generic", problem(2, 32, 13, 11, 48, 3, 3, pad=(1, 1), stride=(2, 1)), "bf16", "int", dict(split_k=7)),
