@@ -180,40 +180,54 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const WgradArgs a)
     // half add up the dy values their fragments hold (every dy element of
     // the slice once); lane holds channel wm*64 + 32*i + l%32
     const bool dbw = a.with_db && nt == 0 && wn == 0;  // wave-uniform
+    const bool idle = mt * BM + wm * 64 >= a.Kg;        // wave-uniform
     float dbacc[2] = {0.0f, 0.0f};
 
 #pragma unroll
     for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
         if (s0 < KT) dma_stage(s0);
-    for (int kt = 0; kt < KT; ++kt) {
-        // stage kt has landed when at most the younger stage's loads remain
-        if (kt + 1 < KT)
-            wait_vm_n<PER * (NSTAGE - 2)>();
-        else
-            wait_vm_n<0>();
-        __syncthreads();  // every wave's loads of stage kt are visible; stage kt-1 is consumed
-        if (kt + NSTAGE - 1 < KT) dma_stage(kt + NSTAGE - 1);
-        const unsigned char *ta = smem + (kt % NSTAGE) * STAGE;
-        const unsigned char *tb = ta + TILE;
+    // The main loop; a wave whose 64 rows all lie past the group's K (the
+    // last row tile of K = 192, say) runs it without the MFMA work, only
+    // loading and meeting the barriers, and leaves its SIMD to the other
+    // workgroups' waves.  (Two copies of the loop: a branch inside it around
+    // the MFMAs costs registers.)
+    auto main_loop = [&](auto compute_c) __attribute__((always_inline)) {
+        for (int kt = 0; kt < KT; ++kt) {
+            // stage kt has landed when at most the younger stage's loads remain
+            if (kt + 1 < KT)
+                wait_vm_n<PER * (NSTAGE - 2)>();
+            else
+                wait_vm_n<0>();
+            __syncthreads();  // every wave's loads of stage kt are visible; stage kt-1 is consumed
+            if (kt + NSTAGE - 1 < KT) dma_stage(kt + NSTAGE - 1);
+            if constexpr (decltype(compute_c)::value) {
+                const unsigned char *ta = smem + (kt % NSTAGE) * STAGE;
+                const unsigned char *tb = ta + TILE;
 #pragma unroll
-        for (int ks = 0; ks < SP / 16; ++ks) {
-            u32x4 fa[2], fb[2];
+                for (int ks = 0; ks < SP / 16; ++ks) {
+                    u32x4 fa[2], fb[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = frag(ta, wm * 64 + 32 * i, ks);
+                    for (int i = 0; i < 2; ++i) fa[i] = frag(ta, wm * 64 + 32 * i, ks);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = frag(tb, wn * 64 + 32 * j, ks);
+                    for (int j = 0; j < 2; ++j) fb[j] = frag(tb, wn * 64 + 32 * j, ks);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                    for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = Mfma32x16<E>::run(fa[i], fb[j], acc[i][j]);
-            if (dbw) {
+                        for (int j = 0; j < 2; ++j) acc[i][j] = Mfma32x16<E>::run(fa[i], fb[j], acc[i][j]);
+                    if (dbw) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                        for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) dbacc[i] = DotOne<E>::add(fa[i][q], dbacc[i]);
+                            for (int q = 0; q < 4; ++q) dbacc[i] = DotOne<E>::add(fa[i][q], dbacc[i]);
+                    }
+                }
             }
         }
-    }
+    };
+    if (idle)
+        main_loop(std::integral_constant<bool, false>{});
+    else
+        main_loop(std::integral_constant<bool, true>{});
     if (dbw) {
         // lanes l and l + 32 hold the two pixel halves of a channel
 #pragma unroll
