@@ -58,15 +58,16 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(pass_name):
+def measured_traffic(workload, pass_name):
     """HBM bytes per launch of a pass from the committed counter summary, or
-    None when it is absent or was taken on different kernel sources."""
+    None when it is absent, covers another workload or was taken on different
+    kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
         return None
     p = t.get("passes", {}).get(pass_name)
     return None if p is None else p.get("hbm_bytes")
@@ -75,7 +76,7 @@ def measured_traffic(pass_name):
 COUNTER_FILE = os.path.join(ROOT, "profiles", "c3a_mfma_counters.json")
 
 
-def measured_counters(pass_name):
+def measured_counters(workload, pass_name):
     """(clock GHz, MFMA-busy fraction) of the pass's main kernel under
     rocprofv3, from the committed counter summary, while the kernel sources
     are the ones it was taken on; else None.  The clock is SQ_BUSY_CYCLES per
@@ -87,7 +88,7 @@ def measured_counters(pass_name):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
         return None
     p = t.get("passes", {}).get(pass_name)
     return None if p is None else (p.get("clock_ghz"), p.get("mfma_busy_frac"))
@@ -346,7 +347,7 @@ def main():
             "kernels": kernels[pname],
             "plan": plans[pname],
         }
-        mc = measured_counters(pname) if name == "c3a_resnet3x3" else None
+        mc = measured_counters(name, pname)
         if mc is not None and mc[0]:
             # the dense MFMA rate at the (lower-bound) clock the kernel ran at
             # under the profiler, so this fraction is an upper bound
@@ -365,7 +366,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": d["alg_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(d["alg_gbs"] / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(dom)
+    roof["traffic"] = measured_traffic(name, dom)
     if "frac_mfma_peak_at_clock" in d and roof["bound"] == "mfma":
         roof["clock_ghz_counters"] = d["clock_ghz_counters"]
         roof["frac_at_clock"] = d["frac_mfma_peak_at_clock"]

@@ -352,3 +352,23 @@ def test_winograd_tile_offered_only_where_it_applies():
     with pytest.raises(B.Conv2dError) as e:
         B.conv2d_workspace_size_ex(0, base, "f16", algo=dict(tile=7), epi=dict(alpha=2.0, beta=0.0))
     assert e.value.status == B.CONV2D_ERR_UNSUPPORTED
+
+
+def test_bench_counters_only_for_their_workload():
+    """The committed counter summaries (HBM bytes, clock and MFMA-busy
+    fraction) were taken on one workload; bench.py reports them for that
+    workload only, and only while the kernel sources hash to the ones they
+    were taken on."""
+    import json
+    import bench
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    wl = t["workload"]
+    other = "c4_awkward" if wl != "c4_awkward" else "c3a_resnet3x3"
+    for p in ("fprop", "dgrad", "wgrad"):
+        assert bench.measured_traffic(other, p) is None
+        assert bench.measured_counters(other, p) is None
+        if t["source_hash"] == bench.kernel_source_hash():
+            assert bench.measured_traffic(wl, p) == t["passes"][p]["hbm_bytes"]
+        else:
+            assert bench.measured_traffic(wl, p) is None
