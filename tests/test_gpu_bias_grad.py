@@ -83,8 +83,9 @@ def test_wgrad_with_fused_bias_grad_full_size():
 
 @pytest.mark.parametrize("prob", [
     problem(2, 64, 10, 12, 64, 3, 3, pad=(1, 1)),                       # all three wgrad kernels
+    problem(76, 64, 9, 24, 64, 3, 3, pad=(1, 1)),                       # band kernel by filter rows
     problem(3, 32, 11, 9, 136, 5, 3, pad=(2, 1), stride=(2, 1), dil=(1, 2)),
-], ids=["wband_shape", "strided"])
+], ids=["wband_shape", "wband_rows", "strided"])
 def test_wgrad_db_every_tile(prob):
     """db beside wgrad on every wgrad kernel (fused into the 128x128 and band
     kernels, a second launch after the 64x64 one): dw is bit-identical to the
