@@ -374,11 +374,17 @@ bool wgrad_band_eligible(const Dims &d, int dtype)
 
 constexpr int kWgradBandTile = 2;  // wgrad tile index of the band kernel (algo tile 3), after the generic ones
 
-// Bands of the wgrad band kernel, about one workgroup per CU.  With at least
-// 8 rows per band, bands of the stacked rows of all images, three
-// workgroups (filter rows) each: 85 bands of at most P rows, 255
-// workgroups, fp32 partials of 85 slices.  Otherwise bands within one image,
-// two workgroups (column halves) each.
+// Bands of the wgrad band kernel, about one workgroup per CU: bands within
+// one image, two workgroups (column halves) each, or 85 bands of the stacked
+// rows of all images, three workgroups (filter rows) each (255 workgroups,
+// fp32 partials of 85 slices).  The split with the lower estimated time, from
+// a model fitted to measured passes on one MI355X (64x56x56x64 -> 64 at
+// N = 64, 96 and 128): per unit of band work (the 28 x 58 pixel steps of a
+// column half of N = 64) 14.7 us with halves, 17.6 us with filter rows (more
+// fragment reads per MFMA); 0.5 us per MB of partials (stored, then read by
+// the reduce); 4.0 and 3.1 us of fixed cost.  Halves that need a second
+// round of workgroups pay their band work twice.  Filter rows only with at
+// least 4 rows a band.
 struct WgradBandLayout {
     int nsplit;
     int rows, chunks;      // nsplit = 2: rows per band, bands per image
@@ -386,20 +392,31 @@ struct WgradBandLayout {
 };
 WgradBandLayout wgrad_band_layout(const Dims &d)
 {
-    WgradBandLayout l = {};
-    const long long rows_total = d.N * d.P;
-    const long long nb3 = kNumCUs / 3;
-    if (rows_total >= 8 * nb3 && (rows_total + nb3 - 1) / nb3 <= d.P && rows_total < (1LL << 30)) {
-        l.nsplit = 3;
-        l.nbands = (int)nb3;
-        return l;
-    }
+    WgradBandLayout h = {};
     long long c = (kNumCUs / 2 + d.N - 1) / d.N;
     c = std::max(1LL, std::min(c, d.P));
-    l.nsplit = 2;
-    l.rows = (int)((d.P + c - 1) / c);
-    l.chunks = (int)((d.P + l.rows - 1) / l.rows);
-    l.nbands = (int)(d.N * l.chunks);
+    h.nsplit = 2;
+    h.rows = (int)((d.P + c - 1) / c);
+    h.chunks = (int)((d.P + h.rows - 1) / h.rows);
+    h.nbands = (int)(d.N * h.chunks);
+
+    const long long rows_total = d.N * d.P;
+    const long long nb3 = kNumCUs / 3;
+    // x is read through one 32-bit buffer range over the images a band touches
+    const long long rows3 = (rows_total + nb3 - 1) / nb3;
+    const long long band_imgs = (rows3 + d.P - 1) / d.P + 1;
+    if (rows3 < 4 || rows_total >= (1LL << 30) ||  // (the model is fitted to bands of 42 rows and more)
+        (unsigned long long)(band_imgs * d.H * d.W * d.C * 2) > kBufMaxBytes)
+        return h;
+    const double unit = 28.0 * 58.0, xw = (double)(d.Q + d.dw * (d.S - 1));
+    const double part_mb = (double)(d.K * d.R * d.S * d.C) * 4.0 / 1e6;  // one slice
+    const long long rounds = (2LL * h.nbands + kNumCUs - 1) / kNumCUs;
+    const double t_halves = 14.7 * (double)rounds * h.rows * xw / unit + 0.5 * part_mb * h.nbands + 4.0;
+    const double t_rows = 17.6 * (double)rows3 * xw * (2.0 / 3.0) / unit + 0.5 * part_mb * (double)nb3 + 3.1;
+    if (t_rows >= t_halves) return h;
+    WgradBandLayout l = {};
+    l.nsplit = 3;
+    l.nbands = (int)nb3;
     return l;
 }
 

@@ -319,8 +319,8 @@ hipError_t launch_colsum(int dtype, const ColsumArgs &a, int splits, hipStream_t
 // with 1/nsplit of the R*S*C columns: nsplit = 2 (column halves), bands of
 // rows_per_wg rows of one image, chunks_per_img per image; nsplit = 3 (one
 // filter row each), nbands bands of the stacked rows of all images (row
-// n*P + p), band b = rows [b*rows_total/nbands, (b+1)*rows_total/nbands),
-// at most P rows.  Band b's fp32 partial [K][R*S*C] goes to
+// n*P + p), band b = rows [b*rows_total/nbands, (b+1)*rows_total/nbands).
+// Band b's fp32 partial [K][R*S*C] goes to
 // out + b * part_stride.
 // ---------------------------------------------------------------------------
 struct WgradBandArgs {

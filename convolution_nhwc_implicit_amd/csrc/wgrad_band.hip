@@ -28,7 +28,7 @@
 //   * filter rows (6 blocks each: the S taps x two channel halves of one r),
 //     three workgroups a band, for problems with at least 8 rows a band: 85
 //     bands (255 workgroups) of the stacked rows of all images (row n*P + p;
-//     a band crosses at most one image boundary).  Window row i is x row
+//     a band may cross image boundaries).  Window row i is x row
 //     p + r - pad of dy row i's image, gathered row by row, so the x window
 //     is the dy window plus S-1 pixels and the partials are two thirds of
 //     the halves' (85 slices of the whole filter against 128 on 64x56x56).
@@ -179,8 +179,8 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
         nrows = min(p_start + a.rows_per_wg, a.P) - p_start;  // >= 1 by construction of the grid
         t0 = img * a.P + p_start;
     } else {
-        // nbands bands of about rows_total / nbands rows (at most P, so a
-        // band spans at most two images).  XCD x takes the three filter rows
+        // nbands bands of about rows_total / nbands rows, across image
+        // boundaries.  XCD x takes the three filter rows
         // of bands x*F .. x*F + F - 1 (F = band_f) in its first 3F
         // workgroups; the rest of the grid deals the last bands in order.
         const int bid = blockIdx.x, xcd = bid & 7, m = bid >> 3, F = a.band_f;
@@ -209,9 +209,9 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
     // i/8).  The per-block arithmetic is redone in each call from an opaque
     // copy of them, so that the compiler does not keep every block's
     // addresses in registers across the loop.
-    // x: the band's image (and the next one, which a band of filter rows may
-    // reach into); offsets past the range read zeros
-    const int ximgs = NSPLIT == 2 ? 1 : min(2, a.N - img);
+    // x: the images the band's rows belong to; offsets past them read zeros
+    // (window rows past the band's end meet zero dy)
+    const int ximgs = NSPLIT == 2 ? 1 : (t0 + nrows - 1) / a.P - img + 1;
     const u32x4 x_rs =
         make_buf_rsrc((const elem *)a.x + (size_t)img * a.H * a.W * CH, (uint32_t)ximgs * (uint32_t)(a.H * a.W * CH * 2));
     const u32x4 d_rs = make_buf_rsrc((const elem *)a.dy + (size_t)t0 * Q * CH, (uint32_t)(nrows * Q * CH * 2));
@@ -246,7 +246,7 @@ __device__ __attribute__((always_inline)) inline void wgrad_band_wave(const Wgra
                 const int h = t - n * a.P - a.pad_h + colh * DIL;
                 const bool in = (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W && n - img < ximgs;
                 dma16(x_rs, buf + D_BYTES + b * 1024,
-                      in ? (unsigned)((((n - img) * a.H + h) * a.W + w) * PIXB + ch) : kBufOOB);
+                      in ? (unsigned)(((n - img) * a.H + h) * a.W + w) * (unsigned)PIXB + (unsigned)ch : kBufOOB);
             }
         }
     };

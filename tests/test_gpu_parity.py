@@ -111,8 +111,10 @@ CASES = [
     ("wband3_pad0", problem(24, 64, 32, 16, 64, 3, 3), "f16", "int", False, False),
     ("wband3_pad2", problem(20, 64, 34, 12, 64, 3, 3, pad=(2, 2)), "f16", "int", False, False),
     ("wband3_bf16", problem(12, 64, 60, 24, 64, 3, 3, pad=(1, 1)), "bf16", "gauss", False, False),
-    # 9-row images in bands of 8-9 rows: most bands cross an image boundary
+    # 9-row images in bands of 8-9 rows: most bands cross an image boundary;
+    # 6-row images in bands of 10-11 rows over two or three images
     ("wband3_short_img", problem(76, 64, 9, 24, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
+    ("wband3_three_imgs", problem(150, 64, 6, 16, 64, 3, 3, pad=(1, 1)), "f16", "int", False, False),
     # channel counts that are not whole 16-byte vectors run on zero-padded
     # copies: a stem-like C = 3 7x7 stride-2 layer, an odd K, both odd with
     # stride and dilation, and C = 60 whose padded problem takes the band
@@ -338,14 +340,16 @@ def test_int8_every_tile():
 
 
 @pytest.mark.parametrize("prob,split", [
-    (problem(8, 64, 18, 16, 64, 3, 3, pad=(1, 1)), 8 * 9),    # column halves: 9 bands of 2 rows per image
+    (problem(8, 64, 18, 16, 64, 3, 3, pad=(1, 1)), 8 * 9),    # 2-row bands: column halves, 9 per image
     (problem(13, 64, 56, 20, 64, 3, 3, pad=(1, 1)), 85),      # filter rows: 85 bands
     (problem(64, 64, 56, 56, 64, 3, 3, pad=(1, 1)), 85),
     (problem(76, 64, 9, 24, 64, 3, 3, pad=(1, 1)), 85),       # 684 rows, bands of 8-9 <= P = 9
-    (problem(86, 64, 8, 24, 64, 3, 3, pad=(1, 1)), 86 * 2),   # bands of 9 > P = 8: column halves, 2 per image
-], ids=["halves", "rows_small", "rows_c3a", "rows_short_img", "halves_short_img"])
+    (problem(150, 64, 6, 16, 64, 3, 3, pad=(1, 1)), 85),      # bands of 10-11 rows over 2-3 images
+    (problem(128, 64, 56, 56, 64, 3, 3, pad=(1, 1)), 128),    # twice the benchmark's work per CU: halves
+], ids=["halves", "rows_small", "rows_c3a", "rows_short_img", "rows_three_imgs", "halves_n128"])
 def test_wgrad_band_split(prob, split):
-    """The band kernel's partial slices: one per band."""
+    """The band kernel's partial slices, one per band: the split (column
+    halves or filter rows) with the lower estimated time."""
     info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
     assert info["tile"] == 2 and info["split_k"] == split, info
 
