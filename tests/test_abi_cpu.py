@@ -372,3 +372,18 @@ def test_bench_counters_only_for_their_workload():
             assert bench.measured_traffic(wl, p) == t["passes"][p]["hbm_bytes"]
         else:
             assert bench.measured_traffic(wl, p) is None
+
+
+@pytest.mark.parametrize("prob,split", [
+    (problem(8, 64, 18, 16, 64, 3, 3, pad=(1, 1)), 8 * 9),    # 2-row bands: column halves, 9 per image
+    (problem(13, 64, 56, 20, 64, 3, 3, pad=(1, 1)), 85),      # filter rows: 85 bands
+    (problem(64, 64, 56, 56, 64, 3, 3, pad=(1, 1)), 85),
+    (problem(76, 64, 9, 24, 64, 3, 3, pad=(1, 1)), 85),       # bands of 8-9 rows across 9-row images
+    (problem(150, 64, 6, 16, 64, 3, 3, pad=(1, 1)), 85),      # bands of 10-11 rows over 2-3 images
+    (problem(128, 64, 56, 56, 64, 3, 3, pad=(1, 1)), 128),    # twice the benchmark's work per CU: halves
+], ids=["halves", "rows_small", "rows_c3a", "rows_short_img", "rows_three_imgs", "halves_n128"])
+def test_wgrad_band_split(prob, split):
+    """The band kernel's partial slices, one per band: the split (column
+    halves or filter rows) with the lower estimated time."""
+    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
+    assert info["tile"] == 2 and info["split_k"] == split, info

@@ -339,21 +339,6 @@ def test_int8_every_tile():
         assert np.array_equal(y.cpu().numpy().reshape(-1), exp), f"tile {t}"
 
 
-@pytest.mark.parametrize("prob,split", [
-    (problem(8, 64, 18, 16, 64, 3, 3, pad=(1, 1)), 8 * 9),    # 2-row bands: column halves, 9 per image
-    (problem(13, 64, 56, 20, 64, 3, 3, pad=(1, 1)), 85),      # filter rows: 85 bands
-    (problem(64, 64, 56, 56, 64, 3, 3, pad=(1, 1)), 85),
-    (problem(76, 64, 9, 24, 64, 3, 3, pad=(1, 1)), 85),       # 684 rows, bands of 8-9 <= P = 9
-    (problem(150, 64, 6, 16, 64, 3, 3, pad=(1, 1)), 85),      # bands of 10-11 rows over 2-3 images
-    (problem(128, 64, 56, 56, 64, 3, 3, pad=(1, 1)), 128),    # twice the benchmark's work per CU: halves
-], ids=["halves", "rows_small", "rows_c3a", "rows_short_img", "rows_three_imgs", "halves_n128"])
-def test_wgrad_band_split(prob, split):
-    """The band kernel's partial slices, one per band: the split (column
-    halves or filter rows) with the lower estimated time."""
-    info = B.conv2d_plan_info(B.CONV2D_OP_WGRAD, prob, "f16")
-    assert info["tile"] == 2 and info["split_k"] == split, info
-
-
 def test_wgrad_band_and_generic_agree():
     prob = problem(8, 64, 18, 16, 64, 3, 3, pad=(1, 1))
     x, _, _, dy = case_inputs(prob, "f16", "int", seed=49)
