@@ -26,9 +26,9 @@
 //   * column halves (9 blocks each), bands within one image, two workgroups
 //     a band; the x window holds the group's pixels plus R-1 rows of halo;
 //   * filter rows (6 blocks each: the S taps x two channel halves of one r),
-//     three workgroups a band, for problems with at least 8 rows a band: 85
-//     bands (255 workgroups) of the stacked rows of all images (row n*P + p;
-//     a band may cross image boundaries).  Window row i is x row
+//     three workgroups a band: 85 bands (255 workgroups) of the stacked rows
+//     of all images (row n*P + p; a band may cross image boundaries).  The
+//     host picks the split with the lower estimated time.  Window row i is x row
 //     p + r - pad of dy row i's image, gathered row by row, so the x window
 //     is the dy window plus S-1 pixels and the partials are two thirds of
 //     the halves' (85 slices of the whole filter against 128 on 64x56x56).
